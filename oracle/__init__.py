@@ -1,0 +1,19 @@
+"""CPU oracle of the one-device MoE layer: dispatch, grouped SwiGLU FFN, combine,
+and their backward.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline use it; the product path never imports it.  It is numpy only and shares
+no code with the HIP library.  Each function cites the passage of the
+low_latency_combine page (Ascend CANN API) it follows.
+
+Parity status: every function here is pinned by a CPU test (see tests/test_oracle_pins.py);
+none is "parity unpinned".  The readings of silent points (masked-slot handling,
+duplicate handling, prefix kind, row order, summation order) are pinned only by
+internal consistency, as the pages print no output values.
+"""
+from .moe import (ERR_ID_DUPLICATE, ERR_ID_RANGE, ERR_MASK_NOT_PREFIX, Route, combine,
+                  combine_bwd, decode, dispatch, dispatch_bwd, ffn_bwd, ffn_fwd, layer_bwd,
+                  layer_fwd, route, silu)
+from .numerics import (bf16_to_f32, dequant_e4m3_blocks, dequant_e4m3_rows, dequant_int8_rows,
+                       e4m3_decode, e4m3_encode, f32_to_bf16, quant_e4m3_blocks, quant_e4m3_rows,
+                       quant_int8_rows, round_bf16)

@@ -1,0 +1,404 @@
+"""Plain CPU oracle of the one-device expert-parallel MoE layer (forward and backward).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module; the product path never does.  It shares no code
+with the HIP library and reads nothing the HIP library wrote.
+
+What it computes, and where that is defined
+-------------------------------------------
+The layer is the low_latency_dispatch / expert FFN / low_latency_combine chain of
+the Ascend CANN API page "low_latency_combine" (section "Function": Description and
+Formula; section "Parameters"), run with the expert-parallel world of one device, so
+the all-to-all is an identity permutation:
+
+* dispatch: every active routed slot (token t, choice k) of ``topk_idx`` gets one row
+  of the expanded buffer ``expand_x``; rows are grouped by expert, the per-expert
+  token counts come out as a prefix sum (``ep_recv_counts``, Parameters:
+  ``ep_send_counts``).
+* expert FFN: each expert runs a SwiGLU feed-forward block with intermediate size
+  ``ffn_dim`` (the ``--ffn_dim`` flag of the Triton-distributed benchmark page);
+  ``h = silu(x Wg^T) * (x Wu^T)``, ``y = h Wd^T``.  The weights use the (out, in)
+  layout of a linear layer.
+* combine (Formula): ``out[t] = Sum_k topk_weights[t,k] * v(t,k) + shared_expert_x[t]``
+  where v is the expert output of that slot; zero experts give 0, copy experts give
+  ``ori_x[t]``, constant expert j gives ``alpha_1[j]*ori_x[t] + alpha_2[j]*v[j]``
+  (Formula, special expert use cases; Parameters: zero/copy/const_expert_num give
+  the id ranges).  The shared-expert term is added once, unweighted (Parameters:
+  ``topk_weights`` and ``shared_expert_x``).
+* backward: the derivative of the above, written out step by step.
+
+Readings taken where the page is silent (each is listed in the design notes):
+masked slots contribute nothing and get no row; a duplicate id in a row is an
+error and its later occurrence is dropped; the prefix sum is inclusive; rows of
+one expert are in increasing slot order; sums over k run in k order in fp32 with
+the shared term last and one rounding to bf16 at the end.
+
+Precision modes
+---------------
+``"parity"``  fp32 arithmetic on the exact decode of the bf16 inputs, plus the
+              bf16 roundings of the intermediate tensors the device path stores
+              (expert output y, SwiGLU output h, saved gate/up, dY, dGU, dX, the
+              layer outputs).  Device outputs are judged against this mode.
+``"def"``     fp32, no intermediate roundings (the plain definition).
+``"f64"``     float64 throughout, no roundings; used for finite differences.
+
+Slot-to-row map (our contents of the opaque ``assist_info_for_combine``):
+``slot2row[t*K+k]`` is the row (>= 0) of a routed active slot, -1 for an inactive,
+zero-expert or invalid slot, -2 for a copy-expert slot and -(3+j) for constant
+expert j.  ``row2slot[r]`` is the slot of row r.
+
+Error bits: 1 = expert id out of range, 2 = duplicate id within a row,
+4 = one-dimensional activity mask that is not a prefix of trues.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .numerics import bf16_to_f32, round_bf16
+
+ERR_ID_RANGE = 1
+ERR_ID_DUPLICATE = 2
+ERR_MASK_NOT_PREFIX = 4
+
+PRECISIONS = ("parity", "def", "f64")
+
+
+def _ftype(prec):
+    if prec not in PRECISIONS:
+        raise ValueError(prec)
+    return np.float64 if prec == "f64" else np.float32
+
+
+def _store(prec):
+    """The rounding applied when the device path writes a bf16 tensor."""
+    if prec == "parity":
+        return lambda a: round_bf16(np.asarray(a, dtype=np.float32))
+    return lambda a: a
+
+
+def decode(a, prec="parity"):
+    """bf16 bit patterns (uint16) -> float array of the mode's dtype; floats pass through."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        a = bf16_to_f32(a)
+    return a.astype(_ftype(prec))
+
+
+# ============================================================================ routing
+
+
+@dataclass
+class Route:
+    T: int
+    K: int
+    E: int
+    counts: np.ndarray          # (E,) int32 tokens per routed expert (expert_token_nums)
+    ep_recv_counts: np.ndarray  # (E,) int32 inclusive prefix sum of counts
+    slot2row: np.ndarray        # (T*K,) int32, codes as in the module docstring
+    row2slot: np.ndarray        # (A,) int32
+    err: int
+
+    @property
+    def A(self) -> int:
+        return int(self.ep_recv_counts[-1]) if self.E > 0 else 0
+
+    def row_range(self, e):
+        lo = 0 if e == 0 else int(self.ep_recv_counts[e - 1])
+        return lo, int(self.ep_recv_counts[e])
+
+
+def route(topk_idx, E, Z=0, C=0, Q=0, mask=None) -> Route:
+    """Classify every slot, count tokens per expert and lay the rows out by expert.
+
+    low_latency_combine page, Parameters: ``topk_idx`` (ids in range, no duplicate
+    in a row), ``x_active_mask`` (1-D: token participates, trues first; 2-D: per
+    slot), ``ep_send_counts`` (prefix-summed counts), zero/copy/const id ranges.
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, K = idx.shape
+    err = 0
+    if mask is None:
+        act = np.ones((T, K), dtype=bool)
+    else:
+        m = np.asarray(mask).astype(bool)
+        if m.ndim == 1:
+            # trues must precede falses: no false followed by a true
+            if T > 1 and np.any(~m[:-1] & m[1:]):
+                err |= ERR_MASK_NOT_PREFIX
+            act = np.repeat(m[:, None], K, axis=1)
+        else:
+            act = m.copy()
+    e_tot = E + Z + C + Q
+    valid = (idx >= 0) & (idx < e_tot)
+    if not valid.all():
+        err |= ERR_ID_RANGE
+    dup = np.zeros((T, K), dtype=bool)
+    for k in range(1, K):
+        dup[:, k] = np.any(idx[:, :k] == idx[:, k:k + 1], axis=1)
+    if (dup & valid).any():
+        err |= ERR_ID_DUPLICATE
+    ok = act & valid & ~dup
+    flat_id = idx.reshape(-1)
+    flat_ok = ok.reshape(-1)
+
+    routed = flat_ok & (flat_id < E)
+    counts = np.zeros(E, dtype=np.int64)
+    for e in range(E):
+        counts[e] = np.count_nonzero(routed & (flat_id == e))
+    ep_recv_counts = np.cumsum(counts)
+
+    slot2row = np.full(T * K, -1, dtype=np.int64)
+    copy = flat_ok & (flat_id >= E + Z) & (flat_id < E + Z + C)
+    slot2row[copy] = -2
+    const = flat_ok & (flat_id >= E + Z + C) & (flat_id < e_tot)
+    slot2row[const] = -(3 + (flat_id[const] - (E + Z + C)))
+    A = int(ep_recv_counts[-1]) if E else 0
+    row2slot = np.empty(A, dtype=np.int64)
+    start = 0
+    for e in range(E):
+        slots = np.nonzero(routed & (flat_id == e))[0]  # increasing slot order
+        rows = start + np.arange(slots.size)
+        slot2row[slots] = rows
+        row2slot[rows] = slots
+        start += slots.size
+    return Route(T, K, E, counts.astype(np.int32), ep_recv_counts.astype(np.int32),
+                 slot2row.astype(np.int32), row2slot.astype(np.int32), err)
+
+
+def dispatch(x, r: Route, prec="parity"):
+    """expand_x[row] = x[token of row]: the one-device alltoallv of low_latency_dispatch."""
+    xf = decode(x, prec)
+    return xf[r.row2slot // r.K].copy()
+
+
+# ============================================================================ expert FFN
+
+
+def silu(g):
+    return g / (1 + np.exp(-g))
+
+
+def ffn_fwd(X, ep_recv_counts, w_gate, w_up, w_down, prec="parity"):
+    """Grouped SwiGLU FFN over the expert-sorted rows of X.
+
+    For expert e, rows [prefix[e-1], prefix[e]):  G = X Wg^T, U = X Wu^T,
+    H = silu(G) * U, Y = H Wd^T.  Returns the float arrays G, U, H, Y (with the
+    parity mode's bf16 roundings of what the device stores).
+    """
+    st = _store(prec)
+    ft = _ftype(prec)
+    X = np.asarray(X, dtype=ft)
+    Wg, Wu, Wd = decode(w_gate, prec), decode(w_up, prec), decode(w_down, prec)
+    E, F, H = Wg.shape
+    A = X.shape[0]
+    G = np.zeros((A, F), ft)
+    U = np.zeros((A, F), ft)
+    Hh = np.zeros((A, F), ft)
+    Y = np.zeros((A, H), ft)
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        if hi > lo:
+            g = X[lo:hi] @ Wg[e].T
+            u = X[lo:hi] @ Wu[e].T
+            h = st(silu(g) * u)
+            G[lo:hi], U[lo:hi], Hh[lo:hi] = st(g), st(u), h
+            Y[lo:hi] = st(h @ Wd[e].T)
+        lo = hi
+    return G, U, Hh, Y
+
+
+def ffn_bwd(dY, X, G, U, Hh, ep_recv_counts, w_gate, w_up, w_down, prec="parity"):
+    """Backward of ffn_fwd.
+
+    dH = dY Wd, dWd = dY^T H; with s = sigmoid(G):
+    dG = dH * U * s * (1 + G (1 - s)), dU = dH * G * s;
+    dX = [dG dU] [Wg; Wu], dWg = dG^T X, dWu = dU^T X.
+    Returns dGU (A, 2F), dX (A, H), dWg, dWu, dWd (weight grads unrounded).
+    """
+    st = _store(prec)
+    ft = _ftype(prec)
+    Wg, Wu, Wd = decode(w_gate, prec), decode(w_up, prec), decode(w_down, prec)
+    E, F, H = Wg.shape
+    dY, X, G, U, Hh = (np.asarray(a, dtype=ft) for a in (dY, X, G, U, Hh))
+    A = X.shape[0]
+    dGU = np.zeros((A, 2 * F), ft)
+    dX = np.zeros((A, H), ft)
+    dWg = np.zeros((E, F, H), ft)
+    dWu = np.zeros((E, F, H), ft)
+    dWd = np.zeros((E, H, F), ft)
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        if hi > lo:
+            dh = dY[lo:hi] @ Wd[e]
+            g, u = G[lo:hi], U[lo:hi]
+            s = 1 / (1 + np.exp(-g))
+            dg = st(dh * u * s * (1 + g * (1 - s)))
+            du = st(dh * (g * s))
+            dGU[lo:hi, :F], dGU[lo:hi, F:] = dg, du
+            dX[lo:hi] = st(np.concatenate([dg, du], 1) @ np.concatenate([Wg[e], Wu[e]], 0))
+            dWd[e] = dY[lo:hi].T @ Hh[lo:hi]
+            dWg[e] = dg.T @ X[lo:hi]
+            dWu[e] = du.T @ X[lo:hi]
+        lo = hi
+    return dGU, dX, dWg, dWu, dWd
+
+
+# ============================================================================ combine
+
+
+def _slot_value(code, t, Y, ori_x, a1, a2, v):
+    """Expert output of one slot (Formula of low_latency_combine)."""
+    if code >= 0:
+        return Y[code]
+    if code == -2:
+        return ori_x[t]
+    j = -code - 3
+    return a1[j] * ori_x[t] + a2[j] * v[j]
+
+
+def combine(Y, r: Route, topk_weights, shared_expert_x=None, ori_x=None,
+            const_alpha_1=None, const_alpha_2=None, const_v=None, prec="parity"):
+    """out[t] = Sum_k w[t,k] * v(t,k) (+ shared_expert_x[t]); sum in k order, shared last.
+
+    Slots coded -1 (inactive, zero expert) add nothing.
+    """
+    st = _store(prec)
+    ft = _ftype(prec)
+    T, K = r.T, r.K
+    Y = np.asarray(Y, dtype=ft)
+    w = np.asarray(topk_weights, dtype=ft)
+    ox = decode(ori_x, prec) if ori_x is not None else None
+    a1 = decode(const_alpha_1, prec) if const_alpha_1 is not None else None
+    a2 = decode(const_alpha_2, prec) if const_alpha_2 is not None else None
+    cv = decode(const_v, prec) if const_v is not None else None
+    H = Y.shape[1]
+    out = np.zeros((T, H), ft)
+    codes = r.slot2row.reshape(T, K)
+    for k in range(K):
+        c = codes[:, k]
+        for t in np.nonzero(c != -1)[0]:
+            out[t] = out[t] + w[t, k] * _slot_value(int(c[t]), t, Y, ox, a1, a2, cv)
+    if shared_expert_x is not None:
+        out = out + decode(shared_expert_x, prec)
+    return st(out)
+
+
+def combine_bwd(dOut, Y, r: Route, topk_weights, ori_x=None, const_alpha_1=None,
+                const_alpha_2=None, const_v=None, prec="parity"):
+    """Gradient of combine.
+
+    dY[row] = w[t,k] * dOut[t] for routed rows; dw[t,k] = <v(t,k), dOut[t]>
+    (0 for inactive and zero-expert slots).  The shared term's gradient is dOut
+    itself and the copy/const terms' gradient to ori_x is formed in dispatch_bwd.
+    """
+    st = _store(prec)
+    ft = _ftype(prec)
+    T, K = r.T, r.K
+    d = decode(dOut, prec)
+    Y = np.asarray(Y, dtype=ft)
+    w = np.asarray(topk_weights, dtype=ft)
+    ox = decode(ori_x, prec) if ori_x is not None else None
+    a1 = decode(const_alpha_1, prec) if const_alpha_1 is not None else None
+    a2 = decode(const_alpha_2, prec) if const_alpha_2 is not None else None
+    cv = decode(const_v, prec) if const_v is not None else None
+    dY = np.zeros_like(Y)
+    dw = np.zeros((T, K), ft)
+    codes = r.slot2row.reshape(T, K)
+    for t in range(T):
+        for k in range(K):
+            c = int(codes[t, k])
+            if c == -1:
+                continue
+            if c >= 0:
+                dY[c] = w[t, k] * d[t]
+            dw[t, k] = np.sum(_slot_value(c, t, Y, ox, a1, a2, cv) * d[t], dtype=ft)
+    return st(dY), dw
+
+
+def dispatch_bwd(dX, r: Route, topk_weights, dOut=None, const_alpha_1=None,
+                 grad_x_accum=None, prec="parity"):
+    """dx[t] = Sum_k (k order) of: dX[row] (routed), w*dOut[t] (copy),
+    w*(alpha_1[j]*dOut[t]) (constant j); then + grad_x_accum[t]; one rounding."""
+    st = _store(prec)
+    ft = _ftype(prec)
+    T, K = r.T, r.K
+    dX = np.asarray(dX, dtype=ft)
+    w = np.asarray(topk_weights, dtype=ft)
+    d = decode(dOut, prec) if dOut is not None else None
+    a1 = decode(const_alpha_1, prec) if const_alpha_1 is not None else None
+    H = dX.shape[1]
+    dx = np.zeros((T, H), ft)
+    codes = r.slot2row.reshape(T, K)
+    for k in range(K):
+        c = codes[:, k]
+        for t in np.nonzero(c != -1)[0]:
+            ct = int(c[t])
+            if ct >= 0:
+                dx[t] = dx[t] + dX[ct]
+            elif ct == -2:
+                dx[t] = dx[t] + w[t, k] * d[t]
+            else:
+                dx[t] = dx[t] + w[t, k] * (a1[-ct - 3] * d[t])
+    if grad_x_accum is not None:
+        dx = dx + np.asarray(grad_x_accum, dtype=ft)
+    return st(dx)
+
+
+# ============================================================================ whole layer
+
+
+def layer_fwd(inp: dict, prec="parity"):
+    """Whole forward: route, dispatch, grouped FFN, (shared FFN), combine.
+
+    ``inp`` keys: x, topk_idx, topk_weights, w_gate, w_up, w_down, E (and optional
+    Z, C, Q, mask, const_alpha_1/2, const_v, shared_w_gate/up/down,
+    shared_expert_x).  ``ori_x`` is the layer input x.
+    Returns a dict of every intermediate.
+    """
+    E = inp["E"]
+    Z, C, Q = inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0)
+    r = route(inp["topk_idx"], E, Z, C, Q, inp.get("mask"))
+    X = dispatch(inp["x"], r, prec)
+    G, U, Hh, Y = ffn_fwd(X, r.ep_recv_counts, inp["w_gate"], inp["w_up"], inp["w_down"], prec)
+    res = dict(route=r, X=X, G=G, U=U, Hh=Hh, Y=Y)
+    shared = inp.get("shared_expert_x")
+    if inp.get("shared_w_gate") is not None:
+        xs = decode(inp["x"], prec)
+        sG, sU, sH, sY = ffn_fwd(xs, np.array([xs.shape[0]]), inp["shared_w_gate"],
+                                 inp["shared_w_up"], inp["shared_w_down"], prec)
+        res.update(sX=xs, sG=sG, sU=sU, sH=sH, sY=sY)
+        shared = sY
+    res["out"] = combine(Y, r, inp["topk_weights"], shared, inp["x"], inp.get("const_alpha_1"),
+                         inp.get("const_alpha_2"), inp.get("const_v"), prec)
+    return res
+
+
+def layer_bwd(inp: dict, fwd: dict, grad_out, prec="parity"):
+    """Whole backward from grad_out; returns dx, dw, dWg, dWu, dWd (+ shared-expert grads).
+
+    When a precomputed shared_expert_x is passed its gradient is grad_out itself.
+    """
+    r = fwd["route"]
+    ft = _ftype(prec)
+    dY, dw = combine_bwd(grad_out, fwd["Y"], r, inp["topk_weights"], inp["x"],
+                         inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), prec)
+    dGU, dX, dWg, dWu, dWd = ffn_bwd(dY, fwd["X"], fwd["G"], fwd["U"], fwd["Hh"], r.ep_recv_counts,
+                                     inp["w_gate"], inp["w_up"], inp["w_down"], prec)
+    res = dict(dY=dY, dw=dw, dGU=dGU, dX=dX, dWg=dWg, dWu=dWu, dWd=dWd)
+    accum = None
+    if "sY" in fwd:
+        d = decode(grad_out, prec)
+        T = d.shape[0]
+        sdGU, sdX, sdWg, sdWu, sdWd = ffn_bwd(d, fwd["sX"], fwd["sG"], fwd["sU"], fwd["sH"],
+                                              np.array([T]), inp["shared_w_gate"], inp["shared_w_up"],
+                                              inp["shared_w_down"], prec)
+        res.update(s_dGU=sdGU, s_dX=sdX, s_dWg=sdWg, s_dWu=sdWu, s_dWd=sdWd)
+        accum = sdX
+    elif inp.get("shared_expert_x") is not None:
+        res["d_shared"] = decode(grad_out, prec).astype(ft)
+    res["dx"] = dispatch_bwd(dX, r, inp["topk_weights"], grad_out, inp.get("const_alpha_1"), accum, prec)
+    return res

@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+library routines, closed forms, hand counts from the low_latency_combine page's
+example tables, published format tables, brute force and finite differences.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign or index, a transposed operand, an unstable row order, a missing
+rounding) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as wl
+import oracle as orc
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "page2_topk_examples.json")
+
+
+def _gold():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+# ============================================================================ formats
+
+
+def test_bf16_round_matches_torch_cast():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    # add exact ties: low 16 bits = 0x8000 with both parities of bit 16
+    ties = (rng.integers(0, 2 ** 16, size=4096, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    bits = np.concatenate([bits, ties, np.array([0x7F7FFFFF, 0x7F7F8000, 0x00008000, 0x80018000],
+                                                dtype=np.uint32)])
+    x = bits.view(np.float32)
+    finite = np.isfinite(x)
+    ours = orc.f32_to_bf16(x[finite])
+    ref = torch.from_numpy(x[finite].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    nanx = np.array([np.nan, -np.nan], dtype=np.float32)
+    assert np.isnan(orc.bf16_to_f32(orc.f32_to_bf16(nanx))).all()
+
+
+def test_bf16_decode_is_exact():
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = orc.bf16_to_f32(allbits)
+    ref = torch.from_numpy(allbits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    same = (f == ref) | (np.isnan(f) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3_published_points():
+    g = _gold()["ocp_e4m3_points"]
+    for code, val in g["code_value"]:
+        assert orc.e4m3_decode(np.array([code], np.uint8))[0] == np.float32(val)
+    for code in g["nan_codes"]:
+        assert np.isnan(orc.e4m3_decode(np.array([code], np.uint8))[0])
+
+
+def test_e4m3_encode_roundtrip_and_ties():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = orc.e4m3_decode(codes)
+    assert np.array_equal(orc.e4m3_encode(vals), codes)
+    # midpoints between neighbouring magnitudes go to the even code
+    pos = orc.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    assert np.all((mids.astype(np.float64) == (pos[:-1] + pos[1:]) / 2))  # exact in fp32
+    enc = orc.e4m3_encode(mids)
+    lo = np.arange(0x7E)
+    expect = np.where(lo % 2 == 0, lo, lo + 1)
+    assert np.array_equal(enc, expect.astype(np.uint8))
+    # saturation and NaN
+    assert orc.e4m3_encode(np.array([448.0, 500.0, 1e30, -1e30], np.float32)).tolist() == [0x7E, 0x7E, 0x7E, 0xFE]
+    assert orc.e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch without float8_e4m3fn")
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32) * 30,
+                        rng.standard_normal(20000).astype(np.float32) * 0.01,
+                        (rng.random(20000).astype(np.float32) - 0.5) * 2 * 447.0])
+    ours = orc.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_quant_rows_amax_maps_to_max_code():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 256)).astype(np.float32)
+    q, s = orc.quant_e4m3_rows(x)
+    v = orc.e4m3_decode(q)
+    for r in range(5):
+        for b in range(2):
+            blk = x[r, b * 128:(b + 1) * 128]
+            j = np.argmax(np.abs(blk))
+            assert abs(v[r, b * 128 + j]) == 448.0
+            assert s[r, b] == np.float32(np.abs(blk).max() / np.float32(448.0))
+    # all-zero block
+    q0, s0 = orc.quant_e4m3_rows(np.zeros((1, 128), np.float32))
+    assert (q0 == 0).all() and s0[0, 0] == 1.0
+    # dequantised error within half an e4m3 step (relative 2^-4) of each value's scale
+    deq = orc.dequant_e4m3_rows(q, s)
+    assert np.all(np.abs(deq - x) <= np.repeat(s, 128, axis=1) * 448 * 2 ** -4 + 1e-30)
+    qi, si = orc.quant_int8_rows(x)
+    assert np.all(np.abs(qi).max(axis=1) == 127)
+    ri = orc.quant_int8_rows(np.array([[127.0, 0.5, 1.5, 2.5, -2.5]], np.float32))[0]
+    assert ri.tolist() == [[127, 0, 2, 2, -2]]  # ties to even with scale 1
+
+
+def test_quant_blocks_tile_amax():
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((256, 384)).astype(np.float32)
+    q, s = orc.quant_e4m3_blocks(w)
+    assert s.shape == (2, 3)
+    for i in range(2):
+        for j in range(3):
+            t = w[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            assert s[i, j] == np.float32(np.abs(t).max() / np.float32(448.0))
+    d = orc.dequant_e4m3_blocks(q, s)
+    assert np.abs(d - w).max() <= s.max() * 448 * 2 ** -4
+
+
+# ============================================================================ routing
+
+
+@pytest.mark.parametrize("case", ["single_operator", "graph_mode"])
+def test_route_page2_examples(case):
+    g = _gold()[case]
+    idx = np.array(g["topk_idx"], np.int32)
+    r = orc.route(idx, g["num_experts"], g["zero_expert_num"], g["copy_expert_num"], g["const_expert_num"])
+    assert r.err == 0
+    assert r.counts.tolist() == g["hand_counts"]
+    assert r.A == g["hand_routed_slots"]
+    assert r.ep_recv_counts.tolist() == np.cumsum(g["hand_counts"]).tolist()
+    codes = r.slot2row.reshape(idx.shape)
+    assert int((codes == -2).sum()) == g["hand_copy_slots"]
+    for t, k in g.get("hand_copy_slot_positions", []):
+        assert codes[t, k] == -2
+    for t, k in g.get("hand_zero_slot_positions", []):
+        assert codes[t, k] == -1
+    assert int((codes >= 0).sum()) == g["hand_routed_slots"]
+
+
+def _rand_route(T, K, E, Z=0, C=0, Q=0, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.permutation(E + Z + C + Q)[:K] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("T,K,E", [(1, 1, 1), (7, 3, 5), (64, 8, 64), (300, 2, 8), (33, 16, 16)])
+def test_route_counts_and_stable_permutation(T, K, E):
+    idx = _rand_route(T, K, E, seed=T * 7 + K)
+    r = orc.route(idx, E)
+    assert r.err == 0
+    assert r.counts.sum() == T * K                     # no mask, no special experts
+    assert r.counts.tolist() == np.bincount(idx.reshape(-1), minlength=E).tolist()
+    assert r.ep_recv_counts[-1] == r.A
+    ref_rows = np.argsort(idx.reshape(-1), kind="stable")  # library stable sort
+    assert np.array_equal(r.row2slot, ref_rows)
+    assert np.array_equal(r.slot2row[r.row2slot], np.arange(r.A))
+    assert sorted(r.slot2row.tolist()) == list(range(T * K))  # bijection
+
+
+def test_route_masks_and_specials():
+    T, K, E, Z, C, Q = 50, 6, 10, 2, 1, 3
+    idx = _rand_route(T, K, E, Z, C, Q, seed=5)
+    rng = np.random.default_rng(6)
+    m2 = (rng.random((T, K)) > 0.3).astype(np.uint8)
+    r = orc.route(idx, E, Z, C, Q, m2)
+    codes = r.slot2row.reshape(T, K)
+    act = m2.astype(bool)
+    routed = act & (idx < E)
+    assert np.array_equal(codes >= 0, routed)
+    assert np.all(codes[~act] == -1)
+    assert np.all(codes[act & (idx >= E) & (idx < E + Z)] == -1)
+    assert np.all(codes[act & (idx >= E + Z) & (idx < E + Z + C)] == -2)
+    cj = act & (idx >= E + Z + C)
+    assert np.array_equal(-codes[cj] - 3, idx[cj] - (E + Z + C))
+    inactive, special = int((~act).sum()), int((act & (idx >= E)).sum())
+    assert r.counts.sum() + inactive + special == T * K
+    # 1-D prefix mask: the first 20 tokens participate
+    m1 = np.zeros(T, np.uint8)
+    m1[:20] = 1
+    r1 = orc.route(idx, E, Z, C, Q, m1)
+    assert r1.err == 0
+    assert np.all(r1.slot2row.reshape(T, K)[20:] == -1)
+
+
+def test_route_errors():
+    idx = np.array([[0, 1], [2, 2], [5, 0]], np.int32)
+    r = orc.route(idx, 3)
+    assert r.err & orc.ERR_ID_RANGE and r.err & orc.ERR_ID_DUPLICATE
+    codes = r.slot2row.reshape(3, 2)
+    assert codes[1, 0] >= 0 and codes[1, 1] == -1    # later duplicate dropped
+    assert codes[2, 0] == -1                         # out-of-range dropped
+    assert r.A == 4
+    r2 = orc.route(np.array([[0], [1], [2]], np.int32), 3, mask=np.array([1, 0, 1], np.uint8))
+    assert r2.err == orc.ERR_MASK_NOT_PREFIX
+    assert orc.route(np.array([[0], [1], [2]], np.int32), 3, mask=np.array([1, 1, 0], np.uint8)).err == 0
+
+
+def test_dispatch_rows_are_token_copies():
+    inp = wl.layer_inputs(40, 16, 8, 6, 3, seed=3, weights=False, grad=False)
+    r = orc.route(inp["topk_idx"], 6)
+    X = orc.dispatch(inp["x"], r)
+    xf = orc.bf16_to_f32(inp["x"])
+    for s in range(40 * 3):
+        assert np.array_equal(X[r.slot2row[s]], xf[s // 3])
+
+
+# ============================================================================ combine
+
+
+@pytest.mark.parametrize("K", [2, 3, 8, 16])
+def test_round_trip_unit_weights_is_k_times_x(K):
+    """combine(dispatch(x)) with w = 1 and the FFN bypassed is K*x, bit for bit."""
+    T, H, E = 37, 24, 16
+    inp = wl.layer_inputs(T, H, 8, E, K, seed=K, weights=False, grad=False)
+    r = orc.route(inp["topk_idx"], E)
+    X = orc.dispatch(inp["x"], r)
+    out = orc.combine(X, r, np.ones((T, K), np.float32))
+    kx = orc.bf16_to_f32(inp["x"]) * np.float32(K)            # exact in fp32 for K <= 16
+    ref = torch.from_numpy(kx).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(out, ref)
+
+
+def _special_setup(T=9, H=12, K=4, seed=0):
+    rng = np.random.default_rng(seed)
+    d = dict(ori=rng.standard_normal((T, H)), shared=rng.standard_normal((T, H)),
+             a1=rng.standard_normal((2, H)), a2=rng.standard_normal((2, H)), v=rng.standard_normal((2, H)),
+             w=rng.standard_normal((T, K)))
+    return d
+
+
+def test_combine_closed_forms_special_experts():
+    T, H, K, E, Z, C, Q = 9, 12, 4, 5, 4, 4, 2
+    d = _special_setup(T, H, K)
+    Y = np.zeros((0, H))
+    # all zero experts -> shared
+    idx = np.tile(np.arange(E, E + 4), (T, 1)).astype(np.int32)
+    r = orc.route(idx, E, Z, C, Q)
+    out = orc.combine(Y, r, d["w"], d["shared"], d["ori"], d["a1"], d["a2"], d["v"], prec="f64")
+    assert np.allclose(out, d["shared"], rtol=0, atol=1e-14)
+    out0 = orc.combine(Y, r, d["w"], None, d["ori"], prec="f64")
+    assert np.all(out0 == 0)
+    # all copy experts -> (sum_k w) * ori_x + shared
+    idx = np.tile(np.arange(E + Z, E + Z + 4), (T, 1)).astype(np.int32)
+    r = orc.route(idx, E, Z, C, Q)
+    out = orc.combine(Y, r, d["w"], d["shared"], d["ori"], d["a1"], d["a2"], d["v"], prec="f64")
+    assert np.allclose(out, d["w"].sum(1)[:, None] * d["ori"] + d["shared"], atol=1e-12)
+    # constant experts (two of them in slots 0, 1; slots 2, 3 masked off)
+    idx = np.tile(np.array([E + Z + C, E + Z + C + 1, 0, 1]), (T, 1)).astype(np.int32)
+    m = np.tile(np.array([1, 1, 0, 0], np.uint8), (T, 1))
+    r = orc.route(idx, E, Z, C, Q, m)
+    out = orc.combine(np.zeros((r.A, H)), r, d["w"], None, d["ori"], d["a1"], d["a2"], d["v"], prec="f64")
+    ref = sum(d["w"][:, j:j + 1] * (d["a1"][j] * d["ori"] + d["a2"][j] * d["v"][j]) for j in range(2))
+    assert np.allclose(out, ref, atol=1e-12)
+
+
+def test_combine_is_linear_in_weights_and_masked_tokens_get_shared_only():
+    T, H, K, E = 10, 8, 3, 6
+    rng = np.random.default_rng(4)
+    idx = _rand_route(T, K, E, seed=9)
+    m = np.ones((T, K), np.uint8)
+    m[3] = 0
+    r = orc.route(idx, E, mask=m)
+    Y = rng.standard_normal((r.A, H))
+    sh = rng.standard_normal((T, H))
+    w1, w2 = rng.standard_normal((T, K)), rng.standard_normal((T, K))
+    f = lambda w: orc.combine(Y, r, w, None, prec="f64")
+    assert np.allclose(f(2 * w1 - 3 * w2), 2 * f(w1) - 3 * f(w2), atol=1e-12)
+    out = orc.combine(Y, r, w1, sh, prec="f64")
+    assert np.array_equal(out[3], sh[3])
+
+
+# ============================================================================ expert FFN
+
+
+def _torch_swiglu(x, wg, wu, wd):
+    """Dense SwiGLU FFN of one expert, from torch's own silu and matmul (float64)."""
+    x, wg, wu, wd = (torch.from_numpy(np.asarray(a, np.float64)) for a in (x, wg, wu, wd))
+    return (torch.nn.functional.silu(x @ wg.T) * (x @ wu.T) @ wd.T).numpy()
+
+
+def test_one_hot_weights_reproduce_single_expert():
+    T, H, F, E, K = 24, 32, 16, 5, 3
+    inp = wl.layer_inputs(T, H, F, E, K, seed=11, grad=False)
+    xf = orc.bf16_to_f32(inp["x"]).astype(np.float64)
+    wg, wu, wd = (orc.bf16_to_f32(inp[n]).astype(np.float64) for n in ("w_gate", "w_up", "w_down"))
+    for k0 in range(K):
+        w = np.zeros((T, K), np.float32)
+        w[:, k0] = 1.0
+        inp2 = dict(inp, topk_weights=w)
+        out = orc.layer_fwd(inp2, prec="f64")["out"]
+        ref = np.stack([_torch_swiglu(xf[t:t + 1], wg[e], wu[e], wd[e])[0]
+                        for t, e in enumerate(inp["topk_idx"][:, k0])])
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+        out32 = orc.layer_fwd(inp2, prec="def")["out"]
+        assert np.allclose(out32, ref, rtol=1e-4, atol=1e-5)
+    assert orc.silu(np.float64(0.0)) == 0.0
+
+
+def test_parity_mode_outputs_are_bf16_values():
+    inp = wl.layer_inputs(32, 16, 8, 4, 2, seed=12)
+    f = orc.layer_fwd(inp, prec="parity")
+    b = orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
+    for a in (f["out"], f["Y"], f["Hh"], f["G"], f["U"], b["dY"], b["dGU"], b["dX"], b["dx"]):
+        assert np.array_equal(a, orc.round_bf16(a))
+    # and they agree with the unrounded definition to bf16 accuracy
+    fd = orc.layer_fwd(inp, prec="def")
+    assert np.abs(f["out"] - fd["out"]).max() < 2e-2
+
+
+# ============================================================================ gradients
+
+
+def _fd_problem(seed=0, shared_ffn=False):
+    T, H, F, E, K, Z, C, Q = 4, 8, 4, 3, 2, 1, 1, 1
+    rng = np.random.default_rng(seed)
+    idx = np.array([[0, 1], [2, 3], [4, 5], [1, 0]], np.int32)   # routed, zero, copy, const
+    m = np.array([[1, 1], [1, 1], [1, 1], [1, 0]], np.uint8)
+    inp = dict(T=T, H=H, F=F, E=E, K=K, Z=Z, C=C, Q=Q, topk_idx=idx, mask=m,
+               x=rng.standard_normal((T, H)), topk_weights=rng.standard_normal((T, K)),
+               w_gate=rng.standard_normal((E, F, H)) * 0.5, w_up=rng.standard_normal((E, F, H)) * 0.5,
+               w_down=rng.standard_normal((E, H, F)) * 0.5,
+               const_alpha_1=rng.standard_normal((Q, H)), const_alpha_2=rng.standard_normal((Q, H)),
+               const_v=rng.standard_normal((Q, H)))
+    if shared_ffn:
+        inp.update(shared_w_gate=rng.standard_normal((1, F, H)) * 0.5,
+                   shared_w_up=rng.standard_normal((1, F, H)) * 0.5,
+                   shared_w_down=rng.standard_normal((1, H, F)) * 0.5)
+    else:
+        inp["shared_expert_x"] = rng.standard_normal((T, H))
+    g = rng.standard_normal((T, H))
+    return inp, g
+
+
+def _loss(inp, g):
+    return float(np.sum(orc.layer_fwd(inp, prec="f64")["out"] * g))
+
+
+@pytest.mark.parametrize("shared_ffn", [False, True])
+def test_backward_matches_finite_differences(shared_ffn):
+    inp, g = _fd_problem(shared_ffn=shared_ffn)
+    f = orc.layer_fwd(inp, prec="f64")
+    b = orc.layer_bwd(inp, f, g, prec="f64")
+    grads = dict(x=b["dx"], topk_weights=b["dw"], w_gate=b["dWg"], w_up=b["dWu"], w_down=b["dWd"])
+    if shared_ffn:
+        grads.update(shared_w_gate=b["s_dWg"], shared_w_up=b["s_dWu"], shared_w_down=b["s_dWd"])
+    else:
+        grads["shared_expert_x"] = b["d_shared"]
+    h = 1e-6
+    for name, an in grads.items():
+        base = np.asarray(inp[name], np.float64)
+        num = np.zeros_like(base)
+        for i in np.ndindex(base.shape):
+            p, mnus = base.copy(), base.copy()
+            p[i] += h
+            mnus[i] -= h
+            num[i] = (_loss(dict(inp, **{name: p}), g) - _loss(dict(inp, **{name: mnus}), g)) / (2 * h)
+        scale = max(1.0, np.abs(num).max())
+        assert np.abs(num - an).max() <= 1e-6 * scale, name
+    # masked slot (token 3, k=1) has no weight gradient, the zero-expert slot neither
+    assert b["dw"][3, 1] == 0 and b["dw"][1, 1] == 0
+
+
+def test_fp32_backward_close_to_f64():
+    inp, g = _fd_problem(seed=3)
+    inp32 = {k: (np.asarray(v, np.float32) if isinstance(v, np.ndarray) and v.dtype == np.float64 else v)
+             for k, v in inp.items()}
+    f64 = orc.layer_bwd(inp, orc.layer_fwd(inp, prec="f64"), g, prec="f64")
+    f32 = orc.layer_bwd(inp32, orc.layer_fwd(inp32, prec="def"), g.astype(np.float32), prec="def")
+    for k in ("dx", "dw", "dWg", "dWu", "dWd"):
+        scale = max(1.0, np.abs(f64[k]).max())
+        assert np.abs(f64[k] - f32[k]).max() <= 1e-5 * scale, k
