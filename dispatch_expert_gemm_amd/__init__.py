@@ -1,0 +1,345 @@
+"""Python binding of libmoe.so, the one-device MoE layer library for MI355X (gfx950).
+
+The functions below carry the names of the C entry points in include/moe.h and
+only marshal arguments: every step of the layer runs in the library's HIP
+kernels, on torch's current stream.  torch provides device memory and streams.
+There is no fallback: if libmoe.so is missing, or a tensor is not a contiguous
+GPU tensor of the right dtype, the call raises.
+
+``moe_layer`` wraps the whole forward and backward in a torch.autograd.Function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmoe.so")
+
+MOE_FLAG_ID_RANGE = 1
+MOE_FLAG_ID_DUPLICATE = 2
+MOE_FLAG_MASK_NOT_PREFIX = 4
+MOE_SLOT_NONE = -1
+MOE_SLOT_COPY = -2
+
+# every function include/moe.h declares
+ENTRY_POINTS = (
+    "moe_status_str", "moe_assist_info_size", "moe_workspace_size", "moe_dispatch",
+    "moe_grouped_ffn", "moe_ffn_gate_up_fwd", "moe_ffn_down_fwd", "moe_combine",
+    "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_ffn_down_bwd_data", "moe_ffn_down_bwd_weight",
+    "moe_ffn_gate_up_bwd_data", "moe_ffn_gate_up_bwd_weight", "moe_dispatch_bwd",
+)
+
+
+class MoeShape(ctypes.Structure):
+    """Mirror of struct moe_shape."""
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("F", ctypes.c_int64),
+                ("capacity", ctypes.c_int64), ("K", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("zero_expert_num", ctypes.c_int32),
+                ("copy_expert_num", ctypes.c_int32), ("const_expert_num", ctypes.c_int32),
+                ("mask_ndim", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def make_shape(T, H, K, num_experts, F=0, capacity=None, zero_expert_num=0, copy_expert_num=0,
+               const_expert_num=0, mask_ndim=0) -> MoeShape:
+    if capacity is None:
+        capacity = T * min(num_experts, K)
+    return MoeShape(T, H, F, capacity, K, num_experts, zero_expert_num, copy_expert_num,
+                    const_expert_num, mask_ndim, 0, 0)
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built by dispatch_expert_gemm_amd.build) once."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is missing: run `python -m dispatch_expert_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64P, S = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(MoeShape)
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [ctypes.c_int32]
+        L.moe_assist_info_size.argtypes = [S, I64P]
+        L.moe_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_grouped_ffn.argtypes = [S, P, P, P, P, P, P, P, P, P]
+        L.moe_ffn_gate_up_fwd.argtypes = [S, P, P, P, P, P, P, P]
+        L.moe_ffn_down_fwd.argtypes = [S, P, P, P, P, P]
+        L.moe_combine.argtypes = [S] + [P] * 13
+        L.moe_combine_bwd.argtypes = [S] + [P] * 14
+        L.moe_grouped_ffn_bwd.argtypes = [S] + [P] * 14
+        L.moe_ffn_down_bwd_data.argtypes = [S, P, P, P, P, P, P]
+        L.moe_ffn_down_bwd_weight.argtypes = [S, P, P, P, P, P]
+        L.moe_ffn_gate_up_bwd_data.argtypes = [S, P, P, P, P, P, P]
+        L.moe_ffn_gate_up_bwd_weight.argtypes = [S, P, P, P, P, P, P]
+        L.moe_dispatch_bwd.argtypes = [S] + [P] * 10
+        for name in ENTRY_POINTS:
+            if name != "moe_status_str":
+                getattr(L, name).restype = ctypes.c_int32
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(st: int):
+    if st != 0:
+        raise MoeError(f"libmoe status {st}: {lib().moe_status_str(st).decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+BF16, I32, F32, U8 = torch.bfloat16, torch.int32, torch.float32, (torch.uint8, torch.bool)
+
+# ----------------------------------------------------------------------------- C entries
+
+
+def moe_assist_info_size(shape: MoeShape) -> int:
+    n = ctypes.c_int64()
+    _check(lib().moe_assist_info_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def moe_workspace_size(shape: MoeShape) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def moe_dispatch(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_combine,
+                 expert_token_nums, ep_recv_counts, err_flag, workspace, stream=None):
+    _check(lib().moe_dispatch(
+        ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(x_active_mask, U8, "x_active_mask"), _ptr(expand_x, BF16, "expand_x"),
+        _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
+        _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(err_flag, I32, "err_flag"), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_grouped_ffn(shape, expand_x, w_gate, w_up, w_down, ep_recv_counts, gate_up_save, h_act, y,
+                    stream=None):
+    _check(lib().moe_grouped_ffn(
+        ctypes.byref(shape), _ptr(expand_x, BF16, "expand_x"), _ptr(w_gate, BF16, "w_gate"),
+        _ptr(w_up, BF16, "w_up"), _ptr(w_down, BF16, "w_down"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(h_act, BF16, "h_act"), _ptr(y, BF16, "y"),
+        _stream(stream)))
+
+
+def moe_ffn_gate_up_fwd(shape, expand_x, w_gate, w_up, ep_recv_counts, gate_up_save, h_act, stream=None):
+    _check(lib().moe_ffn_gate_up_fwd(
+        ctypes.byref(shape), _ptr(expand_x, BF16, "expand_x"), _ptr(w_gate, BF16, "w_gate"),
+        _ptr(w_up, BF16, "w_up"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(h_act, BF16, "h_act"), _stream(stream)))
+
+
+def moe_ffn_down_fwd(shape, h_act, w_down, ep_recv_counts, y, stream=None):
+    _check(lib().moe_ffn_down_fwd(
+        ctypes.byref(shape), _ptr(h_act, BF16, "h_act"), _ptr(w_down, BF16, "w_down"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"), _stream(stream)))
+
+
+def moe_combine(shape, y, topk_idx, topk_weights, assist_info_for_combine, ep_send_counts,
+                x_active_mask, shared_expert_x, ori_x, const_alpha_1, const_alpha_2, const_v, out,
+                stream=None):
+    _check(lib().moe_combine(
+        ctypes.byref(shape), _ptr(y, BF16, "y"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(topk_weights, F32, "topk_weights"), _ptr(assist_info_for_combine, I32, "assist"),
+        _ptr(ep_send_counts, I32, "ep_send_counts"), _ptr(x_active_mask, U8, "x_active_mask"),
+        _ptr(shared_expert_x, BF16, "shared_expert_x"), _ptr(ori_x, BF16, "ori_x"),
+        _ptr(const_alpha_1, BF16, "const_alpha_1"), _ptr(const_alpha_2, BF16, "const_alpha_2"),
+        _ptr(const_v, BF16, "const_v"), _ptr(out, BF16, "out"), _stream(stream)))
+
+
+def moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_combine,
+                    ep_send_counts, x_active_mask, ori_x, const_alpha_1, const_alpha_2, const_v,
+                    grad_y, grad_topk_weights, stream=None):
+    _check(lib().moe_combine_bwd(
+        ctypes.byref(shape), _ptr(grad_out, BF16, "grad_out"), _ptr(y, BF16, "y"),
+        _ptr(topk_idx, I32, "topk_idx"), _ptr(topk_weights, F32, "topk_weights"),
+        _ptr(assist_info_for_combine, I32, "assist"), _ptr(ep_send_counts, I32, "ep_send_counts"),
+        _ptr(x_active_mask, U8, "x_active_mask"), _ptr(ori_x, BF16, "ori_x"),
+        _ptr(const_alpha_1, BF16, "const_alpha_1"), _ptr(const_alpha_2, BF16, "const_alpha_2"),
+        _ptr(const_v, BF16, "const_v"), _ptr(grad_y, BF16, "grad_y"),
+        _ptr(grad_topk_weights, F32, "grad_topk_weights"), _stream(stream)))
+
+
+def moe_grouped_ffn_bwd(shape, grad_y, expand_x, gate_up_save, h_act, w_gate, w_up, w_down,
+                        ep_recv_counts, grad_gate_up, grad_expand_x, grad_w_gate, grad_w_up,
+                        grad_w_down, stream=None):
+    _check(lib().moe_grouped_ffn_bwd(
+        ctypes.byref(shape), _ptr(grad_y, BF16, "grad_y"), _ptr(expand_x, BF16, "expand_x"),
+        _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(h_act, BF16, "h_act"),
+        _ptr(w_gate, BF16, "w_gate"), _ptr(w_up, BF16, "w_up"), _ptr(w_down, BF16, "w_down"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_gate_up, BF16, "grad_gate_up"),
+        _ptr(grad_expand_x, BF16, "grad_expand_x"), _ptr(grad_w_gate, F32, "grad_w_gate"),
+        _ptr(grad_w_up, F32, "grad_w_up"), _ptr(grad_w_down, F32, "grad_w_down"), _stream(stream)))
+
+
+def moe_ffn_down_bwd_data(shape, grad_y, w_down, gate_up_save, ep_recv_counts, grad_gate_up,
+                          stream=None):
+    _check(lib().moe_ffn_down_bwd_data(
+        ctypes.byref(shape), _ptr(grad_y, BF16, "grad_y"), _ptr(w_down, BF16, "w_down"),
+        _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(grad_gate_up, BF16, "grad_gate_up"), _stream(stream)))
+
+
+def moe_ffn_down_bwd_weight(shape, grad_y, h_act, ep_recv_counts, grad_w_down, stream=None):
+    _check(lib().moe_ffn_down_bwd_weight(
+        ctypes.byref(shape), _ptr(grad_y, BF16, "grad_y"), _ptr(h_act, BF16, "h_act"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_w_down, F32, "grad_w_down"),
+        _stream(stream)))
+
+
+def moe_ffn_gate_up_bwd_data(shape, grad_gate_up, w_gate, w_up, ep_recv_counts, grad_expand_x,
+                             stream=None):
+    _check(lib().moe_ffn_gate_up_bwd_data(
+        ctypes.byref(shape), _ptr(grad_gate_up, BF16, "grad_gate_up"), _ptr(w_gate, BF16, "w_gate"),
+        _ptr(w_up, BF16, "w_up"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(grad_expand_x, BF16, "grad_expand_x"), _stream(stream)))
+
+
+def moe_ffn_gate_up_bwd_weight(shape, grad_gate_up, expand_x, ep_recv_counts, grad_w_gate,
+                               grad_w_up, stream=None):
+    _check(lib().moe_ffn_gate_up_bwd_weight(
+        ctypes.byref(shape), _ptr(grad_gate_up, BF16, "grad_gate_up"), _ptr(expand_x, BF16, "expand_x"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_w_gate, F32, "grad_w_gate"),
+        _ptr(grad_w_up, F32, "grad_w_up"), _stream(stream)))
+
+
+def moe_dispatch_bwd(shape, grad_expand_x, assist_info_for_combine, topk_idx, topk_weights,
+                     x_active_mask, grad_out, const_alpha_1, grad_x_accum, grad_x, stream=None):
+    _check(lib().moe_dispatch_bwd(
+        ctypes.byref(shape), _ptr(grad_expand_x, BF16, "grad_expand_x"),
+        _ptr(assist_info_for_combine, I32, "assist"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(topk_weights, F32, "topk_weights"), _ptr(x_active_mask, U8, "x_active_mask"),
+        _ptr(grad_out, BF16, "grad_out"), _ptr(const_alpha_1, BF16, "const_alpha_1"),
+        _ptr(grad_x_accum, BF16, "grad_x_accum"), _ptr(grad_x, BF16, "grad_x"), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- buffers + layer
+
+
+@dataclass
+class DispatchOut:
+    expand_x: torch.Tensor
+    assist_info_for_combine: torch.Tensor
+    expert_token_nums: torch.Tensor
+    ep_recv_counts: torch.Tensor
+    err_flag: torch.Tensor
+
+    def slot2row(self, T, K):
+        return self.assist_info_for_combine[:T * K]
+
+    def row2slot(self, T, K):
+        return self.assist_info_for_combine[T * K:]
+
+
+def dispatch(shape, x, topk_idx, x_active_mask=None, workspace=None, stream=None) -> DispatchOut:
+    """Allocate the dispatch outputs with torch and run moe_dispatch."""
+    dev = x.device
+    d = DispatchOut(
+        expand_x=torch.empty((shape.capacity, shape.H), dtype=BF16, device=dev),
+        assist_info_for_combine=torch.empty(moe_assist_info_size(shape), dtype=I32, device=dev),
+        expert_token_nums=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        ep_recv_counts=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        err_flag=torch.empty(1, dtype=I32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    mask = x_active_mask.view(torch.uint8) if x_active_mask is not None and x_active_mask.dtype == torch.bool \
+        else x_active_mask
+    moe_dispatch(shape, x, topk_idx, mask, d.expand_x, d.assist_info_for_combine,
+                 d.expert_token_nums, d.ep_recv_counts, d.err_flag, workspace, stream)
+    return d
+
+
+class _MoELayerFn(torch.autograd.Function):
+    """Forward: dispatch -> grouped SwiGLU FFN -> combine; backward: the reverse chain."""
+
+    @staticmethod
+    def forward(ctx, x, topk_weights, w_gate, w_up, w_down, shared_expert_x, topk_idx, x_active_mask,
+                const_alpha_1, const_alpha_2, const_v, zero_expert_num, copy_expert_num,
+                const_expert_num):
+        T, H = x.shape
+        K = topk_idx.shape[1]
+        E, F, _ = w_gate.shape
+        mask_ndim = 0 if x_active_mask is None else x_active_mask.dim()
+        shape = make_shape(T, H, K, E, F=F, zero_expert_num=zero_expert_num,
+                           copy_expert_num=copy_expert_num, const_expert_num=const_expert_num,
+                           mask_ndim=mask_ndim)
+        mask = None if x_active_mask is None else x_active_mask.view(torch.uint8)
+        d = dispatch(shape, x, topk_idx, mask)
+        cap = shape.capacity
+        gus = torch.empty((cap, 2 * F), dtype=BF16, device=x.device)
+        h = torch.empty((cap, F), dtype=BF16, device=x.device)
+        y = torch.empty((cap, H), dtype=BF16, device=x.device)
+        moe_grouped_ffn(shape, d.expand_x, w_gate, w_up, w_down, d.ep_recv_counts, gus, h, y)
+        out = torch.empty((T, H), dtype=BF16, device=x.device)
+        moe_combine(shape, y, topk_idx, topk_weights, d.assist_info_for_combine, d.ep_recv_counts,
+                    mask, shared_expert_x, x, const_alpha_1, const_alpha_2, const_v, out)
+        ctx.shape = shape
+        ctx.has_shared = shared_expert_x is not None
+        ctx.save_for_backward(x, topk_weights, w_gate, w_up, w_down, topk_idx, mask, const_alpha_1,
+                              const_alpha_2, const_v, d.expand_x, d.assist_info_for_combine,
+                              d.ep_recv_counts, gus, h, y)
+        return out
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (x, topk_weights, w_gate, w_up, w_down, topk_idx, mask, a1, a2, cv, expand_x, assist,
+         recv, gus, h, y) = ctx.saved_tensors
+        shape = ctx.shape
+        grad_out = grad_out.contiguous()
+        cap, H, F, T, K = shape.capacity, shape.H, shape.F, shape.T, shape.K
+        dev = x.device
+        gy = torch.empty((cap, H), dtype=BF16, device=dev)
+        gw = torch.empty((T, K), dtype=F32, device=dev)
+        moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
+                        gy, gw)
+        ggu = torch.empty((cap, 2 * F), dtype=BF16, device=dev)
+        gx_exp = torch.empty((cap, H), dtype=BF16, device=dev)
+        gwg = torch.empty(w_gate.shape, dtype=F32, device=dev)
+        gwu = torch.empty(w_up.shape, dtype=F32, device=dev)
+        gwd = torch.empty(w_down.shape, dtype=F32, device=dev)
+        moe_grouped_ffn_bwd(shape, gy, expand_x, gus, h, w_gate, w_up, w_down, recv, ggu, gx_exp,
+                            gwg, gwu, gwd)
+        gx = torch.empty((T, H), dtype=BF16, device=dev)
+        moe_dispatch_bwd(shape, gx_exp, assist, topk_idx, topk_weights, mask, grad_out, a1, None, gx)
+        g_shared = grad_out if ctx.has_shared else None
+        return (gx, gw, gwg.to(w_gate.dtype), gwu.to(w_up.dtype), gwd.to(w_down.dtype), g_shared,
+                None, None, None, None, None, None, None, None)
+
+
+def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=None,
+              shared_expert_x=None, const_alpha_1=None, const_alpha_2=None, const_v=None,
+              zero_expert_num=0, copy_expert_num=0, const_expert_num=0):
+    """One MoE layer (ori_x is x itself).  Differentiable in x, topk_weights, the
+    expert weights and shared_expert_x.  Weight gradients are computed in fp32 and
+    returned in the weights' dtype; use the C entries directly to keep fp32."""
+    return _MoELayerFn.apply(x, topk_weights, w_gate, w_up, w_down, shared_expert_x, topk_idx,
+                             x_active_mask, const_alpha_1, const_alpha_2, const_v,
+                             zero_expert_num, copy_expert_num, const_expert_num)

@@ -1,0 +1,348 @@
+// Combine (forward and backward) and the gradient of dispatch: token-parallel,
+// HBM-bound gather-reduce kernels.
+//
+// Combine follows the low_latency_combine API page, "Function" (Formula and the
+// special-expert cases) and "Parameters" (topk_weights, shared_expert_x, ori_x,
+// const_expert_alpha_1/_2, const_expert_v, zero/copy/const id ranges):
+//   out[t] = sum_k w[t,k] * v(t,k) + shared_expert_x[t]
+// with v = y[row] (routed), 0 (zero expert or masked slot), ori_x[t] (copy),
+// alpha_1[j]*ori_x[t] + alpha_2[j]*v[j] (constant expert j).
+//
+// Layout: one 64-lane wave per token, four tokens per 256-thread block; each
+// lane owns 16-byte (8 x bf16) column vectors, so every row read or written by
+// a wave is a run of fully coalesced 1 KiB transactions.  The K slot codes and
+// weights of the token are read once by lanes 0..K-1 and broadcast with
+// readlane.  Sums run in k order with separately rounded products and adds (this
+// file is compiled without floating-point contraction), so results do not
+// depend on the launch shape and are bit-reproducible.
+#include "common.hpp"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kMaxK = 16;
+
+struct SlotInfo {
+  int code[kMaxK];
+  float w[kMaxK];
+  bool any_ori;
+};
+
+__device__ __forceinline__ void load_slots(const int32_t* slot2row, const float* w, int64_t t,
+                                           int K, int lane, SlotInfo& si) {
+  const int my = lane < K ? slot2row[t * K + lane] : MOE_SLOT_NONE;
+  const float mw = lane < K ? w[t * K + lane] : 0.f;
+  bool any = false;
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) {
+    si.code[k] = k < K ? __builtin_amdgcn_readlane(my, k) : MOE_SLOT_NONE;
+    si.w[k] = k < K ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), k)) : 0.f;
+    any |= si.code[k] <= MOE_SLOT_COPY;
+  }
+  si.any_ori = any;
+}
+
+// Value of a copy or constant slot for one 8-column vector.
+__device__ __forceinline__ void special_value(int code, const float* ox, const uint4* a1,
+                                              const uint4* a2, const uint4* cv, int64_t Hv,
+                                              int64_t v, float* f) {
+  if (code == MOE_SLOT_COPY) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = ox[i];
+    return;
+  }
+  const int64_t j = -code - 3;
+  float p[8], q[8], c[8];
+  unpack8(a1[j * Hv + v], p);
+  unpack8(a2[j * Hv + v], q);
+  unpack8(cv[j * Hv + v], c);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = p[i] * ox[i] + q[i] * c[i];
+}
+
+struct CombineArgs {
+  const uint4* y;
+  const float* w;
+  const int32_t* slot2row;
+  const uint4* shared;
+  const uint4* ori;
+  const uint4* a1;
+  const uint4* a2;
+  const uint4* cv;
+  uint4* out;
+  int64_t T;
+  int K;
+  int64_t Hv;
+};
+
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (t >= a.T) return;
+  SlotInfo si;
+  load_slots(a.slot2row, a.w, t, a.K, lane, si);
+  const int64_t Hv = a.Hv;
+  for (int64_t v = lane; v < Hv; v += kWave) {
+    uint4 raw[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+      if (si.code[k] >= 0) raw[k] = a.y[(int64_t)si.code[k] * Hv + v];
+    float ox[8];
+    if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      const int c = si.code[k];
+      if (c == MOE_SLOT_NONE) continue;
+      float f[8];
+      if (c >= 0) unpack8(raw[k], f);
+      else special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+      const float wk = si.w[k];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + wk * f[i];
+    }
+    if (a.shared) {
+      float s[8];
+      unpack8(a.shared[t * Hv + v], s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + s[i];
+    }
+    a.out[t * Hv + v] = pack8(acc);
+  }
+}
+
+struct CombineBwdArgs {
+  const uint4* dout;
+  const uint4* y;
+  const float* w;
+  const int32_t* slot2row;
+  const uint4* ori;
+  const uint4* a1;
+  const uint4* a2;
+  const uint4* cv;
+  uint4* dy;
+  float* dw;
+  int64_t T;
+  int K;
+  int64_t Hv;
+};
+
+__global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (t >= a.T) return;
+  SlotInfo si;
+  load_slots(a.slot2row, a.w, t, a.K, lane, si);
+  const int64_t Hv = a.Hv;
+  float dot[kMaxK];
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) dot[k] = 0.f;
+  for (int64_t v = lane; v < Hv; v += kWave) {
+    float d[8];
+    unpack8(a.dout[t * Hv + v], d);
+    uint4 raw[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+      if (si.code[k] >= 0) raw[k] = a.y[(int64_t)si.code[k] * Hv + v];
+    float ox[8];
+    if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      const int c = si.code[k];
+      if (c == MOE_SLOT_NONE) continue;
+      float f[8];
+      if (c >= 0) unpack8(raw[k], f);
+      else special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+      float p = dot[k];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p = p + f[i] * d[i];
+      dot[k] = p;
+      if (c >= 0) {
+        float g[8];
+        const float wk = si.w[k];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] = wk * d[i];
+        a.dy[(int64_t)c * Hv + v] = pack8(g);
+      }
+    }
+  }
+  // fixed-shape butterfly over the wave: the same order for every launch
+#pragma unroll
+  for (int k = 0; k < kMaxK; ++k) {
+    if (k < a.K) {
+      float p = dot[k];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) p = p + __shfl_xor(p, o, kWave);
+      if (lane == 0) a.dw[t * a.K + k] = (si.code[k] == MOE_SLOT_NONE) ? 0.f : p;
+    }
+  }
+}
+
+struct DispatchBwdArgs {
+  const uint4* dx_exp;
+  const int32_t* slot2row;
+  const float* w;
+  const uint4* dout;
+  const uint4* a1;
+  const uint4* accum;
+  uint4* dx;
+  int64_t T;
+  int K;
+  int64_t Hv;
+};
+
+__global__ __launch_bounds__(256) void k_dispatch_bwd(DispatchBwdArgs a) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (t >= a.T) return;
+  SlotInfo si;
+  load_slots(a.slot2row, a.w, t, a.K, lane, si);
+  const int64_t Hv = a.Hv;
+  for (int64_t v = lane; v < Hv; v += kWave) {
+    uint4 raw[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+      if (si.code[k] >= 0) raw[k] = a.dx_exp[(int64_t)si.code[k] * Hv + v];
+    float d[8];
+    if (si.any_ori) unpack8(a.dout[t * Hv + v], d);
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+      const int c = si.code[k];
+      if (c == MOE_SLOT_NONE) continue;
+      float f[8];
+      if (c >= 0) {
+        unpack8(raw[k], f);
+      } else if (c == MOE_SLOT_COPY) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = si.w[k] * d[i];
+      } else {
+        float p[8];
+        unpack8(a.a1[(int64_t)(-c - 3) * Hv + v], p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = si.w[k] * (p[i] * d[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + f[i];
+    }
+    if (a.accum) {
+      float s[8];
+      unpack8(a.accum[t * Hv + v], s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + s[i];
+    }
+    a.dx[t * Hv + v] = pack8(acc);
+  }
+}
+
+inline dim3 token_grid(int64_t T) {
+  return dim3((unsigned)((T + kWavesPerBlock - 1) / kWavesPerBlock));
+}
+
+// Pointers needed by the special experts (Parameters: ori_x required when
+// copy_expert_num or const_expert_num is not 0; the const tensors when
+// const_expert_num is not 0).
+inline moe_status check_special(const moe_shape* s, const void* ori_x, const void* a1,
+                                const void* a2, const void* cv) {
+  if ((s->copy_expert_num > 0 || s->const_expert_num > 0) && !ori_x) return MOE_ERR_NULL_ARG;
+  if (s->const_expert_num > 0 && (!a1 || !a2 || !cv)) return MOE_ERR_NULL_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* topk_idx,
+                                  const float* topk_weights, const int32_t* assist,
+                                  const int32_t* ep_send_counts, const uint8_t* x_active_mask,
+                                  const void* shared_expert_x, const void* ori_x,
+                                  const void* const_alpha_1, const void* const_alpha_2,
+                                  const void* const_v, void* out, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  MOE_NEED(y, s->capacity * s->H);
+  if (!topk_idx || !topk_weights || !assist || !ep_send_counts || !out) return MOE_ERR_NULL_ARG;
+  if (s->mask_ndim > 0 && !x_active_mask) return MOE_ERR_NULL_ARG;
+  st = check_special(s, ori_x, const_alpha_1, const_alpha_2, const_v);
+  if (st != MOE_OK) return st;
+  CombineArgs a{static_cast<const uint4*>(y),     topk_weights,
+                assist,                            static_cast<const uint4*>(shared_expert_x),
+                static_cast<const uint4*>(ori_x), static_cast<const uint4*>(const_alpha_1),
+                static_cast<const uint4*>(const_alpha_2), static_cast<const uint4*>(const_v),
+                static_cast<uint4*>(out),          s->T,
+                s->K,                              s->H / 8};
+  hipLaunchKernelGGL(k_combine, token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, const void* y,
+                                      const int32_t* topk_idx, const float* topk_weights,
+                                      const int32_t* assist, const int32_t* ep_send_counts,
+                                      const uint8_t* x_active_mask, const void* ori_x,
+                                      const void* const_alpha_1, const void* const_alpha_2,
+                                      const void* const_v, void* grad_y, float* grad_topk_weights,
+                                      void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  MOE_NEED(y, s->capacity * s->H);
+  MOE_NEED(grad_y, s->capacity * s->H);
+  if (!grad_out || !topk_idx || !topk_weights || !assist || !ep_send_counts ||
+      !grad_topk_weights)
+    return MOE_ERR_NULL_ARG;
+  if (s->mask_ndim > 0 && !x_active_mask) return MOE_ERR_NULL_ARG;
+  st = check_special(s, ori_x, const_alpha_1, const_alpha_2, const_v);
+  if (st != MOE_OK) return st;
+  CombineBwdArgs a{static_cast<const uint4*>(grad_out),
+                   static_cast<const uint4*>(y),
+                   topk_weights,
+                   assist,
+                   static_cast<const uint4*>(ori_x),
+                   static_cast<const uint4*>(const_alpha_1),
+                   static_cast<const uint4*>(const_alpha_2),
+                   static_cast<const uint4*>(const_v),
+                   static_cast<uint4*>(grad_y),
+                   grad_topk_weights,
+                   s->T,
+                   s->K,
+                   s->H / 8};
+  hipLaunchKernelGGL(k_combine_bwd, token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,
+                                       const int32_t* assist, const int32_t* topk_idx,
+                                       const float* topk_weights, const uint8_t* x_active_mask,
+                                       const void* grad_out, const void* const_alpha_1,
+                                       const void* grad_x_accum, void* grad_x, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->T == 0) return MOE_OK;
+  MOE_NEED(grad_expand_x, s->capacity * s->H);
+  if (!assist || !topk_idx || !topk_weights || !grad_x) return MOE_ERR_NULL_ARG;
+  if (s->mask_ndim > 0 && !x_active_mask) return MOE_ERR_NULL_ARG;
+  if ((s->copy_expert_num > 0 || s->const_expert_num > 0) && !grad_out) return MOE_ERR_NULL_ARG;
+  if (s->const_expert_num > 0 && !const_alpha_1) return MOE_ERR_NULL_ARG;
+  DispatchBwdArgs a{static_cast<const uint4*>(grad_expand_x),
+                    assist,
+                    topk_weights,
+                    static_cast<const uint4*>(grad_out),
+                    static_cast<const uint4*>(const_alpha_1),
+                    static_cast<const uint4*>(grad_x_accum),
+                    static_cast<uint4*>(grad_x),
+                    s->T,
+                    s->K,
+                    s->H / 8};
+  hipLaunchKernelGGL(k_dispatch_bwd, token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+  return launch_status();
+}

@@ -1,0 +1,98 @@
+// Shared helpers of the libmoe HIP sources: bf16 storage conversions, vector
+// types, host-side argument validation and launch checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // storage of an IEEE bfloat16
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Exact widening of a bf16 bit pattern.
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Narrowing float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two floats -> one 32-bit word of two bf16 (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// Unpack the 8 bf16 of a 16-byte vector to floats.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint4 v;
+  v.x = pack_bf2(f[0], f[1]); v.y = pack_bf2(f[2], f[3]);
+  v.z = pack_bf2(f[4], f[5]); v.w = pack_bf2(f[6], f[7]);
+  return v;
+}
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------------------- host side
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int64_t e_total(const moe_shape* s) {
+  return (int64_t)s->num_experts + s->zero_expert_num + s->copy_expert_num + s->const_expert_num;
+}
+
+// Rules shared by every entry point (low_latency_combine page, Constraints:
+// 0 < K <= 16 and K <= E+Z+C+Q; num_experts in [1, 1024]; special expert counts
+// non-negative with a total below 2^31; A >= BS * min(local_expert_num, K)).
+inline moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_NULL_ARG;
+  if (s->reserved != 0) return MOE_ERR_BAD_RANGE;
+  if (s->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->mask_ndim < 0 || s->mask_ndim > 2) return MOE_ERR_BAD_RANGE;
+  if (s->T < 0 || s->H <= 0 || (s->H % 8) != 0) return MOE_ERR_BAD_SHAPE;
+  if (s->K < 1 || s->K > 16) return MOE_ERR_BAD_SHAPE;
+  if (s->num_experts < 1 || s->num_experts > 1024) return MOE_ERR_BAD_SHAPE;
+  if (s->zero_expert_num < 0 || s->copy_expert_num < 0 || s->const_expert_num < 0)
+    return MOE_ERR_BAD_SHAPE;
+  if (e_total(s) >= (int64_t)0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  if ((int64_t)s->K > e_total(s)) return MOE_ERR_BAD_SHAPE;
+  const int64_t need = s->T * (int64_t)(s->num_experts < s->K ? s->num_experts : s->K);
+  if (s->capacity < need) return MOE_ERR_CAPACITY;
+  if (s->capacity > (int64_t)0x7fffffff || s->T * (int64_t)s->K > (int64_t)0x7fffffff)
+    return MOE_ERR_BAD_SHAPE;
+  if (s->H > (int64_t)1 << 20) return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
+
+inline moe_status check_ffn_shape(const moe_shape* s) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->F <= 0 || (s->F % 32) != 0 || s->F > (int64_t)1 << 20) return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
+
+// A pointer may be NULL only when the tensor it stands for has no elements.
+#define MOE_NEED(p, n) \
+  do {                                          \
+    if (!(p) && (int64_t)(n) > 0) return MOE_ERR_NULL_ARG; \
+  } while (0)
+
+inline moe_status launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe

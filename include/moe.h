@@ -1,0 +1,255 @@
+/*
+ * moe.h - C ABI of the one-device MoE layer library (libmoe.so), gfx950 / MI355X.
+ *
+ * The layer is the dispatch -> expert FFN -> combine chain of the Ascend
+ * low_latency_dispatch / low_latency_combine pair (low_latency_combine API page:
+ * "Function" Description and Formula, "Prototype", "Parameters") with an
+ * expert-parallel world of one device, so the all-to-all becomes an on-device
+ * permutation, plus its backward.  Each expert's FFN is SwiGLU with
+ * intermediate size F (the --ffn_dim of the Triton-distributed ep_moe_fused
+ * benchmark page) and every expert's FFN runs as one grouped GEMM.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers to contiguous row-major memory
+ *   owned by the caller.  The library allocates nothing, keeps no state between
+ *   calls and never synchronises: every call only enqueues kernels on `stream`
+ *   (a hipStream_t; NULL means the null stream) and returns.
+ * - bf16 tensors are passed as `const void*` / `void*` (IEEE bfloat16, 2 bytes).
+ *   Indices are int32, masks uint8 (0 = false), weights and weight gradients
+ *   float32.
+ * - Notation: T tokens (BS), H hidden, F expert intermediate size, K top-k,
+ *   E = num_experts (routed experts), Z/C/Q = zero/copy/const expert counts,
+ *   slot s = t*K + k, A = number of active routed slots (= rows actually used in
+ *   the expanded buffers, known only on the device as ep_recv_counts[E-1]),
+ *   capacity = rows allocated for the expanded buffers.
+ * - Host-checkable rule violations return a negative moe_status before any
+ *   launch and leave every output untouched.  Data rules that only the device
+ *   can see (ids out of range, duplicate ids in a row, a 1-D mask that is not a
+ *   prefix) are reported through the err_flag output of moe_dispatch; outputs
+ *   are then unspecified but every kernel stays in bounds (offending slots are
+ *   treated as inactive).
+ * - Results are deterministic: no floating-point atomics anywhere (the page's
+ *   "Deterministic Computation" section).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+
+#define MOE_OK 0
+#define MOE_ERR_NULL_ARG (-1)    /* a required pointer is NULL */
+#define MOE_ERR_BAD_SHAPE (-2)   /* a size is out of range or misaligned */
+#define MOE_ERR_BAD_RANGE (-3)   /* an enum-like field has an unknown value */
+#define MOE_ERR_CAPACITY (-4)    /* capacity < T * min(E, K) */
+#define MOE_ERR_UNSUPPORTED (-5) /* valid but not implemented combination */
+#define MOE_ERR_WORKSPACE (-6)   /* workspace missing or too small */
+#define MOE_ERR_HIP (-7)         /* a HIP launch failed */
+
+/* err_flag bits written by moe_dispatch (device int32). */
+#define MOE_FLAG_ID_RANGE 1          /* topk_idx value outside [0, E+Z+C+Q) */
+#define MOE_FLAG_ID_DUPLICATE 2      /* the same id twice in one row of topk_idx */
+#define MOE_FLAG_MASK_NOT_PREFIX 4   /* 1-D x_active_mask with a true after a false */
+
+#define MOE_DTYPE_BF16 0
+
+/* Codes stored in the slot-to-row part of assist_info_for_combine. */
+#define MOE_SLOT_NONE (-1)  /* inactive slot, zero expert or invalid slot */
+#define MOE_SLOT_COPY (-2)  /* copy expert: the slot's value is ori_x[t] */
+/* constant expert j: code -(3 + j) */
+
+typedef struct moe_shape {
+  int64_t T;                /* tokens, >= 0 */
+  int64_t H;                /* hidden size, > 0, multiple of 8 */
+  int64_t F;                /* expert intermediate size, multiple of 32 (FFN calls only) */
+  int64_t capacity;         /* rows of expand_x / y / grad buffers, >= T*min(E,K) */
+  int32_t K;                /* top-k, 1..16 and <= E+Z+C+Q */
+  int32_t num_experts;      /* routed experts E, 1..1024 */
+  int32_t zero_expert_num;  /* Z >= 0: ids [E, E+Z) */
+  int32_t copy_expert_num;  /* C >= 0: ids [E+Z, E+Z+C) */
+  int32_t const_expert_num; /* Q >= 0: ids [E+Z+C, E+Z+C+Q) */
+  int32_t mask_ndim;        /* 0: no x_active_mask, 1: (T,), 2: (T, K) */
+  int32_t act_dtype;        /* MOE_DTYPE_BF16 */
+  int32_t reserved;         /* must be 0 */
+} moe_shape;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(moe_status st);
+
+/* Size of assist_info_for_combine in int32 elements: T*K (slot -> row) followed
+ * by capacity (row -> slot).  Its contents are opaque to callers, like the
+ * page's assist_info_for_combine (Parameters; Constraints: "pass it on"). */
+moe_status moe_assist_info_size(const moe_shape* s, int64_t* n_int32);
+
+/* Bytes of device workspace that moe_dispatch needs (for per-chunk expert
+ * histograms).  The FFN entries take no workspace. */
+moe_status moe_workspace_size(const moe_shape* s, size_t* bytes);
+
+/*
+ * moe_dispatch - route tokens to experts and build the expert-sorted buffer.
+ * (low_latency_combine page, Parameters: topk_idx, x_active_mask,
+ * assist_info_for_combine, ep_send_counts; with one device the dispatch
+ * all-to-all is the permutation below.)
+ *
+ *  in   x                 (T, H) bf16        tokens
+ *  in   topk_idx          (T, K) int32       expert id per slot
+ *  in   x_active_mask     (T,) or (T, K) uint8, or NULL when mask_ndim == 0
+ *  out  expand_x          (capacity, H) bf16 row r = x[token of row r]; rows >= A untouched
+ *  out  assist_info_for_combine  see moe_assist_info_size:
+ *                         slot2row[s] = row (>= 0) of an active routed slot,
+ *                         MOE_SLOT_NONE, MOE_SLOT_COPY or -(3+j) for const expert j;
+ *                         row2slot[r] = slot of row r (r < A)
+ *  out  expert_token_nums (E,) int32         active routed slots per expert
+ *  out  ep_recv_counts    (E,) int32         inclusive prefix sum of expert_token_nums
+ *  out  err_flag          (1,) int32         MOE_FLAG_* bits (overwritten, 0 when clean)
+ *  ws   workspace         >= moe_workspace_size bytes of device memory
+ *
+ * Rows of one expert are contiguous and in increasing slot order, experts in
+ * id order, so row(s) = prefix[e-1] + #{s' < s : active routed slot of e}.
+ * A masked slot, a zero-expert slot and an invalid slot get no row.
+ */
+moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                        const uint8_t* x_active_mask, void* expand_x,
+                        int32_t* assist_info_for_combine, int32_t* expert_token_nums,
+                        int32_t* ep_recv_counts, int32_t* err_flag, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn - SwiGLU FFN of every expert over its rows, as grouped GEMMs.
+ * For expert e and its rows [prefix[e-1], prefix[e]):
+ *   G = X Wg_e^T, U = X Wu_e^T (fp32 accumulation), h = silu(G) * U,
+ *   y = h Wd_e^T.
+ *  in   expand_x       (capacity, H) bf16
+ *  in   w_gate, w_up   (E, F, H) bf16, (out, in) layout per expert
+ *  in   w_down         (E, H, F) bf16
+ *  in   ep_recv_counts (E,) int32 from moe_dispatch
+ *  out  gate_up_save   (capacity, 2F) bf16: [G | U] per row, kept for backward
+ *  out  h_act          (capacity, F) bf16: h
+ *  out  y              (capacity, H) bf16
+ * Equivalent to moe_ffn_gate_up_fwd followed by moe_ffn_down_fwd.
+ */
+moe_status moe_grouped_ffn(const moe_shape* s, const void* expand_x, const void* w_gate,
+                           const void* w_up, const void* w_down, const int32_t* ep_recv_counts,
+                           void* gate_up_save, void* h_act, void* y, void* stream);
+
+/* First grouped GEMM of moe_grouped_ffn (gate and up projections with the
+ * SwiGLU product fused into its epilogue).  One kernel launch. */
+moe_status moe_ffn_gate_up_fwd(const moe_shape* s, const void* expand_x, const void* w_gate,
+                               const void* w_up, const int32_t* ep_recv_counts,
+                               void* gate_up_save, void* h_act, void* stream);
+
+/* Second grouped GEMM of moe_grouped_ffn: y = h Wd_e^T.  One kernel launch. */
+moe_status moe_ffn_down_fwd(const moe_shape* s, const void* h_act, const void* w_down,
+                            const int32_t* ep_recv_counts, void* y, void* stream);
+
+/*
+ * moe_combine - weighted merge of the expert outputs back to tokens
+ * (low_latency_combine page, Function: Formula; Parameters).
+ *   out[t] = sum over k = 0..K-1 of topk_weights[t,k] * v(t,k), then + shared_expert_x[t]
+ * where v is y[row] for a routed slot, 0 for a zero expert (and for a masked
+ * slot), ori_x[t] for a copy expert and alpha_1[j]*ori_x[t] + alpha_2[j]*v[j]
+ * for constant expert j.  The sum runs in k order in fp32 with separately
+ * rounded products (no fused multiply-add), the shared term is added last and
+ * the result is rounded once to bf16.
+ *  in   y                        (capacity, H) bf16 (rows < A are read)
+ *  in   topk_idx                 (T, K) int32  (shape check only; routing is in assist info)
+ *  in   topk_weights             (T, K) float32
+ *  in   assist_info_for_combine  from moe_dispatch
+ *  in   ep_send_counts           (E,) int32 = ep_recv_counts of moe_dispatch
+ *  in   x_active_mask            as given to moe_dispatch (already folded into assist info)
+ *  in   shared_expert_x          (T, H) bf16 or NULL
+ *  in   ori_x                    (T, H) bf16; required when C + Q > 0
+ *  in   const_alpha_1/_2, const_v  (Q, H) bf16; required when Q > 0
+ *  out  out                      (T, H) bf16
+ */
+moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* topk_idx,
+                       const float* topk_weights, const int32_t* assist_info_for_combine,
+                       const int32_t* ep_send_counts, const uint8_t* x_active_mask,
+                       const void* shared_expert_x, const void* ori_x, const void* const_alpha_1,
+                       const void* const_alpha_2, const void* const_v, void* out, void* stream);
+
+/*
+ * moe_combine_bwd - gradient of moe_combine.
+ *   grad_y[row]          = bf16(topk_weights[t,k] * grad_out[t])      (routed rows)
+ *   grad_topk_weights[t,k] = <v(t,k), grad_out[t]> in fp32 (0 for masked/zero slots)
+ * The gradient of shared_expert_x is grad_out itself; the copy/const terms'
+ * gradient to ori_x is added by moe_dispatch_bwd.
+ */
+moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, const void* y,
+                           const int32_t* topk_idx, const float* topk_weights,
+                           const int32_t* assist_info_for_combine, const int32_t* ep_send_counts,
+                           const uint8_t* x_active_mask, const void* ori_x,
+                           const void* const_alpha_1, const void* const_alpha_2,
+                           const void* const_v, void* grad_y, float* grad_topk_weights,
+                           void* stream);
+
+/*
+ * moe_grouped_ffn_bwd - backward of moe_grouped_ffn, four grouped GEMMs.
+ *   dH = dY Wd_e;  with s = sigmoid(G): dG = dH*U*s*(1 + G(1-s)), dU = dH*G*s
+ *   grad_gate_up = [dG | dU] (bf16), dX = [dG dU] [Wg_e; Wu_e] (bf16)
+ *   dWd_e = dY^T h, dWg_e = dG^T X, dWu_e = dU^T X (fp32; experts with no rows get 0)
+ *  in   grad_y (capacity, H), expand_x (capacity, H), gate_up_save (capacity, 2F),
+ *       h_act (capacity, F): bf16;  w_gate, w_up, w_down as in moe_grouped_ffn
+ *  out  grad_gate_up (capacity, 2F) bf16, grad_expand_x (capacity, H) bf16,
+ *       grad_w_gate, grad_w_up (E, F, H) fp32, grad_w_down (E, H, F) fp32
+ * Equivalent to moe_ffn_down_bwd_data, moe_ffn_down_bwd_weight,
+ * moe_ffn_gate_up_bwd_data and moe_ffn_gate_up_bwd_weight in that order.
+ */
+moe_status moe_grouped_ffn_bwd(const moe_shape* s, const void* grad_y, const void* expand_x,
+                               const void* gate_up_save, const void* h_act, const void* w_gate,
+                               const void* w_up, const void* w_down,
+                               const int32_t* ep_recv_counts, void* grad_gate_up,
+                               void* grad_expand_x, float* grad_w_gate, float* grad_w_up,
+                               float* grad_w_down, void* stream);
+
+/* grad_gate_up = SwiGLU backward of (grad_y Wd_e).  One kernel launch. */
+moe_status moe_ffn_down_bwd_data(const moe_shape* s, const void* grad_y, const void* w_down,
+                                 const void* gate_up_save, const int32_t* ep_recv_counts,
+                                 void* grad_gate_up, void* stream);
+
+/* grad_w_down[e] = grad_y_e^T h_e.  One kernel launch. */
+moe_status moe_ffn_down_bwd_weight(const moe_shape* s, const void* grad_y, const void* h_act,
+                                   const int32_t* ep_recv_counts, float* grad_w_down,
+                                   void* stream);
+
+/* grad_expand_x = grad_gate_up [Wg_e; Wu_e].  One kernel launch. */
+moe_status moe_ffn_gate_up_bwd_data(const moe_shape* s, const void* grad_gate_up,
+                                    const void* w_gate, const void* w_up,
+                                    const int32_t* ep_recv_counts, void* grad_expand_x,
+                                    void* stream);
+
+/* grad_w_gate[e] = dG_e^T X_e, grad_w_up[e] = dU_e^T X_e.  One kernel launch. */
+moe_status moe_ffn_gate_up_bwd_weight(const moe_shape* s, const void* grad_gate_up,
+                                      const void* expand_x, const int32_t* ep_recv_counts,
+                                      float* grad_w_gate, float* grad_w_up, void* stream);
+
+/*
+ * moe_dispatch_bwd - gradient with respect to the layer input x (= ori_x).
+ *   grad_x[t] = sum over k (k order) of: grad_expand_x[row] (routed slot),
+ *               w * grad_out[t] (copy slot), w * (alpha_1[j] * grad_out[t])
+ *               (constant slot j); then + grad_x_accum[t]; one bf16 rounding.
+ *  in   grad_expand_x (capacity, H) bf16, assist_info_for_combine, topk_idx (T,K),
+ *       topk_weights (T,K) fp32, x_active_mask (as for dispatch, folded already),
+ *       grad_out (T,H) bf16 (required when C + Q > 0), const_alpha_1 (Q,H) bf16
+ *       (required when Q > 0), grad_x_accum (T,H) bf16 or NULL (e.g. the
+ *       shared expert's input gradient)
+ *  out  grad_x (T, H) bf16
+ */
+moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,
+                            const int32_t* assist_info_for_combine, const int32_t* topk_idx,
+                            const float* topk_weights, const uint8_t* x_active_mask,
+                            const void* grad_out, const void* const_alpha_1,
+                            const void* grad_x_accum, void* grad_x, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

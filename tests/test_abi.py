@@ -1,0 +1,145 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/moe.h
+declares, and its host-side validation returns the documented status codes
+before touching the GPU (every call below fails validation, so nothing is
+launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dispatch_expert_gemm_amd as dm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, CAPACITY, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dm.LIB_PATH):
+        pytest.skip("libmoe.so not built (run __graft_entry__.build())")
+    return dm.lib()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(dm.ENTRY_POINTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for st in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, CAPACITY, UNSUPPORTED, WORKSPACE, -7):
+        assert L.moe_status_str(st)
+    assert b"unknown" in L.moe_status_str(12345)
+
+
+def S(**kw):
+    base = dict(T=8, H=1536, K=8, num_experts=32, F=480)
+    base.update(kw)
+    return dm.make_shape(**base)
+
+
+def ws(shape):
+    n = ctypes.c_size_t()
+    st = dm.lib().moe_workspace_size(ctypes.byref(shape) if shape is not None else None,
+                                     ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), OK),
+    (dict(K=0), BAD_SHAPE),
+    (dict(K=17, zero_expert_num=4), BAD_SHAPE),          # 0 < K <= 16
+    (dict(K=8, num_experts=4), BAD_SHAPE),                # K > E+Z+C+Q
+    (dict(K=8, num_experts=4, zero_expert_num=2, copy_expert_num=1, const_expert_num=1), OK),
+    (dict(num_experts=0), BAD_SHAPE),
+    (dict(num_experts=1025), BAD_SHAPE),                  # num_experts in [1, 1024]
+    (dict(H=100), BAD_SHAPE),                             # H multiple of 8
+    (dict(T=-1), BAD_SHAPE),
+    (dict(capacity=8 * 8 - 1), CAPACITY),                 # A >= BS * min(E, K)
+    (dict(K=4, num_experts=2, zero_expert_num=2, capacity=8 * 2), OK),
+    (dict(zero_expert_num=-1), BAD_SHAPE),
+    (dict(mask_ndim=3), BAD_RANGE),
+    (dict(T=0), OK),
+])
+def test_shape_validation(L, kw, expect):
+    st, n = ws(S(**kw))
+    assert st == expect
+    if st == OK:
+        assert n > 0 and n % 256 == 0
+
+
+def test_shape_validation_misc(L):
+    assert ws(None)[0] == NULL_ARG
+    s = S()
+    s.act_dtype = 7
+    assert ws(s)[0] == UNSUPPORTED
+    s = S()
+    s.reserved = 1
+    assert ws(s)[0] == BAD_RANGE
+    n = ctypes.c_int64()
+    assert L.moe_assist_info_size(ctypes.byref(S()), ctypes.byref(n)) == OK
+    assert n.value == 8 * 8 + 8 * 8
+
+
+def P(v=0x1000):
+    return ctypes.c_void_p(v)   # a non-NULL stand-in: never dereferenced (validation fails first)
+
+
+def test_entry_points_reject_bad_arguments_before_launch(L):
+    s = S()
+    sp = ctypes.byref(s)
+    Nn = None
+    # dispatch: NULL required outputs, missing mask, small workspace
+    assert L.moe_dispatch(sp, P(), P(), Nn, P(), P(), P(), P(), Nn, P(), 1 << 20, Nn) == NULL_ARG
+    sm = S(mask_ndim=1)
+    assert L.moe_dispatch(ctypes.byref(sm), P(), P(), Nn, P(), P(), P(), P(), P(), P(), 1 << 20, Nn) == NULL_ARG
+    assert L.moe_dispatch(sp, P(), P(), Nn, P(), P(), P(), P(), P(), P(), 16, Nn) == WORKSPACE
+    assert L.moe_dispatch(sp, P(), P(), Nn, P(), P(), P(), P(), P(), Nn, 1 << 20, Nn) == WORKSPACE
+    # combine: ori_x required with copy/const experts, const tensors with const experts
+    sc = S(copy_expert_num=1)
+    assert L.moe_combine(ctypes.byref(sc), P(), P(), P(), P(), P(), Nn, Nn, Nn, Nn, Nn, Nn, P(), Nn) == NULL_ARG
+    sq = S(const_expert_num=2)
+    assert L.moe_combine(ctypes.byref(sq), P(), P(), P(), P(), P(), Nn, Nn, P(), P(), Nn, P(), P(), Nn) == NULL_ARG
+    assert L.moe_combine_bwd(ctypes.byref(sq), P(), P(), P(), P(), P(), P(), Nn, P(), P(), P(), Nn, P(), P(), Nn) == NULL_ARG
+    assert L.moe_dispatch_bwd(ctypes.byref(sq), P(), P(), P(), P(), Nn, P(), Nn, Nn, P(), Nn) == NULL_ARG
+    assert L.moe_dispatch_bwd(ctypes.byref(sc), P(), P(), P(), P(), Nn, Nn, Nn, Nn, P(), Nn) == NULL_ARG
+    # FFN: F must be a positive multiple of 32
+    for F in (0, 48, -32):
+        sf = S(F=F)
+        assert L.moe_grouped_ffn(ctypes.byref(sf), P(), P(), P(), P(), P(), P(), P(), P(), Nn) == BAD_SHAPE
+        assert L.moe_grouped_ffn_bwd(ctypes.byref(sf), *([P()] * 13), Nn) == BAD_SHAPE
+    assert L.moe_grouped_ffn(sp, P(), Nn, P(), P(), P(), P(), P(), P(), Nn) == NULL_ARG
+    assert L.moe_ffn_down_bwd_weight(sp, P(), P(), P(), Nn, Nn) == NULL_ARG
+    assert L.moe_ffn_gate_up_bwd_weight(sp, P(), P(), P(), P(), Nn, Nn) == NULL_ARG
+    assert L.moe_ffn_gate_up_fwd(sp, Nn, P(), P(), P(), P(), P(), Nn) == NULL_ARG
+    assert L.moe_ffn_down_fwd(sp, P(), P(), P(), Nn, Nn) == NULL_ARG
+    assert L.moe_ffn_down_bwd_data(sp, P(), P(), Nn, P(), P(), Nn) == NULL_ARG
+    assert L.moe_ffn_gate_up_bwd_data(sp, P(), P(), Nn, P(), P(), Nn) == NULL_ARG
+    # bad shapes are rejected by every entry
+    bad = ctypes.byref(S(K=0))
+    assert L.moe_combine(bad, *([P()] * 12), Nn) == BAD_SHAPE
+    assert L.moe_dispatch(bad, *([P()] * 8), P(), 1 << 20, Nn) == BAD_SHAPE
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The package never imports the oracle and refuses non-GPU tensors."""
+    pkg = os.path.join(ROOT, "dispatch_expert_gemm_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("oracle/", ""), fn
+    import torch
+    with pytest.raises(dm.MoeError):
+        dm._ptr(torch.zeros(3), torch.float32, "cpu tensor")

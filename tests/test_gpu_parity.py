@@ -1,0 +1,270 @@
+"""GPU parity of every C entry point against the CPU oracle, on seeded inputs.
+
+Indices, counts, prefix sums, both slot/row maps and the permuted rows are
+compared bit for bit; so are the gather-reduce outputs (combine, the dY rows of
+combine_bwd, dispatch_bwd), whose summation order is the oracle's.  Outputs of
+the grouped GEMMs are compared against the oracle's parity mode within
+max |err| <= 2e-2 and relative L2 <= 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as wl
+import oracle as orc
+from gpu_util import DEV, Run, bf, check_close, check_equal, dev, f32
+
+pytestmark = pytest.mark.gpu
+
+# (name, layer_inputs kwargs): several tiles, ragged tails, masks, special experts
+ROUTE_CASES = {
+    "tiny": dict(T=256, H=128, F=64, E=8, K=2),
+    "page1_1k": dict(T=1024, H=1536, F=480, E=64, K=8),
+    "special_2d_mask": dict(T=300, H=64, F=32, E=10, K=6, Z=2, C=1, Q=3, mask="2d"),
+    "prefix_1d_mask": dict(T=77, H=32, F=32, E=5, K=3, C=1, mask="1d", mask_active=40),
+    "one_expert_k1": dict(T=33, H=16, F=32, E=1, K=1),
+    "many_experts_k16": dict(T=200, H=16, F=32, E=1024, K=16),
+    "single_token": dict(T=1, H=8, F=32, E=4, K=2),
+    "no_tokens": dict(T=0, H=8, F=32, E=4, K=2),
+}
+
+
+def _inputs(name, seed=0, weights=False, grad=False):
+    kw = dict(ROUTE_CASES[name])
+    return wl.layer_inputs(seed=seed, weights=weights, grad=grad, **kw)
+
+
+def _check_route(run, inp):
+    r = orc.route(inp["topk_idx"], inp["E"], inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0),
+                  inp.get("mask"))
+    d = run.d
+    T, K = inp["T"], inp["K"]
+    check_equal("expert_token_nums", d.expert_token_nums.cpu().numpy(), r.counts)
+    check_equal("ep_recv_counts", d.ep_recv_counts.cpu().numpy(), r.ep_recv_counts)
+    check_equal("slot2row", d.slot2row(T, K).cpu().numpy(), r.slot2row)
+    check_equal("row2slot", d.row2slot(T, K)[:r.A].cpu().numpy(), r.row2slot)
+    assert int(d.err_flag.item()) == r.err
+    return r
+
+
+@pytest.mark.parametrize("name", list(ROUTE_CASES))
+def test_dispatch_bit_exact(name):
+    inp = _inputs(name)
+    run = Run(inp)
+    print(f"[dispatch] case={name} T={inp['T']} E={inp['E']} K={inp['K']}", flush=True)
+    run.dispatch()
+    r = _check_route(run, inp)
+    X = orc.dispatch(inp["x"], r)
+    check_equal("expand_x", f32(run.d.expand_x[:r.A]), X)
+
+
+def test_dispatch_error_flags():
+    T, K, E = 64, 4, 6
+    inp = wl.layer_inputs(T, 16, 32, E, K, seed=1, weights=False, grad=False)
+    idx = inp["topk_idx"].copy()
+    idx[3, 2] = E + 5          # out of range
+    idx[7, 3] = idx[7, 0]      # duplicate: the later one is dropped
+    idx[9, 0] = -1             # negative
+    inp["topk_idx"] = idx
+    m = np.ones(T, np.uint8)
+    m[10] = 0                  # a false before trues: not a prefix
+    inp["mask"] = m
+    run = Run(inp)
+    run.dispatch()
+    r = _check_route(run, inp)
+    assert r.err == orc.ERR_ID_RANGE | orc.ERR_ID_DUPLICATE | orc.ERR_MASK_NOT_PREFIX
+
+
+FFN_CASES = {
+    "tiny": dict(T=256, H=128, F=64, E=8, K=2),
+    "ragged": dict(T=300, H=256, F=96, E=7, K=3),
+    "page1_512": dict(T=512, H=1536, F=480, E=64, K=8),
+    "empty_experts": dict(T=20, H=64, F=32, E=16, K=1),
+    "special_mask": dict(T=150, H=128, F=64, E=6, K=4, Z=1, C=1, Q=2, mask="2d"),
+}
+
+
+def _forward(inp):
+    run = Run(inp)
+    run.dispatch()
+    run.ffn()
+    return run
+
+
+@pytest.mark.parametrize("name", list(FFN_CASES))
+def test_grouped_ffn_forward(name):
+    inp = wl.layer_inputs(seed=2, **FFN_CASES[name])
+    print(f"[ffn fwd] case={name}", flush=True)
+    run = _forward(inp)
+    f = orc.layer_fwd(inp, prec="parity")
+    A, F = run.A, inp["F"]
+    assert A == f["route"].A
+    check_close("G", f32(run.gus[:A, :F]), f["G"])
+    check_close("U", f32(run.gus[:A, F:]), f["U"])
+    check_close("h", f32(run.h[:A]), f["Hh"])
+    check_close("y", f32(run.y[:A]), f["Y"])
+
+
+COMBINE_CASES = {
+    "routed_only": dict(T=257, H=136, E=9, K=4),
+    "special_2d_mask_shared": dict(T=300, H=256, E=16, K=8, Z=1, C=1, Q=2, mask="2d", shared=True),
+    "copy_const_1d_mask": dict(T=129, H=64, E=4, K=5, C=2, Q=1, mask="1d", shared=False),
+}
+
+
+def _combine_inputs(name, seed=3):
+    kw = dict(COMBINE_CASES[name])
+    shared = kw.pop("shared", False)
+    mask = kw.pop("mask", None)
+    inp = wl.layer_inputs(seed=seed, weights=False, grad=True, F=0, mask=mask,
+                          mask_active=kw["T"] // 2, **kw)
+    rng = np.random.default_rng(seed + 100)
+    cap = kw["T"] * min(kw["E"], kw["K"])
+    inp["y"] = wl.to_bf16_bits(rng.standard_normal((cap, kw["H"]), dtype=np.float32))
+    inp["dX"] = wl.to_bf16_bits(rng.standard_normal((cap, kw["H"]), dtype=np.float32) * 0.1)
+    inp["shared_expert_x"] = wl.to_bf16_bits(rng.standard_normal((kw["T"], kw["H"]), dtype=np.float32)) \
+        if shared else None
+    return inp
+
+
+@pytest.mark.parametrize("name", list(COMBINE_CASES))
+def test_combine_forward_bit_exact(name):
+    inp = _combine_inputs(name)
+    print(f"[combine] case={name}", flush=True)
+    run = Run(inp)
+    run.dispatch()
+    r = _check_route(run, inp)
+    sh = bf(inp["shared_expert_x"]) if inp["shared_expert_x"] is not None else None
+    out = run.combine(y=bf(inp["y"]), shared=sh)
+    Y = orc.bf16_to_f32(inp["y"])[:r.A]
+    ref = orc.combine(Y, r, inp["topk_weights"], inp["shared_expert_x"], inp["x"],
+                      inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"))
+    check_equal("out", f32(out), ref)
+
+
+@pytest.mark.parametrize("name", list(COMBINE_CASES))
+def test_combine_backward(name):
+    inp = _combine_inputs(name)
+    run = Run(inp)
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"], inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0),
+                  inp.get("mask"))
+    gy, gw = run.combine_bwd(bf(inp["grad_out"]), y=bf(inp["y"]))
+    Y = orc.bf16_to_f32(inp["y"])[:r.A]
+    dY, dw = orc.combine_bwd(inp["grad_out"], Y, r, inp["topk_weights"], inp["x"],
+                             inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"))
+    check_equal("grad_y", f32(gy[:r.A]), dY)
+    # dw is a length-H dot product: fp32 summation order differs from numpy's
+    check_close("grad_topk_weights", f32(gw), dw, max_abs=1e-3, rel_l2=1e-5)
+    assert np.all(f32(gw)[r.slot2row.reshape(r.T, r.K) == -1] == 0)
+
+
+@pytest.mark.parametrize("name", list(COMBINE_CASES))
+def test_dispatch_backward_bit_exact(name):
+    inp = _combine_inputs(name)
+    run = Run(inp)
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"], inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0),
+                  inp.get("mask"))
+    rng = np.random.default_rng(7)
+    accum = wl.to_bf16_bits(rng.standard_normal((inp["T"], inp["H"]), dtype=np.float32))
+    for acc in (None, accum):
+        gx = run.dispatch_bwd(bf(inp["dX"]), bf(inp["grad_out"]), None if acc is None else bf(acc))
+        dX = orc.bf16_to_f32(inp["dX"])[:r.A]
+        ref = orc.dispatch_bwd(dX, r, inp["topk_weights"], inp["grad_out"], inp.get("const_alpha_1"),
+                               None if acc is None else orc.bf16_to_f32(acc))
+        check_equal("grad_x", f32(gx), ref)
+
+
+def test_round_trip_is_k_times_x():
+    """dispatch then combine of expand_x itself with unit weights gives K*x exactly."""
+    for T, H, E, K in ((300, 128, 16, 8), (64, 1536, 64, 8), (50, 40, 5, 3)):
+        inp = wl.layer_inputs(T, H, 32, E, K, seed=5, weights=False, grad=False)
+        run = Run(inp)
+        run.dispatch()
+        out = run.combine(y=run.d.expand_x, w=torch.ones((T, K), dtype=torch.float32, device=DEV))
+        ref = (run.x.float().cpu() * K).to(torch.bfloat16)
+        assert torch.equal(out.cpu().view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", list(FFN_CASES))
+def test_grouped_ffn_backward(name):
+    inp = wl.layer_inputs(seed=4, **FFN_CASES[name])
+    print(f"[ffn bwd] case={name}", flush=True)
+    run = _forward(inp)
+    f = orc.layer_fwd(inp, prec="parity")
+    r = f["route"]
+    A = r.A
+    dY_bits = wl.to_bf16_bits(np.random.default_rng(9).standard_normal((run.cap, inp["H"]), dtype=np.float32) * 0.2)
+    ggu, gxe, gwg, gwu, gwd = run.ffn_bwd(bf(dY_bits))
+    dY = orc.bf16_to_f32(dY_bits)[:A]
+    dGU, dX, dWg, dWu, dWd = orc.ffn_bwd(dY, f["X"], f["G"], f["U"], f["Hh"], r.ep_recv_counts,
+                                         inp["w_gate"], inp["w_up"], inp["w_down"])
+    check_close("grad_gate_up", f32(ggu[:A]), dGU)
+    check_close("grad_expand_x", f32(gxe[:A]), dX)
+    check_close("grad_w_gate", f32(gwg), dWg)
+    check_close("grad_w_up", f32(gwu), dWu)
+    check_close("grad_w_down", f32(gwd), dWd)
+
+
+LAYER_CASES = {
+    "tiny": dict(T=256, H=128, F=64, E=8, K=2),
+    "special_mask": dict(T=200, H=256, F=96, E=12, K=6, Z=1, C=1, Q=2, mask="2d"),
+    "page1_1k": dict(T=1024, H=1536, F=480, E=64, K=8),
+}
+
+
+@pytest.mark.parametrize("name", list(LAYER_CASES))
+def test_layer_forward_backward(name):
+    """Whole chain through the C entries: dispatch, FFN, combine and their backward."""
+    inp = wl.layer_inputs(seed=6, **LAYER_CASES[name])
+    print(f"[layer] case={name}", flush=True)
+    run = _forward(inp)
+    out = run.combine()
+    g = bf(inp["grad_out"])
+    gy, gw = run.combine_bwd(g)
+    ggu, gxe, gwg, gwu, gwd = run.ffn_bwd(gy)
+    gx = run.dispatch_bwd(gxe, g)
+    f = orc.layer_fwd(inp, prec="parity")
+    b = orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
+    A = f["route"].A
+    check_close("out", f32(out), f["out"])
+    check_close("grad_y", f32(gy[:A]), b["dY"])
+    check_close("grad_topk_weights", f32(gw), b["dw"])
+    check_close("grad_gate_up", f32(ggu[:A]), b["dGU"])
+    check_close("grad_expand_x", f32(gxe[:A]), b["dX"])
+    check_close("grad_x", f32(gx), b["dx"])
+    check_close("grad_w_gate", f32(gwg), b["dWg"])
+    check_close("grad_w_up", f32(gwu), b["dWu"])
+    check_close("grad_w_down", f32(gwd), b["dWd"])
+
+
+def test_autograd_layer_and_determinism():
+    import dispatch_expert_gemm_amd as dm
+    inp = wl.layer_inputs(seed=8, **LAYER_CASES["special_mask"])
+    res = []
+    for _ in range(2):
+        x = bf(inp["x"]).requires_grad_(True)
+        w = dev(inp["topk_weights"]).requires_grad_(True)
+        wg, wu, wd = (bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down"))
+        sh = bf(wl.to_bf16_bits(np.random.default_rng(1).standard_normal((inp["T"], inp["H"]),
+                                                                          dtype=np.float32))).requires_grad_(True)
+        out = dm.moe_layer(x, dev(inp["topk_idx"]), w, wg, wu, wd, x_active_mask=dev(inp["mask"]).bool(),
+                           shared_expert_x=sh, const_alpha_1=bf(inp["const_alpha_1"]),
+                           const_alpha_2=bf(inp["const_alpha_2"]), const_v=bf(inp["const_v"]),
+                           zero_expert_num=1, copy_expert_num=1, const_expert_num=2)
+        out.backward(bf(inp["grad_out"]))
+        torch.cuda.synchronize()
+        res.append([t.detach().cpu().clone() for t in (out, x.grad, w.grad, wg.grad, wu.grad, wd.grad, sh.grad)])
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    inp2 = dict(inp, shared_expert_x=wl.to_bf16_bits(np.random.default_rng(1).standard_normal(
+        (inp["T"], inp["H"]), dtype=np.float32)))
+    f = orc.layer_fwd(inp2, prec="parity")
+    b = orc.layer_bwd(inp2, f, inp["grad_out"], prec="parity")
+    out, gx, gw = res[0][0], res[0][1], res[0][2]
+    check_close("out", f32(out), f["out"])
+    check_close("grad_x", f32(gx), b["dx"])
+    check_close("grad_topk_weights", f32(gw), b["dw"])
+    assert torch.equal(res[0][6].view(torch.int16), bf(inp["grad_out"]).cpu().view(torch.int16))
