@@ -18,11 +18,12 @@
 //
 // Tiling: 128 x 128 output tile per 256-thread workgroup, four waves in a 2 x 2
 // arrangement, each wave 64 x 64 = 2 x 2 v_mfma_f32_32x32x16_bf16 tiles; K step
-// 32 staged through double-buffered LDS (one barrier per step), the next step's
+// 64 staged through double-buffered LDS (one barrier per step), the next step's
 // global loads in flight in registers while the current step's MFMAs issue.  In
-// LDS both operands are stored K-contiguous (row pitch 40 elements), so every
-// MFMA operand is one 16-byte LDS read; operands that are K-strided in memory
-// are transposed on their way into LDS.
+// LDS both operands are stored K-contiguous with an XOR-swizzled chunk order,
+// so every MFMA operand is one conflict-free 16-byte LDS read; operands that are
+// K-strided in memory are loaded as 4 k-rows x 8 columns per thread, transposed
+// in registers with byte permutes and written as 8-byte LDS stores.
 //
 // Expert counts stay on the device: the grid covers floor(capacity/128) + E row
 // tiles per column tile, and each workgroup finds its expert from the prefix
@@ -44,7 +45,7 @@ enum Mode : int {
   GATE_UP_BWD_W = 5
 };
 
-constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
+constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
 
 struct GemmArgs {
@@ -84,12 +85,20 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ prefix, i
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
+// LDS tile: 128 rows x 64 k of bf16, row pitch 128 bytes, in eight 16-byte chunks
+// of 8 consecutive k.  Chunk c of row r sits at chunk position c ^ swz(r), so the
+// eight rows read by eight consecutive lanes of an MFMA operand fetch, and the
+// eight chunks of one row written by eight consecutive lanes, fall in distinct
+// banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
   constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -125,92 +134,148 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   }
   const int64_t klen = kend - kbeg;
 
-  // ---- global -> register loads of one K step
-  uint4 ra[2], rb[2];
-  auto load_a = [&](int64_t k0) {
+  // Thread roles in one K step.
+  //  K-contiguous operand: vectors i = tid + 256*j (j < 4): row i/8, chunk i%8.
+  //  K-strided operand: k rows 4*k4 .. 4*k4+3 (k4 = tid/16) of 8 columns from
+  //  x8 = 8*(tid%16); transposed in registers, written as 8 x 8-byte stores.
+  // Loads are branch-free: out-of-range addresses are clamped into the operand
+  // and the value replaced by zero.
+  const int k4 = tid >> 4, x8 = (tid & 15) * 8;
+  const int kc_c = (tid & 7) * 8;  // chunk column of a K-contiguous vector (same for all j)
+  auto ld16 = [](const bf16_t* base, uint32_t off) -> uint4 {
+    return *reinterpret_cast<const uint4*>(base + off);
+  };
+  // component-wise select (a select of the whole vector struct goes through memory)
+  auto keep = [](bool ok, const uint4& v) -> uint4 {
+    const uint32_t m = ok ? 0xffffffffu : 0u;
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+  };
+  // Uniform operand bases and per-lane 32-bit element offsets (every operand
+  // slice addressed from one base stays below 2^31 elements).
+  const bf16_t* abase;
+  uint32_t aoff[4];
+  if constexpr (!KGROUP) {
+    abase = g.A + row0 * g.lda;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = tid + kThreads * j;
-      uint4 v = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 3) + 32 * j;
+      aoff[j] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * g.lda + kc_c);
+    }
+  } else {
+    abase = g.A + kbeg * g.lda;
+    const int64_t col = row0 + x8 < g.M ? row0 + x8 : g.M - 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) aoff[j] = (uint32_t)col;
+  }
+  const bf16_t* bbase0;
+  const bf16_t* bbase1;
+  uint32_t boff[4];
+  if constexpr (B_KC) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 3) + 32 * j;
+      int64_t n;
+      if constexpr (MODE == GATE_UP_FWD) {
+        n = n0 + (r & (BN / 2 - 1));
+        if (n >= g.F) n = g.F - 1;
+      } else {
+        n = n0 + r;
+        if (n >= g.N) n = g.N - 1;
+      }
+      boff[j] = (uint32_t)(n * g.ldb + kc_c);
+    }
+    bbase0 = g.B0 + (int64_t)e * g.bstride;
+    bbase1 = (MODE == GATE_UP_FWD) ? g.B1 + (int64_t)e * g.bstride : bbase0;
+  } else {
+    const int64_t col = n0 + x8 < g.N ? n0 + x8 : g.N - 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) boff[j] = (uint32_t)col;
+    if constexpr (KGROUP) {
+      bbase0 = g.B0 + kbeg * g.ldb;
+      bbase1 = bbase0;
+    } else {
+      bbase0 = g.B0 + (int64_t)e * g.bstride;
+      bbase1 = (MODE == GATE_UP_BWD_DATA) ? g.B1 + (int64_t)e * g.bstride - g.F * g.ldb : bbase0;
+    }
+  }
+  const bool col_ok_a = !KGROUP || row0 + x8 < g.M;
+  const bool col_ok_b = B_KC || n0 + x8 < g.N;
+
+  // Loads are branch-free: out-of-range rows, columns and K positions are
+  // clamped into the operand; K positions past the end are replaced by zero
+  // when the registers go to LDS (masking right after the load would make the
+  // wave wait for the load there and defeat the prefetch).
+  auto load_a = [&](int64_t k0, uint4* ra) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       if constexpr (!KGROUP) {
-        const int r = i >> 2, c = (i & 3) * 8;
-        const int64_t src = row0 + (r < rows_valid ? r : rows_valid - 1);
-        if (k0 + c < kend) v = *reinterpret_cast<const uint4*>(g.A + src * g.lda + k0 + c);
+        const uint32_t kk = (uint32_t)(k0 + kc_c < kend ? k0 : kend - 8 - kc_c);
+        ra[j] = ld16(abase, aoff[j] + kk);
       } else {
-        const int kr = i >> 4, x8 = (i & 15) * 8;
-        if (k0 + kr < klen && row0 + x8 < g.M)
-          v = *reinterpret_cast<const uint4*>(g.A + (kbeg + k0 + kr) * g.lda + row0 + x8);
+        const int64_t k = k0 + 4 * k4 + j;
+        const uint32_t kr = (uint32_t)(k < klen ? k : klen - 1);
+        ra[j] = ld16(abase, kr * (uint32_t)g.lda + aoff[j]);
       }
-      ra[j] = v;
     }
   };
-  auto load_b = [&](int64_t k0) {
+  auto load_b = [&](int64_t k0, uint4* rb) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = tid + kThreads * j;
-      uint4 v = make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
       if constexpr (B_KC) {
-        const int r = i >> 2, c = (i & 3) * 8;
-        if (k0 + c < kend) {
-          const bf16_t* base;
-          int64_t n;
-          if constexpr (MODE == GATE_UP_FWD) {
-            base = (r < BN / 2 ? g.B0 : g.B1) + (int64_t)e * g.bstride;
-            n = n0 + (r & (BN / 2 - 1));
-            if (n >= g.F) n = g.F - 1;
-          } else {
-            base = g.B0 + (int64_t)e * g.bstride;
-            n = n0 + r;
-            if (n >= g.N) n = g.N - 1;
-          }
-          v = *reinterpret_cast<const uint4*>(base + n * g.ldb + k0 + c);
-        }
+        const uint32_t kk = (uint32_t)(k0 + kc_c < kend ? k0 : kend - 8 - kc_c);
+        rb[j] = ld16(j < 2 ? bbase0 : bbase1, boff[j] + kk);
       } else {
-        const int kr = i >> 4, x8 = (i & 15) * 8;
-        const int64_t k = k0 + kr;
-        if (k < klen && n0 + x8 < g.N) {
-          const bf16_t* p;
-          if constexpr (MODE == DOWN_BWD_DATA) {
-            p = g.B0 + (int64_t)e * g.bstride + k * g.ldb;
-          } else if constexpr (MODE == GATE_UP_BWD_DATA) {
-            p = (k < g.F ? g.B0 + k * g.ldb : g.B1 + (k - g.F) * g.ldb) + (int64_t)e * g.bstride;
-          } else {
-            p = g.B0 + (kbeg + k) * g.ldb;
-          }
-          v = *reinterpret_cast<const uint4*>(p + n0 + x8);
-        }
+        const int64_t k = k0 + 4 * k4 + j;
+        const uint32_t kr = (uint32_t)(k < klen ? k : klen - 1);
+        const bf16_t* base = bbase0;
+        if constexpr (MODE == GATE_UP_BWD_DATA) base = kr < (uint32_t)g.F ? bbase0 : bbase1;
+        rb[j] = ld16(base, kr * (uint32_t)g.ldb + boff[j]);
       }
-      rb[j] = v;
     }
   };
-  // ---- register -> LDS (K-contiguous rows)
   auto store_kc = [&](bf16_t* S, const uint4* r) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int i = tid + kThreads * j;
-      *reinterpret_cast<uint4*>(S + (i >> 2) * LDK + (i & 3) * 8) = r[j];
+      *reinterpret_cast<uint4*>(S + lds_off(i >> 3, i & 7)) = r[j];
     }
   };
-  auto store_tr = [&](bf16_t* S, const uint4* r) {
+  auto store_t = [&](bf16_t* S, const uint4* v) {
+    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = tid + kThreads * j;
-      const int kr = i >> 4, x8 = (i & 15) * 8;
-      const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        S[(x8 + 2 * q) * LDK + kr] = (bf16_t)(w[q] & 0xffffu);
-        S[(x8 + 2 * q + 1) * LDK + kr] = (bf16_t)(w[q] >> 16);
-      }
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+      uint2 d;
+      d.x = __builtin_amdgcn_perm(w1[q >> 1], w0[q >> 1], sel);
+      d.y = __builtin_amdgcn_perm(w3[q >> 1], w2[q >> 1], sel);
+      *reinterpret_cast<uint2*>(S + lds_off(x8 + q, k4 >> 1) + (k4 & 1) * 4) = d;
     }
   };
-  auto store_a = [&](int s) {
+  auto mask_a = [&](int64_t k0, uint4* ra) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (!KGROUP) ra[j] = keep(k0 + kc_c < kend, ra[j]);
+      else ra[j] = keep(k0 + 4 * k4 + j < klen && col_ok_a, ra[j]);
+    }
+  };
+  auto mask_b = [&](int64_t k0, uint4* rb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (B_KC) rb[j] = keep(k0 + kc_c < kend, rb[j]);
+      else rb[j] = keep(k0 + 4 * k4 + j < klen && col_ok_b, rb[j]);
+    }
+  };
+  // k0: the K position the registers were loaded from
+  auto store_ab = [&](int s, int64_t k0, uint4* ra, uint4* rb) {
+    mask_a(k0, ra);
+    mask_b(k0, rb);
     if constexpr (!KGROUP) store_kc(As[s], ra);
-    else store_tr(As[s], ra);
-  };
-  auto store_b = [&](int s) {
+    else store_t(As[s], ra);
     if constexpr (B_KC) store_kc(Bs[s], rb);
-    else store_tr(Bs[s], rb);
+    else store_t(Bs[s], rb);
   };
 
   f32x16 acc[2][2];
@@ -225,43 +290,59 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
     if constexpr (MODE == GATE_UP_FWD) return j * (BN / 2) + wn * 32;
     else return wn * 64 + j * 32;
   };
+  // LDS element offsets of this lane's MFMA operand rows (chunk 0)
+  int arow[2], brw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) arow[i] = wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) brw[j] = brow(j) + (lane & 31);
 
+  // MFMAs of one K step on LDS stage s; operand fragments of sub-step kk+1 are
+  // read while the MFMAs of sub-step kk issue.
+  auto compute = [&](int s) {
+    const bf16_t* as = As[s];
+    const bf16_t* bs = Bs[s];
+    bf16x8 fa[2][2], fb[2][2];
+    auto fetch = [&](int kk, int slot) {
+      const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[slot][i] = *reinterpret_cast<const bf16x8*>(as + lds_off(arow[i], c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[slot][j] = *reinterpret_cast<const bf16x8*>(bs + lds_off(brw[j], c));
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                             acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Pipeline: two LDS stages, one register stage.  The global loads of step t+1
+  // are in flight while the MFMAs of step t issue, then go to LDS stage (t+1)%2.
+  uint4 ra[4], rb[4];
   const int64_t nk = (klen + BK - 1) / BK;
   if (nk > 0) {
-    load_a(0);
-    load_b(0);
-    store_a(0);
-    store_b(0);
+    load_a(0, ra);
+    load_b(0, rb);
+    store_ab(0, 0, ra, rb);
     __syncthreads();
   }
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int s = (int)(kt & 1);
     if (kt + 1 < nk) {
-      load_a((kt + 1) * BK);
-      load_b((kt + 1) * BK);
+      load_a((kt + 1) * BK, ra);
+      load_b((kt + 1) * BK, rb);
     }
-    const bf16_t* as = As[s];
-    const bf16_t* bs = Bs[s];
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ko = kk * 16 + (lane >> 5) * 8;
-      bf16x8 fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(as + (wm * 64 + i * 32 + (lane & 31)) * LDK + ko);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(bs + (brow(j) + (lane & 31)) * LDK + ko);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      store_a(s ^ 1);
-      store_b(s ^ 1);
-    }
+    compute(s);
+    if (kt + 1 < nk) store_ab(s ^ 1, (kt + 1) * BK, ra, rb);
     __syncthreads();
   }
 
