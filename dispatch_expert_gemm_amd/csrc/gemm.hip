@@ -93,12 +93,26 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
+// Row pitches (elements) of the output tiles staged in LDS by the epilogues;
+// the 16-byte pad puts rows m and m+4 (written by the two half-waves of one
+// store) in different banks.
+constexpr int kCP = BN + 8;      // 128-column tiles
+constexpr int kHP = BN / 2 + 8;  // 64-column tiles of the gate/up forward
+template <int MODE>
+constexpr int kSmemElems = (MODE == DOWN_BWD_DATA) ? (2 * BM * kCP > 2 * (BM + BN) * BK
+                                                          ? 2 * BM * kCP
+                                                          : 2 * (BM + BN) * BK)
+                                                   : 2 * (BM + BN) * BK;
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
   constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BK];
+  // Two LDS stages of the A and B tiles; after the K loop the same memory
+  // stages the output tile (and, for the SwiGLU backward, the saved G/U tile).
+  __shared__ __attribute__((aligned(16))) bf16_t smem[kSmemElems<MODE>];
+  auto As = [&](int st) { return smem + st * BM * BK; };
+  auto Bs = [&](int st) { return smem + 2 * BM * BK + st * BN * BK; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -272,10 +286,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   auto store_ab = [&](int s, int64_t k0, uint4* ra, uint4* rb) {
     mask_a(k0, ra);
     mask_b(k0, rb);
-    if constexpr (!KGROUP) store_kc(As[s], ra);
-    else store_t(As[s], ra);
-    if constexpr (B_KC) store_kc(Bs[s], rb);
-    else store_t(Bs[s], rb);
+    if constexpr (!KGROUP) store_kc(As(s), ra);
+    else store_t(As(s), ra);
+    if constexpr (B_KC) store_kc(Bs(s), rb);
+    else store_t(Bs(s), rb);
   };
 
   f32x16 acc[2][2];
@@ -300,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   // MFMAs of one K step on LDS stage s; operand fragments of sub-step kk+1 are
   // read while the MFMAs of sub-step kk issue.
   auto compute = [&](int s) {
-    const bf16_t* as = As[s];
-    const bf16_t* bs = Bs[s];
+    const bf16_t* as = As(s);
+    const bf16_t* bs = Bs(s);
     bf16x8 fa[2][2], fb[2][2];
     auto fetch = [&](int kk, int slot) {
       const int c = kk * 2 + (lane >> 5);
@@ -348,25 +362,88 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
 
   // ---- epilogue.  acc[i][j][r] holds C(m, n) with
   //   m = wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  n = brow(j) + lane%32
+  // The K loop ended with a barrier, so the LDS stages are free.
   const int ln = lane & 31, lh = lane >> 5;
+  auto mrow = [&](int i, int r) { return wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3); };
   if constexpr (MODE == GATE_UP_FWD) {
-    const int64_t f = n0 + wn * 32 + ln;
-    if (f < g.F) {
+    // h, G and U tiles (128 rows x 64 columns each) -> LDS -> 16-byte row stores
+    bf16_t* th = smem;
+    bf16_t* tg = smem + BM * kHP;
+    bf16_t* tu = smem + 2 * BM * kHP;
+    const int fl = wn * 32 + ln;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mrow(i, r);
+        const float gv = acc[i][0][r], uv = acc[i][1][r];
+        th[m * kHP + fl] = (bf16_t)f2bf(silu_f(gv) * uv);
+        tg[m * kHP + fl] = (bf16_t)f2bf(gv);
+        tu[m * kHP + fl] = (bf16_t)f2bf(uv);
+      }
+    __syncthreads();
+    for (int v = tid; v < 3 * BM * 8; v += kThreads) {
+      const int t = v / (BM * 8), w = v % (BM * 8);
+      const int row = w >> 3, c8 = (w & 7) * 8;
+      if (row >= rows_valid || n0 + c8 >= g.F) continue;
+      const uint4 val = *reinterpret_cast<const uint4*>(smem + t * BM * kHP + row * kHP + c8);
+      const int64_t grow = row0 + row;
+      bf16_t* dst = t == 0 ? g.C0 + grow * g.F + n0 + c8
+                           : g.C1 + grow * 2 * g.F + (t == 2 ? g.F : 0) + n0 + c8;
+      *reinterpret_cast<uint4*>(dst) = val;
+    }
+  } else if constexpr (MODE == DOWN_FWD || MODE == GATE_UP_BWD_DATA) {
+    bf16_t* ct = smem;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ct[mrow(i, r) * kCP + brow(j) + ln] = (bf16_t)f2bf(acc[i][j][r]);
+    __syncthreads();
+    for (int v = tid; v < BM * (BN / 8); v += kThreads) {
+      const int row = v / (BN / 8), c8 = (v % (BN / 8)) * 8;
+      if (row >= rows_valid || n0 + c8 >= g.N) continue;
+      *reinterpret_cast<uint4*>(g.C0 + (row0 + row) * g.N + n0 + c8) =
+          *reinterpret_cast<const uint4*>(ct + row * kCP + c8);
+    }
+  } else if constexpr (MODE == DOWN_BWD_DATA) {
+    // SwiGLU backward: the saved G and U of this tile come in as 16-byte rows
+    // through LDS; dG and dU replace them in place and leave as 16-byte rows.
+    bf16_t* tg = smem;
+    bf16_t* tu = smem + BM * kCP;
+    for (int v = tid; v < 2 * BM * (BN / 8); v += kThreads) {
+      const int t = v / (BM * (BN / 8)), w = v % (BM * (BN / 8));
+      const int row = w / (BN / 8), c8 = (w % (BN / 8)) * 8;
+      const int rr = row < rows_valid ? row : rows_valid - 1;
+      const int64_t col = n0 + c8 < g.N ? n0 + c8 : g.N - 8;
+      *reinterpret_cast<uint4*>(smem + t * BM * kCP + row * kCP + c8) =
+          *reinterpret_cast<const uint4*>(g.aux + (row0 + rr) * 2 * g.F + (t ? g.F : 0) + col);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
-          if (m < rows_valid) {
-            const float gv = acc[i][0][r], uv = acc[i][1][r];
-            const int64_t row = row0 + m;
-            g.C0[row * g.F + f] = (bf16_t)f2bf(silu_f(gv) * uv);
-            g.C1[row * 2 * g.F + f] = (bf16_t)f2bf(gv);
-            g.C1[row * 2 * g.F + g.F + f] = (bf16_t)f2bf(uv);
-          }
+          const int o = mrow(i, r) * kCP + brow(j) + ln;
+          const float gv = bf2f(tg[o]), uv = bf2f(tu[o]);
+          const float c = acc[i][j][r];
+          const float sg = 1.0f / (1.0f + __expf(-gv));
+          tg[o] = (bf16_t)f2bf(c * uv * sg * (1.0f + gv * (1.0f - sg)));
+          tu[o] = (bf16_t)f2bf(c * (gv * sg));
         }
+    __syncthreads();
+    for (int v = tid; v < 2 * BM * (BN / 8); v += kThreads) {
+      const int t = v / (BM * (BN / 8)), w = v % (BM * (BN / 8));
+      const int row = w / (BN / 8), c8 = (w % (BN / 8)) * 8;
+      if (row >= rows_valid || n0 + c8 >= g.N) continue;
+      *reinterpret_cast<uint4*>(g.C0 + (row0 + row) * 2 * g.F + (t ? g.F : 0) + n0 + c8) =
+          *reinterpret_cast<const uint4*>(smem + t * BM * kCP + row * kCP + c8);
     }
   } else {
+    // weight gradients, fp32: each half-wave store is a full 128-byte row run
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t n = n0 + brow(j) + ln;
@@ -375,21 +452,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int m = wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+          const int m = mrow(i, r);
           if (m >= rows_valid) continue;
           const float c = acc[i][j][r];
-          if constexpr (MODE == DOWN_FWD || MODE == GATE_UP_BWD_DATA) {
-            g.C0[(row0 + m) * g.N + n] = (bf16_t)f2bf(c);
-          } else if constexpr (MODE == DOWN_BWD_DATA) {
-            const int64_t row = row0 + m;
-            const float gv = bf2f(g.aux[row * 2 * g.F + n]);
-            const float uv = bf2f(g.aux[row * 2 * g.F + g.F + n]);
-            const float sg = 1.0f / (1.0f + __expf(-gv));
-            const float dg = c * uv * sg * (1.0f + gv * (1.0f - sg));
-            const float du = c * (gv * sg);
-            g.C0[row * 2 * g.F + n] = (bf16_t)f2bf(dg);
-            g.C0[row * 2 * g.F + g.F + n] = (bf16_t)f2bf(du);
-          } else if constexpr (MODE == DOWN_BWD_W) {
+          if constexpr (MODE == DOWN_BWD_W) {
             g.W0[(int64_t)e * g.M * g.N + (row0 + m) * g.N + n] = c;
           } else {  // GATE_UP_BWD_W: rows [0, F) -> dWg, [F, 2F) -> dWu
             const int64_t jrow = row0 + m;
