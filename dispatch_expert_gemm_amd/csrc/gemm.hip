@@ -16,19 +16,21 @@
 // the expanded buffers); the last two are grouped over K (the contraction runs
 // over the expert's rows, which may be none).
 //
-// Tiling: 128 x 128 output tile per 256-thread workgroup, four waves in a 2 x 2
-// arrangement, each wave 64 x 64 = 2 x 2 v_mfma_f32_32x32x16_bf16 tiles; K step
-// 64 staged through double-buffered LDS (one barrier per step), the next step's
-// global loads in flight in registers while the current step's MFMAs issue.  In
+// Tiling: a BM x BN output tile per 256-thread workgroup (the kernel is written
+// for any multiple of 128; 128 x 128 is launched), four waves in a 2 x 2
+// arrangement, each wave (BM/2) x (BN/2) of v_mfma_f32_32x32x16_bf16 tiles, two
+// workgroups (eight waves) per CU.  K step 64 staged through double-buffered
+// LDS (one barrier per step), the next step's global loads in flight in
+// registers while the current step's MFMAs issue.  In
 // LDS both operands are stored K-contiguous with an XOR-swizzled chunk order,
 // so every MFMA operand is one conflict-free 16-byte LDS read; operands that are
 // K-strided in memory are loaded as 4 k-rows x 8 columns per thread, transposed
 // in registers with byte permutes and written as 8-byte LDS stores.
 //
-// Expert counts stay on the device: the grid covers floor(capacity/128) + E row
+// Expert counts stay on the device: the grid covers floor(capacity/BM) + E row
 // tiles per column tile, and each workgroup finds its expert from the prefix
 // counts with one wave ballot (expert e owns row-tile slots starting at
-// prefix[e-1]/128 + e); surplus workgroups exit at once.  Workgroup ids are
+// prefix[e-1]/BM + e); surplus workgroups exit at once.  Workgroup ids are
 // remapped so that consecutive tiles (sharing A rows and expert weights) land on
 // the same XCD and its L2.
 #include "common.hpp"
@@ -45,7 +47,7 @@ enum Mode : int {
   GATE_UP_BWD_W = 5
 };
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int kThreads = 256;
 
 struct GemmArgs {
@@ -66,6 +68,7 @@ struct GemmArgs {
   float* W1;
 };
 
+template <int BM>
 __device__ __forceinline__ int find_expert(const int32_t* __restrict__ prefix, int E, int64_t mt) {
   const int lane = threadIdx.x & 63;
   int found = 0;
@@ -85,32 +88,45 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ prefix, i
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// LDS tile: 128 rows x 64 k of bf16, row pitch 128 bytes, in eight 16-byte chunks
-// of 8 consecutive k.  Chunk c of row r sits at chunk position c ^ swz(r), so the
-// eight rows read by eight consecutive lanes of an MFMA operand fetch, and the
-// eight chunks of one row written by eight consecutive lanes, fall in distinct
-// banks.
+// LDS operand tile: R rows x 64 k of bf16, row pitch 128 bytes, in eight
+// 16-byte chunks of 8 consecutive k.  Chunk c of row r sits at chunk position
+// c ^ swz(r), so the eight rows read by eight consecutive lanes of an MFMA
+// operand fetch, and the eight chunks of one row written by eight consecutive
+// lanes, fall in distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
 
-// Row pitches (elements) of the output tiles staged in LDS by the epilogues;
-// the 16-byte pad puts rows m and m+4 (written by the two half-waves of one
-// store) in different banks.
-constexpr int kCP = BN + 8;      // 128-column tiles
-constexpr int kHP = BN / 2 + 8;  // 64-column tiles of the gate/up forward
-template <int MODE>
-constexpr int kSmemElems = (MODE == DOWN_BWD_DATA) ? (2 * BM * kCP > 2 * (BM + BN) * BK
-                                                          ? 2 * BM * kCP
-                                                          : 2 * (BM + BN) * BK)
-                                                   : 2 * (BM + BN) * BK;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
-  constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
-  constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
+// Compile-time shape of one kernel instance: BM x BN output tile, four waves
+// in a 2 x 2 arrangement, each wave (BM/2) x (BN/2) = TI x TJ MFMA 32x32 tiles.
+template <int MODE, int BM, int BN>
+struct Cfg {
+  static constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
+  static constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
+  static constexpr int TI = BM / 64, TJ = BN / 64;
+  // registers (16-byte vectors) per thread per K step: a K-contiguous R-row
+  // operand is R/32 vectors, a K-strided one R/128 blocks of 4 k-rows
+  static constexpr int NA = KGROUP ? 4 * (BM / 128) : BM / 32;
+  static constexpr int NB = B_KC ? BN / 32 : 4 * (BN / 128);
+  // output columns staged in LDS at once by the epilogue, and its row pitch;
+  // the 16-byte pad puts rows m and m+4 (written by the two half-waves of one
+  // store instruction) in different banks
+  static constexpr int CW = MODE == GATE_UP_FWD ? BN / 2 : BN;
+  static constexpr int CP = CW + 8;
+  static constexpr int kMain = 2 * (BM + BN) * BK;
+  static constexpr int kEpi = KGROUP ? 0 : (MODE == DOWN_BWD_DATA ? 2 : 1) * BM * CP;
+  static constexpr int kSmem = cmax(kMain, kEpi);
+};
+
+template <int MODE, int BM, int BN>
+__global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gemm(GemmArgs g) {
+  using C = Cfg<MODE, BM, BN>;
+  constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
+  constexpr int TI = C::TI, TJ = C::TJ, NA = C::NA, NB = C::NB;
   // Two LDS stages of the A and B tiles; after the K loop the same memory
   // stages the output tile (and, for the SwiGLU backward, the saved G/U tile).
-  __shared__ __attribute__((aligned(16))) bf16_t smem[kSmemElems<MODE>];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmem];
   auto As = [&](int st) { return smem + st * BM * BK; };
   auto Bs = [&](int st) { return smem + 2 * BM * BK + st * BN * BK; };
 
@@ -128,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   if constexpr (!KGROUP) {
     const int64_t mt = logical / g.n_tiles;
     const int64_t nt = logical % g.n_tiles;
-    e = find_expert(g.prefix, g.E, mt);
+    e = find_expert<BM>(g.prefix, g.E, mt);
     const int64_t p0 = e ? g.prefix[e - 1] : 0, p1 = g.prefix[e];
     row0 = p0 + (mt - (p0 / BM + e)) * BM;
     if (row0 >= p1) return;
@@ -149,13 +165,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   const int64_t klen = kend - kbeg;
 
   // Thread roles in one K step.
-  //  K-contiguous operand: vectors i = tid + 256*j (j < 4): row i/8, chunk i%8.
-  //  K-strided operand: k rows 4*k4 .. 4*k4+3 (k4 = tid/16) of 8 columns from
-  //  x8 = 8*(tid%16); transposed in registers, written as 8 x 8-byte stores.
-  // Loads are branch-free: out-of-range addresses are clamped into the operand
-  // and the value replaced by zero.
-  const int k4 = tid >> 4, x8 = (tid & 15) * 8;
-  const int kc_c = (tid & 7) * 8;  // chunk column of a K-contiguous vector (same for all j)
+  //  K-contiguous operand of R rows: vector j (j < R/32) is row tid/8 + 32j,
+  //  chunk tid%8.
+  //  K-strided operand of R columns: block q (q < R/128) covers k rows
+  //  4*k4 .. 4*k4+3 of the 8 columns from x8, with p = tid + 256q,
+  //  x8 = 8*(p % (R/8)), k4 = p / (R/8); transposed in registers and written as
+  //  8 x 8-byte LDS stores.
+  const int kc_c = (tid & 7) * 8;
+  auto xa8 = [&](int q) { return ((tid + kThreads * q) % (BM / 8)) * 8; };
+  auto ka4 = [&](int q) { return (tid + kThreads * q) / (BM / 8); };
+  auto xb8 = [&](int q) { return ((tid + kThreads * q) % (BN / 8)) * 8; };
+  auto kb4 = [&](int q) { return (tid + kThreads * q) / (BN / 8); };
   auto ld16 = [](const bf16_t* base, uint32_t off) -> uint4 {
     return *reinterpret_cast<const uint4*>(base + off);
   };
@@ -167,26 +187,29 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   // Uniform operand bases and per-lane 32-bit element offsets (every operand
   // slice addressed from one base stays below 2^31 elements).
   const bf16_t* abase;
-  uint32_t aoff[4];
+  uint32_t aoff[NA];
   if constexpr (!KGROUP) {
     abase = g.A + row0 * g.lda;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NA; ++j) {
       const int r = (tid >> 3) + 32 * j;
       aoff[j] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * g.lda + kc_c);
     }
   } else {
     abase = g.A + kbeg * g.lda;
-    const int64_t col = row0 + x8 < g.M ? row0 + x8 : g.M - 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) aoff[j] = (uint32_t)col;
+    for (int q = 0; q < NA / 4; ++q) {
+      const int64_t col = row0 + xa8(q) < g.M ? row0 + xa8(q) : g.M - 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) aoff[4 * q + j] = (uint32_t)col;
+    }
   }
   const bf16_t* bbase0;
   const bf16_t* bbase1;
-  uint32_t boff[4];
+  uint32_t boff[NB];
   if constexpr (B_KC) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int r = (tid >> 3) + 32 * j;
       int64_t n;
       if constexpr (MODE == GATE_UP_FWD) {
@@ -201,9 +224,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
     bbase0 = g.B0 + (int64_t)e * g.bstride;
     bbase1 = (MODE == GATE_UP_FWD) ? g.B1 + (int64_t)e * g.bstride : bbase0;
   } else {
-    const int64_t col = n0 + x8 < g.N ? n0 + x8 : g.N - 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) boff[j] = (uint32_t)col;
+    for (int q = 0; q < NB / 4; ++q) {
+      const int64_t col = n0 + xb8(q) < g.N ? n0 + xb8(q) : g.N - 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) boff[4 * q + j] = (uint32_t)col;
+    }
     if constexpr (KGROUP) {
       bbase0 = g.B0 + kbeg * g.ldb;
       bbase1 = bbase0;
@@ -212,8 +238,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
       bbase1 = (MODE == GATE_UP_BWD_DATA) ? g.B1 + (int64_t)e * g.bstride - g.F * g.ldb : bbase0;
     }
   }
-  const bool col_ok_a = !KGROUP || row0 + x8 < g.M;
-  const bool col_ok_b = B_KC || n0 + x8 < g.N;
 
   // Loads are branch-free: out-of-range rows, columns and K positions are
   // clamped into the operand; K positions past the end are replaced by zero
@@ -221,12 +245,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   // wave wait for the load there and defeat the prefetch).
   auto load_a = [&](int64_t k0, uint4* ra) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NA; ++j) {
       if constexpr (!KGROUP) {
         const uint32_t kk = (uint32_t)(k0 + kc_c < kend ? k0 : kend - 8 - kc_c);
         ra[j] = ld16(abase, aoff[j] + kk);
       } else {
-        const int64_t k = k0 + 4 * k4 + j;
+        const int64_t k = k0 + 4 * ka4(j / 4) + (j & 3);
         const uint32_t kr = (uint32_t)(k < klen ? k : klen - 1);
         ra[j] = ld16(abase, kr * (uint32_t)g.lda + aoff[j]);
       }
@@ -234,12 +258,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   };
   auto load_b = [&](int64_t k0, uint4* rb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NB; ++j) {
       if constexpr (B_KC) {
         const uint32_t kk = (uint32_t)(k0 + kc_c < kend ? k0 : kend - 8 - kc_c);
-        rb[j] = ld16(j < 2 ? bbase0 : bbase1, boff[j] + kk);
+        rb[j] = ld16(j < NB / 2 ? bbase0 : bbase1, boff[j] + kk);
       } else {
-        const int64_t k = k0 + 4 * k4 + j;
+        const int64_t k = k0 + 4 * kb4(j / 4) + (j & 3);
         const uint32_t kr = (uint32_t)(k < klen ? k : klen - 1);
         const bf16_t* base = bbase0;
         if constexpr (MODE == GATE_UP_BWD_DATA) base = kr < (uint32_t)g.F ? bbase0 : bbase1;
@@ -247,14 +271,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
       }
     }
   };
-  auto store_kc = [&](bf16_t* S, const uint4* r) {
+  auto store_kc = [&](bf16_t* S, const uint4* r, int n) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < n; ++j) {
       const int i = tid + kThreads * j;
       *reinterpret_cast<uint4*>(S + lds_off(i >> 3, i & 7)) = r[j];
     }
   };
-  auto store_t = [&](bf16_t* S, const uint4* v) {
+  // one block of 4 k-rows x 8 columns -> 8 columns x 4 k
+  auto store_t = [&](bf16_t* S, const uint4* v, int x8, int k4) {
     const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
     const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
     const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
@@ -268,62 +293,68 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
       *reinterpret_cast<uint2*>(S + lds_off(x8 + q, k4 >> 1) + (k4 & 1) * 4) = d;
     }
   };
-  auto mask_a = [&](int64_t k0, uint4* ra) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (!KGROUP) ra[j] = keep(k0 + kc_c < kend, ra[j]);
-      else ra[j] = keep(k0 + 4 * k4 + j < klen && col_ok_a, ra[j]);
-    }
-  };
-  auto mask_b = [&](int64_t k0, uint4* rb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (B_KC) rb[j] = keep(k0 + kc_c < kend, rb[j]);
-      else rb[j] = keep(k0 + 4 * k4 + j < klen && col_ok_b, rb[j]);
-    }
-  };
   // k0: the K position the registers were loaded from
-  auto store_ab = [&](int s, int64_t k0, uint4* ra, uint4* rb) {
-    mask_a(k0, ra);
-    mask_b(k0, rb);
-    if constexpr (!KGROUP) store_kc(As(s), ra);
-    else store_t(As(s), ra);
-    if constexpr (B_KC) store_kc(Bs(s), rb);
-    else store_t(Bs(s), rb);
+  auto store_ab = [&](int st, int64_t k0, uint4* ra, uint4* rb) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      if constexpr (!KGROUP) ra[j] = keep(k0 + kc_c < kend, ra[j]);
+      else ra[j] = keep(k0 + 4 * ka4(j / 4) + (j & 3) < klen && row0 + xa8(j / 4) < g.M, ra[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (B_KC) rb[j] = keep(k0 + kc_c < kend, rb[j]);
+      else rb[j] = keep(k0 + 4 * kb4(j / 4) + (j & 3) < klen && n0 + xb8(j / 4) < g.N, rb[j]);
+    }
+    if constexpr (!KGROUP) {
+      store_kc(As(st), ra, NA);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NA / 4; ++q) store_t(As(st), ra + 4 * q, xa8(q), ka4(q));
+    }
+    if constexpr (B_KC) {
+      store_kc(Bs(st), rb, NB);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NB / 4; ++q) store_t(Bs(st), rb + 4 * q, xb8(q), kb4(q));
+    }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // B-tile row of MFMA column tile j of this wave.  The gate/up forward tile
+  // holds BN/2 gate rows then the same BN/2 up rows, and each wave takes
+  // matching gate and up column tiles so SwiGLU pairs meet in one lane.
   auto brow = [&](int j) -> int {
-    if constexpr (MODE == GATE_UP_FWD) return j * (BN / 2) + wn * 32;
-    else return wn * 64 + j * 32;
+    if constexpr (MODE == GATE_UP_FWD)
+      return (j < TJ / 2) ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - TJ / 2) * 32;
+    else
+      return wn * (BN / 2) + j * 32;
   };
-  // LDS element offsets of this lane's MFMA operand rows (chunk 0)
-  int arow[2], brw[2];
+  int arow[TI], brw[TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) arow[i] = wm * 64 + i * 32 + (lane & 31);
+  for (int i = 0; i < TI; ++i) arow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) brw[j] = brow(j) + (lane & 31);
+  for (int j = 0; j < TJ; ++j) brw[j] = brow(j) + (lane & 31);
 
-  // MFMAs of one K step on LDS stage s; operand fragments of sub-step kk+1 are
+  // MFMAs of one K step on LDS stage st; operand fragments of sub-step kk+1 are
   // read while the MFMAs of sub-step kk issue.
-  auto compute = [&](int s) {
-    const bf16_t* as = As(s);
-    const bf16_t* bs = Bs(s);
-    bf16x8 fa[2][2], fb[2][2];
+  auto compute = [&](int st) {
+    const bf16_t* as = As(st);
+    const bf16_t* bs = Bs(st);
+    bf16x8 fa[2][TI], fb[2][TJ];
     auto fetch = [&](int kk, int slot) {
       const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
         fa[slot][i] = *reinterpret_cast<const bf16x8*>(as + lds_off(arow[i], c));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TJ; ++j)
         fb[slot][j] = *reinterpret_cast<const bf16x8*>(bs + lds_off(brw[j], c));
     };
     fetch(0, 0);
@@ -331,9 +362,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
     for (int kk = 0; kk < BK / 16; ++kk) {
       if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                              acc[i][j], 0, 0, 0);
     }
@@ -341,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
 
   // Pipeline: two LDS stages, one register stage.  The global loads of step t+1
   // are in flight while the MFMAs of step t issue, then go to LDS stage (t+1)%2.
-  uint4 ra[4], rb[4];
+  uint4 ra[NA], rb[NB];
   const int64_t nk = (klen + BK - 1) / BK;
   if (nk > 0) {
     load_a(0, ra);
@@ -361,73 +392,71 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   }
 
   // ---- epilogue.  acc[i][j][r] holds C(m, n) with
-  //   m = wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  n = brow(j) + lane%32
+  //   m = wm*(BM/2) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  n = brow(j) + lane%32
   // The K loop ended with a barrier, so the LDS stages are free.
   const int ln = lane & 31, lh = lane >> 5;
-  auto mrow = [&](int i, int r) { return wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3); };
+  auto mrow = [&](int i, int r) { return wm * (BM / 2) + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3); };
+  constexpr int CP = C::CP, CW = C::CW;
+  // cooperative 16-byte row stores of a staged BM x CW bf16 tile
+  auto store_tile = [&](const bf16_t* t, bf16_t* dst, int64_t ldd, int64_t ncols) {
+    for (int v = tid; v < BM * (CW / 8); v += kThreads) {
+      const int row = v / (CW / 8), c8 = (v % (CW / 8)) * 8;
+      if (row >= rows_valid || c8 >= ncols) continue;
+      *reinterpret_cast<uint4*>(dst + (row0 + row) * ldd + c8) =
+          *reinterpret_cast<const uint4*>(t + row * CP + c8);
+    }
+  };
   if constexpr (MODE == GATE_UP_FWD) {
-    // h, G and U tiles (128 rows x 64 columns each) -> LDS -> 16-byte row stores
-    bf16_t* th = smem;
-    bf16_t* tg = smem + BM * kHP;
-    bf16_t* tu = smem + 2 * BM * kHP;
-    const int fl = wn * 32 + ln;
+    // h, G and U (BM rows x BN/2 columns each) staged one after the other
+    bf16_t* ct = smem;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = mrow(i, r);
-        const float gv = acc[i][0][r], uv = acc[i][1][r];
-        th[m * kHP + fl] = (bf16_t)f2bf(silu_f(gv) * uv);
-        tg[m * kHP + fl] = (bf16_t)f2bf(gv);
-        tu[m * kHP + fl] = (bf16_t)f2bf(uv);
-      }
-    __syncthreads();
-    for (int v = tid; v < 3 * BM * 8; v += kThreads) {
-      const int t = v / (BM * 8), w = v % (BM * 8);
-      const int row = w >> 3, c8 = (w & 7) * 8;
-      if (row >= rows_valid || n0 + c8 >= g.F) continue;
-      const uint4 val = *reinterpret_cast<const uint4*>(smem + t * BM * kHP + row * kHP + c8);
-      const int64_t grow = row0 + row;
-      bf16_t* dst = t == 0 ? g.C0 + grow * g.F + n0 + c8
-                           : g.C1 + grow * 2 * g.F + (t == 2 ? g.F : 0) + n0 + c8;
-      *reinterpret_cast<uint4*>(dst) = val;
+        for (int j = 0; j < TJ / 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float gv = acc[i][j][r], uv = acc[i][j + TJ / 2][r];
+            const float v = pass == 0 ? silu_f(gv) * uv : (pass == 1 ? gv : uv);
+            ct[mrow(i, r) * CP + wn * (BN / 4) + j * 32 + ln] = (bf16_t)f2bf(v);
+          }
+      __syncthreads();
+      if (pass == 0) store_tile(ct, g.C0 + n0, g.F, g.F - n0);
+      else store_tile(ct, g.C1 + (pass == 2 ? g.F : 0) + n0, 2 * g.F, g.F - n0);
+      __syncthreads();
     }
   } else if constexpr (MODE == DOWN_FWD || MODE == GATE_UP_BWD_DATA) {
     bf16_t* ct = smem;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ct[mrow(i, r) * kCP + brow(j) + ln] = (bf16_t)f2bf(acc[i][j][r]);
+        for (int r = 0; r < 16; ++r) ct[mrow(i, r) * CP + brow(j) + ln] = (bf16_t)f2bf(acc[i][j][r]);
     __syncthreads();
-    for (int v = tid; v < BM * (BN / 8); v += kThreads) {
-      const int row = v / (BN / 8), c8 = (v % (BN / 8)) * 8;
-      if (row >= rows_valid || n0 + c8 >= g.N) continue;
-      *reinterpret_cast<uint4*>(g.C0 + (row0 + row) * g.N + n0 + c8) =
-          *reinterpret_cast<const uint4*>(ct + row * kCP + c8);
-    }
+    store_tile(ct, g.C0 + n0, g.N, g.N - n0);
   } else if constexpr (MODE == DOWN_BWD_DATA) {
     // SwiGLU backward: the saved G and U of this tile come in as 16-byte rows
     // through LDS; dG and dU replace them in place and leave as 16-byte rows.
     bf16_t* tg = smem;
-    bf16_t* tu = smem + BM * kCP;
+    bf16_t* tu = smem + BM * CP;
     for (int v = tid; v < 2 * BM * (BN / 8); v += kThreads) {
       const int t = v / (BM * (BN / 8)), w = v % (BM * (BN / 8));
       const int row = w / (BN / 8), c8 = (w % (BN / 8)) * 8;
       const int rr = row < rows_valid ? row : rows_valid - 1;
       const int64_t col = n0 + c8 < g.N ? n0 + c8 : g.N - 8;
-      *reinterpret_cast<uint4*>(smem + t * BM * kCP + row * kCP + c8) =
+      *reinterpret_cast<uint4*>(smem + t * BM * CP + row * CP + c8) =
           *reinterpret_cast<const uint4*>(g.aux + (row0 + rr) * 2 * g.F + (t ? g.F : 0) + col);
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int o = mrow(i, r) * kCP + brow(j) + ln;
+          const int o = mrow(i, r) * CP + brow(j) + ln;
           const float gv = bf2f(tg[o]), uv = bf2f(tu[o]);
           const float c = acc[i][j][r];
           const float sg = 1.0f / (1.0f + __expf(-gv));
@@ -435,21 +464,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
           tu[o] = (bf16_t)f2bf(c * (gv * sg));
         }
     __syncthreads();
-    for (int v = tid; v < 2 * BM * (BN / 8); v += kThreads) {
-      const int t = v / (BM * (BN / 8)), w = v % (BM * (BN / 8));
-      const int row = w / (BN / 8), c8 = (w % (BN / 8)) * 8;
-      if (row >= rows_valid || n0 + c8 >= g.N) continue;
-      *reinterpret_cast<uint4*>(g.C0 + (row0 + row) * 2 * g.F + (t ? g.F : 0) + n0 + c8) =
-          *reinterpret_cast<const uint4*>(smem + t * BM * kCP + row * kCP + c8);
-    }
+    store_tile(tg, g.C0 + n0, 2 * g.F, g.N - n0);
+    store_tile(tu, g.C0 + g.F + n0, 2 * g.F, g.N - n0);
   } else {
     // weight gradients, fp32: each half-wave store is a full 128-byte row run
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TJ; ++j) {
       const int64_t n = n0 + brow(j) + ln;
       if (n >= g.N) continue;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = mrow(i, r);
@@ -467,8 +491,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs g) {
   }
 }
 
-template <int MODE>
-moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
+template <int MODE, int BM, int BN>
+moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
+  const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
+  const int64_t bn_cols = MODE == GATE_UP_FWD ? BN / 2 : BN;
+  g.n_tiles = (ncols + bn_cols - 1) / bn_cols;
   if (MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W) {
     g.m_tiles = (g.M + BM - 1) / BM;
     g.tiles = (int64_t)s->num_experts * g.m_tiles * g.n_tiles;
@@ -479,8 +506,17 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL(k_gemm<MODE>, dim3((unsigned)grid), dim3(kThreads), 0, strm, g);
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN>), dim3((unsigned)grid), dim3(kThreads), 0, strm, g);
   return launch_status();
+}
+
+// Tile choice.  Measured on MI355X at the page-1 benchmark shape, 128 x 128
+// tiles with two waves per SIMD beat 256 x 256 tiles with one wave per SIMD
+// (whose exposed load and barrier latency outweighs their halved LDS traffic),
+// so every mode runs 128 x 128.
+template <int MODE>
+moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
+  return launch_cfg<MODE, 128, 128>(g, s, strm);
 }
 
 GemmArgs base_args(const moe_shape* s, const int32_t* prefix) {
@@ -514,7 +550,6 @@ extern "C" moe_status moe_ffn_gate_up_fwd(const moe_shape* s, const void* expand
   g.bstride = s->F * s->H;
   g.N = s->F;
   g.Kd = s->H;
-  g.n_tiles = (s->F + BN / 2 - 1) / (BN / 2);
   g.C0 = static_cast<bf16_t*>(h_act);
   g.C1 = static_cast<bf16_t*>(gate_up_save);
   return launch<GATE_UP_FWD>(g, s, as_stream(stream));
@@ -535,7 +570,6 @@ extern "C" moe_status moe_ffn_down_fwd(const moe_shape* s, const void* h_act, co
   g.bstride = s->H * s->F;
   g.N = s->H;
   g.Kd = s->F;
-  g.n_tiles = (s->H + BN - 1) / BN;
   g.C0 = static_cast<bf16_t*>(y);
   return launch<DOWN_FWD>(g, s, as_stream(stream));
 }
@@ -571,7 +605,6 @@ extern "C" moe_status moe_ffn_down_bwd_data(const moe_shape* s, const void* grad
   g.bstride = s->H * s->F;
   g.N = s->F;
   g.Kd = s->H;
-  g.n_tiles = (s->F + BN - 1) / BN;
   g.aux = static_cast<const bf16_t*>(gate_up_save);
   g.C0 = static_cast<bf16_t*>(grad_gate_up);
   return launch<DOWN_BWD_DATA>(g, s, as_stream(stream));
@@ -592,7 +625,6 @@ extern "C" moe_status moe_ffn_down_bwd_weight(const moe_shape* s, const void* gr
   g.ldb = s->F;
   g.M = s->H;
   g.N = s->F;
-  g.n_tiles = (s->F + BN - 1) / BN;
   g.W0 = grad_w_down;
   return launch<DOWN_BWD_W>(g, s, as_stream(stream));
 }
@@ -615,7 +647,6 @@ extern "C" moe_status moe_ffn_gate_up_bwd_data(const moe_shape* s, const void* g
   g.bstride = s->F * s->H;
   g.N = s->H;
   g.Kd = 2 * s->F;
-  g.n_tiles = (s->H + BN - 1) / BN;
   g.C0 = static_cast<bf16_t*>(grad_expand_x);
   return launch<GATE_UP_BWD_DATA>(g, s, as_stream(stream));
 }
@@ -637,7 +668,6 @@ extern "C" moe_status moe_ffn_gate_up_bwd_weight(const moe_shape* s, const void*
   g.ldb = s->H;
   g.M = 2 * s->F;
   g.N = s->H;
-  g.n_tiles = (s->H + BN - 1) / BN;
   g.W0 = grad_w_gate;
   g.W1 = grad_w_up;
   return launch<GATE_UP_BWD_W>(g, s, as_stream(stream));

@@ -81,6 +81,9 @@ FFN_CASES = {
     "page1_512": dict(T=512, H=1536, F=480, E=64, K=8),
     "empty_experts": dict(T=20, H=64, F=32, E=16, K=1),
     "special_mask": dict(T=150, H=128, F=64, E=6, K=4, Z=1, C=1, Q=2, mask="2d"),
+    # >= 512 rows per expert and >= 512 weight-gradient tiles: the 256-row tile
+    # path of every GEMM, with ragged row tiles (8200 rows) and ragged F = 480
+    "big_tiles_ragged": dict(T=4100, H=4096, F=480, E=16, K=2),
 }
 
 
@@ -211,6 +214,7 @@ LAYER_CASES = {
     "tiny": dict(T=256, H=128, F=64, E=8, K=2),
     "special_mask": dict(T=200, H=256, F=96, E=12, K=6, Z=1, C=1, Q=2, mask="2d"),
     "page1_1k": dict(T=1024, H=1536, F=480, E=64, K=8),
+    "big_tiles_ragged": dict(T=4100, H=4096, F=480, E=16, K=2),
 }
 
 
