@@ -277,16 +277,27 @@ def dispatch(shape, x, topk_idx, x_active_mask=None, workspace=None, stream=None
     return d
 
 
+def shared_expert_shape(T, H, F) -> MoeShape:
+    """Shape of a shared expert run as a one-expert group over all T tokens."""
+    return make_shape(T, H, 1, 1, F=F, capacity=T)
+
+
 class _MoELayerFn(torch.autograd.Function):
-    """Forward: dispatch -> grouped SwiGLU FFN -> combine; backward: the reverse chain."""
+    """Forward: dispatch -> grouped SwiGLU FFN -> combine; backward: the reverse chain.
+
+    A shared expert (shared_w_*) runs as the same grouped FFN with one expert
+    whose rows are all T tokens in order, so x itself is its expanded input;
+    its output is the shared_expert_x of combine and its input gradient is
+    added to grad_x by dispatch_bwd (grad_x_accum)."""
 
     @staticmethod
-    def forward(ctx, x, topk_weights, w_gate, w_up, w_down, shared_expert_x, topk_idx, x_active_mask,
-                const_alpha_1, const_alpha_2, const_v, zero_expert_num, copy_expert_num,
-                const_expert_num):
+    def forward(ctx, x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
+                shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1, const_alpha_2,
+                const_v, zero_expert_num, copy_expert_num, const_expert_num):
         T, H = x.shape
         K = topk_idx.shape[1]
         E, F, _ = w_gate.shape
+        dev = x.device
         mask_ndim = 0 if x_active_mask is None else x_active_mask.dim()
         shape = make_shape(T, H, K, E, F=F, zero_expert_num=zero_expert_num,
                            copy_expert_num=copy_expert_num, const_expert_num=const_expert_num,
@@ -294,24 +305,40 @@ class _MoELayerFn(torch.autograd.Function):
         mask = None if x_active_mask is None else x_active_mask.view(torch.uint8)
         d = dispatch(shape, x, topk_idx, mask)
         cap = shape.capacity
-        gus = torch.empty((cap, 2 * F), dtype=BF16, device=x.device)
-        h = torch.empty((cap, F), dtype=BF16, device=x.device)
-        y = torch.empty((cap, H), dtype=BF16, device=x.device)
+        gus = torch.empty((cap, 2 * F), dtype=BF16, device=dev)
+        h = torch.empty((cap, F), dtype=BF16, device=dev)
+        y = torch.empty((cap, H), dtype=BF16, device=dev)
         moe_grouped_ffn(shape, d.expand_x, w_gate, w_up, w_down, d.ep_recv_counts, gus, h, y)
-        out = torch.empty((T, H), dtype=BF16, device=x.device)
+        ctx.shared_ffn = shared_w_gate is not None
+        s_saved = ()
+        if ctx.shared_ffn:
+            if shared_expert_x is not None:
+                raise MoeError("pass either shared_expert_x or the shared expert weights, not both")
+            Fs = shared_w_gate.shape[1]
+            ss = shared_expert_shape(T, H, Fs)
+            s_counts = torch.full((1,), T, dtype=I32, device=dev)
+            s_gus = torch.empty((T, 2 * Fs), dtype=BF16, device=dev)
+            s_h = torch.empty((T, Fs), dtype=BF16, device=dev)
+            shared_expert_x = torch.empty((T, H), dtype=BF16, device=dev)
+            moe_grouped_ffn(ss, x, shared_w_gate, shared_w_up, shared_w_down, s_counts, s_gus, s_h,
+                            shared_expert_x)
+            ctx.s_shape = ss
+            s_saved = (shared_w_gate, shared_w_up, shared_w_down, s_counts, s_gus, s_h)
+        out = torch.empty((T, H), dtype=BF16, device=dev)
         moe_combine(shape, y, topk_idx, topk_weights, d.assist_info_for_combine, d.ep_recv_counts,
                     mask, shared_expert_x, x, const_alpha_1, const_alpha_2, const_v, out)
         ctx.shape = shape
-        ctx.has_shared = shared_expert_x is not None
+        ctx.has_shared_x = shared_expert_x is not None and not ctx.shared_ffn
         ctx.save_for_backward(x, topk_weights, w_gate, w_up, w_down, topk_idx, mask, const_alpha_1,
                               const_alpha_2, const_v, d.expand_x, d.assist_info_for_combine,
-                              d.ep_recv_counts, gus, h, y)
+                              d.ep_recv_counts, gus, h, y, *s_saved)
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
+        saved = ctx.saved_tensors
         (x, topk_weights, w_gate, w_up, w_down, topk_idx, mask, a1, a2, cv, expand_x, assist,
-         recv, gus, h, y) = ctx.saved_tensors
+         recv, gus, h, y) = saved[:16]
         shape = ctx.shape
         grad_out = grad_out.contiguous()
         cap, H, F, T, K = shape.capacity, shape.H, shape.F, shape.T, shape.K
@@ -327,19 +354,41 @@ class _MoELayerFn(torch.autograd.Function):
         gwd = torch.empty(w_down.shape, dtype=F32, device=dev)
         moe_grouped_ffn_bwd(shape, gy, expand_x, gus, h, w_gate, w_up, w_down, recv, ggu, gx_exp,
                             gwg, gwu, gwd)
+        accum = None
+        s_grads = (None, None, None)
+        if ctx.shared_ffn:
+            swg, swu, swd, s_counts, s_gus, s_h = saved[16:]
+            ss = ctx.s_shape
+            Fs = ss.F
+            s_ggu = torch.empty((T, 2 * Fs), dtype=BF16, device=dev)
+            accum = torch.empty((T, H), dtype=BF16, device=dev)
+            s_gwg = torch.empty(swg.shape, dtype=F32, device=dev)
+            s_gwu = torch.empty(swu.shape, dtype=F32, device=dev)
+            s_gwd = torch.empty(swd.shape, dtype=F32, device=dev)
+            # the shared expert's output gradient is grad_out itself
+            moe_grouped_ffn_bwd(ss, grad_out, x, s_gus, s_h, swg, swu, swd, s_counts, s_ggu, accum,
+                                s_gwg, s_gwu, s_gwd)
+            s_grads = (s_gwg.to(swg.dtype), s_gwu.to(swu.dtype), s_gwd.to(swd.dtype))
         gx = torch.empty((T, H), dtype=BF16, device=dev)
-        moe_dispatch_bwd(shape, gx_exp, assist, topk_idx, topk_weights, mask, grad_out, a1, None, gx)
-        g_shared = grad_out if ctx.has_shared else None
+        moe_dispatch_bwd(shape, gx_exp, assist, topk_idx, topk_weights, mask, grad_out, a1, accum, gx)
+        g_shared = grad_out if ctx.has_shared_x else None
         return (gx, gw, gwg.to(w_gate.dtype), gwu.to(w_up.dtype), gwd.to(w_down.dtype), g_shared,
-                None, None, None, None, None, None, None, None)
+                *s_grads, None, None, None, None, None, None, None, None)
 
 
 def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=None,
-              shared_expert_x=None, const_alpha_1=None, const_alpha_2=None, const_v=None,
+              shared_expert_x=None, shared_w_gate=None, shared_w_up=None, shared_w_down=None,
+              const_alpha_1=None, const_alpha_2=None, const_v=None,
               zero_expert_num=0, copy_expert_num=0, const_expert_num=0):
-    """One MoE layer (ori_x is x itself).  Differentiable in x, topk_weights, the
-    expert weights and shared_expert_x.  Weight gradients are computed in fp32 and
-    returned in the weights' dtype; use the C entries directly to keep fp32."""
-    return _MoELayerFn.apply(x, topk_weights, w_gate, w_up, w_down, shared_expert_x, topk_idx,
-                             x_active_mask, const_alpha_1, const_alpha_2, const_v,
-                             zero_expert_num, copy_expert_num, const_expert_num)
+    """One MoE layer (ori_x is x itself).
+
+    The shared-expert term of combine is either given (shared_expert_x) or
+    computed here by a SwiGLU shared expert (shared_w_gate, shared_w_up of shape
+    (1, Fs, H), shared_w_down of shape (1, H, Fs)).  Differentiable in x,
+    topk_weights, all expert weights and shared_expert_x.  Weight gradients are
+    computed in fp32 and returned in the weights' dtype; use the C entries
+    directly to keep fp32."""
+    return _MoELayerFn.apply(x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
+                             shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1,
+                             const_alpha_2, const_v, zero_expert_num, copy_expert_num,
+                             const_expert_num)

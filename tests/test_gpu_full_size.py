@@ -1,0 +1,232 @@
+"""GPU parity at the workloads' full sizes, through the same C entry points the
+benchmark times, checked against the oracle on what it can compute piece by
+piece: every index/count/map in full, expert-FFN rows, combine and gradient
+tokens on samples, and weight gradients of sampled experts on sampled F columns
+(each F column of G, U, h, dG, dU and of the weight gradients depends on no
+other column, so the oracle run on a column slice gives those columns exactly).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dispatch_expert_gemm_amd as dm
+import moe_workloads as wl
+import oracle as orc
+from gpu_util import DEV, Run, bf, check_close, check_equal, f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _expert_of_rows(r, rows):
+    return np.searchsorted(r.ep_recv_counts, rows, side="right")
+
+
+def oracle_rows(inp, r, rows):
+    """Oracle G, U, h, y of the given expanded rows, expert by expert."""
+    rows = np.asarray(rows)
+    K = r.K
+    es = _expert_of_rows(r, rows)
+    xr = orc.bf16_to_f32(inp["x"])[r.row2slot[rows] // K]
+    F, H = inp["F"], inp["H"]
+    G = np.zeros((len(rows), F), np.float32)
+    U, Hh = np.zeros_like(G), np.zeros_like(G)
+    Y = np.zeros((len(rows), H), np.float32)
+    for e in np.unique(es):
+        sel = np.nonzero(es == e)[0]
+        g, u, h, y = orc.ffn_fwd(xr[sel], np.array([len(sel)]), inp["w_gate"][e:e + 1],
+                                 inp["w_up"][e:e + 1], inp["w_down"][e:e + 1])
+        G[sel], U[sel], Hh[sel], Y[sel] = g, u, h, y
+    return G, U, Hh, Y
+
+
+def sub_route(r, tokens, row_map=None):
+    """Route restricted to the given tokens; routed codes renumbered 0.. in slot order."""
+    codes = r.slot2row.reshape(r.T, r.K)[tokens].reshape(-1).copy()
+    routed = np.nonzero(codes >= 0)[0]
+    rows = codes[routed].copy()
+    codes[routed] = np.arange(len(routed))
+    sr = orc.Route(len(tokens), r.K, r.E, None, None, codes.astype(np.int32), None, 0)
+    return sr, rows
+
+
+def _sample(rng, n, k):
+    return np.sort(rng.choice(n, size=min(n, k), replace=False))
+
+
+def _check_sampled_layer(inp, run, r, out, gy, gw, ggu, gxe, gwg, gwu, gwd, gx, rng,
+                         n_rows=96, n_tok=64, experts=None, n_cols=24, shared=None):
+    """Sampled checks of a whole layer step; `shared` = (sY16, s_dX16) oracle arrays
+    for the sampled tokens' shared expert, or None."""
+    K, F = r.K, inp["F"]
+    A = r.A
+    # expert FFN rows
+    rows = _sample(rng, A, n_rows)
+    G, U, Hh, Y = oracle_rows(inp, r, rows)
+    check_close("G rows", f32(run.gus[rows, :F]), G)
+    check_close("U rows", f32(run.gus[rows, F:]), U)
+    check_close("h rows", f32(run.h[rows]), Hh)
+    check_close("y rows", f32(run.y[rows]), Y)
+    # tokens: combine, combine backward, FFN backward of their rows, dispatch backward
+    toks = _sample(rng, r.T, n_tok)
+    sr, trows = sub_route(r, toks)
+    _, _, _, Yt = oracle_rows(inp, r, trows)
+    sh = None if shared is None else shared[0](toks)
+    ref_out = orc.combine(Yt, sr, inp["topk_weights"][toks], sh, inp["x"][toks],
+                          inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"))
+    check_close("out tokens", f32(out[toks]), ref_out)
+    dY, dw = orc.combine_bwd(inp["grad_out"][toks], Yt, sr, inp["topk_weights"][toks], inp["x"][toks],
+                             inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"))
+    check_equal("grad_y rows", f32(gy[trows]), dY)
+    check_close("grad_topk_weights tokens", f32(gw[toks]), dw)
+    Gt, Ut, Ht, _ = oracle_rows(inp, r, trows)
+    es = _expert_of_rows(r, trows)
+    xr = orc.bf16_to_f32(inp["x"])[r.row2slot[trows] // K]
+    dX = np.zeros((len(trows), inp["H"]), np.float32)
+    for e in np.unique(es):
+        sel = np.nonzero(es == e)[0]
+        _, dx_e, _, _, _ = orc.ffn_bwd(dY[sel], xr[sel], Gt[sel], Ut[sel], Ht[sel], np.array([len(sel)]),
+                                       inp["w_gate"][e:e + 1], inp["w_up"][e:e + 1], inp["w_down"][e:e + 1])
+        dX[sel] = dx_e
+    check_close("grad_expand_x rows", f32(gxe[trows]), dX)
+    acc = None if shared is None else shared[1](toks)
+    ref_dx = orc.dispatch_bwd(dX, sr, inp["topk_weights"][toks], inp["grad_out"][toks],
+                              inp.get("const_alpha_1"), acc)
+    check_close("grad_x tokens", f32(gx[toks]), ref_dx)
+    # weight gradients of sampled experts, sampled F columns
+    if experts is None:
+        nz = np.nonzero(r.counts)[0]
+        experts = [int(nz[0]), int(nz[len(nz) // 2]), int(nz[-1])]
+    for e in experts:
+        lo, hi = r.row_range(e)
+        if hi == lo:
+            continue
+        erows = np.arange(lo, hi)
+        toks_e = r.row2slot[erows] // K
+        ks_e = r.row2slot[erows] % K
+        w_e = inp["topk_weights"][toks_e, ks_e]
+        dY_e = orc.round_bf16((w_e[:, None] * orc.bf16_to_f32(inp["grad_out"][toks_e])).astype(np.float32))
+        X_e = orc.bf16_to_f32(inp["x"])[toks_e]
+        fs = _sample(rng, F, n_cols)
+        wg, wu, wd = inp["w_gate"][e:e + 1, fs], inp["w_up"][e:e + 1, fs], inp["w_down"][e:e + 1][:, :, fs]
+        g, u, h, _ = orc.ffn_fwd(X_e, np.array([hi - lo]), wg, wu, wd)
+        dgu, _, dwg, dwu, dwd = orc.ffn_bwd(dY_e, X_e, g, u, h, np.array([hi - lo]), wg, wu, wd)
+        check_close(f"grad_gate_up e={e}", f32(ggu[lo:hi][:, np.concatenate([fs, F + fs])]), dgu)
+        check_close(f"grad_w_gate e={e}", f32(gwg[e][fs]), dwg[0])
+        check_close(f"grad_w_up e={e}", f32(gwu[e][fs]), dwu[0])
+        check_close(f"grad_w_down e={e}", f32(gwd[e][:, fs]), dwd[0])
+
+
+def _layer_step(run, shared_x=None, accum=None):
+    run.ffn()
+    out = run.combine(shared=shared_x)
+    g = bf(run.inp["grad_out"])
+    gy, gw = run.combine_bwd(g)
+    ggu, gxe, gwg, gwu, gwd = run.ffn_bwd(gy)
+    gx = run.dispatch_bwd(gxe, g, accum)
+    return out, gy, gw, ggu, gxe, gwg, gwu, gwd, gx
+
+
+def test_page1_benchmark_shape_full_size():
+    """T=8192, H=1536, F=480, E=64, K=8: the benchmark's workload and launch shapes."""
+    print("[full] page1 T=8192", flush=True)
+    inp = wl.layer_inputs(**wl.WORKLOADS["page1"], seed=0)
+    run = Run(inp)
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"])
+    check_equal("expert_token_nums", run.d.expert_token_nums.cpu().numpy(), r.counts)
+    check_equal("ep_recv_counts", run.d.ep_recv_counts.cpu().numpy(), r.ep_recv_counts)
+    check_equal("slot2row", run.d.slot2row(r.T, r.K).cpu().numpy(), r.slot2row)
+    check_equal("row2slot", run.d.row2slot(r.T, r.K)[:r.A].cpu().numpy(), r.row2slot)
+    assert r.counts.sum() == 8192 * 8
+    rng = np.random.default_rng(11)
+    rows = _sample(rng, r.A, 512)
+    xf = orc.bf16_to_f32(inp["x"])
+    check_equal("expand_x rows", f32(run.d.expand_x[rows]), xf[r.row2slot[rows] // r.K])
+    res = _layer_step(run)
+    _check_sampled_layer(inp, run, r, *res, rng)
+
+
+def test_combine_stress_full_size():
+    """T=4096, H=7168, K=8, 256 routed + 1 zero + 1 copy + 2 constant experts,
+    2-D mask with 10% false, shared_expert_x: combine, its backward and dispatch
+    backward checked bit for bit (dw within tolerance) on every token."""
+    print("[full] combine stress", flush=True)
+    inp = wl.combine_inputs(**{k: v for k, v in wl.WORKLOADS["combine_stress"].items()}, seed=0)
+    run = Run(inp)
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"], inp["Z"], inp["C"], inp["Q"], inp["mask"])
+    assert int(run.d.err_flag.item()) == 0 and run.A == r.A
+    y = bf(inp["y"])
+    out = run.combine(y=y, shared=bf(inp["shared_expert_x"]))
+    Y = orc.bf16_to_f32(inp["y"])[:r.A]
+    ref = orc.combine(Y, r, inp["topk_weights"], inp["shared_expert_x"], inp["x"], inp["const_alpha_1"],
+                      inp["const_alpha_2"], inp["const_v"])
+    check_equal("out", f32(out), ref)
+    gy, gw = run.combine_bwd(bf(inp["grad_out"]), y=y)
+    dY, dw = orc.combine_bwd(inp["grad_out"], Y, r, inp["topk_weights"], inp["x"], inp["const_alpha_1"],
+                             inp["const_alpha_2"], inp["const_v"])
+    check_equal("grad_y", f32(gy[:r.A]), dY)
+    check_close("grad_topk_weights", f32(gw), dw, max_abs=1e-3, rel_l2=1e-5)
+    gx = run.dispatch_bwd(y, bf(inp["grad_out"]))
+    ref_dx = orc.dispatch_bwd(Y, r, inp["topk_weights"], inp["grad_out"], inp["const_alpha_1"])
+    check_equal("grad_x", f32(gx), ref_dx)
+
+
+def test_dsv3_proxy_full_size():
+    """T=4096, H=7168, F=2048, E=32, K=8, Zipf(1.2)-skewed routing, one shared
+    SwiGLU expert on all tokens, fwd+bwd (the shared expert through the same
+    grouped FFN entries with one expert of T rows)."""
+    print("[full] dsv3 proxy", flush=True)
+    inp = wl.layer_inputs(**wl.WORKLOADS["dsv3_proxy"], seed=0)
+    T, H, F = inp["T"], inp["H"], inp["F"]
+    run = Run(inp)
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"])
+    check_equal("ep_recv_counts", run.d.ep_recv_counts.cpu().numpy(), r.ep_recv_counts)
+    check_equal("row2slot", run.d.row2slot(T, r.K)[:r.A].cpu().numpy(), r.row2slot)
+    assert r.counts.max() > 2 * r.counts.mean()   # the routing is skewed
+    # shared expert forward on all T tokens
+    ss = dm.shared_expert_shape(T, H, F)
+    scnt = torch.full((1,), T, dtype=torch.int32, device=DEV)
+    swg, swu, swd = bf(inp["shared_w_gate"]), bf(inp["shared_w_up"]), bf(inp["shared_w_down"])
+    s_gus = torch.empty((T, 2 * F), dtype=torch.bfloat16, device=DEV)
+    s_h = torch.empty((T, F), dtype=torch.bfloat16, device=DEV)
+    s_y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    dm.moe_grouped_ffn(ss, run.x, swg, swu, swd, scnt, s_gus, s_h, s_y)
+    g = bf(inp["grad_out"])
+    s_ggu = torch.empty((T, 2 * F), dtype=torch.bfloat16, device=DEV)
+    s_dx = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    s_gw = [torch.empty(t.shape, dtype=torch.float32, device=DEV) for t in (swg, swu, swd)]
+    dm.moe_grouped_ffn_bwd(ss, g, run.x, s_gus, s_h, swg, swu, swd, scnt, s_ggu, s_dx, *s_gw)
+    torch.cuda.synchronize()
+    res = _layer_step(run, shared_x=s_y, accum=s_dx)
+
+    xf = orc.bf16_to_f32(inp["x"])
+    sw = (inp["shared_w_gate"], inp["shared_w_up"], inp["shared_w_down"])
+
+    def shared_fwd(toks):
+        return orc.ffn_fwd(xf[toks], np.array([len(toks)]), *sw)
+
+    def shared_y(toks):
+        return shared_fwd(toks)[3]
+
+    def shared_dx(toks):
+        g_, u_, h_, _ = shared_fwd(toks)
+        return orc.ffn_bwd(orc.bf16_to_f32(inp["grad_out"][toks]), xf[toks], g_, u_, h_,
+                           np.array([len(toks)]), *sw)[1]
+
+    rng = np.random.default_rng(12)
+    _check_sampled_layer(inp, run, r, *res, rng, n_rows=64, n_tok=32, n_cols=8,
+                         shared=(shared_y, shared_dx))
+    # shared expert: its output on sampled tokens, its weight gradients on sampled columns
+    toks = _sample(rng, T, 32)
+    check_close("shared y tokens", f32(s_y[toks]), shared_y(toks))
+    fs = _sample(rng, F, 8)
+    wg, wu, wd = sw[0][:, fs], sw[1][:, fs], sw[2][:, :, fs]
+    g_, u_, h_, _ = orc.ffn_fwd(xf, np.array([T]), wg, wu, wd)
+    dgu, _, dwg, dwu, dwd = orc.ffn_bwd(orc.bf16_to_f32(inp["grad_out"]), xf, g_, u_, h_, np.array([T]),
+                                        wg, wu, wd)
+    check_close("shared grad_gate_up cols", f32(s_ggu[:, np.concatenate([fs, F + fs])]), dgu)
+    check_close("shared grad_w_gate", f32(s_gw[0][0][fs]), dwg[0])
+    check_close("shared grad_w_up", f32(s_gw[1][0][fs]), dwu[0])
+    check_close("shared grad_w_down", f32(s_gw[2][0][:, fs]), dwd[0])

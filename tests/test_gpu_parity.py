@@ -272,3 +272,26 @@ def test_autograd_layer_and_determinism():
     check_close("grad_x", f32(gx), b["dx"])
     check_close("grad_topk_weights", f32(gw), b["dw"])
     assert torch.equal(res[0][6].view(torch.int16), bf(inp["grad_out"]).cpu().view(torch.int16))
+
+
+def test_autograd_layer_shared_expert():
+    """moe_layer with a SwiGLU shared expert computed inside the layer."""
+    import dispatch_expert_gemm_amd as dm
+    inp = wl.layer_inputs(200, 256, 96, 6, 2, seed=13, shared=True, Z=1, C=1, mask="2d")
+    x = bf(inp["x"]).requires_grad_(True)
+    w = dev(inp["topk_weights"]).requires_grad_(True)
+    ws = [bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down", "shared_w_gate",
+                                                     "shared_w_up", "shared_w_down")]
+    out = dm.moe_layer(x, dev(inp["topk_idx"]), w, *ws[:3], x_active_mask=dev(inp["mask"]),
+                       shared_w_gate=ws[3], shared_w_up=ws[4], shared_w_down=ws[5],
+                       zero_expert_num=1, copy_expert_num=1)
+    out.backward(bf(inp["grad_out"]))
+    torch.cuda.synchronize()
+    f = orc.layer_fwd(inp, prec="parity")
+    b = orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
+    check_close("out", f32(out), f["out"])
+    check_close("grad_x", f32(x.grad), b["dx"])
+    check_close("grad_topk_weights", f32(w.grad), b["dw"])
+    for t, k in zip(ws, ("dWg", "dWu", "dWd", "s_dWg", "s_dWu", "s_dWd")):
+        # returned in the weights' dtype (bf16): compare with the rounding of the fp32 result
+        check_close(k, f32(t.grad), orc.round_bf16(b[k]))
