@@ -15,6 +15,8 @@
 // readlane.  Sums run in k order with separately rounded products and adds (this
 // file is compiled without floating-point contraction), so results do not
 // depend on the launch shape and are bit-reproducible.
+#include <type_traits>
+
 #include "common.hpp"
 
 #pragma clang fp contract(off)
@@ -23,21 +25,24 @@ namespace moe {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-constexpr int kMaxK = 16;
 
+// The per-token slot arrays are sized by a compile-time bound KMAX >= K (2, 4,
+// 8 or 16), so a kernel only holds the row registers its K needs.
+template <int KMAX>
 struct SlotInfo {
-  int code[kMaxK];
-  float w[kMaxK];
+  int code[KMAX];
+  float w[KMAX];
   bool any_ori;
 };
 
+template <int KMAX>
 __device__ __forceinline__ void load_slots(const int32_t* slot2row, const float* w, int64_t t,
-                                           int K, int lane, SlotInfo& si) {
+                                           int K, int lane, SlotInfo<KMAX>& si) {
   const int my = lane < K ? slot2row[t * K + lane] : MOE_SLOT_NONE;
   const float mw = lane < K ? w[t * K + lane] : 0.f;
   bool any = false;
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
+  for (int k = 0; k < KMAX; ++k) {
     si.code[k] = k < K ? __builtin_amdgcn_readlane(my, k) : MOE_SLOT_NONE;
     si.w[k] = k < K ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mw), k)) : 0.f;
     any |= si.code[k] <= MOE_SLOT_COPY;
@@ -78,17 +83,18 @@ struct CombineArgs {
   int64_t Hv;
 };
 
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (t >= a.T) return;
-  SlotInfo si;
+  SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
   for (int64_t v = lane; v < Hv; v += kWave) {
-    uint4 raw[kMaxK];
+    uint4 raw[KMAX];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
+    for (int k = 0; k < KMAX; ++k)
       if (si.code[k] >= 0) raw[k] = a.y[(int64_t)si.code[k] * Hv + v];
     float ox[8];
     if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KMAX; ++k) {
       const int c = si.code[k];
       if (c == MOE_SLOT_NONE) continue;
       float f[8];
@@ -132,27 +138,28 @@ struct CombineBwdArgs {
   int64_t Hv;
 };
 
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (t >= a.T) return;
-  SlotInfo si;
+  SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
-  float dot[kMaxK];
+  float dot[KMAX];
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k) dot[k] = 0.f;
+  for (int k = 0; k < KMAX; ++k) dot[k] = 0.f;
   for (int64_t v = lane; v < Hv; v += kWave) {
     float d[8];
     unpack8(a.dout[t * Hv + v], d);
-    uint4 raw[kMaxK];
+    uint4 raw[KMAX];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
+    for (int k = 0; k < KMAX; ++k)
       if (si.code[k] >= 0) raw[k] = a.y[(int64_t)si.code[k] * Hv + v];
     float ox[8];
     if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KMAX; ++k) {
       const int c = si.code[k];
       if (c == MOE_SLOT_NONE) continue;
       float f[8];
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   }
   // fixed-shape butterfly over the wave: the same order for every launch
 #pragma unroll
-  for (int k = 0; k < kMaxK; ++k) {
+  for (int k = 0; k < KMAX; ++k) {
     if (k < a.K) {
       float p = dot[k];
 #pragma unroll
@@ -196,17 +203,18 @@ struct DispatchBwdArgs {
   int64_t Hv;
 };
 
+template <int KMAX>
 __global__ __launch_bounds__(256) void k_dispatch_bwd(DispatchBwdArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (t >= a.T) return;
-  SlotInfo si;
+  SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
   for (int64_t v = lane; v < Hv; v += kWave) {
-    uint4 raw[kMaxK];
+    uint4 raw[KMAX];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
+    for (int k = 0; k < KMAX; ++k)
       if (si.code[k] >= 0) raw[k] = a.dx_exp[(int64_t)si.code[k] * Hv + v];
     float d[8];
     if (si.any_ori) unpack8(a.dout[t * Hv + v], d);
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(256) void k_dispatch_bwd(DispatchBwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
+    for (int k = 0; k < KMAX; ++k) {
       const int c = si.code[k];
       if (c == MOE_SLOT_NONE) continue;
       float f[8];
@@ -240,6 +248,15 @@ __global__ __launch_bounds__(256) void k_dispatch_bwd(DispatchBwdArgs a) {
     }
     a.dx[t * Hv + v] = pack8(acc);
   }
+}
+
+// Calls f with std::integral_constant<int, KMAX> for the smallest KMAX >= K.
+template <typename Fn>
+inline void launch_k(int K, Fn f) {
+  if (K <= 2) f(std::integral_constant<int, 2>{});
+  else if (K <= 4) f(std::integral_constant<int, 4>{});
+  else if (K <= 8) f(std::integral_constant<int, 8>{});
+  else f(std::integral_constant<int, 16>{});
 }
 
 inline dim3 token_grid(int64_t T) {
@@ -281,7 +298,10 @@ extern "C" moe_status moe_combine(const moe_shape* s, const void* y, const int32
                 static_cast<const uint4*>(const_alpha_2), static_cast<const uint4*>(const_v),
                 static_cast<uint4*>(out),          s->T,
                 s->K,                              s->H / 8};
-  hipLaunchKernelGGL(k_combine, token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+  launch_k(s->K, [&](auto km) {
+    hipLaunchKernelGGL(k_combine<decltype(km)::value>, token_grid(s->T), dim3(256), 0,
+                       as_stream(stream), a);
+  });
   return launch_status();
 }
 
@@ -316,7 +336,10 @@ extern "C" moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, 
                    s->T,
                    s->K,
                    s->H / 8};
-  hipLaunchKernelGGL(k_combine_bwd, token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+  launch_k(s->K, [&](auto km) {
+    hipLaunchKernelGGL(k_combine_bwd<decltype(km)::value>, token_grid(s->T), dim3(256), 0,
+                       as_stream(stream), a);
+  });
   return launch_status();
 }
 
@@ -343,6 +366,9 @@ extern "C" moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expa
                     s->T,
                     s->K,
                     s->H / 8};
-  hipLaunchKernelGGL(k_dispatch_bwd, token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+  launch_k(s->K, [&](auto km) {
+    hipLaunchKernelGGL(k_dispatch_bwd<decltype(km)::value>, token_grid(s->T), dim3(256), 0,
+                       as_stream(stream), a);
+  });
   return launch_status();
 }

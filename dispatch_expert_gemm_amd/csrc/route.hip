@@ -11,8 +11,9 @@
 // Kernels (all on the caller's stream, no host synchronisation):
 //   k_route_count  one wave per chunk of 64*R slots: classify, per-chunk expert
 //                  histogram in LDS, chunk error bits
-//   k_route_scan   one block: per-expert sums over chunks, block scan over
-//                  experts, exclusive per-(chunk, expert) row offsets, outputs
+//   k_route_scan   one block: per-expert sums over chunks (each expert's column
+//                  split across thread groups), scan over experts, exclusive
+//                  per-(chunk, expert) row offsets, outputs
 //   k_route_rank   one wave per chunk: stable rank of each routed slot among
 //                  the slots of its expert in the chunk (wave ballots), writes
 //                  slot->row and row->slot
@@ -23,7 +24,7 @@ namespace moe {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-constexpr int kMaxChunks = 128;
+constexpr int kMaxChunks = 256;
 
 struct RouteArgs {
   const int32_t* idx;
@@ -99,38 +100,67 @@ __global__ __launch_bounds__(256) void k_route_count(RouteArgs a, int32_t* __res
   }
 }
 
+// One block of 1024 threads.  Thread (e, grp) with e = tid % Ep, grp = tid / Ep
+// (Ep = E rounded up to a power of two, G = 1024 / Ep groups) owns the chunks
+// [grp*per, (grp+1)*per) of expert e's column: it sums them, the group sums
+// are scanned in LDS, the expert totals are scanned over experts, and each
+// thread rewrites its chunks as exclusive row offsets.
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist,
                                                      const int32_t* __restrict__ chunk_err,
-                                                     int nchunks, int E,
+                                                     int nchunks, int E, int Ep,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ prefix,
                                                      int32_t* __restrict__ err_flag) {
-  __shared__ int32_t tot[1024];
+  __shared__ int32_t part[1024];  // [grp][e] partial sums
+  __shared__ int32_t tot[1024];   // expert totals, then their inclusive scan
   __shared__ int32_t errsh;
-  const int e = threadIdx.x;
-  if (e == 0) errsh = 0;
+  const int tid = threadIdx.x;
+  const int G = 1024 / Ep;
+  const int e = tid % Ep, grp = tid / Ep;
+  const int per = (nchunks + G - 1) / G;
+  const int c0 = grp * per, c1 = (c0 + per < nchunks) ? c0 + per : nchunks;
+  if (tid == 0) errsh = 0;
   int32_t sum = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) sum += hist[(int64_t)c * E + e];
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = hist[(int64_t)(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += v[i];
+    }
+    for (; c < c1; ++c) sum += hist[(int64_t)c * E + e];
   }
-  tot[e] = sum;
+  part[grp * Ep + e] = sum;
   __syncthreads();
   uint32_t er = 0;
-  for (int c = e; c < nchunks; c += 1024) er |= (uint32_t)chunk_err[c];
+  for (int c = tid; c < nchunks; c += 1024) er |= (uint32_t)chunk_err[c];
   if (er) atomicOr(&errsh, (int32_t)er);
-  // inclusive scan of tot (Hillis-Steele)
+  // exclusive prefix of this thread's group within its expert, and the expert total
+  int32_t before = 0, total = 0;
+  for (int q = 0; q < G; ++q) {
+    const int32_t v = part[q * Ep + e];
+    before += q < grp ? v : 0;
+    total += v;
+  }
+  tot[tid] = tid < Ep ? total : 0;  // thread tid < Ep is (expert tid, group 0)
+  __syncthreads();
+  // inclusive scan of the expert totals (Hillis-Steele over 1024 entries)
   for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = e >= off ? tot[e - off] : 0;
+    const int32_t v = tid >= off ? tot[tid - off] : 0;
     __syncthreads();
-    tot[e] += v;
+    tot[tid] += v;
     __syncthreads();
   }
   if (e < E) {
-    counts[e] = sum;
-    prefix[e] = tot[e];
-    int32_t run = tot[e] - sum;  // exclusive base of expert e
-    int c = 0;
-    for (; c + 8 <= nchunks; c += 8) {
+    if (grp == 0) {
+      counts[e] = total;
+      prefix[e] = tot[e];
+    }
+    int32_t run = tot[e] - total + before;  // exclusive base of (expert e, chunk c0)
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
       int32_t v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = hist[(int64_t)(c + i) * E + e];
@@ -140,14 +170,14 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist,
         run += v[i];
       }
     }
-    for (; c < nchunks; ++c) {
+    for (; c < c1; ++c) {
       const int32_t v = hist[(int64_t)c * E + e];
       hist[(int64_t)c * E + e] = run;
       run += v;
     }
   }
   __syncthreads();
-  if (e == 0) *err_flag = errsh;
+  if (tid == 0) *err_flag = errsh;
 }
 
 __global__ __launch_bounds__(256) void k_route_rank(RouteArgs a, const int32_t* __restrict__ offs,
@@ -294,8 +324,10 @@ extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int3
   if (g.nchunks > 0)
     hipLaunchKernelGGL(k_route_count, dim3(blocks), dim3(256), lds, strm, a, hist, cerr,
                        g.nslots, g.nchunks, g.R);
+  int Ep = 1;
+  while (Ep < s->num_experts) Ep <<= 1;
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, strm, hist, cerr, g.nchunks,
-                     s->num_experts, expert_token_nums, ep_recv_counts, err_flag);
+                     s->num_experts, Ep, expert_token_nums, ep_recv_counts, err_flag);
   if (g.nchunks > 0) {
     int nbits = 0;
     while ((1 << nbits) < s->num_experts) ++nbits;
