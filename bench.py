@@ -64,6 +64,25 @@ def bytes_moved(name, T, H, F, K, A, E):
     return None
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (profiles/traffic_page1.json), or None when missing or when the kernel
+    source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_page1.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "dispatch_expert_gemm_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("gemm_source_sha256") != digest:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
 def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
     """The CPU oracle (parity mode) on a T_sample-token slice of the same workload."""
     import moe_workloads as wl
@@ -98,6 +117,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=None, help="override T")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB three times "
+                         "(the reference kernel for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the layer here holds every expert on one device and "
@@ -231,7 +253,7 @@ def main():
                    "flop_per_step": total_flops},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom)},
         "combine": {"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
                     "frac": kernels["moe_combine"]["frac_hbm"]},
         "gemm_ms_per_step": round(gemm_ms, 4),
@@ -239,6 +261,13 @@ def main():
         "kernels": kernels,
         "context": {"page1_fwd_bwd_ms_4_nvidia_gpus_T8192": 5.488},
     }
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
