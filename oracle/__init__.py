@@ -12,8 +12,9 @@ duplicate handling, prefix kind, row order, summation order) are pinned only by
 internal consistency, as the pages print no output values.
 """
 from .moe import (ERR_ID_DUPLICATE, ERR_ID_RANGE, ERR_MASK_NOT_PREFIX, Route, combine,
-                  combine_bwd, decode, dispatch, dispatch_bwd, ffn_bwd, ffn_fwd, layer_bwd,
-                  layer_fwd, route, silu)
+                  combine_bwd, decode, dequant_weights_fp8, dispatch, dispatch_bwd, ffn_bwd,
+                  ffn_bwd_fp8, ffn_fwd, ffn_fwd_fp8, layer_bwd, layer_bwd_fp8, layer_fwd,
+                  layer_fwd_fp8, qdq_rows_fp8, qdq_rows_int8, quant_weights_fp8, route, silu)
 from .numerics import (bf16_to_f32, dequant_e4m3_blocks, dequant_e4m3_rows, dequant_int8_rows,
                        e4m3_decode, e4m3_encode, f32_to_bf16, quant_e4m3_blocks, quant_e4m3_rows,
                        quant_int8_rows, round_bf16)

@@ -56,7 +56,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .numerics import bf16_to_f32, round_bf16
+from .numerics import (bf16_to_f32, dequant_e4m3_blocks, dequant_e4m3_rows, dequant_int8_rows,
+                       quant_e4m3_blocks, quant_e4m3_rows, quant_int8_rows, round_bf16)
 
 ERR_ID_RANGE = 1
 ERR_ID_DUPLICATE = 2
@@ -402,3 +403,130 @@ def layer_bwd(inp: dict, fwd: dict, grad_out, prec="parity"):
         res["d_shared"] = decode(grad_out, prec).astype(ft)
     res["dx"] = dispatch_bwd(dX, r, inp["topk_weights"], grad_out, inp.get("const_alpha_1"), accum, prec)
     return res
+
+
+# ============================================================================ fp8 / int8 path
+#
+# Readings (the pages name FP8 as a precision of the MoE performance tests on the
+# Megatron-LM page, section "Added Test Cases", and int8 communication quantisation
+# as comm_quant_mode 2 on the low_latency_combine page, Parameters; neither gives a
+# recipe, so these are ours):
+#  * weights: e4m3 codes with one fp32 scale per 128 x 128 block of each expert's
+#    (out, in) matrix; activations entering a fp8 GEMM: e4m3 codes with one scale
+#    per (row, 128 consecutive columns of the contraction dimension);
+#  * the forward GEMMs and the two data-gradient GEMMs run on the quantised
+#    operands (fp32 accumulation of dequantised products); G, U, h, y, dY, dG, dU,
+#    dX, dx keep their bf16 storage; the weight-gradient GEMMs run in bf16 on the
+#    unquantised bf16 activations (per-token scales do not factor out of a
+#    contraction over tokens);
+#  * the quantisers are applied to the bf16 tensors the device stores;
+#  * int8 payload: every expert-output row y is quantised per row (symmetric,
+#    127/amax) and dequantised before the weighted sum; dw uses that dequantised y.
+
+
+def quant_weights_fp8(w_bits):
+    """(E, N, K) bf16 weights -> (codes (E,N,K) uint8, scales (E,N/128,K/128) fp32)."""
+    W = decode(w_bits, "parity")
+    qs = [quant_e4m3_blocks(W[e]) for e in range(W.shape[0])]
+    return np.stack([q for q, _ in qs]), np.stack([s for _, s in qs])
+
+
+def dequant_weights_fp8(codes, scales):
+    return np.stack([dequant_e4m3_blocks(codes[e], scales[e]) for e in range(codes.shape[0])])
+
+
+def qdq_rows_fp8(a):
+    """Quantise rows per 128 columns to e4m3 and dequantise (float32)."""
+    q, s = quant_e4m3_rows(np.asarray(a, np.float32))
+    return dequant_e4m3_rows(q, s)
+
+
+def ffn_fwd_fp8(X16, ep_recv_counts, wq_gate, wq_up, wq_down):
+    """fp8 forward of the grouped SwiGLU FFN (parity mode).
+
+    wq_*: (codes, scales) from quant_weights_fp8.  X16: the bf16 expanded rows (float32
+    values).  Returns G16, U16, H16 (bf16 values) and Y16.
+    """
+    st = _store("parity")
+    Wg, Wu, Wd = (dequant_weights_fp8(*w) for w in (wq_gate, wq_up, wq_down))
+    X16 = np.asarray(X16, np.float32)
+    Xd = qdq_rows_fp8(X16) if X16.shape[0] else X16
+    E, F, H = Wg.shape
+    A = X16.shape[0]
+    G, U, Hh = (np.zeros((A, F), np.float32) for _ in range(3))
+    Y = np.zeros((A, H), np.float32)
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        if hi > lo:
+            g = Xd[lo:hi] @ Wg[e].T
+            u = Xd[lo:hi] @ Wu[e].T
+            h = st(silu(g) * u)
+            G[lo:hi], U[lo:hi], Hh[lo:hi] = st(g), st(u), h
+            Y[lo:hi] = st(qdq_rows_fp8(h) @ Wd[e].T)
+        lo = hi
+    return G, U, Hh, Y
+
+
+def ffn_bwd_fp8(dY16, X16, G16, U16, H16, ep_recv_counts, wq_gate, wq_up, wq_down):
+    """fp8 backward: data gradients on quantised dY / dGU and fp8 weights,
+    weight gradients in bf16 (parity mode).  Returns dGU, dX, dWg, dWu, dWd."""
+    st = _store("parity")
+    Wg, Wu, Wd = (dequant_weights_fp8(*w) for w in (wq_gate, wq_up, wq_down))
+    E, F, H = Wg.shape
+    dY16, X16, G16, U16, H16 = (np.asarray(a, np.float32) for a in (dY16, X16, G16, U16, H16))
+    A = X16.shape[0]
+    dGU = np.zeros((A, 2 * F), np.float32)
+    dX = np.zeros((A, H), np.float32)
+    dWg, dWu = np.zeros((E, F, H), np.float32), np.zeros((E, F, H), np.float32)
+    dWd = np.zeros((E, H, F), np.float32)
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        if hi > lo:
+            dh = qdq_rows_fp8(dY16[lo:hi]) @ Wd[e]
+            g, u = G16[lo:hi], U16[lo:hi]
+            s = 1 / (1 + np.exp(-g))
+            dg = st(dh * u * s * (1 + g * (1 - s)))
+            du = st(dh * (g * s))
+            dgu = np.concatenate([dg, du], 1)
+            dGU[lo:hi] = dgu
+            dX[lo:hi] = st(qdq_rows_fp8(dgu) @ np.concatenate([Wg[e], Wu[e]], 0))
+            dWd[e] = dY16[lo:hi].T @ H16[lo:hi]
+            dWg[e] = dg.T @ X16[lo:hi]
+            dWu[e] = du.T @ X16[lo:hi]
+        lo = hi
+    return dGU, dX, dWg, dWu, dWd
+
+
+def qdq_rows_int8(Y16):
+    """The int8 combine payload: per-row symmetric int8 round trip of y."""
+    Y16 = np.asarray(Y16, np.float32)
+    if Y16.shape[0] == 0:
+        return Y16
+    return dequant_int8_rows(*quant_int8_rows(Y16))
+
+
+def layer_fwd_fp8(inp: dict, comm_quant=True):
+    """Whole forward on the fp8 path (parity mode): weights and activations
+    quantised as described above, int8 combine payload when comm_quant."""
+    E = inp["E"]
+    Z, C, Q = inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0)
+    r = route(inp["topk_idx"], E, Z, C, Q, inp.get("mask"))
+    X = dispatch(inp["x"], r, "parity")
+    wq = tuple(quant_weights_fp8(inp[k]) for k in ("w_gate", "w_up", "w_down"))
+    G, U, Hh, Y = ffn_fwd_fp8(X, r.ep_recv_counts, *wq)
+    Yc = qdq_rows_int8(Y) if comm_quant else Y
+    out = combine(Yc, r, inp["topk_weights"], inp.get("shared_expert_x"), inp["x"],
+                  inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), "parity")
+    return dict(route=r, X=X, wq=wq, G=G, U=U, Hh=Hh, Y=Y, Yc=Yc, out=out)
+
+
+def layer_bwd_fp8(inp: dict, fwd: dict, grad_out):
+    r = fwd["route"]
+    dY, dw = combine_bwd(grad_out, fwd["Yc"], r, inp["topk_weights"], inp["x"],
+                         inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), "parity")
+    dGU, dX, dWg, dWu, dWd = ffn_bwd_fp8(dY, fwd["X"], fwd["G"], fwd["U"], fwd["Hh"], r.ep_recv_counts,
+                                         *fwd["wq"])
+    dx = dispatch_bwd(dX, r, inp["topk_weights"], grad_out, inp.get("const_alpha_1"), None, "parity")
+    return dict(dY=dY, dw=dw, dGU=dGU, dX=dX, dWg=dWg, dWu=dWu, dWd=dWd, dx=dx)

@@ -376,3 +376,83 @@ def test_fp32_backward_close_to_f64():
     for k in ("dx", "dw", "dWg", "dWu", "dWd"):
         scale = max(1.0, np.abs(f64[k]).max())
         assert np.abs(f64[k] - f32[k]).max() <= 1e-5 * scale, k
+
+
+# ============================================================================ fp8 / int8 path
+
+
+def _lossless_fp8_rows(rng, R, C):
+    """Rows whose every 128-column block is e4m3 codes times a power of two, with
+    one element at +-448 times that power: per-(row,128) quantisation is exact."""
+    codes = rng.integers(0, 0x7F, size=(R, C)).astype(np.uint8) | (rng.integers(0, 2, size=(R, C)) << 7).astype(np.uint8)
+    v = orc.e4m3_decode(codes).astype(np.float64)
+    v[:, ::128] = 448.0
+    pw = 2.0 ** rng.integers(-6, 2, size=(R, C // 128))
+    return (v * np.repeat(pw, 128, axis=1)).astype(np.float32)
+
+
+def _lossless_fp8_blocks(rng, E, N, K):
+    out = np.zeros((E, N, K), np.float32)
+    for e in range(E):
+        codes = rng.integers(0, 0x7F, size=(N, K)).astype(np.uint8)
+        v = orc.e4m3_decode(codes).astype(np.float64) * np.where(rng.random((N, K)) < 0.5, -1, 1)
+        v[::128, ::128] = 448.0
+        pw = 2.0 ** rng.integers(-9, -4, size=(N // 128, K // 128))
+        out[e] = v * np.kron(pw, np.ones((128, 128)))
+    return out
+
+
+def test_fp8_lossless_inputs_reproduce_bf16_gemm():
+    """With inputs that the block quantisers represent exactly, the fp8 forward's
+    G and U equal the bf16 path's bit for bit (pins block/scale indexing)."""
+    rng = np.random.default_rng(21)
+    E, F, H, A = 2, 256, 384, 96
+    X = _lossless_fp8_rows(rng, A, H)
+    Wg, Wu, Wd = _lossless_fp8_blocks(rng, E, F, H), _lossless_fp8_blocks(rng, E, F, H), \
+        _lossless_fp8_blocks(rng, E, H, F)
+    bits = [orc.f32_to_bf16(a) for a in (X, Wg, Wu, Wd)]
+    assert all(np.array_equal(orc.bf16_to_f32(b), a) for b, a in zip(bits, (X, Wg, Wu, Wd)))
+    counts = np.array([40, 96])
+    wq = tuple(orc.quant_weights_fp8(b) for b in bits[1:])
+    assert np.array_equal(orc.dequant_weights_fp8(*wq[0]), Wg)
+    G8, U8, H8, Y8 = orc.ffn_fwd_fp8(X, counts, *wq)
+    G, U, Hh, Y = orc.ffn_fwd(X, counts, *bits[1:], prec="parity")
+    assert np.array_equal(G8, G) and np.array_equal(U8, U) and np.array_equal(H8, Hh)
+    # the down GEMM's input h is quantised: close, not equal
+    assert 0 < np.linalg.norm(Y8 - Y) / np.linalg.norm(Y) < 0.1
+
+
+def test_fp8_layer_close_to_bf16_layer():
+    inp = wl.layer_inputs(64, 256, 128, 4, 2, seed=22)
+    f8 = orc.layer_fwd_fp8(inp)
+    b8 = orc.layer_bwd_fp8(inp, f8, inp["grad_out"])
+    f = orc.layer_fwd(inp, prec="parity")
+    b = orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
+    rel = lambda a, c: np.linalg.norm(a - c) / np.linalg.norm(c)
+    for k in ("out",):
+        assert 0.003 < rel(f8[k], f[k]) < 0.1, k
+    for k in ("dx", "dw", "dWg", "dWu", "dWd"):
+        assert 0.001 < rel(b8[k], b[k]) < 0.15, k
+    # weight gradient of the down projection is a bf16 GEMM of dY and h: with the
+    # fp8 path's own dY and h it is exactly the bf16 formula
+    A = f8["route"].A
+    ref = np.zeros_like(b8["dWd"])
+    lo = 0
+    for e in range(4):
+        hi = int(f8["route"].ep_recv_counts[e])
+        ref[e] = b8["dY"][lo:hi].T @ f8["Hh"][lo:hi]
+        lo = hi
+    assert np.array_equal(ref, b8["dWd"])
+
+
+def test_int8_payload_lossless_rows_and_rounding():
+    rng = np.random.default_rng(23)
+    k = rng.integers(-127, 128, size=(10, 64)).astype(np.float64)
+    k[:, 0] = 127
+    s = 2.0 ** rng.integers(-8, 0, size=(10, 1))
+    Y = (k * s).astype(np.float32)
+    assert np.array_equal(orc.qdq_rows_int8(Y), Y)
+    Y2 = rng.standard_normal((10, 64)).astype(np.float32)
+    d = orc.qdq_rows_int8(Y2)
+    amax = np.abs(Y2).max(axis=1, keepdims=True)
+    assert np.all(np.abs(d - Y2) <= amax / 127 / 2 * 1.0001)
