@@ -32,6 +32,8 @@ ENTRY_POINTS = (
     "moe_grouped_ffn", "moe_ffn_gate_up_fwd", "moe_ffn_down_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_ffn_down_bwd_data", "moe_ffn_down_bwd_weight",
     "moe_ffn_gate_up_bwd_data", "moe_ffn_gate_up_bwd_weight", "moe_dispatch_bwd",
+    "moe_quant_rows_fp8", "moe_quantize_weights_fp8", "moe_ffn_gate_up_fwd_fp8",
+    "moe_ffn_down_fwd_fp8", "moe_ffn_down_bwd_data_fp8", "moe_ffn_gate_up_bwd_data_fp8",
 )
 
 
@@ -42,15 +44,15 @@ class MoeShape(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("zero_expert_num", ctypes.c_int32),
                 ("copy_expert_num", ctypes.c_int32), ("const_expert_num", ctypes.c_int32),
                 ("mask_ndim", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("comm_quant_mode", ctypes.c_int32)]
 
 
 def make_shape(T, H, K, num_experts, F=0, capacity=None, zero_expert_num=0, copy_expert_num=0,
-               const_expert_num=0, mask_ndim=0) -> MoeShape:
+               const_expert_num=0, mask_ndim=0, comm_quant_mode=0) -> MoeShape:
     if capacity is None:
         capacity = T * min(num_experts, K)
     return MoeShape(T, H, F, capacity, K, num_experts, zero_expert_num, copy_expert_num,
-                    const_expert_num, mask_ndim, 0, 0)
+                    const_expert_num, mask_ndim, 0, comm_quant_mode)
 
 
 class MoeError(RuntimeError):
@@ -84,6 +86,13 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_gate_up_bwd_data.argtypes = [S, P, P, P, P, P, P]
         L.moe_ffn_gate_up_bwd_weight.argtypes = [S, P, P, P, P, P, P]
         L.moe_dispatch_bwd.argtypes = [S] + [P] * 10
+        I64 = ctypes.c_int64
+        L.moe_quant_rows_fp8.argtypes = [I64, I64, P, P, P, P, P]
+        L.moe_quantize_weights_fp8.argtypes = [I64, I64, I64, P, P, P, P, P]
+        L.moe_ffn_gate_up_fwd_fp8.argtypes = [S] + [P] * 10
+        L.moe_ffn_down_fwd_fp8.argtypes = [S] + [P] * 7
+        L.moe_ffn_down_bwd_data_fp8.argtypes = [S] + [P] * 8
+        L.moe_ffn_gate_up_bwd_data_fp8.argtypes = [S] + [P] * 9
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
                 getattr(L, name).restype = ctypes.c_int32
@@ -239,6 +248,82 @@ def moe_dispatch_bwd(shape, grad_expand_x, assist_info_for_combine, topk_idx, to
         _ptr(topk_weights, F32, "topk_weights"), _ptr(x_active_mask, U8, "x_active_mask"),
         _ptr(grad_out, BF16, "grad_out"), _ptr(const_alpha_1, BF16, "const_alpha_1"),
         _ptr(grad_x_accum, BF16, "grad_x_accum"), _ptr(grad_x, BF16, "grad_x"), _stream(stream)))
+
+
+U8T, F32T = torch.uint8, torch.float32
+
+
+def moe_quant_rows_fp8(src, codes, scales, nrows=None, stream=None):
+    R, C = src.shape
+    _check(lib().moe_quant_rows_fp8(R, C, _ptr(src, BF16, "src"), _ptr(nrows, I32, "nrows"),
+                                    _ptr(codes, U8T, "codes"), _ptr(scales, F32T, "scales"),
+                                    _stream(stream)))
+
+
+def moe_quantize_weights_fp8(w, codes, codes_t, scales, stream=None):
+    E, N, K = w.shape
+    _check(lib().moe_quantize_weights_fp8(E, N, K, _ptr(w, BF16, "w"), _ptr(codes, U8T, "codes"),
+                                          _ptr(codes_t, U8T, "codes_t"), _ptr(scales, F32T, "scales"),
+                                          _stream(stream)))
+
+
+def moe_ffn_gate_up_fwd_fp8(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act,
+                            stream=None):
+    _check(lib().moe_ffn_gate_up_fwd_fp8(
+        ctypes.byref(shape), _ptr(xq, U8T, "xq"), _ptr(xs, F32T, "xs"), _ptr(wgq, U8T, "wgq"),
+        _ptr(wgs, F32T, "wgs"), _ptr(wuq, U8T, "wuq"), _ptr(wus, F32T, "wus"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(h_act, BF16, "h_act"), _stream(stream)))
+
+
+def moe_ffn_down_fwd_fp8(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
+    _check(lib().moe_ffn_down_fwd_fp8(
+        ctypes.byref(shape), _ptr(hq, U8T, "hq"), _ptr(hs, F32T, "hs"), _ptr(wdq, U8T, "wdq"),
+        _ptr(wds, F32T, "wds"), _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"),
+        _stream(stream)))
+
+
+def moe_ffn_down_bwd_data_fp8(shape, dyq, dys, wdq_t, wds, gate_up_save, ep_recv_counts, grad_gate_up,
+                              stream=None):
+    _check(lib().moe_ffn_down_bwd_data_fp8(
+        ctypes.byref(shape), _ptr(dyq, U8T, "dyq"), _ptr(dys, F32T, "dys"), _ptr(wdq_t, U8T, "wdq_t"),
+        _ptr(wds, F32T, "wds"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_gate_up, BF16, "grad_gate_up"),
+        _stream(stream)))
+
+
+def moe_ffn_gate_up_bwd_data_fp8(shape, dguq, dgus, wgq_t, wgs, wuq_t, wus, ep_recv_counts,
+                                 grad_expand_x, stream=None):
+    _check(lib().moe_ffn_gate_up_bwd_data_fp8(
+        ctypes.byref(shape), _ptr(dguq, U8T, "dguq"), _ptr(dgus, F32T, "dgus"),
+        _ptr(wgq_t, U8T, "wgq_t"), _ptr(wgs, F32T, "wgs"), _ptr(wuq_t, U8T, "wuq_t"),
+        _ptr(wus, F32T, "wus"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(grad_expand_x, BF16, "grad_expand_x"), _stream(stream)))
+
+
+@dataclass
+class Fp8Weights:
+    """e4m3 codes (and transposed codes) with 128 x 128 block scales of one weight tensor."""
+    codes: torch.Tensor
+    codes_t: torch.Tensor
+    scales: torch.Tensor
+
+    @staticmethod
+    def quantize(w, stream=None):
+        E, N, K = w.shape
+        q = Fp8Weights(torch.empty((E, N, K), dtype=U8T, device=w.device),
+                       torch.empty((E, K, N), dtype=U8T, device=w.device),
+                       torch.empty((E, N // 128, K // 128), dtype=F32T, device=w.device))
+        moe_quantize_weights_fp8(w, q.codes, q.codes_t, q.scales, stream)
+        return q
+
+
+def quant_rows_fp8(src, nrows=None, stream=None):
+    R, C = src.shape
+    codes = torch.empty((R, C), dtype=U8T, device=src.device)
+    scales = torch.empty((R, C // 128), dtype=F32T, device=src.device)
+    moe_quant_rows_fp8(src, codes, scales, nrows, stream)
+    return codes, scales
 
 
 # ----------------------------------------------------------------------------- buffers + layer

@@ -68,6 +68,41 @@ __device__ __forceinline__ void special_value(int code, const float* ox, const u
   for (int i = 0; i < 8; ++i) f[i] = p[i] * ox[i] + q[i] * c[i];
 }
 
+// int8 payload (comm_quant_mode 2, Parameters of the low_latency_combine page):
+// every routed slot's expert-output row is quantised symmetrically per row,
+// q = clamp(rint(y * (127/amax)), -127, 127), and used as q * (amax/127).  The
+// row's amax comes from a first pass over the row (wave max).
+template <int KMAX>
+__device__ __forceinline__ void int8_params(const uint4* y, const SlotInfo<KMAX>& si, int64_t Hv,
+                                            int lane, float* qinv, float* qsc) {
+  float mx[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) mx[k] = 0.f;
+  for (int64_t v = lane; v < Hv; v += kWave) {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (si.code[k] >= 0) {
+        float f[8];
+        unpack8(y[(int64_t)si.code[k] * Hv + v], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx[k] = fmaxf(mx[k], fabsf(f[i]));
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    float m = mx[k];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    qinv[k] = m > 0.f ? __fdiv_rn(127.0f, m) : 0.f;
+    qsc[k] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
+  }
+}
+
+__device__ __forceinline__ void int8_qdq(float* f, float inv, float sc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = fminf(fmaxf(rintf(f[i] * inv), -127.0f), 127.0f) * sc;
+}
+
 struct CombineArgs {
   const uint4* y;
   const float* w;
@@ -81,6 +116,7 @@ struct CombineArgs {
   int64_t T;
   int K;
   int64_t Hv;
+  int qpay;  // comm_quant_mode 2: int8 round trip of every expert-output row
 };
 
 template <int KMAX>
@@ -91,6 +127,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
+  float qinv[KMAX], qsc[KMAX];
+  if (a.qpay) int8_params(a.y, si, Hv, lane, qinv, qsc);
   for (int64_t v = lane; v < Hv; v += kWave) {
     uint4 raw[KMAX];
 #pragma unroll
@@ -106,8 +144,12 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       const int c = si.code[k];
       if (c == MOE_SLOT_NONE) continue;
       float f[8];
-      if (c >= 0) unpack8(raw[k], f);
-      else special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+      if (c >= 0) {
+        unpack8(raw[k], f);
+        if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
+      } else {
+        special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+      }
       const float wk = si.w[k];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = acc[i] + wk * f[i];
@@ -136,6 +178,7 @@ struct CombineBwdArgs {
   int64_t T;
   int K;
   int64_t Hv;
+  int qpay;
 };
 
 template <int KMAX>
@@ -146,6 +189,8 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
+  float qinv[KMAX], qsc[KMAX];
+  if (a.qpay) int8_params(a.y, si, Hv, lane, qinv, qsc);
   float dot[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) dot[k] = 0.f;
@@ -163,8 +208,12 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
       const int c = si.code[k];
       if (c == MOE_SLOT_NONE) continue;
       float f[8];
-      if (c >= 0) unpack8(raw[k], f);
-      else special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+      if (c >= 0) {
+        unpack8(raw[k], f);
+        if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
+      } else {
+        special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+      }
       float p = dot[k];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p = p + f[i] * d[i];
@@ -297,7 +346,8 @@ extern "C" moe_status moe_combine(const moe_shape* s, const void* y, const int32
                 static_cast<const uint4*>(ori_x), static_cast<const uint4*>(const_alpha_1),
                 static_cast<const uint4*>(const_alpha_2), static_cast<const uint4*>(const_v),
                 static_cast<uint4*>(out),          s->T,
-                s->K,                              s->H / 8};
+                s->K,                              s->H / 8,
+                s->comm_quant_mode == 2};
   launch_k(s->K, [&](auto km) {
     hipLaunchKernelGGL(k_combine<decltype(km)::value>, token_grid(s->T), dim3(256), 0,
                        as_stream(stream), a);
@@ -335,7 +385,8 @@ extern "C" moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, 
                    grad_topk_weights,
                    s->T,
                    s->K,
-                   s->H / 8};
+                   s->H / 8,
+                   s->comm_quant_mode == 2};
   launch_k(s->K, [&](auto km) {
     hipLaunchKernelGGL(k_combine_bwd<decltype(km)::value>, token_grid(s->T), dim3(256), 0,
                        as_stream(stream), a);

@@ -45,6 +45,37 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return v;
 }
 
+// float -> OCP fp8 e4m3 code (1-4-3, bias 7, largest finite 448, S.1111.111 = NaN),
+// round to nearest with ties to the even code, saturating at +-448; NaN gives
+// 0x7F; the sign of zero is kept.  Written from the format definition: below
+// 2^-6 the code is the subnormal count m * 2^-9, above it the 23-bit fp32
+// mantissa is rounded to 3 bits.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  const float af = __uint_as_float(a);
+  if (af >= 448.0f) return sign | 0x7eu;
+  const int e = (int)(a >> 23) - 127;
+  uint32_t code;
+  if (e < -6) {
+    code = (uint32_t)rintf(af * 512.0f);  // exact product, rint = ties to even
+  } else {
+    const uint32_t mant = a & 0x7fffffu;
+    uint32_t q = mant >> 20;
+    const uint32_t rem = mant & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    uint32_t ee = (uint32_t)(e + 7);
+    if (q == 8u) {
+      q = 0u;
+      ++ee;
+    }
+    code = (ee << 3) | q;
+  }
+  return sign | code;
+}
+
 constexpr int kWave = 64;
 
 // ----------------------------------------------------------------------------- host side
@@ -60,7 +91,7 @@ inline int64_t e_total(const moe_shape* s) {
 // non-negative with a total below 2^31; A >= BS * min(local_expert_num, K)).
 inline moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_NULL_ARG;
-  if (s->reserved != 0) return MOE_ERR_BAD_RANGE;
+  if (s->comm_quant_mode != 0 && s->comm_quant_mode != 2) return MOE_ERR_BAD_RANGE;
   if (s->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (s->mask_ndim < 0 || s->mask_ndim > 2) return MOE_ERR_BAD_RANGE;
   if (s->T < 0 || s->H <= 0 || (s->H % 8) != 0) return MOE_ERR_BAD_SHAPE;
@@ -90,6 +121,14 @@ inline moe_status check_ffn_shape(const moe_shape* s) {
   do {                                          \
     if (!(p) && (int64_t)(n) > 0) return MOE_ERR_NULL_ARG; \
   } while (0)
+
+// fp8 GEMMs: the 128-wide scale blocks must tile H and F exactly.
+inline moe_status check_fp8_shape(const moe_shape* s) {
+  moe_status st = check_ffn_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->H % 128 != 0 || s->F % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  return MOE_OK;
+}
 
 inline moe_status launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -66,6 +66,15 @@ struct GemmArgs {
   const bf16_t* aux;
   float* W0;
   float* W1;
+  // fp8 operands: e4m3 codes, A scales per (row, 128 of K) (row stride Kd/128),
+  // B scales per 128 x 128 block at sB[e*sbe + nblock*sbn + kblock*sbk]
+  const uint8_t* qA;
+  const float* sA;
+  const uint8_t* qB0;
+  const uint8_t* qB1;
+  const float* sB0;
+  const float* sB1;
+  int64_t sbe, sbn, sbk;
 };
 
 template <int BM>
@@ -119,7 +128,9 @@ struct Cfg {
   static constexpr int kSmem = cmax(kMain, kEpi);
 };
 
-template <int MODE, int BM, int BN>
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int MODE, int BM, int BN, bool FP8>
 __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gemm(GemmArgs g) {
   using C = Cfg<MODE, BM, BN>;
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
@@ -164,6 +175,172 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
   }
   const int64_t klen = kend - kbeg;
 
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // B-tile row of MFMA column tile j of this wave.  The gate/up forward tile
+  // holds BN/2 gate rows then the same BN/2 up rows, and each wave takes
+  // matching gate and up column tiles so SwiGLU pairs meet in one lane.
+  auto brow = [&](int j) -> int {
+    if constexpr (MODE == GATE_UP_FWD)
+      return (j < TJ / 2) ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - TJ / 2) * 32;
+    else
+      return wn * (BN / 2) + j * 32;
+  };
+  int arow[TI], brw[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) arow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) brw[j] = brow(j) + (lane & 31);
+
+  if constexpr (FP8) {
+  // fp8 path (K-contiguous e4m3 codes for both operands; K a multiple of 128).
+  // One K step is 128 codes = one 128-byte LDS row, two 32x32x64 MFMA sub-steps
+  // into a temporary, then acc += tmp * (A row scale * B block scale).
+  __shared__ float sAl[2][BM];
+  const int kc_c = (tid & 7) * 16;  // byte column of this thread's 16-byte chunk
+  const uint8_t* qa = g.qA + row0 * g.lda;
+  uint32_t aoff[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int r = (tid >> 3) + 32 * j;
+    aoff[j] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * g.lda + kc_c);
+  }
+  uint32_t boff[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r = (tid >> 3) + 32 * j;
+    int64_t n;
+    if constexpr (MODE == GATE_UP_FWD) {
+      n = n0 + (r & (BN / 2 - 1));
+      if (n >= g.F) n = g.F - 1;
+    } else {
+      n = n0 + r;
+      if (n >= g.N) n = g.N - 1;
+    }
+    boff[j] = (uint32_t)(n * g.ldb + kc_c);
+  }
+  const int64_t nks = g.Kd / 128;  // scale columns of A
+  const int srow = tid < BM ? (tid < rows_valid ? tid : rows_valid - 1) : 0;
+  // B bases and scale of K step kt (k0 = 128 kt): uniform across the workgroup
+  auto bsrc = [&](int64_t k0, int half) -> const uint8_t* {
+    if constexpr (MODE == GATE_UP_FWD) {
+      return (half ? g.qB1 : g.qB0) + (int64_t)e * g.bstride + k0;
+    } else if constexpr (MODE == GATE_UP_BWD_DATA) {
+      return k0 < g.F ? g.qB0 + (int64_t)e * g.bstride + k0 : g.qB1 + (int64_t)e * g.bstride + (k0 - g.F);
+    } else {
+      return g.qB0 + (int64_t)e * g.bstride + k0;
+    }
+  };
+  auto bscale = [&](int64_t k0, int half) -> float {
+    const int64_t kb = k0 / 128;
+    if constexpr (MODE == GATE_UP_FWD) {
+      const float* sb = half ? g.sB1 : g.sB0;
+      return sb[e * g.sbe + (n0 / 128) * g.sbn + kb * g.sbk];
+    } else if constexpr (MODE == GATE_UP_BWD_DATA) {
+      const int64_t fb = g.F / 128;
+      return kb < fb ? g.sB0[e * g.sbe + (n0 / 128) * g.sbn + kb * g.sbk]
+                     : g.sB1[e * g.sbe + (n0 / 128) * g.sbn + (kb - fb) * g.sbk];
+    } else {
+      return g.sB0[e * g.sbe + (n0 / 128) * g.sbn + kb * g.sbk];
+    }
+  };
+  uint4 ra[NA], rb[NB];
+  float rsa = 0.f;
+  auto load8 = [&](int64_t k0) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) ra[j] = *reinterpret_cast<const uint4*>(qa + aoff[j] + k0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const uint8_t* b = bsrc(k0, (MODE == GATE_UP_FWD) ? (j >= NB / 2) : 0);
+      rb[j] = *reinterpret_cast<const uint4*>(b + boff[j]);
+    }
+    if (tid < BM) rsa = g.sA[(row0 + srow) * nks + k0 / 128];
+  };
+  auto store8 = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      const int i = tid + kThreads * j;
+      *reinterpret_cast<uint4*>(As(st) + lds_off(i >> 3, i & 7)) = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int i = tid + kThreads * j;
+      *reinterpret_cast<uint4*>(Bs(st) + lds_off(i >> 3, i & 7)) = rb[j];
+    }
+    if (tid < BM) sAl[st][tid] = rsa;
+  };
+  auto compute8 = [&](int st, int64_t k0) {
+    const bf16_t* as = As(st);
+    const bf16_t* bs = Bs(st);
+    f32x16 tmp[TI][TJ];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 4 + (lane >> 5) * 2;
+      i32x8 fa[TI], fb[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(as + lds_off(arow[i], c));
+        const uint4 hi = *reinterpret_cast<const uint4*>(as + lds_off(arow[i], c + 1));
+        fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(bs + lds_off(brw[j], c));
+        const uint4 hi = *reinterpret_cast<const uint4*>(bs + lds_off(brw[j], c + 1));
+        fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          if (kk == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            // e4m3 x e4m3 (format 0 for both), unit E8M0 scales (127)
+            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], z, 0, 0, 0, 127, 0, 127);
+          } else {
+            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], tmp[i][j], 0, 0, 0,
+                                                                         127, 0, 127);
+          }
+        }
+    }
+    float sbv[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      sbv[j] = bscale(k0, (MODE == GATE_UP_FWD) ? (j >= TJ / 2) : 0);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = wm * (BM / 2) + i * 32 + q * 8 + (lane >> 5) * 4;
+        const float4 sa = *reinterpret_cast<const float4*>(&sAl[st][m]);
+        const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[i][j][q * 4 + t] += tmp[i][j][q * 4 + t] * (sav[t] * sbv[j]);
+      }
+  };
+  const int64_t nk = g.Kd / 128;
+  if (nk > 0) {
+    load8(0);
+    store8(0);
+    __syncthreads();
+  }
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int s = (int)(kt & 1);
+    if (kt + 1 < nk) load8((kt + 1) * 128);
+    compute8(s, kt * 128);
+    if (kt + 1 < nk) store8(s ^ 1);
+    __syncthreads();
+  }
+  } else {
   // Thread roles in one K step.
   //  K-contiguous operand of R rows: vector j (j < R/32) is row tid/8 + 32j,
   //  chunk tid%8.
@@ -319,28 +496,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     }
   };
 
-  f32x16 acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // B-tile row of MFMA column tile j of this wave.  The gate/up forward tile
-  // holds BN/2 gate rows then the same BN/2 up rows, and each wave takes
-  // matching gate and up column tiles so SwiGLU pairs meet in one lane.
-  auto brow = [&](int j) -> int {
-    if constexpr (MODE == GATE_UP_FWD)
-      return (j < TJ / 2) ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - TJ / 2) * 32;
-    else
-      return wn * (BN / 2) + j * 32;
-  };
-  int arow[TI], brw[TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i) arow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) brw[j] = brow(j) + (lane & 31);
 
   // MFMAs of one K step on LDS stage st; operand fragments of sub-step kk+1 are
   // read while the MFMAs of sub-step kk issue.
@@ -389,6 +545,8 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     compute(s);
     if (kt + 1 < nk) store_ab(s ^ 1, (kt + 1) * BK, ra, rb);
     __syncthreads();
+  }
+
   }
 
   // ---- epilogue.  acc[i][j][r] holds C(m, n) with
@@ -491,7 +649,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
   }
 }
 
-template <int MODE, int BM, int BN>
+template <int MODE, int BM, int BN, bool FP8>
 moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
   const int64_t bn_cols = MODE == GATE_UP_FWD ? BN / 2 : BN;
@@ -506,7 +664,7 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL((k_gemm<MODE, BM, BN>), dim3((unsigned)grid), dim3(kThreads), 0, strm, g);
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8>), dim3((unsigned)grid), dim3(kThreads), 0, strm, g);
   return launch_status();
 }
 
@@ -514,9 +672,9 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
 // tiles with two waves per SIMD beat 256 x 256 tiles with one wave per SIMD
 // (whose exposed load and barrier latency outweighs their halved LDS traffic),
 // so every mode runs 128 x 128.
-template <int MODE>
+template <int MODE, bool FP8 = false>
 moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
-  return launch_cfg<MODE, 128, 128>(g, s, strm);
+  return launch_cfg<MODE, 128, 128, FP8>(g, s, strm);
 }
 
 GemmArgs base_args(const moe_shape* s, const int32_t* prefix) {
@@ -698,4 +856,118 @@ extern "C" moe_status moe_grouped_ffn_bwd(const moe_shape* s, const void* grad_y
   if (st != MOE_OK) return st;
   return moe_ffn_gate_up_bwd_weight(s, grad_gate_up, expand_x, ep_recv_counts, grad_w_gate,
                                     grad_w_up, stream);
+}
+
+// ----------------------------------------------------------------------------- fp8 entries
+
+extern "C" moe_status moe_ffn_gate_up_fwd_fp8(const moe_shape* s, const uint8_t* xq,
+                                              const float* xs, const uint8_t* wgq,
+                                              const float* wgs, const uint8_t* wuq,
+                                              const float* wus, const int32_t* ep_recv_counts,
+                                              void* gate_up_save, void* h_act, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wgq || !wgs || !wuq || !wus || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!xq || !xs || !gate_up_save || !h_act) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = xq;
+  g.sA = xs;
+  g.lda = s->H;
+  g.qB0 = wgq;
+  g.qB1 = wuq;
+  g.sB0 = wgs;
+  g.sB1 = wus;
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.sbe = (s->F / 128) * (s->H / 128);  // (E, F/128, H/128): [e][n-block][k-block]
+  g.sbn = s->H / 128;
+  g.sbk = 1;
+  g.N = s->F;
+  g.Kd = s->H;
+  g.C0 = static_cast<bf16_t*>(h_act);
+  g.C1 = static_cast<bf16_t*>(gate_up_save);
+  return launch<GATE_UP_FWD, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_down_fwd_fp8(const moe_shape* s, const uint8_t* hq, const float* hs,
+                                           const uint8_t* wdq, const float* wds,
+                                           const int32_t* ep_recv_counts, void* y, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wdq || !wds || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!hq || !hs || !y) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = hq;
+  g.sA = hs;
+  g.lda = s->F;
+  g.qB0 = wdq;
+  g.sB0 = wds;
+  g.ldb = s->F;
+  g.bstride = s->H * s->F;
+  g.sbe = (s->H / 128) * (s->F / 128);  // (E, H/128, F/128): [e][n-block][k-block]
+  g.sbn = s->F / 128;
+  g.sbk = 1;
+  g.N = s->H;
+  g.Kd = s->F;
+  g.C0 = static_cast<bf16_t*>(y);
+  return launch<DOWN_FWD, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_down_bwd_data_fp8(const moe_shape* s, const uint8_t* dyq,
+                                                const float* dys, const uint8_t* wdq_t,
+                                                const float* wds, const void* gate_up_save,
+                                                const int32_t* ep_recv_counts, void* grad_gate_up,
+                                                void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wdq_t || !wds || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!dyq || !dys || !gate_up_save || !grad_gate_up) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = dyq;
+  g.sA = dys;
+  g.lda = s->H;
+  g.qB0 = wdq_t;  // (E, F, H): row f of expert e holds Wd_e[:, f]
+  g.sB0 = wds;    // scales of Wd (E, H/128, F/128): [e][k-block (h)][n-block (f)]
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.sbe = (s->H / 128) * (s->F / 128);
+  g.sbn = 1;
+  g.sbk = s->F / 128;
+  g.N = s->F;
+  g.Kd = s->H;
+  g.aux = static_cast<const bf16_t*>(gate_up_save);
+  g.C0 = static_cast<bf16_t*>(grad_gate_up);
+  return launch<DOWN_BWD_DATA, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_gate_up_bwd_data_fp8(const moe_shape* s, const uint8_t* dguq,
+                                                   const float* dgus, const uint8_t* wgq_t,
+                                                   const float* wgs, const uint8_t* wuq_t,
+                                                   const float* wus, const int32_t* ep_recv_counts,
+                                                   void* grad_expand_x, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wgq_t || !wgs || !wuq_t || !wus || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!dguq || !dgus || !grad_expand_x) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = dguq;
+  g.sA = dgus;
+  g.lda = 2 * s->F;
+  g.qB0 = wgq_t;  // (E, H, F): row h of expert e holds Wg_e[:, h]
+  g.qB1 = wuq_t;
+  g.sB0 = wgs;    // scales of Wg (E, F/128, H/128): [e][k-block (f)][n-block (h)]
+  g.sB1 = wus;
+  g.ldb = s->F;
+  g.bstride = s->F * s->H;
+  g.sbe = (s->F / 128) * (s->H / 128);
+  g.sbn = 1;
+  g.sbk = s->H / 128;
+  g.N = s->H;
+  g.Kd = 2 * s->F;
+  g.C0 = static_cast<bf16_t*>(grad_expand_x);
+  return launch<GATE_UP_BWD_DATA, true>(g, s, as_stream(stream));
 }

@@ -1,0 +1,135 @@
+// fp8 e4m3 quantisers of the fp8 FFN path.
+//
+//  * rows: one scale per (row, 128 consecutive columns), codes = e4m3(x * (448/amax)),
+//    scale = amax/448 (both fp32, correctly rounded); an all-zero block gets codes 0
+//    and scale 1.  16 lanes own one block (8 columns each), so the block's amax is
+//    a 16-lane butterfly and every load and store is a full vector.
+//  * weights: one scale per 128 x 128 block of each expert's (out, in) matrix, same
+//    rule; the kernel also writes the codes transposed, so the data-gradient GEMMs
+//    read their fp8 weights K-contiguous like the forward ones.  The block scales
+//    serve both layouts (the transposed GEMM indexes them with swapped block
+//    coordinates).
+//
+// The pages name FP8 only as a precision of the MoE layer performance tests
+// (Megatron-LM page, "Added Test Cases"); the block recipe is this library's.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_quant_rows_fp8(const uint4* __restrict__ src, int64_t R,
+                                                        int64_t C, const int32_t* __restrict__ nrows,
+                                                        uint2* __restrict__ codes,
+                                                        float* __restrict__ scales) {
+  const int64_t nb = C / 128;  // blocks per row
+  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // block id
+  const int sub = threadIdx.x & 15;
+  const int64_t row = g / nb, blk = g % nb;
+  const int64_t rows = nrows ? (int64_t)*nrows : R;
+  if (row >= R || row >= rows) return;  // a whole 16-lane group leaves together
+  const int64_t v = row * (C / 8) + blk * 16 + sub;  // 8-element vector index
+  float f[8];
+  unpack8(src[v], f);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__fmul_rn(f[i], inv)) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__fmul_rn(f[4 + i], inv)) << (8 * i);
+  codes[v] = make_uint2(lo, hi);
+  if (sub == 0) scales[row * nb + blk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+}
+
+// One 256-thread block per 128 x 128 weight block.  Thread t owns rows
+// t/16 + 16j (j < 8), columns 8*(t%16) .. +7.
+__global__ __launch_bounds__(256) void k_quant_weights_fp8(const uint4* __restrict__ w, int64_t N,
+                                                           int64_t Kd, uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ codes_t,
+                                                           float* __restrict__ scales) {
+  __shared__ float wmax[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tr[128 * 144];  // transposed tile, padded rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nbn = N / 128, nbk = Kd / 128;
+  const int64_t e = blockIdx.x / (nbn * nbk);
+  const int64_t rem = blockIdx.x % (nbn * nbk);
+  const int64_t bn = rem / nbk, bk = rem % nbk;
+  const int64_t n0 = bn * 128, k0 = bk * 128;
+  const int c8 = (tid & 15) * 8;
+  float f[8][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (tid >> 4) + 16 * j;
+    unpack8(w[((e * N + n0 + r) * Kd + k0 + c8) / 8], f[j]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[j][i]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (tid >> 4) + 16 * j;
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = f32_to_e4m3(__fmul_rn(f[j][i], inv));
+    const uint2 pk = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                                b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+    *reinterpret_cast<uint2*>(codes + (e * N + n0 + r) * Kd + k0 + c8) = pk;
+    if (codes_t) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) tr[(c8 + i) * 144 + r] = (uint8_t)b[i];
+    }
+  }
+  if (tid == 0) scales[(e * nbn + bn) * nbk + bk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  if (codes_t) {
+    __syncthreads();
+    // row c of the transposed block = column c of the block: 128 bytes = 8 x 16
+    for (int v = tid; v < 128 * 8; v += 256) {
+      const int c = v >> 3, part = (v & 7) * 16;
+      *reinterpret_cast<uint4*>(codes_t + (e * Kd + k0 + c) * N + n0 + part) =
+          *reinterpret_cast<const uint4*>(tr + c * 144 + part);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_quant_rows_fp8(int64_t R, int64_t C, const void* src,
+                                         const int32_t* nrows, uint8_t* codes, float* scales,
+                                         void* stream) {
+  if (R < 0 || C <= 0 || C % 128 != 0 || R * (C / 128) > ((int64_t)1 << 35))
+    return MOE_ERR_BAD_SHAPE;
+  if (R == 0) return MOE_OK;
+  if (!src || !codes || !scales) return MOE_ERR_NULL_ARG;
+  const int64_t groups = R * (C / 128);        // 16 lanes each
+  const int64_t blocks = (groups * 16 + 255) / 256;
+  hipLaunchKernelGGL(k_quant_rows_fp8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(src), R, C, nrows, reinterpret_cast<uint2*>(codes),
+                     scales);
+  return launch_status();
+}
+
+extern "C" moe_status moe_quantize_weights_fp8(int64_t E, int64_t N, int64_t Kdim, const void* w,
+                                               uint8_t* codes, uint8_t* codes_t, float* scales,
+                                               void* stream) {
+  if (E <= 0 || N <= 0 || Kdim <= 0 || N % 128 != 0 || Kdim % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  if (E * N * Kdim >= ((int64_t)1 << 40)) return MOE_ERR_BAD_SHAPE;
+  if (!w || !codes || !scales) return MOE_ERR_NULL_ARG;
+  const int64_t blocks = E * (N / 128) * (Kdim / 128);
+  if (blocks > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(k_quant_weights_fp8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(w), N, Kdim, codes, codes_t, scales);
+  return launch_status();
+}

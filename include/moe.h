@@ -77,7 +77,7 @@ typedef struct moe_shape {
   int32_t const_expert_num; /* Q >= 0: ids [E+Z+C, E+Z+C+Q) */
   int32_t mask_ndim;        /* 0: no x_active_mask, 1: (T,), 2: (T, K) */
   int32_t act_dtype;        /* MOE_DTYPE_BF16 */
-  int32_t reserved;         /* must be 0 */
+  int32_t comm_quant_mode;  /* 0: none; 2: int8 expert-output payload in combine (see moe_combine) */
 } moe_shape;
 
 /* Human-readable name of a status code (static string). */
@@ -85,7 +85,7 @@ const char* moe_status_str(moe_status st);
 
 /* Size of assist_info_for_combine in int32 elements: T*K (slot -> row) followed
  * by capacity (row -> slot).  Its contents are opaque to callers, like the
- * page's assist_info_for_combine (Parameters; Constraints: "pass it on"). */
+ * page's assist_info_for_combine (Parameters; Constraints: callers hand it to combine unchanged). */
 moe_status moe_assist_info_size(const moe_shape* s, int64_t* n_int32);
 
 /* Bytes of device workspace that moe_dispatch needs (for per-chunk expert
@@ -157,7 +157,10 @@ moe_status moe_ffn_down_fwd(const moe_shape* s, const void* h_act, const void* w
  * slot), ori_x[t] for a copy expert and alpha_1[j]*ori_x[t] + alpha_2[j]*v[j]
  * for constant expert j.  The sum runs in k order in fp32 with separately
  * rounded products (no fused multiply-add), the shared term is added last and
- * the result is rounded once to bf16.
+ * the result is rounded once to bf16.  With s->comm_quant_mode == 2 (the page's
+ * int8 communication quantisation, Parameters: comm_quant_mode) every routed
+ * slot's row of y is first replaced by its per-row symmetric int8 round trip,
+ * clamp(rint(y * (127/amax)), -127, 127) * (amax/127), amax = max |y| over the row.
  *  in   y                        (capacity, H) bf16 (rows < A are read)
  *  in   topk_idx                 (T, K) int32  (shape check only; routing is in assist info)
  *  in   topk_weights             (T, K) float32
@@ -180,7 +183,8 @@ moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* topk_id
  *   grad_y[row]          = bf16(topk_weights[t,k] * grad_out[t])      (routed rows)
  *   grad_topk_weights[t,k] = <v(t,k), grad_out[t]> in fp32 (0 for masked/zero slots)
  * The gradient of shared_expert_x is grad_out itself; the copy/const terms'
- * gradient to ori_x is added by moe_dispatch_bwd.
+ * gradient to ori_x is added by moe_dispatch_bwd.  With comm_quant_mode == 2 the
+ * dot product uses the int8 round trip of y, as the forward did.
  */
 moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, const void* y,
                            const int32_t* topk_idx, const float* topk_weights,
@@ -247,6 +251,59 @@ moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,
                             const float* topk_weights, const uint8_t* x_active_mask,
                             const void* grad_out, const void* const_alpha_1,
                             const void* grad_x_accum, void* grad_x, void* stream);
+
+/* ------------------------------------------------------------------ fp8 path
+ * Block-scaled OCP e4m3 (1-4-3, bias 7, max 448, round to nearest even,
+ * saturating): scale = amax/448 per block (fp32, 1 for an all-zero block),
+ * code = e4m3(x * (448/amax)), value = code * scale.  The forward GEMMs and the
+ * two data-gradient GEMMs of the FFN run on e4m3 operands with fp32
+ * accumulation (each 128-wide K block's partial sum times its A and B scales);
+ * the weight gradients keep the bf16 entries above.  The pages name FP8 only as
+ * a precision of the MoE layer performance tests (Megatron-LM page, Added Test
+ * Cases); the block recipe is this library's.  H and F must be multiples of 128.
+ */
+
+/* Rows of a bf16 (R, C) matrix to e4m3 with one scale per (row, 128 columns).
+ *  codes (R, C) uint8, scales (R, C/128) fp32.  nrows: optional device int32;
+ *  when given only rows < *nrows are written (e.g. ep_recv_counts + E-1). */
+moe_status moe_quant_rows_fp8(int64_t R, int64_t C, const void* src, const int32_t* nrows,
+                              uint8_t* codes, float* scales, void* stream);
+
+/* Expert weights (E, N, K) bf16 to e4m3 with one scale per 128 x 128 block:
+ *  codes (E, N, K) uint8, scales (E, N/128, K/128) fp32, and (optional) the
+ *  codes transposed per expert, codes_t (E, K, N), for the data-gradient GEMMs. */
+moe_status moe_quantize_weights_fp8(int64_t E, int64_t N, int64_t K, const void* w,
+                                    uint8_t* codes, uint8_t* codes_t, float* scales,
+                                    void* stream);
+
+/* fp8 moe_ffn_gate_up_fwd: xq/xs = moe_quant_rows_fp8 of expand_x (capacity, H);
+ * wgq/wgs, wuq/wus = moe_quantize_weights_fp8 of w_gate, w_up.  Outputs as the
+ * bf16 entry (gate_up_save, h_act in bf16). */
+moe_status moe_ffn_gate_up_fwd_fp8(const moe_shape* s, const uint8_t* xq, const float* xs,
+                                   const uint8_t* wgq, const float* wgs, const uint8_t* wuq,
+                                   const float* wus, const int32_t* ep_recv_counts,
+                                   void* gate_up_save, void* h_act, void* stream);
+
+/* fp8 moe_ffn_down_fwd: hq/hs = moe_quant_rows_fp8 of h_act (capacity, F);
+ * wdq/wds = moe_quantize_weights_fp8 of w_down.  y in bf16. */
+moe_status moe_ffn_down_fwd_fp8(const moe_shape* s, const uint8_t* hq, const float* hs,
+                                const uint8_t* wdq, const float* wds,
+                                const int32_t* ep_recv_counts, void* y, void* stream);
+
+/* fp8 moe_ffn_down_bwd_data: dyq/dys = moe_quant_rows_fp8 of grad_y (capacity, H);
+ * wdq_t = transposed codes of w_down (E, F, H), wds its block scales. */
+moe_status moe_ffn_down_bwd_data_fp8(const moe_shape* s, const uint8_t* dyq, const float* dys,
+                                     const uint8_t* wdq_t, const float* wds,
+                                     const void* gate_up_save, const int32_t* ep_recv_counts,
+                                     void* grad_gate_up, void* stream);
+
+/* fp8 moe_ffn_gate_up_bwd_data: dguq/dgus = moe_quant_rows_fp8 of grad_gate_up
+ * (capacity, 2F); wgq_t/wuq_t = transposed codes of w_gate, w_up (E, H, F). */
+moe_status moe_ffn_gate_up_bwd_data_fp8(const moe_shape* s, const uint8_t* dguq,
+                                        const float* dgus, const uint8_t* wgq_t, const float* wgs,
+                                        const uint8_t* wuq_t, const float* wus,
+                                        const int32_t* ep_recv_counts, void* grad_expand_x,
+                                        void* stream);
 
 #ifdef __cplusplus
 }

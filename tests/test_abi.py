@@ -86,8 +86,10 @@ def test_shape_validation_misc(L):
     s.act_dtype = 7
     assert ws(s)[0] == UNSUPPORTED
     s = S()
-    s.reserved = 1
+    s.comm_quant_mode = 1
     assert ws(s)[0] == BAD_RANGE
+    s.comm_quant_mode = 2
+    assert ws(s)[0] == OK
     n = ctypes.c_int64()
     assert L.moe_assist_info_size(ctypes.byref(S()), ctypes.byref(n)) == OK
     assert n.value == 8 * 8 + 8 * 8

@@ -1,0 +1,182 @@
+"""GPU parity of the fp8 path: e4m3 quantisers (bit-exact), block-scaled fp8 grouped
+GEMMs (forward and data gradients) and the int8 combine payload, against the
+oracle's fp8 functions.  Floating outputs of the fp8 GEMMs are held to
+max|err| <= 2e-2 * max(1, max|ref|) and relative L2 <= 2e-2 (the fp8 bar)."""
+import numpy as np
+import pytest
+import torch
+
+import dispatch_expert_gemm_amd as dm
+import moe_workloads as wl
+import oracle as orc
+from gpu_util import DEV, Run, bf, check_close, check_equal, dev, f32
+
+pytestmark = pytest.mark.gpu
+
+REL_FP8 = 2e-2
+
+
+def _u8(t):
+    return t.detach().cpu().numpy()
+
+
+def test_quant_rows_fp8_bit_exact():
+    rng = np.random.default_rng(31)
+    R, C = 70, 512
+    a = rng.standard_normal((R, C)).astype(np.float32)
+    a[3] = 0.0                                   # all-zero row
+    a[5, 128:256] = 0.0                          # all-zero block
+    a[7] *= 1e-4                                 # subnormal e4m3 range after scaling
+    a[9] *= 3e3                                  # large magnitudes
+    a[11, ::7] = 0.0
+    bits = wl.to_bf16_bits(a)
+    codes, scales = dm.quant_rows_fp8(bf(bits))
+    torch.cuda.synchronize()
+    q, s = orc.quant_e4m3_rows(orc.bf16_to_f32(bits))
+    check_equal("codes", _u8(codes), q)
+    check_equal("scales", scales.cpu().numpy(), s)
+    # only the first n rows when a device row count is given
+    codes2 = torch.full((R, C), 0xAB, dtype=torch.uint8, device=DEV)
+    scales2 = torch.zeros((R, C // 128), dtype=torch.float32, device=DEV)
+    dm.moe_quant_rows_fp8(bf(bits), codes2, scales2, nrows=torch.tensor([33], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    check_equal("codes rows<33", _u8(codes2)[:33], q[:33])
+    assert (_u8(codes2)[33:] == 0xAB).all()
+
+
+def test_quantize_weights_fp8_bit_exact():
+    rng = np.random.default_rng(32)
+    E, N, K = 3, 256, 384
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    w[1, :128, 128:256] = 0.0
+    bits = wl.to_bf16_bits(w)
+    q = dm.Fp8Weights.quantize(bf(bits))
+    torch.cuda.synchronize()
+    codes, scales = orc.quant_weights_fp8(bits)
+    check_equal("codes", _u8(q.codes), codes)
+    check_equal("codes_t", _u8(q.codes_t), codes.transpose(0, 2, 1))
+    check_equal("scales", q.scales.cpu().numpy(), scales)
+
+
+FP8_CASES = {
+    "small": dict(T=300, H=256, F=384, E=5, K=2),
+    "ragged_rows": dict(T=517, H=512, F=256, E=7, K=3),
+    "empty_experts": dict(T=40, H=128, F=128, E=12, K=1),
+}
+
+
+class Fp8Run(Run):
+    """The fp8 chain through the C entries, on top of the bf16 dispatch."""
+
+    def quant_weights(self):
+        self.wq = [dm.Fp8Weights.quantize(bf(self.inp[k])) for k in ("w_gate", "w_up", "w_down")]
+
+    def ffn8(self):
+        F, H, cap = self.shape.F, self.H, self.cap
+        nrows = self.d.ep_recv_counts[-1:]
+        self.xq, self.xs = dm.quant_rows_fp8(self.d.expand_x, nrows)
+        self.gus = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+        self.h = torch.empty((cap, F), dtype=torch.bfloat16, device=DEV)
+        self.y = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+        wg, wu, wd = self.wq
+        dm.moe_ffn_gate_up_fwd_fp8(self.shape, self.xq, self.xs, wg.codes, wg.scales, wu.codes, wu.scales,
+                                   self.d.ep_recv_counts, self.gus, self.h)
+        self.hq, self.hs = dm.quant_rows_fp8(self.h, nrows)
+        dm.moe_ffn_down_fwd_fp8(self.shape, self.hq, self.hs, wd.codes, wd.scales, self.d.ep_recv_counts,
+                                self.y)
+        torch.cuda.synchronize()
+
+    def ffn8_bwd_data(self, gy):
+        F, H, cap = self.shape.F, self.H, self.cap
+        nrows = self.d.ep_recv_counts[-1:]
+        wg, wu, wd = self.wq
+        dyq, dys = dm.quant_rows_fp8(gy, nrows)
+        ggu = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+        dm.moe_ffn_down_bwd_data_fp8(self.shape, dyq, dys, wd.codes_t, wd.scales, self.gus,
+                                     self.d.ep_recv_counts, ggu)
+        dguq, dgus = dm.quant_rows_fp8(ggu, nrows)
+        gxe = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+        dm.moe_ffn_gate_up_bwd_data_fp8(self.shape, dguq, dgus, wg.codes_t, wg.scales, wu.codes_t, wu.scales,
+                                        self.d.ep_recv_counts, gxe)
+        torch.cuda.synchronize()
+        return ggu, gxe
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES))
+def test_fp8_grouped_ffn_forward_and_data_gradients(name):
+    inp = wl.layer_inputs(seed=33, **FP8_CASES[name])
+    print(f"[fp8] case={name}", flush=True)
+    run = Fp8Run(inp)
+    run.dispatch()
+    run.quant_weights()
+    run.ffn8()
+    r = orc.route(inp["topk_idx"], inp["E"])
+    A, F = r.A, inp["F"]
+    X = orc.dispatch(inp["x"], r)
+    wq = tuple(orc.quant_weights_fp8(inp[k]) for k in ("w_gate", "w_up", "w_down"))
+    G, U, Hh, Y = orc.ffn_fwd_fp8(X, r.ep_recv_counts, *wq)
+    check_close("G", f32(run.gus[:A, :F]), G, rel_l2=REL_FP8)
+    check_close("U", f32(run.gus[:A, F:]), U, rel_l2=REL_FP8)
+    check_close("h", f32(run.h[:A]), Hh, rel_l2=REL_FP8)
+    check_close("y", f32(run.y[:A]), Y, rel_l2=REL_FP8)
+    # data gradients from a bf16 dY of realistic scale (w * dOut ~ 0.125 N(0,1))
+    dY_bits = wl.to_bf16_bits(np.random.default_rng(34).standard_normal((run.cap, inp["H"]),
+                                                                       dtype=np.float32) * 0.125)
+    ggu, gxe = run.ffn8_bwd_data(bf(dY_bits))
+    dGU, dX, _, _, _ = orc.ffn_bwd_fp8(orc.bf16_to_f32(dY_bits)[:A], X, G, U, Hh, r.ep_recv_counts, *wq)
+    check_close("grad_gate_up", f32(ggu[:A]), dGU, rel_l2=REL_FP8)
+    check_close("grad_expand_x", f32(gxe[:A]), dX, rel_l2=REL_FP8)
+
+
+@pytest.mark.parametrize("special", [False, True])
+def test_int8_payload_combine(special):
+    kw = dict(T=201, H=256, E=8, K=4)
+    if special:
+        kw.update(Z=1, C=1, Q=2, mask="2d")
+    inp = wl.layer_inputs(seed=35, weights=False, F=0, **kw)
+    cap = kw["T"] * min(kw["E"], kw["K"])
+    y_bits = wl.to_bf16_bits(np.random.default_rng(36).standard_normal((cap, kw["H"]), dtype=np.float32))
+    run = Run(inp)
+    run.shape.comm_quant_mode = 2
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"], inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0), inp.get("mask"))
+    y = bf(y_bits)
+    out = run.combine(y=y)
+    Yc = orc.qdq_rows_int8(orc.bf16_to_f32(y_bits)[:r.A])
+    ref = orc.combine(Yc, r, inp["topk_weights"], None, inp["x"], inp.get("const_alpha_1"),
+                      inp.get("const_alpha_2"), inp.get("const_v"))
+    check_equal("out", f32(out), ref)
+    gy, gw = run.combine_bwd(bf(inp["grad_out"]), y=y)
+    dY, dw = orc.combine_bwd(inp["grad_out"], Yc, r, inp["topk_weights"], inp["x"], inp.get("const_alpha_1"),
+                             inp.get("const_alpha_2"), inp.get("const_v"))
+    check_equal("grad_y", f32(gy[:r.A]), dY)
+    check_close("grad_topk_weights", f32(gw), dw, max_abs=1e-3, rel_l2=1e-5)
+
+
+def test_fp8_layer_forward_backward():
+    """The whole fp8 step (int8 combine payload, bf16 weight gradients) vs the oracle."""
+    inp = wl.layer_inputs(400, 256, 256, 6, 2, seed=37)
+    run = Fp8Run(inp)
+    run.shape.comm_quant_mode = 2
+    run.dispatch()
+    run.quant_weights()
+    run.ffn8()
+    out = run.combine()
+    g = bf(inp["grad_out"])
+    gy, gw = run.combine_bwd(g)
+    ggu, gxe = run.ffn8_bwd_data(gy)
+    E, F, H = inp["E"], inp["F"], inp["H"]
+    gwg = torch.empty((E, F, H), dtype=torch.float32, device=DEV)
+    gwu = torch.empty((E, F, H), dtype=torch.float32, device=DEV)
+    gwd = torch.empty((E, H, F), dtype=torch.float32, device=DEV)
+    dm.moe_ffn_down_bwd_weight(run.shape, gy, run.h, run.d.ep_recv_counts, gwd)
+    dm.moe_ffn_gate_up_bwd_weight(run.shape, ggu, run.d.expand_x, run.d.ep_recv_counts, gwg, gwu)
+    gx = run.dispatch_bwd(gxe, g)
+    f = orc.layer_fwd_fp8(inp)
+    b = orc.layer_bwd_fp8(inp, f, inp["grad_out"])
+    check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
+    check_close("grad_topk_weights", f32(gw), b["dw"], rel_l2=REL_FP8)
+    check_close("grad_x", f32(gx), b["dx"], rel_l2=REL_FP8)
+    check_close("grad_w_gate", f32(gwg), b["dWg"], rel_l2=REL_FP8)
+    check_close("grad_w_up", f32(gwu), b["dWu"], rel_l2=REL_FP8)
+    check_close("grad_w_down", f32(gwd), b["dWd"], rel_l2=REL_FP8)
