@@ -10,9 +10,15 @@ the one GPU.
 
 Prints one JSON line.  `value` is the step's algorithmic GEMM throughput
 (18*A*H*F FLOP per step, A = routed rows) in TFLOP/s; `roofline` is the dominant
-GEMM kernel's FLOP rate against the bf16 MFMA peak, timed with HIP events on the
-stream the kernels run on; `combine` is the combine kernel's algorithmic
+GEMM kernel's FLOP rate against the MFMA peak of its dtype, timed with HIP events
+on the stream the kernels run on; `combine` is the combine kernel's algorithmic
 bandwidth against HBM; `cpu_baseline` is the CPU oracle on a bounded sample.
+
+`--workload` picks extra measurements (not the default line): `dsv3_proxy`
+(T=4096, hidden 7168, ffn 2048, 32 experts, top-8, Zipf-skewed routing, one
+shared expert run as a one-group GEMM over all tokens) and `mixtral` (T=8192,
+hidden 4096, ffn 14336, 8 experts, top-2, fp8 e4m3 block-scaled forward and
+data-gradient GEMMs, bf16 weight gradients, int8 combine payload).
 """
 from __future__ import annotations
 
@@ -28,10 +34,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# page1 is the default (the benchmark line); the others are extra measurements
 WORKLOADS = {
     "page1": dict(T=8192, H=1536, F=480, E=64, K=8),
+    "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
+    "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
 }
 
 
@@ -92,20 +102,181 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    inp = wl.layer_inputs(T_sample, cfg["H"], cfg["F"], cfg["E"], cfg["K"], seed=0)
+    fp8 = cfg.get("fp8", False)
+    inp = wl.layer_inputs(T_sample, cfg["H"], cfg["F"], cfg["E"], cfg["K"], seed=0,
+                          zipf=cfg.get("zipf"), shared=cfg.get("shared", False))
     runs, t0 = 0, time.perf_counter()
     while True:
-        f = orc.layer_fwd(inp, prec="parity")
-        orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
+        if fp8:
+            f = orc.layer_fwd_fp8(inp)
+            orc.layer_bwd_fp8(inp, f, inp["grad_out"])
+        else:
+            f = orc.layer_fwd(inp, prec="parity")
+            orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
         runs += 1
         el = time.perf_counter() - t0
         if el >= seconds or runs >= 50:
             break
     A = f["route"].A
-    flops = 18.0 * A * cfg["H"] * cfg["F"] * runs
+    flops = 18.0 * (A + (T_sample if cfg.get("shared") else 0)) * cfg["H"] * cfg["F"] * runs
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{runs} oracle fwd+bwd runs (parity mode, numpy) of a {T_sample}-token slice of the "
                       f"same workload (H={cfg['H']} F={cfg['F']} E={cfg['E']} K={cfg['K']}), {el:.1f} s"}
+
+
+class Step:
+    """The C-entry calls of one fwd+bwd step of a workload (name, thunk), in order,
+    plus calls timed outside the step (fp8 weight quantisation)."""
+
+    def __init__(self):
+        self.calls, self.config, self.cfg = [], {}, {}
+        self.recv = self.err = None
+        self.dtype = "bf16"
+        self.extra_calls = []
+
+
+def _bf(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def build_step(name, T_override=None):
+    import torch
+    import dispatch_expert_gemm_amd as dm
+    import moe_workloads as wl
+
+    cfg = dict(WORKLOADS[name])
+    if T_override:
+        cfg["T"] = T_override
+    T, H, F, E, K = cfg["T"], cfg["H"], cfg["F"], cfg["E"], cfg["K"]
+    dev = torch.device("cuda:0")
+    shared = cfg.get("shared", False)
+    fp8 = cfg.get("fp8", False)
+    log(f"[bench] {name}: generating inputs T={T} H={H} F={F} E={E} K={K}")
+    inp = wl.layer_inputs(T, H, F, E, K, seed=0, zipf=cfg.get("zipf"), shared=shared)
+    x, gout = _bf(inp["x"], dev), _bf(inp["grad_out"], dev)
+    wg, wu, wd = (_bf(inp[k], dev) for k in ("w_gate", "w_up", "w_down"))
+    del inp["w_gate"], inp["w_up"], inp["w_down"]
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_weights"]).to(dev)
+    shape = dm.make_shape(T, H, K, E, F=F, comm_quant_mode=2 if fp8 else 0)
+    cap = shape.capacity
+    bf16, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    z = lambda *sh, dt=bf16: torch.empty(sh, dtype=dt, device=dev)
+    ex, assist = z(cap, H), z(dm.moe_assist_info_size(shape), dt=i32)
+    cnt, recv, err = z(E, dt=i32), z(E, dt=i32), z(1, dt=i32)
+    ws = z(dm.moe_workspace_size(shape), dt=torch.uint8)
+    gus, h, y, out = z(cap, 2 * F), z(cap, F), z(cap, H), z(T, H)
+    gy, gw, ggu, gxe, gx = z(cap, H), z(T, K, dt=f32), z(cap, 2 * F), z(cap, H), z(T, H)
+    gwg, gwu, gwd = z(E, F, H, dt=f32), z(E, F, H, dt=f32), z(E, H, F, dt=f32)
+    st = Step()
+    st.recv, st.err = recv, err
+    C = st.calls
+    C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
+    sy = sdx = None
+    if fp8:
+        st.dtype = "fp8 e4m3 (fwd + data grads), bf16 (weight grads)"
+        nrows = recv[-1:]
+        wq = [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)]
+        xq, xs = z(cap, H, dt=torch.uint8), z(cap, H // 128, dt=f32)
+        hq, hs = z(cap, F, dt=torch.uint8), z(cap, F // 128, dt=f32)
+        dyq, dys = z(cap, H, dt=torch.uint8), z(cap, H // 128, dt=f32)
+        dgq, dgs = z(cap, 2 * F, dt=torch.uint8), z(cap, 2 * F // 128, dt=f32)
+        C += [
+            ("moe_quant_rows_fp8 (x)", lambda: dm.moe_quant_rows_fp8(ex, xq, xs, nrows)),
+            ("moe_ffn_gate_up_fwd_fp8", lambda: dm.moe_ffn_gate_up_fwd_fp8(
+                shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h)),
+            ("moe_quant_rows_fp8 (h)", lambda: dm.moe_quant_rows_fp8(h, hq, hs, nrows)),
+            ("moe_ffn_down_fwd_fp8", lambda: dm.moe_ffn_down_fwd_fp8(shape, hq, hs, wq[2].codes, wq[2].scales,
+                                                                     recv, y)),
+        ]
+    else:
+        C += [
+            ("moe_ffn_gate_up_fwd", lambda: dm.moe_ffn_gate_up_fwd(shape, ex, wg, wu, recv, gus, h)),
+            ("moe_ffn_down_fwd", lambda: dm.moe_ffn_down_fwd(shape, h, wd, recv, y)),
+        ]
+    if shared:
+        swg, swu, swd = (_bf(inp[k], dev) for k in ("shared_w_gate", "shared_w_up", "shared_w_down"))
+        ss = dm.shared_expert_shape(T, H, F)
+        scnt = torch.full((1,), T, dtype=i32, device=dev)
+        s_gus, s_h, sy = z(T, 2 * F), z(T, F), z(T, H)
+        s_ggu, sdx = z(T, 2 * F), z(T, H)
+        s_gw = [z(1, F, H, dt=f32), z(1, F, H, dt=f32), z(1, H, F, dt=f32)]
+        C += [
+            ("shared moe_ffn_gate_up_fwd", lambda: dm.moe_ffn_gate_up_fwd(ss, x, swg, swu, scnt, s_gus, s_h)),
+            ("shared moe_ffn_down_fwd", lambda: dm.moe_ffn_down_fwd(ss, s_h, swd, scnt, sy)),
+        ]
+    C += [
+        ("moe_combine", lambda: dm.moe_combine(shape, y, idx, w, assist, recv, None, sy, x, None, None, None,
+                                               out)),
+        ("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x, None,
+                                                       None, None, gy, gw)),
+    ]
+    if fp8:
+        C += [
+            ("moe_quant_rows_fp8 (dY)", lambda: dm.moe_quant_rows_fp8(gy, dyq, dys, nrows)),
+            ("moe_ffn_down_bwd_data_fp8", lambda: dm.moe_ffn_down_bwd_data_fp8(
+                shape, dyq, dys, wq[2].codes_t, wq[2].scales, gus, recv, ggu)),
+            ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
+            ("moe_quant_rows_fp8 (dGU)", lambda: dm.moe_quant_rows_fp8(ggu, dgq, dgs, nrows)),
+            ("moe_ffn_gate_up_bwd_data_fp8", lambda: dm.moe_ffn_gate_up_bwd_data_fp8(
+                shape, dgq, dgs, wq[0].codes_t, wq[0].scales, wq[1].codes_t, wq[1].scales, recv, gxe)),
+            ("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
+                                                                                 gwu)),
+        ]
+    else:
+        C += [
+            ("moe_ffn_down_bwd_data", lambda: dm.moe_ffn_down_bwd_data(shape, gy, wd, gus, recv, ggu)),
+            ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
+            ("moe_ffn_gate_up_bwd_data", lambda: dm.moe_ffn_gate_up_bwd_data(shape, ggu, wg, wu, recv, gxe)),
+            ("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
+                                                                                 gwu)),
+        ]
+    if shared:
+        C.append(("shared moe_grouped_ffn_bwd (4 GEMMs)", lambda: dm.moe_grouped_ffn_bwd(
+            ss, gout, x, s_gus, s_h, swg, swu, swd, scnt, s_ggu, sdx, *s_gw)))
+    C.append(("moe_dispatch_bwd", lambda: dm.moe_dispatch_bwd(shape, gxe, assist, idx, w, None, gout, None, sdx,
+                                                              gx)))
+    st.config = {"T": T, "H": H, "F": F, "E": E, "K": K}
+    st.cfg = cfg
+    st.shape_info = (T, H, F, K, E)
+    if fp8:
+        # weight quantisation (once per weight update) is timed outside the step
+        st.extra_calls = [("moe_quantize_weights_fp8 (3 tensors)",
+                           lambda: [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)])]
+    else:
+        st.extra_calls = []
+    return st
+
+
+def account(st, A):
+    """FLOP and byte counts of every call of the step, given the routed rows A."""
+    T, H, F, K, E = st.shape_info
+    fp8 = st.cfg.get("fp8", False)
+    pk = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    fl = {}
+    for n, (mult, peak) in {"moe_ffn_gate_up_fwd": (4, pk), "moe_ffn_down_fwd": (2, pk),
+                            "moe_ffn_down_bwd_data": (2, pk), "moe_ffn_down_bwd_weight": (2, PEAK_BF16_TFLOPS),
+                            "moe_ffn_gate_up_bwd_data": (4, pk),
+                            "moe_ffn_gate_up_bwd_weight": (4, PEAK_BF16_TFLOPS)}.items():
+        key = n + "_fp8" if fp8 and ("fwd" in n or "data" in n) else n
+        fl[key] = (mult * A * H * F, peak)
+    if st.cfg.get("shared"):
+        fl["shared moe_ffn_gate_up_fwd"] = (4 * T * H * F, PEAK_BF16_TFLOPS)
+        fl["shared moe_ffn_down_fwd"] = (2 * T * H * F, PEAK_BF16_TFLOPS)
+        fl["shared moe_grouped_ffn_bwd (4 GEMMs)"] = (12 * T * H * F, PEAK_BF16_TFLOPS)
+    nb = {}
+    for n in ("moe_dispatch", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd"):
+        nb[n] = bytes_moved(n, T, H, F, K, A, E)
+    if st.cfg.get("shared"):
+        nb["moe_combine"] += T * H * 2
+        nb["moe_dispatch_bwd"] += T * H * 2
+    if fp8:
+        nb["moe_quant_rows_fp8 (x)"] = A * H * 3 + A * H // 128 * 4
+        nb["moe_quant_rows_fp8 (h)"] = A * F * 3 + A * F // 128 * 4
+        nb["moe_quant_rows_fp8 (dY)"] = A * H * 3 + A * H // 128 * 4
+        nb["moe_quant_rows_fp8 (dGU)"] = A * 2 * F * 3 + A * 2 * F // 128 * 4
+    return fl, nb
 
 
 def main():
@@ -127,61 +298,9 @@ def main():
         sys.exit(2)
 
     import torch
-    import dispatch_expert_gemm_amd as dm
-    import moe_workloads as wl
 
-    cfg = dict(WORKLOADS[args.workload])
-    if args.tokens:
-        cfg["T"] = args.tokens
-    T, H, F, E, K = cfg["T"], cfg["H"], cfg["F"], cfg["E"], cfg["K"]
-    dev = torch.device("cuda:0")
-    log(f"[bench] generating inputs T={T} H={H} F={F} E={E} K={K}")
-    inp = wl.layer_inputs(T, H, F, E, K, seed=0)
-
-    def bf(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x, gout = bf(inp["x"]), bf(inp["grad_out"])
-    wg, wu, wd = bf(inp["w_gate"]), bf(inp["w_up"]), bf(inp["w_down"])
-    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
-    w = torch.from_numpy(inp["topk_weights"]).to(dev)
-    shape = dm.make_shape(T, H, K, E, F=F)
-    cap = shape.capacity
-    bf16, f32, i32 = torch.bfloat16, torch.float32, torch.int32
-    ex = torch.empty((cap, H), dtype=bf16, device=dev)
-    assist = torch.empty(dm.moe_assist_info_size(shape), dtype=i32, device=dev)
-    cnt = torch.empty(E, dtype=i32, device=dev)
-    recv = torch.empty(E, dtype=i32, device=dev)
-    err = torch.empty(1, dtype=i32, device=dev)
-    ws = torch.empty(dm.moe_workspace_size(shape), dtype=torch.uint8, device=dev)
-    gus = torch.empty((cap, 2 * F), dtype=bf16, device=dev)
-    h = torch.empty((cap, F), dtype=bf16, device=dev)
-    y = torch.empty((cap, H), dtype=bf16, device=dev)
-    out = torch.empty((T, H), dtype=bf16, device=dev)
-    gy = torch.empty((cap, H), dtype=bf16, device=dev)
-    gw = torch.empty((T, K), dtype=f32, device=dev)
-    ggu = torch.empty((cap, 2 * F), dtype=bf16, device=dev)
-    gxe = torch.empty((cap, H), dtype=bf16, device=dev)
-    gwg = torch.empty((E, F, H), dtype=f32, device=dev)
-    gwu = torch.empty((E, F, H), dtype=f32, device=dev)
-    gwd = torch.empty((E, H, F), dtype=f32, device=dev)
-    gx = torch.empty((T, H), dtype=bf16, device=dev)
-
-    calls = [
-        ("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)),
-        ("moe_ffn_gate_up_fwd", lambda: dm.moe_ffn_gate_up_fwd(shape, ex, wg, wu, recv, gus, h)),
-        ("moe_ffn_down_fwd", lambda: dm.moe_ffn_down_fwd(shape, h, wd, recv, y)),
-        ("moe_combine", lambda: dm.moe_combine(shape, y, idx, w, assist, recv, None, None, x, None, None,
-                                               None, out)),
-        ("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x, None,
-                                                       None, None, gy, gw)),
-        ("moe_ffn_down_bwd_data", lambda: dm.moe_ffn_down_bwd_data(shape, gy, wd, gus, recv, ggu)),
-        ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
-        ("moe_ffn_gate_up_bwd_data", lambda: dm.moe_ffn_gate_up_bwd_data(shape, ggu, wg, wu, recv, gxe)),
-        ("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg, gwu)),
-        ("moe_dispatch_bwd", lambda: dm.moe_dispatch_bwd(shape, gxe, assist, idx, w, None, gout, None, None,
-                                                         gx)),
-    ]
+    st = build_step(args.workload, args.tokens)
+    calls = st.calls
 
     def step():
         for _, fn in calls:
@@ -191,8 +310,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    A = int(recv[-1].item())
-    assert int(err.item()) == 0
+    A = int(st.recv[-1].item())
+    assert int(st.err.item()) == 0
 
     # timed region: K whole steps, synchronised on both sides
     log(f"[bench] timing {args.steps} steps")
@@ -216,24 +335,40 @@ def main():
     torch.cuda.synchronize()
     per = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
            for i, (name, _) in enumerate(calls)}
+    extra = {}
+    for name, fn in st.extra_calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        extra[name] = {"ms": round(e0.elapsed_time(e1), 4)}
 
-    fl = gemm_flops(A, H, F)
-    total_flops = sum(fl.values())
+    fl, nb = account(st, A)
+    total_flops = sum(f for f, _ in fl.values())
     dom = max(fl, key=lambda k: per[k])
-    achieved = fl[dom] / (per[dom] * 1e-3) / 1e12
+    dflop, dpeak = fl[dom]
+    achieved = dflop / (per[dom] * 1e-3) / 1e12
     kernels = {}
     for name, ms in per.items():
         rec = {"ms": round(ms, 4)}
         if name in fl:
-            rec["TFLOP/s"] = round(fl[name] / (ms * 1e-3) / 1e12, 1)
-            rec["frac_mfma"] = round(rec["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
-        b = bytes_moved(name, T, H, F, K, A, E)
-        if b is not None:
-            rec["GB/s"] = round(b / (ms * 1e-3) / 1e9, 1)
+            f, pk = fl[name]
+            rec["TFLOP/s"] = round(f / (ms * 1e-3) / 1e12, 1)
+            rec["frac_mfma"] = round(rec["TFLOP/s"] / pk, 4)
+        if nb.get(name) is not None:
+            rec["GB/s"] = round(nb[name] / (ms * 1e-3) / 1e9, 1)
             rec["frac_hbm"] = round(rec["GB/s"] / PEAK_HBM_GBS, 4)
         kernels[name] = rec
     gemm_ms = sum(per[k] for k in fl)
-
+    ideal_ms = sum(f / (pk * 1e12) for f, pk in fl.values()) * 1e3
+    T, H, F, E, K = (st.config[k] for k in ("T", "H", "F", "E", "K"))
+    descr = {
+        "page1": "Triton-distributed benchmark shape",
+        "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
+        "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
+    }[args.workload]
     res = {
         "metric": "MoE layer fwd+bwd ms & TFLOP/s (% MFMA peak); combine GB/s (% HBM) at 1 GPU",
         "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
@@ -245,32 +380,41 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": st.dtype,
         "data": "synthetic",
-        "config": {"workload": f"MoE layer fwd+bwd, Triton-distributed benchmark shape: T={T} tokens, "
-                               f"H={H}, F={F} SwiGLU, E={E} experts on one GPU, top-{K}",
+        "config": {"workload": f"MoE layer fwd+bwd, {descr}: T={T} tokens, H={H}, F={F} SwiGLU, "
+                               f"E={E} experts on one GPU, top-{K}",
                    "T": T, "H": H, "F": F, "E": E, "K": K, "routed_rows": A,
                    "flop_per_step": total_flops},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom)},
+                     "peak": dpeak, "unit": "TFLOP/s",
+                     "frac": round(achieved / dpeak, 4),
+                     "traffic": measured_traffic(dom) if args.workload == "page1" and not args.tokens else None},
         "combine": {"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
                     "frac": kernels["moe_combine"]["frac_hbm"]},
         "gemm_ms_per_step": round(gemm_ms, 4),
-        "gemm_frac_mfma": round(total_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gemm_frac_of_mfma_roofline": round(ideal_ms / gemm_ms, 4),
         "kernels": kernels,
-        "context": {"page1_fwd_bwd_ms_4_nvidia_gpus_T8192": 5.488},
     }
+    if extra:
+        res["outside_step"] = extra
+    if args.workload == "page1":
+        res["context"] = {"page1_fwd_bwd_ms_4_nvidia_gpus_T8192": 5.488}
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    if not args.no_cpu_baseline:
+    if args.no_cpu_baseline:
+        pass
+    elif st.cfg.get("fp8"):
+        # the oracle re-quantises all expert weights blockwise per run (minutes at this size)
+        res["cpu_baseline"] = None
+    else:
         log("[bench] CPU oracle baseline")
-        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(st.cfg, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

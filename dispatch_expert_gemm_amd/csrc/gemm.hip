@@ -30,9 +30,9 @@
 // Expert counts stay on the device: the grid covers floor(capacity/BM) + E row
 // tiles per column tile, and each workgroup finds its expert from the prefix
 // counts with one wave ballot (expert e owns row-tile slots starting at
-// prefix[e-1]/BM + e); surplus workgroups exit at once.  Workgroup ids are
-// remapped so that consecutive tiles (sharing A rows and expert weights) land on
-// the same XCD and its L2.
+// prefix[e-1]/BM + e); surplus workgroups exit at once.  In the row-grouped
+// GEMMs workgroup ids are remapped so that consecutive tiles (sharing A rows
+// and expert weights) land on the same XCD and its L2.
 #include "common.hpp"
 
 namespace moe {
@@ -49,6 +49,9 @@ enum Mode : int {
 
 constexpr int BK = 64;
 constexpr int kThreads = 256;
+// buffer resource word 3 for raw (untyped, unswizzled) buffer loads on gfx9:
+// 32-bit data format, so every access is checked against the byte range only
+constexpr int kBufferFlags = 0x00020000;
 
 struct GemmArgs {
   const bf16_t* A;
@@ -146,7 +149,15 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
 
   const int64_t nb = gridDim.x;
   const int64_t bid = blockIdx.x;
-  const int64_t logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+  // Row-grouped GEMMs: XCD x (workgroups dispatch round-robin over the eight
+  // XCDs) takes the x-th contiguous eighth of the tiles; the work per row tile
+  // is the same for every expert, so the eighths are balanced.  Expert-grouped
+  // (weight-gradient) GEMMs keep the dispatch order: a tile's work grows with
+  // its expert's row count, and contiguous eighths would give the XCD holding
+  // the most popular experts most of the work under skewed routing; round-robin
+  // gives every XCD an equal share of every expert, and XCD x then reads only
+  // the B column strips nt = x (mod 8) when n_tiles is a multiple of eight.
+  const int64_t logical = Cfg<MODE, BM, BN>::KGROUP ? bid : (bid & 7) * (nb >> 3) + (bid >> 3);
   if (logical >= g.tiles) return;
 
   int e;
@@ -345,14 +356,24 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
   //  K-contiguous operand of R rows: vector j (j < R/32) is row tid/8 + 32j,
   //  chunk tid%8.
   //  K-strided operand of R columns: block q (q < R/128) covers k rows
-  //  4*k4 .. 4*k4+3 of the 8 columns from x8, with p = tid + 256q,
-  //  x8 = 8*(p % (R/8)), k4 = p / (R/8); transposed in registers and written as
-  //  8 x 8-byte LDS stores.
+  //  4*k4 .. 4*k4+3 of the 8 columns from x8, transposed in registers and
+  //  written as 8 x 8-byte LDS stores.  With p = tid + 256q, the low three bits
+  //  of p pick eight neighbouring column groups and bit 3 the two k4 halves of
+  //  one 16-byte chunk, so the 16 lanes of one LDS store cycle write 16
+  //  distinct 8-byte bank slots.
   const int kc_c = (tid & 7) * 8;
-  auto xa8 = [&](int q) { return ((tid + kThreads * q) % (BM / 8)) * 8; };
-  auto ka4 = [&](int q) { return (tid + kThreads * q) / (BM / 8); };
-  auto xb8 = [&](int q) { return ((tid + kThreads * q) % (BN / 8)) * 8; };
-  auto kb4 = [&](int q) { return (tid + kThreads * q) / (BN / 8); };
+  auto xcol = [&](int q, int R) {
+    const int p = tid + kThreads * q;
+    return (((p >> 4) % (R / 64)) * 8 + (p & 7)) * 8;
+  };
+  auto krow4 = [&](int q, int R) {
+    const int p = tid + kThreads * q;
+    return ((p >> 4) / (R / 64)) * 2 + ((p >> 3) & 1);
+  };
+  auto xa8 = [&](int q) { return xcol(q, BM); };
+  auto ka4 = [&](int q) { return krow4(q, BM); };
+  auto xb8 = [&](int q) { return xcol(q, BN); };
+  auto kb4 = [&](int q) { return krow4(q, BN); };
   auto ld16 = [](const bf16_t* base, uint32_t off) -> uint4 {
     return *reinterpret_cast<const uint4*>(base + off);
   };
@@ -362,15 +383,18 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
   };
   // Uniform operand bases and per-lane 32-bit element offsets (every operand
-  // slice addressed from one base stays below 2^31 elements).
+  // slice addressed from one base stays below 2^31 elements).  The byte
+  // offsets fa_off/fb_off serve full K steps: the K position goes into the
+  // uniform base, so a load costs no vector arithmetic.
   const bf16_t* abase;
-  uint32_t aoff[NA];
+  uint32_t aoff[NA], fa_off[NA];
   if constexpr (!KGROUP) {
     abase = g.A + row0 * g.lda;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       const int r = (tid >> 3) + 32 * j;
       aoff[j] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * g.lda + kc_c);
+      fa_off[j] = aoff[j] * 2;
     }
   } else {
     abase = g.A + kbeg * g.lda;
@@ -378,12 +402,15 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     for (int q = 0; q < NA / 4; ++q) {
       const int64_t col = row0 + xa8(q) < g.M ? row0 + xa8(q) : g.M - 8;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) aoff[4 * q + j] = (uint32_t)col;
+      for (int j = 0; j < 4; ++j) {
+        aoff[4 * q + j] = (uint32_t)col;
+        fa_off[4 * q + j] = (uint32_t)(((4 * ka4(q) + j) * g.lda + col) * 2);
+      }
     }
   }
   const bf16_t* bbase0;
   const bf16_t* bbase1;
-  uint32_t boff[NB];
+  uint32_t boff[NB], fb_off[NB];
   if constexpr (B_KC) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -397,6 +424,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
         if (n >= g.N) n = g.N - 1;
       }
       boff[j] = (uint32_t)(n * g.ldb + kc_c);
+      fb_off[j] = boff[j] * 2;
     }
     bbase0 = g.B0 + (int64_t)e * g.bstride;
     bbase1 = (MODE == GATE_UP_FWD) ? g.B1 + (int64_t)e * g.bstride : bbase0;
@@ -405,7 +433,10 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     for (int q = 0; q < NB / 4; ++q) {
       const int64_t col = n0 + xb8(q) < g.N ? n0 + xb8(q) : g.N - 8;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) boff[4 * q + j] = (uint32_t)col;
+      for (int j = 0; j < 4; ++j) {
+        boff[4 * q + j] = (uint32_t)col;
+        fb_off[4 * q + j] = (uint32_t)(((4 * kb4(q) + j) * g.ldb + col) * 2);
+      }
     }
     if constexpr (KGROUP) {
       bbase0 = g.B0 + kbeg * g.ldb;
@@ -416,10 +447,44 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     }
   }
 
-  // Loads are branch-free: out-of-range rows, columns and K positions are
-  // clamped into the operand; K positions past the end are replaced by zero
-  // when the registers go to LDS (masking right after the load would make the
-  // wave wait for the load there and defeat the prefetch).
+  // A K step is full when all BK of its positions lie inside the contraction
+  // (and, for the gate/up data gradient, on one side of the gate/up seam, so
+  // one weight matrix serves the whole step).  Full steps load without clamps
+  // or masks; only the last step of a ragged contraction (and the seam step)
+  // takes the general path below.
+  auto full_step = [&](int64_t k0) -> bool {
+    if (k0 + BK > klen) return false;
+    if constexpr (MODE == GATE_UP_BWD_DATA) return k0 + BK <= g.F || k0 >= g.F;
+    return true;
+  };
+  // Full steps load through buffer resources built per step from the uniform
+  // base (scalar registers), with the per-lane byte offsets as the only vector
+  // operand.
+  auto rsrc = [](const char* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, -1, kBufferFlags);
+  };
+  auto bload = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint4 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  auto load_full = [&](int64_t k0, uint4* ra, uint4* rb) {
+    const auto r_a = rsrc(reinterpret_cast<const char*>(abase) + (KGROUP ? k0 * g.lda : k0) * 2);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) ra[j] = bload(r_a, fa_off[j]);
+    const bf16_t* b0 = bbase0;
+    const bf16_t* b1 = bbase1;
+    if constexpr (MODE == GATE_UP_BWD_DATA) b0 = b1 = (k0 < g.F ? bbase0 : bbase1);
+    const int64_t kb = (B_KC ? k0 : k0 * g.ldb) * 2;
+    const auto r_b0 = rsrc(reinterpret_cast<const char*>(b0) + kb);
+    const auto r_b1 = rsrc(reinterpret_cast<const char*>(b1) + kb);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) rb[j] = bload(j < NB / 2 ? r_b0 : r_b1, fb_off[j]);
+  };
+
+  // General loads: out-of-range rows, columns and K positions are clamped into
+  // the operand; K positions past the end are replaced by zero when the
+  // registers go to LDS (masking right after the load would make the wave wait
+  // for the load there and defeat the prefetch).
   auto load_a = [&](int64_t k0, uint4* ra) {
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
@@ -448,6 +513,19 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
       }
     }
   };
+  // zero the K positions past the end (k0: the K position the registers were loaded from)
+  auto mask_k = [&](int64_t k0, uint4* ra, uint4* rb) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      if constexpr (!KGROUP) ra[j] = keep(k0 + kc_c < kend, ra[j]);
+      else ra[j] = keep(k0 + 4 * ka4(j / 4) + (j & 3) < klen, ra[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (B_KC) rb[j] = keep(k0 + kc_c < kend, rb[j]);
+      else rb[j] = keep(k0 + 4 * kb4(j / 4) + (j & 3) < klen, rb[j]);
+    }
+  };
   auto store_kc = [&](bf16_t* S, const uint4* r, int n) {
 #pragma unroll
     for (int j = 0; j < n; ++j) {
@@ -470,18 +548,8 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
       *reinterpret_cast<uint2*>(S + lds_off(x8 + q, k4 >> 1) + (k4 & 1) * 4) = d;
     }
   };
-  // k0: the K position the registers were loaded from
-  auto store_ab = [&](int st, int64_t k0, uint4* ra, uint4* rb) {
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      if constexpr (!KGROUP) ra[j] = keep(k0 + kc_c < kend, ra[j]);
-      else ra[j] = keep(k0 + 4 * ka4(j / 4) + (j & 3) < klen && row0 + xa8(j / 4) < g.M, ra[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if constexpr (B_KC) rb[j] = keep(k0 + kc_c < kend, rb[j]);
-      else rb[j] = keep(k0 + 4 * kb4(j / 4) + (j & 3) < klen && n0 + xb8(j / 4) < g.N, rb[j]);
-    }
+  auto store_ab = [&](auto ST, const uint4* ra, const uint4* rb) {
+    constexpr int st = decltype(ST)::value;
     if constexpr (!KGROUP) {
       store_kc(As(st), ra, NA);
     } else {
@@ -496,11 +564,10 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     }
   };
 
-
-
   // MFMAs of one K step on LDS stage st; operand fragments of sub-step kk+1 are
   // read while the MFMAs of sub-step kk issue.
-  auto compute = [&](int st) {
+  auto compute = [&](auto ST) {
+    constexpr int st = decltype(ST)::value;
     const bf16_t* as = As(st);
     const bf16_t* bs = Bs(st);
     bf16x8 fa[2][TI], fb[2][TJ];
@@ -528,23 +595,37 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
 
   // Pipeline: two LDS stages, one register stage.  The global loads of step t+1
   // are in flight while the MFMAs of step t issue, then go to LDS stage (t+1)%2.
+  // The loop is unrolled by two so that the stage is a compile-time constant
+  // and every LDS address is a fixed register plus an immediate offset.
   uint4 ra[NA], rb[NB];
+  auto load_step = [&](int64_t k0) {
+    if (full_step(k0)) {
+      load_full(k0, ra, rb);
+    } else {
+      load_a(k0, ra);
+      load_b(k0, rb);
+    }
+  };
+  auto store_step = [&](auto ST, int64_t k0) {
+    if (!full_step(k0)) mask_k(k0, ra, rb);
+    store_ab(ST, ra, rb);
+  };
+  auto kstep = [&](auto ST, int64_t kt, int64_t nk) {
+    constexpr int st = decltype(ST)::value;
+    if (kt + 1 < nk) load_step((kt + 1) * BK);
+    compute(ST);
+    if (kt + 1 < nk) store_step(std::integral_constant<int, st ^ 1>(), (kt + 1) * BK);
+    __syncthreads();
+  };
   const int64_t nk = (klen + BK - 1) / BK;
   if (nk > 0) {
-    load_a(0, ra);
-    load_b(0, rb);
-    store_ab(0, 0, ra, rb);
+    load_step(0);
+    store_step(std::integral_constant<int, 0>(), 0);
     __syncthreads();
   }
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int s = (int)(kt & 1);
-    if (kt + 1 < nk) {
-      load_a((kt + 1) * BK, ra);
-      load_b((kt + 1) * BK, rb);
-    }
-    compute(s);
-    if (kt + 1 < nk) store_ab(s ^ 1, (kt + 1) * BK, ra, rb);
-    __syncthreads();
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    kstep(std::integral_constant<int, 0>(), kt, nk);
+    if (kt + 1 < nk) kstep(std::integral_constant<int, 1>(), kt + 1, nk);
   }
 
   }
