@@ -16,16 +16,15 @@
 // the expanded buffers); the last two are grouped over K (the contraction runs
 // over the expert's rows, which may be none).
 //
-// Tiling: a BM x BN output tile per 256-thread workgroup (the kernel is written
-// for any multiple of 128; 128 x 128 is launched), four waves in a 2 x 2
-// arrangement, each wave (BM/2) x (BN/2) of v_mfma_f32_32x32x16_bf16 tiles, two
-// workgroups (eight waves) per CU.  K step 64 staged through double-buffered
-// LDS (one barrier per step), the next step's global loads in flight in
-// registers while the current step's MFMAs issue.  In
-// LDS both operands are stored K-contiguous with an XOR-swizzled chunk order,
-// so every MFMA operand is one conflict-free 16-byte LDS read; operands that are
-// K-strided in memory are loaded as 4 k-rows x 8 columns per thread, transposed
-// in registers with byte permutes and written as 8-byte LDS stores.
+// Tiling: a BM x BN output tile per 256-thread workgroup (128 x 128 is
+// launched), four waves in a 2 x 2 arrangement, each wave (BM/2) x (BN/2) of
+// v_mfma_f32_32x32x16_bf16 tiles, two workgroups (eight waves) per CU.  K steps
+// of 64 go from memory straight into LDS (buffer loads with an LDS
+// destination, no register staging), two LDS stages: the loads of step t+1
+// are in flight while the MFMAs of step t issue.  Operands keep their memory
+// layout in LDS: K-contiguous tiles as rows of 64 k with an XOR-swizzled
+// chunk order (one conflict-free 16-byte read per MFMA operand), K-strided
+// tiles as k-rows read into MFMA operands with the transposing LDS read.
 //
 // Expert counts stay on the device: the grid covers floor(capacity/BM) + E row
 // tiles per column tile, and each workgroup finds its expert from the prefix
@@ -49,6 +48,9 @@ enum Mode : int {
 
 constexpr int BK = 64;
 constexpr int kThreads = 256;
+// gfx9 s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations (vmcnt in bits 3:0 and 15:14) and leaves the other counters free
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 // buffer resource word 3 for raw (untyped, unswizzled) buffer loads on gfx9:
 // 32-bit data format, so every access is checked against the byte range only
 constexpr int kBufferFlags = 0x00020000;
@@ -126,15 +128,23 @@ struct Cfg {
   // store instruction) in different banks
   static constexpr int CW = MODE == GATE_UP_FWD ? BN / 2 : BN;
   static constexpr int CP = CW + 8;
-  static constexpr int kMain = 2 * (BM + BN) * BK;
+  // LDS stages of the operand tiles (the fp8 path uses the first two)
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 2
+#endif
+  static constexpr int S = MOE_GEMM_STAGES;
+  static constexpr int kMain = S * (BM + BN) * BK;
   static constexpr int kEpi = KGROUP ? 0 : (MODE == DOWN_BWD_DATA ? 2 : 1) * BM * CP;
   static constexpr int kSmem = cmax(kMain, kEpi);
+  // workgroups per CU that the LDS allows (160 KB per CU)
+  static constexpr int kMinBlocks = kSmem * 2 <= 80 * 1024 ? 2 : 1;
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int MODE, int BM, int BN, bool FP8>
-__global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gemm(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_gemm(GemmArgs g) {
   using C = Cfg<MODE, BM, BN>;
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
   constexpr int TI = C::TI, TJ = C::TJ, NA = C::NA, NB = C::NB;
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
   // stages the output tile (and, for the SwiGLU backward, the saved G/U tile).
   __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmem];
   auto As = [&](int st) { return smem + st * BM * BK; };
-  auto Bs = [&](int st) { return smem + 2 * BM * BK + st * BN * BK; };
+  auto Bs = [&](int st) { return smem + C::S * BM * BK + st * BN * BK; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -352,69 +362,72 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     __syncthreads();
   }
   } else {
-  // Thread roles in one K step.
-  //  K-contiguous operand of R rows: vector j (j < R/32) is row tid/8 + 32j,
-  //  chunk tid%8.
-  //  K-strided operand of R columns: block q (q < R/128) covers k rows
-  //  4*k4 .. 4*k4+3 of the 8 columns from x8, transposed in registers and
-  //  written as 8 x 8-byte LDS stores.  With p = tid + 256q, the low three bits
-  //  of p pick eight neighbouring column groups and bit 3 the two k4 halves of
-  //  one 16-byte chunk, so the 16 lanes of one LDS store cycle write 16
-  //  distinct 8-byte bank slots.
-  const int kc_c = (tid & 7) * 8;
-  auto xcol = [&](int q, int R) {
-    const int p = tid + kThreads * q;
-    return (((p >> 4) % (R / 64)) * 8 + (p & 7)) * 8;
+  // Operand tiles go from memory straight into LDS (buffer loads with an LDS
+  // destination: lane l of one instruction writes the 16 bytes at
+  // instruction base + 16 l), in the operand's own memory layout:
+  //  * K-contiguous operand of R rows: R rows x 128 bytes (BK bf16), chunk c
+  //    of row r at chunk position c ^ swz(r); one instruction fills 8 rows,
+  //    lane l taking row 8q + l/8, position l%8, i.e. memory chunk
+  //    (l%8) ^ swz(row).
+  //  * K-strided operand of R columns: BK k-rows x 2R bytes, 16-byte chunk c
+  //    of k-row k at position c ^ (2 (k%4)); one instruction fills 512/R
+  //    k-rows.  MFMA fragments come out of it with transposing LDS reads
+  //    (ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+  //    element i of the group's four 8-byte rows read in lane order, for
+  //    each of the four rows), two reads per 8-k fragment.
+  // Rows past the operand are clamped to its last row (their products only
+  // reach output rows or columns that are not stored).  Past the end of the
+  // contraction the loads return zero: K-strided operands through the range
+  // of the buffer resource (its byte count ends at the last k-row), the
+  // K-contiguous A through an out-of-range offset in the last step.
+  constexpr int S = C::S;
+  constexpr int LA = BM / 32, LB = BN / 32;  // load instructions per wave per stage
+  constexpr uint32_t kOOB = 0x80000000u;
+  constexpr int kRange = 0x7ffffff0;
+  auto sw2 = [](int k) { return 2 * (k & 3); };
+  // buffer resource (base, byte range) in scalar registers
+  auto rsrc = [](const void* p, int64_t bytes) -> i32x4 {
+    const int64_t n = bytes < 0 ? 0 : (bytes < kRange ? bytes : kRange);
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
+                 __builtin_amdgcn_readfirstlane((int)n), kBufferFlags};
   };
-  auto krow4 = [&](int q, int R) {
-    const int p = tid + kThreads * q;
-    return ((p >> 4) / (R / 64)) * 2 + ((p >> 3) & 1);
+  // One 16-byte-per-lane load into LDS at byte address `lds` (+ 16 * lane).
+  // Written as an instruction of its own so that the compiler, which would
+  // otherwise wait for every such load before any LDS read, leaves the
+  // waiting to the pipeline below (explicit vmcnt waits); the instruction has
+  // no register result.
+  auto dma = [](const i32x4& r, const bf16_t* lds, uint32_t vo) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) bf16_t*)(lds));
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0) : "memory");
   };
-  auto xa8 = [&](int q) { return xcol(q, BM); };
-  auto ka4 = [&](int q) { return krow4(q, BM); };
-  auto xb8 = [&](int q) { return xcol(q, BN); };
-  auto kb4 = [&](int q) { return krow4(q, BN); };
-  auto ld16 = [](const bf16_t* base, uint32_t off) -> uint4 {
-    return *reinterpret_cast<const uint4*>(base + off);
-  };
-  // component-wise select (a select of the whole vector struct goes through memory)
-  auto keep = [](bool ok, const uint4& v) -> uint4 {
-    const uint32_t m = ok ? 0xffffffffu : 0u;
-    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-  };
-  // Uniform operand bases and per-lane 32-bit element offsets (every operand
-  // slice addressed from one base stays below 2^31 elements).  The byte
-  // offsets fa_off/fb_off serve full K steps: the K position goes into the
-  // uniform base, so a load costs no vector arithmetic.
-  const bf16_t* abase;
-  uint32_t aoff[NA], fa_off[NA];
-  if constexpr (!KGROUP) {
-    abase = g.A + row0 * g.lda;
+  // per-lane byte offsets of this wave's load instructions (relative to the
+  // step's base) and the K offset of the lane's chunk (K-contiguous operands)
+  uint32_t voA[LA], voB[LB];
+  int kcA[LA], kcB[LB];
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int r = (tid >> 3) + 32 * j;
-      aoff[j] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * g.lda + kc_c);
-      fa_off[j] = aoff[j] * 2;
-    }
-  } else {
-    abase = g.A + kbeg * g.lda;
-#pragma unroll
-    for (int q = 0; q < NA / 4; ++q) {
-      const int64_t col = row0 + xa8(q) < g.M ? row0 + xa8(q) : g.M - 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        aoff[4 * q + j] = (uint32_t)col;
-        fa_off[4 * q + j] = (uint32_t)(((4 * ka4(q) + j) * g.lda + col) * 2);
-      }
+  for (int j = 0; j < LA; ++j) {
+    const int q = wave * LA + j;
+    if constexpr (!KGROUP) {
+      const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz(r);
+      const int rr = r < rows_valid ? r : rows_valid - 1;
+      voA[j] = (uint32_t)((rr * g.lda + c * 8) * 2);
+      kcA[j] = c * 8;
+    } else {
+      constexpr int CPR = BM / 8, RPI = 64 / CPR;
+      const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw2(k);
+      const int64_t col = row0 + c * 8 < g.M ? row0 + c * 8 : g.M - 8;
+      voA[j] = (uint32_t)((k * g.lda + col) * 2);
+      kcA[j] = 0;
     }
   }
-  const bf16_t* bbase0;
-  const bf16_t* bbase1;
-  uint32_t boff[NB], fb_off[NB];
-  if constexpr (B_KC) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int r = (tid >> 3) + 32 * j;
+  for (int j = 0; j < LB; ++j) {
+    const int q = wave * LB + j;
+    if constexpr (B_KC) {
+      const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz(r);
       int64_t n;
       if constexpr (MODE == GATE_UP_FWD) {
         n = n0 + (r & (BN / 2 - 1));
@@ -423,167 +436,135 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
         n = n0 + r;
         if (n >= g.N) n = g.N - 1;
       }
-      boff[j] = (uint32_t)(n * g.ldb + kc_c);
-      fb_off[j] = boff[j] * 2;
-    }
-    bbase0 = g.B0 + (int64_t)e * g.bstride;
-    bbase1 = (MODE == GATE_UP_FWD) ? g.B1 + (int64_t)e * g.bstride : bbase0;
-  } else {
-#pragma unroll
-    for (int q = 0; q < NB / 4; ++q) {
-      const int64_t col = n0 + xb8(q) < g.N ? n0 + xb8(q) : g.N - 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        boff[4 * q + j] = (uint32_t)col;
-        fb_off[4 * q + j] = (uint32_t)(((4 * kb4(q) + j) * g.ldb + col) * 2);
-      }
-    }
-    if constexpr (KGROUP) {
-      bbase0 = g.B0 + kbeg * g.ldb;
-      bbase1 = bbase0;
+      voB[j] = (uint32_t)((n * g.ldb + c * 8) * 2);
+      kcB[j] = c * 8;
     } else {
-      bbase0 = g.B0 + (int64_t)e * g.bstride;
-      bbase1 = (MODE == GATE_UP_BWD_DATA) ? g.B1 + (int64_t)e * g.bstride - g.F * g.ldb : bbase0;
+      constexpr int CPR = BN / 8, RPI = 64 / CPR;
+      const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw2(k);
+      const int64_t col = n0 + c * 8 < g.N ? n0 + c * 8 : g.N - 8;
+      voB[j] = (uint32_t)((k * g.ldb + col) * 2);
+      kcB[j] = 0;
     }
   }
+  const char* abase = reinterpret_cast<const char*>(KGROUP ? g.A + kbeg * g.lda : g.A + row0 * g.lda);
+  const char* bbase0;
+  const char* bbase1;
+  if constexpr (KGROUP) {
+    bbase0 = bbase1 = reinterpret_cast<const char*>(g.B0 + kbeg * g.ldb);
+  } else {
+    bbase0 = reinterpret_cast<const char*>(g.B0 + (int64_t)e * g.bstride);
+    bbase1 = reinterpret_cast<const char*>((MODE == GATE_UP_FWD || MODE == GATE_UP_BWD_DATA)
+                                               ? g.B1 + (int64_t)e * g.bstride
+                                               : g.B0 + (int64_t)e * g.bstride);
+  }
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave index, in a scalar register
 
-  // A K step is full when all BK of its positions lie inside the contraction
-  // (and, for the gate/up data gradient, on one side of the gate/up seam, so
-  // one weight matrix serves the whole step).  Full steps load without clamps
-  // or masks; only the last step of a ragged contraction (and the seam step)
-  // takes the general path below.
-  auto full_step = [&](int64_t k0) -> bool {
-    if (k0 + BK > klen) return false;
-    if constexpr (MODE == GATE_UP_BWD_DATA) return k0 + BK <= g.F || k0 >= g.F;
-    return true;
-  };
-  // Full steps load through buffer resources built per step from the uniform
-  // base (scalar registers), with the per-lane byte offsets as the only vector
-  // operand.
-  auto rsrc = [](const char* p) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, -1, kBufferFlags);
-  };
-  auto bload = [](__amdgpu_buffer_rsrc_t r, uint32_t off) -> uint4 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-  };
-  auto load_full = [&](int64_t k0, uint4* ra, uint4* rb) {
-    const auto r_a = rsrc(reinterpret_cast<const char*>(abase) + (KGROUP ? k0 * g.lda : k0) * 2);
-#pragma unroll
-    for (int j = 0; j < NA; ++j) ra[j] = bload(r_a, fa_off[j]);
-    const bf16_t* b0 = bbase0;
-    const bf16_t* b1 = bbase1;
-    if constexpr (MODE == GATE_UP_BWD_DATA) b0 = b1 = (k0 < g.F ? bbase0 : bbase1);
-    const int64_t kb = (B_KC ? k0 : k0 * g.ldb) * 2;
-    const auto r_b0 = rsrc(reinterpret_cast<const char*>(b0) + kb);
-    const auto r_b1 = rsrc(reinterpret_cast<const char*>(b1) + kb);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) rb[j] = bload(j < NB / 2 ? r_b0 : r_b1, fb_off[j]);
-  };
-
-  // General loads: out-of-range rows, columns and K positions are clamped into
-  // the operand; K positions past the end are replaced by zero when the
-  // registers go to LDS (masking right after the load would make the wave wait
-  // for the load there and defeat the prefetch).
-  auto load_a = [&](int64_t k0, uint4* ra) {
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      if constexpr (!KGROUP) {
-        const uint32_t kk = (uint32_t)(k0 + kc_c < kend ? k0 : kend - 8 - kc_c);
-        ra[j] = ld16(abase, aoff[j] + kk);
-      } else {
-        const int64_t k = k0 + 4 * ka4(j / 4) + (j & 3);
-        const uint32_t kr = (uint32_t)(k < klen ? k : klen - 1);
-        ra[j] = ld16(abase, kr * (uint32_t)g.lda + aoff[j]);
-      }
-    }
-  };
-  auto load_b = [&](int64_t k0, uint4* rb) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if constexpr (B_KC) {
-        const uint32_t kk = (uint32_t)(k0 + kc_c < kend ? k0 : kend - 8 - kc_c);
-        rb[j] = ld16(j < NB / 2 ? bbase0 : bbase1, boff[j] + kk);
-      } else {
-        const int64_t k = k0 + 4 * kb4(j / 4) + (j & 3);
-        const uint32_t kr = (uint32_t)(k < klen ? k : klen - 1);
-        const bf16_t* base = bbase0;
-        if constexpr (MODE == GATE_UP_BWD_DATA) base = kr < (uint32_t)g.F ? bbase0 : bbase1;
-        rb[j] = ld16(base, kr * (uint32_t)g.ldb + boff[j]);
-      }
-    }
-  };
-  // zero the K positions past the end (k0: the K position the registers were loaded from)
-  auto mask_k = [&](int64_t k0, uint4* ra, uint4* rb) {
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      if constexpr (!KGROUP) ra[j] = keep(k0 + kc_c < kend, ra[j]);
-      else ra[j] = keep(k0 + 4 * ka4(j / 4) + (j & 3) < klen, ra[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if constexpr (B_KC) rb[j] = keep(k0 + kc_c < kend, rb[j]);
-      else rb[j] = keep(k0 + 4 * kb4(j / 4) + (j & 3) < klen, rb[j]);
-    }
-  };
-  auto store_kc = [&](bf16_t* S, const uint4* r, int n) {
-#pragma unroll
-    for (int j = 0; j < n; ++j) {
-      const int i = tid + kThreads * j;
-      *reinterpret_cast<uint4*>(S + lds_off(i >> 3, i & 7)) = r[j];
-    }
-  };
-  // one block of 4 k-rows x 8 columns -> 8 columns x 4 k
-  auto store_t = [&](bf16_t* S, const uint4* v, int x8, int k4) {
-    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
-      uint2 d;
-      d.x = __builtin_amdgcn_perm(w1[q >> 1], w0[q >> 1], sel);
-      d.y = __builtin_amdgcn_perm(w3[q >> 1], w2[q >> 1], sel);
-      *reinterpret_cast<uint2*>(S + lds_off(x8 + q, k4 >> 1) + (k4 & 1) * 4) = d;
-    }
-  };
-  auto store_ab = [&](auto ST, const uint4* ra, const uint4* rb) {
+  // direct loads of K step kt into LDS stage ST
+  auto issue = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
+    const int64_t k0 = kt * BK;
+    const bool tail = k0 + BK > klen;
+    bf16_t* sa = smem + st * BM * BK;
+    bf16_t* sb = smem + S * BM * BK + st * BN * BK;
     if constexpr (!KGROUP) {
-      store_kc(As(st), ra, NA);
-    } else {
+      const auto r = rsrc(abase + k0 * 2, kRange);
 #pragma unroll
-      for (int q = 0; q < NA / 4; ++q) store_t(As(st), ra + 4 * q, xa8(q), ka4(q));
+      for (int j = 0; j < LA; ++j) {
+        const uint32_t vo = (tail && k0 + kcA[j] >= kend) ? kOOB : voA[j];
+        dma(r, sa + (wv * LA + j) * 512, vo);
+      }
+    } else {
+      const auto r = rsrc(abase + k0 * g.lda * 2, (klen - k0) * g.lda * 2);
+#pragma unroll
+      for (int j = 0; j < LA; ++j)
+        dma(r, sa + (wv * LA + j) * 512, voA[j]);
     }
     if constexpr (B_KC) {
-      store_kc(Bs(st), rb, NB);
-    } else {
+      const auto r0 = rsrc(bbase0 + k0 * 2, kRange);
+      const auto r1 = rsrc(bbase1 + k0 * 2, kRange);
 #pragma unroll
-      for (int q = 0; q < NB / 4; ++q) store_t(Bs(st), rb + 4 * q, xb8(q), kb4(q));
+      for (int j = 0; j < LB; ++j) {
+        const int q = wv * LB + j;
+        const uint32_t vo = (tail && k0 + kcB[j] >= kend) ? kOOB : voB[j];
+        // gate/up forward: rows BN/2.. of the B tile are the up rows
+        const bool up = MODE == GATE_UP_FWD && 8 * q >= BN / 2;
+        dma(up ? r1 : r0, sb + q * 512, vo);
+      }
+    } else if constexpr (KGROUP) {
+      const auto r = rsrc(bbase0 + k0 * g.ldb * 2, (klen - k0) * g.ldb * 2);
+#pragma unroll
+      for (int j = 0; j < LB; ++j)
+        dma(r, sb + (wv * LB + j) * 512, voB[j]);
+    } else {
+      // data gradients: B = the expert's weights, K-strided over Kd (= H, or
+      // 2F with the gate rows < F and the up rows >= F; F is a multiple of
+      // 32, so the k-rows of one instruction lie on one side)
+      constexpr int RPI = 64 / (BN / 8);
+      const int64_t Fk = MODE == GATE_UP_BWD_DATA ? g.F : g.Kd;
+      const auto r0 = rsrc(bbase0 + k0 * g.ldb * 2, (Fk - k0) * g.ldb * 2);
+      const auto r1 = rsrc(bbase1 + (k0 - Fk) * g.ldb * 2, (g.Kd - k0) * g.ldb * 2);
+#pragma unroll
+      for (int j = 0; j < LB; ++j) {
+        const int q = wv * LB + j;
+        const bool up = MODE == GATE_UP_BWD_DATA && k0 + RPI * q >= Fk;
+        dma(up ? r1 : r0, sb + q * 512, voB[j]);
+      }
     }
   };
 
-  // MFMAs of one K step on LDS stage st; operand fragments of sub-step kk+1 are
+  // LDS read offsets (bf16 elements) of the MFMA fragments, stage 0, sub-step 0
+  // K-contiguous operand: one 16-byte read at lds_off(row, 2 kk + lane/32)
+  // K-strided operand: two transposing reads at tr_off(i) + (16 kk + 4 r) k-rows
+  const int g16 = lane >> 4, i16 = lane & 15;
+  auto tr_off = [&](int mbase, int R) {
+    const int m = mbase + (g16 & 1) * 16 + 4 * (i16 & 3);
+    const int k = (g16 >> 1) * 8 + (i16 >> 2);
+    return k * R + (((m >> 3) ^ sw2(k)) << 3) + ((m >> 2) & 1) * 4;
+  };
+  int trA[TI], trB[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) trA[i] = tr_off(wm * (BM / 2) + i * 32, BM);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) trB[j] = tr_off(brow(j), BN);
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  auto trread = [](const bf16_t* p) -> v4i16 {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  };
+  auto frag_tr = [&](const bf16_t* base, int kk, int R) -> bf16x8 {
+    const v4i16 lo = trread(base + (16 * kk) * R);
+    const v4i16 hi = trread(base + (16 * kk + 4) * R);
+    const v4i16 v[2] = {lo, hi};
+    bf16x8 out;
+    __builtin_memcpy(&out, v, 16);
+    return out;
+  };
+
+  // MFMAs of one K step on LDS stage ST; operand fragments of sub-step kk+1 are
   // read while the MFMAs of sub-step kk issue.
   auto compute = [&](auto ST) {
     constexpr int st = decltype(ST)::value;
-    const bf16_t* as = As(st);
-    const bf16_t* bs = Bs(st);
+    const bf16_t* as = smem + st * BM * BK;
+    const bf16_t* bs = smem + S * BM * BK + st * BN * BK;
     bf16x8 fa[2][TI], fb[2][TJ];
     auto fetch = [&](int kk, int slot) {
       const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-        fa[slot][i] = *reinterpret_cast<const bf16x8*>(as + lds_off(arow[i], c));
+      for (int i = 0; i < TI; ++i) {
+        if constexpr (!KGROUP) fa[slot][i] = *reinterpret_cast<const bf16x8*>(as + lds_off(arow[i], c));
+        else fa[slot][i] = frag_tr(as + trA[i], kk, BM);
+      }
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        fb[slot][j] = *reinterpret_cast<const bf16x8*>(bs + lds_off(brw[j], c));
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (B_KC) fb[slot][j] = *reinterpret_cast<const bf16x8*>(bs + lds_off(brw[j], c));
+        else fb[slot][j] = frag_tr(bs + trB[j], kk, BN);
+      }
     };
     fetch(0, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
+      // keep the reads of sub-step kk+1 ahead of the MFMAs of sub-step kk
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -593,40 +574,39 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128 ? 1 : 2)) void k_gem
     }
   };
 
-  // Pipeline: two LDS stages, one register stage.  The global loads of step t+1
-  // are in flight while the MFMAs of step t issue, then go to LDS stage (t+1)%2.
-  // The loop is unrolled by two so that the stage is a compile-time constant
-  // and every LDS address is a fixed register plus an immediate offset.
-  uint4 ra[NA], rb[NB];
-  auto load_step = [&](int64_t k0) {
-    if (full_step(k0)) {
-      load_full(k0, ra, rb);
-    } else {
-      load_a(k0, ra);
-      load_b(k0, rb);
-    }
-  };
-  auto store_step = [&](auto ST, int64_t k0) {
-    if (!full_step(k0)) mask_k(k0, ra, rb);
-    store_ab(ST, ra, rb);
-  };
-  auto kstep = [&](auto ST, int64_t kt, int64_t nk) {
-    constexpr int st = decltype(ST)::value;
-    if (kt + 1 < nk) load_step((kt + 1) * BK);
-    compute(ST);
-    if (kt + 1 < nk) store_step(std::integral_constant<int, st ^ 1>(), (kt + 1) * BK);
-    __syncthreads();
-  };
+  // Pipeline: S LDS stages, loads of step t+S-1 issued at step t.  Each step
+  // waits for its own loads (the loads of the later steps may stay in
+  // flight), then a barrier makes every wave's part of the stage visible and
+  // frees the stage of step t-1 for the next loads.
+  constexpr int L = LA + LB;
   const int64_t nk = (klen + BK - 1) / BK;
-  if (nk > 0) {
-    load_step(0);
-    store_step(std::integral_constant<int, 0>(), 0);
-    __syncthreads();
+  auto kstep = [&](auto ST, int64_t kt) {
+    constexpr int st = decltype(ST)::value;
+    if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L * (S - 2)));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // a plain barrier: the LDS reads of step t-1 have completed (their MFMAs
+    // consumed them) and the loads of step t were waited for above; the empty
+    // statements keep the compiler from moving memory accesses across it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + S - 1 < nk) issue(std::integral_constant<int, (st + S - 1) % S>(), kt + S - 1);
+    compute(ST);
+  };
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t)
+    if (t < nk) {
+      if (t == 0) issue(std::integral_constant<int, 0>(), 0);
+      if (t == 1) issue(std::integral_constant<int, 1 % S>(), 1);
+      if (t == 2) issue(std::integral_constant<int, 2 % S>(), 2);
+    }
+  for (int64_t kt = 0; kt < nk; kt += S) {
+    kstep(std::integral_constant<int, 0>(), kt);
+    if (kt + 1 < nk) kstep(std::integral_constant<int, 1 % S>(), kt + 1);
+    if constexpr (S > 2) if (kt + 2 < nk) kstep(std::integral_constant<int, 2 % S>(), kt + 2);
+    if constexpr (S > 3) if (kt + 3 < nk) kstep(std::integral_constant<int, 3 % S>(), kt + 3);
   }
-  for (int64_t kt = 0; kt < nk; kt += 2) {
-    kstep(std::integral_constant<int, 0>(), kt, nk);
-    if (kt + 1 < nk) kstep(std::integral_constant<int, 1>(), kt + 1, nk);
-  }
+  __syncthreads();
 
   }
 
