@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return f2bf(lo) | (f2bf(hi) << 16);
 }
 
+// Two floats -> two bf16 (lo in the low half) with the hardware conversion
+// (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Unpack the 8 bf16 of a 16-byte vector to floats.
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);

@@ -47,7 +47,6 @@ enum Mode : int {
 };
 
 constexpr int BK = 64;
-constexpr int kThreads = 256;
 // gfx9 s_waitcnt immediate that waits for at most n outstanding vector memory
 // operations (vmcnt in bits 3:0 and 15:14) and leaves the other counters free
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -118,7 +117,9 @@ template <int MODE, int BM, int BN>
 struct Cfg {
   static constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
   static constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
-  static constexpr int TI = BM / 64, TJ = BN / 64;
+  // waves: WM along M x WN along N, each a 64 x 64 block of 2 x 2 MFMA tiles
+  static constexpr int WM = BM / 64, WN = BN / 64, kThreads = 64 * WM * WN;
+  static constexpr int TI = 2, TJ = 2;
   // registers (16-byte vectors) per thread per K step: a K-contiguous R-row
   // operand is R/32 vectors, a K-strided one R/128 blocks of 4 k-rows
   static constexpr int NA = KGROUP ? 4 * (BM / 128) : BM / 32;
@@ -134,7 +135,7 @@ struct Cfg {
 #endif
   static constexpr int S = MOE_GEMM_STAGES;
   static constexpr int kMain = S * (BM + BN) * BK;
-  static constexpr int kEpi = KGROUP ? 0 : (MODE == DOWN_BWD_DATA ? 2 : 1) * BM * CP;
+  static constexpr int kEpi = KGROUP ? 0 : (MODE == GATE_UP_FWD ? 3 : MODE == DOWN_BWD_DATA ? 2 : 1) * BM * CP;
   static constexpr int kSmem = cmax(kMain, kEpi);
   // workgroups per CU that the LDS allows (160 KB per CU)
   static constexpr int kMinBlocks = kSmem * 2 <= 80 * 1024 ? 2 : 1;
@@ -144,7 +145,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int MODE, int BM, int BN, bool FP8>
-__global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_gemm(GemmArgs g) {
+__global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::kMinBlocks)) void k_gemm(GemmArgs g) {
   using C = Cfg<MODE, BM, BN>;
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
   constexpr int TI = C::TI, TJ = C::TJ, NA = C::NA, NB = C::NB;
@@ -155,7 +156,9 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
   auto Bs = [&](int st) { return smem + C::S * BM * BK + st * BN * BK; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int WM = C::WM, WN = C::WN, kThreads = C::kThreads;
+  static_assert(!FP8 || kThreads == 256, "the fp8 loop is written for four waves");
+  const int wm = wave / WN, wn = wave % WN;
 
   const int64_t nb = gridDim.x;
   const int64_t bid = blockIdx.x;
@@ -208,13 +211,13 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
   // matching gate and up column tiles so SwiGLU pairs meet in one lane.
   auto brow = [&](int j) -> int {
     if constexpr (MODE == GATE_UP_FWD)
-      return (j < TJ / 2) ? wn * (BN / 4) + j * 32 : BN / 2 + wn * (BN / 4) + (j - TJ / 2) * 32;
+      return (j < TJ / 2) ? wn * (BN / 2 / WN) + j * 32 : BN / 2 + wn * (BN / 2 / WN) + (j - TJ / 2) * 32;
     else
-      return wn * (BN / 2) + j * 32;
+      return wn * (BN / WN) + j * 32;
   };
   int arow[TI], brw[TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) arow[i] = wm * (BM / 2) + i * 32 + (lane & 31);
+  for (int i = 0; i < TI; ++i) arow[i] = wm * (BM / WM) + i * 32 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < TJ; ++j) brw[j] = brow(j) + (lane & 31);
 
@@ -324,9 +327,9 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
 #pragma unroll
             for (int r = 0; r < 16; ++r) z[r] = 0.f;
             // e4m3 x e4m3 (format 0 for both), unit E8M0 scales (127)
-            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], z, 0, 0, 0, 127, 0, 127);
+            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], z, 0, 0, 0, 127, 0, 127);
           } else {
-            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], tmp[i][j], 0, 0, 0,
+            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], tmp[i][j], 0, 0, 0,
                                                                          127, 0, 127);
           }
         }
@@ -335,18 +338,18 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
       sbv[j] = bscale(k0, (MODE == GATE_UP_FWD) ? (j >= TJ / 2) : 0);
+    // transposed fragments: the lane's row m (one A scale) and the j tile's
+    // columns (one B block scale)
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i) {
+      const float sa = sAl[st][wm * (BM / WM) + i * 32 + (lane & 31)];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int m = wm * (BM / 2) + i * 32 + q * 8 + (lane >> 5) * 4;
-        const float4 sa = *reinterpret_cast<const float4*>(&sAl[st][m]);
-        const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+      for (int j = 0; j < TJ; ++j) {
+        const float f = sa * sbv[j];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) acc[i][j][q * 4 + t] += tmp[i][j][q * 4 + t] * (sav[t] * sbv[j]);
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += tmp[i][j][r] * f;
       }
+    }
   };
   const int64_t nk = g.Kd / 128;
   if (nk > 0) {
@@ -381,7 +384,8 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
   // of the buffer resource (its byte count ends at the last k-row), the
   // K-contiguous A through an out-of-range offset in the last step.
   constexpr int S = C::S;
-  constexpr int LA = BM / 32, LB = BN / 32;  // load instructions per wave per stage
+  // load instructions per wave per stage (a tile is R/8 instructions of 1 KB)
+  constexpr int LA = BM / 8 / (WM * WN), LB = BN / 8 / (WM * WN);
   constexpr uint32_t kOOB = 0x80000000u;
   constexpr int kRange = 0x7ffffff0;
   auto sw2 = [](int k) { return 2 * (k & 3); };
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
   };
   int trA[TI], trB[TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) trA[i] = tr_off(wm * (BM / 2) + i * 32, BM);
+  for (int i = 0; i < TI; ++i) trA[i] = tr_off(wm * (BM / WM) + i * 32, BM);
 #pragma unroll
   for (int j = 0; j < TJ; ++j) trB[j] = tr_off(brow(j), BN);
   typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -569,8 +573,10 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
-                                                             acc[i][j], 0, 0, 0);
+          acc[i][j] = KGROUP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                                      acc[i][j], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
+                                                                      acc[i][j], 0, 0, 0);
     }
   };
 
@@ -610,11 +616,20 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
 
   }
 
-  // ---- epilogue.  acc[i][j][r] holds C(m, n) with
-  //   m = wm*(BM/2) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  n = brow(j) + lane%32
-  // The K loop ended with a barrier, so the LDS stages are free.
+  // ---- epilogue.
+  // Row-grouped GEMMs accumulate transposed fragments (the MFMA takes the B
+  // fragment as its first operand), so acc[i][j][r] holds C(m, n) with
+  //   m = wm*(BM/WM) + i*32 + lane%32,  n = brow(j) + (r/4)*8 + (lane/32)*4 + r%4:
+  // every lane owns runs of four consecutive columns and writes them to the
+  // LDS staging tile as one 8-byte store.  Weight gradients keep the plain
+  // fragments: m = wm*(BM/WM) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+  // n = brow(j) + lane%32.  The K loop ended with a barrier, so the LDS
+  // stages are free.
   const int ln = lane & 31, lh = lane >> 5;
-  auto mrow = [&](int i, int r) { return wm * (BM / 2) + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3); };
+  auto mrow = [&](int i, int r) { return wm * (BM / WM) + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3); };
+  auto tm = [&](int i) { return wm * (BM / WM) + i * 32 + ln; };
+  auto tn = [&](int j, int t) { return brow(j) + t * 8 + lh * 4; };
+  auto pack4 = [](float a, float b, float c, float d) { return make_uint2(pk_bf16(a, b), pk_bf16(c, d)); };
   constexpr int CP = C::CP, CW = C::CW;
   // cooperative 16-byte row stores of a staged BM x CW bf16 tile
   auto store_tile = [&](const bf16_t* t, bf16_t* dst, int64_t ldd, int64_t ncols) {
@@ -626,25 +641,32 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
     }
   };
   if constexpr (MODE == GATE_UP_FWD) {
-    // h, G and U (BM rows x BN/2 columns each) staged one after the other
-    bf16_t* ct = smem;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
+    // h, G and U (BM rows x BN/2 columns each) staged side by side
+    bf16_t* th = smem;
+    bf16_t* tg = smem + BM * CP;
+    bf16_t* tu = smem + 2 * BM * CP;
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ / 2; ++j)
+      for (int j = 0; j < TJ / 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float gv = acc[i][j][r], uv = acc[i][j + TJ / 2][r];
-            const float v = pass == 0 ? silu_f(gv) * uv : (pass == 1 ? gv : uv);
-            ct[mrow(i, r) * CP + wn * (BN / 4) + j * 32 + ln] = (bf16_t)f2bf(v);
+        for (int t = 0; t < 4; ++t) {
+          float gv[4], uv[4], hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            gv[q] = acc[i][j][4 * t + q];
+            uv[q] = acc[i][j + TJ / 2][4 * t + q];
+            hv[q] = silu_f(gv[q]) * uv[q];
           }
-      __syncthreads();
-      if (pass == 0) store_tile(ct, g.C0 + n0, g.F, g.F - n0);
-      else store_tile(ct, g.C1 + (pass == 2 ? g.F : 0) + n0, 2 * g.F, g.F - n0);
-      __syncthreads();
-    }
+          const int o = tm(i) * CP + wn * (BN / 2 / WN) + j * 32 + t * 8 + lh * 4;
+          *reinterpret_cast<uint2*>(th + o) = pack4(hv[0], hv[1], hv[2], hv[3]);
+          *reinterpret_cast<uint2*>(tg + o) = pack4(gv[0], gv[1], gv[2], gv[3]);
+          *reinterpret_cast<uint2*>(tu + o) = pack4(uv[0], uv[1], uv[2], uv[3]);
+        }
+    __syncthreads();
+    store_tile(th, g.C0 + n0, g.F, g.F - n0);
+    store_tile(tg, g.C1 + n0, 2 * g.F, g.F - n0);
+    store_tile(tu, g.C1 + g.F + n0, 2 * g.F, g.F - n0);
   } else if constexpr (MODE == DOWN_FWD || MODE == GATE_UP_BWD_DATA) {
     bf16_t* ct = smem;
 #pragma unroll
@@ -652,7 +674,9 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ct[mrow(i, r) * CP + brow(j) + ln] = (bf16_t)f2bf(acc[i][j][r]);
+        for (int t = 0; t < 4; ++t)
+          *reinterpret_cast<uint2*>(ct + tm(i) * CP + tn(j, t)) =
+              pack4(acc[i][j][4 * t], acc[i][j][4 * t + 1], acc[i][j][4 * t + 2], acc[i][j][4 * t + 3]);
     __syncthreads();
     store_tile(ct, g.C0 + n0, g.N, g.N - n0);
   } else if constexpr (MODE == DOWN_BWD_DATA) {
@@ -674,13 +698,22 @@ __global__ __launch_bounds__(kThreads, (Cfg<MODE, BM, BN>::kMinBlocks)) void k_g
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int o = mrow(i, r) * CP + brow(j) + ln;
-          const float gv = bf2f(tg[o]), uv = bf2f(tu[o]);
-          const float c = acc[i][j][r];
-          const float sg = 1.0f / (1.0f + __expf(-gv));
-          tg[o] = (bf16_t)f2bf(c * uv * sg * (1.0f + gv * (1.0f - sg)));
-          tu[o] = (bf16_t)f2bf(c * (gv * sg));
+        for (int t = 0; t < 4; ++t) {
+          const int o = tm(i) * CP + tn(j, t);
+          const uint2 gp = *reinterpret_cast<const uint2*>(tg + o);
+          const uint2 up = *reinterpret_cast<const uint2*>(tu + o);
+          const float gv[4] = {bf2f(gp.x & 0xffffu), bf2f(gp.x >> 16), bf2f(gp.y & 0xffffu), bf2f(gp.y >> 16)};
+          const float uv[4] = {bf2f(up.x & 0xffffu), bf2f(up.x >> 16), bf2f(up.y & 0xffffu), bf2f(up.y >> 16)};
+          float dg[4], du[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float c = acc[i][j][4 * t + q];
+            const float sg = 1.0f / (1.0f + __expf(-gv[q]));
+            dg[q] = c * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+            du[q] = c * (gv[q] * sg);
+          }
+          *reinterpret_cast<uint2*>(tg + o) = pack4(dg[0], dg[1], dg[2], dg[3]);
+          *reinterpret_cast<uint2*>(tu + o) = pack4(du[0], du[1], du[2], du[3]);
         }
     __syncthreads();
     store_tile(tg, g.C0 + n0, 2 * g.F, g.N - n0);
@@ -725,7 +758,8 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8>), dim3((unsigned)grid), dim3(kThreads), 0, strm, g);
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8>), dim3((unsigned)grid), dim3(Cfg<MODE, BM, BN>::kThreads), 0,
+                     strm, g);
   return launch_status();
 }
 
@@ -735,7 +769,11 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
 // so every mode runs 128 x 128.
 template <int MODE, bool FP8 = false>
 moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
-  return launch_cfg<MODE, 128, 128, FP8>(g, s, strm);
+#ifndef MOE_GEMM_BN
+#define MOE_GEMM_BN 128
+#endif
+  if constexpr (FP8) return launch_cfg<MODE, 128, 128, FP8>(g, s, strm);
+  else return launch_cfg<MODE, 128, MOE_GEMM_BN, FP8>(g, s, strm);
 }
 
 GemmArgs base_args(const moe_shape* s, const int32_t* prefix) {
