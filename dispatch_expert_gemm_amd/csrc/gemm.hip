@@ -222,22 +222,37 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   for (int j = 0; j < TJ; ++j) brw[j] = brow(j) + (lane & 31);
 
   if constexpr (FP8) {
-  // fp8 path (K-contiguous e4m3 codes for both operands; K a multiple of 128).
-  // One K step is 128 codes = one 128-byte LDS row, two 32x32x64 MFMA sub-steps
-  // into a temporary, then acc += tmp * (A row scale * B block scale).
-  __shared__ float sAl[2][BM];
-  const int kc_c = (tid & 7) * 16;  // byte column of this thread's 16-byte chunk
-  const uint8_t* qa = g.qA + row0 * g.lda;
-  uint32_t aoff[NA];
+  // fp8 path: e4m3 codes, K-contiguous for both operands, K a multiple of 128.
+  // One K step is 128 codes = one 128-byte LDS row per operand row, loaded
+  // straight into LDS like the bf16 K-contiguous tiles (same swizzle, two
+  // stages); two 32x32x64 MFMA sub-steps go into a temporary, then
+  // acc += tmp * (A row scale * B block scale).  The accumulators hold
+  // transposed fragments, so a lane's values share one row (one A scale) and
+  // one j tile (one B block scale).
+  constexpr int S8 = 2;
+  constexpr int LA = BM / 8 / (WM * WN), LB = BN / 8 / (WM * WN);
+  static_assert(S8 <= C::S || C::kMain >= S8 * (BM + BN) * BK, "fp8 stages must fit the operand LDS");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto rsrc8 = [](const void* p) -> i32x4 {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff), 0x7ffffff0, kBufferFlags};
+  };
+  auto dma8 = [](const i32x4& r, const bf16_t* lds, uint32_t vo) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) bf16_t*)(lds));
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0) : "memory");
+  };
+  uint32_t voA[LA], voB[LB];
 #pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int r = (tid >> 3) + 32 * j;
-    aoff[j] = (uint32_t)((r < rows_valid ? r : rows_valid - 1) * g.lda + kc_c);
+  for (int j = 0; j < LA; ++j) {
+    const int r = 8 * (wave * LA + j) + (lane >> 3), c = (lane & 7) ^ swz(r);
+    const int rr = r < rows_valid ? r : rows_valid - 1;
+    voA[j] = (uint32_t)(rr * g.lda + c * 16);
   }
-  uint32_t boff[NB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int r = (tid >> 3) + 32 * j;
+  for (int j = 0; j < LB; ++j) {
+    const int r = 8 * (wave * LB + j) + (lane >> 3), c = (lane & 7) ^ swz(r);
     int64_t n;
     if constexpr (MODE == GATE_UP_FWD) {
       n = n0 + (r & (BN / 2 - 1));
@@ -246,11 +261,11 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
       n = n0 + r;
       if (n >= g.N) n = g.N - 1;
     }
-    boff[j] = (uint32_t)(n * g.ldb + kc_c);
+    voB[j] = (uint32_t)(n * g.ldb + c * 16);
   }
-  const int64_t nks = g.Kd / 128;  // scale columns of A
-  const int srow = tid < BM ? (tid < rows_valid ? tid : rows_valid - 1) : 0;
-  // B bases and scale of K step kt (k0 = 128 kt): uniform across the workgroup
+  const uint8_t* qa = g.qA + row0 * g.lda;
+  // B codes of K step k0 (gate/up forward: half 1 = the up matrix; gate/up
+  // data gradient: the gate codes for k < F, the up codes after)
   auto bsrc = [&](int64_t k0, int half) -> const uint8_t* {
     if constexpr (MODE == GATE_UP_FWD) {
       return (half ? g.qB1 : g.qB0) + (int64_t)e * g.bstride + k0;
@@ -273,32 +288,31 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
       return g.sB0[e * g.sbe + (n0 / 128) * g.sbn + kb * g.sbk];
     }
   };
-  uint4 ra[NA], rb[NB];
-  float rsa = 0.f;
-  auto load8 = [&](int64_t k0) {
+  auto issue8 = [&](auto ST, int64_t kt) {
+    constexpr int st = decltype(ST)::value;
+    const int64_t k0 = kt * 128;
+    const auto ra = rsrc8(qa + k0);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) ra[j] = *reinterpret_cast<const uint4*>(qa + aoff[j] + k0);
+    for (int j = 0; j < LA; ++j) dma8(ra, As(st) + (wv * LA + j) * 512, voA[j]);
+    const auto rb0 = rsrc8(bsrc(k0, 0));
+    const auto rb1 = rsrc8(bsrc(k0, 1));
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const uint8_t* b = bsrc(k0, (MODE == GATE_UP_FWD) ? (j >= NB / 2) : 0);
-      rb[j] = *reinterpret_cast<const uint4*>(b + boff[j]);
+    for (int j = 0; j < LB; ++j) {
+      const int q = wv * LB + j;
+      const bool up = MODE == GATE_UP_FWD && 8 * q >= BN / 2;
+      dma8(up ? rb1 : rb0, Bs(st) + q * 512, voB[j]);
     }
-    if (tid < BM) rsa = g.sA[(row0 + srow) * nks + k0 / 128];
   };
-  auto store8 = [&](int st) {
+  // A row scales of the lane's rows (transposed fragments: row = lane%32)
+  const int64_t nks = g.Kd / 128;
+  const float* sa_row[TI];
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      const int i = tid + kThreads * j;
-      *reinterpret_cast<uint4*>(As(st) + lds_off(i >> 3, i & 7)) = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int i = tid + kThreads * j;
-      *reinterpret_cast<uint4*>(Bs(st) + lds_off(i >> 3, i & 7)) = rb[j];
-    }
-    if (tid < BM) sAl[st][tid] = rsa;
-  };
-  auto compute8 = [&](int st, int64_t k0) {
+  for (int i = 0; i < TI; ++i) {
+    const int m = wm * (BM / WM) + i * 32 + (lane & 31);
+    sa_row[i] = g.sA + (row0 + (m < rows_valid ? m : rows_valid - 1)) * nks;
+  }
+  auto compute8 = [&](auto ST, int64_t kt, const float* sa) {
+    constexpr int st = decltype(ST)::value;
     const bf16_t* as = As(st);
     const bf16_t* bs = Bs(st);
     f32x16 tmp[TI][TJ];
@@ -334,36 +348,46 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
           }
         }
     }
+    const int64_t k0 = kt * 128;
     float sbv[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      sbv[j] = bscale(k0, (MODE == GATE_UP_FWD) ? (j >= TJ / 2) : 0);
-    // transposed fragments: the lane's row m (one A scale) and the j tile's
-    // columns (one B block scale)
+    for (int j = 0; j < TJ; ++j) sbv[j] = bscale(k0, (MODE == GATE_UP_FWD) ? (j >= TJ / 2) : 0);
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const float sa = sAl[st][wm * (BM / WM) + i * 32 + (lane & 31)];
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const float f = sa * sbv[j];
+        const float f = sa[i] * sbv[j];
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] += tmp[i][j][r] * f;
       }
-    }
   };
   const int64_t nk = g.Kd / 128;
+  float sa_cur[TI], sa_nxt[TI];
+  auto kstep8 = [&](auto ST, int64_t kt) {
+    constexpr int st = decltype(ST)::value;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk) {
+      issue8(std::integral_constant<int, st ^ 1>(), kt + 1);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) sa_nxt[i] = sa_row[i][kt + 1];
+    }
+    compute8(ST, kt, sa_cur);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) sa_cur[i] = sa_nxt[i];
+  };
   if (nk > 0) {
-    load8(0);
-    store8(0);
-    __syncthreads();
+    issue8(std::integral_constant<int, 0>(), 0);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) sa_cur[i] = sa_row[i][0];
   }
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int s = (int)(kt & 1);
-    if (kt + 1 < nk) load8((kt + 1) * 128);
-    compute8(s, kt * 128);
-    if (kt + 1 < nk) store8(s ^ 1);
-    __syncthreads();
+  for (int64_t kt = 0; kt < nk; kt += 2) {
+    kstep8(std::integral_constant<int, 0>(), kt);
+    if (kt + 1 < nk) kstep8(std::integral_constant<int, 1>(), kt + 1);
   }
+  __syncthreads();
   } else {
   // Operand tiles go from memory straight into LDS (buffer loads with an LDS
   // destination: lane l of one instruction writes the 16 bytes at
