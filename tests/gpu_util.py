@@ -139,3 +139,53 @@ class Run:
                             grad_out, self.a1, accum, gx)
         torch.cuda.synchronize()
         return gx
+
+
+class Fp8Run(Run):
+    """The fp8 chain through the C entries, on top of the bf16 dispatch."""
+
+    def quant_weights(self):
+        self.wq = [dm.Fp8Weights.quantize(bf(self.inp[k])) for k in ("w_gate", "w_up", "w_down")]
+
+    def ffn8(self):
+        """fp8 forward: quantise x rows, fp8 gate/up GEMM, quantise h, fp8 down GEMM."""
+        F, H, cap = self.shape.F, self.H, self.cap
+        nrows = self.d.ep_recv_counts[-1:]
+        self.xq, self.xs = dm.quant_rows_fp8(self.d.expand_x, nrows)
+        self.gus = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+        self.h = torch.empty((cap, F), dtype=torch.bfloat16, device=DEV)
+        self.y = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+        wg, wu, wd = self.wq
+        dm.moe_ffn_gate_up_fwd_fp8(self.shape, self.xq, self.xs, wg.codes, wg.scales, wu.codes, wu.scales,
+                                   self.d.ep_recv_counts, self.gus, self.h)
+        self.hq, self.hs = dm.quant_rows_fp8(self.h, nrows)
+        dm.moe_ffn_down_fwd_fp8(self.shape, self.hq, self.hs, wd.codes, wd.scales, self.d.ep_recv_counts,
+                                self.y)
+        torch.cuda.synchronize()
+
+    def ffn8_bwd_data(self, gy):
+        """fp8 data gradients: quantise dY, fp8 down dgrad, quantise dGU, fp8 gate/up dgrad."""
+        F, H, cap = self.shape.F, self.H, self.cap
+        nrows = self.d.ep_recv_counts[-1:]
+        wg, wu, wd = self.wq
+        dyq, dys = dm.quant_rows_fp8(gy, nrows)
+        ggu = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+        dm.moe_ffn_down_bwd_data_fp8(self.shape, dyq, dys, wd.codes_t, wd.scales, self.gus,
+                                     self.d.ep_recv_counts, ggu)
+        dguq, dgus = dm.quant_rows_fp8(ggu, nrows)
+        gxe = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+        dm.moe_ffn_gate_up_bwd_data_fp8(self.shape, dguq, dgus, wg.codes_t, wg.scales, wu.codes_t, wu.scales,
+                                        self.d.ep_recv_counts, gxe)
+        torch.cuda.synchronize()
+        return ggu, gxe
+
+    def weight_grads(self, gy, ggu):
+        """bf16 weight gradients (fp32 out) of the fp8 path."""
+        E, F, H = self.shape.num_experts, self.shape.F, self.H
+        gwg = torch.empty((E, F, H), dtype=torch.float32, device=DEV)
+        gwu = torch.empty((E, F, H), dtype=torch.float32, device=DEV)
+        gwd = torch.empty((E, H, F), dtype=torch.float32, device=DEV)
+        dm.moe_ffn_down_bwd_weight(self.shape, gy, self.h, self.d.ep_recv_counts, gwd)
+        dm.moe_ffn_gate_up_bwd_weight(self.shape, ggu, self.d.expand_x, self.d.ep_recv_counts, gwg, gwu)
+        torch.cuda.synchronize()
+        return gwg, gwu, gwd

@@ -9,7 +9,7 @@ import torch
 import dispatch_expert_gemm_amd as dm
 import moe_workloads as wl
 import oracle as orc
-from gpu_util import DEV, Run, bf, check_close, check_equal, dev, f32
+from gpu_util import DEV, Fp8Run, Run, bf, check_close, check_equal, dev, f32
 
 pytestmark = pytest.mark.gpu
 
@@ -63,43 +63,6 @@ FP8_CASES = {
     "ragged_rows": dict(T=517, H=512, F=256, E=7, K=3),
     "empty_experts": dict(T=40, H=128, F=128, E=12, K=1),
 }
-
-
-class Fp8Run(Run):
-    """The fp8 chain through the C entries, on top of the bf16 dispatch."""
-
-    def quant_weights(self):
-        self.wq = [dm.Fp8Weights.quantize(bf(self.inp[k])) for k in ("w_gate", "w_up", "w_down")]
-
-    def ffn8(self):
-        F, H, cap = self.shape.F, self.H, self.cap
-        nrows = self.d.ep_recv_counts[-1:]
-        self.xq, self.xs = dm.quant_rows_fp8(self.d.expand_x, nrows)
-        self.gus = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
-        self.h = torch.empty((cap, F), dtype=torch.bfloat16, device=DEV)
-        self.y = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
-        wg, wu, wd = self.wq
-        dm.moe_ffn_gate_up_fwd_fp8(self.shape, self.xq, self.xs, wg.codes, wg.scales, wu.codes, wu.scales,
-                                   self.d.ep_recv_counts, self.gus, self.h)
-        self.hq, self.hs = dm.quant_rows_fp8(self.h, nrows)
-        dm.moe_ffn_down_fwd_fp8(self.shape, self.hq, self.hs, wd.codes, wd.scales, self.d.ep_recv_counts,
-                                self.y)
-        torch.cuda.synchronize()
-
-    def ffn8_bwd_data(self, gy):
-        F, H, cap = self.shape.F, self.H, self.cap
-        nrows = self.d.ep_recv_counts[-1:]
-        wg, wu, wd = self.wq
-        dyq, dys = dm.quant_rows_fp8(gy, nrows)
-        ggu = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
-        dm.moe_ffn_down_bwd_data_fp8(self.shape, dyq, dys, wd.codes_t, wd.scales, self.gus,
-                                     self.d.ep_recv_counts, ggu)
-        dguq, dgus = dm.quant_rows_fp8(ggu, nrows)
-        gxe = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
-        dm.moe_ffn_gate_up_bwd_data_fp8(self.shape, dguq, dgus, wg.codes_t, wg.scales, wu.codes_t, wu.scales,
-                                        self.d.ep_recv_counts, gxe)
-        torch.cuda.synchronize()
-        return ggu, gxe
 
 
 @pytest.mark.parametrize("name", list(FP8_CASES))

@@ -12,9 +12,11 @@ import torch
 import dispatch_expert_gemm_amd as dm
 import moe_workloads as wl
 import oracle as orc
-from gpu_util import DEV, Run, bf, check_close, check_equal, f32
+from gpu_util import DEV, Fp8Run, Run, bf, check_close, check_equal, f32
 
 pytestmark = pytest.mark.gpu
+
+REL_FP8 = 2e-2
 
 
 def _expert_of_rows(r, rows):
@@ -230,3 +232,119 @@ def test_dsv3_proxy_full_size():
     check_close("shared grad_w_gate", f32(s_gw[0][0][fs]), dwg[0])
     check_close("shared grad_w_up", f32(s_gw[1][0][fs]), dwu[0])
     check_close("shared grad_w_down", f32(s_gw[2][0][:, fs]), dwd[0])
+
+
+@pytest.mark.timeout(900)
+def test_mixtral_fp8_full_size():
+    """T=8192, H=4096, F=14336, E=8, K=2 on the fp8 path (e4m3 block-scaled
+    forward and data-gradient GEMMs, bf16 weight gradients, int8 combine
+    payload): the chain the benchmark times.  Against the oracle: the route in
+    full; the fp8 codes (both layouts) and block scales of the two busiest
+    experts bit for bit; sampled rows of those experts through the forward;
+    tokens routed to exactly those two experts through combine, its backward,
+    the data gradients and dispatch backward; one 128-column F block of the
+    busiest expert through G, U, h, dG, dU and the three weight gradients (an F
+    block of the weights is one column of quantisation blocks, so the oracle on
+    the block slice gives those columns exactly)."""
+    print("[full] mixtral fp8", flush=True)
+    inp = wl.layer_inputs(**{k: v for k, v in wl.WORKLOADS["mixtral"].items()}, seed=0)
+    T, H, F, K = inp["T"], inp["H"], inp["F"], inp["K"]
+    run = Fp8Run(inp)
+    run.shape.comm_quant_mode = 2
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"])
+    check_equal("ep_recv_counts", run.d.ep_recv_counts.cpu().numpy(), r.ep_recv_counts)
+    check_equal("row2slot", run.d.row2slot(T, K)[:r.A].cpu().numpy(), r.row2slot)
+    run.quant_weights()
+    run.ffn8()
+    out = run.combine()
+    g = bf(inp["grad_out"])
+    gy, gw = run.combine_bwd(g)
+    ggu, gxe = run.ffn8_bwd_data(gy)
+    gwg, gwu, gwd = run.weight_grads(gy, ggu)
+    gx = run.dispatch_bwd(gxe, g)
+    print("[full] mixtral fp8: GPU chain done, oracle quantisation of two experts", flush=True)
+
+    ea, eb = (int(e) for e in np.argsort(-r.counts, kind="stable")[:2])
+    names = ("w_gate", "w_up", "w_down")
+    wq = {}
+    for e in (ea, eb):
+        wq[e] = tuple(orc.quant_weights_fp8(inp[k][e:e + 1]) for k in names)
+        for (codes, scales), q, name in zip(wq[e], run.wq, names):
+            check_equal(f"{name} codes e={e}", q.codes[e].cpu().numpy(), codes[0])
+            check_equal(f"{name} codes_t e={e}", q.codes_t[e].cpu().numpy(), codes[0].T)
+            check_equal(f"{name} scales e={e}", q.scales[e].cpu().numpy(), scales[0])
+    X = orc.bf16_to_f32(inp["x"])
+    expert_of = _expert_of_rows(r, np.arange(r.A))
+
+    def fwd_rows(rows):
+        """Oracle fp8 forward (G, U, h, y) of expanded rows, expert by expert."""
+        G = np.zeros((len(rows), F), np.float32)
+        U, Hh = np.zeros_like(G), np.zeros_like(G)
+        Y = np.zeros((len(rows), H), np.float32)
+        es = expert_of[rows]
+        for e in np.unique(es):
+            sel = np.nonzero(es == e)[0]
+            xr = X[r.row2slot[rows[sel]] // K]
+            G[sel], U[sel], Hh[sel], Y[sel] = orc.ffn_fwd_fp8(xr, np.array([len(sel)]), *wq[int(e)])
+        return G, U, Hh, Y
+
+    rng = np.random.default_rng(13)
+    # sampled rows of both experts, and the rows of tokens routed to exactly
+    # those two experts; one oracle forward over all of them
+    samp = np.concatenate([lo + _sample(rng, hi - lo, 16) for lo, hi in (r.row_range(ea), r.row_range(eb))])
+    idx = inp["topk_idx"]
+    pair = np.nonzero(((idx[:, 0] == ea) & (idx[:, 1] == eb)) | ((idx[:, 0] == eb) & (idx[:, 1] == ea)))[0]
+    assert len(pair) >= 16
+    toks = pair[_sample(rng, len(pair), 16)]
+    sr, trows = sub_route(r, toks)
+    allrows = np.concatenate([samp, trows])
+    Ga, Ua, Ha, Ya = fwd_rows(allrows)
+    ns = len(samp)
+    check_close("G rows", f32(run.gus[samp, :F]), Ga[:ns], rel_l2=REL_FP8)
+    check_close("U rows", f32(run.gus[samp, F:]), Ua[:ns], rel_l2=REL_FP8)
+    check_close("h rows", f32(run.h[samp]), Ha[:ns], rel_l2=REL_FP8)
+    check_close("y rows", f32(run.y[samp]), Ya[:ns], rel_l2=REL_FP8)
+    Gt, Ut, Ht, Yt = Ga[ns:], Ua[ns:], Ha[ns:], Ya[ns:]
+    Yc = orc.qdq_rows_int8(Yt)
+    w_t = inp["topk_weights"][toks]
+    ref_out = orc.combine(Yc, sr, w_t, None, inp["x"][toks], None, None, None)
+    check_close("out tokens", f32(out[toks]), ref_out, rel_l2=REL_FP8)
+    dY, dw = orc.combine_bwd(inp["grad_out"][toks], Yc, sr, w_t, inp["x"][toks], None, None, None)
+    check_equal("grad_y rows", f32(gy[trows]), dY)
+    check_close("grad_topk_weights tokens", f32(gw[toks]), dw, rel_l2=REL_FP8)
+    dGU = np.zeros((len(trows), 2 * F), np.float32)
+    dX = np.zeros((len(trows), H), np.float32)
+    es = expert_of[trows]
+    for e in np.unique(es):
+        sel = np.nonzero(es == e)[0]
+        xr = X[r.row2slot[trows[sel]] // K]
+        dGU[sel], dX[sel], _, _, _ = orc.ffn_bwd_fp8(dY[sel], xr, Gt[sel], Ut[sel], Ht[sel],
+                                                     np.array([len(sel)]), *wq[int(e)])
+    check_close("grad_gate_up rows", f32(ggu[trows]), dGU, rel_l2=REL_FP8)
+    check_close("grad_expand_x rows", f32(gxe[trows]), dX, rel_l2=REL_FP8)
+    ref_dx = orc.dispatch_bwd(dX, sr, w_t, inp["grad_out"][toks], None, None)
+    check_close("grad_x tokens", f32(gx[toks]), ref_dx, rel_l2=REL_FP8)
+
+    # one F block of the busiest expert, all its rows
+    lo, hi = r.row_range(ea)
+    erows = np.arange(lo, hi)
+    toks_e, ks_e = r.row2slot[erows] // K, r.row2slot[erows] % K
+    w_e = inp["topk_weights"][toks_e, ks_e]
+    dY_e = orc.round_bf16((w_e[:, None] * orc.bf16_to_f32(inp["grad_out"][toks_e])).astype(np.float32))
+    X_e = X[toks_e]
+    b = F // 256
+    cs = slice(128 * b, 128 * b + 128)
+    (cg, sg), (cu, su), (cd, sd) = wq[ea]
+    wq_b = ((cg[:, cs], sg[:, b:b + 1]), (cu[:, cs], su[:, b:b + 1]), (cd[:, :, cs], sd[:, :, b:b + 1]))
+    n_e = np.array([hi - lo])
+    G, U, Hh, _ = orc.ffn_fwd_fp8(X_e, n_e, *wq_b)
+    check_close("G block", f32(run.gus[lo:hi, cs]), G, rel_l2=REL_FP8)
+    check_close("U block", f32(run.gus[lo:hi, F + 128 * b:F + 128 * b + 128]), U, rel_l2=REL_FP8)
+    check_close("h block", f32(run.h[lo:hi, cs]), Hh, rel_l2=REL_FP8)
+    dgu, _, dwg, dwu, dwd = orc.ffn_bwd_fp8(dY_e, X_e, G, U, Hh, n_e, *wq_b)
+    check_close("grad_gate block", f32(ggu[lo:hi, cs]), dgu[:, :128], rel_l2=REL_FP8)
+    check_close("grad_up block", f32(ggu[lo:hi, F + 128 * b:F + 128 * b + 128]), dgu[:, 128:], rel_l2=REL_FP8)
+    check_close("grad_w_gate block", f32(gwg[ea][cs]), dwg[0], rel_l2=REL_FP8)
+    check_close("grad_w_up block", f32(gwu[ea][cs]), dwu[0], rel_l2=REL_FP8)
+    check_close("grad_w_down block", f32(gwd[ea][:, cs]), dwd[0], rel_l2=REL_FP8)
