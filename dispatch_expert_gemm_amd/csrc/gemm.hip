@@ -65,6 +65,8 @@ struct GemmArgs {
   int E;
   int64_t M, N, Kd, F;
   int64_t n_tiles, m_tiles, tiles;
+  int64_t mch, nch;  // weight gradients: tiles per block along M and N
+  int kp;            // weight gradients: row blocks of an expert's tile grid
   bf16_t* C0;
   bf16_t* C1;
   const bf16_t* aux;
@@ -162,21 +164,23 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
 
   const int64_t nb = gridDim.x;
   const int64_t bid = blockIdx.x;
-  // Row-grouped GEMMs: XCD x (workgroups dispatch round-robin over the eight
-  // XCDs) takes the x-th contiguous eighth of the tiles; the work per row tile
-  // is the same for every expert, so the eighths are balanced.  Expert-grouped
-  // (weight-gradient) GEMMs keep the dispatch order: a tile's work grows with
-  // its expert's row count, and contiguous eighths would give the XCD holding
-  // the most popular experts most of the work under skewed routing; round-robin
-  // gives every XCD an equal share of every expert, and XCD x then reads only
-  // the B column strips nt = x (mod 8) when n_tiles is a multiple of eight.
-  const int64_t logical = Cfg<MODE, BM, BN>::KGROUP ? bid : (bid & 7) * (nb >> 3) + (bid >> 3);
-  if (logical >= g.tiles) return;
-
+  // Workgroups are dispatched round-robin over the eight XCDs (XCD = bid % 8).
+  // Row-grouped GEMMs: XCD x takes the x-th contiguous eighth of the tiles;
+  // the work per row tile is the same for every expert, so the eighths are
+  // balanced, and neighbouring tiles (same A rows, same expert weights) share
+  // an L2.  Expert-grouped (weight-gradient) GEMMs: a tile's work grows with
+  // its expert's row count, so each expert's tile grid is cut into eight
+  // blocks (kp row blocks x 8/kp column blocks) and every XCD takes one block
+  // of every expert (block (x + e) % 8), which balances any routing skew; an
+  // XCD then reads 1/kp of the expert's A column strips and kp/8 of its B
+  // strips (A is read 8/kp times over the chip and B kp times, instead of
+  // eight times each).
   int e;
   int64_t row0, n0, kbeg, kend;
   int rows_valid;
   if constexpr (!KGROUP) {
+    const int64_t logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+    if (logical >= g.tiles) return;
     const int64_t mt = logical / g.n_tiles;
     const int64_t nt = logical % g.n_tiles;
     e = find_expert<BM>(g.prefix, g.E, mt);
@@ -188,11 +192,18 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
     kbeg = 0;
     kend = g.Kd;
   } else {
-    const int64_t per = g.m_tiles * g.n_tiles;
-    e = (int)(logical / per);
-    const int64_t rem = logical % per;
-    row0 = (rem / g.n_tiles) * BM;  // first output row (weight row)
-    n0 = (rem % g.n_tiles) * BN;
+    const int64_t xcd = bid & 7, k = bid >> 3;
+    const int64_t per = g.mch * g.nch;  // tiles of one block
+    e = (int)(k / per);
+    if (e >= g.E) return;
+    const int64_t w = k % per;
+    const int blk = (int)((xcd + e) & 7);
+    const int kq = 8 / g.kp;
+    const int64_t mt = (blk / kq) * g.mch + w / g.nch;
+    const int64_t nt = (blk % kq) * g.nch + w % g.nch;
+    if (mt >= g.m_tiles || nt >= g.n_tiles) return;
+    row0 = mt * BM;  // first output row (weight row)
+    n0 = nt * BN;
     kbeg = e ? g.prefix[e - 1] : 0;
     kend = g.prefix[e];
     rows_valid = (int)((g.M - row0) < BM ? (g.M - row0) : BM);
@@ -774,13 +785,26 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   g.n_tiles = (ncols + bn_cols - 1) / bn_cols;
   if (MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W) {
     g.m_tiles = (g.M + BM - 1) / BM;
-    g.tiles = (int64_t)s->num_experts * g.m_tiles * g.n_tiles;
+    // blocks of the per-expert tile grid, one per XCD: kp row blocks x 8/kp
+    // column blocks, kp chosen to minimise the operand bytes the eight XCDs
+    // read (A strips are read 8/kp times, B strips kp times)
+    int best = 1;
+    double cost = -1.0;
+    for (int kp = 1; kp <= 8; kp *= 2) {
+      if (kp > g.m_tiles && kp > 1) break;
+      const double c = (double)g.M * (8 / kp) + (double)g.N * kp;
+      if (cost < 0 || c < cost) { cost = c; best = kp; }
+    }
+    g.kp = best;
+    g.mch = (g.m_tiles + best - 1) / best;
+    g.nch = (g.n_tiles + 8 / best - 1) / (8 / best);
+    g.tiles = (int64_t)s->num_experts * g.mch * g.nch * 8;
   } else {
     g.m_tiles = s->capacity / BM + s->num_experts;
     g.tiles = g.m_tiles * g.n_tiles;
   }
   if (g.tiles == 0) return MOE_OK;
-  const int64_t grid = (g.tiles + 7) / 8 * 8;
+  const int64_t grid = (g.tiles + 7) / 8 * 8;  // weight gradients: already 8 * E * block
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8>), dim3((unsigned)grid), dim3(Cfg<MODE, BM, BN>::kThreads), 0,
                      strm, g);
