@@ -46,7 +46,13 @@ enum Mode : int {
   GATE_UP_BWD_W = 5
 };
 
-constexpr int BK = 64;
+// K step of the bf16 GEMMs (elements); the fp8 GEMMs step by 128 codes, one
+// 128-byte LDS row, like a 64-element bf16 step
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+constexpr int BK = MOE_GEMM_BK;
+static_assert(BK == 64 || BK == 32, "K step of 32 or 64 bf16");
 // gfx9 s_waitcnt immediate that waits for at most n outstanding vector memory
 // operations (vmcnt in bits 3:0 and 15:14) and leaves the other counters free
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -108,8 +114,19 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 // c ^ swz(r), so the eight rows read by eight consecutive lanes of an MFMA
 // operand fetch, and the eight chunks of one row written by eight consecutive
 // lanes, fall in distinct banks.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+// Rows of W bf16 (2W bytes): W = 64 is eight chunks, swizzled by
+// (r ^ r/8) % 8; W = 32 is four chunks, swizzled by (r/2) % 4 (two neighbouring
+// 64-byte rows share one 128-byte bank window, so eight consecutive rows still
+// reach eight distinct chunk slots).
+template <int W>
+__device__ __forceinline__ int swzw(int r) {
+  if constexpr (W == 64) return (r ^ (r >> 3)) & 7;
+  else return (r >> 1) & 3;
+}
+template <int W>
+__device__ __forceinline__ int lds_offw(int r, int c) { return r * W + ((c ^ swzw<W>(r)) << 3); }
+__device__ __forceinline__ int swz(int r) { return swzw<BK>(r); }
+__device__ __forceinline__ int lds_off(int r, int c) { return lds_offw<BK>(r, c); }
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -136,7 +153,7 @@ struct Cfg {
 #define MOE_GEMM_STAGES 2
 #endif
   static constexpr int S = MOE_GEMM_STAGES;
-  static constexpr int kMain = S * (BM + BN) * BK;
+  static constexpr int kMain = cmax(S * (BM + BN) * BK, 2 * (BM + BN) * 64);  // bf16 stages / fp8 stages
   static constexpr int kEpi = KGROUP ? 0 : (MODE == GATE_UP_FWD ? 3 : MODE == DOWN_BWD_DATA ? 2 : 1) * BM * CP;
   static constexpr int kSmem = cmax(kMain, kEpi);
   // workgroups per CU that the LDS allows (160 KB per CU)
@@ -154,8 +171,9 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   // Two LDS stages of the A and B tiles; after the K loop the same memory
   // stages the output tile (and, for the SwiGLU backward, the saved G/U tile).
   __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmem];
-  auto As = [&](int st) { return smem + st * BM * BK; };
-  auto Bs = [&](int st) { return smem + C::S * BM * BK + st * BN * BK; };
+  // fp8 operand stages: BM (BN) rows of 128 bytes, two stages
+  auto As = [&](int st) { return smem + st * BM * 64; };
+  auto Bs = [&](int st) { return smem + 2 * BM * 64 + st * BN * 64; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int WM = C::WM, WN = C::WN, kThreads = C::kThreads;
@@ -242,7 +260,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   // one j tile (one B block scale).
   constexpr int S8 = 2;
   constexpr int LA = BM / 8 / (WM * WN), LB = BN / 8 / (WM * WN);
-  static_assert(S8 <= C::S || C::kMain >= S8 * (BM + BN) * BK, "fp8 stages must fit the operand LDS");
+  static_assert(C::kMain >= S8 * (BM + BN) * 64, "fp8 stages must fit the operand LDS");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto rsrc8 = [](const void* p) -> i32x4 {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
@@ -257,13 +275,13 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   uint32_t voA[LA], voB[LB];
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
-    const int r = 8 * (wave * LA + j) + (lane >> 3), c = (lane & 7) ^ swz(r);
+    const int r = 8 * (wave * LA + j) + (lane >> 3), c = (lane & 7) ^ swzw<64>(r);
     const int rr = r < rows_valid ? r : rows_valid - 1;
     voA[j] = (uint32_t)(rr * g.lda + c * 16);
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
-    const int r = 8 * (wave * LB + j) + (lane >> 3), c = (lane & 7) ^ swz(r);
+    const int r = 8 * (wave * LB + j) + (lane >> 3), c = (lane & 7) ^ swzw<64>(r);
     int64_t n;
     if constexpr (MODE == GATE_UP_FWD) {
       n = n0 + (r & (BN / 2 - 1));
@@ -333,14 +351,14 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
       i32x8 fa[TI], fb[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(as + lds_off(arow[i], c));
-        const uint4 hi = *reinterpret_cast<const uint4*>(as + lds_off(arow[i], c + 1));
+        const uint4 lo = *reinterpret_cast<const uint4*>(as + lds_offw<64>(arow[i], c));
+        const uint4 hi = *reinterpret_cast<const uint4*>(as + lds_offw<64>(arow[i], c + 1));
         fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(bs + lds_off(brw[j], c));
-        const uint4 hi = *reinterpret_cast<const uint4*>(bs + lds_off(brw[j], c + 1));
+        const uint4 lo = *reinterpret_cast<const uint4*>(bs + lds_offw<64>(brw[j], c));
+        const uint4 hi = *reinterpret_cast<const uint4*>(bs + lds_offw<64>(brw[j], c + 1));
         fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
@@ -403,10 +421,10 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   // Operand tiles go from memory straight into LDS (buffer loads with an LDS
   // destination: lane l of one instruction writes the 16 bytes at
   // instruction base + 16 l), in the operand's own memory layout:
-  //  * K-contiguous operand of R rows: R rows x 128 bytes (BK bf16), chunk c
-  //    of row r at chunk position c ^ swz(r); one instruction fills 8 rows,
-  //    lane l taking row 8q + l/8, position l%8, i.e. memory chunk
-  //    (l%8) ^ swz(row).
+  //  * K-contiguous operand of R rows: R rows x 2 BK bytes, chunk c of row r
+  //    at chunk position c ^ swz(r); one instruction fills 512/BK rows, lane l
+  //    taking row (512/BK) q + l/(BK/8), position l%(BK/8), i.e. memory chunk
+  //    position ^ swz(row).
   //  * K-strided operand of R columns: BK k-rows x 2R bytes, 16-byte chunk c
   //    of k-row k at position c ^ (2 (k%4)); one instruction fills 512/R
   //    k-rows.  MFMA fragments come out of it with transposing LDS reads
@@ -419,8 +437,10 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   // of the buffer resource (its byte count ends at the last k-row), the
   // K-contiguous A through an out-of-range offset in the last step.
   constexpr int S = C::S;
-  // load instructions per wave per stage (a tile is R/8 instructions of 1 KB)
-  constexpr int LA = BM / 8 / (WM * WN), LB = BN / 8 / (WM * WN);
+  // load instructions per wave per stage (an R x BK tile is R*BK/512
+  // instructions of 1 KB)
+  constexpr int LA = BM * BK / 512 / (WM * WN), LB = BN * BK / 512 / (WM * WN);
+  constexpr int CPRK = BK / 8, RPIK = 64 / CPRK;  // K-contiguous: chunks per row, rows per instruction
   constexpr uint32_t kOOB = 0x80000000u;
   constexpr int kRange = 0x7ffffff0;
   auto sw2 = [](int k) { return 2 * (k & 3); };
@@ -450,7 +470,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   for (int j = 0; j < LA; ++j) {
     const int q = wave * LA + j;
     if constexpr (!KGROUP) {
-      const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz(r);
+      const int r = RPIK * q + lane / CPRK, c = (lane % CPRK) ^ swz(r);
       const int rr = r < rows_valid ? r : rows_valid - 1;
       voA[j] = (uint32_t)((rr * g.lda + c * 8) * 2);
       kcA[j] = c * 8;
@@ -466,7 +486,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
   for (int j = 0; j < LB; ++j) {
     const int q = wave * LB + j;
     if constexpr (B_KC) {
-      const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ swz(r);
+      const int r = RPIK * q + lane / CPRK, c = (lane % CPRK) ^ swz(r);
       int64_t n;
       if constexpr (MODE == GATE_UP_FWD) {
         n = n0 + (r & (BN / 2 - 1));
@@ -526,7 +546,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::
         const int q = wv * LB + j;
         const uint32_t vo = (tail && k0 + kcB[j] >= kend) ? kOOB : voB[j];
         // gate/up forward: rows BN/2.. of the B tile are the up rows
-        const bool up = MODE == GATE_UP_FWD && 8 * q >= BN / 2;
+        const bool up = MODE == GATE_UP_FWD && RPIK * q >= BN / 2;
         dma(up ? r1 : r0, sb + q * 512, vo);
       }
     } else if constexpr (KGROUP) {
