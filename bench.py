@@ -212,6 +212,9 @@ def build_step(name, T_override=None):
         ("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x, None,
                                                        None, None, gy, gw)),
     ]
+    # backward order: each gather/scatter right after the kernel that produced
+    # its input (grad_expand_x goes to dispatch backward before the last
+    # weight gradient evicts it from the caches)
     if fp8:
         C += [
             ("moe_quant_rows_fp8 (dY)", lambda: dm.moe_quant_rows_fp8(gy, dyq, dys, nrows)),
@@ -221,22 +224,20 @@ def build_step(name, T_override=None):
             ("moe_quant_rows_fp8 (dGU)", lambda: dm.moe_quant_rows_fp8(ggu, dgq, dgs, nrows)),
             ("moe_ffn_gate_up_bwd_data_fp8", lambda: dm.moe_ffn_gate_up_bwd_data_fp8(
                 shape, dgq, dgs, wq[0].codes_t, wq[0].scales, wq[1].codes_t, wq[1].scales, recv, gxe)),
-            ("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
-                                                                                 gwu)),
         ]
     else:
         C += [
             ("moe_ffn_down_bwd_data", lambda: dm.moe_ffn_down_bwd_data(shape, gy, wd, gus, recv, ggu)),
             ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
             ("moe_ffn_gate_up_bwd_data", lambda: dm.moe_ffn_gate_up_bwd_data(shape, ggu, wg, wu, recv, gxe)),
-            ("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
-                                                                                 gwu)),
         ]
     if shared:
         C.append(("shared moe_grouped_ffn_bwd (4 GEMMs)", lambda: dm.moe_grouped_ffn_bwd(
             ss, gout, x, s_gus, s_h, swg, swu, swd, scnt, s_ggu, sdx, *s_gw)))
     C.append(("moe_dispatch_bwd", lambda: dm.moe_dispatch_bwd(shape, gxe, assist, idx, w, None, gout, None, sdx,
                                                               gx)))
+    C.append(("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
+                                                                                  gwu)))
     st.config = {"T": T, "H": H, "F": F, "E": E, "K": K}
     st.cfg = cfg
     st.shape_info = (T, H, F, K, E)

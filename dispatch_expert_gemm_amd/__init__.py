@@ -437,8 +437,11 @@ class _MoELayerFn(torch.autograd.Function):
         gwg = torch.empty(w_gate.shape, dtype=F32, device=dev)
         gwu = torch.empty(w_up.shape, dtype=F32, device=dev)
         gwd = torch.empty(w_down.shape, dtype=F32, device=dev)
-        moe_grouped_ffn_bwd(shape, gy, expand_x, gus, h, w_gate, w_up, w_down, recv, ggu, gx_exp,
-                            gwg, gwu, gwd)
+        # data gradients first, the gate/up weight gradient after dispatch
+        # backward (each gather right after the kernel that wrote its input)
+        moe_ffn_down_bwd_data(shape, gy, w_down, gus, recv, ggu)
+        moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
+        moe_ffn_gate_up_bwd_data(shape, ggu, w_gate, w_up, recv, gx_exp)
         accum = None
         s_grads = (None, None, None)
         if ctx.shared_ffn:
@@ -456,6 +459,7 @@ class _MoELayerFn(torch.autograd.Function):
             s_grads = (s_gwg.to(swg.dtype), s_gwu.to(swu.dtype), s_gwd.to(swd.dtype))
         gx = torch.empty((T, H), dtype=BF16, device=dev)
         moe_dispatch_bwd(shape, gx_exp, assist, topk_idx, topk_weights, mask, grad_out, a1, accum, gx)
+        moe_ffn_gate_up_bwd_weight(shape, ggu, expand_x, recv, gwg, gwu)
         g_shared = grad_out if ctx.has_shared_x else None
         return (gx, gw, gwg.to(w_gate.dtype), gwu.to(w_up.dtype), gwd.to(w_down.dtype), g_shared,
                 *s_grads, None, None, None, None, None, None, None, None)

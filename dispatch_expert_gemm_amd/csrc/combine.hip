@@ -119,6 +119,12 @@ struct CombineArgs {
   int qpay;  // comm_quant_mode 2: int8 round trip of every expert-output row
 };
 
+// Vectors per lane whose row loads are issued together before any of them is
+// used: U * KMAX 16-byte registers (at most 16), so a wave keeps up to 16 KiB of
+// row reads in flight.
+template <int KMAX>
+constexpr int kChunk = KMAX >= 16 ? 1 : 16 / KMAX;
+
 template <int KMAX>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -127,40 +133,57 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
+  const uint4* __restrict__ y = a.y;
+  const uint4* __restrict__ shared = a.shared;
+  uint4* __restrict__ out = a.out;
   float qinv[KMAX], qsc[KMAX];
-  if (a.qpay) int8_params(a.y, si, Hv, lane, qinv, qsc);
-  for (int64_t v = lane; v < Hv; v += kWave) {
-    uint4 raw[KMAX];
+  if (a.qpay) int8_params(y, si, Hv, lane, qinv, qsc);
+  constexpr int U = kChunk<KMAX>;
+  for (int64_t v0 = lane; v0 < Hv; v0 += U * kWave) {
+    uint4 raw[U][KMAX], sh[U];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (si.code[k] >= 0) raw[k] = a.y[(int64_t)si.code[k] * Hv + v];
-    float ox[8];
-    if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
-    float acc[8];
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < Hv) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      const int c = si.code[k];
-      if (c == MOE_SLOT_NONE) continue;
-      float f[8];
-      if (c >= 0) {
-        unpack8(raw[k], f);
-        if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
-      } else {
-        special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+        for (int k = 0; k < KMAX; ++k)
+          if (si.code[k] >= 0) raw[u][k] = y[(int64_t)si.code[k] * Hv + v];
+        if (shared) sh[u] = shared[t * Hv + v];
       }
-      const float wk = si.w[k];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + wk * f[i];
     }
-    if (a.shared) {
-      float s[8];
-      unpack8(a.shared[t * Hv + v], s);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + s[i];
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < Hv) {
+        float ox[8];
+        if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const int c = si.code[k];
+          if (c == MOE_SLOT_NONE) continue;
+          float f[8];
+          if (c >= 0) {
+            unpack8(raw[u][k], f);
+            if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
+          } else {
+            special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+          }
+          const float wk = si.w[k];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = acc[i] + wk * f[i];
+        }
+        if (shared) {
+          float sv[8];
+          unpack8(sh[u], sv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = acc[i] + sv[i];
+        }
+        out[t * Hv + v] = pack8(acc);
+      }
     }
-    a.out[t * Hv + v] = pack8(acc);
   }
 }
 
@@ -189,41 +212,58 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
+  const uint4* __restrict__ y = a.y;
+  const uint4* __restrict__ dout = a.dout;
+  uint4* __restrict__ dy = a.dy;
   float qinv[KMAX], qsc[KMAX];
-  if (a.qpay) int8_params(a.y, si, Hv, lane, qinv, qsc);
+  if (a.qpay) int8_params(y, si, Hv, lane, qinv, qsc);
   float dot[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) dot[k] = 0.f;
-  for (int64_t v = lane; v < Hv; v += kWave) {
-    float d[8];
-    unpack8(a.dout[t * Hv + v], d);
-    uint4 raw[KMAX];
+  constexpr int U = kChunk<KMAX>;
+  for (int64_t v0 = lane; v0 < Hv; v0 += U * kWave) {
+    uint4 raw[U][KMAX], dr[U];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (si.code[k] >= 0) raw[k] = a.y[(int64_t)si.code[k] * Hv + v];
-    float ox[8];
-    if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < Hv) {
+        dr[u] = dout[t * Hv + v];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      const int c = si.code[k];
-      if (c == MOE_SLOT_NONE) continue;
-      float f[8];
-      if (c >= 0) {
-        unpack8(raw[k], f);
-        if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
-      } else {
-        special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+        for (int k = 0; k < KMAX; ++k)
+          if (si.code[k] >= 0) raw[u][k] = y[(int64_t)si.code[k] * Hv + v];
       }
-      float p = dot[k];
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p = p + f[i] * d[i];
-      dot[k] = p;
-      if (c >= 0) {
-        float g[8];
-        const float wk = si.w[k];
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < Hv) {
+        float d[8];
+        unpack8(dr[u], d);
+        float ox[8];
+        if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) g[i] = wk * d[i];
-        a.dy[(int64_t)c * Hv + v] = pack8(g);
+        for (int k = 0; k < KMAX; ++k) {
+          const int c = si.code[k];
+          if (c == MOE_SLOT_NONE) continue;
+          float f[8];
+          if (c >= 0) {
+            unpack8(raw[u][k], f);
+            if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
+          } else {
+            special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+          }
+          float p = dot[k];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p = p + f[i] * d[i];
+          dot[k] = p;
+          if (c >= 0) {
+            float g[8];
+            const float wk = si.w[k];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i] = wk * d[i];
+            dy[(int64_t)c * Hv + v] = pack8(g);
+          }
+        }
       }
     }
   }
@@ -260,42 +300,59 @@ __global__ __launch_bounds__(256) void k_dispatch_bwd(DispatchBwdArgs a) {
   SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
   const int64_t Hv = a.Hv;
-  for (int64_t v = lane; v < Hv; v += kWave) {
-    uint4 raw[KMAX];
+  const uint4* __restrict__ dx_exp = a.dx_exp;
+  const uint4* __restrict__ accum = a.accum;
+  uint4* __restrict__ dx = a.dx;
+  constexpr int U = kChunk<KMAX>;
+  for (int64_t v0 = lane; v0 < Hv; v0 += U * kWave) {
+    uint4 raw[U][KMAX], ac[U];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (si.code[k] >= 0) raw[k] = a.dx_exp[(int64_t)si.code[k] * Hv + v];
-    float d[8];
-    if (si.any_ori) unpack8(a.dout[t * Hv + v], d);
-    float acc[8];
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < Hv) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      const int c = si.code[k];
-      if (c == MOE_SLOT_NONE) continue;
-      float f[8];
-      if (c >= 0) {
-        unpack8(raw[k], f);
-      } else if (c == MOE_SLOT_COPY) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = si.w[k] * d[i];
-      } else {
-        float p[8];
-        unpack8(a.a1[(int64_t)(-c - 3) * Hv + v], p);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = si.w[k] * (p[i] * d[i]);
+        for (int k = 0; k < KMAX; ++k)
+          if (si.code[k] >= 0) raw[u][k] = dx_exp[(int64_t)si.code[k] * Hv + v];
+        if (accum) ac[u] = accum[t * Hv + v];
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + f[i];
     }
-    if (a.accum) {
-      float s[8];
-      unpack8(a.accum[t * Hv + v], s);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + s[i];
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < Hv) {
+        float d[8];
+        if (si.any_ori) unpack8(a.dout[t * Hv + v], d);
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const int c = si.code[k];
+          if (c == MOE_SLOT_NONE) continue;
+          float f[8];
+          if (c >= 0) {
+            unpack8(raw[u][k], f);
+          } else if (c == MOE_SLOT_COPY) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = si.w[k] * d[i];
+          } else {
+            float p[8];
+            unpack8(a.a1[(int64_t)(-c - 3) * Hv + v], p);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = si.w[k] * (p[i] * d[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = acc[i] + f[i];
+        }
+        if (accum) {
+          float sv[8];
+          unpack8(ac[u], sv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = acc[i] + sv[i];
+        }
+        dx[t * Hv + v] = pack8(acc);
+      }
     }
-    a.dx[t * Hv + v] = pack8(acc);
   }
 }
 
