@@ -81,9 +81,15 @@ FFN_CASES = {
     "page1_512": dict(T=512, H=1536, F=480, E=64, K=8),
     "empty_experts": dict(T=20, H=64, F=32, E=16, K=1),
     "special_mask": dict(T=150, H=128, F=64, E=6, K=4, Z=1, C=1, Q=2, mask="2d"),
-    # >= 512 rows per expert and >= 512 weight-gradient tiles: the 256-row tile
-    # path of every GEMM, with ragged row tiles (8200 rows) and ragged F = 480
+    # many rows per expert and many weight-gradient tiles, ragged row tiles
+    # (8200 rows) and ragged F = 480 (K tail of the down GEMM, gate/up seam
+    # inside a K step of the gate/up data gradient)
     "big_tiles_ragged": dict(T=4100, H=4096, F=480, E=16, K=2),
+    # H not a multiple of the 64-wide K step: K tail of the gate/up forward
+    # and of the down data gradient (K = H), one 8-column last tile in the
+    # H-wide outputs and weight-gradient rows
+    "ragged_h": dict(T=300, H=200, F=96, E=5, K=2),
+    "ragged_h_1k": dict(T=1000, H=1096, F=224, E=9, K=3),
 }
 
 
