@@ -132,7 +132,7 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Compile-time shape of one kernel instance: BM x BN output tile, four waves
 // in a 2 x 2 arrangement, each wave (BM/2) x (BN/2) = TI x TJ MFMA 32x32 tiles.
-template <int MODE, int BM, int BN>
+template <int MODE, int BM, int BN, bool FP8>
 struct Cfg {
   static constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
   static constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
@@ -153,19 +153,21 @@ struct Cfg {
 #define MOE_GEMM_STAGES 2
 #endif
   static constexpr int S = MOE_GEMM_STAGES;
-  static constexpr int kMain = cmax(S * (BM + BN) * BK, 2 * (BM + BN) * 64);  // bf16 stages / fp8 stages
+  // bf16: S stages of BK-wide tiles; fp8: two stages of 128-byte rows
+  static constexpr int kMain = FP8 ? 2 * (BM + BN) * 64 : S * (BM + BN) * BK;
   static constexpr int kEpi = KGROUP ? 0 : (MODE == GATE_UP_FWD ? 3 : MODE == DOWN_BWD_DATA ? 2 : 1) * BM * CP;
   static constexpr int kSmem = cmax(kMain, kEpi);
-  // workgroups per CU that the LDS allows (160 KB per CU)
-  static constexpr int kMinBlocks = kSmem * 2 <= 80 * 1024 ? 2 : 1;
+  // workgroups per CU that the LDS allows (160 KB per CU), at most three
+  static constexpr int kMinBlocks =
+      kSmem * 2 <= 160 * 1024 / 3 ? 3 : (kSmem * 2 <= 80 * 1024 ? 2 : 1);
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <int MODE, int BM, int BN, bool FP8>
-__global__ __launch_bounds__((Cfg<MODE, BM, BN>::kThreads), (Cfg<MODE, BM, BN>::kMinBlocks)) void k_gemm(GemmArgs g) {
-  using C = Cfg<MODE, BM, BN>;
+__global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, BN, FP8>::kMinBlocks)) void k_gemm(GemmArgs g) {
+  using C = Cfg<MODE, BM, BN, FP8>;
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
   constexpr int TI = C::TI, TJ = C::TJ, NA = C::NA, NB = C::NB;
   // Two LDS stages of the A and B tiles; after the K loop the same memory
@@ -826,7 +828,7 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;  // weight gradients: already 8 * E * block
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8>), dim3((unsigned)grid), dim3(Cfg<MODE, BM, BN>::kThreads), 0,
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8>), dim3((unsigned)grid), dim3(Cfg<MODE, BM, BN, FP8>::kThreads), 0,
                      strm, g);
   return launch_status();
 }
