@@ -135,6 +135,9 @@ inline moe_status check_fp8_shape(const moe_shape* s) {
   moe_status st = check_ffn_shape(s);
   if (st != MOE_OK) return st;
   if (s->H % 128 != 0 || s->F % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  // the fp8 GEMMs keep one B block scale per 128-wide K block in LDS: K = H or
+  // 2F at most 32768
+  if (s->H > 32768 || 2 * s->F > 32768) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -53,6 +53,8 @@ enum Mode : int {
 #endif
 constexpr int BK = MOE_GEMM_BK;
 static_assert(BK == 64 || BK == 32, "K step of 32 or 64 bf16");
+// fp8 GEMMs: at most this many 128-wide K blocks (K <= 32768)
+constexpr int kMaxKBlocks8 = 256;
 // gfx9 s_waitcnt immediate that waits for at most n outstanding vector memory
 // operations (vmcnt in bits 3:0 and 15:14) and leaves the other counters free
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -203,7 +205,9 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
     if (logical >= g.tiles) return;
     const int64_t mt = logical / g.n_tiles;
     const int64_t nt = logical % g.n_tiles;
-    e = find_expert<BM>(g.prefix, g.E, mt);
+    // the expert index is the same in every lane; readfirstlane keeps it (and
+    // every address derived from it) in scalar registers
+    e = __builtin_amdgcn_readfirstlane(find_expert<BM>(g.prefix, g.E, mt));
     const int64_t p0 = e ? g.prefix[e - 1] : 0, p1 = g.prefix[e];
     row0 = p0 + (mt - (p0 / BM + e)) * BM;
     if (row0 >= p1) return;
@@ -272,7 +276,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
   auto dma8 = [](const i32x4& r, const bf16_t* lds, uint32_t vo) {
     const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
         (const __attribute__((address_space(3))) bf16_t*)(lds));
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0));
   };
   uint32_t voA[LA], voB[LB];
 #pragma unroll
@@ -334,15 +338,31 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
       dma8(up ? rb1 : rb0, Bs(st) + q * 512, voB[j]);
     }
   };
-  // A row scales of the lane's rows (transposed fragments: row = lane%32)
+  // A row scales of step kt go to LDS with the tiles (one 4-byte load per
+  // tile row, issued by wave 0): a plain vector load here would make the
+  // compiler wait for every load in flight, the tile loads included
+  __shared__ float sAl[2][BM];
+  __shared__ float sBl[2][kMaxKBlocks8];
   const int64_t nks = g.Kd / 128;
-  const float* sa_row[TI];
+  uint32_t vos[BM / 64];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int m = wm * (BM / WM) + i * 32 + (lane & 31);
-    sa_row[i] = g.sA + (row0 + (m < rows_valid ? m : rows_valid - 1)) * nks;
+  for (int q = 0; q < BM / 64; ++q) {
+    const int r = q * 64 + lane;
+    vos[q] = (uint32_t)((row0 + (r < rows_valid ? r : rows_valid - 1)) * nks * 4);
   }
-  auto compute8 = [&](auto ST, int64_t kt, const float* sa) {
+  auto issue_scales = [&](auto ST, int64_t kt) {
+    constexpr int st = decltype(ST)::value;
+    if (wv != 0) return;
+    const auto r = rsrc8(g.sA + kt);
+#pragma unroll
+    for (int q = 0; q < BM / 64; ++q) {
+      const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+          (const __attribute__((address_space(3))) float*)(&sAl[st][q * 64]));
+      const uint32_t vo = vos[q];
+      asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0));
+    }
+  };
+  auto compute8 = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
     const bf16_t* as = As(st);
     const bf16_t* bs = Bs(st);
@@ -379,21 +399,24 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
           }
         }
     }
-    const int64_t k0 = kt * 128;
     float sbv[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) sbv[j] = bscale(k0, (MODE == GATE_UP_FWD) ? (j >= TJ / 2) : 0);
+    for (int j = 0; j < TJ; ++j) sbv[j] = sBl[(MODE == GATE_UP_FWD && j >= TJ / 2) ? 1 : 0][kt];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const float f = sa[i] * sbv[j];
+        const float f = sAl[st][wm * (BM / WM) + i * 32 + (lane & 31)] * sbv[j];
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] += tmp[i][j][r] * f;
       }
   };
   const int64_t nk = g.Kd / 128;
-  float sa_cur[TI], sa_nxt[TI];
+  // B block scales of every K step, read once before the pipeline starts
+  for (int64_t kb = tid; kb < nk; kb += kThreads) {
+    sBl[0][kb] = bscale(kb * 128, 0);
+    if (MODE == GATE_UP_FWD) sBl[1][kb] = bscale(kb * 128, 1);
+  }
   auto kstep8 = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -402,17 +425,13 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
     asm volatile("" ::: "memory");
     if (kt + 1 < nk) {
       issue8(std::integral_constant<int, st ^ 1>(), kt + 1);
-#pragma unroll
-      for (int i = 0; i < TI; ++i) sa_nxt[i] = sa_row[i][kt + 1];
+      issue_scales(std::integral_constant<int, st ^ 1>(), kt + 1);
     }
-    compute8(ST, kt, sa_cur);
-#pragma unroll
-    for (int i = 0; i < TI; ++i) sa_cur[i] = sa_nxt[i];
+    compute8(ST, kt);
   };
   if (nk > 0) {
     issue8(std::integral_constant<int, 0>(), 0);
-#pragma unroll
-    for (int i = 0; i < TI; ++i) sa_cur[i] = sa_row[i][0];
+    issue_scales(std::integral_constant<int, 0>(), 0);
   }
   for (int64_t kt = 0; kt < nk; kt += 2) {
     kstep8(std::integral_constant<int, 0>(), kt);
@@ -462,7 +481,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
   auto dma = [](const i32x4& r, const bf16_t* lds, uint32_t vo) {
     const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
         (const __attribute__((address_space(3))) bf16_t*)(lds));
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0) : "memory");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0));
   };
   // per-lane byte offsets of this wave's load instructions (relative to the
   // step's base) and the K offset of the lane's chunk (K-contiguous operands)
