@@ -16,9 +16,19 @@ bandwidth against HBM; `cpu_baseline` is the CPU oracle on a bounded sample.
 
 `--workload` picks extra measurements (not the default line): `dsv3_proxy`
 (T=4096, hidden 7168, ffn 2048, 32 experts, top-8, Zipf-skewed routing, one
-shared expert run as a one-group GEMM over all tokens) and `mixtral` (T=8192,
+shared expert run as a one-group GEMM over all tokens), `mixtral` (T=8192,
 hidden 4096, ffn 14336, 8 experts, top-2, fp8 e4m3 block-scaled forward and
-data-gradient GEMMs, bf16 weight gradients, int8 combine payload).
+data-gradient GEMMs, bf16 weight gradients, int8 combine payload) and
+`combine_stress` (combine, its backward and dispatch backward alone at T=4096,
+hidden 7168, 256 routed + zero + copy + 2 constant experts, 2-D mask, shared
+term; `value` is the combine's GB/s).
+
+Besides the per-kernel rates inside the step, the line carries the step time
+statistics of the event pass (mean, std, mean without the three slowest
+steps), the bandwidth-bound kernels re-timed in isolation after a 512 MB write
+that evicts the Infinity Cache (`kernels_hbm_isolated`), and the layer roofline
+fraction (every GEMM at its MFMA peak plus every other kernel at HBM peak,
+over the measured step time).
 """
 from __future__ import annotations
 
@@ -42,6 +52,10 @@ WORKLOADS = {
     "page1": dict(T=8192, H=1536, F=480, E=64, K=8),
     "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
+    # combine only: 256 routed + 1 zero + 1 copy + 2 constant experts, 2-D mask
+    # with 10% false, shared_expert_x; the step is combine, combine backward and
+    # dispatch backward (on the expert-output buffer)
+    "combine_stress": dict(T=4096, H=7168, E=256, K=8, Z=1, C=1, Q=2, combine_only=True),
 }
 
 
@@ -124,13 +138,40 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
                       f"same workload (H={cfg['H']} F={cfg['F']} E={cfg['E']} K={cfg['K']}), {el:.1f} s"}
 
 
+def cpu_baseline_combine(cfg, seconds=10.0, T_sample=512):
+    """The CPU oracle's combine (parity mode) on a T_sample-token slice of the combine stress workload."""
+    import moe_workloads as wl
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    T, H, E, K, Z, C, Q = (cfg[k] for k in ("T", "H", "E", "K", "Z", "C", "Q"))
+    inp = wl.combine_inputs(T_sample, H, E, K, Z, C, Q, seed=0)
+    r = orc.route(inp["topk_idx"], E, Z, C, Q, inp["mask"])
+    Y = orc.bf16_to_f32(inp["y"])[:r.A]
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        orc.combine(Y, r, inp["topk_weights"], inp["shared_expert_x"], inp["x"], inp["const_alpha_1"],
+                    inp["const_alpha_2"], inp["const_v"])
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 200:
+            break
+    nbytes = r.A * H * 2 + T_sample * K * 12 + 2 * T_sample * H * 2
+    return {"value": nbytes * runs / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} oracle combine runs (parity mode, numpy) of a {T_sample}-token slice of the same "
+                      f"workload (H={H}, E={E}+{Z}+{C}+{Q}, K={K}), {el:.1f} s"}
+
+
 class Step:
     """The C-entry calls of one fwd+bwd step of a workload (name, thunk), in order,
     plus calls timed outside the step (fp8 weight quantisation)."""
 
     def __init__(self):
         self.calls, self.config, self.cfg = [], {}, {}
-        self.recv = self.err = None
+        self.recv = self.err = self.counts = None
         self.dtype = "bf16"
         self.extra_calls = []
 
@@ -138,6 +179,51 @@ class Step:
 def _bf(a, dev):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def build_combine_step(cfg):
+    """Combine-only step of the combine stress workload: moe_dispatch runs once
+    outside the step to build the routing maps."""
+    import torch
+    import dispatch_expert_gemm_amd as dm
+    import moe_workloads as wl
+
+    T, H, E, K, Z, C, Q = (cfg[k] for k in ("T", "H", "E", "K", "Z", "C", "Q"))
+    dev = torch.device("cuda:0")
+    log(f"[bench] combine_stress: generating inputs T={T} H={H} E={E}+{Z}+{C}+{Q} K={K}")
+    inp = wl.combine_inputs(T, H, E, K, Z, C, Q, seed=0)
+    x, y, sh, gout = (_bf(inp[k], dev) for k in ("x", "y", "shared_expert_x", "grad_out"))
+    a1, a2, cv = (_bf(inp[k], dev) for k in ("const_alpha_1", "const_alpha_2", "const_v"))
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_weights"]).to(dev)
+    mask = torch.from_numpy(inp["mask"]).to(dev)
+    shape = dm.make_shape(T, H, K, E, zero_expert_num=Z, copy_expert_num=C, const_expert_num=Q, mask_ndim=2)
+    d = dm.dispatch(shape, x, idx, mask)
+    torch.cuda.synchronize()
+    assert int(d.err_flag.item()) == 0
+    cap = shape.capacity
+    out, gy, gx = (torch.empty(sz, dtype=torch.bfloat16, device=dev) for sz in ((T, H), (cap, H), (T, H)))
+    gw = torch.empty((T, K), dtype=torch.float32, device=dev)
+    st = Step()
+    st.recv, st.err = d.ep_recv_counts, d.err_flag
+    st.calls = [
+        ("moe_combine", lambda: dm.moe_combine(shape, y, idx, w, d.assist_info_for_combine, d.ep_recv_counts,
+                                               mask, sh, x, a1, a2, cv, out)),
+        ("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, d.assist_info_for_combine,
+                                                       d.ep_recv_counts, mask, x, a1, a2, cv, gy, gw)),
+        ("moe_dispatch_bwd", lambda: dm.moe_dispatch_bwd(shape, y, d.assist_info_for_combine, idx, w, mask, gout,
+                                                         a1, None, gx)),
+    ]
+    # tokens with at least one active copy or constant slot read their ori_x /
+    # grad_out row once more
+    ids, m = inp["topk_idx"], inp["mask"].astype(bool)
+    special = ((ids >= E + Z) & m).any(axis=1)
+    st.n_ori = int(special.sum())
+    st.mask_bytes = T * K
+    st.config = {"T": T, "H": H, "F": 0, "E": E, "K": K}
+    st.cfg = cfg
+    st.shape_info = (T, H, 0, K, E)
+    return st
 
 
 def build_step(name, T_override=None):
@@ -148,6 +234,8 @@ def build_step(name, T_override=None):
     cfg = dict(WORKLOADS[name])
     if T_override:
         cfg["T"] = T_override
+    if cfg.get("combine_only"):
+        return build_combine_step(cfg)
     T, H, F, E, K = cfg["T"], cfg["H"], cfg["F"], cfg["E"], cfg["K"]
     dev = torch.device("cuda:0")
     shared = cfg.get("shared", False)
@@ -170,7 +258,7 @@ def build_step(name, T_override=None):
     gy, gw, ggu, gxe, gx = z(cap, H), z(T, K, dt=f32), z(cap, 2 * F), z(cap, H), z(T, H)
     gwg, gwu, gwd = z(E, F, H, dt=f32), z(E, F, H, dt=f32), z(E, H, F, dt=f32)
     st = Step()
-    st.recv, st.err = recv, err
+    st.recv, st.err, st.counts = recv, err, cnt
     C = st.calls
     C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
     sy = sdx = None
@@ -253,6 +341,15 @@ def build_step(name, T_override=None):
 def account(st, A):
     """FLOP and byte counts of every call of the step, given the routed rows A."""
     T, H, F, K, E = st.shape_info
+    if st.cfg.get("combine_only"):
+        Q = st.cfg["Q"]
+        nb = {"moe_combine": bytes_moved("moe_combine", T, H, F, K, A, E) + T * H * 2 + st.n_ori * H * 2
+              + 3 * Q * H * 2 + st.mask_bytes,
+              "moe_combine_bwd": bytes_moved("moe_combine_bwd", T, H, F, K, A, E) + st.n_ori * H * 2
+              + 3 * Q * H * 2 + st.mask_bytes,
+              "moe_dispatch_bwd": bytes_moved("moe_dispatch_bwd", T, H, F, K, A, E) + st.n_ori * H * 2
+              + Q * H * 2 + st.mask_bytes}
+        return {}, nb
     fp8 = st.cfg.get("fp8", False)
     pk = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     fl = {}
@@ -288,6 +385,8 @@ def main():
     ap.add_argument("--workload", default="page1", choices=list(WORKLOADS))
     ap.add_argument("--tokens", type=int, default=None, help="override T")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the cache-flushed re-timing of the bandwidth-bound kernels")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB three times "
@@ -347,10 +446,7 @@ def main():
         extra[name] = {"ms": round(e0.elapsed_time(e1), 4)}
 
     fl, nb = account(st, A)
-    total_flops = sum(f for f, _ in fl.values())
-    dom = max(fl, key=lambda k: per[k])
-    dflop, dpeak = fl[dom]
-    achieved = dflop / (per[dom] * 1e-3) / 1e12
+    combine_only = st.cfg.get("combine_only", False)
     kernels = {}
     for name, ms in per.items():
         rec = {"ms": round(ms, 4)}
@@ -362,18 +458,46 @@ def main():
             rec["GB/s"] = round(nb[name] / (ms * 1e-3) / 1e9, 1)
             rec["frac_hbm"] = round(rec["GB/s"] / PEAK_HBM_GBS, 4)
         kernels[name] = rec
-    gemm_ms = sum(per[k] for k in fl)
-    ideal_ms = sum(f / (pk * 1e12) for f, pk in fl.values()) * 1e3
+    # per-step durations from the event pass: mean, std and the mean without the
+    # three slowest steps (the Megatron page's timing protocol)
+    step_ms = sorted(ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(args.steps))
+    kept = step_ms[:-3] if len(step_ms) > 3 else step_ms
+    step_stats = {"mean": round(float(np.mean(step_ms)), 4), "std": round(float(np.std(step_ms)), 4),
+                  "mean_without_3_slowest": round(float(np.mean(kept)), 4)}
+    # the bandwidth-bound kernels once more in isolation, after writing a buffer
+    # larger than the 256 MB Infinity Cache, so their inputs come from HBM
+    isolated = {}
+    if not args.no_isolated:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        for name, fn in calls:
+            if nb.get(name) is None:
+                continue
+            times = []
+            for _ in range(5):
+                flush.zero_()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = float(np.median(times))
+            isolated[name] = {"ms": round(ms, 4), "GB/s": round(nb[name] / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(nb[name] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del flush
+    # layer roofline: every GEMM at its MFMA peak and every other kernel at HBM peak
+    t_ideal_ms = (sum(f / (pk * 1e12) for f, pk in fl.values())
+                  + sum(b / (PEAK_HBM_GBS * 1e9) for b in nb.values() if b is not None)) * 1e3
     T, H, F, E, K = (st.config[k] for k in ("T", "H", "F", "E", "K"))
     descr = {
         "page1": "Triton-distributed benchmark shape",
         "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
+        "combine_stress": "combine only, 256 routed + 1 zero + 1 copy + 2 constant experts, "
+                          "2-D mask 10% false, shared_expert_x",
     }[args.workload]
     res = {
         "metric": "MoE layer fwd+bwd ms & TFLOP/s (% MFMA peak); combine GB/s (% HBM) at 1 GPU",
-        "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -383,20 +507,48 @@ def main():
         "vs_baseline": None,
         "dtype": st.dtype,
         "data": "synthetic",
-        "config": {"workload": f"MoE layer fwd+bwd, {descr}: T={T} tokens, H={H}, F={F} SwiGLU, "
-                               f"E={E} experts on one GPU, top-{K}",
-                   "T": T, "H": H, "F": F, "E": E, "K": K, "routed_rows": A,
-                   "flop_per_step": total_flops},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                     "peak": dpeak, "unit": "TFLOP/s",
-                     "frac": round(achieved / dpeak, 4),
-                     "traffic": measured_traffic(dom) if args.workload == "page1" and not args.tokens else None},
-        "combine": {"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
-                    "frac": kernels["moe_combine"]["frac_hbm"]},
-        "gemm_ms_per_step": round(gemm_ms, 4),
-        "gemm_frac_of_mfma_roofline": round(ideal_ms / gemm_ms, 4),
-        "kernels": kernels,
     }
+    if combine_only:
+        comb = nb["moe_combine"] / (per["moe_combine"] * 1e-3) / 1e9
+        res.update({
+            "value": round(comb, 1), "unit": "GB/s",
+            "config": {"workload": f"{descr}: T={T} tokens, H={H}, E={E}, top-{K}", "T": T, "H": H, "E": E,
+                       "K": K, "routed_rows": A, "combine_bytes": nb["moe_combine"]},
+            "roofline": {"bound": "hbm", "kernel": "moe_combine", "achieved": round(comb, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(comb / PEAK_HBM_GBS, 4),
+                         "traffic": None},
+        })
+    else:
+        total_flops = sum(f for f, _ in fl.values())
+        dom = max(fl, key=lambda k: per[k])
+        dflop, dpeak = fl[dom]
+        achieved = dflop / (per[dom] * 1e-3) / 1e12
+        gemm_ms = sum(per[k] for k in fl)
+        ideal_ms = sum(f / (pk * 1e12) for f, pk in fl.values()) * 1e3
+        config = {"workload": f"MoE layer fwd+bwd, {descr}: T={T} tokens, H={H}, F={F} SwiGLU, "
+                              f"E={E} experts on one GPU, top-{K}",
+                  "T": T, "H": H, "F": F, "E": E, "K": K, "routed_rows": A, "flop_per_step": total_flops}
+        if st.counts is not None:
+            c = st.counts.cpu().numpy()
+            config["expert_rows_max_over_mean"] = round(float(c.max() / max(c.mean(), 1e-9)), 3)
+        res.update({
+            "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s",
+            "config": config,
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                         "peak": dpeak, "unit": "TFLOP/s",
+                         "frac": round(achieved / dpeak, 4),
+                         "traffic": measured_traffic(dom) if args.workload == "page1" and not args.tokens else None},
+            "combine": {"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
+                        "frac": kernels["moe_combine"]["frac_hbm"]},
+            "gemm_ms_per_step": round(gemm_ms, 4),
+            "gemm_frac_of_mfma_roofline": round(ideal_ms / gemm_ms, 4),
+        })
+    res["layer_roofline_frac"] = round(t_ideal_ms / ms_per_step, 4)
+    res["step_ms_events"] = step_stats
+    res["kernels"] = kernels
+    if isolated:
+        res["kernels_hbm_isolated"] = isolated
     if extra:
         res["outside_step"] = extra
     if args.workload == "page1":
@@ -410,6 +562,9 @@ def main():
         torch.cuda.synchronize()
     if args.no_cpu_baseline:
         pass
+    elif combine_only:
+        log("[bench] CPU oracle baseline (combine)")
+        res["cpu_baseline"] = cpu_baseline_combine(st.cfg, args.cpu_seconds)
     elif st.cfg.get("fp8"):
         # the oracle re-quantises all expert weights blockwise per run (minutes at this size)
         res["cpu_baseline"] = None
