@@ -119,6 +119,16 @@ struct CombineArgs {
   int qpay;  // comm_quant_mode 2: int8 round trip of every expert-output row
 };
 
+// A gathered expert-row vector, loaded non-temporally: each row is read once
+// (by its token's wave), so the load should not displace cached data (measured
+// on MI355X: 3.1 -> 4.0 TB/s for combine and 3.2 -> 4.5 TB/s for dispatch
+// backward with the inputs in HBM).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_row(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Vectors per lane whose row loads are issued together before any of them is
 // used: U * KMAX 16-byte registers (at most 16), so a wave keeps up to 16 KiB of
 // row reads in flight.
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       if (v < Hv) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (si.code[k] >= 0) raw[u][k] = y[(int64_t)si.code[k] * Hv + v];
+          if (si.code[k] >= 0) raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
         if (shared) sh[u] = shared[t * Hv + v];
       }
     }
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
         dr[u] = dout[t * Hv + v];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (si.code[k] >= 0) raw[u][k] = y[(int64_t)si.code[k] * Hv + v];
+          if (si.code[k] >= 0) raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
       }
     }
 #pragma unroll
@@ -312,7 +322,7 @@ __global__ __launch_bounds__(256) void k_dispatch_bwd(DispatchBwdArgs a) {
       if (v < Hv) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (si.code[k] >= 0) raw[u][k] = dx_exp[(int64_t)si.code[k] * Hv + v];
+          if (si.code[k] >= 0) raw[u][k] = ld_row(&dx_exp[(int64_t)si.code[k] * Hv + v]);
         if (accum) ac[u] = accum[t * Hv + v];
       }
     }
