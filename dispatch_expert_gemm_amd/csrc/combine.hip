@@ -383,12 +383,6 @@ inline void launch_k(int K, Fn f) {
   else f(std::integral_constant<int, 16>{});
 }
 
-// Waves per token for the column-parallel kernels (combine, dispatch
-// backward): wide rows are split over several waves so that more row loads are
-// in flight (measured on MI355X at H = 7168: 4.1 -> 4.6 TB/s for combine with
-// the inputs in HBM).
-inline int token_split(int64_t Hv) { return Hv >= 512 ? 4 : (Hv >= 256 ? 2 : 1); }
-
 inline dim3 token_grid(int64_t T) {
   return dim3((unsigned)((T + kWavesPerBlock - 1) / kWavesPerBlock));
 }
@@ -428,7 +422,10 @@ extern "C" moe_status moe_combine(const moe_shape* s, const void* y, const int32
                 static_cast<const uint4*>(const_alpha_2), static_cast<const uint4*>(const_v),
                 static_cast<uint4*>(out),          s->T,
                 s->K,                              s->H / 8,
-                s->comm_quant_mode == 2,           token_split(s->H / 8)};
+                s->comm_quant_mode == 2,
+                // the int8 payload needs every row's amax, which one wave per
+                // token computes once
+                s->comm_quant_mode == 2 ? 1 : token_split(s->H / 8, s->K)};
   launch_k(s->K, [&](auto km) {
     hipLaunchKernelGGL(k_combine<decltype(km)::value>, token_grid(s->T * a.split), dim3(256), 0,
                        as_stream(stream), a);
@@ -498,7 +495,7 @@ extern "C" moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expa
                     s->T,
                     s->K,
                     s->H / 8,
-                    token_split(s->H / 8)};
+                    token_split(s->H / 8, s->K)};
   launch_k(s->K, [&](auto km) {
     hipLaunchKernelGGL(k_dispatch_bwd<decltype(km)::value>, token_grid(s->T * a.split), dim3(256), 0,
                        as_stream(stream), a);

@@ -17,7 +17,8 @@
 //   k_route_rank   one wave per chunk: stable rank of each routed slot among
 //                  the slots of its expert in the chunk (wave ballots), writes
 //                  slot->row and row->slot
-//   k_permute      one wave per token: read x[t] once, write it to its rows
+//   k_permute      one wave (or 2-4 for wide rows) per token: read x[t] once,
+//                  write it to its rows
 #include "common.hpp"
 
 namespace moe {
@@ -220,16 +221,19 @@ __global__ __launch_bounds__(256) void k_route_rank(RouteArgs a, const int32_t* 
 
 __global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x,
                                                  const int32_t* __restrict__ slot2row, int64_t T,
-                                                 int K, int64_t Hv, uint4* __restrict__ ex) {
+                                                 int K, int64_t Hv, int split, uint4* __restrict__ ex) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const int64_t t = gw / split;
+  const int part = (int)(gw - t * split);
   if (t >= T) return;
   const int my = lane < K ? slot2row[t * K + lane] : -1;
   int rows[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) rows[k] = k < K ? __builtin_amdgcn_readlane(my, k) : -1;
   const uint4* xr = x + t * Hv;
-  for (int64_t v = lane; v < Hv; v += kWave) {
+  // the wave's column blocks are part, part + split, ...
+  for (int64_t v = lane + part * kWave; v < Hv; v += (int64_t)split * kWave) {
     const uint4 val = xr[v];
 #pragma unroll
     for (int k = 0; k < 16; ++k)
@@ -335,9 +339,10 @@ extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int3
                        g.nchunks, g.R, nbits, slot2row, row2slot);
   }
   if (s->T > 0) {
-    const int64_t pb = (s->T + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int split = token_split(s->H / 8, s->K);
+    const int64_t pb = (s->T * split + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(k_permute, dim3((unsigned)pb), dim3(256), 0, strm,
-                       static_cast<const uint4*>(x), slot2row, s->T, s->K, s->H / 8,
+                       static_cast<const uint4*>(x), slot2row, s->T, s->K, s->H / 8, split,
                        static_cast<uint4*>(expand_x));
   }
   return launch_status();
