@@ -103,6 +103,36 @@ __device__ __forceinline__ void int8_qdq(float* f, float inv, float sc) {
   for (int i = 0; i < 8; ++i) f[i] = fminf(fmaxf(rintf(f[i] * inv), -127.0f), 127.0f) * sc;
 }
 
+// int8 parameters from rows already in registers: the token's whole rows are
+// one chunk of U vectors per lane (all lanes take part in the butterfly).
+template <int KMAX, int U>
+__device__ __forceinline__ void int8_params_regs(const uint4 (&raw)[U][KMAX], const SlotInfo<KMAX>& si,
+                                                 int lane, int64_t Hv, float* qinv, float* qsc) {
+  float mx[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) mx[k] = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (lane + u * kWave < Hv) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (si.code[k] >= 0) {
+          float f[8];
+          unpack8(raw[u][k], f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mx[k] = fmaxf(mx[k], fabsf(f[i]));
+        }
+    }
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    float m = mx[k];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    qinv[k] = m > 0.f ? __fdiv_rn(127.0f, m) : 0.f;
+    qsc[k] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
+  }
+}
+
 struct CombineArgs {
   const uint4* y;
   const float* w;
@@ -136,7 +166,7 @@ __device__ __forceinline__ uint4 ld_row(const uint4* p) {
 template <int KMAX>
 constexpr int kChunk = KMAX >= 16 ? 1 : 16 / KMAX;
 
-template <int KMAX>
+template <int KMAX, bool ONE_PASS>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -150,9 +180,25 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const uint4* __restrict__ shared = a.shared;
   uint4* __restrict__ out = a.out;
   float qinv[KMAX], qsc[KMAX];
-  if (a.qpay) int8_params(y, si, Hv, lane, qinv, qsc);
   constexpr int U = kChunk<KMAX>;
   const int64_t vs = (int64_t)a.split * kWave;  // stride between a wave's column blocks
+  // int8 payload: when the token's rows fit in one chunk (ONE_PASS; split is 1
+  // with the payload), the rows are read once and the amax comes from the
+  // registers; otherwise a first pass over the rows finds it
+  constexpr bool one_pass = ONE_PASS;
+  uint4 pre[ONE_PASS ? U : 1][KMAX];
+  if constexpr (ONE_PASS) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (lane + u * kWave < Hv) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          if (si.code[k] >= 0) pre[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + lane + u * kWave]);
+      }
+    int8_params_regs<KMAX, U>(pre, si, lane, Hv, qinv, qsc);
+  } else if (a.qpay) {
+    int8_params(y, si, Hv, lane, qinv, qsc);
+  }
   for (int64_t v0 = lane + part * kWave; v0 < Hv; v0 += U * vs) {
     uint4 raw[U][KMAX], sh[U];
 #pragma unroll
@@ -161,7 +207,10 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       if (v < Hv) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (si.code[k] >= 0) raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
+          if (si.code[k] >= 0) {
+            if constexpr (one_pass) raw[u][k] = pre[u][k];
+            else raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
+          }
         if (shared) sh[u] = shared[t * Hv + v];
       }
     }
@@ -218,7 +267,7 @@ struct CombineBwdArgs {
   int qpay;
 };
 
-template <int KMAX>
+template <int KMAX, bool ONE_PASS>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -230,11 +279,25 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   const uint4* __restrict__ dout = a.dout;
   uint4* __restrict__ dy = a.dy;
   float qinv[KMAX], qsc[KMAX];
-  if (a.qpay) int8_params(y, si, Hv, lane, qinv, qsc);
+  constexpr int U = kChunk<KMAX>;
+  // int8 payload: one read of the rows when they fit in one chunk (as in combine)
+  constexpr bool one_pass = ONE_PASS;
+  uint4 pre[ONE_PASS ? U : 1][KMAX];
+  if constexpr (ONE_PASS) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (lane + u * kWave < Hv) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          if (si.code[k] >= 0) pre[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + lane + u * kWave]);
+      }
+    int8_params_regs<KMAX, U>(pre, si, lane, Hv, qinv, qsc);
+  } else if (a.qpay) {
+    int8_params(y, si, Hv, lane, qinv, qsc);
+  }
   float dot[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) dot[k] = 0.f;
-  constexpr int U = kChunk<KMAX>;
   for (int64_t v0 = lane; v0 < Hv; v0 += U * kWave) {
     uint4 raw[U][KMAX], dr[U];
 #pragma unroll
@@ -244,7 +307,10 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
         dr[u] = dout[t * Hv + v];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (si.code[k] >= 0) raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
+          if (si.code[k] >= 0) {
+            if constexpr (one_pass) raw[u][k] = pre[u][k];
+            else raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
+          }
       }
     }
 #pragma unroll
@@ -427,8 +493,11 @@ extern "C" moe_status moe_combine(const moe_shape* s, const void* y, const int32
                 // token computes once
                 s->comm_quant_mode == 2 ? 1 : token_split(s->H / 8, s->K)};
   launch_k(s->K, [&](auto km) {
-    hipLaunchKernelGGL(k_combine<decltype(km)::value>, token_grid(s->T * a.split), dim3(256), 0,
-                       as_stream(stream), a);
+    constexpr int KM = decltype(km)::value;
+    if (a.qpay && a.Hv <= (int64_t)kChunk<KM> * kWave)
+      hipLaunchKernelGGL((k_combine<KM, true>), token_grid(s->T * a.split), dim3(256), 0, as_stream(stream), a);
+    else
+      hipLaunchKernelGGL((k_combine<KM, false>), token_grid(s->T * a.split), dim3(256), 0, as_stream(stream), a);
   });
   return launch_status();
 }
@@ -466,8 +535,11 @@ extern "C" moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, 
                    s->H / 8,
                    s->comm_quant_mode == 2};
   launch_k(s->K, [&](auto km) {
-    hipLaunchKernelGGL(k_combine_bwd<decltype(km)::value>, token_grid(s->T), dim3(256), 0,
-                       as_stream(stream), a);
+    constexpr int KM = decltype(km)::value;
+    if (a.qpay && a.Hv <= (int64_t)kChunk<KM> * kWave)
+      hipLaunchKernelGGL((k_combine_bwd<KM, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+    else
+      hipLaunchKernelGGL((k_combine_bwd<KM, false>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
   });
   return launch_status();
 }
