@@ -17,21 +17,25 @@
 // over the expert's rows, which may be none).
 //
 // Tiling: a BM x BN output tile per 256-thread workgroup (128 x 128 is
-// launched), four waves in a 2 x 2 arrangement, each wave (BM/2) x (BN/2) of
-// v_mfma_f32_32x32x16_bf16 tiles, two workgroups (eight waves) per CU.  K steps
-// of 64 go from memory straight into LDS (buffer loads with an LDS
-// destination, no register staging), two LDS stages: the loads of step t+1
-// are in flight while the MFMAs of step t issue.  Operands keep their memory
-// layout in LDS: K-contiguous tiles as rows of 64 k with an XOR-swizzled
-// chunk order (one conflict-free 16-byte read per MFMA operand), K-strided
-// tiles as k-rows read into MFMA operands with the transposing LDS read.
+// launched), four waves in a 2 x 2 arrangement, each wave 64 x 64 of
+// v_mfma_f32_32x32x16_bf16 tiles (fp8: v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit block scales, the fp32 scales applied per 128-wide K block), two
+// workgroups (eight waves) per CU.  K steps of 64 (fp8: 128 codes) go from
+// memory straight into LDS (buffer loads with an LDS destination, no register
+// staging), two LDS stages: the loads of step t+1 are in flight while the
+// MFMAs of step t issue.  Operands keep their memory layout in LDS:
+// K-contiguous tiles as rows of 128 bytes with an XOR-swizzled chunk order
+// (one conflict-free 16-byte read per MFMA operand), K-strided tiles as
+// k-rows read into MFMA operands with the transposing LDS read.  Row-grouped
+// modes accumulate transposed fragments, so each lane holds runs of four
+// output columns for the epilogue.
 //
 // Expert counts stay on the device: the grid covers floor(capacity/BM) + E row
 // tiles per column tile, and each workgroup finds its expert from the prefix
 // counts with one wave ballot (expert e owns row-tile slots starting at
-// prefix[e-1]/BM + e); surplus workgroups exit at once.  In the row-grouped
-// GEMMs workgroup ids are remapped so that consecutive tiles (sharing A rows
-// and expert weights) land on the same XCD and its L2.
+// prefix[e-1]/BM + e); surplus workgroups exit at once.  Workgroups are dealt
+// to the XCDs so that neighbouring row tiles share an L2 (row-grouped modes)
+// and every XCD gets a block of every expert (weight gradients).
 #include "common.hpp"
 
 namespace moe {
@@ -141,10 +145,6 @@ struct Cfg {
   // waves: WM along M x WN along N, each a 64 x 64 block of 2 x 2 MFMA tiles
   static constexpr int WM = BM / 64, WN = BN / 64, kThreads = 64 * WM * WN;
   static constexpr int TI = 2, TJ = 2;
-  // registers (16-byte vectors) per thread per K step: a K-contiguous R-row
-  // operand is R/32 vectors, a K-strided one R/128 blocks of 4 k-rows
-  static constexpr int NA = KGROUP ? 4 * (BM / 128) : BM / 32;
-  static constexpr int NB = B_KC ? BN / 32 : 4 * (BN / 128);
   // output columns staged in LDS at once by the epilogue, and its row pitch;
   // the 16-byte pad puts rows m and m+4 (written by the two half-waves of one
   // store instruction) in different banks
@@ -171,7 +171,7 @@ template <int MODE, int BM, int BN, bool FP8>
 __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, BN, FP8>::kMinBlocks)) void k_gemm(GemmArgs g) {
   using C = Cfg<MODE, BM, BN, FP8>;
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
-  constexpr int TI = C::TI, TJ = C::TJ, NA = C::NA, NB = C::NB;
+  constexpr int TI = C::TI, TJ = C::TJ;
   // Two LDS stages of the A and B tiles; after the K loop the same memory
   // stages the output tile (and, for the SwiGLU backward, the saved G/U tile).
   __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmem];
