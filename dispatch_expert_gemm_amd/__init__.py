@@ -373,12 +373,17 @@ class _MoELayerFn(torch.autograd.Function):
     A shared expert (shared_w_*) runs as the same grouped FFN with one expert
     whose rows are all T tokens in order, so x itself is its expanded input;
     its output is the shared_expert_x of combine and its input gradient is
-    added to grad_x by dispatch_bwd (grad_x_accum)."""
+    added to grad_x by dispatch_bwd (grad_x_accum).
+
+    fp8: the routed experts' forward and data-gradient GEMMs run on e4m3
+    operands (weights quantised in 128 x 128 blocks at every forward,
+    activations per (row, 128 columns)), the weight gradients in bf16; the
+    shared expert stays bf16.  comm_quant_mode 2: the int8 combine payload."""
 
     @staticmethod
     def forward(ctx, x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
                 shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1, const_alpha_2,
-                const_v, zero_expert_num, copy_expert_num, const_expert_num):
+                const_v, zero_expert_num, copy_expert_num, const_expert_num, fp8, comm_quant_mode):
         T, H = x.shape
         K = topk_idx.shape[1]
         E, F, _ = w_gate.shape
@@ -386,14 +391,26 @@ class _MoELayerFn(torch.autograd.Function):
         mask_ndim = 0 if x_active_mask is None else x_active_mask.dim()
         shape = make_shape(T, H, K, E, F=F, zero_expert_num=zero_expert_num,
                            copy_expert_num=copy_expert_num, const_expert_num=const_expert_num,
-                           mask_ndim=mask_ndim)
+                           mask_ndim=mask_ndim, comm_quant_mode=comm_quant_mode)
         mask = None if x_active_mask is None else x_active_mask.view(torch.uint8)
         d = dispatch(shape, x, topk_idx, mask)
         cap = shape.capacity
         gus = torch.empty((cap, 2 * F), dtype=BF16, device=dev)
         h = torch.empty((cap, F), dtype=BF16, device=dev)
         y = torch.empty((cap, H), dtype=BF16, device=dev)
-        moe_grouped_ffn(shape, d.expand_x, w_gate, w_up, w_down, d.ep_recv_counts, gus, h, y)
+        ctx.fp8 = bool(fp8)
+        wq = ()
+        if ctx.fp8:
+            nrows = d.ep_recv_counts[-1:]
+            wq = tuple(Fp8Weights.quantize(w) for w in (w_gate, w_up, w_down))
+            xq, xs = quant_rows_fp8(d.expand_x, nrows)
+            moe_ffn_gate_up_fwd_fp8(shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales,
+                                    d.ep_recv_counts, gus, h)
+            hq, hs = quant_rows_fp8(h, nrows)
+            moe_ffn_down_fwd_fp8(shape, hq, hs, wq[2].codes, wq[2].scales, d.ep_recv_counts, y)
+            del xq, xs, hq, hs
+        else:
+            moe_grouped_ffn(shape, d.expand_x, w_gate, w_up, w_down, d.ep_recv_counts, gus, h, y)
         ctx.shared_ffn = shared_w_gate is not None
         s_saved = ()
         if ctx.shared_ffn:
@@ -417,6 +434,9 @@ class _MoELayerFn(torch.autograd.Function):
         ctx.save_for_backward(x, topk_weights, w_gate, w_up, w_down, topk_idx, mask, const_alpha_1,
                               const_alpha_2, const_v, d.expand_x, d.assist_info_for_combine,
                               d.ep_recv_counts, gus, h, y, *s_saved)
+        # the transposed weight codes of the data-gradient GEMMs (not tensors
+        # of the graph, so kept on ctx)
+        ctx.wq = tuple((q.codes_t, q.scales) for q in wq)
         return out
 
     @staticmethod
@@ -439,9 +459,20 @@ class _MoELayerFn(torch.autograd.Function):
         gwd = torch.empty(w_down.shape, dtype=F32, device=dev)
         # data gradients first, the gate/up weight gradient after dispatch
         # backward (each gather right after the kernel that wrote its input)
-        moe_ffn_down_bwd_data(shape, gy, w_down, gus, recv, ggu)
-        moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
-        moe_ffn_gate_up_bwd_data(shape, ggu, w_gate, w_up, recv, gx_exp)
+        if ctx.fp8:
+            (wgt, wgs), (wut, wus), (wdt, wds) = ctx.wq
+            nrows = recv[-1:]
+            dyq, dys = quant_rows_fp8(gy, nrows)
+            moe_ffn_down_bwd_data_fp8(shape, dyq, dys, wdt, wds, gus, recv, ggu)
+            moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
+            del dyq, dys
+            dgq, dgs = quant_rows_fp8(ggu, nrows)
+            moe_ffn_gate_up_bwd_data_fp8(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)
+            del dgq, dgs
+        else:
+            moe_ffn_down_bwd_data(shape, gy, w_down, gus, recv, ggu)
+            moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
+            moe_ffn_gate_up_bwd_data(shape, ggu, w_gate, w_up, recv, gx_exp)
         accum = None
         s_grads = (None, None, None)
         if ctx.shared_ffn:
@@ -462,13 +493,14 @@ class _MoELayerFn(torch.autograd.Function):
         moe_ffn_gate_up_bwd_weight(shape, ggu, expand_x, recv, gwg, gwu)
         g_shared = grad_out if ctx.has_shared_x else None
         return (gx, gw, gwg.to(w_gate.dtype), gwu.to(w_up.dtype), gwd.to(w_down.dtype), g_shared,
-                *s_grads, None, None, None, None, None, None, None, None)
+                *s_grads, None, None, None, None, None, None, None, None, None, None)
 
 
 def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=None,
               shared_expert_x=None, shared_w_gate=None, shared_w_up=None, shared_w_down=None,
               const_alpha_1=None, const_alpha_2=None, const_v=None,
-              zero_expert_num=0, copy_expert_num=0, const_expert_num=0):
+              zero_expert_num=0, copy_expert_num=0, const_expert_num=0, fp8=False,
+              comm_quant_mode=0):
     """One MoE layer (ori_x is x itself).
 
     The shared-expert term of combine is either given (shared_expert_x) or
@@ -476,8 +508,12 @@ def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=
     (1, Fs, H), shared_w_down of shape (1, H, Fs)).  Differentiable in x,
     topk_weights, all expert weights and shared_expert_x.  Weight gradients are
     computed in fp32 and returned in the weights' dtype; use the C entries
-    directly to keep fp32."""
+    directly to keep fp32.
+
+    fp8=True runs the routed experts' forward and data-gradient GEMMs on
+    block-scaled e4m3 operands (H and F multiples of 128); comm_quant_mode=2
+    sends the expert outputs through the int8 combine payload."""
     return _MoELayerFn.apply(x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
                              shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1,
                              const_alpha_2, const_v, zero_expert_num, copy_expert_num,
-                             const_expert_num)
+                             const_expert_num, fp8, comm_quant_mode)

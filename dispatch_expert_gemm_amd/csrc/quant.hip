@@ -2,8 +2,9 @@
 //
 //  * rows: one scale per (row, 128 consecutive columns), codes = e4m3(x * (448/amax)),
 //    scale = amax/448 (both fp32, correctly rounded); an all-zero block gets codes 0
-//    and scale 1.  16 lanes own one block (8 columns each), so the block's amax is
-//    a 16-lane butterfly and every load and store is a full vector.
+//    and scale 1.  16 lanes own one block (8 columns each) of four consecutive
+//    rows, so the block's amax is a 16-lane butterfly and every load and store is
+//    a full vector.
 //  * weights: one scale per 128 x 128 block of each expert's (out, in) matrix, same
 //    rule; the kernel also writes the codes transposed, so the data-gradient GEMMs
 //    read their fp8 weights K-contiguous like the forward ones.  The block scales
@@ -17,32 +18,50 @@
 namespace moe {
 namespace {
 
+// 16 lanes own one (row, 128-column) block, 8 columns each, and take the same
+// block of kRowsPerGroup consecutive rows, all loads issued before the first
+// amax, so each lane keeps several row reads in flight.
+constexpr int kRowsPerGroup = 4;
+
 __global__ __launch_bounds__(256) void k_quant_rows_fp8(const uint4* __restrict__ src, int64_t R,
                                                         int64_t C, const int32_t* __restrict__ nrows,
                                                         uint2* __restrict__ codes,
                                                         float* __restrict__ scales) {
   const int64_t nb = C / 128;  // blocks per row
-  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // block id
+  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // 16-lane group id
   const int sub = threadIdx.x & 15;
-  const int64_t row = g / nb, blk = g % nb;
-  const int64_t rows = nrows ? (int64_t)*nrows : R;
-  if (row >= R || row >= rows) return;  // a whole 16-lane group leaves together
-  const int64_t v = row * (C / 8) + blk * 16 + sub;  // 8-element vector index
-  float f[8];
-  unpack8(src[v], f);
-  float amax = 0.f;
+  const int64_t rg = g / nb, blk = g % nb;
+  int64_t rows = nrows ? (int64_t)*nrows : R;
+  if (rows > R) rows = R;
+  const int64_t r0 = rg * kRowsPerGroup;
+  if (r0 >= rows) return;  // a whole 16-lane group leaves together
+  uint4 raw[kRowsPerGroup];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  for (int i = 0; i < kRowsPerGroup; ++i)
+    if (r0 + i < rows) raw[i] = src[(r0 + i) * (C / 8) + blk * 16 + sub];
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-  const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
-  uint32_t lo = 0, hi = 0;
+  for (int i = 0; i < kRowsPerGroup; ++i) {
+    const int64_t row = r0 + i;
+    float f[8];
+    if (row < rows) unpack8(raw[i], f);
+    else
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__fmul_rn(f[i], inv)) << (8 * i);
+      for (int q = 0; q < 8; ++q) f[q] = 0.f;
+    float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__fmul_rn(f[4 + i], inv)) << (8 * i);
-  codes[v] = make_uint2(lo, hi);
-  if (sub == 0) scales[row * nb + blk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    if (row >= rows) continue;
+    const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo |= f32_to_e4m3(__fmul_rn(f[q], inv)) << (8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hi |= f32_to_e4m3(__fmul_rn(f[4 + q], inv)) << (8 * q);
+    codes[row * (C / 8) + blk * 16 + sub] = make_uint2(lo, hi);
+    if (sub == 0) scales[row * nb + blk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  }
 }
 
 // One 256-thread block per 128 x 128 weight block.  Thread t owns rows
@@ -113,7 +132,7 @@ extern "C" moe_status moe_quant_rows_fp8(int64_t R, int64_t C, const void* src,
     return MOE_ERR_BAD_SHAPE;
   if (R == 0) return MOE_OK;
   if (!src || !codes || !scales) return MOE_ERR_NULL_ARG;
-  const int64_t groups = R * (C / 128);        // 16 lanes each
+  const int64_t groups = (R + kRowsPerGroup - 1) / kRowsPerGroup * (C / 128);  // 16 lanes each
   const int64_t blocks = (groups * 16 + 255) / 256;
   hipLaunchKernelGGL(k_quant_rows_fp8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const uint4*>(src), R, C, nrows, reinterpret_cast<uint2*>(codes),

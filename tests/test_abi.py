@@ -145,3 +145,13 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
     import torch
     with pytest.raises(dm.MoeError):
         dm._ptr(torch.zeros(3), torch.float32, "cpu tensor")
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

@@ -143,3 +143,24 @@ def test_fp8_layer_forward_backward():
     check_close("grad_w_gate", f32(gwg), b["dWg"], rel_l2=REL_FP8)
     check_close("grad_w_up", f32(gwu), b["dWu"], rel_l2=REL_FP8)
     check_close("grad_w_down", f32(gwd), b["dWd"], rel_l2=REL_FP8)
+
+
+def test_autograd_layer_fp8_int8_payload():
+    """moe_layer(fp8=True, comm_quant_mode=2): the autograd function on the fp8
+    path (weights quantised inside the layer) against the oracle's fp8 layer."""
+    inp = wl.layer_inputs(384, 256, 256, 6, 2, seed=39, mask="2d", Z=1)
+    x = bf(inp["x"]).requires_grad_(True)
+    w = dev(inp["topk_weights"]).requires_grad_(True)
+    ws = [bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down")]
+    out = dm.moe_layer(x, dev(inp["topk_idx"]), w, *ws, x_active_mask=dev(inp["mask"]), zero_expert_num=1,
+                       fp8=True, comm_quant_mode=2)
+    out.backward(bf(inp["grad_out"]))
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_fp8(inp)
+    b = orc.layer_bwd_fp8(inp, f, inp["grad_out"])
+    check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
+    check_close("grad_x", f32(x.grad), b["dx"], rel_l2=REL_FP8)
+    check_close("grad_topk_weights", f32(w.grad), b["dw"], rel_l2=REL_FP8)
+    for t, k in zip(ws, ("dWg", "dWu", "dWd")):
+        # returned in the weights' dtype (bf16)
+        check_close(k, f32(t.grad), orc.round_bf16(b[k]), rel_l2=REL_FP8)
