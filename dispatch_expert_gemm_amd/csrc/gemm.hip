@@ -50,13 +50,9 @@ enum Mode : int {
   GATE_UP_BWD_W = 5
 };
 
-// K step of the bf16 GEMMs (elements); the fp8 GEMMs step by 128 codes, one
-// 128-byte LDS row, like a 64-element bf16 step
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-constexpr int BK = MOE_GEMM_BK;
-static_assert(BK == 64 || BK == 32, "K step of 32 or 64 bf16");
+// The K step of the bf16 GEMMs (BK elements, 64 or 32) is a parameter of the
+// kernel; the fp8 GEMMs step by 128 codes, one 128-byte LDS row, like a
+// 64-element bf16 step.
 // fp8 GEMMs: at most this many 128-wide K blocks (K <= 32768)
 constexpr int kMaxKBlocks8 = 256;
 // gfx9 s_waitcnt immediate that waits for at most n outstanding vector memory
@@ -131,33 +127,37 @@ __device__ __forceinline__ int swzw(int r) {
 }
 template <int W>
 __device__ __forceinline__ int lds_offw(int r, int c) { return r * W + ((c ^ swzw<W>(r)) << 3); }
-__device__ __forceinline__ int swz(int r) { return swzw<BK>(r); }
-__device__ __forceinline__ int lds_off(int r, int c) { return lds_offw<BK>(r, c); }
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Compile-time shape of one kernel instance: BM x BN output tile, four waves
-// in a 2 x 2 arrangement, each wave (BM/2) x (BN/2) = TI x TJ MFMA 32x32 tiles.
-template <int MODE, int BM, int BN, bool FP8>
+// Compile-time shape of one kernel instance: BM x BN output tile.
+template <int MODE, int BM, int BN, bool FP8, int BK, int S_>
 struct Cfg {
+  static_assert(BK == 64 || BK == 32, "K step of 32 or 64 bf16");
   static constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
   static constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
-  // waves: WM along M x WN along N, each a 64 x 64 block of 2 x 2 MFMA tiles
-  static constexpr int WM = BM / 64, WN = BN / 64, kThreads = 64 * WM * WN;
-  static constexpr int TI = 2, TJ = 2;
+  // four waves, 2 x 2, each a (BM/2) x (BN/2) block of TI x TJ MFMA 32x32 tiles
+  static constexpr int WM = 2, WN = 2, kThreads = 256;
+  static constexpr int TI = BM / 64, TJ = BN / 64;
   // output columns staged in LDS at once by the epilogue, and its row pitch;
   // the 16-byte pad puts rows m and m+4 (written by the two half-waves of one
   // store instruction) in different banks
   static constexpr int CW = MODE == GATE_UP_FWD ? BN / 2 : BN;
   static constexpr int CP = CW + 8;
-  // LDS stages of the operand tiles (the fp8 path uses the first two)
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 2
-#endif
-  static constexpr int S = MOE_GEMM_STAGES;
+  // LDS stages of the bf16 operand tiles (the fp8 path has two)
+  static constexpr int S = S_;
   // bf16: S stages of BK-wide tiles; fp8: two stages of 128-byte rows
   static constexpr int kMain = FP8 ? 2 * (BM + BN) * 64 : S * (BM + BN) * BK;
-  static constexpr int kEpi = KGROUP ? 0 : (MODE == GATE_UP_FWD ? 3 : MODE == DOWN_BWD_DATA ? 2 : 1) * BM * CP;
+  // epilogue staging: h, G and U side by side (or one after the other when the
+  // three do not fit the operand LDS); the SwiGLU backward stages the saved G
+  // and U tiles (per wave column when the whole tile does not fit)
+  static constexpr bool kEpiOnePass =
+      MODE == GATE_UP_FWD ? 3 * BM * CP <= kMain : (MODE == DOWN_BWD_DATA ? 2 * BM * CP <= kMain : true);
+  static constexpr int CPH = BN / WN + 8;  // pitch of one wave column's staging
+  static constexpr int kEpi =
+      KGROUP ? 0
+             : (MODE == GATE_UP_FWD ? (kEpiOnePass ? 3 : 1) * BM * CP
+                                    : (MODE == DOWN_BWD_DATA ? (kEpiOnePass ? 2 * BM * CP : 2 * BM * CPH) : BM * CP));
   static constexpr int kSmem = cmax(kMain, kEpi);
   // workgroups per CU that the LDS allows (160 KB per CU), at most three
   static constexpr int kMinBlocks =
@@ -167,9 +167,12 @@ struct Cfg {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <int MODE, int BM, int BN, bool FP8>
-__global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, BN, FP8>::kMinBlocks)) void k_gemm(GemmArgs g) {
-  using C = Cfg<MODE, BM, BN, FP8>;
+template <int MODE, int BM, int BN, bool FP8, int BK, int S_>
+__global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
+                             (Cfg<MODE, BM, BN, FP8, BK, S_>::kMinBlocks)) void k_gemm(GemmArgs g) {
+  using C = Cfg<MODE, BM, BN, FP8, BK, S_>;
+  auto swz = [](int r) { return swzw<BK>(r); };
+  auto lds_off = [](int r, int c) { return lds_offw<BK>(r, c); };
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
   constexpr int TI = C::TI, TJ = C::TJ;
   // Two LDS stages of the A and B tiles; after the K loop the same memory
@@ -707,16 +710,90 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
   auto tn = [&](int j, int t) { return brow(j) + t * 8 + lh * 4; };
   auto pack4 = [](float a, float b, float c, float d) { return make_uint2(pk_bf16(a, b), pk_bf16(c, d)); };
   constexpr int CP = C::CP, CW = C::CW;
-  // cooperative 16-byte row stores of a staged BM x CW bf16 tile
-  auto store_tile = [&](const bf16_t* t, bf16_t* dst, int64_t ldd, int64_t ncols) {
-    for (int v = tid; v < BM * (CW / 8); v += kThreads) {
-      const int row = v / (CW / 8), c8 = (v % (CW / 8)) * 8;
+  // cooperative 16-byte row stores of a staged BM x w bf16 tile of pitch p
+  auto store_tile_w = [&](const bf16_t* t, int w, int p, bf16_t* dst, int64_t ldd, int64_t ncols) {
+    for (int v = tid; v < BM * (w / 8); v += kThreads) {
+      const int row = v / (w / 8), c8 = (v % (w / 8)) * 8;
       if (row >= rows_valid || c8 >= ncols) continue;
       *reinterpret_cast<uint4*>(dst + (row0 + row) * ldd + c8) =
-          *reinterpret_cast<const uint4*>(t + row * CP + c8);
+          *reinterpret_cast<const uint4*>(t + row * p + c8);
     }
   };
-  if constexpr (MODE == GATE_UP_FWD) {
+  auto store_tile = [&](const bf16_t* t, bf16_t* dst, int64_t ldd, int64_t ncols) {
+    store_tile_w(t, CW, CP, dst, ldd, ncols);
+  };
+  if constexpr (MODE == GATE_UP_FWD && !C::kEpiOnePass) {
+    // h, then G, then U through one staging tile
+    bf16_t* ct = smem;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ / 2; ++j)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float gv = acc[i][j][4 * t + q], uv = acc[i][j + TJ / 2][4 * t + q];
+              v[q] = pass == 0 ? silu_f(gv) * uv : (pass == 1 ? gv : uv);
+            }
+            *reinterpret_cast<uint2*>(ct + tm(i) * CP + wn * (BN / 2 / WN) + j * 32 + t * 8 + lh * 4) =
+                pack4(v[0], v[1], v[2], v[3]);
+          }
+      __syncthreads();
+      if (pass == 0) store_tile(ct, g.C0 + n0, g.F, g.F - n0);
+      else store_tile(ct, g.C1 + (pass == 2 ? g.F : 0) + n0, 2 * g.F, g.F - n0);
+      __syncthreads();
+    }
+  } else if constexpr (MODE == DOWN_BWD_DATA && !C::kEpiOnePass) {
+    // SwiGLU backward one wave column (BN/2 output columns) at a time
+    constexpr int WC = BN / WN, CPH = C::CPH;
+    bf16_t* tg = smem;
+    bf16_t* tu = smem + BM * CPH;
+#pragma unroll 1
+    for (int pc = 0; pc < WN; ++pc) {
+      const int64_t c0 = n0 + pc * WC;
+      for (int v = tid; v < 2 * BM * (WC / 8); v += kThreads) {
+        const int t = v / (BM * (WC / 8)), w = v % (BM * (WC / 8));
+        const int row = w / (WC / 8), c8 = (w % (WC / 8)) * 8;
+        const int rr = row < rows_valid ? row : rows_valid - 1;
+        const int64_t col = c0 + c8 < g.N ? c0 + c8 : g.N - 8;
+        *reinterpret_cast<uint4*>(smem + t * BM * CPH + row * CPH + c8) =
+            *reinterpret_cast<const uint4*>(g.aux + (row0 + rr) * 2 * g.F + (t ? g.F : 0) + col);
+      }
+      __syncthreads();
+      if (wn == pc) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int o = tm(i) * CPH + tn(j, t) - pc * WC;
+              const uint2 gp = *reinterpret_cast<const uint2*>(tg + o);
+              const uint2 up = *reinterpret_cast<const uint2*>(tu + o);
+              const float gv[4] = {bf2f(gp.x & 0xffffu), bf2f(gp.x >> 16), bf2f(gp.y & 0xffffu), bf2f(gp.y >> 16)};
+              const float uv[4] = {bf2f(up.x & 0xffffu), bf2f(up.x >> 16), bf2f(up.y & 0xffffu), bf2f(up.y >> 16)};
+              float dg[4], du[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float c = acc[i][j][4 * t + q];
+                const float sg = 1.0f / (1.0f + __expf(-gv[q]));
+                dg[q] = c * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                du[q] = c * (gv[q] * sg);
+              }
+              *reinterpret_cast<uint2*>(tg + o) = pack4(dg[0], dg[1], dg[2], dg[3]);
+              *reinterpret_cast<uint2*>(tu + o) = pack4(du[0], du[1], du[2], du[3]);
+            }
+      }
+      __syncthreads();
+      store_tile_w(tg, WC, CPH, g.C0 + c0, 2 * g.F, g.N - c0);
+      store_tile_w(tu, WC, CPH, g.C0 + g.F + c0, 2 * g.F, g.N - c0);
+      __syncthreads();
+    }
+  } else if constexpr (MODE == GATE_UP_FWD) {
     // h, G and U (BM rows x BN/2 columns each) staged side by side
     bf16_t* th = smem;
     bf16_t* tg = smem + BM * CP;
@@ -819,7 +896,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8>::kThreads), (Cfg<MODE, BM, 
   }
 }
 
-template <int MODE, int BM, int BN, bool FP8>
+template <int MODE, int BM, int BN, bool FP8, int BK = 64, int S = 2>
 moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
   const int64_t bn_cols = MODE == GATE_UP_FWD ? BN / 2 : BN;
@@ -847,8 +924,8 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;  // weight gradients: already 8 * E * block
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8>), dim3((unsigned)grid), dim3(Cfg<MODE, BM, BN, FP8>::kThreads), 0,
-                     strm, g);
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8, BK, S>), dim3((unsigned)grid),
+                     dim3(Cfg<MODE, BM, BN, FP8, BK, S>::kThreads), 0, strm, g);
   return launch_status();
 }
 
@@ -858,11 +935,22 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
 // so every mode runs 128 x 128.
 template <int MODE, bool FP8 = false>
 moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
-#ifndef MOE_GEMM_BN
-#define MOE_GEMM_BN 128
-#endif
-  if constexpr (FP8) return launch_cfg<MODE, 128, 128, FP8>(g, s, strm);
-  else return launch_cfg<MODE, 128, MOE_GEMM_BN, FP8>(g, s, strm);
+  // Tile shapes per GEMM kind, chosen by measurement on MI355X (MoE layers at
+  // H = 1536 / F = 480 and H = 7168 / F = 2048): 128 x 256 tiles (wave tiles
+  // 64 x 128, K step 32, three LDS stages, two workgroups per CU) move a
+  // quarter fewer operand bytes per FLOP and win for the gate/up data gradient
+  // and both weight gradients, and for the down data gradient once its N (= F)
+  // is wide; the forward GEMMs stay on 128 x 128 tiles (K step 64, two stages).
+  if constexpr (FP8) {
+    return launch_cfg<MODE, 128, 128, true>(g, s, strm);
+  } else if constexpr (MODE == GATE_UP_BWD_DATA || MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W) {
+    return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
+  } else if constexpr (MODE == DOWN_BWD_DATA) {
+    if (g.N >= 1024) return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
+    return launch_cfg<MODE, 128, 128, false>(g, s, strm);
+  } else {
+    return launch_cfg<MODE, 128, 128, false>(g, s, strm);
+  }
 }
 
 GemmArgs base_args(const moe_shape* s, const int32_t* prefix) {
