@@ -16,15 +16,16 @@
 // the expanded buffers); the last two are grouped over K (the contraction runs
 // over the expert's rows, which may be none).
 //
-// Tiling: a BM x BN output tile per 256-thread workgroup (128 x 128 is
-// launched), four waves in a 2 x 2 arrangement, each wave 64 x 64 of
-// v_mfma_f32_32x32x16_bf16 tiles (fp8: v_mfma_scale_f32_32x32x64_f8f6f4 with
-// unit block scales, the fp32 scales applied per 128-wide K block), two
-// workgroups (eight waves) per CU.  K steps of 64 (fp8: 128 codes) go from
-// memory straight into LDS (buffer loads with an LDS destination, no register
-// staging), two LDS stages: the loads of step t+1 are in flight while the
-// MFMAs of step t issue.  Operands keep their memory layout in LDS:
-// K-contiguous tiles as rows of 128 bytes with an XOR-swizzled chunk order
+// Tiling: a BM x BN output tile per 256-thread workgroup (128 x 128 or
+// 128 x 256 per GEMM kind, see launch()), four waves in a 2 x 2 arrangement,
+// each wave (BM/2) x (BN/2) of v_mfma_f32_32x32x16_bf16 tiles (fp8:
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales, the fp32 scales
+// applied per 128-wide K block), two or three workgroups per CU.  K steps of
+// 64 or 32 (fp8: 128 codes) go from memory straight into LDS (buffer loads
+// with an LDS destination, no register staging), two or three LDS stages: the
+// loads of the next steps are in flight while the MFMAs of step t issue.
+// Operands keep their memory layout in LDS:
+// K-contiguous tiles as rows of 2 BK bytes with an XOR-swizzled chunk order
 // (one conflict-free 16-byte read per MFMA operand), K-strided tiles as
 // k-rows read into MFMA operands with the transposing LDS read.  Row-grouped
 // modes accumulate transposed fragments, so each lane holds runs of four
@@ -929,10 +930,6 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   return launch_status();
 }
 
-// Tile choice.  Measured on MI355X at the page-1 benchmark shape, 128 x 128
-// tiles with two waves per SIMD beat 256 x 256 tiles with one wave per SIMD
-// (whose exposed load and barrier latency outweighs their halved LDS traffic),
-// so every mode runs 128 x 128.
 template <int MODE, bool FP8 = false>
 moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // Tile shapes per GEMM kind, chosen by measurement on MI355X (MoE layers at
@@ -940,14 +937,18 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // 64 x 128, K step 32, three LDS stages, two workgroups per CU) move a
   // quarter fewer operand bytes per FLOP and win for the gate/up data gradient
   // and both weight gradients, and for the down data gradient once its N (= F)
-  // is wide; the forward GEMMs stay on 128 x 128 tiles (K step 64, two stages).
+  // is wide.  A narrow down data gradient has few column tiles; 128 x 128
+  // tiles with K step 32 and two stages (36 KB of LDS, three workgroups per
+  // CU) give it more tiles in flight.  The forward GEMMs stay on 128 x 128
+  // tiles with K step 64 and two stages (two workgroups per CU): with three,
+  // the larger MoE layer ran a third slower.
   if constexpr (FP8) {
     return launch_cfg<MODE, 128, 128, true>(g, s, strm);
   } else if constexpr (MODE == GATE_UP_BWD_DATA || MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W) {
     return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
   } else if constexpr (MODE == DOWN_BWD_DATA) {
     if (g.N >= 1024) return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
-    return launch_cfg<MODE, 128, 128, false>(g, s, strm);
+    return launch_cfg<MODE, 128, 128, false, 32, 2>(g, s, strm);
   } else {
     return launch_cfg<MODE, 128, 128, false>(g, s, strm);
   }
