@@ -238,8 +238,15 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
     const int64_t w = k % per;
     const int blk = (int)((xcd + e) & 7);
     const int kq = 8 / g.kp;
-    const int64_t mt = (blk / kq) * g.mch + w / g.nch;
-    const int64_t nt = (blk % kq) * g.nch + w % g.nch;
+    // within the block, groups of eight row tiles, column tile by column tile
+    // (the same grouped order as the wide row-grouped GEMMs)
+    constexpr int64_t kGroup = 8;
+    const int64_t gsz = kGroup * g.nch;
+    const int64_t grp = w / gsz, rem = w - grp * gsz;
+    const int64_t first = grp * kGroup;
+    const int64_t gmm = (g.mch - first) < kGroup ? (g.mch - first) : kGroup;
+    const int64_t mt = (blk / kq) * g.mch + first + rem % gmm;
+    const int64_t nt = (blk % kq) * g.nch + rem / gmm;
     if (mt >= g.m_tiles || nt >= g.n_tiles) return;
     row0 = mt * BM;  // first output row (weight row)
     n0 = nt * BN;
