@@ -114,19 +114,17 @@ __device__ __forceinline__ int find_expert(const int32_t* __restrict__ prefix, i
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// LDS operand tile: R rows x 64 k of bf16, row pitch 128 bytes, in eight
-// 16-byte chunks of 8 consecutive k.  Chunk c of row r sits at chunk position
-// c ^ swz(r), so the eight rows read by eight consecutive lanes of an MFMA
-// operand fetch, and the eight chunks of one row written by eight consecutive
-// lanes, fall in distinct banks.
-// Rows of W bf16 (2W bytes): W = 64 is eight chunks, swizzled by
-// (r ^ r/8) % 8; W = 32 is four chunks, swizzled by (r/2) % 4 (two neighbouring
-// 64-byte rows share one 128-byte bank window, so eight consecutive rows still
-// reach eight distinct chunk slots).
+// LDS operand tile: R rows x W k of bf16, row pitch 2W bytes, in 16-byte
+// chunks of 8 consecutive k.  Chunk c of row r sits at chunk position
+// c ^ swz(r).  The LDS serves 256 bytes (64 banks of 4 bytes) per cycle, so
+// the 16 lanes of one 16-byte read phase (16 consecutive rows, one chunk
+// each) must cover the 16 distinct 16-byte slots of a 256-byte window:
+// W = 64 (128-byte rows, two rows per window) swizzles by (r ^ r/8) % 8;
+// W = 32 (64-byte rows, four rows per window) by (r/4) % 4.
 template <int W>
 __device__ __forceinline__ int swzw(int r) {
   if constexpr (W == 64) return (r ^ (r >> 3)) & 7;
-  else return (r >> 1) & 3;
+  else return (r >> 2) & 3;
 }
 template <int W>
 __device__ __forceinline__ int lds_offw(int r, int c) { return r * W + ((c ^ swzw<W>(r)) << 3); }
@@ -137,6 +135,7 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 template <int MODE, int BM, int BN, bool FP8, int BK, int S_>
 struct Cfg {
   static_assert(BK == 64 || BK == 32, "K step of 32 or 64 bf16");
+  static_assert(BM >= 128 && BN >= 128, "K-strided tiles swizzle over 16 chunks of a k-row");
   static constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
   static constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
   // four waves, 2 x 2, each a (BM/2) x (BN/2) block of TI x TJ MFMA 32x32 tiles
@@ -469,11 +468,13 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   //    taking row (512/BK) q + l/(BK/8), position l%(BK/8), i.e. memory chunk
   //    position ^ swz(row).
   //  * K-strided operand of R columns: BK k-rows x 2R bytes, 16-byte chunk c
-  //    of k-row k at position c ^ (2 (k%4)); one instruction fills 512/R
+  //    of k-row k at position c ^ (4 (k%4)); one instruction fills 512/R
   //    k-rows.  MFMA fragments come out of it with transposing LDS reads
   //    (ds_read_b64_tr_b16: within each 16-lane group, lane i receives
   //    element i of the group's four 8-byte rows read in lane order, for
-  //    each of the four rows), two reads per 8-k fragment.
+  //    each of the four rows), two reads per 8-k fragment.  The 32 lanes of
+  //    one read phase take four chunks of four k-rows; the swizzle puts them
+  //    in the 16 distinct 16-byte slots of a 256-byte bank window.
   // Rows past the operand are clamped to its last row (their products only
   // reach output rows or columns that are not stored).  Past the end of the
   // contraction the loads return zero: K-strided operands through the range
@@ -486,7 +487,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   constexpr int CPRK = BK / 8, RPIK = 64 / CPRK;  // K-contiguous: chunks per row, rows per instruction
   constexpr uint32_t kOOB = 0x80000000u;
   constexpr int kRange = 0x7ffffff0;
-  auto sw2 = [](int k) { return 2 * (k & 3); };
+  auto sw4 = [](int k) { return 4 * (k & 3); };
   // buffer resource (base, byte range) in scalar registers
   auto rsrc = [](const void* p, int64_t bytes) -> i32x4 {
     const int64_t n = bytes < 0 ? 0 : (bytes < kRange ? bytes : kRange);
@@ -519,7 +520,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
       kcA[j] = c * 8;
     } else {
       constexpr int CPR = BM / 8, RPI = 64 / CPR;
-      const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw2(k);
+      const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw4(k);
       const int64_t col = row0 + c * 8 < g.M ? row0 + c * 8 : g.M - 8;
       voA[j] = (uint32_t)((k * g.lda + col) * 2);
       kcA[j] = 0;
@@ -542,7 +543,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
       kcB[j] = c * 8;
     } else {
       constexpr int CPR = BN / 8, RPI = 64 / CPR;
-      const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw2(k);
+      const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw4(k);
       const int64_t col = n0 + c * 8 < g.N ? n0 + c * 8 : g.N - 8;
       voB[j] = (uint32_t)((k * g.ldb + col) * 2);
       kcB[j] = 0;
@@ -621,7 +622,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   auto tr_off = [&](int mbase, int R) {
     const int m = mbase + (g16 & 1) * 16 + 4 * (i16 & 3);
     const int k = (g16 >> 1) * 8 + (i16 >> 2);
-    return k * R + (((m >> 3) ^ sw2(k)) << 3) + ((m >> 2) & 1) * 4;
+    return k * R + (((m >> 3) ^ sw4(k)) << 3) + ((m >> 2) & 1) * 4;
   };
   int trA[TI], trB[TJ];
 #pragma unroll
