@@ -78,6 +78,7 @@ struct GemmArgs {
   int64_t mch, nch;  // weight gradients: tiles per block along M and N
   int kp;            // weight gradients: row blocks of an expert's tile grid
   int64_t gm;        // row-grouped GEMMs: row tiles per rasterisation group
+  int krot;          // K steps of stagger between tiles sharing an operand tile
   bf16_t* C0;
   bf16_t* C1;
   const bf16_t* aux;
@@ -205,6 +206,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   int e;
   int64_t row0, n0, kbeg, kend;
   int rows_valid;
+  int kseed = 0;  // (row tile + column tile) % 8: staggers the K start, see krot
   if constexpr (!KGROUP) {
     const int64_t logical = (bid & 7) * (nb >> 3) + (bid >> 3);
     if (logical >= g.tiles) return;
@@ -219,6 +221,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
     const int64_t gm = (g.m_tiles - first) < g.gm ? (g.m_tiles - first) : g.gm;
     const int64_t mt = first + rem % gm;
     const int64_t nt = rem / gm;
+    kseed = (int)((mt + nt) & 7);
     // the expert index is the same in every lane; readfirstlane keeps it (and
     // every address derived from it) in scalar registers
     e = __builtin_amdgcn_readfirstlane(find_expert<BM>(g.prefix, g.E, mt));
@@ -685,6 +688,12 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   // frees the stage of step t-1 for the next loads.
   constexpr int L = LA + LB;
   const int64_t nk = (klen + BK - 1) / BK;
+  // K steps run from ks to the end and wrap around.  With krot > 0, the
+  // eight tiles that share an A row tile (or a B column tile) start krot
+  // steps apart, so one of them fetches each K step's operands from HBM ahead
+  // of the others instead of all of them waiting on the same misses.
+  const int64_t ks = nk ? ((int64_t)kseed * g.krot) % nk : 0;
+  auto rot = [&](int64_t t) -> int64_t { const int64_t u = t + ks; return u < nk ? u : u - nk; };
   auto kstep = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
     if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L * (S - 2)));
@@ -695,15 +704,15 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + S - 1 < nk) issue(std::integral_constant<int, (st + S - 1) % S>(), kt + S - 1);
+    if (kt + S - 1 < nk) issue(std::integral_constant<int, (st + S - 1) % S>(), rot(kt + S - 1));
     compute(ST);
   };
 #pragma unroll
   for (int t = 0; t < S - 1; ++t)
     if (t < nk) {
-      if (t == 0) issue(std::integral_constant<int, 0>(), 0);
-      if (t == 1) issue(std::integral_constant<int, 1 % S>(), 1);
-      if (t == 2) issue(std::integral_constant<int, 2 % S>(), 2);
+      if (t == 0) issue(std::integral_constant<int, 0>(), rot(0));
+      if (t == 1) issue(std::integral_constant<int, 1 % S>(), rot(1));
+      if (t == 2) issue(std::integral_constant<int, 2 % S>(), rot(2));
     }
   for (int64_t kt = 0; kt < nk; kt += S) {
     kstep(std::integral_constant<int, 0>(), kt);
@@ -943,6 +952,10 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
     // grouped rasterisation pays once a row tile spans many column tiles
     // (measured: 28 or more column tiles gain 10-30%, 12 or fewer lose a few %)
     g.gm = g.n_tiles >= 16 ? 8 : 1;
+    // staggered K starts: measured faster for the forward GEMMs in row-tile
+    // order (H = 1536, F = 480: 3-7%), slower for the data gradients and in
+    // grouped order, where it stays off
+    g.krot = (!FP8 && (MODE == GATE_UP_FWD || MODE == DOWN_FWD) && g.gm == 1) ? 1 : 0;
   }
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;  // weight gradients: already 8 * E * block
