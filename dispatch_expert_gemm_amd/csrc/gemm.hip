@@ -27,9 +27,9 @@
 // Operands keep their memory layout in LDS:
 // K-contiguous tiles as rows of 2 BK bytes with an XOR-swizzled chunk order
 // (one conflict-free 16-byte read per MFMA operand), K-strided tiles as
-// k-rows read into MFMA operands with the transposing LDS read.  Row-grouped
-// modes accumulate transposed fragments, so each lane holds runs of four
-// output columns for the epilogue.
+// k-rows read into MFMA operands with the transposing LDS read.  Every mode
+// accumulates transposed fragments, so each lane holds runs of four output
+// columns for the epilogue.
 //
 // Expert counts stay on the device: the grid covers floor(capacity/BM) + E row
 // tiles per column tile, and each workgroup finds its expert from the prefix
@@ -675,10 +675,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = KGROUP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
-                                                                      acc[i][j], 0, 0, 0)
-                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i],
-                                                                      acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -725,16 +722,14 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   }
 
   // ---- epilogue.
-  // Row-grouped GEMMs accumulate transposed fragments (the MFMA takes the B
-  // fragment as its first operand), so acc[i][j][r] holds C(m, n) with
+  // The GEMMs accumulate transposed fragments (the MFMA takes the B fragment
+  // as its first operand), so acc[i][j][r] holds C(m, n) with
   //   m = wm*(BM/WM) + i*32 + lane%32,  n = brow(j) + (r/4)*8 + (lane/32)*4 + r%4:
-  // every lane owns runs of four consecutive columns and writes them to the
-  // LDS staging tile as one 8-byte store.  Weight gradients keep the plain
-  // fragments: m = wm*(BM/WM) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
-  // n = brow(j) + lane%32.  The K loop ended with a barrier, so the LDS
-  // stages are free.
+  // every lane owns runs of four consecutive columns: the row-grouped GEMMs
+  // write them to an LDS staging tile as one 8-byte store, the weight
+  // gradients straight to memory as one 16-byte fp32 store.  The K loop
+  // ended with a barrier, so the LDS stages are free.
   const int ln = lane & 31, lh = lane >> 5;
-  auto mrow = [&](int i, int r) { return wm * (BM / WM) + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3); };
   auto tm = [&](int i) { return wm * (BM / WM) + i * 32 + ln; };
   auto tn = [&](int j, int t) { return brow(j) + t * 8 + lh * 4; };
   auto pack4 = [](float a, float b, float c, float d) { return make_uint2(pk_bf16(a, b), pk_bf16(c, d)); };
@@ -901,27 +896,29 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
     store_tile(tg, g.C0 + n0, 2 * g.F, g.N - n0);
     store_tile(tu, g.C0 + g.F + n0, 2 * g.F, g.N - n0);
   } else {
-    // weight gradients, fp32: each half-wave store is a full 128-byte row run
+    // weight gradients, fp32: 16-byte stores of four consecutive columns
+    // (N is a multiple of 8, so a run is either wholly inside or outside)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int64_t n = n0 + brow(j) + ln;
-      if (n >= g.N) continue;
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+      for (int t = 0; t < 4; ++t) {
+        const int64_t n = n0 + tn(j, t);
+        if (n >= g.N) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mrow(i, r);
+        for (int i = 0; i < TI; ++i) {
+          const int m = tm(i);
           if (m >= rows_valid) continue;
-          const float c = acc[i][j][r];
+          const float4 v =
+              make_float4(acc[i][j][4 * t], acc[i][j][4 * t + 1], acc[i][j][4 * t + 2], acc[i][j][4 * t + 3]);
           if constexpr (MODE == DOWN_BWD_W) {
-            g.W0[(int64_t)e * g.M * g.N + (row0 + m) * g.N + n] = c;
+            *reinterpret_cast<float4*>(g.W0 + (int64_t)e * g.M * g.N + (row0 + m) * g.N + n) = v;
           } else {  // GATE_UP_BWD_W: rows [0, F) -> dWg, [F, 2F) -> dWu
             const int64_t jrow = row0 + m;
-            if (jrow < g.F) g.W0[(int64_t)e * g.F * g.N + jrow * g.N + n] = c;
-            else g.W1[(int64_t)e * g.F * g.N + (jrow - g.F) * g.N + n] = c;
+            if (jrow < g.F) *reinterpret_cast<float4*>(g.W0 + (int64_t)e * g.F * g.N + jrow * g.N + n) = v;
+            else *reinterpret_cast<float4*>(g.W1 + (int64_t)e * g.F * g.N + (jrow - g.F) * g.N + n) = v;
           }
         }
-    }
+      }
   }
 }
 
