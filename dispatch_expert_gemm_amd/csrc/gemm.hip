@@ -746,6 +746,17 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   auto store_tile = [&](const bf16_t* t, bf16_t* dst, int64_t ldd, int64_t ncols) {
     store_tile_w(t, CW, CP, dst, ldd, ncols);
   };
+  // the same with non-temporal stores, for outputs read back only much later
+  // (the saved G and U, read by the backward pass)
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  auto store_tile_nt = [&](const bf16_t* t, bf16_t* dst, int64_t ldd, int64_t ncols) {
+    for (int v = tid; v < BM * (CW / 8); v += kThreads) {
+      const int row = v / (CW / 8), c8 = (v % (CW / 8)) * 8;
+      if (row >= rows_valid || c8 >= ncols) continue;
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(t + row * CP + c8),
+                                  reinterpret_cast<u32x4*>(dst + (row0 + row) * ldd + c8));
+    }
+  };
   if constexpr (MODE == GATE_UP_FWD && !C::kEpiOnePass) {
     // h, then G, then U through one staging tile
     bf16_t* ct = smem;
@@ -768,7 +779,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
           }
       __syncthreads();
       if (pass == 0) store_tile(ct, g.C0 + n0, g.F, g.F - n0);
-      else store_tile(ct, g.C1 + (pass == 2 ? g.F : 0) + n0, 2 * g.F, g.F - n0);
+      else store_tile_nt(ct, g.C1 + (pass == 2 ? g.F : 0) + n0, 2 * g.F, g.F - n0);
       __syncthreads();
     }
   } else if constexpr (MODE == DOWN_BWD_DATA && !C::kEpiOnePass) {
@@ -842,8 +853,8 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
         }
     __syncthreads();
     store_tile(th, g.C0 + n0, g.F, g.F - n0);
-    store_tile(tg, g.C1 + n0, 2 * g.F, g.F - n0);
-    store_tile(tu, g.C1 + g.F + n0, 2 * g.F, g.F - n0);
+    store_tile_nt(tg, g.C1 + n0, 2 * g.F, g.F - n0);
+    store_tile_nt(tu, g.C1 + g.F + n0, 2 * g.F, g.F - n0);
   } else if constexpr (MODE == DOWN_FWD || MODE == GATE_UP_BWD_DATA) {
     bf16_t* ct = smem;
 #pragma unroll
