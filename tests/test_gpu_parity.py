@@ -90,6 +90,15 @@ FFN_CASES = {
     # H-wide outputs and weight-gradient rows
     "ragged_h": dict(T=300, H=200, F=96, E=5, K=2),
     "ragged_h_1k": dict(T=1000, H=1096, F=224, E=9, K=3),
+    # wide outputs: the gate/up forward spans 16 column tiles (grouped tile
+    # order, 13 row-tile slots = one full group of 8 and a partial one); the
+    # down data gradient takes the 128 x 256 tiles (N = F = 1024)
+    "wide_ffn": dict(T=700, H=256, F=1024, E=3, K=2),
+    # wide weight gradients: gate/up weight-gradient blocks of 12 row tiles
+    # (a full and a partial group of 8), down weight-gradient blocks of 8 x 3
+    # tiles; grouped order for the gate/up forward, down forward and gate/up
+    # data gradient (24, 32 and 16 column tiles)
+    "wide_wgrad": dict(T=600, H=4096, F=1536, E=2, K=1),
 }
 
 
