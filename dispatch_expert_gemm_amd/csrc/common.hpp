@@ -121,6 +121,9 @@ inline moe_status check_ffn_shape(const moe_shape* s) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->F <= 0 || (s->F % 32) != 0 || s->F > (int64_t)1 << 20) return MOE_ERR_BAD_SHAPE;
+  // the GEMMs address one expert's weight matrix through a buffer resource
+  // with 32-bit offsets and a byte range below 2^31
+  if (s->F * s->H * 2 >= (int64_t)0x7ffffff0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -134,6 +134,9 @@ moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_i
  *  out  h_act          (capacity, F) bf16: h
  *  out  y              (capacity, H) bf16
  * Equivalent to moe_ffn_gate_up_fwd followed by moe_ffn_down_fwd.
+ * Every FFN entry (forward and backward) needs one expert's weight matrix
+ * below 2 GiB (F * H * 2 bytes < 2^31 - 16; the kernels address it with
+ * 32-bit offsets), else MOE_ERR_UNSUPPORTED.
  */
 moe_status moe_grouped_ffn(const moe_shape* s, const void* expand_x, const void* w_gate,
                            const void* w_up, const void* w_down, const int32_t* ep_recv_counts,

@@ -122,6 +122,13 @@ def test_entry_points_reject_bad_arguments_before_launch(L):
         sf = S(F=F)
         assert L.moe_grouped_ffn(ctypes.byref(sf), P(), P(), P(), P(), P(), P(), P(), P(), Nn) == BAD_SHAPE
         assert L.moe_grouped_ffn_bwd(ctypes.byref(sf), *([P()] * 13), Nn) == BAD_SHAPE
+    # one expert's weight matrix must stay below 2 GiB (32-bit offsets)
+    big = ctypes.byref(S(H=32768, F=32768))
+    assert L.moe_grouped_ffn(big, P(), P(), P(), P(), P(), P(), P(), P(), Nn) == UNSUPPORTED
+    assert L.moe_grouped_ffn_bwd(big, *([P()] * 13), Nn) == UNSUPPORTED
+    assert L.moe_ffn_gate_up_bwd_weight(big, P(), P(), P(), P(), P(), Nn) == UNSUPPORTED
+    ok = ctypes.byref(S(H=32768, F=32736))   # 2^31 - 2^21 bytes per matrix: accepted
+    assert L.moe_ffn_gate_up_fwd(ok, Nn, P(), P(), P(), P(), P(), Nn) == NULL_ARG
     assert L.moe_grouped_ffn(sp, P(), Nn, P(), P(), P(), P(), P(), P(), Nn) == NULL_ARG
     assert L.moe_ffn_down_bwd_weight(sp, P(), P(), P(), Nn, Nn) == NULL_ARG
     assert L.moe_ffn_gate_up_bwd_weight(sp, P(), P(), P(), P(), Nn, Nn) == NULL_ARG
