@@ -141,6 +141,9 @@ inline moe_status check_fp8_shape(const moe_shape* s) {
   // the fp8 GEMMs keep one B block scale per 128-wide K block in LDS: K = H or
   // 2F at most 32768
   if (s->H > 32768 || 2 * s->F > 32768) return MOE_ERR_UNSUPPORTED;
+  // the activation scales of all rows are read with 32-bit byte offsets
+  const int64_t kmax = s->H > 2 * s->F ? s->H : 2 * s->F;
+  if (s->capacity * (kmax / 128) * 4 >= (int64_t)0x7ffffff0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

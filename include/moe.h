@@ -264,7 +264,8 @@ moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,
  * the weight gradients keep the bf16 entries above.  The pages name FP8 only as
  * a precision of the MoE layer performance tests (Megatron-LM page, Added Test
  * Cases); the block recipe is this library's.  H and F must be multiples of 128
- * (else MOE_ERR_BAD_SHAPE), H and 2F at most 32768 (else MOE_ERR_UNSUPPORTED).
+ * (else MOE_ERR_BAD_SHAPE), H and 2F at most 32768 and the activation scales
+ * below 2 GiB (capacity * max(H, 2F)/128 * 4 bytes; else MOE_ERR_UNSUPPORTED).
  */
 
 /* Rows of a bf16 (R, C) matrix to e4m3 with one scale per (row, 128 columns).

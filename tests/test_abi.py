@@ -127,6 +127,9 @@ def test_entry_points_reject_bad_arguments_before_launch(L):
     assert L.moe_grouped_ffn(big, P(), P(), P(), P(), P(), P(), P(), P(), Nn) == UNSUPPORTED
     assert L.moe_grouped_ffn_bwd(big, *([P()] * 13), Nn) == UNSUPPORTED
     assert L.moe_ffn_gate_up_bwd_weight(big, P(), P(), P(), P(), P(), Nn) == UNSUPPORTED
+    # fp8: the activation scales of all rows must stay below 2 GiB
+    s8 = S(T=1 << 21, K=8, num_experts=8, H=32768, F=128)   # capacity 2^24 rows x 256 blocks x 4 B
+    assert L.moe_ffn_gate_up_fwd_fp8(ctypes.byref(s8), *([P()] * 9), Nn) == UNSUPPORTED
     ok = ctypes.byref(S(H=32768, F=32736))   # 2^31 - 2^21 bytes per matrix: accepted
     assert L.moe_ffn_gate_up_fwd(ok, Nn, P(), P(), P(), P(), P(), Nn) == NULL_ARG
     assert L.moe_grouped_ffn(sp, P(), Nn, P(), P(), P(), P(), P(), P(), Nn) == NULL_ARG
