@@ -16,11 +16,12 @@
 // the expanded buffers); the last two are grouped over K (the contraction runs
 // over the expert's rows, which may be none).
 //
-// Tiling: a BM x BN output tile per 256-thread workgroup (128 x 128 or
-// 128 x 256 per GEMM kind, see launch()), four waves in a 2 x 2 arrangement,
-// each wave (BM/2) x (BN/2) of v_mfma_f32_32x32x16_bf16 tiles (fp8:
-// v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales, the fp32 scales
-// applied per 128-wide K block), two or three workgroups per CU.  K steps of
+// Tiling: a BM x BN output tile per workgroup of WM x WN waves (128 x 128 or
+// 128 x 256 with 2 x 2 waves, 256 x 256 with 2 x 4 waves, per GEMM kind and
+// shape, see launch()), each wave (BM/WM) x (BN/WN) of
+// v_mfma_f32_32x32x16_bf16 tiles (fp8: v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit block scales, the fp32 scales applied per 128-wide K block), one to
+// three workgroups per CU.  K steps of
 // 64 or 32 (fp8: 128 codes) go from memory straight into LDS (buffer loads
 // with an LDS destination, no register staging), two or three LDS stages: the
 // loads of the next steps are in flight while the MFMAs of step t issue.
@@ -57,6 +58,8 @@ enum Mode : int {
 // 64-element bf16 step.
 // fp8 GEMMs: at most this many 128-wide K blocks (K <= 32768)
 constexpr int kMaxKBlocks8 = 256;
+// compute units of an MI355X (gfx950): 8 XCDs of 32
+constexpr int kCUs = 256;
 // gfx9 s_waitcnt immediate that waits for at most n outstanding vector memory
 // operations (vmcnt in bits 3:0 and 15:14) and leaves the other counters free
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -133,15 +136,15 @@ __device__ __forceinline__ int lds_offw(int r, int c) { return r * W + ((c ^ swz
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // Compile-time shape of one kernel instance: BM x BN output tile.
-template <int MODE, int BM, int BN, bool FP8, int BK, int S_>
+template <int MODE, int BM, int BN, bool FP8, int BK, int S_, int WM_ = 2, int WN_ = 2>
 struct Cfg {
   static_assert(BK == 64 || BK == 32, "K step of 32 or 64 bf16");
   static_assert(BM >= 128 && BN >= 128, "K-strided tiles swizzle over 16 chunks of a k-row");
   static constexpr bool KGROUP = MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W;
   static constexpr bool B_KC = MODE == GATE_UP_FWD || MODE == DOWN_FWD;
-  // four waves, 2 x 2, each a (BM/2) x (BN/2) block of TI x TJ MFMA 32x32 tiles
-  static constexpr int WM = 2, WN = 2, kThreads = 256;
-  static constexpr int TI = BM / 64, TJ = BN / 64;
+  // WM x WN waves, each a (BM/WM) x (BN/WN) block of TI x TJ MFMA 32x32 tiles
+  static constexpr int WM = WM_, WN = WN_, kThreads = 64 * WM * WN;
+  static constexpr int TI = BM / WM / 32, TJ = BN / WN / 32;
   // output columns staged in LDS at once by the epilogue, and its row pitch;
   // the 16-byte pad puts rows m and m+4 (written by the two half-waves of one
   // store instruction) in different banks
@@ -170,10 +173,10 @@ struct Cfg {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <int MODE, int BM, int BN, bool FP8, int BK, int S_>
-__global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
-                             (Cfg<MODE, BM, BN, FP8, BK, S_>::kMinBlocks)) void k_gemm(GemmArgs g) {
-  using C = Cfg<MODE, BM, BN, FP8, BK, S_>;
+template <int MODE, int BM, int BN, bool FP8, int BK, int S_, int WM_, int WN_>
+__global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads),
+                             (Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kMinBlocks)) void k_gemm(GemmArgs g) {
+  using C = Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>;
   auto swz = [](int r) { return swzw<BK>(r); };
   auto lds_off = [](int r, int c) { return lds_offw<BK>(r, c); };
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
@@ -933,7 +936,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_>::kThreads),
   }
 }
 
-template <int MODE, int BM, int BN, bool FP8, int BK = 64, int S = 2>
+template <int MODE, int BM, int BN, bool FP8, int BK = 64, int S = 2, int WM = 2, int WN = 2>
 moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
   const int64_t bn_cols = MODE == GATE_UP_FWD ? BN / 2 : BN;
@@ -968,8 +971,8 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;  // weight gradients: already 8 * E * block
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8, BK, S>), dim3((unsigned)grid),
-                     dim3(Cfg<MODE, BM, BN, FP8, BK, S>::kThreads), 0, strm, g);
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8, BK, S, WM, WN>), dim3((unsigned)grid),
+                     dim3(Cfg<MODE, BM, BN, FP8, BK, S, WM, WN>::kThreads), 0, strm, g);
   return launch_status();
 }
 
@@ -982,9 +985,12 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // and both weight gradients, and for the down data gradient once its N (= F)
   // is wide.  A narrow down data gradient has few column tiles; 128 x 128
   // tiles with K step 32 and two stages (36 KB of LDS, three workgroups per
-  // CU) give it more tiles in flight.  The forward GEMMs stay on 128 x 128
-  // tiles with K step 64 and two stages (two workgroups per CU): with three,
-  // the larger MoE layer ran a third slower.
+  // CU) give it more tiles in flight.  The forward GEMMs run 128 x 128 tiles
+  // with K step 64 and two stages (two workgroups per CU; three ran the larger
+  // MoE layer a third slower) or 256 x 256 tiles (below).  Eight-wave
+  // 256 x 256 tiles lost for the backward GEMMs: the SwiGLU backward epilogue
+  // runs four wave-column passes, and the weight gradients get too few tiles
+  // per expert block.
   if constexpr (FP8) {
     return launch_cfg<MODE, 128, 128, true>(g, s, strm);
   } else if constexpr (MODE == GATE_UP_BWD_DATA || MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W) {
@@ -993,6 +999,17 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
     if (g.N >= 1024) return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
     return launch_cfg<MODE, 128, 128, false, 32, 2>(g, s, strm);
   } else {
+    // forward: 256 x 256 tiles of eight waves (wave tiles 128 x 64, one
+    // workgroup of 128 KB LDS per CU) do a fifth more work per memory latency
+    // than two 128 x 128 workgroups, but come in quarter as many tiles; they
+    // are taken when their rounds of tiles over the CUs, weighted by the 1.7x
+    // time one round of them takes, beat the rounds of 128 x 128 tiles
+    const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
+    const int64_t cols128 = MODE == GATE_UP_FWD ? 64 : 128, cols256 = 2 * cols128;
+    const int64_t t128 = (s->capacity / 128 + s->num_experts) * ((ncols + cols128 - 1) / cols128);
+    const int64_t t256 = (s->capacity / 256 + s->num_experts) * ((ncols + cols256 - 1) / cols256);
+    const int64_t r128 = (t128 + 2 * kCUs - 1) / (2 * kCUs), r256 = (t256 + kCUs - 1) / kCUs;
+    if (17 * r256 < 10 * r128) return launch_cfg<MODE, 256, 256, false, 64, 2, 2, 4>(g, s, strm);
     return launch_cfg<MODE, 128, 128, false>(g, s, strm);
   }
 }

@@ -99,6 +99,12 @@ FFN_CASES = {
     # tiles; grouped order for the gate/up forward, down forward and gate/up
     # data gradient (24, 32 and 16 column tiles)
     "wide_wgrad": dict(T=600, H=4096, F=1536, E=2, K=1),
+    # enough tiles for the 256 x 256 eight-wave forward tiles: the gate/up
+    # forward with a K tail (H = 1096) and a partial last column tile (F = 224)
+    "w8_gate_up_ragged": dict(T=8000, H=1096, F=224, E=16, K=2),
+    # the down forward on 256 x 256 tiles: partial last column tile (N = H =
+    # 1096 = 4 x 256 + 72) and a K tail (F = 224)
+    "w8_down_ragged": dict(T=4000, H=1096, F=224, E=8, K=2),
 }
 
 
