@@ -145,20 +145,20 @@ struct Cfg {
   // WM x WN waves, each a (BM/WM) x (BN/WN) block of TI x TJ MFMA 32x32 tiles
   static constexpr int WM = WM_, WN = WN_, kThreads = 64 * WM * WN;
   static constexpr int TI = BM / WM / 32, TJ = BN / WN / 32;
-  // output columns staged in LDS at once by the epilogue, and its row pitch;
-  // the 16-byte pad puts rows m and m+4 (written by the two half-waves of one
-  // store instruction) in different banks
+  // output columns staged in LDS at once by the epilogue, and its row pitch
+  // (16 bytes of padding per row)
   static constexpr int CW = MODE == GATE_UP_FWD ? BN / 2 : BN;
   static constexpr int CP = CW + 8;
   // LDS stages of the bf16 operand tiles (the fp8 path has two)
   static constexpr int S = S_;
   // bf16: S stages of BK-wide tiles; fp8: two stages of 128-byte rows
   static constexpr int kMain = FP8 ? 2 * (BM + BN) * 64 : S * (BM + BN) * BK;
-  // epilogue staging: h, G and U side by side (or one after the other when the
-  // three do not fit the operand LDS); the SwiGLU backward stages the saved G
-  // and U tiles (per wave column when the whole tile does not fit)
-  // (the fp8 down data gradient stages G and U in one pass even beyond its
-  // operand LDS, at two workgroups per CU: measured 5% faster than two passes)
+  // epilogue staging: h, G and U side by side when the three fit the operand
+  // LDS, else h and G, then U (two passes) or one after the other (three);
+  // the SwiGLU backward stages the saved G and U tiles, per wave column when
+  // the whole tile does not fit the operand LDS (the fp8 down data gradient
+  // stages them in one pass even beyond its operand LDS, at two workgroups
+  // per CU: measured 5% faster than per wave column)
   static constexpr bool kEpiOnePass =
       MODE == GATE_UP_FWD ? 3 * BM * CP <= kMain
                           : (MODE == DOWN_BWD_DATA ? (FP8 ? 2 * BM * CP * 2 <= 80 * 1024 : 2 * BM * CP <= kMain) : true);
@@ -186,7 +186,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   auto lds_off = [](int r, int c) { return lds_offw<BK>(r, c); };
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
   constexpr int TI = C::TI, TJ = C::TJ;
-  // Two LDS stages of the A and B tiles; after the K loop the same memory
+  // S LDS stages of the A and B tiles; after the K loop the same memory
   // stages the output tile (and, for the SwiGLU backward, the saved G/U tile).
   __shared__ __attribute__((aligned(16))) bf16_t smem[C::kSmem];
   // fp8 operand stages: BM (BN) rows of 128 bytes, two stages
