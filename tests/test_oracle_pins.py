@@ -456,3 +456,77 @@ def test_int8_payload_lossless_rows_and_rounding():
     d = orc.qdq_rows_int8(Y2)
     amax = np.abs(Y2).max(axis=1, keepdims=True)
     assert np.all(np.abs(d - Y2) <= amax / 127 / 2 * 1.0001)
+
+
+# ============================================================================ router
+
+
+def test_router_selection_is_the_k_largest_with_ties_to_lower_id():
+    """Brute force on small rows with many equal logits: the selection is the first K
+    ids in (logit descending, id ascending) order, checked by a plain key sort."""
+    rng = np.random.default_rng(41)
+    for n, K in ((7, 3), (12, 12), (30, 8), (5, 1)):
+        logits = rng.integers(-3, 4, size=(40, n)).astype(np.float32)   # many ties
+        idx = orc.select_topk(logits, K)
+        for r in range(logits.shape[0]):
+            want = sorted(range(n), key=lambda i: (-float(logits[r, i]), i))[:K]
+            assert idx[r].tolist() == want
+
+
+def test_router_closed_forms():
+    """logits = log(1..4): softmax = (1,2,3,4)/10; top-2 plain = (.4,.3), renormalised (4/7,3/7)."""
+    logits = np.log(np.array([[1.0, 2.0, 3.0, 4.0]]))
+    idx, w = orc.router_fwd(logits, 2, renorm=False)
+    assert idx.tolist() == [[3, 2]]
+    np.testing.assert_allclose(w, [[0.4, 0.3]], rtol=1e-14)
+    _, w = orc.router_fwd(logits, 2, renorm=True)
+    np.testing.assert_allclose(w, [[4 / 7, 3 / 7]], rtol=1e-14)
+    _, w = orc.router_fwd(logits, 4, renorm=False)
+    np.testing.assert_allclose(w, [[0.4, 0.3, 0.2, 0.1]], rtol=1e-14)
+
+
+def test_router_weights_match_torch_softmax():
+    """Plain weights = torch.softmax over all ids at the selection; renormalised =
+    torch.softmax over the selected logits."""
+    rng = np.random.default_rng(42)
+    logits = rng.standard_normal((64, 37)) * 3
+    t = torch.from_numpy(logits)
+    for renorm in (False, True):
+        idx, w = orc.router_fwd(logits, 6, renorm)
+        ti = torch.from_numpy(idx.astype(np.int64))
+        ref = torch.softmax(t.gather(1, ti), dim=1) if renorm else torch.softmax(t, dim=1).gather(1, ti)
+        np.testing.assert_allclose(w, ref.numpy(), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_router_backward_matches_torch_autograd_and_finite_differences(renorm):
+    rng = np.random.default_rng(43 + renorm)
+    T, n, K = 16, 21, 5
+    # distinct, well separated logits: the selection does not move under the FD step
+    logits = np.stack([rng.permutation(n) * 0.37 + rng.standard_normal() for _ in range(T)])
+    idx, _ = orc.router_fwd(logits, K, renorm)
+    dw = rng.standard_normal((T, K))
+    dl = orc.router_bwd(logits, idx, dw, renorm)
+    # torch autograd through softmax / gather (/ renormalisation), selection fixed
+    t = torch.from_numpy(logits).requires_grad_(True)
+    ti = torch.from_numpy(idx.astype(np.int64))
+    w = torch.softmax(t, dim=1).gather(1, ti)
+    if renorm:
+        w = w / w.sum(dim=1, keepdim=True)
+    (w * torch.from_numpy(dw)).sum().backward()
+    np.testing.assert_allclose(dl, t.grad.numpy(), rtol=1e-12, atol=1e-14)
+    # central differences of L(l) = sum(dw * w(l))
+    def L(z):
+        return float((orc.router_fwd(z, K, renorm)[1] * dw).sum())
+    eps = 1e-6
+    for r, i in ((0, int(idx[0, 0])), (3, int(idx[3, K - 1])), (5, int(np.argmin(logits[5]))), (9, 0)):
+        zp, zm = logits.copy(), logits.copy()
+        zp[r, i] += eps
+        zm[r, i] -= eps
+        assert abs((L(zp) - L(zm)) / (2 * eps) - dl[r, i]) < 1e-7
+    # softmax-type gradients sum to zero over a row; unselected ids get none when renormalised
+    np.testing.assert_allclose(dl.sum(axis=1), 0.0, atol=1e-13)
+    if renorm:
+        mask = np.ones_like(dl, dtype=bool)
+        np.put_along_axis(mask, idx.astype(np.int64), False, axis=1)
+        assert (dl[mask] == 0).all()
