@@ -34,6 +34,7 @@ ENTRY_POINTS = (
     "moe_ffn_gate_up_bwd_data", "moe_ffn_gate_up_bwd_weight", "moe_dispatch_bwd",
     "moe_quant_rows_fp8", "moe_quantize_weights_fp8", "moe_ffn_gate_up_fwd_fp8",
     "moe_ffn_down_fwd_fp8", "moe_ffn_down_bwd_data_fp8", "moe_ffn_gate_up_bwd_data_fp8",
+    "moe_router", "moe_router_bwd",
 )
 
 
@@ -93,6 +94,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_down_fwd_fp8.argtypes = [S] + [P] * 7
         L.moe_ffn_down_bwd_data_fp8.argtypes = [S] + [P] * 8
         L.moe_ffn_gate_up_bwd_data_fp8.argtypes = [S] + [P] * 9
+        I32C = ctypes.c_int32
+        L.moe_router.argtypes = [I64, I64, I32C, I32C, P, P, P, P]
+        L.moe_router_bwd.argtypes = [I64, I64, I32C, I32C, P, P, P, P, P, P]
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
                 getattr(L, name).restype = ctypes.c_int32
@@ -299,6 +303,53 @@ def moe_ffn_gate_up_bwd_data_fp8(shape, dguq, dgus, wgq_t, wgs, wuq_t, wus, ep_r
         _ptr(wgq_t, U8T, "wgq_t"), _ptr(wgs, F32T, "wgs"), _ptr(wuq_t, U8T, "wuq_t"),
         _ptr(wus, F32T, "wus"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
         _ptr(grad_expand_x, BF16, "grad_expand_x"), _stream(stream)))
+
+
+def moe_router(logits, K, renorm, topk_idx, topk_weights, stream=None):
+    T, n = logits.shape
+    _check(lib().moe_router(T, n, int(K), int(bool(renorm)), _ptr(logits, F32, "logits"),
+                            _ptr(topk_idx, I32, "topk_idx"), _ptr(topk_weights, F32, "topk_weights"),
+                            _stream(stream)))
+
+
+def moe_router_bwd(logits, K, renorm, topk_idx, topk_weights, grad_topk_weights, grad_logits,
+                   stream=None):
+    T, n = grad_logits.shape
+    _check(lib().moe_router_bwd(T, n, int(K), int(bool(renorm)), _ptr(logits, F32, "logits"),
+                                _ptr(topk_idx, I32, "topk_idx"), _ptr(topk_weights, F32, "topk_weights"),
+                                _ptr(grad_topk_weights, F32, "grad_topk_weights"),
+                                _ptr(grad_logits, F32, "grad_logits"), _stream(stream)))
+
+
+class _RouterFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, K, renorm):
+        logits = logits.contiguous()
+        T = logits.shape[0]
+        idx = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+        w = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+        moe_router(logits, K, renorm, idx, w)
+        ctx.save_for_backward(logits, idx, w)
+        ctx.K, ctx.renorm = K, renorm
+        ctx.mark_non_differentiable(idx)
+        return idx, w
+
+    @staticmethod
+    def backward(ctx, g_idx, g_w):
+        logits, idx, w = ctx.saved_tensors
+        gl = torch.empty_like(logits)
+        if g_w is None:
+            return torch.zeros_like(logits), None, None
+        moe_router_bwd(logits, ctx.K, ctx.renorm, idx, w, g_w.float().contiguous(), gl)
+        return gl, None, None
+
+
+def router(logits, K, renorm=True):
+    """Softmax top-K gating of fp32 logits (T, n_ids) -> (topk_idx int32 (T, K),
+    topk_weights fp32 (T, K)); differentiable in the logits through topk_weights."""
+    if logits.dtype != torch.float32:
+        raise MoeError(f"logits must be float32, got {logits.dtype}")
+    return _RouterFn.apply(logits, int(K), bool(renorm))
 
 
 @dataclass

@@ -310,6 +310,38 @@ moe_status moe_ffn_gate_up_bwd_data_fp8(const moe_shape* s, const uint8_t* dguq,
                                         const int32_t* ep_recv_counts, void* grad_expand_x,
                                         void* stream);
 
+/* ------------------------------------------------------------------ router
+ * The pages take topk_idx and topk_weights as inputs (low_latency_combine page,
+ * "Parameters": K distinct ids per token in [0, E+Z+C+Q), one float weight per
+ * token and choice) and print no router.  These two entries give the plain
+ * softmax top-K gating that produces them, over every id a slot may take
+ * (routed and special experts), and its backward.  Sizes: T >= 0 tokens,
+ * n_ids ids per token (1 <= n_ids <= 4096), 0 < K <= min(16, n_ids), renorm 0
+ * or 1 (else MOE_ERR_BAD_SHAPE / MOE_ERR_BAD_RANGE).  Logits are fp32; a NaN
+ * logit counts as -inf.
+ */
+
+/* moe_router - topk_idx (T, K) int32: the ids of the K largest logits of each
+ * row, in descending order, equal logits by increasing id.  topk_weights (T, K)
+ * fp32: softmax(logits row)[topk_idx] (renorm = 0), or those K values divided by
+ * their sum (renorm = 1, a softmax over the selected logits).
+ *  in  logits (T, n_ids) fp32.  One kernel launch. */
+moe_status moe_router(int64_t T, int64_t n_ids, int32_t K, int32_t renorm, const float* logits,
+                      int32_t* topk_idx, float* topk_weights, void* stream);
+
+/* moe_router_bwd - gradient of sum(grad_topk_weights * topk_weights) with
+ * respect to the logits, the selection held fixed:
+ *   renorm = 1: grad_logits[i] = w_i (dw_i - sum_k w_k dw_k) for a chosen id i,
+ *               0 for the others (logits may be NULL);
+ *   renorm = 0: grad_logits[i] = p_i ([i chosen] dw_i - sum_k w_k dw_k) for every
+ *               id, p = softmax(logits row).
+ *  in  logits (T, n_ids) fp32; topk_idx, topk_weights (T, K) from moe_router;
+ *      grad_topk_weights (T, K) fp32 (e.g. from moe_combine_bwd)
+ *  out grad_logits (T, n_ids) fp32, every element written.  One kernel launch. */
+moe_status moe_router_bwd(int64_t T, int64_t n_ids, int32_t K, int32_t renorm, const float* logits,
+                          const int32_t* topk_idx, const float* topk_weights,
+                          const float* grad_topk_weights, float* grad_logits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

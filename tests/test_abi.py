@@ -165,3 +165,17 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_router_rejects_bad_arguments_before_launch(L):
+    Nn = None
+    # (T, n_ids, K, renorm): K in (0, min(16, n_ids)], n_ids in [1, 4096], renorm 0/1
+    for T, n, K, rn, want in ((4, 8, 0, 1, BAD_SHAPE), (4, 8, 9, 1, BAD_SHAPE), (4, 64, 17, 1, BAD_SHAPE),
+                              (4, 4097, 8, 1, BAD_SHAPE), (4, 0, 1, 1, BAD_SHAPE), (-1, 8, 2, 1, BAD_SHAPE),
+                              (4, 8, 2, 2, BAD_RANGE)):
+        assert L.moe_router(T, n, K, rn, P(), P(), P(), Nn) == want
+        assert L.moe_router_bwd(T, n, K, rn, P(), P(), P(), P(), P(), Nn) == want
+    assert L.moe_router(0, 8, 2, 1, Nn, Nn, Nn, Nn) == OK            # no tokens: nothing to do
+    assert L.moe_router(4, 8, 2, 1, P(), Nn, P(), Nn) == NULL_ARG
+    assert L.moe_router_bwd(4, 8, 2, 0, Nn, P(), P(), P(), P(), Nn) == NULL_ARG   # plain gating needs logits
+    assert L.moe_router_bwd(4, 4096, 16, 1, P(), P(), P(), P(), Nn, Nn) == NULL_ARG
