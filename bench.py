@@ -223,6 +223,20 @@ def build_combine_step(cfg):
     st.config = {"T": T, "H": H, "F": 0, "E": E, "K": K}
     st.cfg = cfg
     st.shape_info = (T, H, 0, K, E)
+    # the router over the 260 ids of this layer (weights not renormalised, as in
+    # the combine inputs), timed apart from the step
+    n_ids = E + Z + C + Q
+    gen = torch.Generator(device=dev).manual_seed(5)
+    logits = torch.randn((T, n_ids), dtype=torch.float32, device=dev, generator=gen)
+    r_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    r_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    r_dw = torch.randn((T, K), dtype=torch.float32, device=dev, generator=gen)
+    r_dl = torch.empty((T, n_ids), dtype=torch.float32, device=dev)
+    st.extra_calls = [
+        (f"moe_router ({n_ids} ids, top-{K})", lambda: dm.moe_router(logits, K, False, r_idx, r_w)),
+        (f"moe_router_bwd ({n_ids} ids, top-{K})",
+         lambda: dm.moe_router_bwd(logits, K, False, r_idx, r_w, r_dw, r_dl)),
+    ]
     return st
 
 
@@ -335,6 +349,19 @@ def build_step(name, T_override=None):
                            lambda: [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)])]
     else:
         st.extra_calls = []
+    # the router that produces topk_idx / topk_weights from gating logits, and
+    # its backward (the step takes the routing as input, so these are timed apart)
+    n_ids = E + cfg.get("Z", 0) + cfg.get("C", 0) + cfg.get("Q", 0)
+    gen = torch.Generator(device=dev).manual_seed(5)
+    logits = torch.randn((T, n_ids), dtype=f32, device=dev, generator=gen)
+    r_idx, r_w = z(T, K, dt=i32), z(T, K, dt=f32)
+    r_dw, r_dl = torch.randn((T, K), dtype=f32, device=dev, generator=gen), z(T, n_ids, dt=f32)
+    renorm = cfg.get("renorm", True)
+    st.extra_calls += [
+        (f"moe_router ({n_ids} ids, top-{K})", lambda: dm.moe_router(logits, K, renorm, r_idx, r_w)),
+        (f"moe_router_bwd ({n_ids} ids, top-{K})",
+         lambda: dm.moe_router_bwd(logits, K, renorm, r_idx, r_w, r_dw, r_dl)),
+    ]
     return st
 
 
@@ -440,10 +467,11 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
         e0.record()
-        fn()
+        for _ in range(10):
+            fn()
         e1.record()
         torch.cuda.synchronize()
-        extra[name] = {"ms": round(e0.elapsed_time(e1), 4)}
+        extra[name] = {"ms": round(e0.elapsed_time(e1) / 10, 4)}
 
     fl, nb = account(st, A)
     combine_only = st.cfg.get("combine_only", False)
