@@ -56,6 +56,9 @@ WORKLOADS = {
     # with 10% false, shared_expert_x; the step is combine, combine backward and
     # dispatch backward (on the expert-output buffer)
     "combine_stress": dict(T=4096, H=7168, E=256, K=8, Z=1, C=1, Q=2, combine_only=True),
+    # the low_latency_combine page's decode regime (BS <= 512 tokens, H = 7168,
+    # top-8, 32 experts in its example), every expert on one GPU, forward only
+    "decode": dict(T=512, H=7168, F=2048, E=32, K=8, forward_only=True),
 }
 
 
@@ -72,6 +75,16 @@ def gemm_flops(A, H, F):
         "moe_ffn_gate_up_bwd_data": 4 * A * H * F,
         "moe_ffn_gate_up_bwd_weight": 4 * A * H * F,
     }
+
+
+def gemm_bytes(name, A, H, F, E):
+    """Algorithmic HBM bytes of a forward grouped GEMM: every expert's weights once, its
+    input rows and its outputs (decode-sized batches read the weights far more than rows)."""
+    if name.startswith("moe_ffn_gate_up_fwd"):
+        return E * 2 * F * H * 2 + A * H * 2 + A * 3 * F * 2
+    if name.startswith("moe_ffn_down_fwd"):
+        return E * H * F * 2 + A * F * 2 + A * H * 2
+    return 0
 
 
 def bytes_moved(name, T, H, F, K, A, E):
@@ -117,6 +130,8 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     fp8 = cfg.get("fp8", False)
+    fwd_only = cfg.get("forward_only", False)
+    T_sample = min(T_sample, cfg["T"])
     inp = wl.layer_inputs(T_sample, cfg["H"], cfg["F"], cfg["E"], cfg["K"], seed=0,
                           zipf=cfg.get("zipf"), shared=cfg.get("shared", False))
     runs, t0 = 0, time.perf_counter()
@@ -126,15 +141,17 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
             orc.layer_bwd_fp8(inp, f, inp["grad_out"])
         else:
             f = orc.layer_fwd(inp, prec="parity")
-            orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
+            if not fwd_only:
+                orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
         runs += 1
         el = time.perf_counter() - t0
         if el >= seconds or runs >= 50:
             break
     A = f["route"].A
-    flops = 18.0 * (A + (T_sample if cfg.get("shared") else 0)) * cfg["H"] * cfg["F"] * runs
+    flops = (6.0 if fwd_only else 18.0) * (A + (T_sample if cfg.get("shared") else 0)) * cfg["H"] * cfg["F"] * runs
+    what = "forward" if fwd_only else "fwd+bwd"
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{runs} oracle fwd+bwd runs (parity mode, numpy) of a {T_sample}-token slice of the "
+            "sample": f"{runs} oracle {what} runs (parity mode, numpy) of a {T_sample}-token slice of the "
                       f"same workload (H={cfg['H']} F={cfg['F']} E={cfg['E']} K={cfg['K']}), {el:.1f} s"}
 
 
@@ -225,18 +242,7 @@ def build_combine_step(cfg):
     st.shape_info = (T, H, 0, K, E)
     # the router over the 260 ids of this layer (weights not renormalised, as in
     # the combine inputs), timed apart from the step
-    n_ids = E + Z + C + Q
-    gen = torch.Generator(device=dev).manual_seed(5)
-    logits = torch.randn((T, n_ids), dtype=torch.float32, device=dev, generator=gen)
-    r_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    r_w = torch.empty((T, K), dtype=torch.float32, device=dev)
-    r_dw = torch.randn((T, K), dtype=torch.float32, device=dev, generator=gen)
-    r_dl = torch.empty((T, n_ids), dtype=torch.float32, device=dev)
-    st.extra_calls = [
-        (f"moe_router ({n_ids} ids, top-{K})", lambda: dm.moe_router(logits, K, False, r_idx, r_w)),
-        (f"moe_router_bwd ({n_ids} ids, top-{K})",
-         lambda: dm.moe_router_bwd(logits, K, False, r_idx, r_w, r_dw, r_dl)),
-    ]
+    _add_router(st, cfg, T, K, E, dev, False)
     return st
 
 
@@ -311,9 +317,15 @@ def build_step(name, T_override=None):
     C += [
         ("moe_combine", lambda: dm.moe_combine(shape, y, idx, w, assist, recv, None, sy, x, None, None, None,
                                                out)),
-        ("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x, None,
-                                                       None, None, gy, gw)),
     ]
+    st.config = {"T": T, "H": H, "F": F, "E": E, "K": K}
+    st.cfg = cfg
+    st.shape_info = (T, H, F, K, E)
+    _add_router(st, cfg, T, K, E, dev, cfg.get("renorm", True))
+    if cfg.get("forward_only"):
+        return st
+    C.append(("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x, None,
+                                                           None, None, gy, gw)))
     # backward order: each gather/scatter right after the kernel that produced
     # its input (grad_expand_x goes to dispatch backward before the last
     # weight gradient evicts it from the caches)
@@ -340,29 +352,31 @@ def build_step(name, T_override=None):
                                                               gx)))
     C.append(("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
                                                                                   gwu)))
-    st.config = {"T": T, "H": H, "F": F, "E": E, "K": K}
-    st.cfg = cfg
-    st.shape_info = (T, H, F, K, E)
     if fp8:
         # weight quantisation (once per weight update) is timed outside the step
-        st.extra_calls = [("moe_quantize_weights_fp8 (3 tensors)",
-                           lambda: [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)])]
-    else:
-        st.extra_calls = []
-    # the router that produces topk_idx / topk_weights from gating logits, and
-    # its backward (the step takes the routing as input, so these are timed apart)
+        st.extra_calls.insert(0, ("moe_quantize_weights_fp8 (3 tensors)",
+                                  lambda: [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)]))
+    return st
+
+
+def _add_router(st, cfg, T, K, E, dev, renorm):
+    """Time the router that produces topk_idx / topk_weights from gating logits, and
+    its backward, apart from the step (the step takes the routing as input)."""
+    import torch
+    import dispatch_expert_gemm_amd as dm
     n_ids = E + cfg.get("Z", 0) + cfg.get("C", 0) + cfg.get("Q", 0)
     gen = torch.Generator(device=dev).manual_seed(5)
+    f32 = torch.float32
     logits = torch.randn((T, n_ids), dtype=f32, device=dev, generator=gen)
-    r_idx, r_w = z(T, K, dt=i32), z(T, K, dt=f32)
-    r_dw, r_dl = torch.randn((T, K), dtype=f32, device=dev, generator=gen), z(T, n_ids, dt=f32)
-    renorm = cfg.get("renorm", True)
+    r_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    r_w = torch.empty((T, K), dtype=f32, device=dev)
+    r_dw = torch.randn((T, K), dtype=f32, device=dev, generator=gen)
+    r_dl = torch.empty((T, n_ids), dtype=f32, device=dev)
     st.extra_calls += [
         (f"moe_router ({n_ids} ids, top-{K})", lambda: dm.moe_router(logits, K, renorm, r_idx, r_w)),
         (f"moe_router_bwd ({n_ids} ids, top-{K})",
          lambda: dm.moe_router_bwd(logits, K, renorm, r_idx, r_w, r_dw, r_dl)),
     ]
-    return st
 
 
 def account(st, A):
@@ -380,18 +394,22 @@ def account(st, A):
     fp8 = st.cfg.get("fp8", False)
     pk = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     fl = {}
+    fwd_only = st.cfg.get("forward_only", False)
     for n, (mult, peak) in {"moe_ffn_gate_up_fwd": (4, pk), "moe_ffn_down_fwd": (2, pk),
                             "moe_ffn_down_bwd_data": (2, pk), "moe_ffn_down_bwd_weight": (2, PEAK_BF16_TFLOPS),
                             "moe_ffn_gate_up_bwd_data": (4, pk),
                             "moe_ffn_gate_up_bwd_weight": (4, PEAK_BF16_TFLOPS)}.items():
         key = n + "_fp8" if fp8 and ("fwd" in n or "data" in n) else n
+        if fwd_only and "fwd" not in n:
+            continue
         fl[key] = (mult * A * H * F, peak)
     if st.cfg.get("shared"):
         fl["shared moe_ffn_gate_up_fwd"] = (4 * T * H * F, PEAK_BF16_TFLOPS)
         fl["shared moe_ffn_down_fwd"] = (2 * T * H * F, PEAK_BF16_TFLOPS)
         fl["shared moe_grouped_ffn_bwd (4 GEMMs)"] = (12 * T * H * F, PEAK_BF16_TFLOPS)
     nb = {}
-    for n in ("moe_dispatch", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd"):
+    for n in ("moe_dispatch", "moe_combine") if fwd_only else ("moe_dispatch", "moe_combine", "moe_combine_bwd",
+                                                                "moe_dispatch_bwd"):
         nb[n] = bytes_moved(n, T, H, F, K, A, E)
     if st.cfg.get("shared"):
         nb["moe_combine"] += T * H * 2
@@ -513,8 +531,13 @@ def main():
             isolated[name] = {"ms": round(ms, 4), "GB/s": round(nb[name] / (ms * 1e-3) / 1e9, 1),
                               "frac_hbm": round(nb[name] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del flush
-    # layer roofline: every GEMM at its MFMA peak and every other kernel at HBM peak
-    t_ideal_ms = (sum(f / (pk * 1e12) for f, pk in fl.values())
+    # layer roofline: every GEMM at its MFMA peak (or, at decode batch sizes, at the
+    # HBM rate its expert weights allow, whichever is slower) and every other
+    # kernel at HBM peak
+    fwd_only = st.cfg.get("forward_only", False)
+    Tq, Hq, Fq, Kq, Eq = st.shape_info
+    gb = {k: gemm_bytes(k, A, Hq, Fq, Eq) for k in fl} if fwd_only else {}
+    t_ideal_ms = (sum(max(f / (pk * 1e12), gb.get(k, 0) / (PEAK_HBM_GBS * 1e9)) for k, (f, pk) in fl.items())
                   + sum(b / (PEAK_HBM_GBS * 1e9) for b in nb.values() if b is not None)) * 1e3
     T, H, F, E, K = (st.config[k] for k in ("T", "H", "F", "E", "K"))
     descr = {
@@ -523,7 +546,9 @@ def main():
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
         "combine_stress": "combine only, 256 routed + 1 zero + 1 copy + 2 constant experts, "
                           "2-D mask 10% false, shared_expert_x",
+        "decode": "decode batch (the low_latency_combine page's largest BS), forward only",
     }[args.workload]
+    fwd_only = st.cfg.get("forward_only", False)
     res = {
         "metric": "MoE layer fwd+bwd ms & TFLOP/s (% MFMA peak); combine GB/s (% HBM) at 1 GPU",
         "n_gpus": 1,
@@ -553,7 +578,8 @@ def main():
         achieved = dflop / (per[dom] * 1e-3) / 1e12
         gemm_ms = sum(per[k] for k in fl)
         ideal_ms = sum(f / (pk * 1e12) for f, pk in fl.values()) * 1e3
-        config = {"workload": f"MoE layer fwd+bwd, {descr}: T={T} tokens, H={H}, F={F} SwiGLU, "
+        config = {"workload": f"MoE layer {'forward' if fwd_only else 'fwd+bwd'}, {descr}: T={T} tokens, "
+                              f"H={H}, F={F} SwiGLU, "
                               f"E={E} experts on one GPU, top-{K}",
                   "T": T, "H": H, "F": F, "E": E, "K": K, "routed_rows": A, "flop_per_step": total_flops}
         if st.counts is not None:
@@ -563,10 +589,15 @@ def main():
             "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
             "unit": "TFLOP/s",
             "config": config,
-            "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                         "peak": dpeak, "unit": "TFLOP/s",
-                         "frac": round(achieved / dpeak, 4),
-                         "traffic": measured_traffic(dom) if args.workload == "page1" and not args.tokens else None},
+            "roofline": ({"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                          "peak": dpeak, "unit": "TFLOP/s",
+                          "frac": round(achieved / dpeak, 4),
+                          "traffic": measured_traffic(dom) if args.workload == "page1" and not args.tokens
+                          else None} if not fwd_only else
+                         {"bound": "hbm", "kernel": dom,
+                          "achieved": round(gb[dom] / (per[dom] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(gb[dom] / (per[dom] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "traffic": None}),
             "combine": {"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
                         "frac": kernels["moe_combine"]["frac_hbm"]},
             "gemm_ms_per_step": round(gemm_ms, 4),

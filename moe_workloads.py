@@ -30,6 +30,9 @@ WORKLOADS = {
     "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
     # Mixtral-8x7B-style layer
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2),
+    # decode batch of the low_latency_combine page (BS <= 512, H = 7168, top-8,
+    # 32 experts in its example), forward only
+    "decode": dict(T=512, H=7168, F=2048, E=32, K=8),
 }
 
 

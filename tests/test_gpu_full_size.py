@@ -174,6 +174,27 @@ def test_combine_stress_full_size():
     check_equal("grad_x", f32(gx), ref_dx)
 
 
+def test_decode_forward_full_size():
+    """Decode batch, forward only: T=512, H=7168, F=2048, E=32, K=8 (every expert on
+    one GPU; about 128 rows per expert, so every GEMM tile is a partial one).  The
+    whole forward against the oracle: maps bit-exact, G/U/h/y rows and out in full."""
+    print("[full] decode", flush=True)
+    inp = wl.layer_inputs(**wl.WORKLOADS["decode"], seed=0, grad=False)
+    run = Run(inp)
+    run.dispatch()
+    run.ffn()
+    out = run.combine()
+    f = orc.layer_fwd(inp, prec="parity")
+    r = f["route"]
+    A, F = r.A, inp["F"]
+    check_equal("ep_recv_counts", run.d.ep_recv_counts.cpu().numpy(), r.ep_recv_counts)
+    check_close("G", f32(run.gus[:A, :F]), f["G"])
+    check_close("U", f32(run.gus[:A, F:]), f["U"])
+    check_close("h", f32(run.h[:A]), f["Hh"])
+    check_close("y", f32(run.y[:A]), f["Y"])
+    check_close("out", f32(out), f["out"])
+
+
 def test_dsv3_proxy_full_size():
     """T=4096, H=7168, F=2048, E=32, K=8, Zipf(1.2)-skewed routing, one shared
     SwiGLU expert on all tokens, fwd+bwd (the shared expert through the same
