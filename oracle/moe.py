@@ -57,7 +57,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .numerics import (bf16_to_f32, dequant_e4m3_blocks, dequant_e4m3_rows, dequant_int8_rows,
-                       quant_e4m3_blocks, quant_e4m3_rows, quant_int8_rows, round_bf16)
+                       e4m3_decode, quant_e4m3_blocks, quant_e4m3_rows, quant_int8_rows, round_bf16)
 
 ERR_ID_RANGE = 1
 ERR_ID_DUPLICATE = 2
@@ -419,6 +419,10 @@ def layer_bwd(inp: dict, fwd: dict, grad_out, prec="parity"):
 #    dX, dx keep their bf16 storage; the weight-gradient GEMMs run in bf16 on the
 #    unquantised bf16 activations (per-token scales do not factor out of a
 #    contraction over tokens);
+#  * or, with wgrad="fp8", the weight gradients run on operands requantised along
+#    the token axis: each expert's rows are cut into blocks of 128 consecutive rows
+#    from its first row (the last block may be shorter), and every column of a block
+#    gets one e4m3 scale (the row rule above, applied to that column's entries);
 #  * the quantisers are applied to the bf16 tensors the device stores;
 #  * int8 payload: every expert-output row y is quantised per row (symmetric,
 #    127/amax) and dequantised before the weighted sum; dw uses that dequantised y.
@@ -439,6 +443,47 @@ def qdq_rows_fp8(a):
     """Quantise rows per 128 columns to e4m3 and dequantise (float32)."""
     q, s = quant_e4m3_rows(np.asarray(a, np.float32))
     return dequant_e4m3_rows(q, s)
+
+
+def quant_cols_fp8(a, ep_recv_counts, block=128):
+    """Per-128-token e4m3 quantisation of expert-sorted rows (the weight-gradient
+    operands): each expert's rows are cut into blocks of `block` consecutive rows
+    starting at its first row, and each column of a block is quantised as one block of
+    quant_e4m3_rows.  Returns a list of (expert, first row, end row, codes (rows, D)
+    uint8, scales (D,) float32), in row order."""
+    a = np.asarray(a, np.float32)
+    out = []
+    lo = 0
+    for e, hi in enumerate(np.asarray(ep_recv_counts, np.int64).tolist()):
+        for r0 in range(lo, hi, block):
+            r1 = min(r0 + block, hi)
+            q, s = quant_e4m3_rows(a[r0:r1].T, block=r1 - r0)  # a column is one block
+            out.append((e, r0, r1, q.T.copy(), s[:, 0].copy()))
+        lo = hi
+    return out
+
+
+def qdq_cols_fp8(a, ep_recv_counts, block=128):
+    """quant_cols_fp8 then dequantisation: code value times scale, exact in float64."""
+    a = np.asarray(a, np.float32)
+    d = np.zeros(a.shape, np.float64)
+    for _, r0, r1, q, s in quant_cols_fp8(a, ep_recv_counts, block):
+        d[r0:r1] = e4m3_decode(q).astype(np.float64) * s.astype(np.float64)[None, :]
+    return d
+
+
+def wgrad_fp8(P16, Q16, ep_recv_counts):
+    """Weight gradient on per-128-token fp8 operands: for every expert e,
+    qdq_cols_fp8(P)[rows of e]^T @ qdq_cols_fp8(Q)[rows of e], float64 (E, Dp, Dq)."""
+    Pd, Qd = qdq_cols_fp8(P16, ep_recv_counts), qdq_cols_fp8(Q16, ep_recv_counts)
+    E = len(ep_recv_counts)
+    out = np.zeros((E, Pd.shape[1], Qd.shape[1]))
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        out[e] = Pd[lo:hi].T @ Qd[lo:hi]
+        lo = hi
+    return out
 
 
 def ffn_fwd_fp8(X16, ep_recv_counts, wq_gate, wq_up, wq_down):
@@ -468,9 +513,11 @@ def ffn_fwd_fp8(X16, ep_recv_counts, wq_gate, wq_up, wq_down):
     return G, U, Hh, Y
 
 
-def ffn_bwd_fp8(dY16, X16, G16, U16, H16, ep_recv_counts, wq_gate, wq_up, wq_down):
-    """fp8 backward: data gradients on quantised dY / dGU and fp8 weights,
-    weight gradients in bf16 (parity mode).  Returns dGU, dX, dWg, dWu, dWd."""
+def ffn_bwd_fp8(dY16, X16, G16, U16, H16, ep_recv_counts, wq_gate, wq_up, wq_down, wgrad="bf16"):
+    """fp8 backward: data gradients on quantised dY / dGU and fp8 weights, weight
+    gradients in bf16, or on per-128-token fp8 operands with wgrad="fp8" (parity
+    mode).  Returns dGU, dX, dWg, dWu, dWd."""
+    assert wgrad in ("bf16", "fp8")
     st = _store("parity")
     Wg, Wu, Wd = (dequant_weights_fp8(*w) for w in (wq_gate, wq_up, wq_down))
     E, F, H = Wg.shape
@@ -492,10 +539,15 @@ def ffn_bwd_fp8(dY16, X16, G16, U16, H16, ep_recv_counts, wq_gate, wq_up, wq_dow
             dgu = np.concatenate([dg, du], 1)
             dGU[lo:hi] = dgu
             dX[lo:hi] = st(qdq_rows_fp8(dgu) @ np.concatenate([Wg[e], Wu[e]], 0))
-            dWd[e] = dY16[lo:hi].T @ H16[lo:hi]
-            dWg[e] = dg.T @ X16[lo:hi]
-            dWu[e] = du.T @ X16[lo:hi]
+            if wgrad == "bf16":
+                dWd[e] = dY16[lo:hi].T @ H16[lo:hi]
+                dWg[e] = dg.T @ X16[lo:hi]
+                dWu[e] = du.T @ X16[lo:hi]
         lo = hi
+    if wgrad == "fp8":
+        dWd[:] = wgrad_fp8(dY16, H16, ep_recv_counts)
+        dWgu = wgrad_fp8(dGU, X16, ep_recv_counts)
+        dWg[:], dWu[:] = dWgu[:, :F], dWgu[:, F:]
     return dGU, dX, dWg, dWu, dWd
 
 
@@ -522,11 +574,11 @@ def layer_fwd_fp8(inp: dict, comm_quant=True):
     return dict(route=r, X=X, wq=wq, G=G, U=U, Hh=Hh, Y=Y, Yc=Yc, out=out)
 
 
-def layer_bwd_fp8(inp: dict, fwd: dict, grad_out):
+def layer_bwd_fp8(inp: dict, fwd: dict, grad_out, wgrad="bf16"):
     r = fwd["route"]
     dY, dw = combine_bwd(grad_out, fwd["Yc"], r, inp["topk_weights"], inp["x"],
                          inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), "parity")
     dGU, dX, dWg, dWu, dWd = ffn_bwd_fp8(dY, fwd["X"], fwd["G"], fwd["U"], fwd["Hh"], r.ep_recv_counts,
-                                         *fwd["wq"])
+                                         *fwd["wq"], wgrad=wgrad)
     dx = dispatch_bwd(dX, r, inp["topk_weights"], grad_out, inp.get("const_alpha_1"), None, "parity")
     return dict(dY=dY, dw=dw, dGU=dGU, dX=dX, dWg=dWg, dWu=dWu, dWd=dWd, dx=dx)

@@ -445,6 +445,80 @@ def test_fp8_layer_close_to_bf16_layer():
     assert np.array_equal(ref, b8["dWd"])
 
 
+# Expert row counts 3, 133, 0 and 128 (inclusive prefix 3, 136, 136, 264): the
+# per-128-token blocks, written out by hand, are expert 0 rows [0, 3), expert 1 rows
+# [3, 131) and [131, 136), expert 3 rows [136, 264).
+_COLS_PREFIX = np.array([3, 136, 136, 264])
+_COLS_BLOCKS = [(0, 0, 3), (1, 3, 131), (1, 131, 136), (3, 136, 264)]
+
+
+def test_cols_fp8_blocks_follow_expert_rows():
+    rng = np.random.default_rng(31)
+    a = rng.standard_normal((264, 4)).astype(np.float32)
+    blocks = orc.quant_cols_fp8(a, _COLS_PREFIX)
+    assert [(e, r0, r1) for e, r0, r1, _, _ in blocks] == _COLS_BLOCKS
+    # a value changed in one (block, column) changes no other dequantised value,
+    # and does change its own block's column (its scale moves)
+    base = orc.qdq_cols_fp8(a, _COLS_PREFIX)
+    b = a.copy()
+    b[132, 1] *= 100.0
+    d = orc.qdq_cols_fp8(b, _COLS_PREFIX) - base
+    outside = np.ones(d.shape, bool)
+    outside[131:136, 1] = False
+    assert not d[outside].any()
+    assert np.count_nonzero(d[131:136, 1]) >= 4
+
+
+def _lossless_fp8_cols(rng, D):
+    """Rows whose every (block, column) is e4m3 codes times a power of two with one
+    entry at +-448 times it: per-128-token quantisation represents them exactly."""
+    v = orc.e4m3_decode(rng.integers(0, 0x7F, size=(264, D)).astype(np.uint8)).astype(np.float64)
+    v *= np.where(rng.random((264, D)) < 0.5, -1.0, 1.0)
+    for _, r0, r1, in _COLS_BLOCKS:
+        v[r0 + (r1 - r0) // 2] = 448.0
+        v[r0:r1] *= 2.0 ** rng.integers(-12, 3, size=(1, D))
+    return v.astype(np.float32)
+
+
+def test_cols_fp8_lossless_inputs_give_exact_weight_gradient():
+    rng = np.random.default_rng(32)
+    P, Q = _lossless_fp8_cols(rng, 256), _lossless_fp8_cols(rng, 384)
+    assert np.array_equal(orc.qdq_cols_fp8(P, _COLS_PREFIX), P)
+    dW = orc.wgrad_fp8(P, Q, _COLS_PREFIX)
+    for e, (lo, hi) in enumerate([(0, 3), (3, 136), (136, 136), (136, 264)]):
+        ref = P[lo:hi].astype(np.float64).T @ Q[lo:hi].astype(np.float64)
+        assert np.allclose(dW[e], ref, rtol=1e-12, atol=0), e
+    assert not dW[2].any()  # an expert without rows has a zero gradient
+
+
+def test_cols_fp8_error_within_half_ulp_of_the_block_scale():
+    rng = np.random.default_rng(33)
+    a = (rng.standard_normal((264, 8)) * np.exp(rng.standard_normal((1, 8)))).astype(np.float32)
+    d = orc.qdq_cols_fp8(a, _COLS_PREFIX)
+    worst = 0.0
+    for _, r0, r1 in _COLS_BLOCKS:
+        blk = a[r0:r1].astype(np.float64)
+        step = np.abs(blk).max(axis=0) / 448.0           # the block scale of each column
+        # e4m3: 3 mantissa bits (half ulp 2^-4 relative), subnormal spacing 2^-9
+        bound = np.maximum(np.abs(blk) * 2.0 ** -4, step * 2.0 ** -10) * (1 + 1e-6)
+        err = np.abs(d[r0:r1] - blk)
+        assert np.all(err <= bound)
+        worst = max(worst, float((err / bound).max()))
+    assert worst > 0.5  # the rounding really happens
+
+
+def test_fp8_weight_gradients_on_requantised_operands():
+    inp = wl.layer_inputs(300, 256, 128, 3, 2, seed=34)
+    f8 = orc.layer_fwd_fp8(inp)
+    b16 = orc.layer_bwd_fp8(inp, f8, inp["grad_out"])
+    b8 = orc.layer_bwd_fp8(inp, f8, inp["grad_out"], wgrad="fp8")
+    for k in ("dGU", "dX", "dx", "dw"):
+        assert np.array_equal(b8[k], b16[k]), k
+    rel = lambda x, y: np.linalg.norm(x - y) / np.linalg.norm(y)
+    for k in ("dWg", "dWu", "dWd"):
+        assert 1e-3 < rel(b8[k], b16[k]) < 0.08, k
+
+
 def test_int8_payload_lossless_rows_and_rounding():
     rng = np.random.default_rng(23)
     k = rng.integers(-127, 128, size=(10, 64)).astype(np.float64)
