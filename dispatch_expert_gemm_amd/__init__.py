@@ -34,7 +34,8 @@ ENTRY_POINTS = (
     "moe_ffn_gate_up_bwd_data", "moe_ffn_gate_up_bwd_weight", "moe_dispatch_bwd",
     "moe_quant_rows_fp8", "moe_quantize_weights_fp8", "moe_ffn_gate_up_fwd_fp8",
     "moe_ffn_down_fwd_fp8", "moe_ffn_down_bwd_data_fp8", "moe_ffn_gate_up_bwd_data_fp8",
-    "moe_router", "moe_router_bwd",
+    "moe_router", "moe_router_bwd", "moe_quant_cols_fp8", "moe_ffn_down_bwd_weight_fp8",
+    "moe_ffn_gate_up_bwd_weight_fp8",
 )
 
 
@@ -97,6 +98,9 @@ def lib() -> ctypes.CDLL:
         I32C = ctypes.c_int32
         L.moe_router.argtypes = [I64, I64, I32C, I32C, P, P, P, P]
         L.moe_router_bwd.argtypes = [I64, I64, I32C, I32C, P, P, P, P, P, P]
+        L.moe_quant_cols_fp8.argtypes = [I64, I64, I32C, P, P, P, P, P]
+        L.moe_ffn_down_bwd_weight_fp8.argtypes = [S] + [P] * 7
+        L.moe_ffn_gate_up_bwd_weight_fp8.argtypes = [S] + [P] * 8
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
                 getattr(L, name).restype = ctypes.c_int32
@@ -305,6 +309,34 @@ def moe_ffn_gate_up_bwd_data_fp8(shape, dguq, dgus, wgq_t, wgs, wuq_t, wus, ep_r
         _ptr(grad_expand_x, BF16, "grad_expand_x"), _stream(stream)))
 
 
+def cols_fp8_slots(capacity, num_experts):
+    """Token slots of the per-128-token fp8 layout: capacity/128 + num_experts."""
+    return capacity // 128 + num_experts
+
+
+def moe_quant_cols_fp8(src, ep_recv_counts, codes_t, scales, stream=None):
+    cap, D = src.shape
+    _check(lib().moe_quant_cols_fp8(cap, D, ep_recv_counts.numel(), _ptr(src, BF16, "src"),
+                                    _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+                                    _ptr(codes_t, U8T, "codes_t"), _ptr(scales, F32T, "scales"),
+                                    _stream(stream)))
+
+
+def moe_ffn_down_bwd_weight_fp8(shape, dyq_t, dys, hq_t, hs, ep_recv_counts, grad_w_down, stream=None):
+    _check(lib().moe_ffn_down_bwd_weight_fp8(
+        ctypes.byref(shape), _ptr(dyq_t, U8T, "dyq_t"), _ptr(dys, F32T, "dys"), _ptr(hq_t, U8T, "hq_t"),
+        _ptr(hs, F32T, "hs"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(grad_w_down, F32T, "grad_w_down"), _stream(stream)))
+
+
+def moe_ffn_gate_up_bwd_weight_fp8(shape, dguq_t, dgus, xq_t, xs, ep_recv_counts, grad_w_gate, grad_w_up,
+                                   stream=None):
+    _check(lib().moe_ffn_gate_up_bwd_weight_fp8(
+        ctypes.byref(shape), _ptr(dguq_t, U8T, "dguq_t"), _ptr(dgus, F32T, "dgus"),
+        _ptr(xq_t, U8T, "xq_t"), _ptr(xs, F32T, "xs"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(grad_w_gate, F32T, "grad_w_gate"), _ptr(grad_w_up, F32T, "grad_w_up"), _stream(stream)))
+
+
 def moe_router(logits, K, renorm, topk_idx, topk_weights, stream=None):
     T, n = logits.shape
     _check(lib().moe_router(T, n, int(K), int(bool(renorm)), _ptr(logits, F32, "logits"),
@@ -369,6 +401,17 @@ class Fp8Weights:
         return q
 
 
+def quant_cols_fp8(src, ep_recv_counts, stream=None):
+    """Per-128-token e4m3 codes of expert-sorted rows (capacity, D): codes_t
+    (D, 128 * slots) and scales (slots, D), slots = cols_fp8_slots(capacity, E)."""
+    cap, D = src.shape
+    ns = cols_fp8_slots(cap, ep_recv_counts.numel())
+    codes_t = torch.empty((D, 128 * ns), dtype=U8T, device=src.device)
+    scales = torch.empty((ns, D), dtype=F32T, device=src.device)
+    moe_quant_cols_fp8(src, ep_recv_counts, codes_t, scales, stream)
+    return codes_t, scales
+
+
 def quant_rows_fp8(src, nrows=None, stream=None):
     R, C = src.shape
     codes = torch.empty((R, C), dtype=U8T, device=src.device)
@@ -428,13 +471,15 @@ class _MoELayerFn(torch.autograd.Function):
 
     fp8: the routed experts' forward and data-gradient GEMMs run on e4m3
     operands (weights quantised in 128 x 128 blocks at every forward,
-    activations per (row, 128 columns)), the weight gradients in bf16; the
-    shared expert stays bf16.  comm_quant_mode 2: the int8 combine payload."""
+    activations per (row, 128 columns)), the weight gradients in bf16, or with
+    fp8_wgrad on e4m3 operands with one scale per (128 tokens of an expert,
+    column); the shared expert stays bf16.  comm_quant_mode 2: the int8 combine payload."""
 
     @staticmethod
     def forward(ctx, x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
                 shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1, const_alpha_2,
-                const_v, zero_expert_num, copy_expert_num, const_expert_num, fp8, comm_quant_mode):
+                const_v, zero_expert_num, copy_expert_num, const_expert_num, fp8, comm_quant_mode,
+                fp8_wgrad):
         T, H = x.shape
         K = topk_idx.shape[1]
         E, F, _ = w_gate.shape
@@ -450,6 +495,7 @@ class _MoELayerFn(torch.autograd.Function):
         h = torch.empty((cap, F), dtype=BF16, device=dev)
         y = torch.empty((cap, H), dtype=BF16, device=dev)
         ctx.fp8 = bool(fp8)
+        ctx.fp8_wgrad = ctx.fp8 and bool(fp8_wgrad)
         wq = ()
         if ctx.fp8:
             nrows = d.ep_recv_counts[-1:]
@@ -515,8 +561,14 @@ class _MoELayerFn(torch.autograd.Function):
             nrows = recv[-1:]
             dyq, dys = quant_rows_fp8(gy, nrows)
             moe_ffn_down_bwd_data_fp8(shape, dyq, dys, wdt, wds, gus, recv, ggu)
-            moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
             del dyq, dys
+            if ctx.fp8_wgrad:
+                dyq_t, dys_t = quant_cols_fp8(gy, recv)
+                hq_t, hs_t = quant_cols_fp8(h, recv)
+                moe_ffn_down_bwd_weight_fp8(shape, dyq_t, dys_t, hq_t, hs_t, recv, gwd)
+                del dyq_t, dys_t, hq_t, hs_t
+            else:
+                moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
             dgq, dgs = quant_rows_fp8(ggu, nrows)
             moe_ffn_gate_up_bwd_data_fp8(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)
             del dgq, dgs
@@ -541,17 +593,23 @@ class _MoELayerFn(torch.autograd.Function):
             s_grads = (s_gwg.to(swg.dtype), s_gwu.to(swu.dtype), s_gwd.to(swd.dtype))
         gx = torch.empty((T, H), dtype=BF16, device=dev)
         moe_dispatch_bwd(shape, gx_exp, assist, topk_idx, topk_weights, mask, grad_out, a1, accum, gx)
-        moe_ffn_gate_up_bwd_weight(shape, ggu, expand_x, recv, gwg, gwu)
+        if ctx.fp8_wgrad:
+            dgq_t, dgs_t = quant_cols_fp8(ggu, recv)
+            xq_t, xs_t = quant_cols_fp8(expand_x, recv)
+            moe_ffn_gate_up_bwd_weight_fp8(shape, dgq_t, dgs_t, xq_t, xs_t, recv, gwg, gwu)
+            del dgq_t, dgs_t, xq_t, xs_t
+        else:
+            moe_ffn_gate_up_bwd_weight(shape, ggu, expand_x, recv, gwg, gwu)
         g_shared = grad_out if ctx.has_shared_x else None
         return (gx, gw, gwg.to(w_gate.dtype), gwu.to(w_up.dtype), gwd.to(w_down.dtype), g_shared,
-                *s_grads, None, None, None, None, None, None, None, None, None, None)
+                *s_grads, None, None, None, None, None, None, None, None, None, None, None)
 
 
 def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=None,
               shared_expert_x=None, shared_w_gate=None, shared_w_up=None, shared_w_down=None,
               const_alpha_1=None, const_alpha_2=None, const_v=None,
               zero_expert_num=0, copy_expert_num=0, const_expert_num=0, fp8=False,
-              comm_quant_mode=0):
+              comm_quant_mode=0, fp8_wgrad=False):
     """One MoE layer (ori_x is x itself).
 
     The shared-expert term of combine is either given (shared_expert_x) or
@@ -562,9 +620,11 @@ def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=
     directly to keep fp32.
 
     fp8=True runs the routed experts' forward and data-gradient GEMMs on
-    block-scaled e4m3 operands (H and F multiples of 128); comm_quant_mode=2
-    sends the expert outputs through the int8 combine payload."""
+    block-scaled e4m3 operands (H and F multiples of 128), and with
+    fp8_wgrad=True its weight gradients too, on operands requantised per 128
+    tokens of each expert; comm_quant_mode=2 sends the expert outputs through
+    the int8 combine payload."""
     return _MoELayerFn.apply(x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
                              shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1,
                              const_alpha_2, const_v, zero_expert_num, copy_expert_num,
-                             const_expert_num, fp8, comm_quant_mode)
+                             const_expert_num, fp8, comm_quant_mode, fp8_wgrad)

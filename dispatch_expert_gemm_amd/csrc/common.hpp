@@ -88,6 +88,28 @@ constexpr int kWave = 64;
 
 // ----------------------------------------------------------------------------- host side
 
+// Expert of row-tile slot mt when expert e owns BM-row slots starting at
+// prefix[e-1]/BM + e (prefix = inclusive row counts): the largest e whose first
+// slot is <= mt, by one wave ballot per 64 experts.  Every lane of the wave
+// gets the same answer.
+template <int BM>
+__device__ __forceinline__ int find_expert(const int32_t* __restrict__ prefix, int E, int64_t mt) {
+  const int lane = threadIdx.x & 63;
+  int found = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    bool le = false;
+    if (e < E) {
+      const int64_t P = e ? prefix[e - 1] : 0;
+      le = (P / BM + e) <= mt;
+    }
+    const uint64_t m = __ballot(le);
+    if (m) found = base + 63 - __clzll(m);
+    if (m != ~0ull) break;
+  }
+  return found;
+}
+
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline int64_t e_total(const moe_shape* s) {

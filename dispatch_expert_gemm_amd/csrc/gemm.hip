@@ -98,24 +98,6 @@ struct GemmArgs {
   int64_t sbe, sbn, sbk;
 };
 
-template <int BM>
-__device__ __forceinline__ int find_expert(const int32_t* __restrict__ prefix, int E, int64_t mt) {
-  const int lane = threadIdx.x & 63;
-  int found = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    bool le = false;
-    if (e < E) {
-      const int64_t P = e ? prefix[e - 1] : 0;
-      le = (P / BM + e) <= mt;
-    }
-    const uint64_t m = __ballot(le);
-    if (m) found = base + 63 - __clzll(m);
-    if (m != ~0ull) break;
-  }
-  return found;
-}
-
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 // LDS operand tile: R rows x W k of bf16, row pitch 2W bytes, in 16-byte
@@ -295,7 +277,11 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   // stages); two 32x32x64 MFMA sub-steps go into a temporary, then
   // acc += tmp * (A row scale * B block scale).  The accumulators hold
   // transposed fragments, so a lane's values share one row (one A scale) and
-  // one j tile (one B block scale).
+  // one j tile (one B block scale).  Weight gradients (KGROUP): both operands
+  // are per-128-token codes, transposed (one row per output row or column,
+  // the expert's token slots along it), a K step is one slot, and its scales
+  // are one per A row and one per B column: acc += tmp * (A scale * B scale)
+  // element by element.
   constexpr int S8 = 2;
   constexpr int LA = BM / 8 / (WM * WN), LB = BN / 8 / (WM * WN);
   static_assert(C::kMain >= S8 * (BM + BN) * 64, "fp8 stages must fit the operand LDS");
@@ -331,11 +317,15 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     voB[j] = (uint32_t)(n * g.ldb + c * 16);
   }
   const uint8_t* qa = g.qA + row0 * g.lda;
+  // weight gradients: the expert's first token slot (K step 0)
+  const int64_t slot0 = KGROUP ? kbeg / 128 + e : 0;
   // B codes of K step k0 (gate/up forward: half 1 = the up matrix; gate/up
   // data gradient: the gate codes for k < F, the up codes after)
   auto bsrc = [&](int64_t k0, int half) -> const uint8_t* {
     if constexpr (MODE == GATE_UP_FWD) {
       return (half ? g.qB1 : g.qB0) + (int64_t)e * g.bstride + k0;
+    } else if constexpr (KGROUP) {
+      return g.qB0 + k0;
     } else if constexpr (MODE == GATE_UP_BWD_DATA) {
       return k0 < g.F ? g.qB0 + (int64_t)e * g.bstride + k0 : g.qB1 + (int64_t)e * g.bstride + (k0 - g.F);
     } else {
@@ -357,7 +347,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   };
   auto issue8 = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
-    const int64_t k0 = kt * 128;
+    const int64_t k0 = (slot0 + kt) * 128;
     const auto ra = rsrc8(qa + k0);
 #pragma unroll
     for (int j = 0; j < LA; ++j) dma8(ra, As(st) + (wv * LA + j) * 512, voA[j]);
@@ -373,25 +363,42 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   // A row scales of step kt go to LDS with the tiles (one 4-byte load per
   // tile row, issued by wave 0): a plain vector load here would make the
   // compiler wait for every load in flight, the tile loads included
+  // (weight gradients: the B column scales of step kt go the same way, into
+  // sBl[st][0, BN))
   __shared__ float sAl[2][BM];
   __shared__ float sBl[2][kMaxKBlocks8];
+  static_assert(!KGROUP || BN <= kMaxKBlocks8, "B column scales of one step fit sBl");
   const int64_t nks = g.Kd / 128;
-  uint32_t vos[BM / 64];
+  uint32_t vos[BM / 64], vosb[BN / 64];
 #pragma unroll
   for (int q = 0; q < BM / 64; ++q) {
     const int r = q * 64 + lane;
-    vos[q] = (uint32_t)((row0 + (r < rows_valid ? r : rows_valid - 1)) * nks * 4);
+    const int rr = r < rows_valid ? r : rows_valid - 1;
+    vos[q] = (uint32_t)(KGROUP ? rr * 4 : (row0 + rr) * nks * 4);
   }
+#pragma unroll
+  for (int q = 0; q < BN / 64; ++q) {
+    const int64_t n = n0 + q * 64 + lane;
+    vosb[q] = (uint32_t)(((n < g.N ? n : g.N - 1) - n0) * 4);
+  }
+  auto lds_dword = [](const i32x4& r, const float* lds, uint32_t vo) {
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) float*)(lds));
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0));
+  };
   auto issue_scales = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
     if (wv != 0) return;
-    const auto r = rsrc8(g.sA + kt);
+    if constexpr (KGROUP) {
+      const auto ra = rsrc8(g.sA + (slot0 + kt) * g.M + row0);
 #pragma unroll
-    for (int q = 0; q < BM / 64; ++q) {
-      const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
-          (const __attribute__((address_space(3))) float*)(&sAl[st][q * 64]));
-      const uint32_t vo = vos[q];
-      asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0));
+      for (int q = 0; q < BM / 64; ++q) lds_dword(ra, &sAl[st][q * 64], vos[q]);
+      const auto rb = rsrc8(g.sB0 + (slot0 + kt) * g.N + n0);
+#pragma unroll
+      for (int q = 0; q < BN / 64; ++q) lds_dword(rb, &sBl[st][q * 64], vosb[q]);
+    } else {
+      const auto r = rsrc8(g.sA + kt);
+#pragma unroll
+      for (int q = 0; q < BM / 64; ++q) lds_dword(r, &sAl[st][q * 64], vos[q]);
     }
   };
   auto compute8 = [&](auto ST, int64_t kt) {
@@ -431,24 +438,49 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
           }
         }
     }
-    float sbv[TJ];
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) sbv[j] = sBl[(MODE == GATE_UP_FWD && j >= TJ / 2) ? 1 : 0][kt];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
+    if constexpr (KGROUP) {
+      // column n = brow(j) + 8 t + 4 (lane/32) + q of the tile: runs of four
+      // consecutive B scales
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const float f = sAl[st][wm * (BM / WM) + i * 32 + (lane & 31)] * sbv[j];
+        float4 sb[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += tmp[i][j][r] * f;
+        for (int t = 0; t < 4; ++t)
+          sb[t] = *reinterpret_cast<const float4*>(&sBl[st][brow(j) + 8 * t + 4 * (lane >> 5)]);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const float sa = sAl[st][wm * (BM / WM) + i * 32 + (lane & 31)];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            acc[i][j][4 * t + 0] += tmp[i][j][4 * t + 0] * (sa * sb[t].x);
+            acc[i][j][4 * t + 1] += tmp[i][j][4 * t + 1] * (sa * sb[t].y);
+            acc[i][j][4 * t + 2] += tmp[i][j][4 * t + 2] * (sa * sb[t].z);
+            acc[i][j][4 * t + 3] += tmp[i][j][4 * t + 3] * (sa * sb[t].w);
+          }
+        }
       }
+    } else {
+      float sbv[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) sbv[j] = sBl[(MODE == GATE_UP_FWD && j >= TJ / 2) ? 1 : 0][kt];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const float f = sAl[st][wm * (BM / WM) + i * 32 + (lane & 31)] * sbv[j];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += tmp[i][j][r] * f;
+        }
+    }
   };
-  const int64_t nk = g.Kd / 128;
+  // K steps: 128-wide blocks of K, or the expert's token slots
+  const int64_t nk = KGROUP ? (klen + 127) / 128 : g.Kd / 128;
   // B block scales of every K step, read once before the pipeline starts
-  for (int64_t kb = tid; kb < nk; kb += kThreads) {
-    sBl[0][kb] = bscale(kb * 128, 0);
-    if (MODE == GATE_UP_FWD) sBl[1][kb] = bscale(kb * 128, 1);
-  }
+  if constexpr (!KGROUP)
+    for (int64_t kb = tid; kb < nk; kb += kThreads) {
+      sBl[0][kb] = bscale(kb * 128, 0);
+      if (MODE == GATE_UP_FWD) sBl[1][kb] = bscale(kb * 128, 1);
+    }
   auto kstep8 = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1349,4 +1381,64 @@ extern "C" moe_status moe_ffn_gate_up_bwd_data_fp8(const moe_shape* s, const uin
   g.Kd = 2 * s->F;
   g.C0 = static_cast<bf16_t*>(grad_expand_x);
   return launch<GATE_UP_BWD_DATA, true>(g, s, as_stream(stream));
+}
+
+// fp8 weight gradients on per-128-token codes (moe_quant_cols_fp8 layout): row
+// r of a code matrix holds column r of the activation, the expert's token
+// slots along it, ld = 128 * (capacity/128 + E) codes; scales (slots, D).
+namespace {
+moe_status check_wgrad_fp8(const moe_shape* s, int64_t ncols) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  const int64_t ldq = 128 * (s->capacity / 128 + s->num_experts);
+  // code rows are addressed with 32-bit byte offsets from the K step's base
+  if (ncols * ldq + 128 >= (int64_t)0x7ffffff0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status moe_ffn_down_bwd_weight_fp8(const moe_shape* s, const uint8_t* dyq_t,
+                                                  const float* dys, const uint8_t* hq_t,
+                                                  const float* hs, const int32_t* ep_recv_counts,
+                                                  float* grad_w_down, void* stream) {
+  moe_status st = check_wgrad_fp8(s, s ? (s->H > s->F ? s->H : s->F) : 0);
+  if (st != MOE_OK) return st;
+  if (!ep_recv_counts || !grad_w_down) return MOE_ERR_NULL_ARG;
+  if (s->capacity > 0 && (!dyq_t || !dys || !hq_t || !hs)) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  const int64_t ldq = 128 * (s->capacity / 128 + s->num_experts);
+  g.qA = dyq_t;
+  g.sA = dys;
+  g.lda = ldq;
+  g.qB0 = hq_t;
+  g.sB0 = hs;
+  g.ldb = ldq;
+  g.M = s->H;
+  g.N = s->F;
+  g.W0 = grad_w_down;
+  return launch<DOWN_BWD_W, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_gate_up_bwd_weight_fp8(const moe_shape* s, const uint8_t* dguq_t,
+                                                     const float* dgus, const uint8_t* xq_t,
+                                                     const float* xs, const int32_t* ep_recv_counts,
+                                                     float* grad_w_gate, float* grad_w_up,
+                                                     void* stream) {
+  moe_status st = check_wgrad_fp8(s, s ? (2 * s->F > s->H ? 2 * s->F : s->H) : 0);
+  if (st != MOE_OK) return st;
+  if (!ep_recv_counts || !grad_w_gate || !grad_w_up) return MOE_ERR_NULL_ARG;
+  if (s->capacity > 0 && (!dguq_t || !dgus || !xq_t || !xs)) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  const int64_t ldq = 128 * (s->capacity / 128 + s->num_experts);
+  g.qA = dguq_t;
+  g.sA = dgus;
+  g.lda = ldq;
+  g.qB0 = xq_t;
+  g.sB0 = xs;
+  g.ldb = ldq;
+  g.M = 2 * s->F;
+  g.N = s->H;
+  g.W0 = grad_w_gate;
+  g.W1 = grad_w_up;
+  return launch<GATE_UP_BWD_W, true>(g, s, as_stream(stream));
 }

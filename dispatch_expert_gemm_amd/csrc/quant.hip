@@ -11,6 +11,13 @@
 //    serve both layouts (the transposed GEMM indexes them with swapped block
 //    coordinates).
 //
+//  * columns per 128 tokens (the weight-gradient operands, which contract over
+//    an expert's rows): each expert's rows are cut into 128-row slots from its
+//    first row, and each (slot, column) gets one scale, same rule.  The codes
+//    are written transposed, column by column, with slot s at codes s*128 ..
+//    s*128+127 of every column, so the weight-gradient GEMMs read them
+//    K-contiguous; a slot's rows past the expert's end get code 0.
+//
 // The pages name FP8 only as a precision of the MoE layer performance tests
 // (Megatron-LM page, "Added Test Cases"); the block recipe is this library's.
 #include "common.hpp"
@@ -61,6 +68,70 @@ __global__ __launch_bounds__(256) void k_quant_rows_fp8(const uint4* __restrict_
     for (int q = 0; q < 4; ++q) hi |= f32_to_e4m3(__fmul_rn(f[4 + q], inv)) << (8 * q);
     codes[row * (C / 8) + blk * 16 + sub] = make_uint2(lo, hi);
     if (sub == 0) scales[row * nb + blk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  }
+}
+
+// One 256-thread block per (slot, 128 columns).  Thread t loads rows
+// 8 (t/16) .. +7, columns 8 (t%16) .. +7; the column amax is a reduction over
+// the 16 row groups (two shuffles in a wave, then LDS across the four waves).
+// The codes go through LDS transposed (column-major, 144-byte pitch) and leave
+// as 16-byte stores, eight lanes per column.
+__global__ __launch_bounds__(256) void k_quant_cols_fp8(const uint4* __restrict__ src, int64_t D, int E,
+                                                        const int32_t* __restrict__ prefix, int64_t ldc,
+                                                        uint8_t* __restrict__ codes_t,
+                                                        float* __restrict__ scales) {
+  const int64_t nb = D / 128;
+  const int64_t slot = blockIdx.x / nb, cb = blockIdx.x % nb;
+  const int e = find_expert<128>(prefix, E, slot);
+  const int64_t p0 = e ? prefix[e - 1] : 0, p1 = prefix[e];
+  const int64_t row0 = p0 + (slot - (p0 / 128 + e)) * 128;
+  if (row0 >= p1) return;  // a slot no expert row falls in: never read
+  const int rows = (int)((p1 - row0) < 128 ? (p1 - row0) : 128);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, c = t & 15, rg = t >> 4;
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * rg + i;
+    if (r < rows) unpack8(src[(row0 + r) * (D / 8) + cb * 16 + c], v[i]);
+    else
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[i][q] = 0.f;
+  }
+  __shared__ float red[4][128];
+  __shared__ __attribute__((aligned(16))) uint8_t ct[128 * 144];
+  float m[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i][q]));
+    a = fmaxf(a, __shfl_xor(a, 16, 64));
+    a = fmaxf(a, __shfl_xor(a, 32, 64));
+    m[q] = a;
+  }
+  if (lane < 16)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) red[wave][8 * c + q] = m[q];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int col = 8 * c + q;
+    const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
+    const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__fmul_rn(v[i][q], inv)) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__fmul_rn(v[4 + i][q], inv)) << (8 * i);
+    *reinterpret_cast<uint2*>(ct + col * 144 + 8 * rg) = make_uint2(lo, hi);
+    if (rg == 0) scales[slot * D + cb * 128 + col] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = t + 256 * k, col = idx >> 3, ch = idx & 7;
+    *reinterpret_cast<uint4*>(codes_t + (cb * 128 + col) * ldc + slot * 128 + ch * 16) =
+        *reinterpret_cast<const uint4*>(ct + col * 144 + ch * 16);
   }
 }
 
@@ -137,6 +208,22 @@ extern "C" moe_status moe_quant_rows_fp8(int64_t R, int64_t C, const void* src,
   hipLaunchKernelGGL(k_quant_rows_fp8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const uint4*>(src), R, C, nrows, reinterpret_cast<uint2*>(codes),
                      scales);
+  return launch_status();
+}
+
+extern "C" moe_status moe_quant_cols_fp8(int64_t capacity, int64_t D, int32_t num_experts,
+                                         const void* src, const int32_t* ep_recv_counts,
+                                         uint8_t* codes_t, float* scales, void* stream) {
+  if (capacity < 0 || D <= 0 || D % 128 != 0 || num_experts < 1) return MOE_ERR_BAD_SHAPE;
+  const int64_t slots = capacity / 128 + num_experts;
+  const int64_t blocks = slots * (D / 128);
+  if (blocks > 0x7fffffff || D * slots * 128 >= ((int64_t)1 << 40)) return MOE_ERR_BAD_SHAPE;
+  if (!ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (capacity == 0) return MOE_OK;
+  if (!src || !codes_t || !scales) return MOE_ERR_NULL_ARG;
+  hipLaunchKernelGGL(k_quant_cols_fp8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(src), D, (int)num_experts, ep_recv_counts, slots * 128,
+                     codes_t, scales);
   return launch_status();
 }
 

@@ -261,7 +261,8 @@ moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,
  * code = e4m3(x * (448/amax)), value = code * scale.  The forward GEMMs and the
  * two data-gradient GEMMs of the FFN run on e4m3 operands with fp32
  * accumulation (each 128-wide K block's partial sum times its A and B scales);
- * the weight gradients keep the bf16 entries above.  The pages name FP8 only as
+ * the weight gradients keep the bf16 entries above, or run on per-128-token
+ * codes (the fp8 weight-gradient entries below).  The pages name FP8 only as
  * a precision of the MoE layer performance tests (Megatron-LM page, Added Test
  * Cases); the block recipe is this library's.  H and F must be multiples of 128
  * (else MOE_ERR_BAD_SHAPE), H and 2F at most 32768 and the activation scales
@@ -309,6 +310,50 @@ moe_status moe_ffn_gate_up_bwd_data_fp8(const moe_shape* s, const uint8_t* dguq,
                                         const uint8_t* wuq_t, const float* wus,
                                         const int32_t* ep_recv_counts, void* grad_expand_x,
                                         void* stream);
+
+/* ------------------------------------------------------ fp8 weight gradients
+ * The weight-gradient GEMMs contract over an expert's rows, so their e4m3
+ * operands carry one scale per (128 tokens, column) instead of per (row, 128
+ * columns): each expert's rows are cut into 128-row token slots starting at its
+ * first row (the last one may be shorter), and each (slot, column) is one
+ * quantisation block (same rule as above).  Expert e's slots are numbered from
+ * prefix[e-1]/128 + e (prefix = ep_recv_counts), so with
+ *   slots = capacity/128 + E,  ld = 128 * slots
+ * a code matrix of a (capacity, D) activation is (D, ld) uint8, row d holding
+ * column d with slot s at codes [128 s, 128 s + 128), and its scales are
+ * (slots, D) fp32.  Codes of a slot's rows past its expert's end are 0; slots
+ * that no row falls in are left unwritten (and never read).  The reading of
+ * "per-128-token requantisation" and the layout are this library's.
+ */
+
+/* Per-128-token e4m3 codes of an expert-sorted bf16 (capacity, D) matrix
+ * (expand_x, h_act, grad_y or grad_gate_up), D a multiple of 128.
+ *  in  src (capacity, D) bf16, ep_recv_counts (E) int32 (device, from dispatch)
+ *  out codes_t (D, 128 * slots) uint8, scales (slots, D) fp32
+ * Errors: MOE_ERR_BAD_SHAPE (D not a positive multiple of 128, E < 1, sizes
+ * beyond 2^40 codes), MOE_ERR_NULL_ARG.  One kernel launch. */
+moe_status moe_quant_cols_fp8(int64_t capacity, int64_t D, int32_t num_experts, const void* src,
+                              const int32_t* ep_recv_counts, uint8_t* codes_t, float* scales,
+                              void* stream);
+
+/* fp8 moe_ffn_down_bwd_weight: grad_w_down (E, H, F) fp32 = per expert the sum
+ * over its token slots of (dY codes x h codes) times the two slots' column
+ * scales.  dyq_t/dys = moe_quant_cols_fp8 of grad_y (D = H), hq_t/hs of h_act
+ * (D = F).  Experts without rows get zero gradients.  Shape rules of the fp8
+ * path; MOE_ERR_UNSUPPORTED when max(H, F) * ld reaches 2^31 bytes. */
+moe_status moe_ffn_down_bwd_weight_fp8(const moe_shape* s, const uint8_t* dyq_t, const float* dys,
+                                       const uint8_t* hq_t, const float* hs,
+                                       const int32_t* ep_recv_counts, float* grad_w_down,
+                                       void* stream);
+
+/* fp8 moe_ffn_gate_up_bwd_weight: grad_w_gate, grad_w_up (E, F, H) fp32 from
+ * dguq_t/dgus = moe_quant_cols_fp8 of grad_gate_up (D = 2F; rows < F of the
+ * code matrix are the gate columns) and xq_t/xs of expand_x (D = H).
+ * MOE_ERR_UNSUPPORTED when max(2F, H) * ld reaches 2^31 bytes. */
+moe_status moe_ffn_gate_up_bwd_weight_fp8(const moe_shape* s, const uint8_t* dguq_t,
+                                          const float* dgus, const uint8_t* xq_t, const float* xs,
+                                          const int32_t* ep_recv_counts, float* grad_w_gate,
+                                          float* grad_w_up, void* stream);
 
 /* ------------------------------------------------------------------ router
  * The pages take topk_idx and topk_weights as inputs (low_latency_combine page,

@@ -179,3 +179,27 @@ def test_router_rejects_bad_arguments_before_launch(L):
     assert L.moe_router(4, 8, 2, 1, P(), Nn, P(), Nn) == NULL_ARG
     assert L.moe_router_bwd(4, 8, 2, 0, Nn, P(), P(), P(), P(), Nn) == NULL_ARG   # plain gating needs logits
     assert L.moe_router_bwd(4, 4096, 16, 1, P(), P(), P(), P(), Nn, Nn) == NULL_ARG
+
+
+def test_fp8_weight_gradient_entries_reject_bad_arguments_before_launch(L):
+    Nn = None
+    # column quantiser: D a positive multiple of 128, at least one expert, counts given
+    for D in (0, 100, -128):
+        assert L.moe_quant_cols_fp8(256, D, 4, P(), P(), P(), P(), Nn) == BAD_SHAPE
+    assert L.moe_quant_cols_fp8(256, 128, 0, P(), P(), P(), P(), Nn) == BAD_SHAPE
+    assert L.moe_quant_cols_fp8(-1, 128, 4, P(), P(), P(), P(), Nn) == BAD_SHAPE
+    assert L.moe_quant_cols_fp8(256, 128, 4, P(), Nn, P(), P(), Nn) == NULL_ARG
+    assert L.moe_quant_cols_fp8(256, 128, 4, P(), P(), Nn, P(), Nn) == NULL_ARG
+    assert L.moe_quant_cols_fp8(0, 128, 4, Nn, P(), Nn, Nn, Nn) == OK   # nothing to do
+    # GEMMs: the fp8 shape rules (H = 1536, F = 480 is not a multiple of 128)
+    s = ctypes.byref(S())
+    assert L.moe_ffn_down_bwd_weight_fp8(s, *([P()] * 6), Nn) == BAD_SHAPE
+    assert L.moe_ffn_gate_up_bwd_weight_fp8(s, *([P()] * 7), Nn) == BAD_SHAPE
+    s8 = ctypes.byref(S(F=512))
+    assert L.moe_ffn_down_bwd_weight_fp8(s8, P(), P(), P(), P(), Nn, P(), Nn) == NULL_ARG
+    assert L.moe_ffn_gate_up_bwd_weight_fp8(s8, P(), P(), P(), P(), P(), P(), Nn, Nn) == NULL_ARG
+    assert L.moe_ffn_down_bwd_weight_fp8(s8, Nn, P(), P(), P(), P(), P(), Nn) == NULL_ARG
+    # code rows of (capacity/128 + E) * 128 bytes, addressed with 32-bit offsets
+    wide = ctypes.byref(S(T=1 << 16, K=8, num_experts=8, H=4096, F=512))   # 2^19 rows: 4096 * 2^19 > 2^31
+    assert L.moe_ffn_down_bwd_weight_fp8(wide, *([P()] * 6), Nn) == UNSUPPORTED
+    assert L.moe_ffn_gate_up_bwd_weight_fp8(wide, *([P()] * 7), Nn) == UNSUPPORTED

@@ -164,3 +164,110 @@ def test_autograd_layer_fp8_int8_payload():
     for t, k in zip(ws, ("dWg", "dWu", "dWd")):
         # returned in the weights' dtype (bf16)
         check_close(k, f32(t.grad), orc.round_bf16(b[k]), rel_l2=REL_FP8)
+
+
+# ----------------------------------------------------------------------------- fp8 weight gradients
+
+
+def _slot_of(prefix, e, r0):
+    """Token slot of the per-128-token block starting at row r0 of expert e: expert
+    e's slots are numbered from prefix[e-1]/128 + e (the C header's layout)."""
+    start = int(prefix[e - 1]) if e else 0
+    return start // 128 + e + (r0 - start) // 128
+
+
+def test_quant_cols_fp8_bit_exact():
+    rng = np.random.default_rng(41)
+    sizes = [0, 1, 127, 128, 129, 300, 0, 5]
+    prefix = np.cumsum(sizes)
+    A, E, D = int(prefix[-1]), len(sizes), 384
+    cap = A + 37                                  # rows past the experts' rows are not read
+    a = rng.standard_normal((cap, D)).astype(np.float32)
+    a[300:428, 5] = 0.0                           # an all-zero column of one block
+    a[:, 7] *= 1e-4                               # e4m3 subnormals after scaling
+    a[:, 9] *= 3e3
+    a[:, 200:256] *= np.exp(rng.standard_normal((1, 56)) * 3).astype(np.float32)
+    bits = wl.to_bf16_bits(a)
+    counts = torch.from_numpy(prefix.astype(np.int32)).to(DEV)
+    codes_t, scales = dm.quant_cols_fp8(bf(bits), counts)
+    torch.cuda.synchronize()
+    ns = cap // 128 + E
+    assert codes_t.shape == (D, 128 * ns) and scales.shape == (ns, D)
+    ct, sc = _u8(codes_t), scales.cpu().numpy()
+    blocks = orc.quant_cols_fp8(orc.bf16_to_f32(bits)[:A], prefix)
+    assert len(blocks) == 1 + 1 + 1 + 2 + 3 + 1
+    for e, r0, r1, q, s in blocks:
+        sl = _slot_of(prefix, e, r0)
+        n = r1 - r0
+        check_equal(f"codes e={e} r0={r0}", ct[:, sl * 128:sl * 128 + n], q.T)
+        assert not ct[:, sl * 128 + n:(sl + 1) * 128].any(), "rows past the expert's end must be code 0"
+        check_equal(f"scales e={e} r0={r0}", sc[sl], s)
+
+
+WG_CASES = {
+    # expert row counts, H, F
+    "ragged": ([0, 1, 127, 128, 129, 300, 0, 5], 256, 384),
+    "one_long_expert": ([1500], 384, 128),
+    "many_experts": (list(np.random.default_rng(42).integers(0, 260, size=40)), 128, 256),
+    "no_rows": ([0, 0, 0], 128, 128),
+}
+
+
+@pytest.mark.parametrize("name", list(WG_CASES))
+def test_fp8_weight_gradient_gemms(name):
+    """moe_quant_cols_fp8 + the two fp8 weight-gradient GEMMs on seeded bf16
+    operands against the oracle's wgrad_fp8 of the same operands: the codes are
+    bit-exact, so only the accumulation differs (float64 in the oracle; fp32
+    sums inside the fp8 MFMA and across token slots on the GPU, measured at
+    1.3e-5 relative L2 on the ragged case, hence the 1e-4 bar)."""
+    sizes, H, F = WG_CASES[name]
+    print(f"[fp8 wgrad] case={name}", flush=True)
+    prefix = np.cumsum(sizes).astype(np.int64)
+    A, E = int(prefix[-1]), len(sizes)
+    cap = A + 20
+    rng = np.random.default_rng(43)
+    mats = {k: wl.to_bf16_bits((rng.standard_normal((cap, d)) * s).astype(np.float32))
+            for k, d, s in (("dY", H, 0.1), ("h", F, 1.0), ("dGU", 2 * F, 0.05), ("x", H, 1.0))}
+    counts = torch.from_numpy(prefix.astype(np.int32)).to(DEV)
+    shape = dm.make_shape(max(A, 1), H, 1, E, F=F, capacity=cap)
+    q = {k: dm.quant_cols_fp8(bf(v), counts) for k, v in mats.items()}
+    gwd = torch.full((E, H, F), float("nan"), dtype=torch.float32, device=DEV)
+    gwg = torch.full((E, F, H), float("nan"), dtype=torch.float32, device=DEV)
+    gwu = torch.full((E, F, H), float("nan"), dtype=torch.float32, device=DEV)
+    dm.moe_ffn_down_bwd_weight_fp8(shape, *q["dY"], *q["h"], counts, gwd)
+    dm.moe_ffn_gate_up_bwd_weight_fp8(shape, *q["dGU"], *q["x"], counts, gwg, gwu)
+    torch.cuda.synchronize()
+    f = {k: orc.bf16_to_f32(v)[:A] for k, v in mats.items()}
+    ref_d = orc.wgrad_fp8(f["dY"], f["h"], prefix)
+    ref_gu = orc.wgrad_fp8(f["dGU"], f["x"], prefix)
+    check_close("grad_w_down", f32(gwd), ref_d, max_abs=1e-4, rel_l2=1e-4)
+    check_close("grad_w_gate", f32(gwg), ref_gu[:, :F], max_abs=1e-4, rel_l2=1e-4)
+    check_close("grad_w_up", f32(gwu), ref_gu[:, F:], max_abs=1e-4, rel_l2=1e-4)
+
+
+def test_fp8_layer_with_fp8_weight_gradients():
+    """The whole fp8 step with fp8 weight gradients (moe_layer(fp8_wgrad=True))
+    against the oracle's fp8 layer with wgrad='fp8'.
+
+    The weight gradients here quantise the GPU's own dG/dU, h and dY, which differ
+    from the oracle's in the last bf16 bit at a fraction of entries (accumulation
+    order of the GEMMs that produce them).  e4m3 rounding is discontinuous: moving
+    0.1-1% of dG/dU entries by one bf16 ulp moves the fp8 weight gradient of this
+    layer by 1-2% of its largest entry (measured on the oracle alone), so its max|err|
+    bar is 5e-2 of the largest entry; the L2 bar stays the fp8 one, and the GEMMs
+    themselves are held to 1e-4 on identical operands above."""
+    inp = wl.layer_inputs(700, 256, 384, 5, 2, seed=44, mask="2d", C=1)
+    x = bf(inp["x"]).requires_grad_(True)
+    w = dev(inp["topk_weights"]).requires_grad_(True)
+    ws = [bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down")]
+    out = dm.moe_layer(x, dev(inp["topk_idx"]), w, *ws, x_active_mask=dev(inp["mask"]), copy_expert_num=1,
+                       fp8=True, comm_quant_mode=2, fp8_wgrad=True)
+    out.backward(bf(inp["grad_out"]))
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_fp8(inp)
+    b = orc.layer_bwd_fp8(inp, f, inp["grad_out"], wgrad="fp8")
+    check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
+    check_close("grad_x", f32(x.grad), b["dx"], rel_l2=REL_FP8)
+    check_close("grad_topk_weights", f32(w.grad), b["dw"], rel_l2=REL_FP8)
+    for t, k in zip(ws, ("dWg", "dWu", "dWd")):
+        check_close(k, f32(t.grad), orc.round_bf16(b[k]), max_abs=5e-2, rel_l2=REL_FP8)
