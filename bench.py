@@ -52,6 +52,8 @@ WORKLOADS = {
     "page1": dict(T=8192, H=1536, F=480, E=64, K=8),
     "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
+    # the same layer with the weight gradients in fp8 too (per-128-token operands)
+    "mixtral_fp8w": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True, fp8_wgrad=True),
     # combine only: 256 routed + 1 zero + 1 copy + 2 constant experts, 2-D mask
     # with 10% false, shared_expert_x; the step is combine, combine backward and
     # dispatch backward (on the expert-output buffer)
@@ -138,7 +140,7 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
     while True:
         if fp8:
             f = orc.layer_fwd_fp8(inp)
-            orc.layer_bwd_fp8(inp, f, inp["grad_out"])
+            orc.layer_bwd_fp8(inp, f, inp["grad_out"], wgrad="fp8" if cfg.get("fp8_wgrad") else "bf16")
         else:
             f = orc.layer_fwd(inp, prec="parity")
             if not fwd_only:
@@ -260,6 +262,7 @@ def build_step(name, T_override=None):
     dev = torch.device("cuda:0")
     shared = cfg.get("shared", False)
     fp8 = cfg.get("fp8", False)
+    fp8w = fp8 and cfg.get("fp8_wgrad", False)
     log(f"[bench] {name}: generating inputs T={T} H={H} F={F} E={E} K={K}")
     inp = wl.layer_inputs(T, H, F, E, K, seed=0, zipf=cfg.get("zipf"), shared=shared)
     x, gout = _bf(inp["x"], dev), _bf(inp["grad_out"], dev)
@@ -283,7 +286,8 @@ def build_step(name, T_override=None):
     C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
     sy = sdx = None
     if fp8:
-        st.dtype = "fp8 e4m3 (fwd + data grads), bf16 (weight grads)"
+        st.dtype = ("fp8 e4m3 (all six GEMMs; weight grads on per-128-token operands)" if fp8w
+                    else "fp8 e4m3 (fwd + data grads), bf16 (weight grads)")
         nrows = recv[-1:]
         wq = [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)]
         xq, xs = z(cap, H, dt=torch.uint8), z(cap, H // 128, dt=f32)
@@ -298,6 +302,16 @@ def build_step(name, T_override=None):
             ("moe_ffn_down_fwd_fp8", lambda: dm.moe_ffn_down_fwd_fp8(shape, hq, hs, wq[2].codes, wq[2].scales,
                                                                      recv, y)),
         ]
+        if fp8w:
+            # per-128-token codes of the weight-gradient operands, each taken right
+            # after the kernel that wrote its source
+            ns = dm.cols_fp8_slots(cap, E)
+            cq = {k: (z(d, 128 * ns, dt=torch.uint8), z(ns, d, dt=f32))
+                  for k, d in (("x", H), ("h", F), ("dY", H), ("dGU", 2 * F))}
+            i = [n for n, _ in C].index("moe_quant_rows_fp8 (x)")
+            C.insert(i + 1, ("moe_quant_cols_fp8 (x)", lambda: dm.moe_quant_cols_fp8(ex, recv, *cq["x"])))
+            i = [n for n, _ in C].index("moe_ffn_gate_up_fwd_fp8")
+            C.insert(i + 1, ("moe_quant_cols_fp8 (h)", lambda: dm.moe_quant_cols_fp8(h, recv, *cq["h"])))
     else:
         C += [
             ("moe_ffn_gate_up_fwd", lambda: dm.moe_ffn_gate_up_fwd(shape, ex, wg, wu, recv, gus, h)),
@@ -329,13 +343,26 @@ def build_step(name, T_override=None):
     # backward order: each gather/scatter right after the kernel that produced
     # its input (grad_expand_x goes to dispatch backward before the last
     # weight gradient evicts it from the caches)
-    if fp8:
+    if fp8w:
         C += [
             ("moe_quant_rows_fp8 (dY)", lambda: dm.moe_quant_rows_fp8(gy, dyq, dys, nrows)),
-            ("moe_ffn_down_bwd_data_fp8", lambda: dm.moe_ffn_down_bwd_data_fp8(
-                shape, dyq, dys, wq[2].codes_t, wq[2].scales, gus, recv, ggu)),
+            ("moe_quant_cols_fp8 (dY)", lambda: dm.moe_quant_cols_fp8(gy, recv, *cq["dY"])),
+            # dG/dU leave the data gradient as row codes and per-128-token codes
+            # only (nothing else reads them)
+            ("moe_ffn_down_bwd_data_fp8", lambda: dm.moe_ffn_down_bwd_data_fp8_quant(
+                shape, dyq, dys, wq[2].codes_t, wq[2].scales, gus, recv, None, (dgq, dgs), cq["dGU"])),
+            ("moe_ffn_down_bwd_weight_fp8", lambda: dm.moe_ffn_down_bwd_weight_fp8(
+                shape, *cq["dY"], *cq["h"], recv, gwd)),
+            ("moe_ffn_gate_up_bwd_data_fp8", lambda: dm.moe_ffn_gate_up_bwd_data_fp8(
+                shape, dgq, dgs, wq[0].codes_t, wq[0].scales, wq[1].codes_t, wq[1].scales, recv, gxe)),
+        ]
+    elif fp8:
+        C += [
+            ("moe_quant_rows_fp8 (dY)", lambda: dm.moe_quant_rows_fp8(gy, dyq, dys, nrows)),
+            # bf16 dG/dU (for the bf16 weight gradient) and their row codes
+            ("moe_ffn_down_bwd_data_fp8", lambda: dm.moe_ffn_down_bwd_data_fp8_quant(
+                shape, dyq, dys, wq[2].codes_t, wq[2].scales, gus, recv, ggu, (dgq, dgs))),
             ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
-            ("moe_quant_rows_fp8 (dGU)", lambda: dm.moe_quant_rows_fp8(ggu, dgq, dgs, nrows)),
             ("moe_ffn_gate_up_bwd_data_fp8", lambda: dm.moe_ffn_gate_up_bwd_data_fp8(
                 shape, dgq, dgs, wq[0].codes_t, wq[0].scales, wq[1].codes_t, wq[1].scales, recv, gxe)),
         ]
@@ -350,8 +377,12 @@ def build_step(name, T_override=None):
             ss, gout, x, s_gus, s_h, swg, swu, swd, scnt, s_ggu, sdx, *s_gw)))
     C.append(("moe_dispatch_bwd", lambda: dm.moe_dispatch_bwd(shape, gxe, assist, idx, w, None, gout, None, sdx,
                                                               gx)))
-    C.append(("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
-                                                                                  gwu)))
+    if fp8w:
+        C.append(("moe_ffn_gate_up_bwd_weight_fp8", lambda: dm.moe_ffn_gate_up_bwd_weight_fp8(
+            shape, *cq["dGU"], *cq["x"], recv, gwg, gwu)))
+    else:
+        C.append(("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
+                                                                                      gwu)))
     if fp8:
         # weight quantisation (once per weight update) is timed outside the step
         st.extra_calls.insert(0, ("moe_quantize_weights_fp8 (3 tensors)",
@@ -392,14 +423,16 @@ def account(st, A):
               + Q * H * 2 + st.mask_bytes}
         return {}, nb
     fp8 = st.cfg.get("fp8", False)
+    fp8w = fp8 and st.cfg.get("fp8_wgrad", False)
     pk = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    pkw = PEAK_FP8_TFLOPS if fp8w else PEAK_BF16_TFLOPS
     fl = {}
     fwd_only = st.cfg.get("forward_only", False)
     for n, (mult, peak) in {"moe_ffn_gate_up_fwd": (4, pk), "moe_ffn_down_fwd": (2, pk),
-                            "moe_ffn_down_bwd_data": (2, pk), "moe_ffn_down_bwd_weight": (2, PEAK_BF16_TFLOPS),
+                            "moe_ffn_down_bwd_data": (2, pk), "moe_ffn_down_bwd_weight": (2, pkw),
                             "moe_ffn_gate_up_bwd_data": (4, pk),
-                            "moe_ffn_gate_up_bwd_weight": (4, PEAK_BF16_TFLOPS)}.items():
-        key = n + "_fp8" if fp8 and ("fwd" in n or "data" in n) else n
+                            "moe_ffn_gate_up_bwd_weight": (4, pkw)}.items():
+        key = n + "_fp8" if fp8 and ("fwd" in n or "data" in n or fp8w) else n
         if fwd_only and "fwd" not in n:
             continue
         fl[key] = (mult * A * H * F, peak)
@@ -418,7 +451,10 @@ def account(st, A):
         nb["moe_quant_rows_fp8 (x)"] = A * H * 3 + A * H // 128 * 4
         nb["moe_quant_rows_fp8 (h)"] = A * F * 3 + A * F // 128 * 4
         nb["moe_quant_rows_fp8 (dY)"] = A * H * 3 + A * H // 128 * 4
-        nb["moe_quant_rows_fp8 (dGU)"] = A * 2 * F * 3 + A * 2 * F // 128 * 4
+    if fp8w:
+        # bf16 in, codes out, one fp32 scale per (128 tokens, column)
+        for k, d in (("x", H), ("h", F), ("dY", H)):
+            nb[f"moe_quant_cols_fp8 ({k})"] = A * d * 3 + -(-A // 128) * d * 4
     return fl, nb
 
 
@@ -544,6 +580,8 @@ def main():
         "page1": "Triton-distributed benchmark shape",
         "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
+        "mixtral_fp8w": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs including the weight "
+                        "gradients (per-128-token operands), int8 combine payload",
         "combine_stress": "combine only, 256 routed + 1 zero + 1 copy + 2 constant experts, "
                           "2-D mask 10% false, shared_expert_x",
         "decode": "decode batch (the low_latency_combine page's largest BS), forward only",

@@ -35,7 +35,7 @@ ENTRY_POINTS = (
     "moe_quant_rows_fp8", "moe_quantize_weights_fp8", "moe_ffn_gate_up_fwd_fp8",
     "moe_ffn_down_fwd_fp8", "moe_ffn_down_bwd_data_fp8", "moe_ffn_gate_up_bwd_data_fp8",
     "moe_router", "moe_router_bwd", "moe_quant_cols_fp8", "moe_ffn_down_bwd_weight_fp8",
-    "moe_ffn_gate_up_bwd_weight_fp8",
+    "moe_ffn_gate_up_bwd_weight_fp8", "moe_ffn_down_bwd_data_fp8_quant",
 )
 
 
@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
         L.moe_quant_cols_fp8.argtypes = [I64, I64, I32C, P, P, P, P, P]
         L.moe_ffn_down_bwd_weight_fp8.argtypes = [S] + [P] * 7
         L.moe_ffn_gate_up_bwd_weight_fp8.argtypes = [S] + [P] * 8
+        L.moe_ffn_down_bwd_data_fp8_quant.argtypes = [S] + [P] * 12
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
                 getattr(L, name).restype = ctypes.c_int32
@@ -298,6 +299,21 @@ def moe_ffn_down_bwd_data_fp8(shape, dyq, dys, wdq_t, wds, gate_up_save, ep_recv
         _ptr(wds, F32T, "wds"), _ptr(gate_up_save, BF16, "gate_up_save"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_gate_up, BF16, "grad_gate_up"),
         _stream(stream)))
+
+
+def moe_ffn_down_bwd_data_fp8_quant(shape, dyq, dys, wdq_t, wds, gate_up_save, ep_recv_counts,
+                                    grad_gate_up=None, rows=None, cols=None, stream=None):
+    """moe_ffn_down_bwd_data_fp8 writing any of: bf16 grad_gate_up, rows = (codes,
+    scales) of moe_quant_rows_fp8 layout, cols = (codes_t, scales) of
+    moe_quant_cols_fp8 layout."""
+    dguq, dgus = rows if rows is not None else (None, None)
+    dguq_t, dgus_t = cols if cols is not None else (None, None)
+    _check(lib().moe_ffn_down_bwd_data_fp8_quant(
+        ctypes.byref(shape), _ptr(dyq, U8T, "dyq"), _ptr(dys, F32T, "dys"), _ptr(wdq_t, U8T, "wdq_t"),
+        _ptr(wds, F32T, "wds"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_gate_up, BF16, "grad_gate_up"),
+        _ptr(dguq, U8T, "dguq"), _ptr(dgus, F32T, "dgus"), _ptr(dguq_t, U8T, "dguq_t"),
+        _ptr(dgus_t, F32T, "dgus_t"), _stream(stream)))
 
 
 def moe_ffn_gate_up_bwd_data_fp8(shape, dguq, dgus, wgq_t, wgs, wuq_t, wus, ep_recv_counts,
@@ -549,7 +565,9 @@ class _MoELayerFn(torch.autograd.Function):
         gw = torch.empty((T, K), dtype=F32, device=dev)
         moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
                         gy, gw)
-        ggu = torch.empty((cap, 2 * F), dtype=BF16, device=dev)
+        # the fp8 weight gradients need no bf16 dG/dU (its codes come out of the
+        # down data gradient)
+        ggu = None if ctx.fp8_wgrad else torch.empty((cap, 2 * F), dtype=BF16, device=dev)
         gx_exp = torch.empty((cap, H), dtype=BF16, device=dev)
         gwg = torch.empty(w_gate.shape, dtype=F32, device=dev)
         gwu = torch.empty(w_up.shape, dtype=F32, device=dev)
@@ -560,7 +578,15 @@ class _MoELayerFn(torch.autograd.Function):
             (wgt, wgs), (wut, wus), (wdt, wds) = ctx.wq
             nrows = recv[-1:]
             dyq, dys = quant_rows_fp8(gy, nrows)
-            moe_ffn_down_bwd_data_fp8(shape, dyq, dys, wdt, wds, gus, recv, ggu)
+            dgq = torch.empty((cap, 2 * F), dtype=U8T, device=dev)
+            dgs = torch.empty((cap, 2 * F // 128), dtype=F32T, device=dev)
+            if ctx.fp8_wgrad:
+                ns = cols_fp8_slots(cap, shape.num_experts)
+                dg_cols = (torch.empty((2 * F, 128 * ns), dtype=U8T, device=dev),
+                           torch.empty((ns, 2 * F), dtype=F32T, device=dev))
+                moe_ffn_down_bwd_data_fp8_quant(shape, dyq, dys, wdt, wds, gus, recv, None, (dgq, dgs), dg_cols)
+            else:
+                moe_ffn_down_bwd_data_fp8_quant(shape, dyq, dys, wdt, wds, gus, recv, ggu, (dgq, dgs))
             del dyq, dys
             if ctx.fp8_wgrad:
                 dyq_t, dys_t = quant_cols_fp8(gy, recv)
@@ -569,7 +595,6 @@ class _MoELayerFn(torch.autograd.Function):
                 del dyq_t, dys_t, hq_t, hs_t
             else:
                 moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
-            dgq, dgs = quant_rows_fp8(ggu, nrows)
             moe_ffn_gate_up_bwd_data_fp8(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)
             del dgq, dgs
         else:
@@ -594,10 +619,9 @@ class _MoELayerFn(torch.autograd.Function):
         gx = torch.empty((T, H), dtype=BF16, device=dev)
         moe_dispatch_bwd(shape, gx_exp, assist, topk_idx, topk_weights, mask, grad_out, a1, accum, gx)
         if ctx.fp8_wgrad:
-            dgq_t, dgs_t = quant_cols_fp8(ggu, recv)
             xq_t, xs_t = quant_cols_fp8(expand_x, recv)
-            moe_ffn_gate_up_bwd_weight_fp8(shape, dgq_t, dgs_t, xq_t, xs_t, recv, gwg, gwu)
-            del dgq_t, dgs_t, xq_t, xs_t
+            moe_ffn_gate_up_bwd_weight_fp8(shape, *dg_cols, xq_t, xs_t, recv, gwg, gwu)
+            del dg_cols, xq_t, xs_t
         else:
             moe_ffn_gate_up_bwd_weight(shape, ggu, expand_x, recv, gwg, gwu)
         g_shared = grad_out if ctx.has_shared_x else None

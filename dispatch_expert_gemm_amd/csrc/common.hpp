@@ -84,6 +84,21 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
+// Four codes packed into a word (byte i = code of the i-th value), through the
+// hardware conversion (v_cvt_pk_fp8_f32: OCP e4m3 on gfx950, round to nearest
+// even) of the inputs clamped to +-448.  That agrees with f32_to_e4m3 on every
+// one of the 2^32 float inputs except NaN, which the clamp turns into -448
+// (compared exhaustively on MI355X); a word with a NaN input takes
+// f32_to_e4m3.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), (int)w, true);
+  if (a != a || b != b || c != c || d != d)
+    w = f32_to_e4m3(a) | f32_to_e4m3(b) << 8 | f32_to_e4m3(c) << 16 | f32_to_e4m3(d) << 24;
+  return w;
+}
+
 constexpr int kWave = 64;
 
 // ----------------------------------------------------------------------------- host side

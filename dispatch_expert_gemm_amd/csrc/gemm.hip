@@ -96,6 +96,15 @@ struct GemmArgs {
   const float* sB0;
   const float* sB1;
   int64_t sbe, sbn, sbk;
+  // fp8 down data gradient: optional e4m3 codes of the bf16 dG/dU it produces,
+  // per (row, 128 columns) (qr/sr, the layout of moe_quant_rows_fp8) and per
+  // (128-token slot, column) (qc/sc, the layout of moe_quant_cols_fp8, ldq
+  // codes per row)
+  uint8_t* qr;
+  float* sr;
+  uint8_t* qc;
+  float* sc;
+  int64_t ldq;
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
@@ -197,6 +206,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   int64_t row0, n0, kbeg, kend;
   int rows_valid;
   int kseed = 0;  // (row tile + column tile) % 8: staggers the K start, see krot
+  int64_t tile_m = 0;  // row tile (row-grouped GEMMs): with BM = 128, the rows' token slot
   if constexpr (!KGROUP) {
     const int64_t logical = (bid & 7) * (nb >> 3) + (bid >> 3);
     if (logical >= g.tiles) return;
@@ -212,6 +222,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     const int64_t mt = first + rem % gm;
     const int64_t nt = rem / gm;
     kseed = (int)((mt + nt) & 7);
+    tile_m = mt;
     // the expert index is the same in every lane; readfirstlane keeps it (and
     // every address derived from it) in scalar registers
     e = __builtin_amdgcn_readfirstlane(find_expert<BM>(g.prefix, g.E, mt));
@@ -981,8 +992,85 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
           *reinterpret_cast<uint2*>(tu + o) = pack4(du[0], du[1], du[2], du[3]);
         }
     __syncthreads();
-    store_tile(tg, g.C0 + n0, 2 * g.F, g.N - n0);
-    store_tile(tu, g.C0 + g.F + n0, 2 * g.F, g.N - n0);
+    if (g.C0) {
+      store_tile(tg, g.C0 + n0, 2 * g.F, g.N - n0);
+      store_tile(tu, g.C0 + g.F + n0, 2 * g.F, g.N - n0);
+    }
+    if constexpr (FP8) {
+      // e4m3 codes of the staged bf16 dG/dU (the values the bf16 output holds),
+      // same rule as the quantiser kernels: F is a multiple of 128 and the tile
+      // is 128 x 128, so its dG (dU) columns are one whole 128-column block of
+      // every row, and its rows one whole 128-token slot (slot = row tile).
+      static_assert(BN == 128 && BM == 128 && kThreads == 256, "one block per row, one slot per tile");
+      if (g.qr) {
+        // rows: 16 lanes per (row, block), 8 columns each
+        const int sub = tid & 15;
+        for (int p = tid >> 4; p < 2 * BM; p += kThreads / 16) {
+          const int row = p >> 1, half = p & 1;
+          if (row >= rows_valid) continue;  // the same for the 16 lanes of a group
+          float f[8];
+          unpack8(*reinterpret_cast<const uint4*>((half ? tu : tg) + row * CP + sub * 8), f);
+          float amax = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+#pragma unroll
+          for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+          const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+          const uint32_t lo = e4m3x4(__fmul_rn(f[0], inv), __fmul_rn(f[1], inv), __fmul_rn(f[2], inv),
+                                     __fmul_rn(f[3], inv));
+          const uint32_t hi = e4m3x4(__fmul_rn(f[4], inv), __fmul_rn(f[5], inv), __fmul_rn(f[6], inv),
+                                     __fmul_rn(f[7], inv));
+          const int64_t col = (half ? g.F : 0) + n0;
+          *reinterpret_cast<uint2*>(g.qr + (row0 + row) * 2 * g.F + col + sub * 8) = make_uint2(lo, hi);
+          if (sub == 0) g.sr[(row0 + row) * (2 * g.F / 128) + col / 128] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+        }
+      }
+      if (g.qc) {
+        // columns: thread t owns the column pair 2 (t%128), +1 of [dG | dU]
+        // over rows 64 (t/128) .. +63 (read once into registers as bf16
+        // pairs); the two row halves meet through a small LDS array, rows past
+        // the expert's end get code 0
+        const int pr = tid & 127, rh = tid >> 7;
+        const bf16_t* cs = (pr < BN / 2 ? tg : tu) + 2 * (pr & (BN / 2 - 1)) + rh * 64 * CP;
+        uint32_t pv[64];
+        float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+          pv[i] = rh * 64 + i < rows_valid ? *reinterpret_cast<const uint32_t*>(cs + i * CP) : 0u;
+          m0 = fmaxf(m0, fabsf(bf2f(pv[i] & 0xffffu)));
+          m1 = fmaxf(m1, fabsf(bf2f(pv[i] >> 16)));
+        }
+        __shared__ float part[2 * kThreads];
+        part[2 * tid] = m0;
+        part[2 * tid + 1] = m1;
+        __syncthreads();
+        m0 = fmaxf(m0, part[2 * (tid ^ 128)]);
+        m1 = fmaxf(m1, part[2 * (tid ^ 128) + 1]);
+        const float inv0 = m0 > 0.f ? __fdiv_rn(448.0f, m0) : 0.f;
+        const float inv1 = m1 > 0.f ? __fdiv_rn(448.0f, m1) : 0.f;
+        const int64_t col = (pr < BN / 2 ? 0 : g.F) + n0 + 2 * (pr & (BN / 2 - 1));
+        uint8_t* d0 = g.qc + col * g.ldq + tile_m * 128 + rh * 64;
+        uint8_t* d1 = d0 + g.ldq;
+#pragma unroll
+        for (int r0 = 0; r0 < 64; r0 += 16) {
+          uint32_t w0[4], w1[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = r0 + 4 * q;
+            w0[q] = e4m3x4(__fmul_rn(bf2f(pv[i] & 0xffffu), inv0), __fmul_rn(bf2f(pv[i + 1] & 0xffffu), inv0),
+                           __fmul_rn(bf2f(pv[i + 2] & 0xffffu), inv0), __fmul_rn(bf2f(pv[i + 3] & 0xffffu), inv0));
+            w1[q] = e4m3x4(__fmul_rn(bf2f(pv[i] >> 16), inv1), __fmul_rn(bf2f(pv[i + 1] >> 16), inv1),
+                           __fmul_rn(bf2f(pv[i + 2] >> 16), inv1), __fmul_rn(bf2f(pv[i + 3] >> 16), inv1));
+          }
+          *reinterpret_cast<uint4*>(d0 + r0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+          *reinterpret_cast<uint4*>(d1 + r0) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        }
+        if (rh == 0) {
+          g.sc[tile_m * 2 * g.F + col] = m0 > 0.f ? __fdiv_rn(m0, 448.0f) : 1.0f;
+          g.sc[tile_m * 2 * g.F + col + 1] = m1 > 0.f ? __fdiv_rn(m1, 448.0f) : 1.0f;
+        }
+      }
+    }
   } else {
     // weight gradients, fp32: 16-byte stores of four consecutive columns
     // (N is a multiple of 8, so a run is either wholly inside or outside)
@@ -1351,6 +1439,42 @@ extern "C" moe_status moe_ffn_down_bwd_data_fp8(const moe_shape* s, const uint8_
   g.Kd = s->H;
   g.aux = static_cast<const bf16_t*>(gate_up_save);
   g.C0 = static_cast<bf16_t*>(grad_gate_up);
+  return launch<DOWN_BWD_DATA, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_down_bwd_data_fp8_quant(const moe_shape* s, const uint8_t* dyq,
+                                                      const float* dys, const uint8_t* wdq_t,
+                                                      const float* wds, const void* gate_up_save,
+                                                      const int32_t* ep_recv_counts, void* grad_gate_up,
+                                                      uint8_t* dguq, float* dgus, uint8_t* dguq_t,
+                                                      float* dgus_t, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wdq_t || !wds || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (!grad_gate_up && !dguq && !dguq_t) return MOE_ERR_NULL_ARG;  // nothing to produce
+  if (!dguq != !dgus || !dguq_t != !dgus_t) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!dyq || !dys || !gate_up_save) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = dyq;
+  g.sA = dys;
+  g.lda = s->H;
+  g.qB0 = wdq_t;
+  g.sB0 = wds;
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.sbe = (s->H / 128) * (s->F / 128);
+  g.sbn = 1;
+  g.sbk = s->F / 128;
+  g.N = s->F;
+  g.Kd = s->H;
+  g.aux = static_cast<const bf16_t*>(gate_up_save);
+  g.C0 = static_cast<bf16_t*>(grad_gate_up);
+  g.qr = dguq;
+  g.sr = dgus;
+  g.qc = dguq_t;
+  g.sc = dgus_t;
+  g.ldq = 128 * (s->capacity / 128 + s->num_experts);
   return launch<DOWN_BWD_DATA, true>(g, s, as_stream(stream));
 }
 

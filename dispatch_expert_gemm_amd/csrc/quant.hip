@@ -61,11 +61,8 @@ __global__ __launch_bounds__(256) void k_quant_rows_fp8(const uint4* __restrict_
     for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
     if (row >= rows) continue;
     const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lo |= f32_to_e4m3(__fmul_rn(f[q], inv)) << (8 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hi |= f32_to_e4m3(__fmul_rn(f[4 + q], inv)) << (8 * q);
+    const uint32_t lo = e4m3x4(__fmul_rn(f[0], inv), __fmul_rn(f[1], inv), __fmul_rn(f[2], inv), __fmul_rn(f[3], inv));
+    const uint32_t hi = e4m3x4(__fmul_rn(f[4], inv), __fmul_rn(f[5], inv), __fmul_rn(f[6], inv), __fmul_rn(f[7], inv));
     codes[row * (C / 8) + blk * 16 + sub] = make_uint2(lo, hi);
     if (sub == 0) scales[row * nb + blk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
   }
@@ -118,11 +115,10 @@ __global__ __launch_bounds__(256) void k_quant_cols_fp8(const uint4* __restrict_
     const int col = 8 * c + q;
     const float amax = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
     const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(__fmul_rn(v[i][q], inv)) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(__fmul_rn(v[4 + i][q], inv)) << (8 * i);
+    const uint32_t lo = e4m3x4(__fmul_rn(v[0][q], inv), __fmul_rn(v[1][q], inv), __fmul_rn(v[2][q], inv),
+                               __fmul_rn(v[3][q], inv));
+    const uint32_t hi = e4m3x4(__fmul_rn(v[4][q], inv), __fmul_rn(v[5][q], inv), __fmul_rn(v[6][q], inv),
+                               __fmul_rn(v[7][q], inv));
     *reinterpret_cast<uint2*>(ct + col * 144 + 8 * rg) = make_uint2(lo, hi);
     if (rg == 0) scales[slot * D + cb * 128 + col] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
   }
@@ -168,15 +164,13 @@ __global__ __launch_bounds__(256) void k_quant_weights_fp8(const uint4* __restri
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (tid >> 4) + 16 * j;
-    uint32_t b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = f32_to_e4m3(__fmul_rn(f[j][i], inv));
-    const uint2 pk = make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                                b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+    const uint2 pk = make_uint2(
+        e4m3x4(__fmul_rn(f[j][0], inv), __fmul_rn(f[j][1], inv), __fmul_rn(f[j][2], inv), __fmul_rn(f[j][3], inv)),
+        e4m3x4(__fmul_rn(f[j][4], inv), __fmul_rn(f[j][5], inv), __fmul_rn(f[j][6], inv), __fmul_rn(f[j][7], inv)));
     *reinterpret_cast<uint2*>(codes + (e * N + n0 + r) * Kd + k0 + c8) = pk;
     if (codes_t) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) tr[(c8 + i) * 144 + r] = (uint8_t)b[i];
+      for (int i = 0; i < 8; ++i) tr[(c8 + i) * 144 + r] = (uint8_t)((i < 4 ? pk.x : pk.y) >> (8 * (i & 3)));
     }
   }
   if (tid == 0) scales[(e * nbn + bn) * nbk + bk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;

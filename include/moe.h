@@ -303,6 +303,21 @@ moe_status moe_ffn_down_bwd_data_fp8(const moe_shape* s, const uint8_t* dyq, con
                                      const void* gate_up_save, const int32_t* ep_recv_counts,
                                      void* grad_gate_up, void* stream);
 
+/* moe_ffn_down_bwd_data_fp8 with the quantisation of its output fused in: the
+ * same dG/dU, rounded to bf16, written as any of
+ *   grad_gate_up (capacity, 2F) bf16               (optional),
+ *   dguq (capacity, 2F) / dgus (capacity, 2F/128)  = moe_quant_rows_fp8 of it
+ *                                                    for rows < ep_recv_counts[E-1],
+ *   dguq_t (2F, ld) / dgus_t (slots, 2F)           = moe_quant_cols_fp8 of it
+ * (each code/scale pair given together or not at all; at least one output,
+ * else MOE_ERR_NULL_ARG).  Bit-identical to running the quantisers on
+ * grad_gate_up.  The fp8 weight-gradient path needs no bf16 dG/dU at all. */
+moe_status moe_ffn_down_bwd_data_fp8_quant(const moe_shape* s, const uint8_t* dyq, const float* dys,
+                                           const uint8_t* wdq_t, const float* wds,
+                                           const void* gate_up_save, const int32_t* ep_recv_counts,
+                                           void* grad_gate_up, uint8_t* dguq, float* dgus,
+                                           uint8_t* dguq_t, float* dgus_t, void* stream);
+
 /* fp8 moe_ffn_gate_up_bwd_data: dguq/dgus = moe_quant_rows_fp8 of grad_gate_up
  * (capacity, 2F); wgq_t/wuq_t = transposed codes of w_gate, w_up (E, H, F). */
 moe_status moe_ffn_gate_up_bwd_data_fp8(const moe_shape* s, const uint8_t* dguq,

@@ -203,3 +203,16 @@ def test_fp8_weight_gradient_entries_reject_bad_arguments_before_launch(L):
     wide = ctypes.byref(S(T=1 << 16, K=8, num_experts=8, H=4096, F=512))   # 2^19 rows: 4096 * 2^19 > 2^31
     assert L.moe_ffn_down_bwd_weight_fp8(wide, *([P()] * 6), Nn) == UNSUPPORTED
     assert L.moe_ffn_gate_up_bwd_weight_fp8(wide, *([P()] * 7), Nn) == UNSUPPORTED
+
+
+def test_fused_quantising_data_gradient_rejects_bad_arguments(L):
+    Nn = None
+    s8 = ctypes.byref(S(F=512))
+    args = [P()] * 6   # dyq, dys, wdq_t, wds, gate_up_save, ep_recv_counts
+    # nothing to produce
+    assert L.moe_ffn_down_bwd_data_fp8_quant(s8, *args, Nn, Nn, Nn, Nn, Nn, Nn) == NULL_ARG
+    # codes without scales (and the reverse)
+    assert L.moe_ffn_down_bwd_data_fp8_quant(s8, *args, Nn, P(), Nn, Nn, Nn, Nn) == NULL_ARG
+    assert L.moe_ffn_down_bwd_data_fp8_quant(s8, *args, Nn, Nn, Nn, Nn, P(), Nn) == NULL_ARG
+    # fp8 shape rules
+    assert L.moe_ffn_down_bwd_data_fp8_quant(ctypes.byref(S()), *args, P(), Nn, Nn, Nn, Nn, Nn) == BAD_SHAPE

@@ -271,3 +271,54 @@ def test_fp8_layer_with_fp8_weight_gradients():
     check_close("grad_topk_weights", f32(w.grad), b["dw"], rel_l2=REL_FP8)
     for t, k in zip(ws, ("dWg", "dWu", "dWd")):
         check_close(k, f32(t.grad), orc.round_bf16(b[k]), max_abs=5e-2, rel_l2=REL_FP8)
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES))
+def test_fused_quantisation_of_the_down_data_gradient(name):
+    """moe_ffn_down_bwd_data_fp8_quant: its bf16 dG/dU equal the unfused entry's,
+    and its row and per-128-token codes equal the quantiser kernels run on that
+    output (both quantisers are bit-exact against the oracle's above)."""
+    inp = wl.layer_inputs(seed=45, **FP8_CASES[name])
+    print(f"[fp8 fused quant] case={name}", flush=True)
+    run = Fp8Run(inp)
+    run.dispatch()
+    run.quant_weights()
+    run.ffn8()
+    F, H, E, cap = inp["F"], inp["H"], inp["E"], run.cap
+    recv = run.d.ep_recv_counts
+    nrows = recv[-1:]
+    gy = bf(wl.to_bf16_bits(np.random.default_rng(46).standard_normal((cap, H), dtype=np.float32) * 0.125))
+    dyq, dys = dm.quant_rows_fp8(gy, nrows)
+    wd = run.wq[2]
+    ggu = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+    dm.moe_ffn_down_bwd_data_fp8(run.shape, dyq, dys, wd.codes_t, wd.scales, run.gus, recv, ggu)
+    rows_ref = dm.quant_rows_fp8(ggu, nrows)
+    cols_ref = dm.quant_cols_fp8(ggu, recv)
+    ns = dm.cols_fp8_slots(cap, E)
+    ggu2 = torch.empty_like(ggu)
+    rows = (torch.empty((cap, 2 * F), dtype=torch.uint8, device=DEV),
+            torch.empty((cap, 2 * F // 128), dtype=torch.float32, device=DEV))
+    cols = (torch.empty((2 * F, 128 * ns), dtype=torch.uint8, device=DEV),
+            torch.empty((ns, 2 * F), dtype=torch.float32, device=DEV))
+    dm.moe_ffn_down_bwd_data_fp8_quant(run.shape, dyq, dys, wd.codes_t, wd.scales, run.gus, recv, ggu2,
+                                       rows, cols)
+    # codes only (the fp8 weight-gradient path): no bf16 output
+    cols3 = (torch.empty_like(cols[0]), torch.empty_like(cols[1]))
+    dm.moe_ffn_down_bwd_data_fp8_quant(run.shape, dyq, dys, wd.codes_t, wd.scales, run.gus, recv, None,
+                                       None, cols3)
+    torch.cuda.synchronize()
+    prefix = recv.cpu().numpy().astype(np.int64)
+    A = int(prefix[-1])
+    check_equal("grad_gate_up", _u8(ggu2.view(torch.uint8))[:A], _u8(ggu.view(torch.uint8))[:A])
+    check_equal("row codes", _u8(rows[0])[:A], _u8(rows_ref[0])[:A])
+    check_equal("row scales", rows[1].cpu().numpy()[:A], rows_ref[1].cpu().numpy()[:A])
+    lo = 0
+    for e in range(E):
+        hi = int(prefix[e])
+        for r0 in range(lo, hi, 128):
+            sl = _slot_of(prefix, e, r0)
+            for got in (cols, cols3):
+                check_equal(f"col codes e={e} slot={sl}", _u8(got[0])[:, sl * 128:(sl + 1) * 128],
+                            _u8(cols_ref[0])[:, sl * 128:(sl + 1) * 128])
+                check_equal(f"col scales e={e} slot={sl}", got[1].cpu().numpy()[sl], cols_ref[1].cpu().numpy()[sl])
+        lo = hi
