@@ -310,8 +310,10 @@ def build_step(name, T_override=None):
                   for k, d in (("x", H), ("h", F), ("dY", H), ("dGU", 2 * F))}
             i = [n for n, _ in C].index("moe_quant_rows_fp8 (x)")
             C.insert(i + 1, ("moe_quant_cols_fp8 (x)", lambda: dm.moe_quant_cols_fp8(ex, recv, *cq["x"])))
+            # h's codes come out of the gate/up GEMM itself
             i = [n for n, _ in C].index("moe_ffn_gate_up_fwd_fp8")
-            C.insert(i + 1, ("moe_quant_cols_fp8 (h)", lambda: dm.moe_quant_cols_fp8(h, recv, *cq["h"])))
+            C[i] = ("moe_ffn_gate_up_fwd_fp8", lambda: dm.moe_ffn_gate_up_fwd_fp8_quant(
+                shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h, *cq["h"]))
     else:
         C += [
             ("moe_ffn_gate_up_fwd", lambda: dm.moe_ffn_gate_up_fwd(shape, ex, wg, wu, recv, gus, h)),
@@ -453,7 +455,7 @@ def account(st, A):
         nb["moe_quant_rows_fp8 (dY)"] = A * H * 3 + A * H // 128 * 4
     if fp8w:
         # bf16 in, codes out, one fp32 scale per (128 tokens, column)
-        for k, d in (("x", H), ("h", F), ("dY", H)):
+        for k, d in (("x", H), ("dY", H)):
             nb[f"moe_quant_cols_fp8 ({k})"] = A * d * 3 + -(-A // 128) * d * 4
     return fl, nb
 

@@ -35,7 +35,7 @@ ENTRY_POINTS = (
     "moe_quant_rows_fp8", "moe_quantize_weights_fp8", "moe_ffn_gate_up_fwd_fp8",
     "moe_ffn_down_fwd_fp8", "moe_ffn_down_bwd_data_fp8", "moe_ffn_gate_up_bwd_data_fp8",
     "moe_router", "moe_router_bwd", "moe_quant_cols_fp8", "moe_ffn_down_bwd_weight_fp8",
-    "moe_ffn_gate_up_bwd_weight_fp8", "moe_ffn_down_bwd_data_fp8_quant",
+    "moe_ffn_gate_up_bwd_weight_fp8", "moe_ffn_down_bwd_data_fp8_quant", "moe_ffn_gate_up_fwd_fp8_quant",
 )
 
 
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_down_bwd_weight_fp8.argtypes = [S] + [P] * 7
         L.moe_ffn_gate_up_bwd_weight_fp8.argtypes = [S] + [P] * 8
         L.moe_ffn_down_bwd_data_fp8_quant.argtypes = [S] + [P] * 12
+        L.moe_ffn_gate_up_fwd_fp8_quant.argtypes = [S] + [P] * 12
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
                 getattr(L, name).restype = ctypes.c_int32
@@ -283,6 +284,15 @@ def moe_ffn_gate_up_fwd_fp8(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, g
         _ptr(wgs, F32T, "wgs"), _ptr(wuq, U8T, "wuq"), _ptr(wus, F32T, "wus"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(gate_up_save, BF16, "gate_up_save"),
         _ptr(h_act, BF16, "h_act"), _stream(stream)))
+
+
+def moe_ffn_gate_up_fwd_fp8_quant(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act,
+                                  hq_t, hs_t, stream=None):
+    _check(lib().moe_ffn_gate_up_fwd_fp8_quant(
+        ctypes.byref(shape), _ptr(xq, U8T, "xq"), _ptr(xs, F32T, "xs"), _ptr(wgq, U8T, "wgq"),
+        _ptr(wgs, F32T, "wgs"), _ptr(wuq, U8T, "wuq"), _ptr(wus, F32T, "wus"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(h_act, BF16, "h_act"), _ptr(hq_t, U8T, "hq_t"), _ptr(hs_t, F32T, "hs_t"), _stream(stream)))
 
 
 def moe_ffn_down_fwd_fp8(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
@@ -517,8 +527,17 @@ class _MoELayerFn(torch.autograd.Function):
             nrows = d.ep_recv_counts[-1:]
             wq = tuple(Fp8Weights.quantize(w) for w in (w_gate, w_up, w_down))
             xq, xs = quant_rows_fp8(d.expand_x, nrows)
-            moe_ffn_gate_up_fwd_fp8(shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales,
-                                    d.ep_recv_counts, gus, h)
+            if ctx.fp8_wgrad:
+                # h's per-128-token codes for the weight gradient come out of the GEMM
+                ns = cols_fp8_slots(cap, E)
+                h_cols = (torch.empty((F, 128 * ns), dtype=U8T, device=dev),
+                          torch.empty((ns, F), dtype=F32T, device=dev))
+                moe_ffn_gate_up_fwd_fp8_quant(shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes,
+                                              wq[1].scales, d.ep_recv_counts, gus, h, *h_cols)
+                ctx.h_cols = h_cols
+            else:
+                moe_ffn_gate_up_fwd_fp8(shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales,
+                                        d.ep_recv_counts, gus, h)
             hq, hs = quant_rows_fp8(h, nrows)
             moe_ffn_down_fwd_fp8(shape, hq, hs, wq[2].codes, wq[2].scales, d.ep_recv_counts, y)
             del xq, xs, hq, hs
@@ -590,9 +609,9 @@ class _MoELayerFn(torch.autograd.Function):
             del dyq, dys
             if ctx.fp8_wgrad:
                 dyq_t, dys_t = quant_cols_fp8(gy, recv)
-                hq_t, hs_t = quant_cols_fp8(h, recv)
-                moe_ffn_down_bwd_weight_fp8(shape, dyq_t, dys_t, hq_t, hs_t, recv, gwd)
-                del dyq_t, dys_t, hq_t, hs_t
+                moe_ffn_down_bwd_weight_fp8(shape, dyq_t, dys_t, *ctx.h_cols, recv, gwd)
+                del dyq_t, dys_t
+                ctx.h_cols = None
             else:
                 moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
             moe_ffn_gate_up_bwd_data_fp8(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)

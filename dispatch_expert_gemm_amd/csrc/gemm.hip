@@ -943,6 +943,52 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     store_tile(th, g.C0 + n0, g.F, g.F - n0);
     store_tile_nt(tg, g.C1 + n0, 2 * g.F, g.F - n0);
     store_tile_nt(tu, g.C1 + g.F + n0, 2 * g.F, g.F - n0);
+    if constexpr (FP8) {
+      if (g.qc) {
+        // per-128-token e4m3 codes of the staged bf16 h (the tile's rows are
+        // one token slot): thread t takes the column pair 2 (t%32), +1 over
+        // rows 16 (t/32) .. +15; the eight row parts meet through LDS
+        static_assert(BM == 128 && BN == 128 && kThreads == 256, "one slot, 64 h columns per tile");
+        const int pr = tid & 31, rq = tid >> 5;
+        uint32_t pv[16];
+        float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = rq * 16 + i;
+          pv[i] = r < rows_valid ? *reinterpret_cast<const uint32_t*>(th + r * CP + 2 * pr) : 0u;
+          m0 = fmaxf(m0, fabsf(bf2f(pv[i] & 0xffffu)));
+          m1 = fmaxf(m1, fabsf(bf2f(pv[i] >> 16)));
+        }
+        __shared__ float part[8][64];
+        part[rq][2 * pr] = m0;
+        part[rq][2 * pr + 1] = m1;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          m0 = fmaxf(m0, part[q][2 * pr]);
+          m1 = fmaxf(m1, part[q][2 * pr + 1]);
+        }
+        const float inv0 = m0 > 0.f ? __fdiv_rn(448.0f, m0) : 0.f;
+        const float inv1 = m1 > 0.f ? __fdiv_rn(448.0f, m1) : 0.f;
+        uint32_t w0[4], w1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t* v = pv + 4 * q;
+          w0[q] = e4m3x4(__fmul_rn(bf2f(v[0] & 0xffffu), inv0), __fmul_rn(bf2f(v[1] & 0xffffu), inv0),
+                         __fmul_rn(bf2f(v[2] & 0xffffu), inv0), __fmul_rn(bf2f(v[3] & 0xffffu), inv0));
+          w1[q] = e4m3x4(__fmul_rn(bf2f(v[0] >> 16), inv1), __fmul_rn(bf2f(v[1] >> 16), inv1),
+                         __fmul_rn(bf2f(v[2] >> 16), inv1), __fmul_rn(bf2f(v[3] >> 16), inv1));
+        }
+        const int64_t col = n0 + 2 * pr;
+        uint8_t* d0 = g.qc + col * g.ldq + tile_m * 128 + rq * 16;
+        *reinterpret_cast<uint4*>(d0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+        *reinterpret_cast<uint4*>(d0 + g.ldq) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        if (rq == 0) {
+          g.sc[tile_m * g.F + col] = m0 > 0.f ? __fdiv_rn(m0, 448.0f) : 1.0f;
+          g.sc[tile_m * g.F + col + 1] = m1 > 0.f ? __fdiv_rn(m1, 448.0f) : 1.0f;
+        }
+      }
+    }
   } else if constexpr (MODE == DOWN_FWD || MODE == GATE_UP_BWD_DATA) {
     bf16_t* ct = smem;
 #pragma unroll
@@ -1386,6 +1432,40 @@ extern "C" moe_status moe_ffn_gate_up_fwd_fp8(const moe_shape* s, const uint8_t*
   g.Kd = s->H;
   g.C0 = static_cast<bf16_t*>(h_act);
   g.C1 = static_cast<bf16_t*>(gate_up_save);
+  return launch<GATE_UP_FWD, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_gate_up_fwd_fp8_quant(const moe_shape* s, const uint8_t* xq,
+                                                    const float* xs, const uint8_t* wgq,
+                                                    const float* wgs, const uint8_t* wuq,
+                                                    const float* wus, const int32_t* ep_recv_counts,
+                                                    void* gate_up_save, void* h_act, uint8_t* hq_t,
+                                                    float* hs_t, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wgq || !wgs || !wuq || !wus || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!xq || !xs || !gate_up_save || !h_act || !hq_t || !hs_t) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = xq;
+  g.sA = xs;
+  g.lda = s->H;
+  g.qB0 = wgq;
+  g.qB1 = wuq;
+  g.sB0 = wgs;
+  g.sB1 = wus;
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.sbe = (s->F / 128) * (s->H / 128);
+  g.sbn = s->H / 128;
+  g.sbk = 1;
+  g.N = s->F;
+  g.Kd = s->H;
+  g.C0 = static_cast<bf16_t*>(h_act);
+  g.C1 = static_cast<bf16_t*>(gate_up_save);
+  g.qc = hq_t;
+  g.sc = hs_t;
+  g.ldq = 128 * (s->capacity / 128 + s->num_experts);
   return launch<GATE_UP_FWD, true>(g, s, as_stream(stream));
 }
 

@@ -290,6 +290,15 @@ moe_status moe_ffn_gate_up_fwd_fp8(const moe_shape* s, const uint8_t* xq, const 
                                    const float* wus, const int32_t* ep_recv_counts,
                                    void* gate_up_save, void* h_act, void* stream);
 
+/* moe_ffn_gate_up_fwd_fp8 that also writes the per-128-token e4m3 codes of the
+ * h_act it produces: hq_t (F, ld) / hs_t (slots, F), bit-identical to
+ * moe_quant_cols_fp8 of h_act (the fp8 weight-gradient operand). */
+moe_status moe_ffn_gate_up_fwd_fp8_quant(const moe_shape* s, const uint8_t* xq, const float* xs,
+                                         const uint8_t* wgq, const float* wgs, const uint8_t* wuq,
+                                         const float* wus, const int32_t* ep_recv_counts,
+                                         void* gate_up_save, void* h_act, uint8_t* hq_t, float* hs_t,
+                                         void* stream);
+
 /* fp8 moe_ffn_down_fwd: hq/hs = moe_quant_rows_fp8 of h_act (capacity, F);
  * wdq/wds = moe_quantize_weights_fp8 of w_down.  y in bf16. */
 moe_status moe_ffn_down_fwd_fp8(const moe_shape* s, const uint8_t* hq, const float* hs,

@@ -322,3 +322,69 @@ def test_fused_quantisation_of_the_down_data_gradient(name):
                             _u8(cols_ref[0])[:, sl * 128:(sl + 1) * 128])
                 check_equal(f"col scales e={e} slot={sl}", got[1].cpu().numpy()[sl], cols_ref[1].cpu().numpy()[sl])
         lo = hi
+
+
+def test_quant_rows_fp8_every_bf16_value():
+    """Every finite bf16 value through moe_quant_rows_fp8, bit-exact against the
+    oracle's e4m3 rule: values sorted by magnitude, 127 per block plus one anchor
+    448 * 2^k >= the block's largest magnitude, so x * (448/amax) = x / 2^k is exact
+    and the codes are e4m3(x / 2^k) over the whole bf16 range."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = orc.bf16_to_f32(bits)
+    keep = np.isfinite(vals)
+    bits, vals = bits[keep], vals[keep]
+    order = np.argsort(np.abs(vals), kind="stable")
+    bits, vals = bits[order], vals[order]
+    nb = -(-len(bits) // 127)
+    pad = nb * 127 - len(bits)
+    bits = np.concatenate([bits, np.zeros(pad, np.uint16)]).reshape(nb, 127)
+    vals = np.concatenate([vals, np.zeros(pad, np.float32)]).reshape(nb, 127)
+    top = np.abs(vals).max(axis=1).astype(np.float64)
+    k = np.ceil(np.log2(np.maximum(top, 1e-300) / 448.0)).clip(-120, None)
+    anchor = 448.0 * np.exp2(k)
+    # the last blocks reach past 448 * 2^119: their anchor is the largest bf16
+    anchor = np.where(anchor > 3.3895313892515355e38, 3.3895313892515355e38, anchor).astype(np.float32)
+    assert np.all(np.isfinite(anchor)) and np.all(anchor >= top)
+    rows = np.concatenate([orc.f32_to_bf16(anchor)[:, None], bits], axis=1)   # (nb, 128) bf16 bits
+    codes, scales = dm.quant_rows_fp8(bf(rows))
+    torch.cuda.synchronize()
+    q, s = orc.quant_e4m3_rows(orc.bf16_to_f32(rows))
+    check_equal("codes", _u8(codes), q)
+    check_equal("scales", scales.cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES))
+def test_fused_quantisation_of_h_in_the_gate_up_forward(name):
+    """moe_ffn_gate_up_fwd_fp8_quant: G, U and h equal the plain entry's, and its
+    per-128-token codes of h equal moe_quant_cols_fp8 run on that h."""
+    inp = wl.layer_inputs(seed=47, **FP8_CASES[name])
+    print(f"[fp8 fused h quant] case={name}", flush=True)
+    run = Fp8Run(inp)
+    run.dispatch()
+    run.quant_weights()
+    run.ffn8()
+    F, E, cap = inp["F"], inp["E"], run.cap
+    recv = run.d.ep_recv_counts
+    wg, wu, _ = run.wq
+    gus = torch.empty_like(run.gus)
+    h = torch.empty_like(run.h)
+    ns = dm.cols_fp8_slots(cap, E)
+    hq_t = torch.empty((F, 128 * ns), dtype=torch.uint8, device=DEV)
+    hs_t = torch.empty((ns, F), dtype=torch.float32, device=DEV)
+    dm.moe_ffn_gate_up_fwd_fp8_quant(run.shape, run.xq, run.xs, wg.codes, wg.scales, wu.codes, wu.scales, recv,
+                                     gus, h, hq_t, hs_t)
+    ref_q, ref_s = dm.quant_cols_fp8(run.h, recv)
+    torch.cuda.synchronize()
+    prefix = recv.cpu().numpy().astype(np.int64)
+    A = int(prefix[-1])
+    check_equal("gate_up_save", _u8(gus.view(torch.uint8))[:A], _u8(run.gus.view(torch.uint8))[:A])
+    check_equal("h", _u8(h.view(torch.uint8))[:A], _u8(run.h.view(torch.uint8))[:A])
+    lo = 0
+    for e in range(E):
+        hi = int(prefix[e])
+        for r0 in range(lo, hi, 128):
+            sl = _slot_of(prefix, e, r0)
+            check_equal(f"h col codes e={e} slot={sl}", _u8(hq_t)[:, sl * 128:(sl + 1) * 128],
+                        _u8(ref_q)[:, sl * 128:(sl + 1) * 128])
+            check_equal(f"h col scales e={e} slot={sl}", hs_t.cpu().numpy()[sl], ref_s.cpu().numpy()[sl])
+        lo = hi
