@@ -582,3 +582,84 @@ def layer_bwd_fp8(inp: dict, fwd: dict, grad_out, wgrad="bf16"):
                                          *fwd["wq"], wgrad=wgrad)
     dx = dispatch_bwd(dX, r, inp["topk_weights"], grad_out, inp.get("const_alpha_1"), None, "parity")
     return dict(dY=dY, dw=dw, dGU=dGU, dX=dX, dWg=dWg, dWu=dWu, dWd=dWd, dx=dx)
+
+
+# ============================================================================ int8 dispatch + w8a8 FFN
+#
+# Readings (low_latency_dispatch as used on the low_latency_combine page, example
+# programs: quant_mode 2 is "dynamic quantization", dispatch then returns an int8
+# expand_x with dynamic_scales, and an optional fp32 scales tensor of shape
+# (num_experts, H) may be passed; the page gives no formula, so these are ours):
+#  * every expanded row (token t sent to routed expert e) is x_t times scales[e]
+#    (elementwise, float32; no product without scales), quantised per row with the
+#    int8 rule of the combine payload: codes clamp(rint(v * (127/amax)), -127, 127),
+#    dynamic scale amax/127 (an all-zero row: codes 0, scale 1);
+#  * the grouped FFN on those rows (not on the pages; the decode-regime consumer of
+#    an int8 expand_x): int8 weights with one scale per output channel (row of the
+#    (out, in) matrix, same rule), integer products summed exactly, times (row scale
+#    x channel scale); G, U, h, y stored as bf16; h requantised per row (same rule)
+#    for the down projection.
+
+
+def dispatch_int8(x, r: Route, smooth_scales=None):
+    """int8 expand_x (A, H) and dynamic_scales (A,) of the routed rows, in row order."""
+    X = dispatch(x, r, "parity").astype(np.float32)
+    if smooth_scales is not None:
+        S = np.asarray(smooth_scales, np.float32)
+        experts = np.repeat(np.arange(len(r.ep_recv_counts)), np.diff(np.concatenate([[0], r.ep_recv_counts])))
+        X = (X * S[experts]).astype(np.float32)
+    if X.shape[0] == 0:
+        return np.zeros(X.shape, np.int8), np.zeros(0, np.float32)
+    return quant_int8_rows(X)
+
+
+def quant_weights_int8(w_bits):
+    """(E, N, K) bf16 weights -> (codes (E, N, K) int8, scales (E, N) fp32), one scale per
+    output channel."""
+    W = decode(w_bits, "parity")
+    qs = [quant_int8_rows(W[e]) for e in range(W.shape[0])]
+    return np.stack([q for q, _ in qs]), np.stack([s for _, s in qs])
+
+
+def _i8_gemm(q_rows, s_rows, q_w, s_w):
+    """(q_rows @ q_w^T) exactly in integers, times (row scale x channel scale), float64."""
+    acc = q_rows.astype(np.int64) @ q_w.astype(np.int64).T
+    return acc.astype(np.float64) * s_rows.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :]
+
+
+def ffn_fwd_int8(Xq, xs, ep_recv_counts, wq_gate, wq_up, wq_down):
+    """w8a8 forward of the grouped SwiGLU FFN on int8 expanded rows (parity mode).
+    Returns G, U, h (bf16 values), the int8 codes/scales of h, and y (bf16 values)."""
+    st = _store("parity")
+    (gq, gs), (uq, us), (dq, ds) = wq_gate, wq_up, wq_down
+    A, E = Xq.shape[0], gq.shape[0]
+    F, H = gq.shape[1], dq.shape[1]
+    G, U, Hh = (np.zeros((A, F), np.float32) for _ in range(3))
+    Y = np.zeros((A, H), np.float32)
+    hq, hs = np.zeros((A, F), np.int8), np.ones(A, np.float32)
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        if hi > lo:
+            g = _i8_gemm(Xq[lo:hi], xs[lo:hi], gq[e], gs[e])
+            u = _i8_gemm(Xq[lo:hi], xs[lo:hi], uq[e], us[e])
+            h = st(silu(g) * u)
+            G[lo:hi], U[lo:hi], Hh[lo:hi] = st(g), st(u), h
+            hq[lo:hi], hs[lo:hi] = quant_int8_rows(h)
+            Y[lo:hi] = st(_i8_gemm(hq[lo:hi], hs[lo:hi], dq[e], ds[e]))
+        lo = hi
+    return G, U, Hh, hq, hs, Y
+
+
+def layer_fwd_int8(inp: dict, smooth_scales=None):
+    """Decode-regime forward: int8 dispatch (optionally smooth-scaled), w8a8 FFN,
+    bf16 combine (parity mode)."""
+    E = inp["E"]
+    Z, C, Q = inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0)
+    r = route(inp["topk_idx"], E, Z, C, Q, inp.get("mask"))
+    Xq, xs = dispatch_int8(inp["x"], r, smooth_scales)
+    wq = tuple(quant_weights_int8(inp[k]) for k in ("w_gate", "w_up", "w_down"))
+    G, U, Hh, hq, hs, Y = ffn_fwd_int8(Xq, xs, r.ep_recv_counts, *wq)
+    out = combine(Y, r, inp["topk_weights"], inp.get("shared_expert_x"), inp["x"],
+                  inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), "parity")
+    return dict(route=r, Xq=Xq, xs=xs, wq=wq, G=G, U=U, Hh=Hh, hq=hq, hs=hs, Y=Y, out=out)

@@ -604,3 +604,75 @@ def test_router_backward_matches_torch_autograd_and_finite_differences(renorm):
         mask = np.ones_like(dl, dtype=bool)
         np.put_along_axis(mask, idx.astype(np.int64), False, axis=1)
         assert (dl[mask] == 0).all()
+
+
+# ============================================================================ int8 dispatch + w8a8 FFN
+
+
+def test_int8_dispatch_hand_example():
+    """One token routed to expert 1 of 2, H = 8, smooth scales chosen by hand:
+    x * scales[1] = [3, -3, 2, 0, 0, 0, 0, 2], amax 3, so the codes are
+    rint(v * 127/3) = [127, -127, 85, 0, 0, 0, 0, 85] and the scale 3/127."""
+    x = np.array([[3, -6, 1, 0, 0, 0, 0, 0.5]], np.float32)
+    S = np.ones((2, 8), np.float32)
+    S[1] = [1, 0.5, 2, 1, 1, 1, 1, 4]
+    r = orc.route(np.array([[1]], np.int32), 2)
+    q, s = orc.dispatch_int8(orc.f32_to_bf16(x), r, S)
+    assert q.tolist() == [[127, -127, 85, 0, 0, 0, 0, 85]]
+    assert s.tolist() == [np.float32(3.0) / np.float32(127.0)]
+    # without smooth scales: amax 6, codes rint(v * 127/6)
+    q, s = orc.dispatch_int8(orc.f32_to_bf16(x), r)
+    assert q.tolist() == [[64, -127, 21, 0, 0, 0, 0, 11]] and s.tolist() == [np.float32(6.0) / np.float32(127.0)]
+
+
+def test_int8_dispatch_uses_each_rows_own_expert_scales():
+    """Integer rows with a +-127 entry are exact in int8; expert e's smooth scale
+    2^e then leaves the codes unchanged and makes the row's dynamic scale exactly
+    2^e, which names the scale row each expanded row used."""
+    rng = np.random.default_rng(51)
+    T, H, E, K = 40, 64, 5, 3
+    x = rng.integers(-127, 128, size=(T, H)).astype(np.float32)
+    x[:, 7] = 127.0
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    r = orc.route(idx, E)
+    q0, s0 = orc.dispatch_int8(orc.f32_to_bf16(x), r)
+    X = orc.dispatch(orc.f32_to_bf16(x), r)
+    assert np.array_equal(q0.astype(np.float32), X) and np.all(s0 == 1.0)
+    S = np.exp2(np.arange(E, dtype=np.float32))[:, None] * np.ones((E, H), np.float32)
+    q1, s1 = orc.dispatch_int8(orc.f32_to_bf16(x), r, S)
+    assert np.array_equal(q1, q0)
+    row_expert = np.repeat(np.arange(E), np.diff(np.concatenate([[0], r.ep_recv_counts])))
+    assert np.array_equal(s1, np.exp2(row_expert).astype(np.float32))
+
+
+def test_int8_ffn_lossless_inputs_reproduce_bf16_gate_up():
+    """Integer activations and weights with a +-127 per row and channel quantise
+    exactly (scale 1); the integer products are exact in fp32 too, so G, U and h of
+    the w8a8 FFN equal the bf16 FFN's bit for bit."""
+    rng = np.random.default_rng(52)
+    E, F, H, A = 3, 64, 128, 50
+    X = rng.integers(-127, 128, size=(A, H)).astype(np.float32)
+    X[:, 3] = -127.0
+    def w(n, k):
+        a = rng.integers(-127, 128, size=(E, n, k)).astype(np.float32)
+        a[:, :, 5] = 127.0
+        return a
+    Wg, Wu, Wd = w(F, H), w(F, H), w(H, F)
+    counts = np.array([10, 10, 50])
+    wq = tuple(orc.quant_weights_int8(orc.f32_to_bf16(a)) for a in (Wg, Wu, Wd))
+    assert np.array_equal(wq[0][0].astype(np.float32), Wg) and np.all(wq[0][1] == 1.0)
+    Xq, xs = orc.quant_int8_rows(X)
+    assert np.array_equal(Xq.astype(np.float32), X) and np.all(xs == 1.0)
+    G8, U8, H8, hq, hs, Y8 = orc.ffn_fwd_int8(Xq, xs, counts, *wq)
+    G, U, Hh, Y = orc.ffn_fwd(X, counts, *(orc.f32_to_bf16(a) for a in (Wg, Wu, Wd)), prec="parity")
+    assert np.array_equal(G8, G) and np.array_equal(U8, U) and np.array_equal(H8, Hh)
+    assert np.array_equal(orc.dequant_int8_rows(hq, hs)[10:], orc.qdq_rows_int8(Hh[10:]))
+    assert 0 < np.linalg.norm(Y8 - Y) / np.linalg.norm(Y) < 0.02
+
+
+def test_int8_layer_close_to_bf16_layer():
+    inp = wl.layer_inputs(96, 256, 128, 6, 2, seed=53, Z=1, C=1)
+    f8 = orc.layer_fwd_int8(inp)
+    f = orc.layer_fwd(inp, prec="parity")
+    rel = np.linalg.norm(f8["out"] - f["out"]) / np.linalg.norm(f["out"])
+    assert 1e-3 < rel < 0.05
