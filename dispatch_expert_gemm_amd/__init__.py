@@ -36,6 +36,7 @@ ENTRY_POINTS = (
     "moe_ffn_down_fwd_fp8", "moe_ffn_down_bwd_data_fp8", "moe_ffn_gate_up_bwd_data_fp8",
     "moe_router", "moe_router_bwd", "moe_quant_cols_fp8", "moe_ffn_down_bwd_weight_fp8",
     "moe_ffn_gate_up_bwd_weight_fp8", "moe_ffn_down_bwd_data_fp8_quant", "moe_ffn_gate_up_fwd_fp8_quant",
+    "moe_dispatch_int8", "moe_quant_rows_int8", "moe_ffn_gate_up_fwd_int8", "moe_ffn_down_fwd_int8",
 )
 
 
@@ -103,6 +104,10 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_gate_up_bwd_weight_fp8.argtypes = [S] + [P] * 8
         L.moe_ffn_down_bwd_data_fp8_quant.argtypes = [S] + [P] * 12
         L.moe_ffn_gate_up_fwd_fp8_quant.argtypes = [S] + [P] * 12
+        L.moe_dispatch_int8.argtypes = [S] + [P] * 11 + [ctypes.c_size_t, P]
+        L.moe_quant_rows_int8.argtypes = [I64, I64, P, P, P, P, P]
+        L.moe_ffn_gate_up_fwd_int8.argtypes = [S] + [P] * 10
+        L.moe_ffn_down_fwd_int8.argtypes = [S] + [P] * 7
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
                 getattr(L, name).restype = ctypes.c_int32
@@ -363,6 +368,54 @@ def moe_ffn_gate_up_bwd_weight_fp8(shape, dguq_t, dgus, xq_t, xs, ep_recv_counts
         _ptr(grad_w_gate, F32T, "grad_w_gate"), _ptr(grad_w_up, F32T, "grad_w_up"), _stream(stream)))
 
 
+I8T = torch.int8
+
+
+def moe_dispatch_int8(shape, x, topk_idx, x_active_mask, smooth_scales, expand_x, dynamic_scales,
+                      assist_info_for_combine, expert_token_nums, ep_recv_counts, err_flag, workspace,
+                      stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().moe_dispatch_int8(
+        ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(x_active_mask, U8, "x_active_mask"), _ptr(smooth_scales, F32, "smooth_scales"),
+        _ptr(expand_x, I8T, "expand_x"), _ptr(dynamic_scales, F32, "dynamic_scales"),
+        _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
+        _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(err_flag, I32, "err_flag"), _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream)))
+
+
+def moe_quant_rows_int8(src, codes, scales, nrows=None, stream=None):
+    C = src.shape[-1]
+    R = src.numel() // C
+    _check(lib().moe_quant_rows_int8(R, C, _ptr(src, BF16, "src"), _ptr(nrows, I32, "nrows"),
+                                     _ptr(codes, I8T, "codes"), _ptr(scales, F32, "scales"), _stream(stream)))
+
+
+def moe_ffn_gate_up_fwd_int8(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act,
+                             stream=None):
+    _check(lib().moe_ffn_gate_up_fwd_int8(
+        ctypes.byref(shape), _ptr(xq, I8T, "xq"), _ptr(xs, F32, "xs"), _ptr(wgq, I8T, "wgq"),
+        _ptr(wgs, F32, "wgs"), _ptr(wuq, I8T, "wuq"), _ptr(wus, F32, "wus"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(h_act, BF16, "h_act"), _stream(stream)))
+
+
+def moe_ffn_down_fwd_int8(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
+    _check(lib().moe_ffn_down_fwd_int8(
+        ctypes.byref(shape), _ptr(hq, I8T, "hq"), _ptr(hs, F32, "hs"), _ptr(wdq, I8T, "wdq"),
+        _ptr(wds, F32, "wds"), _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"),
+        _stream(stream)))
+
+
+def quant_rows_int8(src, nrows=None, stream=None):
+    """Per-row int8 codes (same shape as src) and scales (src.shape[:-1]) of a bf16 tensor;
+    (E, N, K) weights give one scale per output channel."""
+    codes = torch.empty(src.shape, dtype=I8T, device=src.device)
+    scales = torch.empty(src.shape[:-1], dtype=F32, device=src.device)
+    moe_quant_rows_int8(src, codes, scales, nrows, stream)
+    return codes, scales
+
+
 def moe_router(logits, K, renorm, topk_idx, topk_weights, stream=None):
     T, n = logits.shape
     _check(lib().moe_router(T, n, int(K), int(bool(renorm)), _ptr(logits, F32, "logits"),
@@ -480,6 +533,26 @@ def dispatch(shape, x, topk_idx, x_active_mask=None, workspace=None, stream=None
     moe_dispatch(shape, x, topk_idx, mask, d.expand_x, d.assist_info_for_combine,
                  d.expert_token_nums, d.ep_recv_counts, d.err_flag, workspace, stream)
     return d
+
+
+def dispatch_int8(shape, x, topk_idx, x_active_mask=None, smooth_scales=None, workspace=None, stream=None):
+    """Allocate the outputs with torch and run moe_dispatch_int8: (DispatchOut with an
+    int8 expand_x, dynamic_scales (capacity,) fp32)."""
+    dev = x.device
+    d = DispatchOut(
+        expand_x=torch.empty((shape.capacity, shape.H), dtype=I8T, device=dev),
+        assist_info_for_combine=torch.empty(moe_assist_info_size(shape), dtype=I32, device=dev),
+        expert_token_nums=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        ep_recv_counts=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        err_flag=torch.empty(1, dtype=I32, device=dev))
+    dyn = torch.empty(shape.capacity, dtype=F32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    mask = x_active_mask.view(torch.uint8) if x_active_mask is not None and x_active_mask.dtype == torch.bool \
+        else x_active_mask
+    moe_dispatch_int8(shape, x, topk_idx, mask, smooth_scales, d.expand_x, dyn, d.assist_info_for_combine,
+                      d.expert_token_nums, d.ep_recv_counts, d.err_flag, workspace, stream)
+    return d, dyn
 
 
 def shared_expert_shape(T, H, F) -> MoeShape:

@@ -99,6 +99,19 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return w;
 }
 
+// Four int8 codes packed into a word: clamp(rint(v * inv), -127, 127) each (the
+// product rounded to fp32 first, ties to even), byte i = the i-th value.
+__device__ __forceinline__ uint32_t i8x4(float a, float b, float c, float d, float inv) {
+  auto q = [inv](float v) { return (uint32_t)(int)fminf(fmaxf(rintf(__fmul_rn(v, inv)), -127.0f), 127.0f) & 0xffu; };
+  return q(a) | q(b) << 8 | q(c) << 16 | q(d) << 24;
+}
+
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 constexpr int kWave = 64;
 
 // ----------------------------------------------------------------------------- host side

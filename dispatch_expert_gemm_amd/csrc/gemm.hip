@@ -169,10 +169,14 @@ struct Cfg {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <int MODE, int BM, int BN, bool FP8, int BK, int S_, int WM_, int WN_>
+// I8 (with FP8 set: the 8-bit operand path): int8 codes with one scale per A
+// row and one per B row (output channel), integer MFMAs accumulated over the
+// whole K, the scales applied once after the loop.
+template <int MODE, int BM, int BN, bool FP8, int BK, int S_, int WM_, int WN_, bool I8>
 __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads),
                              (Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kMinBlocks)) void k_gemm(GemmArgs g) {
   using C = Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>;
+  static_assert(!I8 || (FP8 && (MODE == GATE_UP_FWD || MODE == DOWN_FWD)), "int8: forward GEMMs on the 8-bit path");
   auto swz = [](int r) { return swzw<BK>(r); };
   auto lds_off = [](int r, int c) { return lds_offw<BK>(r, c); };
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
@@ -416,6 +420,28 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     constexpr int st = decltype(ST)::value;
     const bf16_t* as = As(st);
     const bf16_t* bs = Bs(st);
+    if constexpr (I8) {
+      // four 32x32x32 int8 MFMAs per 128-code step; lane l supplies the 16
+      // codes of chunk 2 kk + l/32 of its row (the same K split for A and B,
+      // which is all a dot product needs)
+      typedef int i32x16 __attribute__((ext_vector_type(16)));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int c = kk * 2 + (lane >> 5);
+        i32x4 fa[TI], fb[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) fa[i] = *reinterpret_cast<const i32x4*>(as + lds_offw<64>(arow[i], c));
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) fb[j] = *reinterpret_cast<const i32x4*>(bs + lds_offw<64>(brw[j], c));
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_bit_cast(
+                f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], __builtin_bit_cast(i32x16, acc[i][j]), 0, 0, 0));
+      }
+      return;
+    } else {
     f32x16 tmp[TI][TJ];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -483,11 +509,12 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
           for (int r = 0; r < 16; ++r) acc[i][j][r] += tmp[i][j][r] * f;
         }
     }
+    }
   };
   // K steps: 128-wide blocks of K, or the expert's token slots
   const int64_t nk = KGROUP ? (klen + 127) / 128 : g.Kd / 128;
   // B block scales of every K step, read once before the pipeline starts
-  if constexpr (!KGROUP)
+  if constexpr (!KGROUP && !I8)
     for (int64_t kb = tid; kb < nk; kb += kThreads) {
       sBl[0][kb] = bscale(kb * 128, 0);
       if (MODE == GATE_UP_FWD) sBl[1][kb] = bscale(kb * 128, 1);
@@ -500,19 +527,48 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     asm volatile("" ::: "memory");
     if (kt + 1 < nk) {
       issue8(std::integral_constant<int, st ^ 1>(), kt + 1);
-      issue_scales(std::integral_constant<int, st ^ 1>(), kt + 1);
+      if constexpr (!I8) issue_scales(std::integral_constant<int, st ^ 1>(), kt + 1);
     }
     compute8(ST, kt);
   };
   if (nk > 0) {
     issue8(std::integral_constant<int, 0>(), 0);
-    issue_scales(std::integral_constant<int, 0>(), 0);
+    if constexpr (!I8) issue_scales(std::integral_constant<int, 0>(), 0);
   }
   for (int64_t kt = 0; kt < nk; kt += 2) {
     kstep8(std::integral_constant<int, 0>(), kt);
     if (kt + 1 < nk) kstep8(std::integral_constant<int, 1>(), kt + 1);
   }
   __syncthreads();
+  if constexpr (I8) {
+    // integer sums times (A row scale x B channel scale): B tile row rb is
+    // channel n0 + rb (gate/up: rows BN/2.. are the up matrix's channels
+    // n0 + rb - BN/2); a lane's four consecutive rows rb share a float4 of scales
+    typedef int i32x16 __attribute__((ext_vector_type(16)));
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int m = wm * (BM / WM) + i * 32 + (lane & 31);
+      const float sa = g.sA[row0 + (m < rows_valid ? m : rows_valid - 1)];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const i32x16 ai = __builtin_bit_cast(i32x16, acc[i][j]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int rb = brow(j) + 8 * t + 4 * (lane >> 5);
+          float4 sb;
+          if constexpr (MODE == GATE_UP_FWD)
+            sb = *reinterpret_cast<const float4*>((rb >= BN / 2 ? g.sB1 : g.sB0) + (int64_t)e * g.F + n0 +
+                                                  (rb & (BN / 2 - 1)));
+          else
+            sb = *reinterpret_cast<const float4*>(g.sB0 + (int64_t)e * g.N + n0 + rb);
+          acc[i][j][4 * t + 0] = (float)ai[4 * t + 0] * (sa * sb.x);
+          acc[i][j][4 * t + 1] = (float)ai[4 * t + 1] * (sa * sb.y);
+          acc[i][j][4 * t + 2] = (float)ai[4 * t + 2] * (sa * sb.z);
+          acc[i][j][4 * t + 3] = (float)ai[4 * t + 3] * (sa * sb.w);
+        }
+      }
+    }
+  }
   } else {
   // Operand tiles go from memory straight into LDS (buffer loads with an LDS
   // destination: lane l of one instruction writes the 16 bytes at
@@ -1144,7 +1200,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   }
 }
 
-template <int MODE, int BM, int BN, bool FP8, int BK = 64, int S = 2, int WM = 2, int WN = 2>
+template <int MODE, int BM, int BN, bool FP8, int BK = 64, int S = 2, int WM = 2, int WN = 2, bool I8 = false>
 moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
   const int64_t bn_cols = MODE == GATE_UP_FWD ? BN / 2 : BN;
@@ -1179,12 +1235,12 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;  // weight gradients: already 8 * E * block
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8, BK, S, WM, WN>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8, BK, S, WM, WN, I8>), dim3((unsigned)grid),
                      dim3(Cfg<MODE, BM, BN, FP8, BK, S, WM, WN>::kThreads), 0, strm, g);
   return launch_status();
 }
 
-template <int MODE, bool FP8 = false>
+template <int MODE, bool FP8 = false, bool I8 = false>
 moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // Tile shapes per GEMM kind, chosen by measurement on MI355X (MoE layers at
   // H = 1536 / F = 480 and H = 7168 / F = 2048): 128 x 256 tiles (wave tiles
@@ -1199,7 +1255,9 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // 256 x 256 tiles lost for the backward GEMMs: the SwiGLU backward epilogue
   // runs four wave-column passes, and the weight gradients get too few tiles
   // per expert block.
-  if constexpr (FP8) {
+  if constexpr (I8) {
+    return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, true>(g, s, strm);
+  } else if constexpr (FP8) {
     return launch_cfg<MODE, 128, 128, true>(g, s, strm);
   } else if constexpr (MODE == GATE_UP_BWD_DATA || MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W) {
     return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
@@ -1645,4 +1703,54 @@ extern "C" moe_status moe_ffn_gate_up_bwd_weight_fp8(const moe_shape* s, const u
   g.W0 = grad_w_gate;
   g.W1 = grad_w_up;
   return launch<GATE_UP_BWD_W, true>(g, s, as_stream(stream));
+}
+
+// ----------------------------------------------------------------------------- int8 entries
+
+extern "C" moe_status moe_ffn_gate_up_fwd_int8(const moe_shape* s, const int8_t* xq, const float* xs,
+                                               const int8_t* wgq, const float* wgs, const int8_t* wuq,
+                                               const float* wus, const int32_t* ep_recv_counts,
+                                               void* gate_up_save, void* h_act, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wgq || !wgs || !wuq || !wus || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!xq || !xs || !gate_up_save || !h_act) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = reinterpret_cast<const uint8_t*>(xq);
+  g.sA = xs;  // one scale per row
+  g.lda = s->H;
+  g.qB0 = reinterpret_cast<const uint8_t*>(wgq);
+  g.qB1 = reinterpret_cast<const uint8_t*>(wuq);
+  g.sB0 = wgs;  // (E, F): one scale per output channel
+  g.sB1 = wus;
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.N = s->F;
+  g.Kd = s->H;
+  g.C0 = static_cast<bf16_t*>(h_act);
+  g.C1 = static_cast<bf16_t*>(gate_up_save);
+  return launch<GATE_UP_FWD, true, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_down_fwd_int8(const moe_shape* s, const int8_t* hq, const float* hs,
+                                            const int8_t* wdq, const float* wds,
+                                            const int32_t* ep_recv_counts, void* y, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wdq || !wds || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!hq || !hs || !y) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = reinterpret_cast<const uint8_t*>(hq);
+  g.sA = hs;
+  g.lda = s->F;
+  g.qB0 = reinterpret_cast<const uint8_t*>(wdq);
+  g.sB0 = wds;  // (E, H)
+  g.ldb = s->F;
+  g.bstride = s->H * s->F;
+  g.N = s->H;
+  g.Kd = s->F;
+  g.C0 = static_cast<bf16_t*>(y);
+  return launch<DOWN_FWD, true, true>(g, s, as_stream(stream));
 }

@@ -185,6 +185,37 @@ __global__ __launch_bounds__(256) void k_quant_weights_fp8(const uint4* __restri
   }
 }
 
+// int8 rows (the per-token requantisation of h on the int8 path, and int8
+// weights with one scale per output channel): one wave per row, an amax pass
+// and a code pass over 16-byte vectors, codes clamp(rint(v * (127/amax)),
+// -127, 127), scale amax/127 (all-zero: codes 0, scale 1).
+__global__ __launch_bounds__(256) void k_quant_rows_int8(const uint4* __restrict__ src, int64_t R, int64_t C,
+                                                         const int32_t* __restrict__ nrows,
+                                                         uint2* __restrict__ codes, float* __restrict__ scales) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+  int64_t rows = nrows ? (int64_t)*nrows : R;
+  if (rows > R) rows = R;
+  if (r >= rows) return;  // a whole wave leaves together
+  const int64_t Cv = C / 8;
+  const uint4* row = src + r * Cv;
+  float m = 0.f;
+  for (int64_t v = lane; v < Cv; v += 64) {
+    float f[8];
+    unpack8(row[v], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  }
+  m = wave_max64(m);
+  const float inv = m > 0.f ? __fdiv_rn(127.0f, m) : 0.f;
+  for (int64_t v = lane; v < Cv; v += 64) {
+    float f[8];
+    unpack8(row[v], f);
+    codes[r * Cv + v] = make_uint2(i8x4(f[0], f[1], f[2], f[3], inv), i8x4(f[4], f[5], f[6], f[7], inv));
+  }
+  if (lane == 0) scales[r] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -231,5 +262,17 @@ extern "C" moe_status moe_quantize_weights_fp8(int64_t E, int64_t N, int64_t Kdi
   if (blocks > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(k_quant_weights_fp8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const uint4*>(w), N, Kdim, codes, codes_t, scales);
+  return launch_status();
+}
+
+extern "C" moe_status moe_quant_rows_int8(int64_t R, int64_t C, const void* src, const int32_t* nrows,
+                                          int8_t* codes, float* scales, void* stream) {
+  if (R < 0 || C <= 0 || C % 8 != 0 || R * C >= ((int64_t)1 << 40)) return MOE_ERR_BAD_SHAPE;
+  if (R == 0) return MOE_OK;
+  if (!src || !codes || !scales) return MOE_ERR_NULL_ARG;
+  const int64_t blocks = (R + 3) / 4;
+  if (blocks > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(k_quant_rows_int8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(src), R, C, nrows, reinterpret_cast<uint2*>(codes), scales);
   return launch_status();
 }

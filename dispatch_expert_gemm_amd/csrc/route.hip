@@ -245,6 +245,83 @@ __global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x,
   }
 }
 
+// int8 dispatch (quant_mode 2): one wave per token, the row's NV 16-byte
+// vectors per lane kept in registers (H <= 64 * 8 * NV).  Each destination row
+// is x (times the smooth-scale row of its expert, when given) quantised with
+// one dynamic scale: codes clamp(rint(v * (127/amax)), -127, 127), scale
+// amax/127 (all-zero: codes 0, scale 1).  Without smooth scales every
+// destination row of a token holds the same codes, computed once.
+template <int NV>
+__global__ __launch_bounds__(256) void k_permute_i8(const uint4* __restrict__ x, const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ slot2row, int64_t T, int K,
+                                                    int64_t Hv, const float* __restrict__ smooth,
+                                                    uint2* __restrict__ exq, float* __restrict__ dyn) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (t >= T) return;
+  const int my = lane < K ? slot2row[t * K + lane] : -1;
+  const int myid = lane < K ? idx[t * K + lane] : 0;
+  // the token's row stays packed (4 registers per 8 values)
+  uint4 xr[NV];
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int64_t v = lane + (int64_t)q * kWave;
+    xr[q] = v < Hv ? x[t * Hv + v] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // the 8 values of vector q, times the smooth-scale row sr when given
+  auto vals = [&](int q, const float4* sr, float (&f)[8]) {
+    unpack8(xr[q], f);
+    if (sr) {
+      const int64_t v = lane + (int64_t)q * kWave;
+      const float4 s0 = sr[2 * v], s1 = sr[2 * v + 1];
+      f[0] = __fmul_rn(f[0], s0.x); f[1] = __fmul_rn(f[1], s0.y);
+      f[2] = __fmul_rn(f[2], s0.z); f[3] = __fmul_rn(f[3], s0.w);
+      f[4] = __fmul_rn(f[4], s1.x); f[5] = __fmul_rn(f[5], s1.y);
+      f[6] = __fmul_rn(f[6], s1.z); f[7] = __fmul_rn(f[7], s1.w);
+    }
+  };
+  float m0 = 0.f;  // amax of the plain row (shared by all rows without smooth scales)
+  if (!smooth) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      float f[8];
+      unpack8(xr[q], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m0 = fmaxf(m0, fabsf(f[i]));
+    }
+    m0 = wave_max64(m0);
+  }
+  for (int k = 0; k < K; ++k) {
+    const int row = __builtin_amdgcn_readlane(my, k);
+    if (row < 0) continue;  // the same in every lane
+    const float4* sr = nullptr;
+    float m = m0;
+    if (smooth) {
+      sr = reinterpret_cast<const float4*>(smooth + (int64_t)__builtin_amdgcn_readlane(myid, k) * Hv * 8);
+      m = 0.f;
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        if (lane + (int64_t)q * kWave >= Hv) continue;
+        float f[8];
+        vals(q, sr, f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+      }
+      m = wave_max64(m);
+    }
+    const float inv = m > 0.f ? __fdiv_rn(127.0f, m) : 0.f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int64_t v = lane + (int64_t)q * kWave;
+      if (v >= Hv) continue;
+      float f[8];
+      vals(q, sr, f);
+      exq[(int64_t)row * Hv + v] = make_uint2(i8x4(f[0], f[1], f[2], f[3], inv), i8x4(f[4], f[5], f[6], f[7], inv));
+    }
+    if (lane == 0) dyn[row] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
+  }
+}
+
 struct RouteGeom {
   int64_t nslots;
   int R;
@@ -302,25 +379,28 @@ extern "C" moe_status moe_workspace_size(const moe_shape* s, size_t* bytes) {
   return MOE_OK;
 }
 
-extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
-                                   const uint8_t* x_active_mask, void* expand_x,
-                                   int32_t* assist, int32_t* expert_token_nums,
-                                   int32_t* ep_recv_counts, int32_t* err_flag, void* workspace,
-                                   size_t ws_bytes, void* stream) {
-  moe_status st = check_shape(s);
-  if (st != MOE_OK) return st;
+namespace {
+// argument checks shared by the two dispatch entries (the expanded-row buffer is
+// checked by each)
+moe_status check_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                          const uint8_t* x_active_mask, int32_t* assist, int32_t* expert_token_nums,
+                          int32_t* ep_recv_counts, int32_t* err_flag, void* workspace, size_t ws_bytes) {
   const int64_t TK = s->T * s->K;
   MOE_NEED(x, s->T * s->H);
   MOE_NEED(topk_idx, TK);
   MOE_NEED(x_active_mask, s->mask_ndim == 0 ? 0 : (s->mask_ndim == 1 ? s->T : TK));
-  MOE_NEED(expand_x, s->capacity * s->H);
   MOE_NEED(assist, TK + s->capacity);
   if (!expert_token_nums || !ep_recv_counts || !err_flag) return MOE_ERR_NULL_ARG;
   const size_t need = route_ws_bytes(s);
   if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
 
+// the routing kernels of both dispatch entries: counts, scan, rank (maps)
+void launch_route(const moe_shape* s, const int32_t* topk_idx, const uint8_t* x_active_mask,
+                  int32_t* assist, int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                  int32_t* err_flag, void* workspace, hipStream_t strm) {
   const RouteGeom g = route_geom(s);
-  hipStream_t strm = as_stream(stream);
   RouteArgs a{topk_idx, x_active_mask, s->T, s->K, s->num_experts, s->zero_expert_num,
               s->copy_expert_num, s->const_expert_num, s->mask_ndim};
   int32_t* hist = static_cast<int32_t*>(workspace);
@@ -342,12 +422,65 @@ extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int3
     hipLaunchKernelGGL(k_route_rank, dim3(blocks), dim3(256), lds, strm, a, hist, g.nslots,
                        g.nchunks, g.R, nbits, slot2row, row2slot);
   }
+}
+}  // namespace
+
+extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                                   const uint8_t* x_active_mask, void* expand_x,
+                                   int32_t* assist, int32_t* expert_token_nums,
+                                   int32_t* ep_recv_counts, int32_t* err_flag, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_dispatch(s, x, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
+                      workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  MOE_NEED(expand_x, s->capacity * s->H);
+  hipStream_t strm = as_stream(stream);
+  launch_route(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag, workspace, strm);
+  const int32_t* slot2row = assist;
   if (s->T > 0) {
     const int split = token_split(s->H / 8, s->K);
     const int64_t pb = (s->T * split + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(k_permute, dim3((unsigned)pb), dim3(256), 0, strm,
                        static_cast<const uint4*>(x), slot2row, s->T, s->K, s->H / 8, split,
                        static_cast<uint4*>(expand_x));
+  }
+  return launch_status();
+}
+
+extern "C" moe_status moe_dispatch_int8(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                                        const uint8_t* x_active_mask, const float* smooth_scales,
+                                        int8_t* expand_x, float* dynamic_scales, int32_t* assist,
+                                        int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                                        int32_t* err_flag, void* workspace, size_t ws_bytes,
+                                        void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  // the row lives in registers: at most 16 vectors of 8 per lane
+  if (s->H > 64 * 8 * 16) return MOE_ERR_UNSUPPORTED;
+  st = check_dispatch(s, x, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
+                      workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  MOE_NEED(expand_x, s->capacity * s->H);
+  MOE_NEED(dynamic_scales, s->capacity);
+  hipStream_t strm = as_stream(stream);
+  launch_route(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag, workspace, strm);
+  if (s->T > 0) {
+    const int64_t Hv = s->H / 8;
+    const int nv = (int)((Hv + kWave - 1) / kWave);
+    const dim3 grid((unsigned)((s->T + kWavesPerBlock - 1) / kWavesPerBlock)), block(256);
+    const uint4* xv = static_cast<const uint4*>(x);
+    uint2* out = reinterpret_cast<uint2*>(expand_x);
+#define PERMUTE_I8(N)                                                                                    \
+  hipLaunchKernelGGL(k_permute_i8<N>, grid, block, 0, strm, xv, topk_idx, assist, s->T, s->K, Hv, smooth_scales, \
+                     out, dynamic_scales)
+    if (nv <= 1) PERMUTE_I8(1);
+    else if (nv <= 2) PERMUTE_I8(2);
+    else if (nv <= 4) PERMUTE_I8(4);
+    else if (nv <= 8) PERMUTE_I8(8);
+    else PERMUTE_I8(16);
+#undef PERMUTE_I8
   }
   return launch_status();
 }

@@ -379,6 +379,53 @@ moe_status moe_ffn_gate_up_bwd_weight_fp8(const moe_shape* s, const uint8_t* dgu
                                           const int32_t* ep_recv_counts, float* grad_w_gate,
                                           float* grad_w_up, void* stream);
 
+/* ------------------------------------------------------------------ int8 path
+ * The decode regime of the low_latency_combine page's examples: dispatch with
+ * quant_mode 2 ("dynamic quantization") returns an int8 expand_x and
+ * dynamic_scales, optionally scaling each row first by an fp32 (num_experts, H)
+ * scales tensor (example programs; the page gives no formula).  Reading taken
+ * here: row = x_t times scales[e] for the routed expert e (float32 products),
+ * codes clamp(rint(v * (127/amax)), -127, 127) (ties to even), dynamic scale
+ * amax/127 (an all-zero row: codes 0, scale 1) -- the rule of the int8 combine
+ * payload.  The grouped FFN on those rows (not on the pages) runs w8a8: int8
+ * weights with one scale per output channel (moe_quant_rows_int8 over the
+ * E*N rows of the (out, in) matrices), exact integer sums times (row scale x
+ * channel scale), bf16 outputs; h is requantised per row for the down
+ * projection.  H and F multiples of 128 for the GEMMs (MOE_ERR_BAD_SHAPE).
+ */
+
+/* moe_dispatch with int8 expanded rows.  Same routing outputs (assist,
+ * counts, err_flag) as moe_dispatch; expand_x (capacity, H) int8 and
+ * dynamic_scales (capacity) fp32 for the rows < ep_recv_counts[E-1].
+ * smooth_scales: NULL or (num_experts, H) fp32.  H <= 8192 (the row is held in
+ * registers; else MOE_ERR_UNSUPPORTED).  Five kernel launches. */
+moe_status moe_dispatch_int8(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                             const uint8_t* x_active_mask, const float* smooth_scales,
+                             int8_t* expand_x, float* dynamic_scales, int32_t* assist_info_for_combine,
+                             int32_t* expert_token_nums, int32_t* ep_recv_counts, int32_t* err_flag,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Rows of a bf16 (R, C) matrix to int8 with one scale per row (rule above),
+ * C a multiple of 8: codes (R, C) int8, scales (R) fp32; nrows: optional device
+ * int32, only rows < *nrows are written.  Also the weight quantiser of the int8
+ * path, with R = E*N rows of K. */
+moe_status moe_quant_rows_int8(int64_t R, int64_t C, const void* src, const int32_t* nrows,
+                               int8_t* codes, float* scales, void* stream);
+
+/* w8a8 moe_ffn_gate_up_fwd: xq/xs = moe_dispatch_int8 outputs; wgq/wgs,
+ * wuq/wus = moe_quant_rows_int8 of w_gate, w_up ((E, F, H) codes, (E, F)
+ * scales).  gate_up_save and h_act in bf16. */
+moe_status moe_ffn_gate_up_fwd_int8(const moe_shape* s, const int8_t* xq, const float* xs,
+                                    const int8_t* wgq, const float* wgs, const int8_t* wuq,
+                                    const float* wus, const int32_t* ep_recv_counts,
+                                    void* gate_up_save, void* h_act, void* stream);
+
+/* w8a8 moe_ffn_down_fwd: hq/hs = moe_quant_rows_int8 of h_act; wdq/wds of
+ * w_down ((E, H, F) codes, (E, H) scales).  y in bf16. */
+moe_status moe_ffn_down_fwd_int8(const moe_shape* s, const int8_t* hq, const float* hs,
+                                 const int8_t* wdq, const float* wds, const int32_t* ep_recv_counts,
+                                 void* y, void* stream);
+
 /* ------------------------------------------------------------------ router
  * The pages take topk_idx and topk_weights as inputs (low_latency_combine page,
  * "Parameters": K distinct ids per token in [0, E+Z+C+Q), one float weight per

@@ -216,3 +216,25 @@ def test_fused_quantising_data_gradient_rejects_bad_arguments(L):
     assert L.moe_ffn_down_bwd_data_fp8_quant(s8, *args, Nn, Nn, Nn, Nn, P(), Nn) == NULL_ARG
     # fp8 shape rules
     assert L.moe_ffn_down_bwd_data_fp8_quant(ctypes.byref(S()), *args, P(), Nn, Nn, Nn, Nn, Nn) == BAD_SHAPE
+
+
+def test_int8_entries_reject_bad_arguments_before_launch(L):
+    Nn = None
+    s = S(F=512)
+    sp = ctypes.byref(s)
+    # dispatch: the row lives in registers, H <= 8192
+    assert L.moe_dispatch_int8(ctypes.byref(S(H=8200)), *([P()] * 11), 1 << 20, Nn) == UNSUPPORTED
+    # NULL expanded rows / scales, small workspace
+    assert L.moe_dispatch_int8(sp, P(), P(), Nn, Nn, Nn, P(), P(), P(), P(), P(), P(), 1 << 20, Nn) == NULL_ARG
+    assert L.moe_dispatch_int8(sp, P(), P(), Nn, Nn, P(), Nn, P(), P(), P(), P(), P(), 1 << 20, Nn) == NULL_ARG
+    assert L.moe_dispatch_int8(sp, P(), P(), Nn, Nn, P(), P(), P(), P(), P(), P(), P(), 16, Nn) == WORKSPACE
+    # row quantiser: C a positive multiple of 8
+    for C in (0, 12, -8):
+        assert L.moe_quant_rows_int8(4, C, P(), Nn, P(), P(), Nn) == BAD_SHAPE
+    assert L.moe_quant_rows_int8(4, 16, P(), Nn, Nn, P(), Nn) == NULL_ARG
+    assert L.moe_quant_rows_int8(0, 16, Nn, Nn, Nn, Nn, Nn) == OK
+    # GEMMs: the 8-bit shape rules (F = 480 is not a multiple of 128), NULL weights
+    assert L.moe_ffn_gate_up_fwd_int8(ctypes.byref(S()), *([P()] * 9), Nn) == BAD_SHAPE
+    assert L.moe_ffn_down_fwd_int8(ctypes.byref(S()), *([P()] * 6), Nn) == BAD_SHAPE
+    assert L.moe_ffn_gate_up_fwd_int8(sp, P(), P(), Nn, P(), P(), P(), P(), P(), P(), Nn) == NULL_ARG
+    assert L.moe_ffn_down_fwd_int8(sp, P(), P(), P(), Nn, P(), P(), Nn) == NULL_ARG
