@@ -622,9 +622,14 @@ def quant_weights_int8(w_bits):
 
 
 def _i8_gemm(q_rows, s_rows, q_w, s_w):
-    """(q_rows @ q_w^T) exactly in integers, times (row scale x channel scale), float64."""
-    acc = q_rows.astype(np.int64) @ q_w.astype(np.int64).T
-    return acc.astype(np.float64) * s_rows.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :]
+    """(q_rows @ q_w^T) exactly, times (row scale x channel scale), float64.
+
+    The integer sums are taken as a float64 matrix product: every product is at most
+    127^2 and every partial sum an integer of magnitude below 127^2 * K < 2^53 (K < 5e11),
+    so each float64 addition is exact and the result equals the integer sum."""
+    assert q_rows.shape[1] < (1 << 53) // (127 * 127)
+    acc = q_rows.astype(np.float64) @ q_w.astype(np.float64).T
+    return acc * s_rows.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :]
 
 
 def ffn_fwd_int8(Xq, xs, ep_recv_counts, wq_gate, wq_up, wq_down):

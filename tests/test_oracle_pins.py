@@ -676,3 +676,17 @@ def test_int8_layer_close_to_bf16_layer():
     f = orc.layer_fwd(inp, prec="parity")
     rel = np.linalg.norm(f8["out"] - f["out"]) / np.linalg.norm(f["out"])
     assert 1e-3 < rel < 0.05
+
+
+def test_int8_gemm_sums_are_exact_integers():
+    """The w8a8 sums equal the integer matrix product (taken in int64 here) at the
+    largest magnitudes: all codes +-127 over a long contraction."""
+    rng = np.random.default_rng(54)
+    K = 20000
+    q = np.where(rng.random((6, K)) < 0.5, -127, 127).astype(np.int8)
+    w = np.where(rng.random((5, K)) < 0.5, -127, 127).astype(np.int8)
+    w[0] = q[0]                                       # a sum of 127^2 * K
+    got = orc.moe._i8_gemm(q, np.ones(6, np.float32), w, np.ones(5, np.float32))
+    ref = q.astype(np.int64) @ w.astype(np.int64).T
+    assert ref[0, 0] == 127 * 127 * K
+    assert np.array_equal(got, ref.astype(np.float64))
