@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # page1 is the default (the benchmark line); the others are extra measurements
@@ -61,6 +62,9 @@ WORKLOADS = {
     # the low_latency_combine page's decode regime (BS <= 512 tokens, H = 7168,
     # top-8, 32 experts in its example), every expert on one GPU, forward only
     "decode": dict(T=512, H=7168, F=2048, E=32, K=8, forward_only=True),
+    # the same batch on the page's quant_mode 2 path: int8 dispatch with per-expert
+    # smooth scales, w8a8 grouped GEMMs (int8 weights: half the bytes to stream)
+    "decode_int8": dict(T=512, H=7168, F=2048, E=32, K=8, forward_only=True, int8=True),
 }
 
 
@@ -81,7 +85,12 @@ def gemm_flops(A, H, F):
 
 def gemm_bytes(name, A, H, F, E):
     """Algorithmic HBM bytes of a forward grouped GEMM: every expert's weights once, its
-    input rows and its outputs (decode-sized batches read the weights far more than rows)."""
+    input rows and its outputs (decode-sized batches read the weights far more than rows);
+    int8 GEMMs read 1-byte weights and rows plus one fp32 scale per row and channel."""
+    if name == "moe_ffn_gate_up_fwd_int8":
+        return E * 2 * F * (H + 4) + A * (H + 4) + A * 3 * F * 2
+    if name == "moe_ffn_down_fwd_int8":
+        return E * H * (F + 4) + A * (F + 4) + A * H * 2
     if name.startswith("moe_ffn_gate_up_fwd"):
         return E * 2 * F * H * 2 + A * H * 2 + A * 3 * F * 2
     if name.startswith("moe_ffn_down_fwd"):
@@ -136,9 +145,12 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
     T_sample = min(T_sample, cfg["T"])
     inp = wl.layer_inputs(T_sample, cfg["H"], cfg["F"], cfg["E"], cfg["K"], seed=0,
                           zipf=cfg.get("zipf"), shared=cfg.get("shared", False))
+    smooth = np.exp(np.random.default_rng(7).standard_normal((cfg["E"], cfg["H"])) * 0.5).astype(np.float32)
     runs, t0 = 0, time.perf_counter()
     while True:
-        if fp8:
+        if cfg.get("int8"):
+            f = orc.layer_fwd_int8(inp, smooth)
+        elif fp8:
             f = orc.layer_fwd_fp8(inp)
             orc.layer_bwd_fp8(inp, f, inp["grad_out"], wgrad="fp8" if cfg.get("fp8_wgrad") else "bf16")
         else:
@@ -263,6 +275,7 @@ def build_step(name, T_override=None):
     shared = cfg.get("shared", False)
     fp8 = cfg.get("fp8", False)
     fp8w = fp8 and cfg.get("fp8_wgrad", False)
+    int8 = cfg.get("int8", False)
     log(f"[bench] {name}: generating inputs T={T} H={H} F={F} E={E} K={K}")
     inp = wl.layer_inputs(T, H, F, E, K, seed=0, zipf=cfg.get("zipf"), shared=shared)
     x, gout = _bf(inp["x"], dev), _bf(inp["grad_out"], dev)
@@ -283,9 +296,30 @@ def build_step(name, T_override=None):
     st = Step()
     st.recv, st.err, st.counts = recv, err, cnt
     C = st.calls
-    C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
     sy = sdx = None
-    if fp8:
+    if int8:
+        st.dtype = "int8 (dispatch rows, w8a8 GEMMs), bf16 outputs"
+        gen = torch.Generator(device=dev).manual_seed(7)
+        smooth = torch.exp(torch.randn((E, H), generator=gen, device=dev) * 0.5)
+        exq, dyn = z(cap, H, dt=torch.int8), z(cap, dt=f32)
+        wq8 = [dm.quant_rows_int8(t) for t in (wg, wu, wd)]
+        hq8, hs8 = z(cap, F, dt=torch.int8), z(cap, dt=f32)
+        C.append(("moe_dispatch_int8", lambda: dm.moe_dispatch_int8(shape, x, idx, None, smooth, exq, dyn, assist,
+                                                                    cnt, recv, err, ws)))
+        # weight quantisation (once per weight update) is timed outside the step
+        st.extra_calls.append(("moe_quant_rows_int8 (3 weight tensors)",
+                               lambda: [dm.quant_rows_int8(t) for t in (wg, wu, wd)]))
+    else:
+        C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
+    if int8:
+        C += [
+            ("moe_ffn_gate_up_fwd_int8", lambda: dm.moe_ffn_gate_up_fwd_int8(
+                shape, exq, dyn, wq8[0][0], wq8[0][1], wq8[1][0], wq8[1][1], recv, gus, h)),
+            ("moe_quant_rows_int8 (h)", lambda: dm.moe_quant_rows_int8(h, hq8, hs8, recv[-1:])),
+            ("moe_ffn_down_fwd_int8", lambda: dm.moe_ffn_down_fwd_int8(shape, hq8, hs8, wq8[2][0], wq8[2][1],
+                                                                       recv, y)),
+        ]
+    elif fp8:
         st.dtype = ("fp8 e4m3 (all six GEMMs; weight grads on per-128-token operands)" if fp8w
                     else "fp8 e4m3 (fwd + data grads), bf16 (weight grads)")
         nrows = recv[-1:]
@@ -426,7 +460,8 @@ def account(st, A):
         return {}, nb
     fp8 = st.cfg.get("fp8", False)
     fp8w = fp8 and st.cfg.get("fp8_wgrad", False)
-    pk = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    int8 = st.cfg.get("int8", False)
+    pk = PEAK_INT8_TOPS if int8 else (PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS)
     pkw = PEAK_FP8_TFLOPS if fp8w else PEAK_BF16_TFLOPS
     fl = {}
     fwd_only = st.cfg.get("forward_only", False)
@@ -435,6 +470,8 @@ def account(st, A):
                             "moe_ffn_gate_up_bwd_data": (4, pk),
                             "moe_ffn_gate_up_bwd_weight": (4, pkw)}.items():
         key = n + "_fp8" if fp8 and ("fwd" in n or "data" in n or fp8w) else n
+        if int8:
+            key = n + "_int8"
         if fwd_only and "fwd" not in n:
             continue
         fl[key] = (mult * A * H * F, peak)
@@ -446,6 +483,10 @@ def account(st, A):
     for n in ("moe_dispatch", "moe_combine") if fwd_only else ("moe_dispatch", "moe_combine", "moe_combine_bwd",
                                                                 "moe_dispatch_bwd"):
         nb[n] = bytes_moved(n, T, H, F, K, A, E)
+    if int8:
+        # int8 rows and one fp32 scale per row written, the smooth scales read once
+        nb["moe_dispatch_int8"] = nb.pop("moe_dispatch") - A * H * 2 + A * H + A * 4 + E * H * 4
+        nb["moe_quant_rows_int8 (h)"] = A * F * 3 + A * 4
     if st.cfg.get("shared"):
         nb["moe_combine"] += T * H * 2
         nb["moe_dispatch_bwd"] += T * H * 2
@@ -587,6 +628,8 @@ def main():
         "combine_stress": "combine only, 256 routed + 1 zero + 1 copy + 2 constant experts, "
                           "2-D mask 10% false, shared_expert_x",
         "decode": "decode batch (the low_latency_combine page's largest BS), forward only",
+        "decode_int8": "decode batch, forward only, int8 dispatch with smooth scales (quant_mode 2) and "
+                       "w8a8 GEMMs",
     }[args.workload]
     fwd_only = st.cfg.get("forward_only", False)
     res = {

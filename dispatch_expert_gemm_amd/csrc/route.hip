@@ -245,31 +245,32 @@ __global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x,
   }
 }
 
-// int8 dispatch (quant_mode 2): one wave per token, the row's NV 16-byte
-// vectors per lane kept in registers (H <= 64 * 8 * NV).  Each destination row
-// is x (times the smooth-scale row of its expert, when given) quantised with
-// one dynamic scale: codes clamp(rint(v * (127/amax)), -127, 127), scale
-// amax/127 (all-zero: codes 0, scale 1).  Without smooth scales every
-// destination row of a token holds the same codes, computed once.
+// int8 dispatch (quant_mode 2): one wave per slot (token, choice), so a decode
+// batch of a few hundred tokens still gives thousands of waves; the wave reads
+// the token's row (NV 16-byte vectors per lane, H <= 64 * 8 * NV, kept packed
+// in registers), multiplies it by the smooth-scale row of the slot's expert when
+// given, and writes the int8 row with one dynamic scale: codes clamp(rint(v *
+// (127/amax)), -127, 127), scale amax/127 (all-zero: codes 0, scale 1).
 template <int NV>
 __global__ __launch_bounds__(256) void k_permute_i8(const uint4* __restrict__ x, const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ slot2row, int64_t T, int K,
+                                                    const int32_t* __restrict__ slot2row, int64_t nslots, int K,
                                                     int64_t Hv, const float* __restrict__ smooth,
                                                     uint2* __restrict__ exq, float* __restrict__ dyn) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  if (t >= T) return;
-  const int my = lane < K ? slot2row[t * K + lane] : -1;
-  const int myid = lane < K ? idx[t * K + lane] : 0;
-  // the token's row stays packed (4 registers per 8 values)
+  const int64_t sl = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  if (sl >= nslots) return;
+  const int row = slot2row[sl];
+  if (row < 0) return;  // the whole wave: not a routed slot
+  const int64_t t = sl / K;
+  const float4* sr = smooth ? reinterpret_cast<const float4*>(smooth + (int64_t)idx[sl] * Hv * 8) : nullptr;
   uint4 xr[NV];
 #pragma unroll
   for (int q = 0; q < NV; ++q) {
     const int64_t v = lane + (int64_t)q * kWave;
     xr[q] = v < Hv ? x[t * Hv + v] : make_uint4(0u, 0u, 0u, 0u);
   }
-  // the 8 values of vector q, times the smooth-scale row sr when given
-  auto vals = [&](int q, const float4* sr, float (&f)[8]) {
+  // the 8 values of vector q, times the smooth-scale row when given
+  auto vals = [&](int q, float (&f)[8]) {
     unpack8(xr[q], f);
     if (sr) {
       const int64_t v = lane + (int64_t)q * kWave;
@@ -280,46 +281,26 @@ __global__ __launch_bounds__(256) void k_permute_i8(const uint4* __restrict__ x,
       f[6] = __fmul_rn(f[6], s1.z); f[7] = __fmul_rn(f[7], s1.w);
     }
   };
-  float m0 = 0.f;  // amax of the plain row (shared by all rows without smooth scales)
-  if (!smooth) {
+  float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      float f[8];
-      unpack8(xr[q], f);
+  for (int q = 0; q < NV; ++q) {
+    if (lane + (int64_t)q * kWave >= Hv) continue;
+    float f[8];
+    vals(q, f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m0 = fmaxf(m0, fabsf(f[i]));
-    }
-    m0 = wave_max64(m0);
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
   }
-  for (int k = 0; k < K; ++k) {
-    const int row = __builtin_amdgcn_readlane(my, k);
-    if (row < 0) continue;  // the same in every lane
-    const float4* sr = nullptr;
-    float m = m0;
-    if (smooth) {
-      sr = reinterpret_cast<const float4*>(smooth + (int64_t)__builtin_amdgcn_readlane(myid, k) * Hv * 8);
-      m = 0.f;
+  m = wave_max64(m);
+  const float inv = m > 0.f ? __fdiv_rn(127.0f, m) : 0.f;
 #pragma unroll
-      for (int q = 0; q < NV; ++q) {
-        if (lane + (int64_t)q * kWave >= Hv) continue;
-        float f[8];
-        vals(q, sr, f);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
-      }
-      m = wave_max64(m);
-    }
-    const float inv = m > 0.f ? __fdiv_rn(127.0f, m) : 0.f;
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int64_t v = lane + (int64_t)q * kWave;
-      if (v >= Hv) continue;
-      float f[8];
-      vals(q, sr, f);
-      exq[(int64_t)row * Hv + v] = make_uint2(i8x4(f[0], f[1], f[2], f[3], inv), i8x4(f[4], f[5], f[6], f[7], inv));
-    }
-    if (lane == 0) dyn[row] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
+  for (int q = 0; q < NV; ++q) {
+    const int64_t v = lane + (int64_t)q * kWave;
+    if (v >= Hv) continue;
+    float f[8];
+    vals(q, f);
+    exq[(int64_t)row * Hv + v] = make_uint2(i8x4(f[0], f[1], f[2], f[3], inv), i8x4(f[4], f[5], f[6], f[7], inv));
   }
+  if (lane == 0) dyn[row] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
 }
 
 struct RouteGeom {
@@ -469,11 +450,12 @@ extern "C" moe_status moe_dispatch_int8(const moe_shape* s, const void* x, const
   if (s->T > 0) {
     const int64_t Hv = s->H / 8;
     const int nv = (int)((Hv + kWave - 1) / kWave);
-    const dim3 grid((unsigned)((s->T + kWavesPerBlock - 1) / kWavesPerBlock)), block(256);
+    const int64_t nslots = s->T * s->K;
+    const dim3 grid((unsigned)((nslots + kWavesPerBlock - 1) / kWavesPerBlock)), block(256);
     const uint4* xv = static_cast<const uint4*>(x);
     uint2* out = reinterpret_cast<uint2*>(expand_x);
-#define PERMUTE_I8(N)                                                                                    \
-  hipLaunchKernelGGL(k_permute_i8<N>, grid, block, 0, strm, xv, topk_idx, assist, s->T, s->K, Hv, smooth_scales, \
+#define PERMUTE_I8(N)                                                                                        \
+  hipLaunchKernelGGL(k_permute_i8<N>, grid, block, 0, strm, xv, topk_idx, assist, nslots, s->K, Hv, smooth_scales, \
                      out, dynamic_scales)
     if (nv <= 1) PERMUTE_I8(1);
     else if (nv <= 2) PERMUTE_I8(2);

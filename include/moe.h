@@ -398,7 +398,8 @@ moe_status moe_ffn_gate_up_bwd_weight_fp8(const moe_shape* s, const uint8_t* dgu
  * counts, err_flag) as moe_dispatch; expand_x (capacity, H) int8 and
  * dynamic_scales (capacity) fp32 for the rows < ep_recv_counts[E-1].
  * smooth_scales: NULL or (num_experts, H) fp32.  H <= 8192 (the row is held in
- * registers; else MOE_ERR_UNSUPPORTED).  Five kernel launches. */
+ * registers; else MOE_ERR_UNSUPPORTED).  Four kernel launches: the three routing
+ * kernels of moe_dispatch and a quantising permute. */
 moe_status moe_dispatch_int8(const moe_shape* s, const void* x, const int32_t* topk_idx,
                              const uint8_t* x_active_mask, const float* smooth_scales,
                              int8_t* expand_x, float* dynamic_scales, int32_t* assist_info_for_combine,
