@@ -126,3 +126,75 @@ def test_random_fp8_layer_shapes(idx):
     check_close("grad_w_gate", f32(gwg), b["dWg"], rel_l2=REL_FP8)
     check_close("grad_w_up", f32(gwu), b["dWu"], rel_l2=REL_FP8)
     check_close("grad_w_down", f32(gwd), b["dWd"], rel_l2=REL_FP8)
+
+
+@pytest.mark.parametrize("idx", range(len(FP8_CASES)))
+def test_random_fp8_layer_shapes_fp8_weight_gradients(idx):
+    """The same fp8 draws through moe_layer with fp8 weight gradients (fused
+    per-128-token quantisation of h and dG|dU) against the oracle's fp8 layer with
+    wgrad='fp8'; weight gradients at the bar derived for a requantised chain."""
+    kw = FP8_CASES[idx]
+    print(f"[random fp8 wgrad] case={idx} {kw}", flush=True)
+    inp = wl.layer_inputs(seed=300 + idx, **kw)
+    x = bf(inp["x"]).requires_grad_(True)
+    w = torch.from_numpy(inp["topk_weights"]).to(DEV).requires_grad_(True)
+    ws = [bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down")]
+    mask = torch.from_numpy(inp["mask"]).to(DEV) if inp.get("mask") is not None else None
+    out = dm.moe_layer(x, torch.from_numpy(inp["topk_idx"]).to(DEV), w, *ws, x_active_mask=mask,
+                       zero_expert_num=kw.get("Z", 0), copy_expert_num=kw.get("C", 0), fp8=True,
+                       comm_quant_mode=2, fp8_wgrad=True)
+    out.backward(bf(inp["grad_out"]))
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_fp8(inp)
+    b = orc.layer_bwd_fp8(inp, f, inp["grad_out"], wgrad="fp8")
+    check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
+    check_close("grad_x", f32(x.grad), b["dx"], rel_l2=REL_FP8)
+    check_close("grad_topk_weights", f32(w.grad), b["dw"], rel_l2=REL_FP8)
+    for t, k in zip(ws, ("dWg", "dWu", "dWd")):
+        check_close(k, f32(t.grad), orc.round_bf16(b[k]), max_abs=5e-2, rel_l2=REL_FP8)
+
+
+def _draw_int8(n, seed=20261205):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([1, 4, 16, 32]))
+        K = int(min(rng.integers(1, 9), E + 2))
+        T = int(rng.integers(1, 600))
+        H = int(128 * rng.integers(1, 40))     # up to 4992
+        F = int(128 * rng.integers(1, 12))
+        kw = dict(T=T, H=H, F=F, E=E, K=K)
+        if rng.random() < 0.5:
+            kw.update(Z=int(rng.integers(0, 2)), C=int(rng.integers(0, 2)), mask="2d")
+        kw["K"] = min(kw["K"], E + kw.get("Z", 0) + kw.get("C", 0))
+        cases.append(kw)
+    return cases
+
+
+INT8_CASES = _draw_int8(5)
+
+
+@pytest.mark.parametrize("idx", range(len(INT8_CASES)))
+def test_random_int8_decode_shapes(idx):
+    """int8 dispatch with smooth scales, w8a8 GEMMs and bf16 combine on seeded random
+    decode-sized layers, against the oracle's int8 forward (8-bit bar)."""
+    kw = INT8_CASES[idx]
+    print(f"[random int8] case={idx} {kw}", flush=True)
+    inp = wl.layer_inputs(seed=400 + idx, **kw)
+    S = np.exp(np.random.default_rng(500 + idx).standard_normal((kw["E"], kw["H"])) * 0.5).astype(np.float32)
+    run = Run(inp)
+    shape, cap, F, H = run.shape, run.cap, kw["F"], kw["H"]
+    run.d, dyn = dm.dispatch_int8(shape, run.x, run.idx, run.mask, torch.from_numpy(S).to(DEV))
+    wq = [dm.quant_rows_int8(bf(inp[k])) for k in ("w_gate", "w_up", "w_down")]
+    gus = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+    h = torch.empty((cap, F), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+    recv = run.d.ep_recv_counts
+    dm.moe_ffn_gate_up_fwd_int8(shape, run.d.expand_x, dyn, wq[0][0], wq[0][1], wq[1][0], wq[1][1], recv, gus, h)
+    hq, hs = dm.quant_rows_int8(h, recv[-1:])
+    dm.moe_ffn_down_fwd_int8(shape, hq, hs, wq[2][0], wq[2][1], recv, y)
+    out = run.combine(y=y)
+    f = orc.layer_fwd_int8(inp, S)
+    A = f["route"].A
+    check_close("h", f32(h[:A]), f["Hh"], rel_l2=REL_FP8)
+    check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
