@@ -721,6 +721,52 @@ class _MoELayerFn(torch.autograd.Function):
                 *s_grads, None, None, None, None, None, None, None, None, None, None, None)
 
 
+@dataclass
+class Int8Weights:
+    """int8 codes (E, N, K) with one fp32 scale per output channel (E, N) of one weight tensor."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+    @staticmethod
+    def quantize(w, stream=None):
+        c, s = quant_rows_int8(w.contiguous(), stream=stream)
+        return Int8Weights(c, s)
+
+
+@torch.no_grad()
+def moe_layer_int8(x, topk_idx, topk_weights, wq_gate, wq_up, wq_down, *, smooth_scales=None,
+                   x_active_mask=None, shared_expert_x=None, const_alpha_1=None, const_alpha_2=None,
+                   const_v=None, zero_expert_num=0, copy_expert_num=0, const_expert_num=0, stream=None):
+    """Forward of one MoE layer on the decode regime's int8 path (inference, no autograd):
+    int8 dispatch (optionally smooth-scaled per expert), w8a8 gate/up GEMM with the SwiGLU
+    epilogue, per-row int8 requantisation of h, w8a8 down GEMM, bf16 combine.
+    wq_*: Int8Weights of w_gate, w_up (E, F, H) and w_down (E, H, F)."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    E, F, _ = wq_gate.codes.shape
+    dev = x.device
+    mask_ndim = 0 if x_active_mask is None else x_active_mask.dim()
+    shape = make_shape(T, H, K, E, F=F, zero_expert_num=zero_expert_num, copy_expert_num=copy_expert_num,
+                       const_expert_num=const_expert_num, mask_ndim=mask_ndim)
+    mask = None if x_active_mask is None else x_active_mask.view(torch.uint8)
+    d, dyn = dispatch_int8(shape, x, topk_idx, mask, smooth_scales, stream=stream)
+    cap = shape.capacity
+    gus = torch.empty((cap, 2 * F), dtype=BF16, device=dev)
+    h = torch.empty((cap, F), dtype=BF16, device=dev)
+    y = torch.empty((cap, H), dtype=BF16, device=dev)
+    recv = d.ep_recv_counts
+    moe_ffn_gate_up_fwd_int8(shape, d.expand_x, dyn, wq_gate.codes, wq_gate.scales, wq_up.codes, wq_up.scales,
+                             recv, gus, h, stream)
+    hq = torch.empty((cap, F), dtype=I8T, device=dev)
+    hs = torch.empty(cap, dtype=F32, device=dev)
+    moe_quant_rows_int8(h, hq, hs, recv[-1:], stream)
+    moe_ffn_down_fwd_int8(shape, hq, hs, wq_down.codes, wq_down.scales, recv, y, stream)
+    out = torch.empty((T, H), dtype=BF16, device=dev)
+    moe_combine(shape, y, topk_idx, topk_weights, d.assist_info_for_combine, recv, mask, shared_expert_x, x,
+                const_alpha_1, const_alpha_2, const_v, out, stream)
+    return out
+
+
 def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=None,
               shared_expert_x=None, shared_w_gate=None, shared_w_up=None, shared_w_down=None,
               const_alpha_1=None, const_alpha_2=None, const_v=None,

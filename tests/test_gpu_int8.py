@@ -131,3 +131,21 @@ def test_int8_decode_forward_full_size():
     A = f["route"].A
     check_close("h", f32(g["h"][:A]), f["Hh"], rel_l2=REL_8BIT)
     check_close("out", f32(g["out"]), f["out"], rel_l2=REL_8BIT)
+
+
+def test_moe_layer_int8_api():
+    """moe_layer_int8 (the Python inference entry of the int8 path) with smooth scales,
+    constant and copy experts, a 1-D mask and a given shared_expert_x, against the
+    oracle's int8 forward."""
+    inp = wl.layer_inputs(seed=68, T=333, H=512, F=256, E=6, K=3, C=1, Q=1, mask="1d")
+    inp["shared_expert_x"] = wl.to_bf16_bits(np.random.default_rng(69).standard_normal((333, 512), dtype=np.float32))
+    S = _smooth(6, 512, 70)
+    wq = [dm.Int8Weights.quantize(bf(inp[k])) for k in ("w_gate", "w_up", "w_down")]
+    out = dm.moe_layer_int8(bf(inp["x"]), dev(inp["topk_idx"]), dev(inp["topk_weights"]), *wq,
+                            smooth_scales=torch.from_numpy(S).to(DEV), x_active_mask=dev(inp["mask"]),
+                            shared_expert_x=bf(inp["shared_expert_x"]), const_alpha_1=bf(inp["const_alpha_1"]),
+                            const_alpha_2=bf(inp["const_alpha_2"]), const_v=bf(inp["const_v"]),
+                            copy_expert_num=1, const_expert_num=1)
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_int8(inp, S)
+    check_close("out", f32(out), f["out"], rel_l2=REL_8BIT)
