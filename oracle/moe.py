@@ -57,7 +57,8 @@ from dataclasses import dataclass
 import numpy as np
 
 from .numerics import (bf16_to_f32, dequant_e4m3_blocks, dequant_e4m3_rows, dequant_int8_rows,
-                       e4m3_decode, quant_e4m3_blocks, quant_e4m3_rows, quant_int8_rows, round_bf16)
+                       dequant_mx_e4m3_rows, e4m3_decode, quant_e4m3_blocks, quant_e4m3_rows,
+                       quant_int8_rows, quant_mx_e4m3_rows, round_bf16)
 
 ERR_ID_RANGE = 1
 ERR_ID_DUPLICATE = 2
@@ -668,3 +669,120 @@ def layer_fwd_int8(inp: dict, smooth_scales=None):
     out = combine(Y, r, inp["topk_weights"], inp.get("shared_expert_x"), inp["x"],
                   inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), "parity")
     return dict(route=r, Xq=Xq, xs=xs, wq=wq, G=G, U=U, Hh=Hh, hq=hq, hs=hs, Y=Y, out=out)
+
+
+# ============================================================================ MX (microscaled) fp8 path
+#
+# Reading (the survey's NEXT-2 names gfx950's block-scaled MFMA; the pages give no
+# recipe): the same fp8 layer with microscaling instead of fp32 block scales: every
+# fp8 operand carries one E8M0 (power of two) scale per 32 consecutive values of its
+# contraction dimension (quant_mx_e4m3_rows; the scale is the smallest power of two
+# that keeps the block maximum within +-448, so nothing saturates): activations x, h, dY, dG|dU along their
+# rows; the weights along H for the forward GEMMs and, for the data gradients, their
+# transposes along F (gate/up) or H (down), i.e. the weights are quantised twice.
+# Weight gradients stay bf16, G, U, h, y, dG|dU, dX keep bf16 storage.
+
+
+def qdq_rows_mx(a):
+    """MX e4m3 round trip along rows (float64)."""
+    a = np.asarray(a, np.float32)
+    if a.shape[0] == 0:
+        return a.astype(np.float64)
+    return dequant_mx_e4m3_rows(*quant_mx_e4m3_rows(a))
+
+
+def quant_weights_mx(w_bits):
+    """(E, N, K) bf16 weights -> MX codes/scales along K, (E, N, K) and (E, N, K/32), and
+    of the transposes along N, (E, K, N) and (E, K, N/32)."""
+    W = decode(w_bits, "parity")
+    fw = [quant_mx_e4m3_rows(W[e]) for e in range(W.shape[0])]
+    tw = [quant_mx_e4m3_rows(np.ascontiguousarray(W[e].T)) for e in range(W.shape[0])]
+    return (np.stack([q for q, _ in fw]), np.stack([s for _, s in fw]),
+            np.stack([q for q, _ in tw]), np.stack([s for _, s in tw]))
+
+
+def _dq_w_mx(wq, transposed=False):
+    """Dequantised weights (float64): (E, N, K) from the K-blocked codes, or the
+    (E, K, N) transposes from the N-blocked codes."""
+    c, s = (wq[2], wq[3]) if transposed else (wq[0], wq[1])
+    return np.stack([dequant_mx_e4m3_rows(c[e], s[e]) for e in range(c.shape[0])])
+
+
+def ffn_fwd_mx(X16, ep_recv_counts, wq_gate, wq_up, wq_down):
+    """MX fp8 forward of the grouped SwiGLU FFN (parity mode); wq_* from quant_weights_mx.
+    Returns G16, U16, H16 and Y16 (bf16 values)."""
+    st = _store("parity")
+    Wg, Wu, Wd = (_dq_w_mx(w) for w in (wq_gate, wq_up, wq_down))
+    X16 = np.asarray(X16, np.float32)
+    Xd = qdq_rows_mx(X16)
+    E, F, H = Wg.shape
+    A = X16.shape[0]
+    G, U, Hh = (np.zeros((A, F), np.float32) for _ in range(3))
+    Y = np.zeros((A, H), np.float32)
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        if hi > lo:
+            g = Xd[lo:hi] @ Wg[e].T
+            u = Xd[lo:hi] @ Wu[e].T
+            h = st(silu(g) * u)
+            G[lo:hi], U[lo:hi], Hh[lo:hi] = st(g), st(u), h
+            Y[lo:hi] = st(qdq_rows_mx(h) @ Wd[e].T)
+        lo = hi
+    return G, U, Hh, Y
+
+
+def ffn_bwd_mx(dY16, X16, G16, U16, H16, ep_recv_counts, wq_gate, wq_up, wq_down):
+    """MX fp8 data gradients (dY and dG|dU quantised along their rows, the transposed
+    weights along F or H), bf16 weight gradients (parity mode).  Returns dGU, dX, dWg,
+    dWu, dWd."""
+    st = _store("parity")
+    WgT, WuT, WdT = (_dq_w_mx(w, transposed=True) for w in (wq_gate, wq_up, wq_down))
+    E, H, F = WgT.shape
+    dY16, X16, G16, U16, H16 = (np.asarray(a, np.float32) for a in (dY16, X16, G16, U16, H16))
+    A = X16.shape[0]
+    dGU = np.zeros((A, 2 * F), np.float32)
+    dX = np.zeros((A, H), np.float32)
+    dWg, dWu = np.zeros((E, F, H), np.float32), np.zeros((E, F, H), np.float32)
+    dWd = np.zeros((E, H, F), np.float32)
+    lo = 0
+    for e in range(E):
+        hi = int(ep_recv_counts[e])
+        if hi > lo:
+            dh = qdq_rows_mx(dY16[lo:hi]) @ WdT[e].T          # WdT[e] is (F, H): dh = dY Wd
+            g, u = G16[lo:hi], U16[lo:hi]
+            s = 1 / (1 + np.exp(-g))
+            dg = st(dh * u * s * (1 + g * (1 - s)))
+            du = st(dh * (g * s))
+            dgu = np.concatenate([dg, du], 1)
+            dGU[lo:hi] = dgu
+            dX[lo:hi] = st(qdq_rows_mx(dgu) @ np.concatenate([WgT[e], WuT[e]], 1).T)
+            dWd[e] = dY16[lo:hi].T @ H16[lo:hi]
+            dWg[e] = dg.T @ X16[lo:hi]
+            dWu[e] = du.T @ X16[lo:hi]
+        lo = hi
+    return dGU, dX, dWg, dWu, dWd
+
+
+def layer_fwd_mx(inp: dict, comm_quant=True):
+    """Whole forward on the MX fp8 path (parity mode), int8 combine payload when comm_quant."""
+    E = inp["E"]
+    Z, C, Q = inp.get("Z", 0), inp.get("C", 0), inp.get("Q", 0)
+    r = route(inp["topk_idx"], E, Z, C, Q, inp.get("mask"))
+    X = dispatch(inp["x"], r, "parity")
+    wq = tuple(quant_weights_mx(inp[k]) for k in ("w_gate", "w_up", "w_down"))
+    G, U, Hh, Y = ffn_fwd_mx(X, r.ep_recv_counts, *wq)
+    Yc = qdq_rows_int8(Y) if comm_quant else Y
+    out = combine(Yc, r, inp["topk_weights"], inp.get("shared_expert_x"), inp["x"],
+                  inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), "parity")
+    return dict(route=r, X=X, wq=wq, G=G, U=U, Hh=Hh, Y=Y, Yc=Yc, out=out)
+
+
+def layer_bwd_mx(inp: dict, fwd: dict, grad_out):
+    r = fwd["route"]
+    dY, dw = combine_bwd(grad_out, fwd["Yc"], r, inp["topk_weights"], inp["x"],
+                         inp.get("const_alpha_1"), inp.get("const_alpha_2"), inp.get("const_v"), "parity")
+    dGU, dX, dWg, dWu, dWd = ffn_bwd_mx(dY, fwd["X"], fwd["G"], fwd["U"], fwd["Hh"], r.ep_recv_counts,
+                                        *fwd["wq"])
+    dx = dispatch_bwd(dX, r, inp["topk_weights"], grad_out, inp.get("const_alpha_1"), None, "parity")
+    return dict(dY=dY, dw=dw, dGU=dGU, dX=dX, dWg=dWg, dWu=dWu, dWd=dWd, dx=dx)

@@ -140,6 +140,36 @@ def dequant_e4m3_blocks(codes: np.ndarray, scales: np.ndarray, block: int = 128)
     return (v * scales[:, None, :, None]).astype(np.float32).reshape(R, Cn)
 
 
+def quant_mx_e4m3_rows(x: np.ndarray, block: int = 32):
+    """Microscaled (MX-style) e4m3 along rows: one E8M0 (power-of-two) scale per block
+    of `block` consecutive values of a row.
+
+    The scale X is the smallest power of two that brings the block maximum within the
+    e4m3 range: amax / X <= 448, i.e. with amax = M * 2^E (1 <= M < 2), X = 2^(E - 8) when
+    M <= 1.75 and 2^(E - 7) otherwise; it is clamped to the E8M0 range 2^-127 .. 2^127.
+    Codes are e4m3(x / X), rounded to nearest even (no value saturates).  The scale byte
+    is the exponent of X plus 127; an all-zero block gets byte 0 and codes 0.  Returns
+    (codes (R, C) uint8, scales (R, C/block) uint8).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    R, Cn = x.shape
+    assert Cn % block == 0
+    xb = x.reshape(R, Cn // block, block).astype(np.float64)
+    amax = np.abs(xb).max(axis=2)
+    m, p = np.frexp(amax)                  # amax = m * 2^p, m in [0.5, 1): M = 2m, E = p - 1
+    shared = np.where(amax > 0, (p - 1) - 8 + (m > 0.875), -127)
+    shared = np.clip(shared, -127, 127)
+    q = e4m3_encode((xb / np.exp2(shared)[:, :, None]).astype(np.float32))
+    return q.reshape(R, Cn), (shared + 127).astype(np.uint8)
+
+
+def dequant_mx_e4m3_rows(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """codes * 2^(scale byte - 127), float64 (exact)."""
+    R, Cn = codes.shape
+    v = e4m3_decode(codes).astype(np.float64).reshape(R, Cn // block, block)
+    return (v * np.exp2(scales.astype(np.float64) - 127.0)[:, :, None]).reshape(R, Cn)
+
+
 # ----------------------------------------------------------------------------- int8
 
 

@@ -690,3 +690,68 @@ def test_int8_gemm_sums_are_exact_integers():
     ref = q.astype(np.int64) @ w.astype(np.int64).T
     assert ref[0, 0] == 127 * 127 * K
     assert np.array_equal(got, ref.astype(np.float64))
+
+
+# ============================================================================ MX (microscaled) fp8
+
+
+def test_mx_quantiser_hand_examples():
+    """448 = 1.75 * 2^8 is the largest block maximum of scale 2^0 (byte 127): codes of
+    448, 1, -2, 0.5 are 0x7E, 0x38, 0xC0, 0x30; 449 needs scale 2^1 (byte 128) and
+    449 / 2 = 224.5 rounds to 224 = 0x76; an all-zero block gets byte 0."""
+    x = np.zeros((3, 32), np.float32)
+    x[0, :4] = [448, 1, -2, 0.5]
+    x[1, 0] = 449
+    q, s = orc.quant_mx_e4m3_rows(x)
+    assert q[0, :4].tolist() == [0x7E, 0x38, 0xC0, 0x30] and not q[0, 4:].any()
+    assert q[1, 0] == 0x76 and s[:, 0].tolist() == [127, 128, 0]
+    assert not q[2].any()
+
+
+def test_mx_scale_is_the_smallest_power_of_two_without_saturation():
+    rng = np.random.default_rng(71)
+    x = (rng.standard_normal((64, 256)) * np.exp2(rng.integers(-30, 30, size=(64, 1)))).astype(np.float32)
+    q, s = orc.quant_mx_e4m3_rows(x)
+    X = np.exp2(s.astype(np.float64) - 127.0)
+    amax = np.abs(x.astype(np.float64)).reshape(64, 8, 32).max(axis=2)
+    assert np.all(amax / X <= 448.0) and np.all(amax / X > 224.0)
+    # every code is the rounding of x / X (half an e4m3 step, subnormal spacing 2^-9)
+    d = orc.dequant_mx_e4m3_rows(q, s)
+    err = np.abs(d - x).reshape(64, 8, 32)
+    bound = np.maximum(np.abs(x.astype(np.float64)).reshape(64, 8, 32) * 2.0 ** -4, X[:, :, None] * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-12))
+
+
+def test_mx_lossless_inputs_reproduce_bf16_gate_up():
+    """Activations and weights whose every 32-block along the contraction is e4m3 codes
+    times 2^k with one entry at 448 * 2^k are exact in MX, so the MX forward's G, U, h
+    equal the bf16 FFN's bit for bit."""
+    rng = np.random.default_rng(72)
+    def lossless(shape):
+        v = orc.e4m3_decode(rng.integers(0, 0x7F, size=shape).astype(np.uint8)).astype(np.float64)
+        v *= np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+        v[..., ::32] = 448.0
+        k = rng.integers(-14, -6, size=shape[:-1] + (shape[-1] // 32,))
+        return (v * np.repeat(np.exp2(k), 32, axis=-1)).astype(np.float32)
+    E, F, H, A = 2, 64, 128, 40
+    X = lossless((A, H))
+    Wg, Wu, Wd = lossless((E, F, H)), lossless((E, F, H)), lossless((E, H, F))
+    bits = [orc.f32_to_bf16(a) for a in (X, Wg, Wu, Wd)]
+    assert all(np.array_equal(orc.bf16_to_f32(b), a) for b, a in zip(bits, (X, Wg, Wu, Wd)))
+    counts = np.array([15, 40])
+    wq = tuple(orc.quant_weights_mx(b) for b in bits[1:])
+    G8, U8, H8, _ = orc.ffn_fwd_mx(X, counts, *wq)
+    G, U, Hh, _ = orc.ffn_fwd(X, counts, *bits[1:], prec="parity")
+    assert np.array_equal(G8, G) and np.array_equal(U8, U) and np.array_equal(H8, Hh)
+
+
+def test_mx_layer_close_to_bf16_layer():
+    inp = wl.layer_inputs(96, 256, 128, 4, 2, seed=73)
+    fm = orc.layer_fwd_mx(inp)
+    bm = orc.layer_bwd_mx(inp, fm, inp["grad_out"])
+    f = orc.layer_fwd(inp, prec="parity")
+    b = orc.layer_bwd(inp, f, inp["grad_out"], prec="parity")
+    rel = lambda a, c: np.linalg.norm(a - c) / np.linalg.norm(c)
+    assert 0.003 < rel(fm["out"], f["out"]) < 0.1
+    for k in ("dx", "dw", "dWg", "dWu", "dWd"):
+        assert 0.001 < rel(bm[k], b[k]) < 0.15, k
