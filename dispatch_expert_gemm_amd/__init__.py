@@ -37,6 +37,8 @@ ENTRY_POINTS = (
     "moe_router", "moe_router_bwd", "moe_quant_cols_fp8", "moe_ffn_down_bwd_weight_fp8",
     "moe_ffn_gate_up_bwd_weight_fp8", "moe_ffn_down_bwd_data_fp8_quant", "moe_ffn_gate_up_fwd_fp8_quant",
     "moe_dispatch_int8", "moe_quant_rows_int8", "moe_ffn_gate_up_fwd_int8", "moe_ffn_down_fwd_int8",
+    "moe_quant_rows_mx", "moe_quantize_weights_mx", "moe_ffn_gate_up_fwd_mx", "moe_ffn_down_fwd_mx",
+    "moe_ffn_down_bwd_data_mx", "moe_ffn_gate_up_bwd_data_mx",
 )
 
 
@@ -108,6 +110,12 @@ def lib() -> ctypes.CDLL:
         L.moe_quant_rows_int8.argtypes = [I64, I64, P, P, P, P, P]
         L.moe_ffn_gate_up_fwd_int8.argtypes = [S] + [P] * 10
         L.moe_ffn_down_fwd_int8.argtypes = [S] + [P] * 7
+        L.moe_quant_rows_mx.argtypes = [I64, I64, P, P, P, P, P]
+        L.moe_quantize_weights_mx.argtypes = [I64, I64, I64, P, P, P, P, P, P]
+        L.moe_ffn_gate_up_fwd_mx.argtypes = [S] + [P] * 10
+        L.moe_ffn_down_fwd_mx.argtypes = [S] + [P] * 7
+        L.moe_ffn_down_bwd_data_mx.argtypes = [S] + [P] * 8
+        L.moe_ffn_gate_up_bwd_data_mx.argtypes = [S] + [P] * 9
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
                 getattr(L, name).restype = ctypes.c_int32
@@ -416,6 +424,61 @@ def quant_rows_int8(src, nrows=None, stream=None):
     return codes, scales
 
 
+def moe_quant_rows_mx(src, codes, scales, nrows=None, stream=None):
+    R, C = src.shape
+    _check(lib().moe_quant_rows_mx(R, C, _ptr(src, BF16, "src"), _ptr(nrows, I32, "nrows"),
+                                   _ptr(codes, U8T, "codes"), _ptr(scales, U8T, "scales"), _stream(stream)))
+
+
+def moe_quantize_weights_mx(w, codes, scales, codes_t=None, scales_t=None, stream=None):
+    E, N, K = w.shape
+    _check(lib().moe_quantize_weights_mx(E, N, K, _ptr(w, BF16, "w"), _ptr(codes, U8T, "codes"),
+                                         _ptr(scales, U8T, "scales"), _ptr(codes_t, U8T, "codes_t"),
+                                         _ptr(scales_t, U8T, "scales_t"), _stream(stream)))
+
+
+def moe_ffn_gate_up_fwd_mx(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act, stream=None):
+    _check(lib().moe_ffn_gate_up_fwd_mx(
+        ctypes.byref(shape), _ptr(xq, U8T, "xq"), _ptr(xs, U8T, "xs"), _ptr(wgq, U8T, "wgq"),
+        _ptr(wgs, U8T, "wgs"), _ptr(wuq, U8T, "wuq"), _ptr(wus, U8T, "wus"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(h_act, BF16, "h_act"), _stream(stream)))
+
+
+def moe_ffn_down_fwd_mx(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
+    _check(lib().moe_ffn_down_fwd_mx(
+        ctypes.byref(shape), _ptr(hq, U8T, "hq"), _ptr(hs, U8T, "hs"), _ptr(wdq, U8T, "wdq"),
+        _ptr(wds, U8T, "wds"), _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"),
+        _stream(stream)))
+
+
+def moe_ffn_down_bwd_data_mx(shape, dyq, dys, wdq_t, wds_t, gate_up_save, ep_recv_counts, grad_gate_up,
+                             stream=None):
+    _check(lib().moe_ffn_down_bwd_data_mx(
+        ctypes.byref(shape), _ptr(dyq, U8T, "dyq"), _ptr(dys, U8T, "dys"), _ptr(wdq_t, U8T, "wdq_t"),
+        _ptr(wds_t, U8T, "wds_t"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_gate_up, BF16, "grad_gate_up"),
+        _stream(stream)))
+
+
+def moe_ffn_gate_up_bwd_data_mx(shape, dguq, dgus, wgq_t, wgs_t, wuq_t, wus_t, ep_recv_counts, grad_expand_x,
+                                stream=None):
+    _check(lib().moe_ffn_gate_up_bwd_data_mx(
+        ctypes.byref(shape), _ptr(dguq, U8T, "dguq"), _ptr(dgus, U8T, "dgus"), _ptr(wgq_t, U8T, "wgq_t"),
+        _ptr(wgs_t, U8T, "wgs_t"), _ptr(wuq_t, U8T, "wuq_t"), _ptr(wus_t, U8T, "wus_t"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_expand_x, BF16, "grad_expand_x"),
+        _stream(stream)))
+
+
+def quant_rows_mx(src, nrows=None, stream=None):
+    """MX e4m3 codes (R, C) and E8M0 scale bytes (R, C/32) of a bf16 (R, C) matrix."""
+    R, C = src.shape
+    codes = torch.empty((R, C), dtype=U8T, device=src.device)
+    scales = torch.empty((R, C // 32), dtype=U8T, device=src.device)
+    moe_quant_rows_mx(src, codes, scales, nrows, stream)
+    return codes, scales
+
+
 def moe_router(logits, K, renorm, topk_idx, topk_weights, stream=None):
     T, n = logits.shape
     _check(lib().moe_router(T, n, int(K), int(bool(renorm)), _ptr(logits, F32, "logits"),
@@ -477,6 +540,25 @@ class Fp8Weights:
                        torch.empty((E, K, N), dtype=U8T, device=w.device),
                        torch.empty((E, N // 128, K // 128), dtype=F32T, device=w.device))
         moe_quantize_weights_fp8(w, q.codes, q.codes_t, q.scales, stream)
+        return q
+
+
+@dataclass
+class MxWeights:
+    """MX e4m3 codes of one weight tensor (E, N, K): along K (codes, scales) for the
+    forward GEMMs and, transposed, along N (codes_t, scales_t) for the data gradients."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    codes_t: torch.Tensor
+    scales_t: torch.Tensor
+
+    @staticmethod
+    def quantize(w, stream=None):
+        E, N, K = w.shape
+        d = w.device
+        q = MxWeights(torch.empty((E, N, K), dtype=U8T, device=d), torch.empty((E, N, K // 32), dtype=U8T, device=d),
+                      torch.empty((E, K, N), dtype=U8T, device=d), torch.empty((E, K, N // 32), dtype=U8T, device=d))
+        moe_quantize_weights_mx(w, q.codes, q.scales, q.codes_t, q.scales_t, stream)
         return q
 
 

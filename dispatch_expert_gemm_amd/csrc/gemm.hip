@@ -105,6 +105,13 @@ struct GemmArgs {
   uint8_t* qc;
   float* sc;
   int64_t ldq;
+  // microscaled fp8 (MX): E8M0 scale bytes, one per 32 codes along K: A rows of
+  // mlda bytes; B (weights) rows of mldb bytes, mbe bytes per expert (gate/up
+  // data gradient: mB0 for K < F, mB1 for the rest)
+  const uint8_t* mA;
+  const uint8_t* mB0;
+  const uint8_t* mB1;
+  int64_t mlda, mldb, mbe;
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
@@ -172,11 +179,14 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // I8 (with FP8 set: the 8-bit operand path): int8 codes with one scale per A
 // row and one per B row (output channel), integer MFMAs accumulated over the
 // whole K, the scales applied once after the loop.
-template <int MODE, int BM, int BN, bool FP8, int BK, int S_, int WM_, int WN_, bool I8>
+// MX (with FP8 set): e4m3 codes with E8M0 scales per 32 codes along K, applied by
+// the MFMA itself (no per-step rescale).
+template <int MODE, int BM, int BN, bool FP8, int BK, int S_, int WM_, int WN_, bool I8, bool MX>
 __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads),
                              (Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kMinBlocks)) void k_gemm(GemmArgs g) {
   using C = Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>;
   static_assert(!I8 || (FP8 && (MODE == GATE_UP_FWD || MODE == DOWN_FWD)), "int8: forward GEMMs on the 8-bit path");
+  static_assert(!MX || (FP8 && !I8 && MODE <= GATE_UP_BWD_DATA), "MX: row-grouped GEMMs on the 8-bit path");
   auto swz = [](int r) { return swzw<BK>(r); };
   auto lds_off = [](int r, int c) { return lds_offw<BK>(r, c); };
   constexpr bool KGROUP = C::KGROUP, B_KC = C::B_KC;
@@ -389,12 +399,20 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   for (int q = 0; q < BM / 64; ++q) {
     const int r = q * 64 + lane;
     const int rr = r < rows_valid ? r : rows_valid - 1;
-    vos[q] = (uint32_t)(KGROUP ? rr * 4 : (row0 + rr) * nks * 4);
+    vos[q] = (uint32_t)(MX ? rr * g.mlda : (KGROUP ? rr * 4 : (row0 + rr) * nks * 4));
   }
 #pragma unroll
   for (int q = 0; q < BN / 64; ++q) {
-    const int64_t n = n0 + q * 64 + lane;
-    vosb[q] = (uint32_t)(((n < g.N ? n : g.N - 1) - n0) * 4);
+    if constexpr (MX) {
+      // B tile row q*64 + lane: its channel relative to n0 (gate/up forward: rows
+      // BN/2.. are the up matrix's channels n0..)
+      const int rb = MODE == GATE_UP_FWD ? ((q * 64 + lane) & (BN / 2 - 1)) : q * 64 + lane;
+      const int64_t lim = (MODE == GATE_UP_FWD ? g.F : g.N) - 1 - n0;
+      vosb[q] = (uint32_t)((rb < lim ? rb : lim) * g.mldb);
+    } else {
+      const int64_t n = n0 + q * 64 + lane;
+      vosb[q] = (uint32_t)(((n < g.N ? n : g.N - 1) - n0) * 4);
+    }
   }
   auto lds_dword = [](const i32x4& r, const float* lds, uint32_t vo) {
     const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) float*)(lds));
@@ -403,7 +421,25 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   auto issue_scales = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
     if (wv != 0) return;
-    if constexpr (KGROUP) {
+    if constexpr (MX) {
+      // the step's four scale bytes of each A row and each B row, one dword each
+      const int64_t k0 = kt * 128;
+      const auto ra = rsrc8(g.mA + row0 * g.mlda + k0 / 32);
+#pragma unroll
+      for (int q = 0; q < BM / 64; ++q) lds_dword(ra, &sAl[st][q * 64], vos[q]);
+#pragma unroll
+      for (int q = 0; q < BN / 64; ++q) {
+        const uint8_t* base;
+        if constexpr (MODE == GATE_UP_FWD)
+          base = (q * 64 >= BN / 2 ? g.mB1 : g.mB0) + e * g.mbe + n0 * g.mldb + k0 / 32;
+        else if constexpr (MODE == GATE_UP_BWD_DATA)
+          base = k0 < g.F ? g.mB0 + e * g.mbe + n0 * g.mldb + k0 / 32
+                          : g.mB1 + e * g.mbe + n0 * g.mldb + (k0 - g.F) / 32;
+        else
+          base = g.mB0 + e * g.mbe + n0 * g.mldb + k0 / 32;
+        lds_dword(rsrc8(base), &sBl[st][q * 64], vosb[q]);
+      }
+    } else if constexpr (KGROUP) {
       const auto ra = rsrc8(g.sA + (slot0 + kt) * g.M + row0);
 #pragma unroll
       for (int q = 0; q < BM / 64; ++q) lds_dword(ra, &sAl[st][q * 64], vos[q]);
@@ -420,7 +456,46 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     constexpr int st = decltype(ST)::value;
     const bf16_t* as = As(st);
     const bf16_t* bs = Bs(st);
-    if constexpr (I8) {
+    if constexpr (MX) {
+      // two 32x32x64 MFMAs per 128-code step, the E8M0 scales applied by the
+      // MFMA: its K block 0 is bytes 0-15 of lanes 0-31 then of lanes 32-63
+      // (scale from lanes 0-31), block 1 their bytes 16-31 (scale from lanes
+      // 32-63), so lane l takes chunks 4 kk + l/32 and 4 kk + 2 + l/32 and the
+      // two blocks are the step's 32-code blocks 2 kk and 2 kk + 1; the row's
+      // four scale bytes, shifted by one byte in lanes 32-63, give both blocks'
+      // scales at byte 2 kk
+      uint32_t sar[TI], sbr[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) sar[i] = __float_as_uint(sAl[st][arow[i]]) >> (8 * (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) sbr[j] = __float_as_uint(sBl[st][brw[j]]) >> (8 * (lane >> 5));
+      auto sub = [&](auto KK) {
+        constexpr int kk = decltype(KK)::value;
+        const int clo = 4 * kk + (lane >> 5), chi = clo + 2;
+        i32x8 fa[TI], fb[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(as + lds_offw<64>(arow[i], clo));
+          const uint4 hi = *reinterpret_cast<const uint4*>(as + lds_offw<64>(arow[i], chi));
+          fa[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(bs + lds_offw<64>(brw[j], clo));
+          const uint4 hi = *reinterpret_cast<const uint4*>(bs + lds_offw<64>(brw[j], chi));
+          fb[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 2 * kk,
+                                                                       (int)sbr[j], 2 * kk, (int)sar[i]);
+      };
+      sub(std::integral_constant<int, 0>());
+      sub(std::integral_constant<int, 1>());
+      return;
+    } else if constexpr (I8) {
       // four 32x32x32 int8 MFMAs per 128-code step; lane l supplies the 16
       // codes of chunk 2 kk + l/32 of its row (the same K split for A and B,
       // which is all a dot product needs)
@@ -514,7 +589,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   // K steps: 128-wide blocks of K, or the expert's token slots
   const int64_t nk = KGROUP ? (klen + 127) / 128 : g.Kd / 128;
   // B block scales of every K step, read once before the pipeline starts
-  if constexpr (!KGROUP && !I8)
+  if constexpr (!KGROUP && !I8 && !MX)
     for (int64_t kb = tid; kb < nk; kb += kThreads) {
       sBl[0][kb] = bscale(kb * 128, 0);
       if (MODE == GATE_UP_FWD) sBl[1][kb] = bscale(kb * 128, 1);
@@ -1200,7 +1275,8 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   }
 }
 
-template <int MODE, int BM, int BN, bool FP8, int BK = 64, int S = 2, int WM = 2, int WN = 2, bool I8 = false>
+template <int MODE, int BM, int BN, bool FP8, int BK = 64, int S = 2, int WM = 2, int WN = 2, bool I8 = false,
+          bool MX = false>
 moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
   const int64_t bn_cols = MODE == GATE_UP_FWD ? BN / 2 : BN;
@@ -1235,12 +1311,12 @@ moe_status launch_cfg(GemmArgs g, const moe_shape* s, hipStream_t strm) {
   if (g.tiles == 0) return MOE_OK;
   const int64_t grid = (g.tiles + 7) / 8 * 8;  // weight gradients: already 8 * E * block
   if (grid > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
-  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8, BK, S, WM, WN, I8>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_gemm<MODE, BM, BN, FP8, BK, S, WM, WN, I8, MX>), dim3((unsigned)grid),
                      dim3(Cfg<MODE, BM, BN, FP8, BK, S, WM, WN>::kThreads), 0, strm, g);
   return launch_status();
 }
 
-template <int MODE, bool FP8 = false, bool I8 = false>
+template <int MODE, bool FP8 = false, bool I8 = false, bool MX = false>
 moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // Tile shapes per GEMM kind, chosen by measurement on MI355X (MoE layers at
   // H = 1536 / F = 480 and H = 7168 / F = 2048): 128 x 256 tiles (wave tiles
@@ -1255,7 +1331,9 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // 256 x 256 tiles lost for the backward GEMMs: the SwiGLU backward epilogue
   // runs four wave-column passes, and the weight gradients get too few tiles
   // per expert block.
-  if constexpr (I8) {
+  if constexpr (MX) {
+    return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, false, true>(g, s, strm);
+  } else if constexpr (I8) {
     return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, true>(g, s, strm);
   } else if constexpr (FP8) {
     return launch_cfg<MODE, 128, 128, true>(g, s, strm);
@@ -1753,4 +1831,115 @@ extern "C" moe_status moe_ffn_down_fwd_int8(const moe_shape* s, const int8_t* hq
   g.Kd = s->F;
   g.C0 = static_cast<bf16_t*>(y);
   return launch<DOWN_FWD, true, true>(g, s, as_stream(stream));
+}
+
+// ----------------------------------------------------------------------------- MX (microscaled fp8) entries
+
+extern "C" moe_status moe_ffn_gate_up_fwd_mx(const moe_shape* s, const uint8_t* xq, const uint8_t* xs,
+                                             const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
+                                             const uint8_t* wus, const int32_t* ep_recv_counts,
+                                             void* gate_up_save, void* h_act, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wgq || !wgs || !wuq || !wus || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!xq || !xs || !gate_up_save || !h_act) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = xq;
+  g.lda = s->H;
+  g.qB0 = wgq;
+  g.qB1 = wuq;
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.mA = xs;
+  g.mlda = s->H / 32;
+  g.mB0 = wgs;  // (E, F, H/32)
+  g.mB1 = wus;
+  g.mldb = s->H / 32;
+  g.mbe = s->F * (s->H / 32);
+  g.N = s->F;
+  g.Kd = s->H;
+  g.C0 = static_cast<bf16_t*>(h_act);
+  g.C1 = static_cast<bf16_t*>(gate_up_save);
+  return launch<GATE_UP_FWD, true, false, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_down_fwd_mx(const moe_shape* s, const uint8_t* hq, const uint8_t* hs,
+                                          const uint8_t* wdq, const uint8_t* wds, const int32_t* ep_recv_counts,
+                                          void* y, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wdq || !wds || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!hq || !hs || !y) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = hq;
+  g.lda = s->F;
+  g.qB0 = wdq;
+  g.ldb = s->F;
+  g.bstride = s->H * s->F;
+  g.mA = hs;
+  g.mlda = s->F / 32;
+  g.mB0 = wds;  // (E, H, F/32)
+  g.mldb = s->F / 32;
+  g.mbe = s->H * (s->F / 32);
+  g.N = s->H;
+  g.Kd = s->F;
+  g.C0 = static_cast<bf16_t*>(y);
+  return launch<DOWN_FWD, true, false, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_down_bwd_data_mx(const moe_shape* s, const uint8_t* dyq, const uint8_t* dys,
+                                               const uint8_t* wdq_t, const uint8_t* wds_t,
+                                               const void* gate_up_save, const int32_t* ep_recv_counts,
+                                               void* grad_gate_up, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wdq_t || !wds_t || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!dyq || !dys || !gate_up_save || !grad_gate_up) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = dyq;
+  g.lda = s->H;
+  g.qB0 = wdq_t;  // (E, F, H): row f holds Wd_e[:, f]
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.mA = dys;
+  g.mlda = s->H / 32;
+  g.mB0 = wds_t;  // (E, F, H/32)
+  g.mldb = s->H / 32;
+  g.mbe = s->F * (s->H / 32);
+  g.N = s->F;
+  g.Kd = s->H;
+  g.aux = static_cast<const bf16_t*>(gate_up_save);
+  g.C0 = static_cast<bf16_t*>(grad_gate_up);
+  return launch<DOWN_BWD_DATA, true, false, true>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_gate_up_bwd_data_mx(const moe_shape* s, const uint8_t* dguq, const uint8_t* dgus,
+                                                  const uint8_t* wgq_t, const uint8_t* wgs_t, const uint8_t* wuq_t,
+                                                  const uint8_t* wus_t, const int32_t* ep_recv_counts,
+                                                  void* grad_expand_x, void* stream) {
+  moe_status st = check_fp8_shape(s);
+  if (st != MOE_OK) return st;
+  if (!wgq_t || !wgs_t || !wuq_t || !wus_t || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (s->capacity == 0) return MOE_OK;
+  if (!dguq || !dgus || !grad_expand_x) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.qA = dguq;
+  g.lda = 2 * s->F;
+  g.qB0 = wgq_t;  // (E, H, F): row h holds Wg_e[:, h]
+  g.qB1 = wuq_t;
+  g.ldb = s->F;
+  g.bstride = s->F * s->H;
+  g.mA = dgus;
+  g.mlda = 2 * s->F / 32;
+  g.mB0 = wgs_t;  // (E, H, F/32)
+  g.mB1 = wus_t;
+  g.mldb = s->F / 32;
+  g.mbe = s->H * (s->F / 32);
+  g.N = s->H;
+  g.Kd = 2 * s->F;
+  g.C0 = static_cast<bf16_t*>(grad_expand_x);
+  return launch<GATE_UP_BWD_DATA, true, false, true>(g, s, as_stream(stream));
 }

@@ -216,6 +216,86 @@ __global__ __launch_bounds__(256) void k_quant_rows_int8(const uint4* __restrict
   if (lane == 0) scales[r] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
 }
 
+// Microscaled e4m3 (E8M0 scale per 32 values): the scale is the smallest power of
+// two 2^e with amax / 2^e <= 448; with amax = M * 2^E (1 <= M < 2) that is e = E - 8,
+// or E - 7 when M > 1.75 (mantissa bits above 0x600000), clamped to [-127, 127]
+// (zero and subnormal amax give -127).  Scale byte e + 127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int biased = (int)(b >> 23);
+  int e = biased - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  if (biased == 0) e = -127;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^-e as a float (e in [-126, 126]; -127 gives 2^127)
+__device__ __forceinline__ float mx_inv(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// rows: 4 lanes per 32-value block, 8 values each (one 16-byte load, one 8-byte store)
+__global__ __launch_bounds__(256) void k_quant_rows_mx(const uint4* __restrict__ src, int64_t R, int64_t C,
+                                                       const int32_t* __restrict__ nrows, uint2* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // vector of 8 values
+  const int64_t Cv = C / 8;
+  const int64_t r = i / Cv;
+  int64_t rows = nrows ? (int64_t)*nrows : R;
+  if (rows > R) rows = R;
+  // C is a multiple of 32, so the 4 lanes of a block are in one row and leave together
+  if (r >= rows) return;
+  float f[8];
+  unpack8(src[i], f);
+  float m = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(f[q]));
+  m = fmaxf(m, __shfl_xor(m, 1, 4));
+  m = fmaxf(m, __shfl_xor(m, 2, 4));
+  const int e = mx_exponent(m);
+  const float inv = mx_inv(e);
+  codes[i] = make_uint2(e4m3x4(__fmul_rn(f[0], inv), __fmul_rn(f[1], inv), __fmul_rn(f[2], inv), __fmul_rn(f[3], inv)),
+                        e4m3x4(__fmul_rn(f[4], inv), __fmul_rn(f[5], inv), __fmul_rn(f[6], inv), __fmul_rn(f[7], inv)));
+  if ((i & 3) == 0) scales[i / 4] = (uint8_t)(e + 127);
+}
+
+// transposed weights: one workgroup per (expert, 32 rows n, 128 columns k) of W
+// (E, N, K); thread t takes column k = t/2 and rows 16 (t%2) .. +15 of the tile,
+// writes the 16 codes of W^T row k (the 32-block n0 .. n0+31 is shared with its
+// neighbour lane) and the block's scale
+__global__ __launch_bounds__(256) void k_quant_weights_mx_t(const uint4* __restrict__ w, int64_t N, int64_t K,
+                                                            uint8_t* __restrict__ codes_t,
+                                                            uint8_t* __restrict__ scales_t) {
+  const int64_t nbk = K / 128, nbn = N / 32;
+  const int64_t b = blockIdx.x;
+  const int64_t e = b / (nbn * nbk), rem = b % (nbn * nbk);
+  const int64_t n0 = (rem / nbk) * 32, k0 = (rem % nbk) * 128;
+  const int t = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) bf16_t tile[32][136];
+  // 32 rows x 16 vectors of 8: two per thread
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int v = t + 256 * j, row = v / 16, c8 = (v % 16) * 8;
+    *reinterpret_cast<uint4*>(&tile[row][c8]) = w[((e * N + n0 + row) * K + k0 + c8) / 8];
+  }
+  __syncthreads();
+  const int col = t >> 1, h = t & 1;
+  float f[16];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    f[i] = bf2f(tile[16 * h + i][col]);
+    m = fmaxf(m, fabsf(f[i]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  const int ex = mx_exponent(m);
+  const float inv = mx_inv(ex);
+  uint32_t wd[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    wd[q] = e4m3x4(__fmul_rn(f[4 * q], inv), __fmul_rn(f[4 * q + 1], inv), __fmul_rn(f[4 * q + 2], inv),
+                   __fmul_rn(f[4 * q + 3], inv));
+  const int64_t rowt = e * K + k0 + col;  // row of W^T
+  *reinterpret_cast<uint4*>(codes_t + rowt * N + n0 + 16 * h) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (h == 0) scales_t[rowt * (N / 32) + n0 / 32] = (uint8_t)(ex + 127);
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -274,5 +354,33 @@ extern "C" moe_status moe_quant_rows_int8(int64_t R, int64_t C, const void* src,
   if (blocks > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(k_quant_rows_int8, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const uint4*>(src), R, C, nrows, reinterpret_cast<uint2*>(codes), scales);
+  return launch_status();
+}
+
+extern "C" moe_status moe_quant_rows_mx(int64_t R, int64_t C, const void* src, const int32_t* nrows,
+                                        uint8_t* codes, uint8_t* scales, void* stream) {
+  if (R < 0 || C <= 0 || C % 32 != 0 || R * C >= ((int64_t)1 << 40)) return MOE_ERR_BAD_SHAPE;
+  if (R == 0) return MOE_OK;
+  if (!src || !codes || !scales) return MOE_ERR_NULL_ARG;
+  const int64_t blocks = (R * (C / 8) + 255) / 256;
+  if (blocks > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(k_quant_rows_mx, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(src), R, C, nrows, reinterpret_cast<uint2*>(codes), scales);
+  return launch_status();
+}
+
+extern "C" moe_status moe_quantize_weights_mx(int64_t E, int64_t N, int64_t K, const void* w, uint8_t* codes,
+                                              uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                                              void* stream) {
+  if (E <= 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  if (E * N * K >= ((int64_t)1 << 40)) return MOE_ERR_BAD_SHAPE;
+  if (!w || !codes || !scales) return MOE_ERR_NULL_ARG;
+  if (!codes_t != !scales_t) return MOE_ERR_NULL_ARG;
+  moe_status st = moe_quant_rows_mx(E * N, K, w, nullptr, codes, scales, stream);
+  if (st != MOE_OK || !codes_t) return st;
+  const int64_t blocks = E * (N / 32) * (K / 128);
+  if (blocks > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(k_quant_weights_mx_t, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(w), N, K, codes_t, scales_t);
   return launch_status();
 }

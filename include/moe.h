@@ -379,6 +379,56 @@ moe_status moe_ffn_gate_up_bwd_weight_fp8(const moe_shape* s, const uint8_t* dgu
                                           const int32_t* ep_recv_counts, float* grad_w_gate,
                                           float* grad_w_up, void* stream);
 
+/* ------------------------------------------------------ microscaled fp8 (MX)
+ * The fp8 GEMMs with gfx950's block-scaled MFMA doing the scaling: every e4m3
+ * operand carries one E8M0 scale byte (2^(byte-127)) per 32 consecutive codes
+ * of its contraction dimension.  The scale is the smallest power of two that
+ * brings the block's largest magnitude within 448 (amax = M * 2^E, 1 <= M < 2:
+ * 2^(E-8), or 2^(E-7) when M > 1.75; clamped to 2^-127 .. 2^127; an all-zero
+ * block gets byte 0), so no code saturates; codes = e4m3(x / scale).  The
+ * recipe is this library's (the survey's NEXT-2 names the hardware feature; the
+ * pages give no recipe).  Weights are quantised twice: along H (the forward
+ * GEMMs) and, transposed, along F or H (the data gradients).  Shape rules of
+ * the fp8 path (H, F multiples of 128).
+ */
+
+/* Rows of a bf16 (R, C) matrix, C a multiple of 32: codes (R, C) uint8, scale
+ * bytes (R, C/32); nrows as in moe_quant_rows_fp8.  One kernel launch. */
+moe_status moe_quant_rows_mx(int64_t R, int64_t C, const void* src, const int32_t* nrows,
+                             uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Expert weights (E, N, K) bf16, N and K multiples of 128: codes (E, N, K) with
+ * scales (E, N, K/32) along K, and (optional, both or neither) the transposes
+ * codes_t (E, K, N) with scales_t (E, K, N/32) along N.  Two kernel launches. */
+moe_status moe_quantize_weights_mx(int64_t E, int64_t N, int64_t K, const void* w, uint8_t* codes,
+                                   uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, void* stream);
+
+/* MX moe_ffn_gate_up_fwd: xq/xs = moe_quant_rows_mx of expand_x; wgq/wgs,
+ * wuq/wus = moe_quantize_weights_mx codes/scales of w_gate, w_up. */
+moe_status moe_ffn_gate_up_fwd_mx(const moe_shape* s, const uint8_t* xq, const uint8_t* xs,
+                                  const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
+                                  const uint8_t* wus, const int32_t* ep_recv_counts,
+                                  void* gate_up_save, void* h_act, void* stream);
+
+/* MX moe_ffn_down_fwd: hq/hs = moe_quant_rows_mx of h_act; wdq/wds of w_down. */
+moe_status moe_ffn_down_fwd_mx(const moe_shape* s, const uint8_t* hq, const uint8_t* hs,
+                               const uint8_t* wdq, const uint8_t* wds, const int32_t* ep_recv_counts,
+                               void* y, void* stream);
+
+/* MX moe_ffn_down_bwd_data: dyq/dys = moe_quant_rows_mx of grad_y; wdq_t/wds_t =
+ * the transposed codes/scales of w_down ((E, F, H), (E, F, H/32)). */
+moe_status moe_ffn_down_bwd_data_mx(const moe_shape* s, const uint8_t* dyq, const uint8_t* dys,
+                                    const uint8_t* wdq_t, const uint8_t* wds_t, const void* gate_up_save,
+                                    const int32_t* ep_recv_counts, void* grad_gate_up, void* stream);
+
+/* MX moe_ffn_gate_up_bwd_data: dguq/dgus = moe_quant_rows_mx of grad_gate_up;
+ * wgq_t/wgs_t, wuq_t/wus_t = transposed codes/scales of w_gate, w_up ((E, H, F),
+ * (E, H, F/32)). */
+moe_status moe_ffn_gate_up_bwd_data_mx(const moe_shape* s, const uint8_t* dguq, const uint8_t* dgus,
+                                       const uint8_t* wgq_t, const uint8_t* wgs_t, const uint8_t* wuq_t,
+                                       const uint8_t* wus_t, const int32_t* ep_recv_counts,
+                                       void* grad_expand_x, void* stream);
+
 /* ------------------------------------------------------------------ int8 path
  * The decode regime of the low_latency_combine page's examples: dispatch with
  * quant_mode 2 ("dynamic quantization") returns an int8 expand_x and

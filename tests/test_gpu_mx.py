@@ -1,0 +1,112 @@
+"""GPU parity of the microscaled fp8 (MX) path: the MX quantisers bit-exact against the
+oracle (codes and E8M0 scale bytes), the four MX GEMMs (block-scaled MFMA applying the
+scales) and the whole MX layer against the oracle's MX functions at the fp8 bar
+(max|err| <= 2e-2 * max(1, max|ref|), relative L2 <= 2e-2)."""
+import numpy as np
+import pytest
+import torch
+
+import dispatch_expert_gemm_amd as dm
+import moe_workloads as wl
+import oracle as orc
+from gpu_util import DEV, Run, bf, check_close, check_equal, f32
+
+pytestmark = pytest.mark.gpu
+
+REL_FP8 = 2e-2
+
+
+def _u8(t):
+    return t.detach().cpu().numpy()
+
+
+def test_quant_rows_mx_bit_exact():
+    rng = np.random.default_rng(81)
+    R, C = 75, 512
+    a = (rng.standard_normal((R, C)) * np.exp2(rng.integers(-40, 40, size=(R, 1)))).astype(np.float32)
+    a[3] = 0.0                                   # all-zero row
+    a[5, 32:64] = 0.0                            # all-zero block
+    a[7, :32] = 448.0                            # maximum exactly 448 * 2^0
+    a[8, :32] = 449.0                            # just above: the next scale
+    a[9] = rng.standard_normal(C) * 1e-39        # subnormal block maxima (scale clamps at 2^-127)
+    a[10] = rng.standard_normal(C) * 3e36        # near the top of the bf16 range
+    a[11, ::5] = -a[11, ::5]
+    bits = orc.f32_to_bf16(a)
+    codes, scales = dm.quant_rows_mx(bf(bits))
+    torch.cuda.synchronize()
+    q, s = orc.quant_mx_e4m3_rows(orc.bf16_to_f32(bits))
+    check_equal("codes", _u8(codes), q)
+    check_equal("scales", _u8(scales), s)
+    # the device row count
+    codes2 = torch.full((R, C), 0xAB, dtype=torch.uint8, device=DEV)
+    scales2 = torch.full((R, C // 32), 0xCD, dtype=torch.uint8, device=DEV)
+    dm.moe_quant_rows_mx(bf(bits), codes2, scales2, nrows=torch.tensor([30], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    check_equal("codes rows<30", _u8(codes2)[:30], q[:30])
+    assert (_u8(codes2)[30:] == 0xAB).all() and (_u8(scales2)[30:] == 0xCD).all()
+
+
+def test_quantize_weights_mx_bit_exact():
+    rng = np.random.default_rng(82)
+    E, N, K = 3, 256, 384
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    w[1, :64, 128:160] = 0.0
+    bits = wl.to_bf16_bits(w)
+    m = dm.MxWeights.quantize(bf(bits))
+    torch.cuda.synchronize()
+    c, s, ct, st = orc.quant_weights_mx(bits)
+    check_equal("codes", _u8(m.codes), c)
+    check_equal("scales", _u8(m.scales), s)
+    check_equal("codes_t", _u8(m.codes_t), ct)
+    check_equal("scales_t", _u8(m.scales_t), st)
+
+
+MX_CASES = {
+    "small": dict(T=300, H=256, F=384, E=5, K=2),
+    "ragged_rows": dict(T=517, H=512, F=256, E=7, K=3),
+    "empty_experts": dict(T=40, H=128, F=128, E=12, K=1),
+    "wide": dict(T=700, H=1024, F=640, E=3, K=2),
+}
+
+
+@pytest.mark.parametrize("name", list(MX_CASES))
+def test_mx_grouped_ffn_forward_and_data_gradients(name):
+    inp = wl.layer_inputs(seed=83, **MX_CASES[name])
+    print(f"[mx] case={name}", flush=True)
+    run = Run(inp)
+    run.dispatch()
+    F, H, cap = inp["F"], inp["H"], run.cap
+    recv = run.d.ep_recv_counts
+    nrows = recv[-1:]
+    wq = [dm.MxWeights.quantize(bf(inp[k])) for k in ("w_gate", "w_up", "w_down")]
+    xq, xs = dm.quant_rows_mx(run.d.expand_x, nrows)
+    gus = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+    h = torch.empty((cap, F), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+    dm.moe_ffn_gate_up_fwd_mx(run.shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h)
+    hq, hs = dm.quant_rows_mx(h, nrows)
+    dm.moe_ffn_down_fwd_mx(run.shape, hq, hs, wq[2].codes, wq[2].scales, recv, y)
+    dY_bits = wl.to_bf16_bits(np.random.default_rng(84).standard_normal((cap, H), dtype=np.float32) * 0.125)
+    dyq, dys = dm.quant_rows_mx(bf(dY_bits), nrows)
+    ggu = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
+    dm.moe_ffn_down_bwd_data_mx(run.shape, dyq, dys, wq[2].codes_t, wq[2].scales_t, gus, recv, ggu)
+    dgq, dgs = dm.quant_rows_mx(ggu, nrows)
+    gxe = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+    dm.moe_ffn_gate_up_bwd_data_mx(run.shape, dgq, dgs, wq[0].codes_t, wq[0].scales_t, wq[1].codes_t,
+                                   wq[1].scales_t, recv, gxe)
+    torch.cuda.synchronize()
+    r = orc.route(inp["topk_idx"], inp["E"])
+    A = r.A
+    X = orc.dispatch(inp["x"], r)
+    owq = tuple(orc.quant_weights_mx(inp[k]) for k in ("w_gate", "w_up", "w_down"))
+    G, U, Hh, Y = orc.ffn_fwd_mx(X, r.ep_recv_counts, *owq)
+    # G and U come from bit-identical codes and scales on both sides: only the fp32
+    # accumulation order and the odd bf16 rounding differ, so a tight bar catches a
+    # scale applied to the wrong 32-code block
+    check_close("G", f32(gus[:A, :F]), G, rel_l2=2e-3)
+    check_close("U", f32(gus[:A, F:]), U, rel_l2=2e-3)
+    check_close("h", f32(h[:A]), Hh, rel_l2=REL_FP8)
+    check_close("y", f32(y[:A]), Y, rel_l2=REL_FP8)
+    dGU, dX, _, _, _ = orc.ffn_bwd_mx(orc.bf16_to_f32(dY_bits)[:A], X, G, U, Hh, r.ep_recv_counts, *owq)
+    check_close("grad_gate_up", f32(ggu[:A]), dGU, rel_l2=REL_FP8)
+    check_close("grad_expand_x", f32(gxe[:A]), dX, rel_l2=REL_FP8)
