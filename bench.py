@@ -55,6 +55,9 @@ WORKLOADS = {
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
     # the same layer with the weight gradients in fp8 too (per-128-token operands)
     "mixtral_fp8w": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True, fp8_wgrad=True),
+    # the same layer with microscaled e4m3 (E8M0 scale per 32 values, applied by the
+    # block-scaled MFMA) for the forward and data-gradient GEMMs
+    "mixtral_mx": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True, mx=True),
     # combine only: 256 routed + 1 zero + 1 copy + 2 constant experts, 2-D mask
     # with 10% false, shared_expert_x; the step is combine, combine backward and
     # dispatch backward (on the expert-output buffer)
@@ -150,6 +153,9 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
     while True:
         if cfg.get("int8"):
             f = orc.layer_fwd_int8(inp, smooth)
+        elif cfg.get("mx"):
+            f = orc.layer_fwd_mx(inp)
+            orc.layer_bwd_mx(inp, f, inp["grad_out"])
         elif fp8:
             f = orc.layer_fwd_fp8(inp)
             orc.layer_bwd_fp8(inp, f, inp["grad_out"], wgrad="fp8" if cfg.get("fp8_wgrad") else "bf16")
@@ -275,6 +281,7 @@ def build_step(name, T_override=None):
     shared = cfg.get("shared", False)
     fp8 = cfg.get("fp8", False)
     fp8w = fp8 and cfg.get("fp8_wgrad", False)
+    mx = fp8 and cfg.get("mx", False)
     int8 = cfg.get("int8", False)
     log(f"[bench] {name}: generating inputs T={T} H={H} F={F} E={E} K={K}")
     inp = wl.layer_inputs(T, H, F, E, K, seed=0, zipf=cfg.get("zipf"), shared=shared)
@@ -318,6 +325,21 @@ def build_step(name, T_override=None):
             ("moe_quant_rows_int8 (h)", lambda: dm.moe_quant_rows_int8(h, hq8, hs8, recv[-1:])),
             ("moe_ffn_down_fwd_int8", lambda: dm.moe_ffn_down_fwd_int8(shape, hq8, hs8, wq8[2][0], wq8[2][1],
                                                                        recv, y)),
+        ]
+    elif mx:
+        st.dtype = "fp8 e4m3 with E8M0 scales per 32 values (fwd + data grads), bf16 (weight grads)"
+        nrows = recv[-1:]
+        wqm = [dm.MxWeights.quantize(t) for t in (wg, wu, wd)]
+        u8 = torch.uint8
+        xq, xs, hq, hs = z(cap, H, dt=u8), z(cap, H // 32, dt=u8), z(cap, F, dt=u8), z(cap, F // 32, dt=u8)
+        dyq, dys, dgq, dgs = z(cap, H, dt=u8), z(cap, H // 32, dt=u8), z(cap, 2 * F, dt=u8), z(cap, 2 * F // 32, dt=u8)
+        C += [
+            ("moe_quant_rows_mx (x)", lambda: dm.moe_quant_rows_mx(ex, xq, xs, nrows)),
+            ("moe_ffn_gate_up_fwd_mx", lambda: dm.moe_ffn_gate_up_fwd_mx(
+                shape, xq, xs, wqm[0].codes, wqm[0].scales, wqm[1].codes, wqm[1].scales, recv, gus, h)),
+            ("moe_quant_rows_mx (h)", lambda: dm.moe_quant_rows_mx(h, hq, hs, nrows)),
+            ("moe_ffn_down_fwd_mx", lambda: dm.moe_ffn_down_fwd_mx(shape, hq, hs, wqm[2].codes, wqm[2].scales,
+                                                                   recv, y)),
         ]
     elif fp8:
         st.dtype = ("fp8 e4m3 (all six GEMMs; weight grads on per-128-token operands)" if fp8w
@@ -379,7 +401,17 @@ def build_step(name, T_override=None):
     # backward order: each gather/scatter right after the kernel that produced
     # its input (grad_expand_x goes to dispatch backward before the last
     # weight gradient evicts it from the caches)
-    if fp8w:
+    if mx:
+        C += [
+            ("moe_quant_rows_mx (dY)", lambda: dm.moe_quant_rows_mx(gy, dyq, dys, nrows)),
+            ("moe_ffn_down_bwd_data_mx", lambda: dm.moe_ffn_down_bwd_data_mx(
+                shape, dyq, dys, wqm[2].codes_t, wqm[2].scales_t, gus, recv, ggu)),
+            ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
+            ("moe_quant_rows_mx (dGU)", lambda: dm.moe_quant_rows_mx(ggu, dgq, dgs, nrows)),
+            ("moe_ffn_gate_up_bwd_data_mx", lambda: dm.moe_ffn_gate_up_bwd_data_mx(
+                shape, dgq, dgs, wqm[0].codes_t, wqm[0].scales_t, wqm[1].codes_t, wqm[1].scales_t, recv, gxe)),
+        ]
+    elif fp8w:
         C += [
             ("moe_quant_rows_fp8 (dY)", lambda: dm.moe_quant_rows_fp8(gy, dyq, dys, nrows)),
             ("moe_quant_cols_fp8 (dY)", lambda: dm.moe_quant_cols_fp8(gy, recv, *cq["dY"])),
@@ -419,7 +451,11 @@ def build_step(name, T_override=None):
     else:
         C.append(("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
                                                                                       gwu)))
-    if fp8:
+    if mx:
+        # weight quantisation (once per weight update, both layouts) is timed outside the step
+        st.extra_calls.insert(0, ("moe_quantize_weights_mx (3 tensors)",
+                                  lambda: [dm.MxWeights.quantize(t) for t in (wg, wu, wd)]))
+    elif fp8:
         # weight quantisation (once per weight update) is timed outside the step
         st.extra_calls.insert(0, ("moe_quantize_weights_fp8 (3 tensors)",
                                   lambda: [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)]))
@@ -472,6 +508,8 @@ def account(st, A):
         key = n + "_fp8" if fp8 and ("fwd" in n or "data" in n or fp8w) else n
         if int8:
             key = n + "_int8"
+        if st.cfg.get("mx") and ("fwd" in n or "data" in n):
+            key = n + "_mx"
         if fwd_only and "fwd" not in n:
             continue
         fl[key] = (mult * A * H * F, peak)
@@ -490,7 +528,10 @@ def account(st, A):
     if st.cfg.get("shared"):
         nb["moe_combine"] += T * H * 2
         nb["moe_dispatch_bwd"] += T * H * 2
-    if fp8:
+    if st.cfg.get("mx"):
+        for k, d in (("x", H), ("h", F), ("dY", H), ("dGU", 2 * F)):
+            nb[f"moe_quant_rows_mx ({k})"] = A * d * 3 + A * d // 32
+    elif fp8:
         nb["moe_quant_rows_fp8 (x)"] = A * H * 3 + A * H // 128 * 4
         nb["moe_quant_rows_fp8 (h)"] = A * F * 3 + A * F // 128 * 4
         nb["moe_quant_rows_fp8 (dY)"] = A * H * 3 + A * H // 128 * 4
@@ -623,6 +664,8 @@ def main():
         "page1": "Triton-distributed benchmark shape",
         "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
+        "mixtral_mx": "Mixtral-8x7B-style layer, microscaled fp8 e4m3 GEMMs (E8M0 per 32, block-scaled MFMA), "
+                      "int8 combine payload",
         "mixtral_fp8w": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs including the weight "
                         "gradients (per-128-token operands), int8 combine payload",
         "combine_stress": "combine only, 256 routed + 1 zero + 1 copy + 2 constant experts, "

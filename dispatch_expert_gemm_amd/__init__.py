@@ -660,7 +660,7 @@ class _MoELayerFn(torch.autograd.Function):
     def forward(ctx, x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
                 shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1, const_alpha_2,
                 const_v, zero_expert_num, copy_expert_num, const_expert_num, fp8, comm_quant_mode,
-                fp8_wgrad):
+                fp8_wgrad, mx):
         T, H = x.shape
         K = topk_idx.shape[1]
         E, F, _ = w_gate.shape
@@ -677,8 +677,20 @@ class _MoELayerFn(torch.autograd.Function):
         y = torch.empty((cap, H), dtype=BF16, device=dev)
         ctx.fp8 = bool(fp8)
         ctx.fp8_wgrad = ctx.fp8 and bool(fp8_wgrad)
+        ctx.mx = ctx.fp8 and bool(mx)
+        if ctx.mx and ctx.fp8_wgrad:
+            raise MoeError("mx=True runs the weight gradients in bf16 (fp8_wgrad uses fp32 block scales)")
         wq = ()
-        if ctx.fp8:
+        if ctx.mx:
+            nrows = d.ep_recv_counts[-1:]
+            wq = tuple(MxWeights.quantize(w) for w in (w_gate, w_up, w_down))
+            xq, xs = quant_rows_mx(d.expand_x, nrows)
+            moe_ffn_gate_up_fwd_mx(shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales,
+                                   d.ep_recv_counts, gus, h)
+            hq, hs = quant_rows_mx(h, nrows)
+            moe_ffn_down_fwd_mx(shape, hq, hs, wq[2].codes, wq[2].scales, d.ep_recv_counts, y)
+            del xq, xs, hq, hs
+        elif ctx.fp8:
             nrows = d.ep_recv_counts[-1:]
             wq = tuple(Fp8Weights.quantize(w) for w in (w_gate, w_up, w_down))
             xq, xs = quant_rows_fp8(d.expand_x, nrows)
@@ -723,7 +735,7 @@ class _MoELayerFn(torch.autograd.Function):
                               d.ep_recv_counts, gus, h, y, *s_saved)
         # the transposed weight codes of the data-gradient GEMMs (not tensors
         # of the graph, so kept on ctx)
-        ctx.wq = tuple((q.codes_t, q.scales) for q in wq)
+        ctx.wq = tuple((q.codes_t, q.scales_t) if ctx.mx else (q.codes_t, q.scales) for q in wq)
         return out
 
     @staticmethod
@@ -748,7 +760,17 @@ class _MoELayerFn(torch.autograd.Function):
         gwd = torch.empty(w_down.shape, dtype=F32, device=dev)
         # data gradients first, the gate/up weight gradient after dispatch
         # backward (each gather right after the kernel that wrote its input)
-        if ctx.fp8:
+        if ctx.mx:
+            (wgt, wgs), (wut, wus), (wdt, wds) = ctx.wq
+            nrows = recv[-1:]
+            dyq, dys = quant_rows_mx(gy, nrows)
+            moe_ffn_down_bwd_data_mx(shape, dyq, dys, wdt, wds, gus, recv, ggu)
+            del dyq, dys
+            moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
+            dgq, dgs = quant_rows_mx(ggu, nrows)
+            moe_ffn_gate_up_bwd_data_mx(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)
+            del dgq, dgs
+        elif ctx.fp8:
             (wgt, wgs), (wut, wus), (wdt, wds) = ctx.wq
             nrows = recv[-1:]
             dyq, dys = quant_rows_fp8(gy, nrows)
@@ -800,7 +822,7 @@ class _MoELayerFn(torch.autograd.Function):
             moe_ffn_gate_up_bwd_weight(shape, ggu, expand_x, recv, gwg, gwu)
         g_shared = grad_out if ctx.has_shared_x else None
         return (gx, gw, gwg.to(w_gate.dtype), gwu.to(w_up.dtype), gwd.to(w_down.dtype), g_shared,
-                *s_grads, None, None, None, None, None, None, None, None, None, None, None)
+                *s_grads, None, None, None, None, None, None, None, None, None, None, None, None)
 
 
 @dataclass
@@ -853,7 +875,7 @@ def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=
               shared_expert_x=None, shared_w_gate=None, shared_w_up=None, shared_w_down=None,
               const_alpha_1=None, const_alpha_2=None, const_v=None,
               zero_expert_num=0, copy_expert_num=0, const_expert_num=0, fp8=False,
-              comm_quant_mode=0, fp8_wgrad=False):
+              comm_quant_mode=0, fp8_wgrad=False, mx=False):
     """One MoE layer (ori_x is x itself).
 
     The shared-expert term of combine is either given (shared_expert_x) or
@@ -866,9 +888,11 @@ def moe_layer(x, topk_idx, topk_weights, w_gate, w_up, w_down, *, x_active_mask=
     fp8=True runs the routed experts' forward and data-gradient GEMMs on
     block-scaled e4m3 operands (H and F multiples of 128), and with
     fp8_wgrad=True its weight gradients too, on operands requantised per 128
-    tokens of each expert; comm_quant_mode=2 sends the expert outputs through
-    the int8 combine payload."""
+    tokens of each expert; mx=True (with fp8=True) uses microscaled e4m3 (E8M0
+    scale per 32 values, applied by the block-scaled MFMA) instead of fp32 block
+    scales for the forward and data-gradient GEMMs; comm_quant_mode=2 sends the
+    expert outputs through the int8 combine payload."""
     return _MoELayerFn.apply(x, topk_weights, w_gate, w_up, w_down, shared_expert_x, shared_w_gate,
                              shared_w_up, shared_w_down, topk_idx, x_active_mask, const_alpha_1,
                              const_alpha_2, const_v, zero_expert_num, copy_expert_num,
-                             const_expert_num, fp8, comm_quant_mode, fp8_wgrad)
+                             const_expert_num, fp8, comm_quant_mode, fp8_wgrad, mx)

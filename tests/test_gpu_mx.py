@@ -110,3 +110,23 @@ def test_mx_grouped_ffn_forward_and_data_gradients(name):
     dGU, dX, _, _, _ = orc.ffn_bwd_mx(orc.bf16_to_f32(dY_bits)[:A], X, G, U, Hh, r.ep_recv_counts, *owq)
     check_close("grad_gate_up", f32(ggu[:A]), dGU, rel_l2=REL_FP8)
     check_close("grad_expand_x", f32(gxe[:A]), dX, rel_l2=REL_FP8)
+
+
+def test_autograd_layer_mx():
+    """moe_layer(fp8=True, mx=True, comm_quant_mode=2) against the oracle's MX layer."""
+    inp = wl.layer_inputs(384, 256, 256, 6, 2, seed=85, mask="2d", Z=1)
+    x = bf(inp["x"]).requires_grad_(True)
+    w = torch.from_numpy(inp["topk_weights"]).to(DEV).requires_grad_(True)
+    ws = [bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down")]
+    out = dm.moe_layer(x, torch.from_numpy(inp["topk_idx"]).to(DEV), w, *ws,
+                       x_active_mask=torch.from_numpy(inp["mask"]).to(DEV), zero_expert_num=1,
+                       fp8=True, mx=True, comm_quant_mode=2)
+    out.backward(bf(inp["grad_out"]))
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_mx(inp)
+    b = orc.layer_bwd_mx(inp, f, inp["grad_out"])
+    check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
+    check_close("grad_x", f32(x.grad), b["dx"], rel_l2=REL_FP8)
+    check_close("grad_topk_weights", f32(w.grad), b["dw"], rel_l2=REL_FP8)
+    for t, k in zip(ws, ("dWg", "dWu", "dWd")):
+        check_close(k, f32(t.grad), orc.round_bf16(b[k]), rel_l2=REL_FP8)
