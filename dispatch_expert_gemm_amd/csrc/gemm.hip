@@ -105,13 +105,14 @@ struct GemmArgs {
   uint8_t* qc;
   float* sc;
   int64_t ldq;
-  // microscaled fp8 (MX): E8M0 scale bytes, one per 32 codes along K: A rows of
-  // mlda bytes; B (weights) rows of mldb bytes, mbe bytes per expert (gate/up
-  // data gradient: mB0 for K < F, mB1 for the rest)
+  // microscaled fp8 (MX): E8M0 scale bytes, one per 32 codes along K, stored as
+  // one 4-byte word per (row, 128-code K step), words ordered (K step, row): A
+  // has mrA rows per K step; B (weights) mrB rows per K step, mbe per expert
+  // (gate/up data gradient: mB0 for K < F, mB1 for the rest)
   const uint8_t* mA;
   const uint8_t* mB0;
   const uint8_t* mB1;
-  int64_t mlda, mldb, mbe;
+  int64_t mrA, mrB, mbe;
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
@@ -399,7 +400,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   for (int q = 0; q < BM / 64; ++q) {
     const int r = q * 64 + lane;
     const int rr = r < rows_valid ? r : rows_valid - 1;
-    vos[q] = (uint32_t)(MX ? rr * g.mlda : (KGROUP ? rr * 4 : (row0 + rr) * nks * 4));
+    vos[q] = (uint32_t)(MX ? rr * 4 : (KGROUP ? rr * 4 : (row0 + rr) * nks * 4));
   }
 #pragma unroll
   for (int q = 0; q < BN / 64; ++q) {
@@ -408,7 +409,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
       // BN/2.. are the up matrix's channels n0..)
       const int rb = MODE == GATE_UP_FWD ? ((q * 64 + lane) & (BN / 2 - 1)) : q * 64 + lane;
       const int64_t lim = (MODE == GATE_UP_FWD ? g.F : g.N) - 1 - n0;
-      vosb[q] = (uint32_t)((rb < lim ? rb : lim) * g.mldb);
+      vosb[q] = (uint32_t)((rb < lim ? rb : lim) * 4);
     } else {
       const int64_t n = n0 + q * 64 + lane;
       vosb[q] = (uint32_t)(((n < g.N ? n : g.N - 1) - n0) * 4);
@@ -423,20 +424,19 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     if (wv != 0) return;
     if constexpr (MX) {
       // the step's four scale bytes of each A row and each B row, one dword each
-      const int64_t k0 = kt * 128;
-      const auto ra = rsrc8(g.mA + row0 * g.mlda + k0 / 32);
+      const auto ra = rsrc8(g.mA + (kt * g.mrA + row0) * 4);
 #pragma unroll
       for (int q = 0; q < BM / 64; ++q) lds_dword(ra, &sAl[st][q * 64], vos[q]);
 #pragma unroll
       for (int q = 0; q < BN / 64; ++q) {
         const uint8_t* base;
         if constexpr (MODE == GATE_UP_FWD)
-          base = (q * 64 >= BN / 2 ? g.mB1 : g.mB0) + e * g.mbe + n0 * g.mldb + k0 / 32;
+          base = (q * 64 >= BN / 2 ? g.mB1 : g.mB0) + (kt * g.mrB + e * g.mbe + n0) * 4;
         else if constexpr (MODE == GATE_UP_BWD_DATA)
-          base = k0 < g.F ? g.mB0 + e * g.mbe + n0 * g.mldb + k0 / 32
-                          : g.mB1 + e * g.mbe + n0 * g.mldb + (k0 - g.F) / 32;
+          base = kt * 128 < g.F ? g.mB0 + (kt * g.mrB + e * g.mbe + n0) * 4
+                                : g.mB1 + ((kt - g.F / 128) * g.mrB + e * g.mbe + n0) * 4;
         else
-          base = g.mB0 + e * g.mbe + n0 * g.mldb + k0 / 32;
+          base = g.mB0 + (kt * g.mrB + e * g.mbe + n0) * 4;
         lds_dword(rsrc8(base), &sBl[st][q * 64], vosb[q]);
       }
     } else if constexpr (KGROUP) {
@@ -1852,11 +1852,11 @@ extern "C" moe_status moe_ffn_gate_up_fwd_mx(const moe_shape* s, const uint8_t* 
   g.ldb = s->H;
   g.bstride = s->F * s->H;
   g.mA = xs;
-  g.mlda = s->H / 32;
-  g.mB0 = wgs;  // (E, F, H/32)
+  g.mrA = s->capacity;
+  g.mB0 = wgs;  // words (H/128, E*F)
   g.mB1 = wus;
-  g.mldb = s->H / 32;
-  g.mbe = s->F * (s->H / 32);
+  g.mrB = (int64_t)s->num_experts * s->F;
+  g.mbe = s->F;
   g.N = s->F;
   g.Kd = s->H;
   g.C0 = static_cast<bf16_t*>(h_act);
@@ -1879,10 +1879,10 @@ extern "C" moe_status moe_ffn_down_fwd_mx(const moe_shape* s, const uint8_t* hq,
   g.ldb = s->F;
   g.bstride = s->H * s->F;
   g.mA = hs;
-  g.mlda = s->F / 32;
-  g.mB0 = wds;  // (E, H, F/32)
-  g.mldb = s->F / 32;
-  g.mbe = s->H * (s->F / 32);
+  g.mrA = s->capacity;
+  g.mB0 = wds;  // words (F/128, E*H)
+  g.mrB = (int64_t)s->num_experts * s->H;
+  g.mbe = s->H;
   g.N = s->H;
   g.Kd = s->F;
   g.C0 = static_cast<bf16_t*>(y);
@@ -1905,10 +1905,10 @@ extern "C" moe_status moe_ffn_down_bwd_data_mx(const moe_shape* s, const uint8_t
   g.ldb = s->H;
   g.bstride = s->F * s->H;
   g.mA = dys;
-  g.mlda = s->H / 32;
-  g.mB0 = wds_t;  // (E, F, H/32)
-  g.mldb = s->H / 32;
-  g.mbe = s->F * (s->H / 32);
+  g.mrA = s->capacity;
+  g.mB0 = wds_t;  // words (H/128, E*F)
+  g.mrB = (int64_t)s->num_experts * s->F;
+  g.mbe = s->F;
   g.N = s->F;
   g.Kd = s->H;
   g.aux = static_cast<const bf16_t*>(gate_up_save);
@@ -1933,11 +1933,11 @@ extern "C" moe_status moe_ffn_gate_up_bwd_data_mx(const moe_shape* s, const uint
   g.ldb = s->F;
   g.bstride = s->F * s->H;
   g.mA = dgus;
-  g.mlda = 2 * s->F / 32;
-  g.mB0 = wgs_t;  // (E, H, F/32)
+  g.mrA = s->capacity;
+  g.mB0 = wgs_t;  // words (F/128, E*H)
   g.mB1 = wus_t;
-  g.mldb = s->F / 32;
-  g.mbe = s->H * (s->F / 32);
+  g.mrB = (int64_t)s->num_experts * s->H;
+  g.mbe = s->H;
   g.N = s->H;
   g.Kd = 2 * s->F;
   g.C0 = static_cast<bf16_t*>(grad_expand_x);

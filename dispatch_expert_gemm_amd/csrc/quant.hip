@@ -252,15 +252,21 @@ __global__ __launch_bounds__(256) void k_quant_rows_mx(const uint4* __restrict__
   const float inv = mx_inv(e);
   codes[i] = make_uint2(e4m3x4(__fmul_rn(f[0], inv), __fmul_rn(f[1], inv), __fmul_rn(f[2], inv), __fmul_rn(f[3], inv)),
                         e4m3x4(__fmul_rn(f[4], inv), __fmul_rn(f[5], inv), __fmul_rn(f[6], inv), __fmul_rn(f[7], inv)));
-  if ((i & 3) == 0) scales[i / 4] = (uint8_t)(e + 127);
+  // scale layout: the four 32-value blocks of one 128-value column block of one
+  // row are one 4-byte word, words ordered (column block, row), so a GEMM K step
+  // reads the scales of consecutive rows from consecutive words
+  if ((i & 3) == 0) {
+    const int64_t b = (i % Cv) / 4;  // 32-block within the row
+    scales[((b / 4) * R + r) * 4 + (b & 3)] = (uint8_t)(e + 127);
+  }
 }
 
 // transposed weights: one workgroup per (expert, 32 rows n, 128 columns k) of W
 // (E, N, K); thread t takes column k = t/2 and rows 16 (t%2) .. +15 of the tile,
 // writes the 16 codes of W^T row k (the 32-block n0 .. n0+31 is shared with its
 // neighbour lane) and the block's scale
-__global__ __launch_bounds__(256) void k_quant_weights_mx_t(const uint4* __restrict__ w, int64_t N, int64_t K,
-                                                            uint8_t* __restrict__ codes_t,
+__global__ __launch_bounds__(256) void k_quant_weights_mx_t(const uint4* __restrict__ w, int64_t E, int64_t N,
+                                                            int64_t K, uint8_t* __restrict__ codes_t,
                                                             uint8_t* __restrict__ scales_t) {
   const int64_t nbk = K / 128, nbn = N / 32;
   const int64_t b = blockIdx.x;
@@ -293,7 +299,12 @@ __global__ __launch_bounds__(256) void k_quant_weights_mx_t(const uint4* __restr
                    __fmul_rn(f[4 * q + 3], inv));
   const int64_t rowt = e * K + k0 + col;  // row of W^T
   *reinterpret_cast<uint4*>(codes_t + rowt * N + n0 + 16 * h) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-  if (h == 0) scales_t[rowt * (N / 32) + n0 / 32] = (uint8_t)(ex + 127);
+  // words ordered (128-column block of W^T, row of W^T over all experts), as the
+  // row quantiser orders them for the E*K rows of W^T
+  if (h == 0) {
+    const int64_t bn = n0 / 32;
+    scales_t[((bn / 4) * (E * K) + rowt) * 4 + (bn & 3)] = (uint8_t)(ex + 127);
+  }
 }
 
 }  // namespace
@@ -381,6 +392,6 @@ extern "C" moe_status moe_quantize_weights_mx(int64_t E, int64_t N, int64_t K, c
   const int64_t blocks = E * (N / 32) * (K / 128);
   if (blocks > 0x7fffffff) return MOE_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(k_quant_weights_mx_t, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
-                     static_cast<const uint4*>(w), N, K, codes_t, scales_t);
+                     static_cast<const uint4*>(w), E, N, K, codes_t, scales_t);
   return launch_status();
 }

@@ -392,14 +392,20 @@ moe_status moe_ffn_gate_up_bwd_weight_fp8(const moe_shape* s, const uint8_t* dgu
  * the fp8 path (H, F multiples of 128).
  */
 
-/* Rows of a bf16 (R, C) matrix, C a multiple of 32: codes (R, C) uint8, scale
- * bytes (R, C/32); nrows as in moe_quant_rows_fp8.  One kernel launch. */
+/* Rows of a bf16 (R, C) matrix, C a multiple of 32: codes (R, C) uint8 and R*C/32
+ * scale bytes, stored as one 4-byte word per (row, 128 columns) -- the scales of
+ * the four 32-blocks in order -- with words ordered (column block, row): byte
+ * ((c/128) * R + r) * 4 + (c/32) % 4 holds the scale of row r, columns c..c+31
+ * (a GEMM K step then reads consecutive rows' scales from consecutive words).
+ * nrows as in moe_quant_rows_fp8.  One kernel launch. */
 moe_status moe_quant_rows_mx(int64_t R, int64_t C, const void* src, const int32_t* nrows,
                              uint8_t* codes, uint8_t* scales, void* stream);
 
 /* Expert weights (E, N, K) bf16, N and K multiples of 128: codes (E, N, K) with
- * scales (E, N, K/32) along K, and (optional, both or neither) the transposes
- * codes_t (E, K, N) with scales_t (E, K, N/32) along N.  Two kernel launches. */
+ * E*N*K/32 scale bytes along K (moe_quant_rows_mx layout over the E*N rows),
+ * and (optional, both or neither) the transposes codes_t (E, K, N) with their
+ * E*K*N/32 scale bytes along N (the same layout over the E*K rows of the
+ * transposes).  Two kernel launches. */
 moe_status moe_quantize_weights_mx(int64_t E, int64_t N, int64_t K, const void* w, uint8_t* codes,
                                    uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, void* stream);
 

@@ -20,6 +20,11 @@ def _u8(t):
     return t.detach().cpu().numpy()
 
 
+def _rows_view(scale_bytes, R, C):
+    """Device scale words (C/128 planes of R rows x 4 bytes) -> (R, C/32) scale bytes."""
+    return np.asarray(scale_bytes).reshape(C // 128, R, 4).transpose(1, 0, 2).reshape(R, C // 32)
+
+
 def test_quant_rows_mx_bit_exact():
     rng = np.random.default_rng(81)
     R, C = 75, 512
@@ -36,14 +41,15 @@ def test_quant_rows_mx_bit_exact():
     torch.cuda.synchronize()
     q, s = orc.quant_mx_e4m3_rows(orc.bf16_to_f32(bits))
     check_equal("codes", _u8(codes), q)
-    check_equal("scales", _u8(scales), s)
+    check_equal("scales", _rows_view(_u8(scales), R, C), s)
     # the device row count
     codes2 = torch.full((R, C), 0xAB, dtype=torch.uint8, device=DEV)
     scales2 = torch.full((R, C // 32), 0xCD, dtype=torch.uint8, device=DEV)
     dm.moe_quant_rows_mx(bf(bits), codes2, scales2, nrows=torch.tensor([30], dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     check_equal("codes rows<30", _u8(codes2)[:30], q[:30])
-    assert (_u8(codes2)[30:] == 0xAB).all() and (_u8(scales2)[30:] == 0xCD).all()
+    check_equal("scales rows<30", _rows_view(_u8(scales2), R, C)[:30], s[:30])
+    assert (_u8(codes2)[30:] == 0xAB).all() and (_rows_view(_u8(scales2), R, C)[30:] == 0xCD).all()
 
 
 def test_quantize_weights_mx_bit_exact():
@@ -56,9 +62,9 @@ def test_quantize_weights_mx_bit_exact():
     torch.cuda.synchronize()
     c, s, ct, st = orc.quant_weights_mx(bits)
     check_equal("codes", _u8(m.codes), c)
-    check_equal("scales", _u8(m.scales), s)
+    check_equal("scales", _rows_view(_u8(m.scales), E * N, K).reshape(E, N, K // 32), s)
     check_equal("codes_t", _u8(m.codes_t), ct)
-    check_equal("scales_t", _u8(m.scales_t), st)
+    check_equal("scales_t", _rows_view(_u8(m.scales_t), E * K, N).reshape(E, K, N // 32), st)
 
 
 MX_CASES = {
