@@ -346,10 +346,11 @@ def build_step(name, T_override=None):
                     else "fp8 e4m3 (fwd + data grads), bf16 (weight grads)")
         nrows = recv[-1:]
         wq = [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)]
-        xq, xs = z(cap, H, dt=torch.uint8), z(cap, H // 128, dt=f32)
-        hq, hs = z(cap, F, dt=torch.uint8), z(cap, F // 128, dt=f32)
-        dyq, dys = z(cap, H, dt=torch.uint8), z(cap, H // 128, dt=f32)
-        dgq, dgs = z(cap, 2 * F, dt=torch.uint8), z(cap, 2 * F // 128, dt=f32)
+        # row scales are column-block major: (C/128, capacity)
+        xq, xs = z(cap, H, dt=torch.uint8), z(H // 128, cap, dt=f32)
+        hq, hs = z(cap, F, dt=torch.uint8), z(F // 128, cap, dt=f32)
+        dyq, dys = z(cap, H, dt=torch.uint8), z(H // 128, cap, dt=f32)
+        dgq, dgs = z(cap, 2 * F, dt=torch.uint8), z(2 * F // 128, cap, dt=f32)
         C += [
             ("moe_quant_rows_fp8 (x)", lambda: dm.moe_quant_rows_fp8(ex, xq, xs, nrows)),
             ("moe_ffn_gate_up_fwd_fp8", lambda: dm.moe_ffn_gate_up_fwd_fp8(

@@ -576,7 +576,7 @@ def quant_cols_fp8(src, ep_recv_counts, stream=None):
 def quant_rows_fp8(src, nrows=None, stream=None):
     R, C = src.shape
     codes = torch.empty((R, C), dtype=U8T, device=src.device)
-    scales = torch.empty((R, C // 128), dtype=F32T, device=src.device)
+    scales = torch.empty((C // 128, R), dtype=F32T, device=src.device)   # column-block major
     moe_quant_rows_fp8(src, codes, scales, nrows, stream)
     return codes, scales
 
@@ -775,7 +775,7 @@ class _MoELayerFn(torch.autograd.Function):
             nrows = recv[-1:]
             dyq, dys = quant_rows_fp8(gy, nrows)
             dgq = torch.empty((cap, 2 * F), dtype=U8T, device=dev)
-            dgs = torch.empty((cap, 2 * F // 128), dtype=F32T, device=dev)
+            dgs = torch.empty((2 * F // 128, cap), dtype=F32T, device=dev)
             if ctx.fp8_wgrad:
                 ns = cols_fp8_slots(cap, shape.num_experts)
                 dg_cols = (torch.empty((2 * F, 128 * ns), dtype=U8T, device=dev),

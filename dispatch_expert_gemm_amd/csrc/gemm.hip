@@ -87,8 +87,9 @@ struct GemmArgs {
   const bf16_t* aux;
   float* W0;
   float* W1;
-  // fp8 operands: e4m3 codes, A scales per (row, 128 of K) (row stride Kd/128),
-  // B scales per 128 x 128 block at sB[e*sbe + nblock*sbn + kblock*sbk]
+  // fp8 operands: e4m3 codes, A scales per (row, 128 of K) stored K-block major
+  // (sA[kblock * rowsA + row], so a K step's scales of consecutive rows are
+  // consecutive), B scales per 128 x 128 block at sB[e*sbe + nblock*sbn + kblock*sbk]
   const uint8_t* qA;
   const float* sA;
   const uint8_t* qB0;
@@ -96,6 +97,7 @@ struct GemmArgs {
   const float* sB0;
   const float* sB1;
   int64_t sbe, sbn, sbk;
+  int64_t rowsA;  // rows of the expanded activations (capacity)
   // fp8 down data gradient: optional e4m3 codes of the bf16 dG/dU it produces,
   // per (row, 128 columns) (qr/sr, the layout of moe_quant_rows_fp8) and per
   // (128-token slot, column) (qc/sc, the layout of moe_quant_cols_fp8, ldq
@@ -394,13 +396,12 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   __shared__ float sAl[2][BM];
   __shared__ float sBl[2][kMaxKBlocks8];
   static_assert(!KGROUP || BN <= kMaxKBlocks8, "B column scales of one step fit sBl");
-  const int64_t nks = g.Kd / 128;
   uint32_t vos[BM / 64], vosb[BN / 64];
 #pragma unroll
   for (int q = 0; q < BM / 64; ++q) {
     const int r = q * 64 + lane;
     const int rr = r < rows_valid ? r : rows_valid - 1;
-    vos[q] = (uint32_t)(MX ? rr * 4 : (KGROUP ? rr * 4 : (row0 + rr) * nks * 4));
+    vos[q] = (uint32_t)(rr * 4);
   }
 #pragma unroll
   for (int q = 0; q < BN / 64; ++q) {
@@ -447,7 +448,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
 #pragma unroll
       for (int q = 0; q < BN / 64; ++q) lds_dword(rb, &sBl[st][q * 64], vosb[q]);
     } else {
-      const auto r = rsrc8(g.sA + kt);
+      const auto r = rsrc8(g.sA + kt * g.rowsA + row0);
 #pragma unroll
       for (int q = 0; q < BM / 64; ++q) lds_dword(r, &sAl[st][q * 64], vos[q]);
     }
@@ -1199,7 +1200,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
                                      __fmul_rn(f[7], inv));
           const int64_t col = (half ? g.F : 0) + n0;
           *reinterpret_cast<uint2*>(g.qr + (row0 + row) * 2 * g.F + col + sub * 8) = make_uint2(lo, hi);
-          if (sub == 0) g.sr[(row0 + row) * (2 * g.F / 128) + col / 128] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+          if (sub == 0) g.sr[(col / 128) * g.rowsA + row0 + row] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
         }
       }
       if (g.qc) {
@@ -1363,6 +1364,7 @@ GemmArgs base_args(const moe_shape* s, const int32_t* prefix) {
   g.prefix = prefix;
   g.E = s->num_experts;
   g.F = s->F;
+  g.rowsA = s->capacity;
   return g;
 }
 

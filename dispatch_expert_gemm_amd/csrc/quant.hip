@@ -2,7 +2,8 @@
 //
 //  * rows: one scale per (row, 128 consecutive columns), codes = e4m3(x * (448/amax)),
 //    scale = amax/448 (both fp32, correctly rounded); an all-zero block gets codes 0
-//    and scale 1.  16 lanes own one block (8 columns each) of four consecutive
+//    and scale 1.  Scales are stored column-block major, (C/128, R), so a GEMM K
+//    step reads the scales of consecutive rows from consecutive words.  16 lanes own one block (8 columns each) of four consecutive
 //    rows, so the block's amax is a 16-lane butterfly and every load and store is
 //    a full vector.
 //  * weights: one scale per 128 x 128 block of each expert's (out, in) matrix, same
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_fp8(const uint4* __restrict_
     const uint32_t lo = e4m3x4(__fmul_rn(f[0], inv), __fmul_rn(f[1], inv), __fmul_rn(f[2], inv), __fmul_rn(f[3], inv));
     const uint32_t hi = e4m3x4(__fmul_rn(f[4], inv), __fmul_rn(f[5], inv), __fmul_rn(f[6], inv), __fmul_rn(f[7], inv));
     codes[row * (C / 8) + blk * 16 + sub] = make_uint2(lo, hi);
-    if (sub == 0) scales[row * nb + blk] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (sub == 0) scales[blk * R + row] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
   }
 }
 

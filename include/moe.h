@@ -270,8 +270,11 @@ moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,
  */
 
 /* Rows of a bf16 (R, C) matrix to e4m3 with one scale per (row, 128 columns).
- *  codes (R, C) uint8, scales (R, C/128) fp32.  nrows: optional device int32;
- *  when given only rows < *nrows are written (e.g. ep_recv_counts + E-1). */
+ *  codes (R, C) uint8, scales (C/128, R) fp32 (column-block major: a GEMM K step
+ *  reads consecutive rows' scales from consecutive words; the GEMM entries take
+ *  scales of all `capacity` rows, so quantise the whole (capacity, C) buffer).
+ *  nrows: optional device int32; when given only rows < *nrows are written
+ *  (e.g. ep_recv_counts + E-1). */
 moe_status moe_quant_rows_fp8(int64_t R, int64_t C, const void* src, const int32_t* nrows,
                               uint8_t* codes, float* scales, void* stream);
 
@@ -315,7 +318,7 @@ moe_status moe_ffn_down_bwd_data_fp8(const moe_shape* s, const uint8_t* dyq, con
 /* moe_ffn_down_bwd_data_fp8 with the quantisation of its output fused in: the
  * same dG/dU, rounded to bf16, written as any of
  *   grad_gate_up (capacity, 2F) bf16               (optional),
- *   dguq (capacity, 2F) / dgus (capacity, 2F/128)  = moe_quant_rows_fp8 of it
+ *   dguq (capacity, 2F) / dgus (2F/128, capacity)  = moe_quant_rows_fp8 of it
  *                                                    for rows < ep_recv_counts[E-1],
  *   dguq_t (2F, ld) / dgus_t (slots, 2F)           = moe_quant_cols_fp8 of it
  * (each code/scale pair given together or not at all; at least one output,

@@ -34,14 +34,15 @@ def test_quant_rows_fp8_bit_exact():
     torch.cuda.synchronize()
     q, s = orc.quant_e4m3_rows(orc.bf16_to_f32(bits))
     check_equal("codes", _u8(codes), q)
-    check_equal("scales", scales.cpu().numpy(), s)
+    check_equal("scales", scales.cpu().numpy().T, s)      # stored (C/128, R)
     # only the first n rows when a device row count is given
     codes2 = torch.full((R, C), 0xAB, dtype=torch.uint8, device=DEV)
-    scales2 = torch.zeros((R, C // 128), dtype=torch.float32, device=DEV)
+    scales2 = torch.zeros((C // 128, R), dtype=torch.float32, device=DEV)
     dm.moe_quant_rows_fp8(bf(bits), codes2, scales2, nrows=torch.tensor([33], dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     check_equal("codes rows<33", _u8(codes2)[:33], q[:33])
-    assert (_u8(codes2)[33:] == 0xAB).all()
+    check_equal("scales rows<33", scales2.cpu().numpy().T[:33], s[:33])
+    assert (_u8(codes2)[33:] == 0xAB).all() and not scales2.cpu().numpy().T[33:].any()
 
 
 def test_quantize_weights_fp8_bit_exact():
@@ -297,7 +298,7 @@ def test_fused_quantisation_of_the_down_data_gradient(name):
     ns = dm.cols_fp8_slots(cap, E)
     ggu2 = torch.empty_like(ggu)
     rows = (torch.empty((cap, 2 * F), dtype=torch.uint8, device=DEV),
-            torch.empty((cap, 2 * F // 128), dtype=torch.float32, device=DEV))
+            torch.empty((2 * F // 128, cap), dtype=torch.float32, device=DEV))
     cols = (torch.empty((2 * F, 128 * ns), dtype=torch.uint8, device=DEV),
             torch.empty((ns, 2 * F), dtype=torch.float32, device=DEV))
     dm.moe_ffn_down_bwd_data_fp8_quant(run.shape, dyq, dys, wd.codes_t, wd.scales, run.gus, recv, ggu2,
@@ -311,7 +312,7 @@ def test_fused_quantisation_of_the_down_data_gradient(name):
     A = int(prefix[-1])
     check_equal("grad_gate_up", _u8(ggu2.view(torch.uint8))[:A], _u8(ggu.view(torch.uint8))[:A])
     check_equal("row codes", _u8(rows[0])[:A], _u8(rows_ref[0])[:A])
-    check_equal("row scales", rows[1].cpu().numpy()[:A], rows_ref[1].cpu().numpy()[:A])
+    check_equal("row scales", rows[1].cpu().numpy()[:, :A], rows_ref[1].cpu().numpy()[:, :A])
     lo = 0
     for e in range(E):
         hi = int(prefix[e])
@@ -350,7 +351,7 @@ def test_quant_rows_fp8_every_bf16_value():
     torch.cuda.synchronize()
     q, s = orc.quant_e4m3_rows(orc.bf16_to_f32(rows))
     check_equal("codes", _u8(codes), q)
-    check_equal("scales", scales.cpu().numpy(), s)
+    check_equal("scales", scales.cpu().numpy().T, s)   # stored (C/128, R)
 
 
 @pytest.mark.parametrize("name", list(FP8_CASES))
