@@ -72,6 +72,7 @@ MX_CASES = {
     "ragged_rows": dict(T=517, H=512, F=256, E=7, K=3),
     "empty_experts": dict(T=40, H=128, F=128, E=12, K=1),
     "wide": dict(T=700, H=1024, F=640, E=3, K=2),
+    "top1_768": dict(T=2496, H=768, F=768, E=4, K=1),
 }
 
 

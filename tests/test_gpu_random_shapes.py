@@ -198,3 +198,32 @@ def test_random_int8_decode_shapes(idx):
     A = f["route"].A
     check_close("h", f32(h[:A]), f["Hh"], rel_l2=REL_FP8)
     check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
+
+
+@pytest.mark.parametrize("idx", range(len(FP8_CASES)))
+def test_random_mx_layer_shapes(idx):
+    """The fp8 draws through moe_layer on the microscaled path (E8M0 per 32, block-scaled
+    MFMA) against the oracle's MX layer.  The chain requantises the GPU's own h (MX) and
+    y (int8 payload), which differ from the oracle's in the last bf16 bit at a fraction
+    of entries; a code that flips moves a top-1 token's output by a whole step, so the
+    max|err| bar is 5e-2 of the largest entry here (the L2 bar is the fp8 one; the MX
+    GEMMs themselves are held to 2e-3 on identical operands in test_gpu_mx.py)."""
+    kw = FP8_CASES[idx]
+    print(f"[random mx] case={idx} {kw}", flush=True)
+    inp = wl.layer_inputs(seed=600 + idx, **kw)
+    x = bf(inp["x"]).requires_grad_(True)
+    w = torch.from_numpy(inp["topk_weights"]).to(DEV).requires_grad_(True)
+    ws = [bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down")]
+    mask = torch.from_numpy(inp["mask"]).to(DEV) if inp.get("mask") is not None else None
+    out = dm.moe_layer(x, torch.from_numpy(inp["topk_idx"]).to(DEV), w, *ws, x_active_mask=mask,
+                       zero_expert_num=kw.get("Z", 0), copy_expert_num=kw.get("C", 0), fp8=True, mx=True,
+                       comm_quant_mode=2)
+    out.backward(bf(inp["grad_out"]))
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_mx(inp)
+    b = orc.layer_bwd_mx(inp, f, inp["grad_out"])
+    check_close("out", f32(out), f["out"], max_abs=5e-2, rel_l2=REL_FP8)
+    check_close("grad_x", f32(x.grad), b["dx"], max_abs=5e-2, rel_l2=REL_FP8)
+    check_close("grad_topk_weights", f32(w.grad), b["dw"], max_abs=5e-2, rel_l2=REL_FP8)
+    for t, k in zip(ws, ("dWg", "dWu", "dWd")):
+        check_close(k, f32(t.grad), orc.round_bf16(b[k]), max_abs=5e-2, rel_l2=REL_FP8)
