@@ -16,15 +16,21 @@
 // the expanded buffers); the last two are grouped over K (the contraction runs
 // over the expert's rows, which may be none).
 //
+// Operand types: bf16; fp8 e4m3 with fp32 scales (activations per (row, 128 of
+// K), weights per 128 x 128 block; weight gradients per (128 tokens, column));
+// microscaled e4m3 (MX: E8M0 scale per 32 of K, applied by the MFMA); int8 (one
+// scale per row and per output channel; forward GEMMs only).
+//
 // Tiling: a BM x BN output tile per workgroup of WM x WN waves (128 x 128 or
 // 128 x 256 with 2 x 2 waves, 256 x 256 with 2 x 4 waves, per GEMM kind and
 // shape, see launch()), each wave (BM/WM) x (BN/WN) of
-// v_mfma_f32_32x32x16_bf16 tiles (fp8: v_mfma_scale_f32_32x32x64_f8f6f4 with
-// unit block scales, the fp32 scales applied per 128-wide K block), one to
-// three workgroups per CU.  K steps of
-// 64 or 32 (fp8: 128 codes) go from memory straight into LDS (buffer loads
-// with an LDS destination, no register staging), two or three LDS stages: the
-// loads of the next steps are in flight while the MFMAs of step t issue.
+// v_mfma_f32_32x32x16_bf16 tiles (fp8: v_mfma_scale_f32_32x32x64_f8f6f4, with
+// unit scales and the fp32 scales applied per 128-wide K block, or with the MX
+// scales; int8: v_mfma_i32_32x32x32_i8), one to three workgroups per CU.  K
+// steps of 64 or 32 (8-bit: 128 codes) go from memory straight into LDS
+// (buffer loads with an LDS destination, no register staging), two or three
+// LDS stages: the loads of the next steps are in flight while the MFMAs of
+// step t issue.
 // Operands keep their memory layout in LDS:
 // K-contiguous tiles as rows of 2 BK bytes with an XOR-swizzled chunk order
 // (one conflict-free 16-byte read per MFMA operand), K-strided tiles as
@@ -150,9 +156,9 @@ struct Cfg {
   // (16 bytes of padding per row)
   static constexpr int CW = MODE == GATE_UP_FWD ? BN / 2 : BN;
   static constexpr int CP = CW + 8;
-  // LDS stages of the bf16 operand tiles (the fp8 path has two)
+  // LDS stages of the bf16 operand tiles (the 8-bit paths have two)
   static constexpr int S = S_;
-  // bf16: S stages of BK-wide tiles; fp8: two stages of 128-byte rows
+  // bf16: S stages of BK-wide tiles; 8-bit: two stages of 128-byte rows
   static constexpr int kMain = FP8 ? 2 * (BM + BN) * 64 : S * (BM + BN) * BK;
   // epilogue staging: h, G and U side by side when the three fit the operand
   // LDS, else h and G, then U (two passes) or one after the other (three);
@@ -309,7 +315,8 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   // are per-128-token codes, transposed (one row per output row or column,
   // the expert's token slots along it), a K step is one slot, and its scales
   // are one per A row and one per B column: acc += tmp * (A scale * B scale)
-  // element by element.
+  // element by element.  MX: the MFMA applies the E8M0 scales, straight into
+  // the accumulators; int8: integer MFMAs, scales applied after the loop.
   constexpr int S8 = 2;
   constexpr int LA = BM / 8 / (WM * WN), LB = BN / 8 / (WM * WN);
   static_assert(C::kMain >= S8 * (BM + BN) * 64, "fp8 stages must fit the operand LDS");
