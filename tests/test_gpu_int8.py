@@ -149,3 +149,19 @@ def test_moe_layer_int8_api():
     torch.cuda.synchronize()
     f = orc.layer_fwd_int8(inp, S)
     check_close("out", f32(out), f["out"], rel_l2=REL_8BIT)
+
+
+def test_int8_path_with_no_routed_rows():
+    """Every slot to a zero or copy expert (no expert rows): the int8 dispatch writes no
+    rows, the GEMMs run on zero rows and combine gives the closed forms (0 and ori_x)."""
+    inp = wl.layer_inputs(seed=71, T=64, H=256, F=128, E=4, K=2, Z=1, C=1)
+    inp["topk_idx"] = np.tile(np.array([[4, 5]], np.int32), (64, 1))   # zero expert 4, copy expert 5
+    run = Run(inp)
+    d, dyn = dm.dispatch_int8(run.shape, run.x, run.idx, None)
+    torch.cuda.synchronize()
+    assert int(d.ep_recv_counts[-1].item()) == 0
+    wq = [dm.Int8Weights.quantize(bf(inp[k])) for k in ("w_gate", "w_up", "w_down")]
+    out = dm.moe_layer_int8(run.x, run.idx, run.w, *wq, copy_expert_num=1, zero_expert_num=1)
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_int8(inp)
+    check_close("out", f32(out), f["out"], rel_l2=REL_8BIT)

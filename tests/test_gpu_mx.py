@@ -137,3 +137,22 @@ def test_autograd_layer_mx():
     check_close("grad_topk_weights", f32(w.grad), b["dw"], rel_l2=REL_FP8)
     for t, k in zip(ws, ("dWg", "dWu", "dWd")):
         check_close(k, f32(t.grad), orc.round_bf16(b[k]), rel_l2=REL_FP8)
+
+
+def test_mx_layer_with_empty_and_single_row_experts():
+    """Most experts without rows, one with a single row (a 1-row tile with clamped
+    loads), through the MX autograd layer."""
+    inp = wl.layer_inputs(seed=86, T=3, H=256, F=128, E=16, K=1)
+    inp["topk_idx"] = np.array([[5], [5], [11]], np.int32)
+    x = bf(inp["x"]).requires_grad_(True)
+    w = torch.from_numpy(inp["topk_weights"]).to(DEV).requires_grad_(True)
+    ws = [bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down")]
+    out = dm.moe_layer(x, torch.from_numpy(inp["topk_idx"]).to(DEV), w, *ws, fp8=True, mx=True)
+    out.backward(bf(inp["grad_out"]))
+    torch.cuda.synchronize()
+    f = orc.layer_fwd_mx(inp, comm_quant=False)
+    b = orc.layer_bwd_mx(inp, f, inp["grad_out"])
+    check_close("out", f32(out), f["out"], rel_l2=REL_FP8)
+    check_close("grad_x", f32(x.grad), b["dx"], rel_l2=REL_FP8)
+    for t, k in zip(ws, ("dWg", "dWu", "dWd")):
+        check_close(k, f32(t.grad), orc.round_bf16(b[k]), rel_l2=REL_FP8)
