@@ -335,9 +335,9 @@ def build_step(name, T_override=None):
         dyq, dys, dgq, dgs = z(cap, H, dt=u8), z(cap, H // 32, dt=u8), z(cap, 2 * F, dt=u8), z(cap, 2 * F // 32, dt=u8)
         C += [
             ("moe_quant_rows_mx (x)", lambda: dm.moe_quant_rows_mx(ex, xq, xs, nrows)),
+            # h's MX codes come out of the gate/up GEMM
             ("moe_ffn_gate_up_fwd_mx", lambda: dm.moe_ffn_gate_up_fwd_mx(
-                shape, xq, xs, wqm[0].codes, wqm[0].scales, wqm[1].codes, wqm[1].scales, recv, gus, h)),
-            ("moe_quant_rows_mx (h)", lambda: dm.moe_quant_rows_mx(h, hq, hs, nrows)),
+                shape, xq, xs, wqm[0].codes, wqm[0].scales, wqm[1].codes, wqm[1].scales, recv, gus, h, (hq, hs))),
             ("moe_ffn_down_fwd_mx", lambda: dm.moe_ffn_down_fwd_mx(shape, hq, hs, wqm[2].codes, wqm[2].scales,
                                                                    recv, y)),
         ]
@@ -405,10 +405,10 @@ def build_step(name, T_override=None):
     if mx:
         C += [
             ("moe_quant_rows_mx (dY)", lambda: dm.moe_quant_rows_mx(gy, dyq, dys, nrows)),
+            # bf16 dG|dU for the bf16 weight gradient and its MX codes, one kernel
             ("moe_ffn_down_bwd_data_mx", lambda: dm.moe_ffn_down_bwd_data_mx(
-                shape, dyq, dys, wqm[2].codes_t, wqm[2].scales_t, gus, recv, ggu)),
+                shape, dyq, dys, wqm[2].codes_t, wqm[2].scales_t, gus, recv, ggu, (dgq, dgs))),
             ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
-            ("moe_quant_rows_mx (dGU)", lambda: dm.moe_quant_rows_mx(ggu, dgq, dgs, nrows)),
             ("moe_ffn_gate_up_bwd_data_mx", lambda: dm.moe_ffn_gate_up_bwd_data_mx(
                 shape, dgq, dgs, wqm[0].codes_t, wqm[0].scales_t, wqm[1].codes_t, wqm[1].scales_t, recv, gxe)),
         ]
@@ -530,7 +530,7 @@ def account(st, A):
         nb["moe_combine"] += T * H * 2
         nb["moe_dispatch_bwd"] += T * H * 2
     if st.cfg.get("mx"):
-        for k, d in (("x", H), ("h", F), ("dY", H), ("dGU", 2 * F)):
+        for k, d in (("x", H), ("dY", H)):
             nb[f"moe_quant_rows_mx ({k})"] = A * d * 3 + A * d // 32
     elif fp8:
         nb["moe_quant_rows_fp8 (x)"] = A * H * 3 + A * H // 128 * 4

@@ -112,9 +112,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_down_fwd_int8.argtypes = [S] + [P] * 7
         L.moe_quant_rows_mx.argtypes = [I64, I64, P, P, P, P, P]
         L.moe_quantize_weights_mx.argtypes = [I64, I64, I64, P, P, P, P, P, P]
-        L.moe_ffn_gate_up_fwd_mx.argtypes = [S] + [P] * 10
+        L.moe_ffn_gate_up_fwd_mx.argtypes = [S] + [P] * 12
         L.moe_ffn_down_fwd_mx.argtypes = [S] + [P] * 7
-        L.moe_ffn_down_bwd_data_mx.argtypes = [S] + [P] * 8
+        L.moe_ffn_down_bwd_data_mx.argtypes = [S] + [P] * 10
         L.moe_ffn_gate_up_bwd_data_mx.argtypes = [S] + [P] * 9
         for name in ENTRY_POINTS:
             if name != "moe_status_str":
@@ -437,12 +437,15 @@ def moe_quantize_weights_mx(w, codes, scales, codes_t=None, scales_t=None, strea
                                          _ptr(scales_t, U8T, "scales_t"), _stream(stream)))
 
 
-def moe_ffn_gate_up_fwd_mx(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act, stream=None):
+def moe_ffn_gate_up_fwd_mx(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act, h_rows=None,
+                           stream=None):
+    """h_rows: optional (codes, scales) receiving the MX row codes of h_act."""
+    hq, hs = h_rows if h_rows is not None else (None, None)
     _check(lib().moe_ffn_gate_up_fwd_mx(
         ctypes.byref(shape), _ptr(xq, U8T, "xq"), _ptr(xs, U8T, "xs"), _ptr(wgq, U8T, "wgq"),
         _ptr(wgs, U8T, "wgs"), _ptr(wuq, U8T, "wuq"), _ptr(wus, U8T, "wus"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(gate_up_save, BF16, "gate_up_save"),
-        _ptr(h_act, BF16, "h_act"), _stream(stream)))
+        _ptr(h_act, BF16, "h_act"), _ptr(hq, U8T, "hq"), _ptr(hs, U8T, "hs"), _stream(stream)))
 
 
 def moe_ffn_down_fwd_mx(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
@@ -453,12 +456,14 @@ def moe_ffn_down_fwd_mx(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None)
 
 
 def moe_ffn_down_bwd_data_mx(shape, dyq, dys, wdq_t, wds_t, gate_up_save, ep_recv_counts, grad_gate_up,
-                             stream=None):
+                             rows=None, stream=None):
+    """rows: optional (codes, scales) receiving the MX row codes of dG|dU."""
+    dguq, dgus = rows if rows is not None else (None, None)
     _check(lib().moe_ffn_down_bwd_data_mx(
         ctypes.byref(shape), _ptr(dyq, U8T, "dyq"), _ptr(dys, U8T, "dys"), _ptr(wdq_t, U8T, "wdq_t"),
         _ptr(wds_t, U8T, "wds_t"), _ptr(gate_up_save, BF16, "gate_up_save"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_gate_up, BF16, "grad_gate_up"),
-        _stream(stream)))
+        _ptr(dguq, U8T, "dguq"), _ptr(dgus, U8T, "dgus"), _stream(stream)))
 
 
 def moe_ffn_gate_up_bwd_data_mx(shape, dguq, dgus, wgq_t, wgs_t, wuq_t, wus_t, ep_recv_counts, grad_expand_x,
@@ -685,9 +690,11 @@ class _MoELayerFn(torch.autograd.Function):
             nrows = d.ep_recv_counts[-1:]
             wq = tuple(MxWeights.quantize(w) for w in (w_gate, w_up, w_down))
             xq, xs = quant_rows_mx(d.expand_x, nrows)
+            # h's MX codes come out of the gate/up GEMM
+            hq = torch.empty((cap, F), dtype=U8T, device=dev)
+            hs = torch.empty((cap, F // 32), dtype=U8T, device=dev)
             moe_ffn_gate_up_fwd_mx(shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales,
-                                   d.ep_recv_counts, gus, h)
-            hq, hs = quant_rows_mx(h, nrows)
+                                   d.ep_recv_counts, gus, h, (hq, hs))
             moe_ffn_down_fwd_mx(shape, hq, hs, wq[2].codes, wq[2].scales, d.ep_recv_counts, y)
             del xq, xs, hq, hs
         elif ctx.fp8:
@@ -764,10 +771,11 @@ class _MoELayerFn(torch.autograd.Function):
             (wgt, wgs), (wut, wus), (wdt, wds) = ctx.wq
             nrows = recv[-1:]
             dyq, dys = quant_rows_mx(gy, nrows)
-            moe_ffn_down_bwd_data_mx(shape, dyq, dys, wdt, wds, gus, recv, ggu)
+            dgq = torch.empty((cap, 2 * F), dtype=U8T, device=dev)
+            dgs = torch.empty((cap, 2 * F // 32), dtype=U8T, device=dev)
+            moe_ffn_down_bwd_data_mx(shape, dyq, dys, wdt, wds, gus, recv, ggu, (dgq, dgs))
             del dyq, dys
             moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
-            dgq, dgs = quant_rows_mx(ggu, nrows)
             moe_ffn_gate_up_bwd_data_mx(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)
             del dgq, dgs
         elif ctx.fp8:

@@ -112,6 +112,20 @@ __device__ __forceinline__ float wave_max64(float v) {
   return v;
 }
 
+// Microscaled e4m3 (E8M0 scale per 32 values): the scale is the smallest power of
+// two 2^e with amax / 2^e <= 448; with amax = M * 2^E (1 <= M < 2) that is e = E - 8,
+// or E - 7 when M > 1.75 (mantissa bits above 0x600000), clamped to [-127, 127]
+// (zero and subnormal amax give -127).  Scale byte e + 127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int biased = (int)(b >> 23);
+  int e = biased - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  if (biased == 0) e = -127;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^-e as a float (e in [-126, 126]; -127 gives 2^127)
+__device__ __forceinline__ float mx_inv(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
 constexpr int kWave = 64;
 
 // ----------------------------------------------------------------------------- host side

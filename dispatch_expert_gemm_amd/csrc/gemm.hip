@@ -121,6 +121,10 @@ struct GemmArgs {
   const uint8_t* mB0;
   const uint8_t* mB1;
   int64_t mrA, mrB, mbe;
+  // MX forward / down data gradient: optional MX row codes of the bf16 output
+  // (h, or dG|dU), in the layout of the MX row quantiser over rowsA rows
+  uint8_t* qmx;
+  uint8_t* smx;
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
@@ -947,6 +951,26 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
                                   reinterpret_cast<u32x4*>(dst + (row0 + row) * ldd + c8));
     }
   };
+  // MX codes of 32 staged bf16 values (one 32-block of an output row): 32 codes
+  // at dst, the scale byte in the step-major word layout (block c32 of the row)
+  auto mx_block = [&](const bf16_t* src, int64_t row, int64_t c32, uint8_t* dst) {
+    float f[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) unpack8(*reinterpret_cast<const uint4*>(src + 8 * q), f + 8 * q);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(f[i]));
+    const int ex = mx_exponent(m);
+    const float inv = mx_inv(ex);
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      w[q] = e4m3x4(__fmul_rn(f[4 * q], inv), __fmul_rn(f[4 * q + 1], inv), __fmul_rn(f[4 * q + 2], inv),
+                    __fmul_rn(f[4 * q + 3], inv));
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+    g.smx[((c32 / 4) * g.rowsA + row) * 4 + (c32 & 3)] = (uint8_t)(ex + 127);
+  };
   if constexpr (MODE == GATE_UP_FWD && C::kEpiGU2) {
     // h and G side by side, then U
     bf16_t* th = smem;
@@ -1083,6 +1107,14 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     store_tile_nt(tg, g.C1 + n0, 2 * g.F, g.F - n0);
     store_tile_nt(tu, g.C1 + g.F + n0, 2 * g.F, g.F - n0);
     if constexpr (FP8) {
+      if (g.qmx) {
+        // MX row codes of h: the tile's BN/2 = 64 columns are two 32-blocks of
+        // each row, one (row, block) per thread
+        static_assert(BN / 2 * BM / 32 == kThreads, "one (row, 32-block) of h per thread");
+        const int row = tid >> 1, b = tid & 1;
+        if (row < rows_valid)
+          mx_block(th + row * CP + 32 * b, row0 + row, (n0 + 32 * b) / 32, g.qmx + (row0 + row) * g.F + n0 + 32 * b);
+      }
       if (g.qc) {
         // per-128-token e4m3 codes of the staged bf16 h (the tile's rows are
         // one token slot): thread t takes the column pair 2 (t%32), +1 over
@@ -1182,6 +1214,16 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
       store_tile(tu, g.C0 + g.F + n0, 2 * g.F, g.N - n0);
     }
     if constexpr (FP8) {
+      if (g.qmx) {
+        // MX row codes of dG|dU: four 32-blocks of dG and four of dU per row
+        for (int p = tid; p < BM * 8; p += kThreads) {
+          const int row = p >> 3, blk = p & 7;
+          if (row >= rows_valid) continue;
+          const int64_t col = (blk < 4 ? 0 : g.F) + n0 + 32 * (blk & 3);
+          mx_block((blk < 4 ? tg : tu) + row * CP + 32 * (blk & 3), row0 + row, col / 32,
+                   g.qmx + (row0 + row) * 2 * g.F + col);
+        }
+      }
       // e4m3 codes of the staged bf16 dG/dU (the values the bf16 output holds),
       // same rule as the quantiser kernels: F is a multiple of 128 and the tile
       // is 128 x 128, so its dG (dU) columns are one whole 128-column block of
@@ -1847,10 +1889,12 @@ extern "C" moe_status moe_ffn_down_fwd_int8(const moe_shape* s, const int8_t* hq
 extern "C" moe_status moe_ffn_gate_up_fwd_mx(const moe_shape* s, const uint8_t* xq, const uint8_t* xs,
                                              const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
                                              const uint8_t* wus, const int32_t* ep_recv_counts,
-                                             void* gate_up_save, void* h_act, void* stream) {
+                                             void* gate_up_save, void* h_act, uint8_t* hq, uint8_t* hs,
+                                             void* stream) {
   moe_status st = check_fp8_shape(s);
   if (st != MOE_OK) return st;
   if (!wgq || !wgs || !wuq || !wus || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (!hq != !hs) return MOE_ERR_NULL_ARG;
   if (s->capacity == 0) return MOE_OK;
   if (!xq || !xs || !gate_up_save || !h_act) return MOE_ERR_NULL_ARG;
   GemmArgs g = base_args(s, ep_recv_counts);
@@ -1870,6 +1914,8 @@ extern "C" moe_status moe_ffn_gate_up_fwd_mx(const moe_shape* s, const uint8_t* 
   g.Kd = s->H;
   g.C0 = static_cast<bf16_t*>(h_act);
   g.C1 = static_cast<bf16_t*>(gate_up_save);
+  g.qmx = hq;
+  g.smx = hs;
   return launch<GATE_UP_FWD, true, false, true>(g, s, as_stream(stream));
 }
 
@@ -1901,12 +1947,14 @@ extern "C" moe_status moe_ffn_down_fwd_mx(const moe_shape* s, const uint8_t* hq,
 extern "C" moe_status moe_ffn_down_bwd_data_mx(const moe_shape* s, const uint8_t* dyq, const uint8_t* dys,
                                                const uint8_t* wdq_t, const uint8_t* wds_t,
                                                const void* gate_up_save, const int32_t* ep_recv_counts,
-                                               void* grad_gate_up, void* stream) {
+                                               void* grad_gate_up, uint8_t* dguq, uint8_t* dgus,
+                                               void* stream) {
   moe_status st = check_fp8_shape(s);
   if (st != MOE_OK) return st;
   if (!wdq_t || !wds_t || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  if (!dguq != !dgus || (!grad_gate_up && !dguq)) return MOE_ERR_NULL_ARG;
   if (s->capacity == 0) return MOE_OK;
-  if (!dyq || !dys || !gate_up_save || !grad_gate_up) return MOE_ERR_NULL_ARG;
+  if (!dyq || !dys || !gate_up_save) return MOE_ERR_NULL_ARG;
   GemmArgs g = base_args(s, ep_recv_counts);
   g.qA = dyq;
   g.lda = s->H;
@@ -1922,6 +1970,8 @@ extern "C" moe_status moe_ffn_down_bwd_data_mx(const moe_shape* s, const uint8_t
   g.Kd = s->H;
   g.aux = static_cast<const bf16_t*>(gate_up_save);
   g.C0 = static_cast<bf16_t*>(grad_gate_up);
+  g.qmx = dguq;
+  g.smx = dgus;
   return launch<DOWN_BWD_DATA, true, false, true>(g, s, as_stream(stream));
 }
 

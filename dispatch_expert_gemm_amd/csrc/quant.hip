@@ -217,20 +217,6 @@ __global__ __launch_bounds__(256) void k_quant_rows_int8(const uint4* __restrict
   if (lane == 0) scales[r] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
 }
 
-// Microscaled e4m3 (E8M0 scale per 32 values): the scale is the smallest power of
-// two 2^e with amax / 2^e <= 448; with amax = M * 2^E (1 <= M < 2) that is e = E - 8,
-// or E - 7 when M > 1.75 (mantissa bits above 0x600000), clamped to [-127, 127]
-// (zero and subnormal amax give -127).  Scale byte e + 127.
-__device__ __forceinline__ int mx_exponent(float amax) {
-  const uint32_t b = __float_as_uint(amax);
-  const int biased = (int)(b >> 23);
-  int e = biased - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
-  if (biased == 0) e = -127;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-// 2^-e as a float (e in [-126, 126]; -127 gives 2^127)
-__device__ __forceinline__ float mx_inv(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
-
 // rows: 4 lanes per 32-value block, 8 values each (one 16-byte load, one 8-byte store)
 __global__ __launch_bounds__(256) void k_quant_rows_mx(const uint4* __restrict__ src, int64_t R, int64_t C,
                                                        const int32_t* __restrict__ nrows, uint2* __restrict__ codes,

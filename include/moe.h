@@ -413,11 +413,15 @@ moe_status moe_quantize_weights_mx(int64_t E, int64_t N, int64_t K, const void* 
                                    uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t, void* stream);
 
 /* MX moe_ffn_gate_up_fwd: xq/xs = moe_quant_rows_mx of expand_x; wgq/wgs,
- * wuq/wus = moe_quantize_weights_mx codes/scales of w_gate, w_up. */
+ * wuq/wus = moe_quantize_weights_mx codes/scales of w_gate, w_up.  hq/hs
+ * (optional, both or neither): the MX row codes of the h_act it writes, as
+ * moe_quant_rows_mx of h_act would give them (codes (capacity, F), scales in its
+ * layout over capacity rows) -- the down GEMM's input without a separate pass. */
 moe_status moe_ffn_gate_up_fwd_mx(const moe_shape* s, const uint8_t* xq, const uint8_t* xs,
                                   const uint8_t* wgq, const uint8_t* wgs, const uint8_t* wuq,
                                   const uint8_t* wus, const int32_t* ep_recv_counts,
-                                  void* gate_up_save, void* h_act, void* stream);
+                                  void* gate_up_save, void* h_act, uint8_t* hq, uint8_t* hs,
+                                  void* stream);
 
 /* MX moe_ffn_down_fwd: hq/hs = moe_quant_rows_mx of h_act; wdq/wds of w_down. */
 moe_status moe_ffn_down_fwd_mx(const moe_shape* s, const uint8_t* hq, const uint8_t* hs,
@@ -425,10 +429,13 @@ moe_status moe_ffn_down_fwd_mx(const moe_shape* s, const uint8_t* hq, const uint
                                void* y, void* stream);
 
 /* MX moe_ffn_down_bwd_data: dyq/dys = moe_quant_rows_mx of grad_y; wdq_t/wds_t =
- * the transposed codes/scales of w_down ((E, F, H), (E, F, H/32)). */
+ * the transposed codes/scales of w_down.  Writes grad_gate_up (bf16, optional)
+ * and/or dguq/dgus (both or neither): the MX row codes of it (capacity, 2F), as
+ * moe_quant_rows_mx would give them; at least one output. */
 moe_status moe_ffn_down_bwd_data_mx(const moe_shape* s, const uint8_t* dyq, const uint8_t* dys,
                                     const uint8_t* wdq_t, const uint8_t* wds_t, const void* gate_up_save,
-                                    const int32_t* ep_recv_counts, void* grad_gate_up, void* stream);
+                                    const int32_t* ep_recv_counts, void* grad_gate_up, uint8_t* dguq,
+                                    uint8_t* dgus, void* stream);
 
 /* MX moe_ffn_gate_up_bwd_data: dguq/dgus = moe_quant_rows_mx of grad_gate_up;
  * wgq_t/wgs_t, wuq_t/wus_t = transposed codes/scales of w_gate, w_up ((E, H, F),

@@ -249,8 +249,9 @@ def test_mx_entries_reject_bad_arguments_before_launch(L):
     assert L.moe_quantize_weights_mx(2, 100, 128, P(), P(), P(), Nn, Nn, Nn) == BAD_SHAPE
     assert L.moe_quantize_weights_mx(2, 128, 128, P(), P(), P(), P(), Nn, Nn) == NULL_ARG   # codes_t without scales_t
     s8 = ctypes.byref(S(F=512))
-    assert L.moe_ffn_gate_up_fwd_mx(ctypes.byref(S()), *([P()] * 9), Nn) == BAD_SHAPE    # F = 480
-    assert L.moe_ffn_gate_up_fwd_mx(s8, P(), P(), Nn, P(), P(), P(), P(), P(), P(), Nn) == NULL_ARG
+    assert L.moe_ffn_gate_up_fwd_mx(ctypes.byref(S()), *([P()] * 11), Nn) == BAD_SHAPE    # F = 480
+    assert L.moe_ffn_gate_up_fwd_mx(s8, P(), P(), Nn, P(), P(), P(), P(), P(), P(), Nn, Nn, Nn) == NULL_ARG
+    assert L.moe_ffn_gate_up_fwd_mx(s8, *([P()] * 9), P(), Nn, Nn) == NULL_ARG       # codes without scales
     assert L.moe_ffn_down_fwd_mx(s8, P(), P(), P(), Nn, P(), P(), Nn) == NULL_ARG
-    assert L.moe_ffn_down_bwd_data_mx(s8, P(), P(), P(), P(), P(), P(), Nn, Nn) == NULL_ARG
+    assert L.moe_ffn_down_bwd_data_mx(s8, P(), P(), P(), P(), P(), P(), Nn, Nn, Nn, Nn) == NULL_ARG  # no output
     assert L.moe_ffn_gate_up_bwd_data_mx(s8, P(), P(), P(), P(), P(), Nn, P(), P(), Nn) == NULL_ARG

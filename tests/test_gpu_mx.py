@@ -90,13 +90,18 @@ def test_mx_grouped_ffn_forward_and_data_gradients(name):
     gus = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
     h = torch.empty((cap, F), dtype=torch.bfloat16, device=DEV)
     y = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
-    dm.moe_ffn_gate_up_fwd_mx(run.shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h)
+    hq2 = torch.empty((cap, F), dtype=torch.uint8, device=DEV)
+    hs2 = torch.empty((cap, F // 32), dtype=torch.uint8, device=DEV)
+    dm.moe_ffn_gate_up_fwd_mx(run.shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h,
+                              (hq2, hs2))
     hq, hs = dm.quant_rows_mx(h, nrows)
     dm.moe_ffn_down_fwd_mx(run.shape, hq, hs, wq[2].codes, wq[2].scales, recv, y)
     dY_bits = wl.to_bf16_bits(np.random.default_rng(84).standard_normal((cap, H), dtype=np.float32) * 0.125)
     dyq, dys = dm.quant_rows_mx(bf(dY_bits), nrows)
     ggu = torch.empty((cap, 2 * F), dtype=torch.bfloat16, device=DEV)
-    dm.moe_ffn_down_bwd_data_mx(run.shape, dyq, dys, wq[2].codes_t, wq[2].scales_t, gus, recv, ggu)
+    dgq2 = torch.empty((cap, 2 * F), dtype=torch.uint8, device=DEV)
+    dgs2 = torch.empty((cap, 2 * F // 32), dtype=torch.uint8, device=DEV)
+    dm.moe_ffn_down_bwd_data_mx(run.shape, dyq, dys, wq[2].codes_t, wq[2].scales_t, gus, recv, ggu, (dgq2, dgs2))
     dgq, dgs = dm.quant_rows_mx(ggu, nrows)
     gxe = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
     dm.moe_ffn_gate_up_bwd_data_mx(run.shape, dgq, dgs, wq[0].codes_t, wq[0].scales_t, wq[1].codes_t,
@@ -104,6 +109,11 @@ def test_mx_grouped_ffn_forward_and_data_gradients(name):
     torch.cuda.synchronize()
     r = orc.route(inp["topk_idx"], inp["E"])
     A = r.A
+    # the codes fused into the GEMM epilogues equal the quantiser's on the same bf16 output
+    check_equal("h codes (fused)", _u8(hq2)[:A], _u8(hq)[:A])
+    check_equal("h scales (fused)", _rows_view(_u8(hs2), cap, F)[:A], _rows_view(_u8(hs), cap, F)[:A])
+    check_equal("dGU codes (fused)", _u8(dgq2)[:A], _u8(dgq)[:A])
+    check_equal("dGU scales (fused)", _rows_view(_u8(dgs2), cap, 2 * F)[:A], _rows_view(_u8(dgs), cap, 2 * F)[:A])
     X = orc.dispatch(inp["x"], r)
     owq = tuple(orc.quant_weights_mx(inp[k]) for k in ("w_gate", "w_up", "w_down"))
     G, U, Hh, Y = orc.ffn_fwd_mx(X, r.ep_recv_counts, *owq)
