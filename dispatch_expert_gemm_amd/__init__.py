@@ -140,6 +140,41 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, n, name):
+    """Raise unless t (when given) holds at least n elements."""
+    if isinstance(t, torch.Tensor) and t.numel() < n:
+        raise MoeError(f"{name} holds {t.numel()} elements, needs at least {n}")
+
+
+def _shape_sizes(shape):
+    """Least element count of each buffer the shape-taking entries name, from the
+    layouts the C header states (a kernel would read or write that far)."""
+    T, H, F, cap, K, E = shape.T, shape.H, shape.F, shape.capacity, shape.K, shape.num_experts
+    Q = shape.const_expert_num
+    return {
+        "x": T * H, "topk_idx": T * K, "topk_weights": T * K, "grad_topk_weights": T * K,
+        "x_active_mask": {1: T, 2: T * K}.get(shape.mask_ndim, 0),
+        "expand_x": cap * H, "grad_expand_x": cap * H, "y": cap * H, "grad_y": cap * H,
+        "gate_up_save": cap * 2 * F, "grad_gate_up": cap * 2 * F, "h_act": cap * F,
+        "xq": cap * H, "dyq": cap * H, "hq": cap * F, "dguq": cap * 2 * F,
+        "w_gate": E * F * H, "w_up": E * F * H, "w_down": E * H * F,
+        "grad_w_gate": E * F * H, "grad_w_up": E * F * H, "grad_w_down": E * H * F,
+        "ep_recv_counts": E, "ep_send_counts": E, "expert_token_nums": E, "err_flag": 1,
+        "assist_info_for_combine": T * K + cap,
+        "out": T * H, "grad_out": T * H, "shared_expert_x": T * H, "ori_x": T * H,
+        "grad_x": T * H, "grad_x_accum": T * H,
+        "const_alpha_1": Q * H, "const_alpha_2": Q * H, "const_v": Q * H,
+        # 8-bit weight codes, one byte each, either layout
+        "wgq": E * F * H, "wuq": E * F * H, "wdq": E * H * F,
+        "wgq_t": E * F * H, "wuq_t": E * F * H, "wdq_t": E * H * F,
+    }
+
+
+def _check_sizes(shape, args):
+    for name, n in _shape_sizes(shape).items():
+        _need(args.get(name), n, name)
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -164,6 +199,7 @@ def moe_workspace_size(shape: MoeShape) -> int:
 
 def moe_dispatch(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_combine,
                  expert_token_nums, ep_recv_counts, err_flag, workspace, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_dispatch(
         ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(topk_idx, I32, "topk_idx"),
         _ptr(x_active_mask, U8, "x_active_mask"), _ptr(expand_x, BF16, "expand_x"),
@@ -175,6 +211,7 @@ def moe_dispatch(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_co
 
 def moe_grouped_ffn(shape, expand_x, w_gate, w_up, w_down, ep_recv_counts, gate_up_save, h_act, y,
                     stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_grouped_ffn(
         ctypes.byref(shape), _ptr(expand_x, BF16, "expand_x"), _ptr(w_gate, BF16, "w_gate"),
         _ptr(w_up, BF16, "w_up"), _ptr(w_down, BF16, "w_down"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
@@ -183,6 +220,7 @@ def moe_grouped_ffn(shape, expand_x, w_gate, w_up, w_down, ep_recv_counts, gate_
 
 
 def moe_ffn_gate_up_fwd(shape, expand_x, w_gate, w_up, ep_recv_counts, gate_up_save, h_act, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_fwd(
         ctypes.byref(shape), _ptr(expand_x, BF16, "expand_x"), _ptr(w_gate, BF16, "w_gate"),
         _ptr(w_up, BF16, "w_up"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
@@ -190,6 +228,7 @@ def moe_ffn_gate_up_fwd(shape, expand_x, w_gate, w_up, ep_recv_counts, gate_up_s
 
 
 def moe_ffn_down_fwd(shape, h_act, w_down, ep_recv_counts, y, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_fwd(
         ctypes.byref(shape), _ptr(h_act, BF16, "h_act"), _ptr(w_down, BF16, "w_down"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"), _stream(stream)))
@@ -198,6 +237,7 @@ def moe_ffn_down_fwd(shape, h_act, w_down, ep_recv_counts, y, stream=None):
 def moe_combine(shape, y, topk_idx, topk_weights, assist_info_for_combine, ep_send_counts,
                 x_active_mask, shared_expert_x, ori_x, const_alpha_1, const_alpha_2, const_v, out,
                 stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_combine(
         ctypes.byref(shape), _ptr(y, BF16, "y"), _ptr(topk_idx, I32, "topk_idx"),
         _ptr(topk_weights, F32, "topk_weights"), _ptr(assist_info_for_combine, I32, "assist"),
@@ -210,6 +250,7 @@ def moe_combine(shape, y, topk_idx, topk_weights, assist_info_for_combine, ep_se
 def moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_combine,
                     ep_send_counts, x_active_mask, ori_x, const_alpha_1, const_alpha_2, const_v,
                     grad_y, grad_topk_weights, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_combine_bwd(
         ctypes.byref(shape), _ptr(grad_out, BF16, "grad_out"), _ptr(y, BF16, "y"),
         _ptr(topk_idx, I32, "topk_idx"), _ptr(topk_weights, F32, "topk_weights"),
@@ -223,6 +264,7 @@ def moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_
 def moe_grouped_ffn_bwd(shape, grad_y, expand_x, gate_up_save, h_act, w_gate, w_up, w_down,
                         ep_recv_counts, grad_gate_up, grad_expand_x, grad_w_gate, grad_w_up,
                         grad_w_down, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_grouped_ffn_bwd(
         ctypes.byref(shape), _ptr(grad_y, BF16, "grad_y"), _ptr(expand_x, BF16, "expand_x"),
         _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(h_act, BF16, "h_act"),
@@ -234,6 +276,7 @@ def moe_grouped_ffn_bwd(shape, grad_y, expand_x, gate_up_save, h_act, w_gate, w_
 
 def moe_ffn_down_bwd_data(shape, grad_y, w_down, gate_up_save, ep_recv_counts, grad_gate_up,
                           stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_bwd_data(
         ctypes.byref(shape), _ptr(grad_y, BF16, "grad_y"), _ptr(w_down, BF16, "w_down"),
         _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
@@ -241,6 +284,7 @@ def moe_ffn_down_bwd_data(shape, grad_y, w_down, gate_up_save, ep_recv_counts, g
 
 
 def moe_ffn_down_bwd_weight(shape, grad_y, h_act, ep_recv_counts, grad_w_down, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_bwd_weight(
         ctypes.byref(shape), _ptr(grad_y, BF16, "grad_y"), _ptr(h_act, BF16, "h_act"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_w_down, F32, "grad_w_down"),
@@ -249,6 +293,7 @@ def moe_ffn_down_bwd_weight(shape, grad_y, h_act, ep_recv_counts, grad_w_down, s
 
 def moe_ffn_gate_up_bwd_data(shape, grad_gate_up, w_gate, w_up, ep_recv_counts, grad_expand_x,
                              stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_bwd_data(
         ctypes.byref(shape), _ptr(grad_gate_up, BF16, "grad_gate_up"), _ptr(w_gate, BF16, "w_gate"),
         _ptr(w_up, BF16, "w_up"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
@@ -257,6 +302,7 @@ def moe_ffn_gate_up_bwd_data(shape, grad_gate_up, w_gate, w_up, ep_recv_counts, 
 
 def moe_ffn_gate_up_bwd_weight(shape, grad_gate_up, expand_x, ep_recv_counts, grad_w_gate,
                                grad_w_up, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_bwd_weight(
         ctypes.byref(shape), _ptr(grad_gate_up, BF16, "grad_gate_up"), _ptr(expand_x, BF16, "expand_x"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_w_gate, F32, "grad_w_gate"),
@@ -265,6 +311,7 @@ def moe_ffn_gate_up_bwd_weight(shape, grad_gate_up, expand_x, ep_recv_counts, gr
 
 def moe_dispatch_bwd(shape, grad_expand_x, assist_info_for_combine, topk_idx, topk_weights,
                      x_active_mask, grad_out, const_alpha_1, grad_x_accum, grad_x, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_dispatch_bwd(
         ctypes.byref(shape), _ptr(grad_expand_x, BF16, "grad_expand_x"),
         _ptr(assist_info_for_combine, I32, "assist"), _ptr(topk_idx, I32, "topk_idx"),
@@ -278,6 +325,8 @@ U8T, F32T = torch.uint8, torch.float32
 
 def moe_quant_rows_fp8(src, codes, scales, nrows=None, stream=None):
     R, C = src.shape
+    _need(codes, R * C, "codes")
+    _need(scales, R * (C // 128), "scales")
     _check(lib().moe_quant_rows_fp8(R, C, _ptr(src, BF16, "src"), _ptr(nrows, I32, "nrows"),
                                     _ptr(codes, U8T, "codes"), _ptr(scales, F32T, "scales"),
                                     _stream(stream)))
@@ -285,6 +334,8 @@ def moe_quant_rows_fp8(src, codes, scales, nrows=None, stream=None):
 
 def moe_quantize_weights_fp8(w, codes, codes_t, scales, stream=None):
     E, N, K = w.shape
+    for t, nm in ((codes, "codes"), (codes_t, "codes_t")):
+        _need(t, E * N * K, nm)
     _check(lib().moe_quantize_weights_fp8(E, N, K, _ptr(w, BF16, "w"), _ptr(codes, U8T, "codes"),
                                           _ptr(codes_t, U8T, "codes_t"), _ptr(scales, F32T, "scales"),
                                           _stream(stream)))
@@ -292,6 +343,7 @@ def moe_quantize_weights_fp8(w, codes, codes_t, scales, stream=None):
 
 def moe_ffn_gate_up_fwd_fp8(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act,
                             stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_fwd_fp8(
         ctypes.byref(shape), _ptr(xq, U8T, "xq"), _ptr(xs, F32T, "xs"), _ptr(wgq, U8T, "wgq"),
         _ptr(wgs, F32T, "wgs"), _ptr(wuq, U8T, "wuq"), _ptr(wus, F32T, "wus"),
@@ -301,6 +353,7 @@ def moe_ffn_gate_up_fwd_fp8(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, g
 
 def moe_ffn_gate_up_fwd_fp8_quant(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act,
                                   hq_t, hs_t, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_fwd_fp8_quant(
         ctypes.byref(shape), _ptr(xq, U8T, "xq"), _ptr(xs, F32T, "xs"), _ptr(wgq, U8T, "wgq"),
         _ptr(wgs, F32T, "wgs"), _ptr(wuq, U8T, "wuq"), _ptr(wus, F32T, "wus"),
@@ -309,6 +362,7 @@ def moe_ffn_gate_up_fwd_fp8_quant(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_cou
 
 
 def moe_ffn_down_fwd_fp8(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_fwd_fp8(
         ctypes.byref(shape), _ptr(hq, U8T, "hq"), _ptr(hs, F32T, "hs"), _ptr(wdq, U8T, "wdq"),
         _ptr(wds, F32T, "wds"), _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"),
@@ -317,6 +371,7 @@ def moe_ffn_down_fwd_fp8(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None
 
 def moe_ffn_down_bwd_data_fp8(shape, dyq, dys, wdq_t, wds, gate_up_save, ep_recv_counts, grad_gate_up,
                               stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_bwd_data_fp8(
         ctypes.byref(shape), _ptr(dyq, U8T, "dyq"), _ptr(dys, F32T, "dys"), _ptr(wdq_t, U8T, "wdq_t"),
         _ptr(wds, F32T, "wds"), _ptr(gate_up_save, BF16, "gate_up_save"),
@@ -329,6 +384,7 @@ def moe_ffn_down_bwd_data_fp8_quant(shape, dyq, dys, wdq_t, wds, gate_up_save, e
     """moe_ffn_down_bwd_data_fp8 writing any of: bf16 grad_gate_up, rows = (codes,
     scales) of moe_quant_rows_fp8 layout, cols = (codes_t, scales) of
     moe_quant_cols_fp8 layout."""
+    _check_sizes(shape, locals())
     dguq, dgus = rows if rows is not None else (None, None)
     dguq_t, dgus_t = cols if cols is not None else (None, None)
     _check(lib().moe_ffn_down_bwd_data_fp8_quant(
@@ -341,6 +397,7 @@ def moe_ffn_down_bwd_data_fp8_quant(shape, dyq, dys, wdq_t, wds, gate_up_save, e
 
 def moe_ffn_gate_up_bwd_data_fp8(shape, dguq, dgus, wgq_t, wgs, wuq_t, wus, ep_recv_counts,
                                  grad_expand_x, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_bwd_data_fp8(
         ctypes.byref(shape), _ptr(dguq, U8T, "dguq"), _ptr(dgus, F32T, "dgus"),
         _ptr(wgq_t, U8T, "wgq_t"), _ptr(wgs, F32T, "wgs"), _ptr(wuq_t, U8T, "wuq_t"),
@@ -362,6 +419,7 @@ def moe_quant_cols_fp8(src, ep_recv_counts, codes_t, scales, stream=None):
 
 
 def moe_ffn_down_bwd_weight_fp8(shape, dyq_t, dys, hq_t, hs, ep_recv_counts, grad_w_down, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_bwd_weight_fp8(
         ctypes.byref(shape), _ptr(dyq_t, U8T, "dyq_t"), _ptr(dys, F32T, "dys"), _ptr(hq_t, U8T, "hq_t"),
         _ptr(hs, F32T, "hs"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
@@ -370,6 +428,7 @@ def moe_ffn_down_bwd_weight_fp8(shape, dyq_t, dys, hq_t, hs, ep_recv_counts, gra
 
 def moe_ffn_gate_up_bwd_weight_fp8(shape, dguq_t, dgus, xq_t, xs, ep_recv_counts, grad_w_gate, grad_w_up,
                                    stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_bwd_weight_fp8(
         ctypes.byref(shape), _ptr(dguq_t, U8T, "dguq_t"), _ptr(dgus, F32T, "dgus"),
         _ptr(xq_t, U8T, "xq_t"), _ptr(xs, F32T, "xs"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
@@ -382,6 +441,7 @@ I8T = torch.int8
 def moe_dispatch_int8(shape, x, topk_idx, x_active_mask, smooth_scales, expand_x, dynamic_scales,
                       assist_info_for_combine, expert_token_nums, ep_recv_counts, err_flag, workspace,
                       stream=None):
+    _check_sizes(shape, locals())
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().moe_dispatch_int8(
         ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(topk_idx, I32, "topk_idx"),
@@ -395,12 +455,15 @@ def moe_dispatch_int8(shape, x, topk_idx, x_active_mask, smooth_scales, expand_x
 def moe_quant_rows_int8(src, codes, scales, nrows=None, stream=None):
     C = src.shape[-1]
     R = src.numel() // C
+    _need(codes, R * C, "codes")
+    _need(scales, R, "scales")
     _check(lib().moe_quant_rows_int8(R, C, _ptr(src, BF16, "src"), _ptr(nrows, I32, "nrows"),
                                      _ptr(codes, I8T, "codes"), _ptr(scales, F32, "scales"), _stream(stream)))
 
 
 def moe_ffn_gate_up_fwd_int8(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act,
                              stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_fwd_int8(
         ctypes.byref(shape), _ptr(xq, I8T, "xq"), _ptr(xs, F32, "xs"), _ptr(wgq, I8T, "wgq"),
         _ptr(wgs, F32, "wgs"), _ptr(wuq, I8T, "wuq"), _ptr(wus, F32, "wus"),
@@ -409,6 +472,7 @@ def moe_ffn_gate_up_fwd_int8(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, 
 
 
 def moe_ffn_down_fwd_int8(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_fwd_int8(
         ctypes.byref(shape), _ptr(hq, I8T, "hq"), _ptr(hs, F32, "hs"), _ptr(wdq, I8T, "wdq"),
         _ptr(wds, F32, "wds"), _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"),
@@ -426,12 +490,17 @@ def quant_rows_int8(src, nrows=None, stream=None):
 
 def moe_quant_rows_mx(src, codes, scales, nrows=None, stream=None):
     R, C = src.shape
+    _need(codes, R * C, "codes")
+    _need(scales, R * (C // 32), "scales")
     _check(lib().moe_quant_rows_mx(R, C, _ptr(src, BF16, "src"), _ptr(nrows, I32, "nrows"),
                                    _ptr(codes, U8T, "codes"), _ptr(scales, U8T, "scales"), _stream(stream)))
 
 
 def moe_quantize_weights_mx(w, codes, scales, codes_t=None, scales_t=None, stream=None):
     E, N, K = w.shape
+    for t, nm, n in ((codes, "codes", E * N * K), (codes_t, "codes_t", E * N * K),
+                     (scales, "scales", E * N * K // 32), (scales_t, "scales_t", E * N * K // 32)):
+        _need(t, n, nm)
     _check(lib().moe_quantize_weights_mx(E, N, K, _ptr(w, BF16, "w"), _ptr(codes, U8T, "codes"),
                                          _ptr(scales, U8T, "scales"), _ptr(codes_t, U8T, "codes_t"),
                                          _ptr(scales_t, U8T, "scales_t"), _stream(stream)))
@@ -440,6 +509,7 @@ def moe_quantize_weights_mx(w, codes, scales, codes_t=None, scales_t=None, strea
 def moe_ffn_gate_up_fwd_mx(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, gate_up_save, h_act, h_rows=None,
                            stream=None):
     """h_rows: optional (codes, scales) receiving the MX row codes of h_act."""
+    _check_sizes(shape, locals())
     hq, hs = h_rows if h_rows is not None else (None, None)
     _check(lib().moe_ffn_gate_up_fwd_mx(
         ctypes.byref(shape), _ptr(xq, U8T, "xq"), _ptr(xs, U8T, "xs"), _ptr(wgq, U8T, "wgq"),
@@ -449,6 +519,7 @@ def moe_ffn_gate_up_fwd_mx(shape, xq, xs, wgq, wgs, wuq, wus, ep_recv_counts, ga
 
 
 def moe_ffn_down_fwd_mx(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_down_fwd_mx(
         ctypes.byref(shape), _ptr(hq, U8T, "hq"), _ptr(hs, U8T, "hs"), _ptr(wdq, U8T, "wdq"),
         _ptr(wds, U8T, "wds"), _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(y, BF16, "y"),
@@ -458,6 +529,7 @@ def moe_ffn_down_fwd_mx(shape, hq, hs, wdq, wds, ep_recv_counts, y, stream=None)
 def moe_ffn_down_bwd_data_mx(shape, dyq, dys, wdq_t, wds_t, gate_up_save, ep_recv_counts, grad_gate_up,
                              rows=None, stream=None):
     """rows: optional (codes, scales) receiving the MX row codes of dG|dU."""
+    _check_sizes(shape, locals())
     dguq, dgus = rows if rows is not None else (None, None)
     _check(lib().moe_ffn_down_bwd_data_mx(
         ctypes.byref(shape), _ptr(dyq, U8T, "dyq"), _ptr(dys, U8T, "dys"), _ptr(wdq_t, U8T, "wdq_t"),
@@ -468,6 +540,7 @@ def moe_ffn_down_bwd_data_mx(shape, dyq, dys, wdq_t, wds_t, gate_up_save, ep_rec
 
 def moe_ffn_gate_up_bwd_data_mx(shape, dguq, dgus, wgq_t, wgs_t, wuq_t, wus_t, ep_recv_counts, grad_expand_x,
                                 stream=None):
+    _check_sizes(shape, locals())
     _check(lib().moe_ffn_gate_up_bwd_data_mx(
         ctypes.byref(shape), _ptr(dguq, U8T, "dguq"), _ptr(dgus, U8T, "dgus"), _ptr(wgq_t, U8T, "wgq_t"),
         _ptr(wgs_t, U8T, "wgs_t"), _ptr(wuq_t, U8T, "wuq_t"), _ptr(wus_t, U8T, "wus_t"),

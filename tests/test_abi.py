@@ -255,3 +255,28 @@ def test_mx_entries_reject_bad_arguments_before_launch(L):
     assert L.moe_ffn_down_fwd_mx(s8, P(), P(), P(), Nn, P(), P(), Nn) == NULL_ARG
     assert L.moe_ffn_down_bwd_data_mx(s8, P(), P(), P(), P(), P(), P(), Nn, Nn, Nn, Nn) == NULL_ARG  # no output
     assert L.moe_ffn_gate_up_bwd_data_mx(s8, P(), P(), P(), P(), P(), Nn, P(), P(), Nn) == NULL_ARG
+
+
+def test_wrappers_reject_short_buffers():
+    """The Python entries compare each buffer with the size its layout needs before
+    any pointer reaches the library (checked ahead of the device check, so CPU
+    tensors show it): a short buffer is an error, not an out-of-bounds access."""
+    import torch
+    import dispatch_expert_gemm_amd as dm
+    s = dm.make_shape(T=16, H=128, K=2, num_experts=4, F=128, capacity=64)
+    bf = lambda *n: torch.zeros(n, dtype=torch.bfloat16)
+    i32 = lambda *n: torch.zeros(n, dtype=torch.int32)
+    ok = dict(expand_x=bf(64, 128), w_gate=bf(4, 128, 128), w_up=bf(4, 128, 128),
+              ep_recv_counts=i32(4), gate_up_save=bf(64, 256), h_act=bf(64, 128))
+    with pytest.raises(dm.MoeError, match="GPU tensor"):      # sizes fine: the device check fires
+        dm.moe_ffn_gate_up_fwd(s, **ok)
+    for name, short in (("expand_x", bf(63, 128)), ("w_up", bf(4, 127, 128)), ("ep_recv_counts", i32(3)),
+                        ("gate_up_save", bf(64, 255)), ("h_act", bf(1))):
+        with pytest.raises(dm.MoeError, match=f"{name} holds"):
+            dm.moe_ffn_gate_up_fwd(s, **{**ok, name: short})
+    with pytest.raises(dm.MoeError, match="codes holds"):
+        dm.moe_quant_rows_mx(bf(8, 256), torch.zeros(8 * 256 - 1, dtype=torch.uint8),
+                             torch.zeros(64, dtype=torch.uint8))
+    with pytest.raises(dm.MoeError, match="scales holds"):
+        dm.moe_quant_rows_fp8(bf(8, 256), torch.zeros(8 * 256, dtype=torch.uint8),
+                              torch.zeros(15, dtype=torch.float32))
