@@ -369,3 +369,69 @@ def test_mixtral_fp8_full_size():
     check_close("grad_w_gate block", f32(gwg[ea][cs]), dwg[0], rel_l2=REL_FP8)
     check_close("grad_w_up block", f32(gwu[ea][cs]), dwu[0], rel_l2=REL_FP8)
     check_close("grad_w_down block", f32(gwd[ea][:, cs]), dwd[0], rel_l2=REL_FP8)
+
+
+@pytest.mark.timeout(300)   # the oracle's MX quantisation of one expert's weights takes about a minute
+def test_mixtral_mx_full_size():
+    """T=8192, H=4096, F=14336, E=8, K=2 through the microscaled GEMM chain the
+    benchmark times (the down GEMM and the gate/up data gradient read the MX codes
+    that the preceding GEMMs' epilogues wrote).  Against the quantiser: those fused
+    codes and scales over every routed row, bit for bit.  Against the oracle: 16
+    sampled rows of the busiest expert (its tiles include the ragged last one)
+    through G, U, h, y, dG|dU and dX (MX quantisation runs along rows, so a row's results need no
+    other row).  y and dX are one requantisation further on (h, dG|dU), where a
+    1-ulp bf16 difference can move a code by one step: their max bar is 5e-2, the
+    relative L2 bar the same as elsewhere."""
+    print("[full] mixtral mx", flush=True)
+    inp = wl.layer_inputs(**{k: v for k, v in wl.WORKLOADS["mixtral"].items()}, seed=1)
+    T, H, F, K, E = inp["T"], inp["H"], inp["F"], inp["K"], inp["E"]
+    run = Run(inp)
+    run.dispatch()
+    cap = run.cap
+    recv = run.d.ep_recv_counts
+    nrows = recv[-1:]
+    wq = [dm.MxWeights.quantize(bf(inp[k])) for k in ("w_gate", "w_up", "w_down")]
+    u8 = lambda *n: torch.empty(n, dtype=torch.uint8, device=DEV)
+    b16 = lambda *n: torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    xq, xs = dm.quant_rows_mx(run.d.expand_x, nrows)
+    gus, h, y = b16(cap, 2 * F), b16(cap, F), b16(cap, H)
+    hq, hs = u8(cap, F), u8(cap, F // 32)
+    dm.moe_ffn_gate_up_fwd_mx(run.shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h,
+                              (hq, hs))
+    dm.moe_ffn_down_fwd_mx(run.shape, hq, hs, wq[2].codes, wq[2].scales, recv, y)
+    dY_bits = wl.to_bf16_bits(np.random.default_rng(31).standard_normal((cap, H), dtype=np.float32) * 0.05)
+    dyq, dys = dm.quant_rows_mx(bf(dY_bits), nrows)
+    ggu, dgq, dgs = b16(cap, 2 * F), u8(cap, 2 * F), u8(cap, 2 * F // 32)
+    dm.moe_ffn_down_bwd_data_mx(run.shape, dyq, dys, wq[2].codes_t, wq[2].scales_t, gus, recv, ggu, (dgq, dgs))
+    gxe = b16(cap, H)
+    dm.moe_ffn_gate_up_bwd_data_mx(run.shape, dgq, dgs, wq[0].codes_t, wq[0].scales_t, wq[1].codes_t,
+                                   wq[1].scales_t, recv, gxe)
+    torch.cuda.synchronize()
+    r = orc.route(inp["topk_idx"], E)
+    A = r.A
+    check_equal("ep_recv_counts", recv.cpu().numpy(), r.ep_recv_counts)
+    # fused codes against the row quantiser on the same bf16 outputs, on the GPU
+    for name, src, q, s, C in (("h", h, hq, hs, F), ("dG|dU", ggu, dgq, dgs, 2 * F)):
+        q2, s2 = dm.quant_rows_mx(src, nrows)
+        torch.cuda.synchronize()
+        assert torch.equal(q[:A], q2[:A]), f"{name} codes (fused) differ"
+        sv, sv2 = s.view(C // 128, cap, 4)[:, :A], s2.view(C // 128, cap, 4)[:, :A]
+        assert torch.equal(sv, sv2), f"{name} scales (fused) differ"
+        del q2, s2
+    print("[full] mixtral mx: GPU chain done, oracle of the busiest expert", flush=True)
+    rng = np.random.default_rng(32)
+    X = orc.bf16_to_f32(inp["x"])
+    for e in (int(np.argmax(r.counts)),):
+        lo, hi = r.row_range(e)
+        rows = lo + np.union1d(_sample(rng, hi - lo, 15), [hi - lo - 1])   # the last row is in the ragged tile
+        owq = tuple(orc.quant_weights_mx(inp[k][e:e + 1]) for k in ("w_gate", "w_up", "w_down"))
+        n = np.array([len(rows)])
+        Xs = X[r.row2slot[rows] // K]
+        G, U, Hh, Y = orc.ffn_fwd_mx(Xs, n, *owq)
+        check_close(f"G e={e}", f32(gus[rows, :F]), G, rel_l2=2e-3)
+        check_close(f"U e={e}", f32(gus[rows, F:]), U, rel_l2=2e-3)
+        check_close(f"h e={e}", f32(h[rows]), Hh, rel_l2=REL_FP8)
+        check_close(f"y e={e}", f32(y[rows]), Y, max_abs=5e-2, rel_l2=REL_FP8)
+        dGU, dX, _, _, _ = orc.ffn_bwd_mx(orc.bf16_to_f32(dY_bits[rows]), Xs, G, U, Hh, n, *owq)
+        check_close(f"grad_gate_up e={e}", f32(ggu[rows]), dGU, rel_l2=REL_FP8)
+        check_close(f"grad_expand_x e={e}", f32(gxe[rows]), dX, max_abs=5e-2, rel_l2=REL_FP8)
