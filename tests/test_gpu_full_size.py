@@ -435,3 +435,45 @@ def test_mixtral_mx_full_size():
         dGU, dX, _, _, _ = orc.ffn_bwd_mx(orc.bf16_to_f32(dY_bits[rows]), Xs, G, U, Hh, n, *owq)
         check_close(f"grad_gate_up e={e}", f32(ggu[rows]), dGU, rel_l2=REL_FP8)
         check_close(f"grad_expand_x e={e}", f32(gxe[rows]), dX, max_abs=5e-2, rel_l2=REL_FP8)
+
+
+@pytest.mark.timeout(300)   # host generation of the four full-size operands takes a few seconds
+def test_mixtral_fp8_weight_gradients_full_size():
+    """The fp8 weight-gradient GEMMs (per-128-token codes) at the Mixtral-style
+    size (T=8192, K=2 over E=8 experts, H=4096, F=14336), in the launch the
+    benchmark's fp8-weight-gradient variant makes.  Every expert's dW_down on 16
+    sampled rows x 16 sampled columns, and dW_gate, dW_up on 16 x 16, against the
+    oracle's wgrad_fp8 on the matching operand columns: the quantisation runs
+    down each column within a 128-token slot, so a column slice gives those
+    entries exactly.  The codes are identical on both sides; the bar is the
+    accumulation-order bar of the small cases (1e-4)."""
+    print("[full] mixtral fp8 weight gradients", flush=True)
+    H, F, E, K, T = 4096, 14336, 8, 2, 8192
+    rng = np.random.default_rng(41)
+    idx, _ = wl.router(rng.standard_normal((T, E)).astype(np.float32), K, True)
+    r = orc.route(idx, E)
+    prefix = r.ep_recv_counts.astype(np.int64)
+    A = int(prefix[-1])
+    cap = A + 128 * E
+    mats = {k: wl.to_bf16_bits(rng.standard_normal((cap, d), dtype=np.float32) * s)
+            for k, d, s in (("dY", H, 0.1), ("h", F, 1.0), ("dGU", 2 * F, 0.05), ("x", H, 1.0))}
+    counts = torch.from_numpy(prefix.astype(np.int32)).to(DEV)
+    shape = dm.make_shape(T, H, K, E, F=F, capacity=cap)
+    q = {k: dm.quant_cols_fp8(bf(v), counts) for k, v in mats.items()}
+    gwd = torch.full((E, H, F), float("nan"), dtype=torch.float32, device=DEV)
+    gwg = torch.full((E, F, H), float("nan"), dtype=torch.float32, device=DEV)
+    gwu = torch.full((E, F, H), float("nan"), dtype=torch.float32, device=DEV)
+    dm.moe_ffn_down_bwd_weight_fp8(shape, *q["dY"], *q["h"], counts, gwd)
+    dm.moe_ffn_gate_up_bwd_weight_fp8(shape, *q["dGU"], *q["x"], counts, gwg, gwu)
+    torch.cuda.synchronize()
+    print("[full] mixtral fp8 weight gradients: GPU done, oracle on column samples", flush=True)
+    hs = np.union1d(_sample(rng, H, 15), [H - 1])
+    fs = np.union1d(_sample(rng, F, 15), [F - 1])
+    col = lambda k, c: orc.bf16_to_f32(mats[k][:A][:, c])
+    ref_d = orc.wgrad_fp8(col("dY", hs), col("h", fs), prefix)
+    ref_g = orc.wgrad_fp8(col("dGU", fs), col("x", hs), prefix)
+    ref_u = orc.wgrad_fp8(col("dGU", F + fs), col("x", hs), prefix)
+    ih, jf = torch.from_numpy(hs).to(DEV), torch.from_numpy(fs).to(DEV)
+    check_close("grad_w_down", f32(gwd[:, ih][:, :, jf]), ref_d, max_abs=1e-4, rel_l2=1e-4)
+    check_close("grad_w_gate", f32(gwg[:, jf][:, :, ih]), ref_g, max_abs=1e-4, rel_l2=1e-4)
+    check_close("grad_w_up", f32(gwu[:, jf][:, :, ih]), ref_u, max_abs=1e-4, rel_l2=1e-4)
