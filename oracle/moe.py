@@ -179,7 +179,10 @@ def dispatch(x, r: Route, prec="parity"):
 
 
 def silu(g):
-    return g / (1 + np.exp(-g))
+    """g * sigmoid(g).  For g below about -709, exp(-g) overflows to inf and the
+    quotient is the limit, -0; the overflow is expected there and not reported."""
+    with np.errstate(over="ignore"):
+        return g / (1 + np.exp(-g))
 
 
 def ffn_fwd(X, ep_recv_counts, w_gate, w_up, w_down, prec="parity"):
