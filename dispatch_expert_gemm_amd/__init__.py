@@ -28,7 +28,8 @@ MOE_SLOT_COPY = -2
 
 # every function include/moe.h declares
 ENTRY_POINTS = (
-    "moe_status_str", "moe_assist_info_size", "moe_workspace_size", "moe_dispatch",
+    "moe_status_str", "moe_assist_info_size", "moe_workspace_size", "moe_dispatch", "moe_route",
+    "moe_ffn_gate_up_fwd_gather",
     "moe_grouped_ffn", "moe_ffn_gate_up_fwd", "moe_ffn_down_fwd", "moe_combine",
     "moe_combine_bwd", "moe_grouped_ffn_bwd", "moe_ffn_down_bwd_data", "moe_ffn_down_bwd_weight",
     "moe_ffn_gate_up_bwd_data", "moe_ffn_gate_up_bwd_weight", "moe_dispatch_bwd",
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_grouped_ffn.argtypes = [S, P, P, P, P, P, P, P, P, P]
         L.moe_ffn_gate_up_fwd.argtypes = [S, P, P, P, P, P, P, P]
+        L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_ffn_gate_up_fwd_gather.argtypes = [S] + [P] * 8
         L.moe_ffn_down_fwd.argtypes = [S, P, P, P, P, P]
         L.moe_combine.argtypes = [S] + [P] * 13
         L.moe_combine_bwd.argtypes = [S] + [P] * 14
@@ -207,6 +210,26 @@ def moe_dispatch(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_co
         _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
         _ptr(err_flag, I32, "err_flag"), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_route(shape, topk_idx, x_active_mask, assist_info_for_combine, expert_token_nums, ep_recv_counts,
+              err_flag, workspace, stream=None):
+    _check_sizes(shape, locals())
+    _check(lib().moe_route(
+        ctypes.byref(shape), _ptr(topk_idx, I32, "topk_idx"), _ptr(x_active_mask, U8, "x_active_mask"),
+        _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
+        _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(err_flag, I32, "err_flag"), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_ffn_gate_up_fwd_gather(shape, x, assist_info_for_combine, w_gate, w_up, ep_recv_counts, gate_up_save,
+                               h_act, stream=None):
+    _check_sizes(shape, locals())
+    _check(lib().moe_ffn_gate_up_fwd_gather(
+        ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
+        _ptr(w_gate, BF16, "w_gate"), _ptr(w_up, BF16, "w_up"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(h_act, BF16, "h_act"), _stream(stream)))
 
 
 def moe_grouped_ffn(shape, expand_x, w_gate, w_up, w_down, ep_recv_counts, gate_up_save, h_act, y,

@@ -76,6 +76,11 @@ constexpr int kBufferFlags = 0x00020000;
 struct GemmArgs {
   const bf16_t* A;
   int64_t lda;
+  // bf16 gate/up forward only: when set, A is the token matrix x and row r of
+  // the expert-sorted operand is x[gather[r] / gK] (gather = the row -> slot
+  // map of the routing, gK = top-K), so the dispatch permute is not needed
+  const int32_t* gather;
+  int gK;
   const bf16_t* B0;
   const bf16_t* B1;
   int64_t ldb;
@@ -713,7 +718,10 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     if constexpr (!KGROUP) {
       const int r = RPIK * q + lane / CPRK, c = (lane % CPRK) ^ swz(r);
       const int rr = r < rows_valid ? r : rows_valid - 1;
-      voA[j] = (uint32_t)((rr * g.lda + c * 8) * 2);
+      int64_t arow = rr;  // row of A relative to abase
+      if constexpr (MODE == GATE_UP_FWD && !FP8)
+        if (g.gather) arow = g.gather[row0 + rr] / g.gK;  // the token of this expanded row
+      voA[j] = (uint32_t)((arow * g.lda + c * 8) * 2);
       kcA[j] = c * 8;
     } else {
       constexpr int CPR = BM / 8, RPI = 64 / CPR;
@@ -746,7 +754,9 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
       kcB[j] = 0;
     }
   }
-  const char* abase = reinterpret_cast<const char*>(KGROUP ? g.A + kbeg * g.lda : g.A + row0 * g.lda);
+  const bool gathered = MODE == GATE_UP_FWD && !FP8 && g.gather;
+  const char* abase =
+      reinterpret_cast<const char*>(KGROUP ? g.A + kbeg * g.lda : (gathered ? g.A : g.A + row0 * g.lda));
   const char* bbase0;
   const char* bbase1;
   if constexpr (KGROUP) {
@@ -1433,6 +1443,34 @@ extern "C" moe_status moe_ffn_gate_up_fwd(const moe_shape* s, const void* expand
   if (!expand_x || !gate_up_save || !h_act) return MOE_ERR_NULL_ARG;
   GemmArgs g = base_args(s, ep_recv_counts);
   g.A = static_cast<const bf16_t*>(expand_x);
+  g.lda = s->H;
+  g.B0 = static_cast<const bf16_t*>(w_gate);
+  g.B1 = static_cast<const bf16_t*>(w_up);
+  g.ldb = s->H;
+  g.bstride = s->F * s->H;
+  g.N = s->F;
+  g.Kd = s->H;
+  g.C0 = static_cast<bf16_t*>(h_act);
+  g.C1 = static_cast<bf16_t*>(gate_up_save);
+  return launch<GATE_UP_FWD>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_gate_up_fwd_gather(const moe_shape* s, const void* x, const int32_t* assist,
+                                                 const void* w_gate, const void* w_up,
+                                                 const int32_t* ep_recv_counts, void* gate_up_save,
+                                                 void* h_act, void* stream) {
+  moe_status st = check_ffn_shape(s);
+  if (st != MOE_OK) return st;
+  if (!w_gate || !w_up || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  // the per-lane byte offsets into x are 31-bit (the top bit marks a load past
+  // the end of the contraction)
+  if ((s->T + 1) * s->H * 2 > 0x7ffffff0LL) return MOE_ERR_UNSUPPORTED;
+  if (s->capacity == 0) return MOE_OK;
+  if (!x || !assist || !gate_up_save || !h_act) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.A = static_cast<const bf16_t*>(x);
+  g.gather = assist + s->T * s->K;  // row -> slot
+  g.gK = s->K;
   g.lda = s->H;
   g.B0 = static_cast<const bf16_t*>(w_gate);
   g.B1 = static_cast<const bf16_t*>(w_up);

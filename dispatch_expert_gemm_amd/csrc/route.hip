@@ -363,11 +363,10 @@ extern "C" moe_status moe_workspace_size(const moe_shape* s, size_t* bytes) {
 namespace {
 // argument checks shared by the two dispatch entries (the expanded-row buffer is
 // checked by each)
-moe_status check_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
+moe_status check_dispatch(const moe_shape* s, const int32_t* topk_idx,
                           const uint8_t* x_active_mask, int32_t* assist, int32_t* expert_token_nums,
                           int32_t* ep_recv_counts, int32_t* err_flag, void* workspace, size_t ws_bytes) {
   const int64_t TK = s->T * s->K;
-  MOE_NEED(x, s->T * s->H);
   MOE_NEED(topk_idx, TK);
   MOE_NEED(x_active_mask, s->mask_ndim == 0 ? 0 : (s->mask_ndim == 1 ? s->T : TK));
   MOE_NEED(assist, TK + s->capacity);
@@ -406,6 +405,19 @@ void launch_route(const moe_shape* s, const int32_t* topk_idx, const uint8_t* x_
 }
 }  // namespace
 
+extern "C" moe_status moe_route(const moe_shape* s, const int32_t* topk_idx, const uint8_t* x_active_mask,
+                                int32_t* assist, int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                                int32_t* err_flag, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_dispatch(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
+                      workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  launch_route(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag, workspace,
+               as_stream(stream));
+  return launch_status();
+}
+
 extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
                                    const uint8_t* x_active_mask, void* expand_x,
                                    int32_t* assist, int32_t* expert_token_nums,
@@ -413,9 +425,10 @@ extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int3
                                    size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  st = check_dispatch(s, x, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
+  st = check_dispatch(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
                       workspace, ws_bytes);
   if (st != MOE_OK) return st;
+  MOE_NEED(x, s->T * s->H);
   MOE_NEED(expand_x, s->capacity * s->H);
   hipStream_t strm = as_stream(stream);
   launch_route(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag, workspace, strm);
@@ -440,9 +453,10 @@ extern "C" moe_status moe_dispatch_int8(const moe_shape* s, const void* x, const
   if (st != MOE_OK) return st;
   // the row lives in registers: at most 16 vectors of 8 per lane
   if (s->H > 64 * 8 * 16) return MOE_ERR_UNSUPPORTED;
-  st = check_dispatch(s, x, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
+  st = check_dispatch(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
                       workspace, ws_bytes);
   if (st != MOE_OK) return st;
+  MOE_NEED(x, s->T * s->H);
   MOE_NEED(expand_x, s->capacity * s->H);
   MOE_NEED(dynamic_scales, s->capacity);
   hipStream_t strm = as_stream(stream);

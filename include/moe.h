@@ -144,6 +144,27 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* expand_x, const void*
 
 /* First grouped GEMM of moe_grouped_ffn (gate and up projections with the
  * SwiGLU product fused into its epilogue).  One kernel launch. */
+/* moe_route - the routing half of moe_dispatch alone: the same assist info,
+ * expert_token_nums, ep_recv_counts and err_flag (same arguments, same checks),
+ * without x and without writing expanded rows.  For callers that read the
+ * tokens through the row -> slot map instead (moe_ffn_gate_up_fwd_gather). */
+moe_status moe_route(const moe_shape* s, const int32_t* topk_idx, const uint8_t* x_active_mask,
+                     int32_t* assist_info_for_combine, int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                     int32_t* err_flag, void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_ffn_gate_up_fwd_gather - moe_ffn_gate_up_fwd with the dispatch permute
+ * folded into its operand loads: expanded row r is read as x[slot(r) / K],
+ * slot(r) from the assist info of moe_route or moe_dispatch, so the result is
+ * bit for bit that of moe_ffn_gate_up_fwd on moe_dispatch's expand_x.
+ *  in   x (T, H) bf16; assist_info_for_combine as written by the routing;
+ *       w_gate, w_up, ep_recv_counts as for moe_ffn_gate_up_fwd
+ *  out  gate_up_save (capacity, 2F), h_act (capacity, F) bf16
+ * MOE_ERR_UNSUPPORTED when (T + 1) * H * 2 bytes exceed 2^31 - 16 (31-bit
+ * operand offsets). */
+moe_status moe_ffn_gate_up_fwd_gather(const moe_shape* s, const void* x, const int32_t* assist_info_for_combine,
+                                      const void* w_gate, const void* w_up, const int32_t* ep_recv_counts,
+                                      void* gate_up_save, void* h_act, void* stream);
+
 moe_status moe_ffn_gate_up_fwd(const moe_shape* s, const void* expand_x, const void* w_gate,
                                const void* w_up, const int32_t* ep_recv_counts,
                                void* gate_up_save, void* h_act, void* stream);
