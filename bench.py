@@ -65,6 +65,7 @@ WORKLOADS = {
     # the low_latency_combine page's decode regime (BS <= 512 tokens, H = 7168,
     # top-8, 32 experts in its example), every expert on one GPU, forward only
     "decode": dict(T=512, H=7168, F=2048, E=32, K=8, forward_only=True),
+    "decode_gather": dict(T=512, H=7168, F=2048, E=32, K=8, forward_only=True, gather=True),
     # the same batch on the page's quant_mode 2 path: int8 dispatch with per-expert
     # smooth scales, w8a8 grouped GEMMs (int8 weights: half the bytes to stream)
     "decode_int8": dict(T=512, H=7168, F=2048, E=32, K=8, forward_only=True, int8=True),
@@ -316,6 +317,9 @@ def build_step(name, T_override=None):
         # weight quantisation (once per weight update) is timed outside the step
         st.extra_calls.append(("moe_quant_rows_int8 (3 weight tensors)",
                                lambda: [dm.quant_rows_int8(t) for t in (wg, wu, wd)]))
+    elif cfg.get("gather"):
+        # routing only: the gate/up GEMM reads the rows from x itself
+        C.append(("moe_route", lambda: dm.moe_route(shape, idx, None, assist, cnt, recv, err, ws)))
     else:
         C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
     if int8:
@@ -371,6 +375,12 @@ def build_step(name, T_override=None):
             i = [n for n, _ in C].index("moe_ffn_gate_up_fwd_fp8")
             C[i] = ("moe_ffn_gate_up_fwd_fp8", lambda: dm.moe_ffn_gate_up_fwd_fp8_quant(
                 shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h, *cq["h"]))
+    elif cfg.get("gather"):
+        C += [
+            ("moe_ffn_gate_up_fwd_gather", lambda: dm.moe_ffn_gate_up_fwd_gather(shape, x, assist, wg, wu, recv,
+                                                                                 gus, h)),
+            ("moe_ffn_down_fwd", lambda: dm.moe_ffn_down_fwd(shape, h, wd, recv, y)),
+        ]
     else:
         C += [
             ("moe_ffn_gate_up_fwd", lambda: dm.moe_ffn_gate_up_fwd(shape, ex, wg, wu, recv, gus, h)),
@@ -522,6 +532,9 @@ def account(st, A):
     for n in ("moe_dispatch", "moe_combine") if fwd_only else ("moe_dispatch", "moe_combine", "moe_combine_bwd",
                                                                 "moe_dispatch_bwd"):
         nb[n] = bytes_moved(n, T, H, F, K, A, E)
+    if st.cfg.get("gather"):
+        fl["moe_ffn_gate_up_fwd_gather"] = fl.pop("moe_ffn_gate_up_fwd")
+        nb["moe_route"] = nb.pop("moe_dispatch") - T * H * 2 - A * H * 2   # no rows moved
     if int8:
         # int8 rows and one fp32 scale per row written, the smooth scales read once
         nb["moe_dispatch_int8"] = nb.pop("moe_dispatch") - A * H * 2 + A * H + A * 4 + E * H * 4
@@ -672,6 +685,7 @@ def main():
         "combine_stress": "combine only, 256 routed + 1 zero + 1 copy + 2 constant experts, "
                           "2-D mask 10% false, shared_expert_x",
         "decode": "decode batch (the low_latency_combine page's largest BS), forward only",
+        "decode_gather": "decode batch, forward only, dispatch folded into the gate/up GEMM's row loads",
         "decode_int8": "decode batch, forward only, int8 dispatch with smooth scales (quant_mode 2) and "
                        "w8a8 GEMMs",
     }[args.workload]
