@@ -3,6 +3,8 @@ and a runner that pushes one set of generated inputs through the library's C
 entry points."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -11,21 +13,144 @@ import oracle as orc
 
 DEV = torch.device("cuda:0")
 
-# Accuracy bar for floating-point outputs (bf16 path), against the oracle's
-# parity mode:  max |err| <= 2e-2 * max(1, max |ref|)  and
-# ||gpu - oracle||_2 / ||oracle||_2 <= 5e-3.
-# The absolute bound applies to the tensor scaled to unit max-magnitude when that
-# magnitude exceeds 1: one bf16 rounding of an intermediate may land on the other
-# neighbour when two fp32 accumulation orders differ in the last bit, and at
-# |v| >= 4 one bf16 ulp is already >= 0.03 (and fp32 reductions over such
-# operands inherit that ulp times the other operand).
+# Accuracy bar for floating-point outputs, against the oracle's parity mode,
+# applied element by element:
+#
+#   |got_i - ref_i| <= MAX_ABS + ulps * ulp_bf16(ref_i) + rho * mag_i
+#
+# and ||got - ref||_2 / ||ref||_2 <= REL_L2 (bf16 path) or REL_L2_8BIT (fp8,
+# MX and int8 paths).
+#
+# * ulps: a bf16-stored output is the round-to-nearest-even of an fp32 value
+#   whose last bits depend on the accumulation order, so the two sides may land
+#   on neighbouring bf16 values: one ulp for a kernel fed the oracle's own
+#   operands (ULPS_KERNEL), two where the kernel's inputs are themselves device
+#   outputs that may sit one ulp off (ULPS_CHAIN).  At |v| >= 4 one bf16 ulp
+#   is >= 0.03, above MAX_ABS, which is why the term is needed at all.
+# * rho * mag: fp32 outputs that contract bf16 device intermediates (the
+#   weight gradients and dw of a chained step).  If every operand entry of
+#   P^T Q is within a relative 2^-6 (two bf16 ulps) of the oracle's, then
+#   |dP^T Q + P^T dQ + dP^T dQ| <= (2^-6 + 2^-6 + 2^-12) (|P|^T |Q|); RHO_CHAIN
+#   rounds that up to 2^-5 and mag = |P|^T |Q| is computed from the oracle's
+#   operands (contraction_mag).  On identical operands rho is 0, or RHO_FP32
+#   against the oracle's float64 sums: fp32 accumulation over n <= 4096 terms
+#   is within n 2^-24 |P|^T |Q| <= 2^-12 |P|^T |Q|.
+# * outliers: a chained 8-bit layer requantises the device's own bf16
+#   intermediates (h, y, dG|dU), which sit one bf16 ulp off the oracle's at a
+#   fraction of entries; where such an entry lies next to a rounding boundary
+#   of the 8-bit grid its code moves by one step (an e4m3 step is up to 1/8 of
+#   the value), and the outputs that contract it move by that step times a
+#   weight.  Those outputs (and nothing else) are held to the element bound on
+#   all but OUTLIER_FRAC of their elements (measured: at most 0.02%), and every
+#   element to OUTLIER_CAP; each GEMM fed the oracle's own codes meets the
+#   plain element bound (the stage-wise tests).
 MAX_ABS = 2e-2
 REL_L2 = 5e-3
+REL_L2_8BIT = 2e-2
+ULPS_KERNEL = 1
+ULPS_CHAIN = 2
+RHO_CHAIN = 2.0 ** -5
+RHO_FP32 = 2.0 ** -12
+OUTLIER_FRAC = 1e-3
+OUTLIER_CAP = 0.15
+OUTLIERS_8BIT = (OUTLIER_FRAC, OUTLIER_CAP)
+
+# PARITY_LOG=<path>: append one line per comparison (the figures printed);
+# PARITY_REPORT=1: record failures without raising (a measurement run).
+_LOG = os.environ.get("PARITY_LOG")
+_REPORT = os.environ.get("PARITY_REPORT") == "1"
+
+
+def ulp_bf16(v):
+    """Spacing of bf16 values next to |v|: 2^(e-7) for |v| in [2^e, 2^(e+1)), the
+    subnormal spacing 2^-133 below 2^-126."""
+    a = np.abs(np.asarray(v, np.float64))
+    _, e = np.frexp(np.maximum(a, 2.0 ** -126))   # a = m * 2^e, m in [0.5, 1)
+    return np.ldexp(1.0, e - 8)
+
+
+def contraction_mag(P, Q, ep_recv_counts):
+    """|P_e|^T |Q_e| for every expert's row range (float64, (E, P cols, Q cols)):
+    the magnitude a weight gradient's error bound scales with."""
+    P = np.abs(np.asarray(P, np.float64))
+    Q = np.abs(np.asarray(Q, np.float64))
+    counts = np.asarray(ep_recv_counts, np.int64)
+    out = np.zeros((len(counts), P.shape[1], Q.shape[1]))
+    lo = 0
+    for e, hi in enumerate(counts.tolist()):
+        if hi > lo:
+            out[e] = P[lo:hi].T @ Q[lo:hi]
+        lo = hi
+    return out
+
+
+def dw_mag(r, Y, grad_out, ori_x=None, const_alpha_1=None, const_alpha_2=None, const_v=None):
+    """Sum_h |v(t,k)_h| |dOut_t,h| for every slot (float64 (T, K)): the magnitude
+    the bound of dw = <v, dOut> scales with.  Y: the oracle's expert rows (float);
+    the bf16 inputs as bits; v as in combine (0 for inactive and zero slots)."""
+    T, K = r.T, r.K
+    d = np.abs(orc.bf16_to_f32(grad_out).astype(np.float64)) if T else np.zeros((0, 0))
+    Y = np.abs(np.asarray(Y, np.float64))
+    ox = None if ori_x is None else np.abs(orc.bf16_to_f32(ori_x).astype(np.float64))
+    a1, a2, cv = (None if a is None else np.abs(orc.bf16_to_f32(a).astype(np.float64))
+                  for a in (const_alpha_1, const_alpha_2, const_v))
+    codes = r.slot2row.reshape(T, K)
+    mag = np.zeros((T, K))
+    for t in range(T):
+        for k in range(K):
+            c = int(codes[t, k])
+            if c >= 0:
+                v = Y[c]
+            elif c == -2:
+                v = ox[t]
+            elif c <= -3:
+                v = a1[-c - 3] * ox[t] + a2[-c - 3] * cv[-c - 3]
+            else:
+                continue
+            mag[t, k] = float(v @ d[t])
+    return mag
+
+
+def layer_mags(inp, f, b):
+    """Magnitudes for the fp32 outputs of a whole layer step (oracle intermediates):
+    dw, and |P|^T |Q| of each weight gradient (routed, and the shared expert's when
+    the layer has one)."""
+    r = f["route"]
+    F = inp["F"]
+    Yv = f["Yc"] if "Yc" in f else f["Y"]
+    m = dict(dw=dw_mag(r, Yv, inp["grad_out"], inp["x"], inp.get("const_alpha_1"),
+                       inp.get("const_alpha_2"), inp.get("const_v")),
+             dWg=contraction_mag(b["dGU"][:, :F], f["X"], r.ep_recv_counts),
+             dWu=contraction_mag(b["dGU"][:, F:], f["X"], r.ep_recv_counts),
+             dWd=contraction_mag(b["dY"], f["Hh"], r.ep_recv_counts))
+    if "s_dGU" in b:
+        T = np.array([f["sX"].shape[0]])
+        dOut = orc.bf16_to_f32(inp["grad_out"])
+        m.update(s_dWg=contraction_mag(b["s_dGU"][:, :F], f["sX"], T),
+                 s_dWu=contraction_mag(b["s_dGU"][:, F:], f["sX"], T),
+                 s_dWd=contraction_mag(dOut, f["sH"], T))
+    return m
+
+
+def _log(line):
+    print(line, flush=True)
+    if _LOG:
+        with open(_LOG, "a") as f:
+            f.write(line + "\n")
 
 
 def bf(a):
     """uint16 bf16 bits (numpy) -> bf16 tensor on the GPU."""
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def dev_rows(a, capacity):
+    """Oracle rows (A, width) of bf16 values -> a zero-padded (capacity, width) bf16
+    device buffer (an expanded-row operand fed to one kernel)."""
+    a = np.asarray(a, np.float32)
+    full = np.zeros((capacity, a.shape[1]), np.float32)
+    full[:a.shape[0]] = a
+    return bf(orc.f32_to_bf16(full))
 
 
 def dev(a):
@@ -40,18 +165,39 @@ def f32(t):
     return t.float().cpu().numpy()
 
 
-def check_close(name, got, ref, max_abs=MAX_ABS, rel_l2=REL_L2):
+def check_close(name, got, ref, *, ulps=ULPS_CHAIN, max_abs=MAX_ABS, rel_l2=REL_L2, mag=None, rho=0.0,
+                outliers=None):
+    """Element-wise bar (see the top of this file); prints max|err| next to the
+    plain MAX_ABS so any element that needs the ulp or magnitude term shows."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     if got.size == 0:
         return
     assert np.isfinite(got).all(), f"{name}: non-finite values"
-    err = np.abs(got - ref).max()
-    scale = max(1.0, float(np.abs(ref).max()))
-    rl2 = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
-    assert err <= max_abs * scale and rl2 <= rel_l2, \
-        f"{name}: max|err|={err:.3e} (bound {max_abs * scale:.3e}) rel_l2={rl2:.3e}"
+    err = np.abs(got - ref)
+    bound = max_abs + ulps * ulp_bf16(ref)
+    if mag is not None and rho:
+        bound = bound + rho * np.broadcast_to(np.asarray(mag, np.float64), ref.shape)
+    ratio = err / bound
+    worst = int(np.argmax(ratio))
+    emax = float(err.max())
+    rl2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    nbad = int((err > bound).sum())
+    if outliers is None:
+        ok = nbad == 0 and rl2 <= rel_l2
+    else:
+        frac, cap = outliers
+        ok = nbad <= frac * got.size and emax <= cap and rl2 <= rel_l2
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    _log(f"[parity] {test} {name}: max|err|={emax:.3e} ({'within' if emax <= MAX_ABS else 'above'} plain "
+         f"{MAX_ABS:g}) worst err/bound={ratio.flat[worst]:.3f} at ref={ref.flat[worst]:.4g} "
+         f"(bound {bound.flat[worst]:.3e}) over={nbad}/{got.size}"
+         f"{'' if outliers is None else f' (allowed {outliers[0] * got.size:.0f}, cap {outliers[1]:g})'}"
+         f" rel_l2={rl2:.2e} (bar {rel_l2:g}){'' if ok else ' FAIL'}")
+    if not ok and not _REPORT:
+        raise AssertionError(f"{name}: {nbad} elements above the bound, max|err|={emax:.3e}, "
+                             f"worst err/bound={ratio.flat[worst]:.3f}, rel_l2={rl2:.3e} (bar {rel_l2:g})")
 
 
 def check_equal(name, got, ref):

@@ -1,7 +1,8 @@
 """GPU parity of the int8 path (the decode regime's quant_mode 2): int8 dispatch with
 optional per-expert smooth scales and the int8 row quantiser bit-exact against the
-oracle; the w8a8 grouped GEMMs and the whole decode forward within the 8-bit bar
-(max|err| <= 2e-2 * max(1, max|ref|), relative L2 <= 2e-2)."""
+oracle; the w8a8 grouped GEMMs fed the oracle's operands within 2e-2 plus one bf16
+ulp per element, and the whole decode forward at the chained bar written out in
+gpu_util (relative L2 <= 2e-2 throughout)."""
 import numpy as np
 import pytest
 import torch
@@ -9,11 +10,11 @@ import torch
 import dispatch_expert_gemm_amd as dm
 import moe_workloads as wl
 import oracle as orc
-from gpu_util import DEV, Run, bf, check_close, check_equal, dev, f32
+from gpu_util import DEV, OUTLIERS_8BIT, REL_L2_8BIT, ULPS_KERNEL, Run, bf, check_close, check_equal, dev, dev_rows, f32
 
 pytestmark = pytest.mark.gpu
 
-REL_8BIT = 2e-2
+REL_8BIT = REL_L2_8BIT
 
 
 def _smooth(E, H, seed):
@@ -113,11 +114,22 @@ def test_int8_grouped_ffn_forward(name):
         q, s = orc.quant_weights_int8(inp[k])
         check_equal(f"{k} codes", wc.cpu().numpy(), q)
         check_equal(f"{k} scales", ws.cpu().numpy(), s)
-    check_close("G", f32(g["gus"][:A, :F]), f["G"], rel_l2=REL_8BIT)
-    check_close("U", f32(g["gus"][:A, F:]), f["U"], rel_l2=REL_8BIT)
-    check_close("h", f32(g["h"][:A]), f["Hh"], rel_l2=REL_8BIT)
-    check_close("y", f32(g["y"][:A]), f["Y"], rel_l2=REL_8BIT)
-    check_close("out", f32(g["out"]), f["out"], rel_l2=REL_8BIT)
+    # G, U, h from bit-exact int8 rows (dispatch) and weights: one kernel on the
+    # oracle's operands; y and out are chained (the device's own h)
+    check_close("G", f32(g["gus"][:A, :F]), f["G"], ulps=ULPS_KERNEL, rel_l2=REL_8BIT)
+    check_close("U", f32(g["gus"][:A, F:]), f["U"], ulps=ULPS_KERNEL, rel_l2=REL_8BIT)
+    check_close("h", f32(g["h"][:A]), f["Hh"], ulps=ULPS_KERNEL, rel_l2=REL_8BIT)
+    check_close("y", f32(g["y"][:A]), f["Y"], rel_l2=REL_8BIT, outliers=OUTLIERS_8BIT)
+    check_close("out", f32(g["out"]), f["out"], rel_l2=REL_8BIT, outliers=OUTLIERS_8BIT)
+    # the down GEMM fed the int8 codes of the oracle's h (the quantiser is bit-exact)
+    shape = Run(inp).shape
+    cap, H = shape.capacity, inp["H"]
+    recv = dev(f["route"].ep_recv_counts.astype(np.int32))
+    hq, hs = dm.quant_rows_int8(dev_rows(f["Hh"], cap), recv[-1:])
+    y2 = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+    dm.moe_ffn_down_fwd_int8(shape, hq, hs, g["wq"][2][0], g["wq"][2][1], recv, y2)
+    torch.cuda.synchronize()
+    check_close("y (oracle h)", f32(y2[:A]), f["Y"], ulps=ULPS_KERNEL, rel_l2=REL_8BIT)
 
 
 def test_int8_decode_forward_full_size():
@@ -129,8 +141,8 @@ def test_int8_decode_forward_full_size():
     g = _int8_forward(inp, S)
     f = orc.layer_fwd_int8(inp, S)
     A = f["route"].A
-    check_close("h", f32(g["h"][:A]), f["Hh"], rel_l2=REL_8BIT)
-    check_close("out", f32(g["out"]), f["out"], rel_l2=REL_8BIT)
+    check_close("h", f32(g["h"][:A]), f["Hh"], rel_l2=REL_8BIT, outliers=OUTLIERS_8BIT)
+    check_close("out", f32(g["out"]), f["out"], rel_l2=REL_8BIT, outliers=OUTLIERS_8BIT)
 
 
 def test_moe_layer_int8_api():
@@ -148,7 +160,7 @@ def test_moe_layer_int8_api():
                             copy_expert_num=1, const_expert_num=1)
     torch.cuda.synchronize()
     f = orc.layer_fwd_int8(inp, S)
-    check_close("out", f32(out), f["out"], rel_l2=REL_8BIT)
+    check_close("out", f32(out), f["out"], rel_l2=REL_8BIT, outliers=OUTLIERS_8BIT)
 
 
 def test_int8_path_with_no_routed_rows():
@@ -164,4 +176,4 @@ def test_int8_path_with_no_routed_rows():
     out = dm.moe_layer_int8(run.x, run.idx, run.w, *wq, copy_expert_num=1, zero_expert_num=1)
     torch.cuda.synchronize()
     f = orc.layer_fwd_int8(inp)
-    check_close("out", f32(out), f["out"], rel_l2=REL_8BIT)
+    check_close("out", f32(out), f["out"], rel_l2=REL_8BIT, outliers=OUTLIERS_8BIT)
