@@ -81,6 +81,7 @@ struct GemmArgs {
   // map of the routing, gK = top-K), so the dispatch permute is not needed
   const int32_t* gather;
   int gK;
+  int64_t gbytes;  // bytes of x (T * H * 2): the range of the gathered A loads
   const bf16_t* B0;
   const bf16_t* B1;
   int64_t ldb;
@@ -777,7 +778,9 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     bf16_t* sa = smem + st * BM * BK;
     bf16_t* sb = smem + S * BM * BK + st * BN * BK;
     if constexpr (!KGROUP) {
-      const auto r = rsrc(abase + k0 * 2, kRange);
+      // gathered rows: the range ends at the end of x, so a token offset from
+      // a stale or foreign row -> slot map reads zeros instead of past x
+      const auto r = rsrc(abase + k0 * 2, gathered ? g.gbytes - k0 * 2 : kRange);
 #pragma unroll
       for (int j = 0; j < LA; ++j) {
         const uint32_t vo = (tail && k0 + kcA[j] >= kend) ? kOOB : voA[j];
@@ -1471,6 +1474,7 @@ extern "C" moe_status moe_ffn_gate_up_fwd_gather(const moe_shape* s, const void*
   g.A = static_cast<const bf16_t*>(x);
   g.gather = assist + s->T * s->K;  // row -> slot
   g.gK = s->K;
+  g.gbytes = s->T * s->H * 2;
   g.lda = s->H;
   g.B0 = static_cast<const bf16_t*>(w_gate);
   g.B1 = static_cast<const bf16_t*>(w_up);

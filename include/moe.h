@@ -142,8 +142,6 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* expand_x, const void*
                            const void* w_up, const void* w_down, const int32_t* ep_recv_counts,
                            void* gate_up_save, void* h_act, void* y, void* stream);
 
-/* First grouped GEMM of moe_grouped_ffn (gate and up projections with the
- * SwiGLU product fused into its epilogue).  One kernel launch. */
 /* moe_route - the routing half of moe_dispatch alone: the same assist info,
  * expert_token_nums, ep_recv_counts and err_flag (same arguments, same checks),
  * without x and without writing expanded rows.  For callers that read the
@@ -165,6 +163,8 @@ moe_status moe_ffn_gate_up_fwd_gather(const moe_shape* s, const void* x, const i
                                       const void* w_gate, const void* w_up, const int32_t* ep_recv_counts,
                                       void* gate_up_save, void* h_act, void* stream);
 
+/* First grouped GEMM of moe_grouped_ffn (gate and up projections with the
+ * SwiGLU product fused into its epilogue).  One kernel launch. */
 moe_status moe_ffn_gate_up_fwd(const moe_shape* s, const void* expand_x, const void* w_gate,
                                const void* w_up, const int32_t* ep_recv_counts,
                                void* gate_up_save, void* h_act, void* stream);
