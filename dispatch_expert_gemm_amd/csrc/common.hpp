@@ -226,4 +226,14 @@ inline moe_status launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// moe_dispatch in parts (route.hip): its workspace size, its argument checks
+// and its launches, for entries that bring the workspace from elsewhere.
+size_t dispatch_ws_bytes(const moe_shape* s);
+moe_status dispatch_check(const moe_shape* s, const void* x, const int32_t* topk_idx, const uint8_t* x_active_mask,
+                          void* expand_x, int32_t* assist, int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                          int32_t* err_flag, void* workspace, size_t ws_bytes);
+moe_status dispatch_impl(const moe_shape* s, const void* x, const int32_t* topk_idx, const uint8_t* x_active_mask,
+                         void* expand_x, int32_t* assist, int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                         int32_t* err_flag, void* workspace, hipStream_t strm);
+
 }  // namespace moe

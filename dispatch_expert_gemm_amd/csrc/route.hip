@@ -8,28 +8,29 @@
 // per-expert counts.  With one device the all-to-all of low_latency_dispatch is
 // the permutation built here.
 //
-// Kernels (all on the caller's stream, no host synchronisation):
-//   k_route_count  one wave per chunk of 64*R slots: classify, per-chunk expert
-//                  histogram in LDS, chunk error bits
-//   k_route_scan   one block: per-expert sums over chunks (each expert's column
-//                  split across thread groups), scan over experts, exclusive
-//                  per-(chunk, expert) row offsets, outputs
-//   k_route_rank   one wave per chunk: stable rank of each routed slot among
-//                  the slots of its expert in the chunk (wave ballots), writes
-//                  slot->row and row->slot
-//   k_permute      one wave (or 2-4 for wide rows) per token: read x[t] once,
-//                  write it to its rows
+// Two kernels, on the caller's stream, no host synchronisation.  The slots are
+// cut into chunks of whole tokens (about 512 slots, more when there are many
+// tokens, so that there are at most 256 chunks and at most 32768 (chunk,
+// expert) counts):
+//   k_route_count  one workgroup per chunk: classify every slot, count the
+//                  chunk's slots per expert with wave ballots (lanes with the
+//                  same expert are found by ballots over the bits of its id;
+//                  the lowest of them adds their number), chunk error bits
+//   k_route_place  P workgroups per chunk: each sums the counts of the chunks
+//                  before its own and of all chunks per expert (16-byte loads
+//                  spread over the workgroup), scans the expert totals, gives
+//                  every routed slot of the chunk its row (stable rank among
+//                  the chunk's slots of its expert, by the same ballots) and
+//                  writes both maps; then, for dispatch, the P workgroups of
+//                  the chunk each copy 1/P of the chunk's tokens to their rows.
+//                  The first workgroup also writes the counts, the prefix sums
+//                  and the error flag.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-// Slot chunks: one wave takes 64 R slots, R >= kMinSlotsPerLane, and R grows
-// once the chunk count would pass kMaxChunks (measured on MI355X at 65536 and
-// 32768 slots: 2 slots per lane and up to 512 chunks beat 4 and 256 by 5%).
-constexpr int kMaxChunks = 512;
-constexpr int kMinSlotsPerLane = 2;
 
 struct RouteArgs {
   const int32_t* idx;
@@ -74,174 +75,233 @@ __device__ __forceinline__ uint32_t wave_or_bits(uint32_t v) {
   return r;
 }
 
+// Lanes of the wave whose slot is routed to the same expert as this lane's (a
+// wave-level multisplit: one ballot per bit of the expert id).  0 when not routed.
+__device__ __forceinline__ uint64_t same_expert(int cls, int nbits) {
+  const bool routed = cls >= 0;
+  uint64_t peers = __ballot(routed);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = routed && ((cls >> b) & 1);
+    const uint64_t bb = __ballot(bit);
+    peers &= bit ? bb : ~bb;
+  }
+  return routed ? peers : 0ull;
+}
+
+// Chunks of whole tokens: chunk c holds tokens [c tpc, (c+1) tpc), its slots
+// t K + k in 64-slot rounds.  Counts are stored per chunk in rows of Ep = E
+// rounded up to a multiple of 4 (16-byte loads).
+struct RouteGeom {
+  int64_t nslots, tpc;
+  int nchunks, rounds, Ep, P;
+};
+
 __global__ __launch_bounds__(256) void k_route_count(RouteArgs a, int32_t* __restrict__ hist,
-                                                     int32_t* __restrict__ chunk_err,
-                                                     int64_t nslots, int nchunks, int R) {
-  extern __shared__ int32_t sh[];
+                                                     int32_t* __restrict__ chunk_err, int64_t tpc, int rounds,
+                                                     int Ep, int nbits) {
+  extern __shared__ int32_t sh[];  // [4][Ep] per-wave counts
+  __shared__ uint32_t errsh;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int chunk = blockIdx.x * kWavesPerBlock + wave;
-  int32_t* h = sh + wave * a.E;
-  for (int e = lane; e < a.E; e += kWave) h[e] = 0;
+  const int64_t c = blockIdx.x;
+  for (int i = threadIdx.x; i < 4 * Ep; i += 256) sh[i] = 0;
+  if (threadIdx.x == 0) errsh = 0;
   __syncthreads();
+  const int64_t t1 = (c + 1) * tpc < a.T ? (c + 1) * tpc : a.T;
+  const int64_t s0 = c * tpc * a.K, s1 = t1 * a.K;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t* h = sh + wave * Ep;
   uint32_t err = 0;
-  if (chunk < nchunks) {
-    for (int r = 0; r < R; ++r) {
-      const int64_t s = ((int64_t)chunk * R + r) * kWave + lane;
-      if (s < nslots) {
-        const int cls = classify(a, s, err);
-        if (cls >= 0) atomicAdd(&h[cls], 1);
-        if (a.mask_ndim == 1 && (s % a.K) == 0) {
-          const int64_t t = s / a.K;
-          if (t > 0 && a.mask[t] != 0 && a.mask[t - 1] == 0) err |= MOE_FLAG_MASK_NOT_PREFIX;
+  for (int r = wave; r < rounds; r += 4) {
+    const int64_t s = s0 + (int64_t)r * kWave + lane;
+    int cls = MOE_SLOT_NONE;
+    if (s < s1) {
+      cls = classify(a, s, err);
+      if (a.mask_ndim == 1 && (s % a.K) == 0) {
+        const int64_t t = s / a.K;
+        if (t > 0 && a.mask[t] != 0 && a.mask[t - 1] == 0) err |= MOE_FLAG_MASK_NOT_PREFIX;
+      }
+    }
+    const uint64_t peers = same_expert(cls, nbits);
+    // one lane per expert present in the round adds the round's count
+    if (peers && (peers & below) == 0) h[cls] += __popcll(peers);
+  }
+  const uint32_t we = wave_or_bits(err);
+  if (lane == 0 && we) atomicOr(&errsh, we);
+  __syncthreads();
+  for (int e = threadIdx.x; e < Ep; e += 256) hist[c * Ep + e] = sh[e] + sh[Ep + e] + sh[2 * Ep + e] + sh[3 * Ep + e];
+  if (threadIdx.x == 0) chunk_err[c] = (int32_t)errsh;
+}
+
+// Inclusive scan of v over the 256 threads of a block (wave scans with lane
+// shuffles, then the wave totals).
+__device__ __forceinline__ int32_t block_scan(int32_t v, int32_t* wtot) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  if (lane == kWave - 1) wtot[wave] = v;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) v += wtot[w];
+  __syncthreads();
+  return v;
+}
+
+template <bool PERMUTE>
+__global__ __launch_bounds__(256) void k_route_place(RouteArgs a, const int32_t* __restrict__ hist,
+                                                     const int32_t* __restrict__ chunk_err, int64_t tpc, int nchunks,
+                                                     int rounds, int Ep, int nbits, int P,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ prefix,
+                                                     int32_t* __restrict__ err_flag, int32_t* __restrict__ slot2row,
+                                                     int32_t* __restrict__ row2slot, const uint4* __restrict__ x,
+                                                     int64_t Hv, uint4* __restrict__ ex) {
+  // LDS: off[4][Ep] running row offsets of each wave's rounds, cnt[4][Ep] their
+  // counts, red[2][G][Ep] partial sums (G * Ep <= 1024), rows of this
+  // workgroup's tokens [tokens of the part][K]
+  extern __shared__ int32_t sh[];
+  int32_t* off = sh;
+  int32_t* cnt = sh + 4 * Ep;
+  int32_t* red = sh + 8 * Ep;
+  int32_t* rows = sh + 8 * Ep + 2048;
+  __shared__ int32_t wtot[4];
+  __shared__ uint32_t errsh;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int64_t c = blockIdx.x / P;
+  const int p = (int)(blockIdx.x % P);
+  for (int i = tid; i < 4 * Ep; i += 256) cnt[i] = 0;
+  // counts of chunks before c (pre) and of all chunks (tot), per expert: thread
+  // tid sums four experts (one 16-byte load per chunk) over every G-th chunk
+  const int q4 = Ep / 4;                       // 16-byte columns per row
+  const int G = q4 >= 256 ? 1 : 256 / q4;      // chunk groups
+  for (int col = tid % (q4 < 256 ? q4 : 256); col < q4; col += 256) {
+    int4 pre4 = {0, 0, 0, 0}, tot4 = {0, 0, 0, 0};
+    const int g = q4 >= 256 ? 0 : tid / q4;
+    if (g < G) {
+      for (int cc = g; cc < nchunks; cc += G) {
+        const int4 v = *reinterpret_cast<const int4*>(hist + (int64_t)cc * Ep + 4 * col);
+        tot4.x += v.x; tot4.y += v.y; tot4.z += v.z; tot4.w += v.w;
+        if (cc < c) { pre4.x += v.x; pre4.y += v.y; pre4.z += v.z; pre4.w += v.w; }
+      }
+      *reinterpret_cast<int4*>(red + g * Ep + 4 * col) = pre4;
+      *reinterpret_cast<int4*>(red + 1024 + g * Ep + 4 * col) = tot4;
+    }
+  }
+  if (tid == 0) errsh = 0;
+  // the chunk's slots: wave w takes the contiguous rounds [w rw, (w+1) rw); it
+  // classifies them and counts them per expert (same ballots as the count kernel)
+  const int64_t t0 = c * tpc;
+  const int64_t t1 = (c + 1) * tpc < a.T ? (c + 1) * tpc : a.T;
+  const int64_t s0 = t0 * a.K, s1 = t1 * a.K;
+  const int rw = (rounds + 3) / 4;
+  const int r0 = wave * rw, r1 = (r0 + rw) < rounds ? r0 + rw : rounds;
+  constexpr int kKeep = 8;  // classes kept in registers between the two passes
+  int keep[kKeep];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  __syncthreads();  // cnt zeroed, red written
+  auto count_round = [&](int r) -> int {
+    const int64_t s = s0 + (int64_t)r * kWave + lane;
+    uint32_t unused = 0;
+    const int cls = s < s1 ? classify(a, s, unused) : MOE_SLOT_NONE;
+    const uint64_t peers = same_expert(cls, nbits);
+    if (peers && (peers & below) == 0) cnt[wave * Ep + cls] += __popcll(peers);
+    return cls;
+  };
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i)
+    if (r0 + i < r1) keep[i] = count_round(r0 + i);
+  for (int r = r0 + kKeep; r < r1; ++r) count_round(r);
+  // expert totals, their exclusive scan (each thread a run of consecutive
+  // experts), and each wave's first row per expert
+  const int per = (Ep + 255) / 256;
+  int32_t mine[4] = {0, 0, 0, 0};  // per <= 4 (Ep <= 1024)
+  int32_t run = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    int32_t t = 0;
+    if (e < Ep)
+      for (int g = 0; g < G; ++g) t += red[1024 + g * Ep + e];
+    mine[i] = t;
+    run += t;
+  }
+  const int32_t incl = block_scan(run, wtot);  // (its barriers also order the cnt updates)
+  int32_t ex0 = incl - run;
+  for (int i = 0; i < per; ++i) {
+    const int e = tid * per + i;
+    if (e < a.E) {
+      int32_t o = ex0;
+      for (int g = 0; g < G; ++g) o += red[g * Ep + e];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        off[w * Ep + e] = o;
+        o += cnt[w * Ep + e];
+      }
+      if (blockIdx.x == 0) {
+        counts[e] = mine[i];
+        prefix[e] = ex0 + mine[i];
+      }
+    }
+    ex0 += mine[i];
+  }
+  if (blockIdx.x == 0) {
+    uint32_t er = 0;
+    for (int cc = tid; cc < nchunks; cc += 256) er |= (uint32_t)chunk_err[cc];
+    if (er) atomicOr(&errsh, er);
+  }
+  // this workgroup's tokens for the copy
+  const int64_t nt = t1 - t0;
+  const int64_t pt0 = t0 + nt * p / P, pt1 = t0 + nt * (p + 1) / P;
+  const int64_t ps0 = pt0 * a.K, ps1 = pt1 * a.K;
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) *err_flag = (int32_t)errsh;
+  // rows: every wave ranks its rounds in slot order (stable ranks)
+  int32_t* o = off + wave * Ep;
+  auto place_round = [&](int r, int cls) {
+    const int64_t s = s0 + (int64_t)r * kWave + lane;
+    const uint64_t peers = same_expert(cls, nbits);
+    int row = cls;
+    if (peers) {
+      const int base = o[cls];
+      row = base + __popcll(peers & below);
+      if ((peers & below) == 0) o[cls] = base + __popcll(peers);
+    }
+    if (p == 0 && s < s1) {
+      slot2row[s] = row;
+      if (peers) row2slot[row] = (int32_t)s;
+    }
+    if (PERMUTE && s >= ps0 && s < ps1) rows[s - ps0] = peers ? row : -1;
+  };
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i)
+    if (r0 + i < r1) place_round(r0 + i, keep[i]);
+  for (int r = r0 + kKeep; r < r1; ++r) {
+    const int64_t s = s0 + (int64_t)r * kWave + lane;
+    uint32_t unused = 0;
+    place_round(r, s < s1 ? classify(a, s, unused) : MOE_SLOT_NONE);
+  }
+  if constexpr (PERMUTE) {
+    __syncthreads();
+    // copy: thread tid takes vectors tid, tid + 256, ... of the part's token rows
+    // (token-major), four loads in flight before their K stores
+    const int64_t nv = (pt1 - pt0) * Hv;
+    for (int64_t v0 = tid; v0 < nv; v0 += 4 * 256) {
+      uint4 val[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t v = v0 + q * 256;
+        if (v < nv) val[q] = x[(pt0 + v / Hv) * Hv + v % Hv];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t v = v0 + q * 256;
+        if (v >= nv) continue;
+        const int64_t lt = v / Hv, col = v % Hv;
+        for (int k = 0; k < a.K; ++k) {
+          const int rr = rows[lt * a.K + k];
+          if (rr >= 0) ex[(int64_t)rr * Hv + col] = val[q];
         }
       }
     }
-  }
-  __syncthreads();
-  if (chunk < nchunks) {
-    for (int e = lane; e < a.E; e += kWave) hist[(int64_t)chunk * a.E + e] = h[e];
-    const uint32_t we = wave_or_bits(err);
-    if (lane == 0) chunk_err[chunk] = (int32_t)we;
-  }
-}
-
-// One block of 1024 threads.  Thread (e, grp) with e = tid % Ep, grp = tid / Ep
-// (Ep = E rounded up to a power of two, G = 1024 / Ep groups) owns the chunks
-// [grp*per, (grp+1)*per) of expert e's column: it sums them, the group sums
-// are scanned in LDS, the expert totals are scanned over experts, and each
-// thread rewrites its chunks as exclusive row offsets.
-__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist,
-                                                     const int32_t* __restrict__ chunk_err,
-                                                     int nchunks, int E, int Ep,
-                                                     int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ prefix,
-                                                     int32_t* __restrict__ err_flag) {
-  __shared__ int32_t part[1024];  // [grp][e] partial sums
-  __shared__ int32_t tot[1024];   // expert totals, then their inclusive scan
-  __shared__ int32_t errsh;
-  const int tid = threadIdx.x;
-  const int G = 1024 / Ep;
-  const int e = tid % Ep, grp = tid / Ep;
-  const int per = (nchunks + G - 1) / G;
-  const int c0 = grp * per, c1 = (c0 + per < nchunks) ? c0 + per : nchunks;
-  if (tid == 0) errsh = 0;
-  int32_t sum = 0;
-  if (e < E) {
-    int c = c0;
-    for (; c + 8 <= c1; c += 8) {
-      int32_t v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = hist[(int64_t)(c + i) * E + e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sum += v[i];
-    }
-    for (; c < c1; ++c) sum += hist[(int64_t)c * E + e];
-  }
-  part[grp * Ep + e] = sum;
-  __syncthreads();
-  uint32_t er = 0;
-  for (int c = tid; c < nchunks; c += 1024) er |= (uint32_t)chunk_err[c];
-  if (er) atomicOr(&errsh, (int32_t)er);
-  // exclusive prefix of this thread's group within its expert, and the expert total
-  int32_t before = 0, total = 0;
-  for (int q = 0; q < G; ++q) {
-    const int32_t v = part[q * Ep + e];
-    before += q < grp ? v : 0;
-    total += v;
-  }
-  tot[tid] = tid < Ep ? total : 0;  // thread tid < Ep is (expert tid, group 0)
-  __syncthreads();
-  // inclusive scan of the expert totals (Hillis-Steele over 1024 entries)
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = tid >= off ? tot[tid - off] : 0;
-    __syncthreads();
-    tot[tid] += v;
-    __syncthreads();
-  }
-  if (e < E) {
-    if (grp == 0) {
-      counts[e] = total;
-      prefix[e] = tot[e];
-    }
-    int32_t run = tot[e] - total + before;  // exclusive base of (expert e, chunk c0)
-    int c = c0;
-    for (; c + 8 <= c1; c += 8) {
-      int32_t v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = hist[(int64_t)(c + i) * E + e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hist[(int64_t)(c + i) * E + e] = run;
-        run += v[i];
-      }
-    }
-    for (; c < c1; ++c) {
-      const int32_t v = hist[(int64_t)c * E + e];
-      hist[(int64_t)c * E + e] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  if (tid == 0) *err_flag = errsh;
-}
-
-__global__ __launch_bounds__(256) void k_route_rank(RouteArgs a, const int32_t* __restrict__ offs,
-                                                    int64_t nslots, int nchunks, int R, int nbits,
-                                                    int32_t* __restrict__ slot2row,
-                                                    int32_t* __restrict__ row2slot) {
-  extern __shared__ int32_t sh[];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int chunk = blockIdx.x * kWavesPerBlock + wave;
-  int32_t* h = sh + wave * a.E;
-  if (chunk < nchunks)
-    for (int e = lane; e < a.E; e += kWave) h[e] = offs[(int64_t)chunk * a.E + e];
-  __syncthreads();
-  if (chunk >= nchunks) return;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = 0; r < R; ++r) {
-    const int64_t s = ((int64_t)chunk * R + r) * kWave + lane;
-    uint32_t unused = 0;
-    const int cls = s < nslots ? classify(a, s, unused) : MOE_SLOT_NONE;
-    const bool routed = cls >= 0;
-    // lanes routed to the same expert: match every bit of the expert id
-    uint64_t peers = __ballot(routed);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = routed && ((cls >> b) & 1);
-      const uint64_t bb = __ballot(bit);
-      peers &= bit ? bb : ~bb;
-    }
-    int base = 0;
-    if (routed) base = h[cls];
-    if (routed) {
-      const int row = base + __popcll(peers & below);
-      slot2row[s] = row;
-      row2slot[row] = (int32_t)s;
-      if ((peers & below) == 0) h[cls] = base + __popcll(peers);
-    } else if (s < nslots) {
-      slot2row[s] = cls;
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x,
-                                                 const int32_t* __restrict__ slot2row, int64_t T,
-                                                 int K, int64_t Hv, int split, uint4* __restrict__ ex) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-  const int64_t t = gw / split;
-  const int part = (int)(gw - t * split);
-  if (t >= T) return;
-  const int my = lane < K ? slot2row[t * K + lane] : -1;
-  int rows[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) rows[k] = k < K ? __builtin_amdgcn_readlane(my, k) : -1;
-  const uint4* xr = x + t * Hv;
-  // the wave's column blocks are part, part + split, ...
-  for (int64_t v = lane + part * kWave; v < Hv; v += (int64_t)split * kWave) {
-    const uint4 val = xr[v];
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (rows[k] >= 0) ex[(int64_t)rows[k] * Hv + v] = val;
   }
 }
 
@@ -303,25 +363,25 @@ __global__ __launch_bounds__(256) void k_permute_i8(const uint4* __restrict__ x,
   if (lane == 0) dyn[row] = m > 0.f ? __fdiv_rn(m, 127.0f) : 1.0f;
 }
 
-struct RouteGeom {
-  int64_t nslots;
-  int R;
-  int nchunks;
-};
-
 RouteGeom route_geom(const moe_shape* s) {
   RouteGeom g;
   g.nslots = s->T * s->K;
-  const int64_t per = (int64_t)kWave * kMaxChunks;
-  int64_t R = (g.nslots + per - 1) / per;
-  g.R = (int)(R < kMinSlotsPerLane ? kMinSlotsPerLane : R);
-  g.nchunks = (int)((g.nslots + (int64_t)kWave * g.R - 1) / ((int64_t)kWave * g.R));
+  g.Ep = (s->num_experts + 3) / 4 * 4;
+  int64_t cmax = 32768 / g.Ep;  // at most 32768 (chunk, expert) counts
+  cmax = cmax < 4 ? 4 : (cmax > 256 ? 256 : cmax);
+  const int64_t by_slots = (512 + s->K - 1) / s->K, by_count = (s->T + cmax - 1) / cmax;
+  g.tpc = by_slots > by_count ? by_slots : by_count;
+  g.nchunks = (int)(s->T > 0 ? (s->T + g.tpc - 1) / g.tpc : 0);
+  g.rounds = (int)((g.tpc * s->K + kWave - 1) / kWave);
+  // about 1024 copying workgroups, each of at least one token
+  int64_t P = (1024 + (g.nchunks > 0 ? g.nchunks : 1) - 1) / (g.nchunks > 0 ? g.nchunks : 1);
+  g.P = (int)(P < 1 ? 1 : (P > g.tpc ? g.tpc : P));
   return g;
 }
 
 size_t route_ws_bytes(const moe_shape* s) {
   const RouteGeom g = route_geom(s);
-  const size_t b = ((size_t)g.nchunks * s->num_experts + g.nchunks + 1) * sizeof(int32_t);
+  const size_t b = ((size_t)g.nchunks * g.Ep + g.nchunks + 1) * sizeof(int32_t);
   return (b + 255) & ~(size_t)255;
 }
 
@@ -376,32 +436,37 @@ moe_status check_dispatch(const moe_shape* s, const int32_t* topk_idx,
   return MOE_OK;
 }
 
-// the routing kernels of both dispatch entries: counts, scan, rank (maps)
+// the routing kernels: counts, then rows, maps (and, given x and expand_x, the
+// copy of every token row to its rows)
 void launch_route(const moe_shape* s, const int32_t* topk_idx, const uint8_t* x_active_mask,
                   int32_t* assist, int32_t* expert_token_nums, int32_t* ep_recv_counts,
-                  int32_t* err_flag, void* workspace, hipStream_t strm) {
+                  int32_t* err_flag, void* workspace, hipStream_t strm, const void* x = nullptr,
+                  void* expand_x = nullptr) {
   const RouteGeom g = route_geom(s);
   RouteArgs a{topk_idx, x_active_mask, s->T, s->K, s->num_experts, s->zero_expert_num,
               s->copy_expert_num, s->const_expert_num, s->mask_ndim};
   int32_t* hist = static_cast<int32_t*>(workspace);
-  int32_t* cerr = hist + (size_t)g.nchunks * s->num_experts;
+  int32_t* cerr = hist + (size_t)g.nchunks * g.Ep;
   int32_t* slot2row = assist;
   int32_t* row2slot = assist + s->T * s->K;
-  const size_t lds = (size_t)kWavesPerBlock * s->num_experts * sizeof(int32_t);
-  const int blocks = (g.nchunks + kWavesPerBlock - 1) / kWavesPerBlock;
+  int nbits = 0;
+  while ((1 << nbits) < s->num_experts) ++nbits;
   if (g.nchunks > 0)
-    hipLaunchKernelGGL(k_route_count, dim3(blocks), dim3(256), lds, strm, a, hist, cerr,
-                       g.nslots, g.nchunks, g.R);
-  int Ep = 1;
-  while (Ep < s->num_experts) Ep <<= 1;
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, strm, hist, cerr, g.nchunks,
-                     s->num_experts, Ep, expert_token_nums, ep_recv_counts, err_flag);
-  if (g.nchunks > 0) {
-    int nbits = 0;
-    while ((1 << nbits) < s->num_experts) ++nbits;
-    hipLaunchKernelGGL(k_route_rank, dim3(blocks), dim3(256), lds, strm, a, hist, g.nslots,
-                       g.nchunks, g.R, nbits, slot2row, row2slot);
-  }
+    hipLaunchKernelGGL(k_route_count, dim3(g.nchunks), dim3(256), (size_t)4 * g.Ep * sizeof(int32_t), strm, a, hist,
+                       cerr, g.tpc, g.rounds, g.Ep, nbits);
+  const bool permute = x != nullptr && g.nchunks > 0;
+  const int P = permute ? g.P : 1;
+  const int64_t part_tokens = (g.tpc + P - 1) / P;
+  const size_t lds = ((size_t)8 * g.Ep + 2048 + (permute ? part_tokens * s->K : 0)) * sizeof(int32_t);
+  const dim3 grid((unsigned)(g.nchunks > 0 ? (int64_t)g.nchunks * P : 1));
+  if (permute)
+    hipLaunchKernelGGL(k_route_place<true>, grid, dim3(256), lds, strm, a, hist, cerr, g.tpc, g.nchunks, g.rounds,
+                       g.Ep, nbits, P, expert_token_nums, ep_recv_counts, err_flag, slot2row, row2slot,
+                       static_cast<const uint4*>(x), s->H / 8, static_cast<uint4*>(expand_x));
+  else
+    hipLaunchKernelGGL(k_route_place<false>, grid, dim3(256), lds, strm, a, hist, cerr, g.tpc, g.nchunks, g.rounds,
+                       g.Ep, nbits, P, expert_token_nums, ep_recv_counts, err_flag, slot2row, row2slot,
+                       static_cast<const uint4*>(nullptr), s->H / 8, static_cast<uint4*>(nullptr));
 }
 }  // namespace
 
@@ -418,11 +483,23 @@ extern "C" moe_status moe_route(const moe_shape* s, const int32_t* topk_idx, con
   return launch_status();
 }
 
-extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
-                                   const uint8_t* x_active_mask, void* expand_x,
-                                   int32_t* assist, int32_t* expert_token_nums,
-                                   int32_t* ep_recv_counts, int32_t* err_flag, void* workspace,
-                                   size_t ws_bytes, void* stream) {
+namespace moe {
+// moe_dispatch after its argument checks: routing, then the permute (declared in
+// common.hpp for the other dispatch entries)
+moe_status dispatch_impl(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                         const uint8_t* x_active_mask, void* expand_x, int32_t* assist,
+                         int32_t* expert_token_nums, int32_t* ep_recv_counts, int32_t* err_flag,
+                         void* workspace, hipStream_t strm) {
+  launch_route(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag, workspace, strm, x,
+               expand_x);
+  return launch_status();
+}
+
+size_t dispatch_ws_bytes(const moe_shape* s) { return route_ws_bytes(s); }
+
+moe_status dispatch_check(const moe_shape* s, const void* x, const int32_t* topk_idx, const uint8_t* x_active_mask,
+                          void* expand_x, int32_t* assist, int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                          int32_t* err_flag, void* workspace, size_t ws_bytes) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   st = check_dispatch(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
@@ -430,17 +507,20 @@ extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int3
   if (st != MOE_OK) return st;
   MOE_NEED(x, s->T * s->H);
   MOE_NEED(expand_x, s->capacity * s->H);
-  hipStream_t strm = as_stream(stream);
-  launch_route(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag, workspace, strm);
-  const int32_t* slot2row = assist;
-  if (s->T > 0) {
-    const int split = token_split(s->H / 8, s->K);
-    const int64_t pb = (s->T * split + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(k_permute, dim3((unsigned)pb), dim3(256), 0, strm,
-                       static_cast<const uint4*>(x), slot2row, s->T, s->K, s->H / 8, split,
-                       static_cast<uint4*>(expand_x));
-  }
-  return launch_status();
+  return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                                   const uint8_t* x_active_mask, void* expand_x,
+                                   int32_t* assist, int32_t* expert_token_nums,
+                                   int32_t* ep_recv_counts, int32_t* err_flag, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  const moe_status st = dispatch_check(s, x, topk_idx, x_active_mask, expand_x, assist, expert_token_nums,
+                                       ep_recv_counts, err_flag, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  return dispatch_impl(s, x, topk_idx, x_active_mask, expand_x, assist, expert_token_nums, ep_recv_counts,
+                       err_flag, workspace, as_stream(stream));
 }
 
 extern "C" moe_status moe_dispatch_int8(const moe_shape* s, const void* x, const int32_t* topk_idx,
