@@ -39,7 +39,7 @@ ENTRY_POINTS = (
     "moe_ffn_gate_up_bwd_weight_fp8", "moe_ffn_down_bwd_data_fp8_quant", "moe_ffn_gate_up_fwd_fp8_quant",
     "moe_dispatch_int8", "moe_quant_rows_int8", "moe_ffn_gate_up_fwd_int8", "moe_ffn_down_fwd_int8",
     "moe_quant_rows_mx", "moe_quantize_weights_mx", "moe_ffn_gate_up_fwd_mx", "moe_ffn_down_fwd_mx",
-    "moe_ffn_down_bwd_data_mx", "moe_ffn_gate_up_bwd_data_mx",
+    "moe_ffn_down_bwd_data_mx", "moe_ffn_gate_up_bwd_data_mx", "moe_dispatch_noalloc",
 )
 
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.moe_assist_info_size.argtypes = [S, I64P]
         L.moe_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_dispatch_noalloc.argtypes = [S] + [P] * 9
         L.moe_grouped_ffn.argtypes = [S, P, P, P, P, P, P, P, P, P]
         L.moe_ffn_gate_up_fwd.argtypes = [S, P, P, P, P, P, P, P]
         L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -210,6 +211,20 @@ def moe_dispatch(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_co
         _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
         _ptr(err_flag, I32, "err_flag"), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_dispatch_noalloc(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_combine,
+                         expert_token_nums, ep_recv_counts, err_flag, stream=None):
+    """moe_dispatch without a workspace argument: the library's own fixed device
+    scratch holds the routing histograms, so the call allocates nothing.  Calls
+    that overlap on one GPU share that scratch and race."""
+    _check_sizes(shape, locals())
+    _check(lib().moe_dispatch_noalloc(
+        ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(x_active_mask, U8, "x_active_mask"), _ptr(expand_x, BF16, "expand_x"),
+        _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
+        _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(err_flag, I32, "err_flag"), _stream(stream)))
 
 
 def moe_route(shape, topk_idx, x_active_mask, assist_info_for_combine, expert_token_nums, ep_recv_counts,

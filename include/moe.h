@@ -142,6 +142,23 @@ moe_status moe_grouped_ffn(const moe_shape* s, const void* expand_x, const void*
                            const void* w_up, const void* w_down, const int32_t* ep_recv_counts,
                            void* gate_up_save, void* h_act, void* y, void* stream);
 
+/* moe_dispatch_noalloc - moe_dispatch for callers that cannot allocate device
+ * memory: code under stream capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, outputs and checks as moe_dispatch, without the
+ * workspace: the routing scratch is a fixed 256 KiB device array inside the
+ * library (one per GPU, held until the process ends; its address is looked up
+ * on the first call on each device).  The call allocates nothing.
+ *  MOE_ERR_WORKSPACE when the shape's routing scratch (moe_workspace_size)
+ *  exceeds 256 KiB; the routing's chunking keeps it at or below 129 KiB for
+ *  every shape check_shape accepts, so this is a guard only.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (different streams, threads) race; calls in one stream order are
+ * safe, and nothing needs clearing between calls. */
+moe_status moe_dispatch_noalloc(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                                const uint8_t* x_active_mask, void* expand_x, int32_t* assist_info_for_combine,
+                                int32_t* expert_token_nums, int32_t* ep_recv_counts, int32_t* err_flag,
+                                void* stream);
+
 /* moe_route - the routing half of moe_dispatch alone: the same assist info,
  * expert_token_nums, ep_recv_counts and err_flag (same arguments, same checks),
  * without x and without writing expanded rows.  For callers that read the

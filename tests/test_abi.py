@@ -280,3 +280,25 @@ def test_wrappers_reject_short_buffers():
     with pytest.raises(dm.MoeError, match="scales holds"):
         dm.moe_quant_rows_fp8(bf(8, 256), torch.zeros(8 * 256, dtype=torch.uint8),
                               torch.zeros(15, dtype=torch.float32))
+
+
+def test_noalloc_dispatch_checks_before_any_device_call(L):
+    """moe_dispatch_noalloc validates like moe_dispatch before touching the GPU, and its
+    fixed 256 KiB routing scratch holds the workspace of every shape the library accepts
+    (at most 256 chunks and 32768 (chunk, expert) counts)."""
+    Nn, sp = None, ctypes.byref(S())
+    assert L.moe_dispatch_noalloc(ctypes.byref(S(K=0)), P(), P(), Nn, P(), P(), P(), P(), P(), Nn) == BAD_SHAPE
+    assert L.moe_dispatch_noalloc(sp, Nn, P(), Nn, P(), P(), P(), P(), P(), Nn) == NULL_ARG
+    assert L.moe_dispatch_noalloc(sp, P(), P(), Nn, P(), P(), P(), P(), Nn, Nn) == NULL_ARG
+    sm = S(mask_ndim=2)
+    assert L.moe_dispatch_noalloc(ctypes.byref(sm), P(), P(), Nn, P(), P(), P(), P(), P(), Nn) == NULL_ARG
+    worst = 0
+    for E in (1, 3, 7, 64, 255, 256, 1000, 1024):
+        for K in (1, 2, 8, 16):
+            if K > E:
+                continue
+            for T in (0, 1, 100, 4096, 65536, 1 << 20, 1 << 24):
+                st, n = ws(dm.make_shape(T, 64, K, E))
+                assert st == OK
+                worst = max(worst, n)
+    assert worst <= 256 << 10, worst
