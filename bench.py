@@ -50,7 +50,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 # page1 is the default (the benchmark line); the others are extra measurements
 WORKLOADS = {
-    "page1": dict(T=8192, H=1536, F=480, E=64, K=8),
+    # the dispatch permute folded into the two GEMMs that read the expanded rows
+    # (moe_route, then x read through the row -> slot map by the gate/up forward
+    # and the gate/up weight gradient): no expand_x is written
+    "page1": dict(T=8192, H=1536, F=480, E=64, K=8, gather=True),
+    # the same layer with the permute as a kernel of its own (moe_dispatch)
+    "page1_permute": dict(T=8192, H=1536, F=480, E=64, K=8),
     "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
     # the same layer with the weight gradients in fp8 too (per-128-token operands)
@@ -174,6 +179,52 @@ def cpu_baseline(cfg, seconds=10.0, T_sample=1024):
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{runs} oracle {what} runs (parity mode, numpy) of a {T_sample}-token slice of the "
                       f"same workload (H={cfg['H']} F={cfg['F']} E={cfg['E']} K={cfg['K']}), {el:.1f} s"}
+
+
+def cpu_baseline_8bit(cfg, seconds=10.0, T_sample=512, F_sample=1024):
+    """The CPU oracle of the fp8 / MX layer (parity mode) on a bounded sample of the
+    same workload: T_sample tokens over all E experts at the full H, with the first
+    F_sample intermediate columns of every expert (a smaller SwiGLU FFN of the same
+    kind).  The weights are quantised once before the timing, as the step takes
+    them quantised (their quantisation is timed apart on the GPU too)."""
+    import moe_workloads as wl
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    mx, fp8w = cfg.get("mx", False), cfg.get("fp8_wgrad", False)
+    H, E, K = cfg["H"], cfg["E"], cfg["K"]
+    F = min(F_sample, cfg["F"])
+    inp = wl.layer_inputs(T_sample, H, F, E, K, seed=0)
+    quant = orc.quant_weights_mx if mx else orc.quant_weights_fp8
+    wq = tuple(quant(inp[k]) for k in ("w_gate", "w_up", "w_down"))
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        r = orc.route(inp["topk_idx"], E)
+        X = orc.dispatch(inp["x"], r)
+        fwd = orc.ffn_fwd_mx if mx else orc.ffn_fwd_fp8
+        G, U, Hh, Y = fwd(X, r.ep_recv_counts, *wq)
+        Yc = orc.qdq_rows_int8(Y)
+        orc.combine(Yc, r, inp["topk_weights"], None, inp["x"])
+        dY, _ = orc.combine_bwd(inp["grad_out"], Yc, r, inp["topk_weights"], inp["x"])
+        if mx:
+            _, dX, _, _, _ = orc.ffn_bwd_mx(dY, X, G, U, Hh, r.ep_recv_counts, *wq)
+        else:
+            _, dX, _, _, _ = orc.ffn_bwd_fp8(dY, X, G, U, Hh, r.ep_recv_counts, *wq,
+                                             wgrad="fp8" if fp8w else "bf16")
+        orc.dispatch_bwd(dX, r, inp["topk_weights"], inp["grad_out"])
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 50:
+            break
+    flops = 18.0 * r.A * H * F * runs
+    kind = "microscaled fp8" if mx else ("fp8 incl. weight gradients" if fp8w else "fp8")
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{runs} oracle {kind} fwd+bwd runs (parity mode, numpy, weights quantised once) of "
+                      f"{T_sample} tokens over all {E} experts with the first {F} of F={cfg['F']} intermediate "
+                      f"columns (H={H}, K={K}), {el:.1f} s"}
 
 
 def cpu_baseline_combine(cfg, seconds=10.0, T_sample=512):
@@ -318,8 +369,11 @@ def build_step(name, T_override=None):
         st.extra_calls.append(("moe_quant_rows_int8 (3 weight tensors)",
                                lambda: [dm.quant_rows_int8(t) for t in (wg, wu, wd)]))
     elif cfg.get("gather"):
-        # routing only: the gate/up GEMM reads the rows from x itself
+        # routing only: the gate/up GEMMs read the rows from x themselves; the
+        # permute as a kernel of its own (moe_dispatch) is timed apart
         C.append(("moe_route", lambda: dm.moe_route(shape, idx, None, assist, cnt, recv, err, ws)))
+        st.extra_calls.append(("moe_dispatch (route + permute, not in the step)",
+                               lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
     else:
         C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
     if int8:
@@ -459,6 +513,9 @@ def build_step(name, T_override=None):
     if fp8w:
         C.append(("moe_ffn_gate_up_bwd_weight_fp8", lambda: dm.moe_ffn_gate_up_bwd_weight_fp8(
             shape, *cq["dGU"], *cq["x"], recv, gwg, gwu)))
+    elif cfg.get("gather"):
+        C.append(("moe_ffn_gate_up_bwd_weight_gather", lambda: dm.moe_ffn_gate_up_bwd_weight_gather(
+            shape, ggu, x, assist, recv, gwg, gwu)))
     else:
         C.append(("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
                                                                                       gwu)))
@@ -534,6 +591,8 @@ def account(st, A):
         nb[n] = bytes_moved(n, T, H, F, K, A, E)
     if st.cfg.get("gather"):
         fl["moe_ffn_gate_up_fwd_gather"] = fl.pop("moe_ffn_gate_up_fwd")
+        if "moe_ffn_gate_up_bwd_weight" in fl:
+            fl["moe_ffn_gate_up_bwd_weight_gather"] = fl.pop("moe_ffn_gate_up_bwd_weight")
         nb["moe_route"] = nb.pop("moe_dispatch") - T * H * 2 - A * H * 2   # no rows moved
     if int8:
         # int8 rows and one fp32 scale per row written, the smooth scales read once
@@ -556,6 +615,74 @@ def account(st, A):
     return fl, nb
 
 
+def time_calls(calls, steps):
+    """Mean wall time (ms) of running `calls` in order, from HIP events on torch's
+    current stream, after one untimed pass."""
+    import torch
+    for _, fn in calls:
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        for _, fn in calls:
+            fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def hbm_ceiling(nbytes=1 << 30, reps=5):
+    """GB/s of the library's reference streaming kernel (moe_hbm_stream): a copy of
+    nbytes (2 * nbytes moved), a read and a write of nbytes, median of reps launches
+    each, timed with HIP events on torch's current stream."""
+    import torch
+    import dispatch_expert_gemm_amd as dm
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(dm.STREAM_SINK_BYTES, dtype=torch.uint8, device=dev)
+    out = {}
+    for mode, name, moved in ((0, "copy", 2 * nbytes), (1, "read", nbytes), (2, "write", nbytes)):
+        times = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dm.moe_hbm_stream(mode, src, dst, nbytes, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        out[f"{name}_GB/s"] = round(moved / (float(np.median(times[1:])) * 1e-3) / 1e9, 1)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    out["kernel"] = f"moe_hbm_stream, {nbytes >> 20} MiB, per-workgroup ranges of 16-byte accesses"
+    return out
+
+
+def token_sweep(workload, tokens, steps):
+    """fwd and fwd+bwd ms and TFLOP/s of the workload at other token counts (the
+    columns of the Triton-distributed benchmark page's summary table)."""
+    import torch
+    rows = []
+    for T in tokens:
+        st = build_step(workload, T)
+        for _ in range(2):
+            for _, fn in st.calls:
+                fn()
+        torch.cuda.synchronize()
+        A = int(st.recv[-1].item())
+        nf = [n for n, _ in st.calls].index("moe_combine") + 1
+        fb = time_calls(st.calls, steps)
+        fw = time_calls(st.calls[:nf], steps)
+        H, F = st.config["H"], st.config["F"]
+        rows.append({"T": T, "routed_rows": A, "fwd_ms": round(fw, 4), "fwd_bwd_ms": round(fb, 4),
+                     "fwd_TFLOP/s": round(6 * A * H * F / (fw * 1e-3) / 1e12, 1),
+                     "fwd_bwd_TFLOP/s": round(18 * A * H * F / (fb * 1e-3) / 1e12, 1)})
+        del st
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -567,6 +694,9 @@ def main():
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the cache-flushed re-timing of the bandwidth-bound kernels")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the page-1 rows at 1024, 2048 and 4096 tokens")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-kernel HBM ceiling")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB three times "
                          "(the reference kernel for scaling HBM counters)")
@@ -625,6 +755,12 @@ def main():
         torch.cuda.synchronize()
         extra[name] = {"ms": round(e0.elapsed_time(e1) / 10, 4)}
 
+    # the forward alone: the step's calls up to and including combine, timed the same way
+    fwd_ms = None
+    if not st.cfg.get("combine_only") and not st.cfg.get("forward_only"):
+        nf = [n for n, _ in calls].index("moe_combine") + 1
+        fwd_ms = time_calls(calls[:nf], args.steps)
+
     fl, nb = account(st, A)
     combine_only = st.cfg.get("combine_only", False)
     kernels = {}
@@ -649,8 +785,14 @@ def main():
     isolated = {}
     if not args.no_isolated:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
-        for name, fn in calls:
-            if nb.get(name) is None:
+        # plus the dispatch permute of a step that folds it into the GEMMs
+        aside = [(n, fn) for n, fn in st.extra_calls if n.startswith("moe_dispatch (")]
+        nbi = dict(nb)
+        for n, _ in aside:
+            Ti, Hi, Fi, Ki, Ei = st.shape_info
+            nbi[n] = bytes_moved("moe_dispatch", Ti, Hi, Fi, Ki, A, Ei)
+        for name, fn in list(calls) + aside:
+            if nbi.get(name) is None:
                 continue
             times = []
             for _ in range(5):
@@ -662,8 +804,8 @@ def main():
                 torch.cuda.synchronize()
                 times.append(e0.elapsed_time(e1))
             ms = float(np.median(times))
-            isolated[name] = {"ms": round(ms, 4), "GB/s": round(nb[name] / (ms * 1e-3) / 1e9, 1),
-                              "frac_hbm": round(nb[name] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            isolated[name] = {"ms": round(ms, 4), "GB/s": round(nbi[name] / (ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(nbi[name] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del flush
     # layer roofline: every GEMM at its MFMA peak (or, at decode batch sizes, at the
     # HBM rate its expert weights allow, whichever is slower) and every other
@@ -675,7 +817,8 @@ def main():
                   + sum(b / (PEAK_HBM_GBS * 1e9) for b in nb.values() if b is not None)) * 1e3
     T, H, F, E, K = (st.config[k] for k in ("T", "H", "F", "E", "K"))
     descr = {
-        "page1": "Triton-distributed benchmark shape",
+        "page1": "Triton-distributed benchmark shape, dispatch permute folded into the gate/up GEMMs' row loads",
+        "page1_permute": "Triton-distributed benchmark shape, dispatch permute as a kernel of its own",
         "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
         "mixtral_mx": "Mixtral-8x7B-style layer, microscaled fp8 e4m3 GEMMs (E8M0 per 32, block-scaled MFMA), "
@@ -746,6 +889,15 @@ def main():
         })
     res["layer_roofline_frac"] = round(t_ideal_ms / ms_per_step, 4)
     res["step_ms_events"] = step_stats
+    if fwd_ms is not None:
+        res["fwd_ms"] = round(fwd_ms, 4)
+    if not args.no_ceiling:
+        log("[bench] HBM ceiling of the streaming kernel")
+        ceil = hbm_ceiling()
+        res["hbm_ceiling"] = ceil
+        for rec in list(kernels.values()) + list(isolated.values()):
+            if "GB/s" in rec:
+                rec["frac_copy_ceiling"] = round(rec["GB/s"] / ceil["copy_GB/s"], 4)
     res["kernels"] = kernels
     if isolated:
         res["kernels_hbm_isolated"] = isolated
@@ -753,6 +905,9 @@ def main():
         res["outside_step"] = extra
     if args.workload == "page1":
         res["context"] = {"page1_fwd_bwd_ms_4_nvidia_gpus_T8192": 5.488}
+        if not args.no_sweep and not args.tokens:
+            log("[bench] page-1 rows at 1024, 2048, 4096 tokens")
+            res["token_rows"] = token_sweep("page1", (1024, 2048, 4096), max(args.steps // 2, 5))
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
@@ -766,8 +921,8 @@ def main():
         log("[bench] CPU oracle baseline (combine)")
         res["cpu_baseline"] = cpu_baseline_combine(st.cfg, args.cpu_seconds)
     elif st.cfg.get("fp8"):
-        # the oracle re-quantises all expert weights blockwise per run (minutes at this size)
-        res["cpu_baseline"] = None
+        log("[bench] CPU oracle baseline (8-bit layer, F sample)")
+        res["cpu_baseline"] = cpu_baseline_8bit(st.cfg, args.cpu_seconds)
     else:
         log("[bench] CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(st.cfg, args.cpu_seconds)

@@ -40,6 +40,9 @@ ENTRY_POINTS = (
     "moe_dispatch_int8", "moe_quant_rows_int8", "moe_ffn_gate_up_fwd_int8", "moe_ffn_down_fwd_int8",
     "moe_quant_rows_mx", "moe_quantize_weights_mx", "moe_ffn_gate_up_fwd_mx", "moe_ffn_down_fwd_mx",
     "moe_ffn_down_bwd_data_mx", "moe_ffn_gate_up_bwd_data_mx", "moe_dispatch_noalloc",
+    "moe_hbm_stream",
+    "moe_ffn_gate_up_bwd_weight_gather", "moe_dispatch_fp8", "moe_combine_bwd_fp8",
+    "moe_ffn_fp8_workspace_size", "moe_grouped_ffn_fp8", "moe_grouped_ffn_bwd_fp8",
 )
 
 
@@ -59,6 +62,11 @@ def make_shape(T, H, K, num_experts, F=0, capacity=None, zero_expert_num=0, copy
         capacity = T * min(num_experts, K)
     return MoeShape(T, H, F, capacity, K, num_experts, zero_expert_num, copy_expert_num,
                     const_expert_num, mask_ndim, 0, comm_quant_mode)
+
+
+class MoeFp8Weight(ctypes.Structure):
+    """Mirror of struct moe_fp8_weight (device pointers)."""
+    _fields_ = [("codes", ctypes.c_void_p), ("codes_t", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -82,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_dispatch_noalloc.argtypes = [S] + [P] * 9
+        L.moe_dispatch_fp8.argtypes = [S] + [P] * 11 + [ctypes.c_size_t, P]
+        L.moe_hbm_stream.argtypes = [ctypes.c_int32, P, P, ctypes.c_int64, P, P]
         L.moe_grouped_ffn.argtypes = [S, P, P, P, P, P, P, P, P, P]
         L.moe_ffn_gate_up_fwd.argtypes = [S, P, P, P, P, P, P, P]
         L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -89,11 +99,17 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_down_fwd.argtypes = [S, P, P, P, P, P]
         L.moe_combine.argtypes = [S] + [P] * 13
         L.moe_combine_bwd.argtypes = [S] + [P] * 14
+        L.moe_combine_bwd_fp8.argtypes = [S] + [P] * 16
+        W8 = ctypes.POINTER(MoeFp8Weight)
+        L.moe_ffn_fp8_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_grouped_ffn_fp8.argtypes = [S, P, P, W8, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_grouped_ffn_bwd_fp8.argtypes = [S, P, P, P, P, P, P, W8, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_grouped_ffn_bwd.argtypes = [S] + [P] * 14
         L.moe_ffn_down_bwd_data.argtypes = [S, P, P, P, P, P, P]
         L.moe_ffn_down_bwd_weight.argtypes = [S, P, P, P, P, P]
         L.moe_ffn_gate_up_bwd_data.argtypes = [S, P, P, P, P, P, P]
         L.moe_ffn_gate_up_bwd_weight.argtypes = [S, P, P, P, P, P, P]
+        L.moe_ffn_gate_up_bwd_weight_gather.argtypes = [S] + [P] * 7
         L.moe_dispatch_bwd.argtypes = [S] + [P] * 10
         I64 = ctypes.c_int64
         L.moe_quant_rows_fp8.argtypes = [I64, I64, P, P, P, P, P]
@@ -213,6 +229,21 @@ def moe_dispatch(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_co
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def moe_dispatch_fp8(shape, x, topk_idx, x_active_mask, expand_x, expand_xq, dynamic_scales,
+                     assist_info_for_combine, expert_token_nums, ep_recv_counts, err_flag, workspace, stream=None):
+    _check_sizes(shape, locals())
+    _need(expand_xq, shape.capacity * shape.H, "expand_xq")
+    _need(dynamic_scales, shape.capacity * (shape.H // 128), "dynamic_scales")
+    _check(lib().moe_dispatch_fp8(
+        ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(x_active_mask, U8, "x_active_mask"), _ptr(expand_x, BF16, "expand_x"),
+        _ptr(expand_xq, U8T, "expand_xq"), _ptr(dynamic_scales, F32, "dynamic_scales"),
+        _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
+        _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(err_flag, I32, "err_flag"), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def moe_dispatch_noalloc(shape, x, topk_idx, x_active_mask, expand_x, assist_info_for_combine,
                          expert_token_nums, ep_recv_counts, err_flag, stream=None):
     """moe_dispatch without a workspace argument: the library's own fixed device
@@ -225,6 +256,19 @@ def moe_dispatch_noalloc(shape, x, topk_idx, x_active_mask, expand_x, assist_inf
         _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
         _ptr(expert_token_nums, I32, "expert_token_nums"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
         _ptr(err_flag, I32, "err_flag"), _stream(stream)))
+
+
+STREAM_SINK_BYTES = 4096 * 256 * 16
+
+
+def moe_hbm_stream(mode, src, dst, nbytes, sink=None, stream=None):
+    """The reference streaming kernel: mode 0 copies nbytes from src to dst, 1 reads
+    src (sink: STREAM_SINK_BYTES of device memory), 2 writes dst."""
+    for t, name in ((src, "src"), (dst, "dst"), (sink, "sink")):
+        if t is not None and t.numel() * t.element_size() < (STREAM_SINK_BYTES if name == "sink" else nbytes):
+            raise MoeError(f"{name} is smaller than the bytes it must hold")
+    _check(lib().moe_hbm_stream(int(mode), _ptr(src, None, "src"), _ptr(dst, None, "dst"), int(nbytes),
+                                _ptr(sink, None, "sink"), _stream(stream)))
 
 
 def moe_route(shape, topk_idx, x_active_mask, assist_info_for_combine, expert_token_nums, ep_recv_counts,
@@ -299,6 +343,75 @@ def moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_
         _ptr(grad_topk_weights, F32, "grad_topk_weights"), _stream(stream)))
 
 
+def moe_combine_bwd_fp8(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_combine, ep_send_counts,
+                        x_active_mask, ori_x, const_alpha_1, const_alpha_2, const_v, grad_y, grad_yq, grad_y_scales,
+                        grad_topk_weights, stream=None):
+    _check_sizes(shape, locals())
+    _need(grad_yq, shape.capacity * shape.H, "grad_yq")
+    _need(grad_y_scales, shape.capacity * (shape.H // 128), "grad_y_scales")
+    _check(lib().moe_combine_bwd_fp8(
+        ctypes.byref(shape), _ptr(grad_out, BF16, "grad_out"), _ptr(y, BF16, "y"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(topk_weights, F32, "topk_weights"), _ptr(assist_info_for_combine, I32, "assist_info_for_combine"),
+        _ptr(ep_send_counts, I32, "ep_send_counts"), _ptr(x_active_mask, U8, "x_active_mask"),
+        _ptr(ori_x, BF16, "ori_x"), _ptr(const_alpha_1, BF16, "const_alpha_1"),
+        _ptr(const_alpha_2, BF16, "const_alpha_2"), _ptr(const_v, BF16, "const_v"), _ptr(grad_y, BF16, "grad_y"),
+        _ptr(grad_yq, U8T, "grad_yq"), _ptr(grad_y_scales, F32, "grad_y_scales"),
+        _ptr(grad_topk_weights, F32, "grad_topk_weights"), _stream(stream)))
+
+
+def moe_ffn_fp8_workspace_size(shape: MoeShape) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_ffn_fp8_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def _fp8_weights(wq):
+    """Three Fp8Weights (gate, up, down) -> a moe_fp8_weight[3] array (kept alive by
+    the caller's tensors)."""
+    for q in wq:
+        for t, dt in ((q.codes, U8T), (q.codes_t, U8T), (q.scales, F32T)):
+            _ptr(t, dt, "fp8 weights")
+    return (MoeFp8Weight * 3)(*[MoeFp8Weight(q.codes.data_ptr(), q.codes_t.data_ptr(), q.scales.data_ptr())
+                                for q in wq])
+
+
+def moe_grouped_ffn_fp8(shape, expand_xq, x_scales, wq, ep_recv_counts, gate_up_save, h_act, y, workspace,
+                        stream=None):
+    """wq: (gate, up, down) Fp8Weights of moe_quantize_weights_fp8."""
+    _check_sizes(shape, locals())
+    _need(expand_xq, shape.capacity * shape.H, "expand_xq")
+    _need(x_scales, shape.capacity * (shape.H // 128), "x_scales")
+    for q, (n, k) in zip(wq, ((shape.F, shape.H), (shape.F, shape.H), (shape.H, shape.F))):
+        _need(q.codes, shape.num_experts * n * k, "weight codes")
+        _need(q.scales, shape.num_experts * (n // 128) * (k // 128), "weight scales")
+    w = _fp8_weights(wq)
+    _check(lib().moe_grouped_ffn_fp8(
+        ctypes.byref(shape), _ptr(expand_xq, U8T, "expand_xq"), _ptr(x_scales, F32, "x_scales"), w,
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(gate_up_save, BF16, "gate_up_save"),
+        _ptr(h_act, BF16, "h_act"), _ptr(y, BF16, "y"), _ptr(workspace, None, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_grouped_ffn_bwd_fp8(shape, grad_y, grad_yq, grad_y_scales, expand_x, gate_up_save, h_act, wq,
+                            ep_recv_counts, grad_gate_up, grad_expand_x, grad_w_gate, grad_w_up, grad_w_down,
+                            workspace, stream=None):
+    _check_sizes(shape, locals())
+    _need(grad_yq, shape.capacity * shape.H, "grad_yq")
+    _need(grad_y_scales, shape.capacity * (shape.H // 128), "grad_y_scales")
+    for q, (n, k) in zip(wq, ((shape.F, shape.H), (shape.F, shape.H), (shape.H, shape.F))):
+        _need(q.codes_t, shape.num_experts * n * k, "weight codes")
+        _need(q.scales, shape.num_experts * (n // 128) * (k // 128), "weight scales")
+    w = _fp8_weights(wq)
+    _check(lib().moe_grouped_ffn_bwd_fp8(
+        ctypes.byref(shape), _ptr(grad_y, BF16, "grad_y"), _ptr(grad_yq, U8T, "grad_yq"),
+        _ptr(grad_y_scales, F32, "grad_y_scales"), _ptr(expand_x, BF16, "expand_x"),
+        _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(h_act, BF16, "h_act"), w,
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_gate_up, BF16, "grad_gate_up"),
+        _ptr(grad_expand_x, BF16, "grad_expand_x"), _ptr(grad_w_gate, F32, "grad_w_gate"),
+        _ptr(grad_w_up, F32, "grad_w_up"), _ptr(grad_w_down, F32, "grad_w_down"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 def moe_grouped_ffn_bwd(shape, grad_y, expand_x, gate_up_save, h_act, w_gate, w_up, w_down,
                         ep_recv_counts, grad_gate_up, grad_expand_x, grad_w_gate, grad_w_up,
                         grad_w_down, stream=None):
@@ -345,6 +458,15 @@ def moe_ffn_gate_up_bwd_weight(shape, grad_gate_up, expand_x, ep_recv_counts, gr
         ctypes.byref(shape), _ptr(grad_gate_up, BF16, "grad_gate_up"), _ptr(expand_x, BF16, "expand_x"),
         _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_w_gate, F32, "grad_w_gate"),
         _ptr(grad_w_up, F32, "grad_w_up"), _stream(stream)))
+
+
+def moe_ffn_gate_up_bwd_weight_gather(shape, grad_gate_up, x, assist_info_for_combine, ep_recv_counts, grad_w_gate,
+                                      grad_w_up, stream=None):
+    _check_sizes(shape, locals())
+    _check(lib().moe_ffn_gate_up_bwd_weight_gather(
+        ctypes.byref(shape), _ptr(grad_gate_up, BF16, "grad_gate_up"), _ptr(x, BF16, "x"),
+        _ptr(assist_info_for_combine, I32, "assist_info_for_combine"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(grad_w_gate, F32, "grad_w_gate"), _ptr(grad_w_up, F32, "grad_w_up"), _stream(stream)))
 
 
 def moe_dispatch_bwd(shape, grad_expand_x, assist_info_for_combine, topk_idx, topk_weights,
@@ -733,6 +855,48 @@ def dispatch(shape, x, topk_idx, x_active_mask=None, workspace=None, stream=None
     return d
 
 
+def dispatch_fp8(shape, x, topk_idx, x_active_mask=None, workspace=None, bf16_rows=True, stream=None):
+    """Allocate the outputs with torch and run moe_dispatch_fp8: (DispatchOut with the
+    bf16 rows in expand_x (None without bf16_rows), e4m3 rows (capacity, H),
+    scales (H/128, capacity))."""
+    dev = x.device
+    cap, H = shape.capacity, shape.H
+    d = DispatchOut(
+        expand_x=torch.empty((cap, H), dtype=BF16, device=dev) if bf16_rows else None,
+        assist_info_for_combine=torch.empty(moe_assist_info_size(shape), dtype=I32, device=dev),
+        expert_token_nums=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        ep_recv_counts=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        err_flag=torch.empty(1, dtype=I32, device=dev))
+    xq = torch.empty((cap, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((H // 128, cap), dtype=F32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    mask = x_active_mask.view(torch.uint8) if x_active_mask is not None and x_active_mask.dtype == torch.bool \
+        else x_active_mask
+    moe_dispatch_fp8(shape, x, topk_idx, mask, d.expand_x, xq, xs, d.assist_info_for_combine, d.expert_token_nums,
+                     d.ep_recv_counts, d.err_flag, workspace, stream)
+    return d, xq, xs
+
+
+def route(shape, topk_idx, x_active_mask=None, workspace=None, stream=None) -> DispatchOut:
+    """Allocate the routing outputs with torch and run moe_route (no expanded rows:
+    expand_x is None; the gathered GEMM entries read x through the assist info)."""
+    dev = topk_idx.device
+    d = DispatchOut(
+        expand_x=None,
+        assist_info_for_combine=torch.empty(moe_assist_info_size(shape), dtype=I32, device=dev),
+        expert_token_nums=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        ep_recv_counts=torch.empty(shape.num_experts, dtype=I32, device=dev),
+        err_flag=torch.empty(1, dtype=I32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_size(shape), dtype=torch.uint8, device=dev)
+    mask = x_active_mask.view(torch.uint8) if x_active_mask is not None and x_active_mask.dtype == torch.bool \
+        else x_active_mask
+    moe_route(shape, topk_idx, mask, d.assist_info_for_combine, d.expert_token_nums, d.ep_recv_counts, d.err_flag,
+              workspace, stream)
+    return d
+
+
 def dispatch_int8(shape, x, topk_idx, x_active_mask=None, smooth_scales=None, workspace=None, stream=None):
     """Allocate the outputs with torch and run moe_dispatch_int8: (DispatchOut with an
     int8 expand_x, dynamic_scales (capacity,) fp32)."""
@@ -760,6 +924,9 @@ def shared_expert_shape(T, H, F) -> MoeShape:
 
 class _MoELayerFn(torch.autograd.Function):
     """Forward: dispatch -> grouped SwiGLU FFN -> combine; backward: the reverse chain.
+    In bf16 the dispatch permute is folded into the two GEMMs that read the
+    expanded rows (moe_route, then the gathered gate/up forward and gate/up weight
+    gradient read x through the row -> slot map), so no expanded rows are kept.
 
     A shared expert (shared_w_*) runs as the same grouped FFN with one expert
     whose rows are all T tokens in order, so x itself is its expanded input;
@@ -786,7 +953,16 @@ class _MoELayerFn(torch.autograd.Function):
                            copy_expert_num=copy_expert_num, const_expert_num=const_expert_num,
                            mask_ndim=mask_ndim, comm_quant_mode=comm_quant_mode)
         mask = None if x_active_mask is None else x_active_mask.view(torch.uint8)
-        d = dispatch(shape, x, topk_idx, mask)
+        # bf16: the routing alone; the gate/up GEMMs read x through the row -> slot
+        # map (no expanded rows).  The 8-bit paths quantise the expanded rows.
+        # fp8 with fp32 block scales and bf16 weight gradients: the whole step through
+        # the fused boundary entries (quantising dispatch, fp8 grouped FFN, combine
+        # backward writing dY's codes, fp8 grouped FFN backward)
+        ctx.fused8 = bool(fp8) and not mx and not fp8_wgrad
+        if ctx.fused8:
+            d, xq8, xs8 = dispatch_fp8(shape, x, topk_idx, mask)
+        else:
+            d = dispatch(shape, x, topk_idx, mask) if fp8 else route(shape, topk_idx, mask)
         cap = shape.capacity
         gus = torch.empty((cap, 2 * F), dtype=BF16, device=dev)
         h = torch.empty((cap, F), dtype=BF16, device=dev)
@@ -808,6 +984,12 @@ class _MoELayerFn(torch.autograd.Function):
                                    d.ep_recv_counts, gus, h, (hq, hs))
             moe_ffn_down_fwd_mx(shape, hq, hs, wq[2].codes, wq[2].scales, d.ep_recv_counts, y)
             del xq, xs, hq, hs
+        elif ctx.fused8:
+            wq = tuple(Fp8Weights.quantize(w) for w in (w_gate, w_up, w_down))
+            ctx.wq8 = wq
+            moe_grouped_ffn_fp8(shape, xq8, xs8, wq, d.ep_recv_counts, gus, h, y,
+                                torch.empty(moe_ffn_fp8_workspace_size(shape), dtype=torch.uint8, device=dev))
+            del xq8, xs8
         elif ctx.fp8:
             nrows = d.ep_recv_counts[-1:]
             wq = tuple(Fp8Weights.quantize(w) for w in (w_gate, w_up, w_down))
@@ -827,7 +1009,8 @@ class _MoELayerFn(torch.autograd.Function):
             moe_ffn_down_fwd_fp8(shape, hq, hs, wq[2].codes, wq[2].scales, d.ep_recv_counts, y)
             del xq, xs, hq, hs
         else:
-            moe_grouped_ffn(shape, d.expand_x, w_gate, w_up, w_down, d.ep_recv_counts, gus, h, y)
+            moe_ffn_gate_up_fwd_gather(shape, x, d.assist_info_for_combine, w_gate, w_up, d.ep_recv_counts, gus, h)
+            moe_ffn_down_fwd(shape, h, w_down, d.ep_recv_counts, y)
         ctx.shared_ffn = shared_w_gate is not None
         s_saved = ()
         if ctx.shared_ffn:
@@ -849,7 +1032,7 @@ class _MoELayerFn(torch.autograd.Function):
         ctx.shape = shape
         ctx.has_shared_x = shared_expert_x is not None and not ctx.shared_ffn
         ctx.save_for_backward(x, topk_weights, w_gate, w_up, w_down, topk_idx, mask, const_alpha_1,
-                              const_alpha_2, const_v, d.expand_x, d.assist_info_for_combine,
+                              const_alpha_2, const_v, d.expand_x if fp8 else None, d.assist_info_for_combine,
                               d.ep_recv_counts, gus, h, y, *s_saved)
         # the transposed weight codes of the data-gradient GEMMs (not tensors
         # of the graph, so kept on ctx)
@@ -867,8 +1050,14 @@ class _MoELayerFn(torch.autograd.Function):
         dev = x.device
         gy = torch.empty((cap, H), dtype=BF16, device=dev)
         gw = torch.empty((T, K), dtype=F32, device=dev)
-        moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
-                        gy, gw)
+        if ctx.fused8:
+            gyq = torch.empty((cap, H), dtype=U8T, device=dev)
+            gys = torch.empty((H // 128, cap), dtype=F32T, device=dev)
+            moe_combine_bwd_fp8(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
+                                gy, gyq, gys, gw)
+        else:
+            moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
+                            gy, gw)
         # the fp8 weight gradients need no bf16 dG/dU (its codes come out of the
         # down data gradient)
         ggu = None if ctx.fp8_wgrad else torch.empty((cap, 2 * F), dtype=BF16, device=dev)
@@ -878,7 +1067,12 @@ class _MoELayerFn(torch.autograd.Function):
         gwd = torch.empty(w_down.shape, dtype=F32, device=dev)
         # data gradients first, the gate/up weight gradient after dispatch
         # backward (each gather right after the kernel that wrote its input)
-        if ctx.mx:
+        if ctx.fused8:
+            moe_grouped_ffn_bwd_fp8(shape, gy, gyq, gys, expand_x, gus, h, ctx.wq8, recv, ggu, gx_exp, gwg, gwu, gwd,
+                                    torch.empty(moe_ffn_fp8_workspace_size(shape), dtype=torch.uint8, device=dev))
+            del gyq, gys
+            ctx.wq8 = None
+        elif ctx.mx:
             (wgt, wgs), (wut, wus), (wdt, wds) = ctx.wq
             nrows = recv[-1:]
             dyq, dys = quant_rows_mx(gy, nrows)
@@ -937,8 +1131,12 @@ class _MoELayerFn(torch.autograd.Function):
             xq_t, xs_t = quant_cols_fp8(expand_x, recv)
             moe_ffn_gate_up_bwd_weight_fp8(shape, *dg_cols, xq_t, xs_t, recv, gwg, gwu)
             del dg_cols, xq_t, xs_t
-        else:
+        elif ctx.fused8:
+            pass  # in moe_grouped_ffn_bwd_fp8
+        elif ctx.fp8:
             moe_ffn_gate_up_bwd_weight(shape, ggu, expand_x, recv, gwg, gwu)
+        else:
+            moe_ffn_gate_up_bwd_weight_gather(shape, ggu, x, assist, recv, gwg, gwu)
         g_shared = grad_out if ctx.has_shared_x else None
         return (gx, gw, gwg.to(w_gate.dtype), gwu.to(w_up.dtype), gwd.to(w_down.dtype), g_shared,
                 *s_grads, None, None, None, None, None, None, None, None, None, None, None, None)

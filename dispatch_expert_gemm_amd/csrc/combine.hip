@@ -265,9 +265,17 @@ struct CombineBwdArgs {
   int K;
   int64_t Hv;
   int qpay;
+  // Q8: e4m3 codes of every dY row (8 per 16-byte vector) with one fp32 scale
+  // per 128 columns, stored (H/128, capacity) like moe_quant_rows_fp8's
+  uint2* dyq;
+  float* dys;
+  int64_t capacity;
 };
 
-template <int KMAX, bool ONE_PASS>
+// Q8: also the e4m3 codes of the bf16 dY rows, by the rule of the row quantiser
+// on the stored bf16 values (the 16 lanes of an aligned group hold one
+// 128-column block: H is a multiple of 128); dy may then be NULL.
+template <int KMAX, bool ONE_PASS, bool Q8 = false>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
@@ -341,7 +349,22 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
             const float wk = si.w[k];
 #pragma unroll
             for (int i = 0; i < 8; ++i) g[i] = wk * d[i];
-            dy[(int64_t)c * Hv + v] = pack8(g);
+            const uint4 gp = pack8(g);
+            if (!Q8 || dy) dy[(int64_t)c * Hv + v] = gp;
+            if constexpr (Q8) {
+              float q[8];
+              unpack8(gp, q);
+              float amax = 0.f;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(q[i]));
+#pragma unroll
+              for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+              const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+              a.dyq[(int64_t)c * Hv + v] = make_uint2(
+                  e4m3x4(__fmul_rn(q[0], inv), __fmul_rn(q[1], inv), __fmul_rn(q[2], inv), __fmul_rn(q[3], inv)),
+                  e4m3x4(__fmul_rn(q[4], inv), __fmul_rn(q[5], inv), __fmul_rn(q[6], inv), __fmul_rn(q[7], inv)));
+              if ((v & 15) == 0) a.dys[(v >> 4) * a.capacity + c] = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+            }
           }
         }
       }
@@ -502,18 +525,21 @@ extern "C" moe_status moe_combine(const moe_shape* s, const void* y, const int32
   return launch_status();
 }
 
-extern "C" moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, const void* y,
-                                      const int32_t* topk_idx, const float* topk_weights,
-                                      const int32_t* assist, const int32_t* ep_send_counts,
-                                      const uint8_t* x_active_mask, const void* ori_x,
-                                      const void* const_alpha_1, const void* const_alpha_2,
-                                      const void* const_v, void* grad_y, float* grad_topk_weights,
-                                      void* stream) {
+namespace {
+moe_status combine_bwd_impl(const moe_shape* s, const void* grad_out, const void* y, const int32_t* topk_idx,
+                            const float* topk_weights, const int32_t* assist, const int32_t* ep_send_counts,
+                            const uint8_t* x_active_mask, const void* ori_x, const void* const_alpha_1,
+                            const void* const_alpha_2, const void* const_v, void* grad_y, uint8_t* grad_yq,
+                            float* grad_y_scales, float* grad_topk_weights, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
+  const bool q8 = grad_yq != nullptr;
+  if (q8 && s->H % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  if (q8 && s->capacity * (s->H / 128) * 4 >= (int64_t)0x7ffffff0) return MOE_ERR_UNSUPPORTED;
   if (s->T == 0) return MOE_OK;
   MOE_NEED(y, s->capacity * s->H);
-  MOE_NEED(grad_y, s->capacity * s->H);
+  if (!q8) MOE_NEED(grad_y, s->capacity * s->H);
+  if (q8) MOE_NEED(grad_y_scales, s->capacity * (s->H / 128));
   if (!grad_out || !topk_idx || !topk_weights || !assist || !ep_send_counts ||
       !grad_topk_weights)
     return MOE_ERR_NULL_ARG;
@@ -533,15 +559,49 @@ extern "C" moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, 
                    s->T,
                    s->K,
                    s->H / 8,
-                   s->comm_quant_mode == 2};
+                   s->comm_quant_mode == 2,
+                   reinterpret_cast<uint2*>(grad_yq),
+                   grad_y_scales,
+                   s->capacity};
   launch_k(s->K, [&](auto km) {
     constexpr int KM = decltype(km)::value;
-    if (a.qpay && a.Hv <= (int64_t)kChunk<KM> * kWave)
+    const bool one = a.qpay && a.Hv <= (int64_t)kChunk<KM> * kWave;
+    if (q8 && one)
+      hipLaunchKernelGGL((k_combine_bwd<KM, true, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+    else if (q8)
+      hipLaunchKernelGGL((k_combine_bwd<KM, false, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+    else if (one)
       hipLaunchKernelGGL((k_combine_bwd<KM, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
     else
       hipLaunchKernelGGL((k_combine_bwd<KM, false>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
   });
   return launch_status();
+}
+}  // namespace
+
+extern "C" moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, const void* y,
+                                      const int32_t* topk_idx, const float* topk_weights,
+                                      const int32_t* assist, const int32_t* ep_send_counts,
+                                      const uint8_t* x_active_mask, const void* ori_x,
+                                      const void* const_alpha_1, const void* const_alpha_2,
+                                      const void* const_v, void* grad_y, float* grad_topk_weights,
+                                      void* stream) {
+  return combine_bwd_impl(s, grad_out, y, topk_idx, topk_weights, assist, ep_send_counts, x_active_mask, ori_x,
+                          const_alpha_1, const_alpha_2, const_v, grad_y, nullptr, nullptr, grad_topk_weights,
+                          stream);
+}
+
+extern "C" moe_status moe_combine_bwd_fp8(const moe_shape* s, const void* grad_out, const void* y,
+                                          const int32_t* topk_idx, const float* topk_weights,
+                                          const int32_t* assist, const int32_t* ep_send_counts,
+                                          const uint8_t* x_active_mask, const void* ori_x,
+                                          const void* const_alpha_1, const void* const_alpha_2,
+                                          const void* const_v, void* grad_y, uint8_t* grad_yq,
+                                          float* grad_y_scales, float* grad_topk_weights, void* stream) {
+  if (!grad_yq) return MOE_ERR_NULL_ARG;
+  return combine_bwd_impl(s, grad_out, y, topk_idx, topk_weights, assist, ep_send_counts, x_active_mask, ori_x,
+                          const_alpha_1, const_alpha_2, const_v, grad_y, grad_yq, grad_y_scales,
+                          grad_topk_weights, stream);
 }
 
 extern "C" moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,

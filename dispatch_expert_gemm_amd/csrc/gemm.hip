@@ -81,7 +81,13 @@ struct GemmArgs {
   // map of the routing, gK = top-K), so the dispatch permute is not needed
   const int32_t* gather;
   int gK;
-  int64_t gbytes;  // bytes of x (T * H * 2): the range of the gathered A loads
+  int64_t gbytes;  // bytes of x (T * H * 2): the range of the gathered loads
+  // gate/up weight gradient with the B operand gathered (rows of x read through
+  // the row -> slot map): rows of the map (capacity), and slot / K as
+  // (slot * kmagic) >> kshift (exact for slots below 2^31)
+  int64_t grows;
+  uint64_t kmagic;
+  int kshift;
   const bf16_t* B0;
   const bf16_t* B1;
   int64_t ldb;
@@ -756,6 +762,23 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     }
   }
   const bool gathered = MODE == GATE_UP_FWD && !FP8 && g.gather;
+  // gate/up weight gradient reading the rows of x through the row -> slot map:
+  // lane k-rows and byte columns of its B loads, and a ring of the map's entries
+  // per K step (8 steps of 64), filled by wave 0 with direct-to-LDS loads two
+  // steps ahead of the step whose tile loads need them
+  constexpr bool GATHER_B = MODE == GATE_UP_BWD_W && !FP8;
+  const bool gatherB = GATHER_B && g.gather;
+  __shared__ int32_t tokr[GATHER_B ? 8 * 64 : 1];
+  int kB[LB];
+  uint32_t colB[LB];
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    constexpr int CPR = BN / 8, RPI = 64 / CPR;
+    const int q = wave * LB + j;
+    const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw4(k);
+    kB[j] = k;
+    colB[j] = (uint32_t)((n0 + c * 8 < g.N ? n0 + c * 8 : g.N - 8) * 2);
+  }
   const char* abase =
       reinterpret_cast<const char*>(KGROUP ? g.A + kbeg * g.lda : (gathered ? g.A : g.A + row0 * g.lda));
   const char* bbase0;
@@ -804,10 +827,27 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
         dma(up ? r1 : r0, sb + q * 512, vo);
       }
     } else if constexpr (KGROUP) {
-      const auto r = rsrc(bbase0 + k0 * g.ldb * 2, (klen - k0) * g.ldb * 2);
+      if (GATHER_B && gatherB) {
+        // k-row k of the step is expanded row kbeg + k0 + k, i.e. row slot/K of x;
+        // k-rows past the expert's end read zeros
+        const auto r = rsrc(g.B0, g.gbytes);
+        const int32_t* tk = tokr + (kt & 7) * 64;
 #pragma unroll
-      for (int j = 0; j < LB; ++j)
-        dma(r, sb + (wv * LB + j) * 512, voB[j]);
+        for (int j = 0; j < LB; ++j) {
+          uint32_t vo = kOOB;
+          if (k0 + kB[j] < klen) {
+            const uint32_t sl = (uint32_t)tk[kB[j]];
+            const uint32_t tok = (uint32_t)(((uint64_t)sl * g.kmagic) >> g.kshift);
+            vo = tok * (uint32_t)(g.ldb * 2) + colB[j];
+          }
+          dma(r, sb + (wv * LB + j) * 512, vo);
+        }
+      } else {
+        const auto r = rsrc(bbase0 + k0 * g.ldb * 2, (klen - k0) * g.ldb * 2);
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+          dma(r, sb + (wv * LB + j) * 512, voB[j]);
+      }
     } else {
       // data gradients: B = the expert's weights, K-strided over Kd (= H, or
       // 2F with the gate rows < F and the up rows >= F; F is a multiple of
@@ -898,6 +938,28 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
   // of the others instead of all of them waiting on the same misses.
   const int64_t ks = nk ? ((int64_t)kseed * g.krot) % nk : 0;
   auto rot = [&](int64_t t) -> int64_t { const int64_t u = t + ks; return u < nk ? u : u - nk; };
+  // map entries of K step kt (and the next) into ring slot kt % 8, by wave 0,
+  // issued at step kt - S - 1 before that step's tile loads: the wait of step
+  // kt - S + 1 covers it (it is older than that step's own tile loads), and that
+  // step's barrier publishes it before the tile loads of step kt are issued
+  auto issue_tok = [&](int64_t kt) {
+    if (wv != 0) return;
+    const int64_t r0 = kbeg + kt * BK;
+    const auto r = rsrc(g.gather + r0, (g.grows - r0) * 4);
+    const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) int32_t*)(tokr + (kt & 7) * 64));
+    const uint32_t vo = (uint32_t)lane * 4;
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0));
+  };
+  if (GATHER_B && gatherB) {
+    // the entries of the first S + 1 steps, with plain loads before the pipeline
+    static_assert(!GATHER_B || kThreads >= 64, "");
+    for (int i = tid; i < (S + 1) * 64; i += kThreads) {
+      const int64_t st = i / 64, r0 = kbeg + st * BK + (i % 64);
+      tokr[(st & 7) * 64 + (i % 64)] = (st < nk && r0 < g.grows) ? g.gather[r0] : 0;
+    }
+    __syncthreads();
+  }
   auto kstep = [&](auto ST, int64_t kt) {
     constexpr int st = decltype(ST)::value;
     if (kt + S - 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L * (S - 2)));
@@ -908,6 +970,9 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // (the map entries go before the tile loads: the wait of a later step then
+    // covers them without waiting on a tile load issued after them)
+    if (GATHER_B && gatherB && kt + S + 1 < nk) issue_tok(kt + S + 1);
     if (kt + S - 1 < nk) issue(std::integral_constant<int, (st + S - 1) % S>(), rot(kt + S - 1));
     compute(ST);
   };
@@ -1598,6 +1663,40 @@ extern "C" moe_status moe_ffn_gate_up_bwd_weight(const moe_shape* s, const void*
   g.lda = 2 * s->F;
   g.B0 = static_cast<const bf16_t*>(expand_x);
   g.ldb = s->H;
+  g.M = 2 * s->F;
+  g.N = s->H;
+  g.W0 = grad_w_gate;
+  g.W1 = grad_w_up;
+  return launch<GATE_UP_BWD_W>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_gate_up_bwd_weight_gather(const moe_shape* s, const void* grad_gate_up,
+                                                        const void* x, const int32_t* assist,
+                                                        const int32_t* ep_recv_counts, float* grad_w_gate,
+                                                        float* grad_w_up, void* stream) {
+  moe_status st = check_ffn_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ep_recv_counts || !grad_w_gate || !grad_w_up) return MOE_ERR_NULL_ARG;
+  // the per-lane byte offsets into x are 31-bit (the top bit marks a k-row past
+  // the expert's end)
+  if ((s->T + 1) * s->H * 2 > 0x7ffffff0LL) return MOE_ERR_UNSUPPORTED;
+  MOE_NEED(grad_gate_up, s->capacity * 2 * s->F);
+  MOE_NEED(x, s->T * s->H);
+  MOE_NEED(assist, s->T * s->K + s->capacity);
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.A = static_cast<const bf16_t*>(grad_gate_up);
+  g.lda = 2 * s->F;
+  g.B0 = static_cast<const bf16_t*>(x);
+  g.ldb = s->H;
+  g.gather = s->capacity > 0 ? assist + s->T * s->K : nullptr;  // row -> slot
+  g.gK = s->K;
+  g.gbytes = s->T * s->H * 2;
+  g.grows = s->capacity;
+  // slot / K = (slot * m) >> (32 + l), l = ceil(log2 K), m = floor(2^(32+l) / K) + 1
+  int l = 0;
+  while ((1 << l) < s->K) ++l;
+  g.kmagic = (((uint64_t)1 << (32 + l)) / (uint64_t)s->K) + 1;
+  g.kshift = 32 + l;
   g.M = 2 * s->F;
   g.N = s->H;
   g.W0 = grad_w_gate;

@@ -39,27 +39,48 @@ struct RouteArgs {
   int K, E, Z, C, Q, mask_ndim;
 };
 
-// Class of slot s: >= 0 routed expert id; MOE_SLOT_NONE; MOE_SLOT_COPY; -(3+j).
-// ORs MOE_FLAG_ID_RANGE / MOE_FLAG_ID_DUPLICATE into err.  Invalid and duplicate
-// slots (the later occurrence) are inactive.
-__device__ __forceinline__ int classify(const RouteArgs& a, int64_t s, uint32_t& err) {
+// Class of slot s = base + lane (the wave's 64 consecutive slots from base; slots
+// at or past s1 are not slots): >= 0 routed expert id; MOE_SLOT_NONE;
+// MOE_SLOT_COPY; -(3+j).  ORs MOE_FLAG_ID_RANGE / MOE_FLAG_ID_DUPLICATE (and,
+// with a 1-D mask, MOE_FLAG_MASK_NOT_PREFIX) into err.  Invalid and duplicate
+// slots (the later occurrence) are inactive.  When K divides 64 the wave's
+// slots are whole tokens (base is a multiple of K), so a slot's earlier ids of
+// its token sit in the lanes just below it: the duplicate test is K-1 lane
+// shuffles instead of K-1 loads.
+__device__ __forceinline__ int classify_wave(const RouteArgs& a, int64_t base, int64_t s1, uint32_t& err) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t s = base + lane;
+  const bool valid = s < s1;
   const int64_t t = s / a.K;
   const int k = (int)(s - t * a.K);
-  const int id = a.idx[s];
+  const int id = valid ? a.idx[s] : -1;
+  bool act = true;
+  if (valid && a.mask_ndim == 1) {
+    act = a.mask[t] != 0;
+    if (k == 0 && t > 0 && act && a.mask[t - 1] == 0) err |= MOE_FLAG_MASK_NOT_PREFIX;
+  } else if (valid && a.mask_ndim == 2) {
+    act = a.mask[s] != 0;
+  }
+  bool dup = false;
+  if (kWave % a.K == 0) {
+    for (int j = 1; j < a.K; ++j) {
+      const int o = __shfl_up(id, (unsigned)j, kWave);
+      dup |= (j <= k) && (o == id);
+    }
+  } else if (valid) {
+    const int32_t* row = a.idx + t * a.K;
+    for (int kk = 0; kk < k; ++kk) dup |= row[kk] == id;
+  }
+  if (!valid) return MOE_SLOT_NONE;
   const int etot = a.E + a.Z + a.C + a.Q;
   if (id < 0 || id >= etot) {
     err |= MOE_FLAG_ID_RANGE;
     return MOE_SLOT_NONE;
   }
-  const int32_t* row = a.idx + t * a.K;
-  for (int kk = 0; kk < k; ++kk)
-    if (row[kk] == id) {
-      err |= MOE_FLAG_ID_DUPLICATE;
-      return MOE_SLOT_NONE;
-    }
-  bool act = true;
-  if (a.mask_ndim == 1) act = a.mask[t] != 0;
-  else if (a.mask_ndim == 2) act = a.mask[s] != 0;
+  if (dup) {
+    err |= MOE_FLAG_ID_DUPLICATE;
+    return MOE_SLOT_NONE;
+  }
   if (!act) return MOE_SLOT_NONE;
   if (id < a.E) return id;
   if (id < a.E + a.Z) return MOE_SLOT_NONE;
@@ -112,15 +133,7 @@ __global__ __launch_bounds__(256) void k_route_count(RouteArgs a, int32_t* __res
   int32_t* h = sh + wave * Ep;
   uint32_t err = 0;
   for (int r = wave; r < rounds; r += 4) {
-    const int64_t s = s0 + (int64_t)r * kWave + lane;
-    int cls = MOE_SLOT_NONE;
-    if (s < s1) {
-      cls = classify(a, s, err);
-      if (a.mask_ndim == 1 && (s % a.K) == 0) {
-        const int64_t t = s / a.K;
-        if (t > 0 && a.mask[t] != 0 && a.mask[t - 1] == 0) err |= MOE_FLAG_MASK_NOT_PREFIX;
-      }
-    }
+    const int cls = classify_wave(a, s0 + (int64_t)r * kWave, s1, err);
     const uint64_t peers = same_expert(cls, nbits);
     // one lane per expert present in the round adds the round's count
     if (peers && (peers & below) == 0) h[cls] += __popcll(peers);
@@ -148,14 +161,19 @@ __device__ __forceinline__ int32_t block_scan(int32_t v, int32_t* wtot) {
   return v;
 }
 
-template <bool PERMUTE>
+// COPY: 0 maps only; 1 bf16 token rows to their rows; 2 e4m3 codes of the
+// token rows (one fp32 scale per 128 columns, the rule of moe_quant_rows_fp8,
+// taken once per token) to their rows, and the bf16 rows too when ex is given.
+template <int COPY>
 __global__ __launch_bounds__(256) void k_route_place(RouteArgs a, const int32_t* __restrict__ hist,
                                                      const int32_t* __restrict__ chunk_err, int64_t tpc, int nchunks,
                                                      int rounds, int Ep, int nbits, int P,
                                                      int32_t* __restrict__ counts, int32_t* __restrict__ prefix,
                                                      int32_t* __restrict__ err_flag, int32_t* __restrict__ slot2row,
                                                      int32_t* __restrict__ row2slot, const uint4* __restrict__ x,
-                                                     int64_t Hv, uint4* __restrict__ ex) {
+                                                     int64_t Hv, uint4* __restrict__ ex, uint2* __restrict__ exq,
+                                                     float* __restrict__ exs, int64_t capacity) {
+  constexpr bool PERMUTE = COPY != 0;
   // LDS: off[4][Ep] running row offsets of each wave's rounds, cnt[4][Ep] their
   // counts, red[2][G][Ep] partial sums (G * Ep <= 1024), rows of this
   // workgroup's tokens [tokens of the part][K]
@@ -178,10 +196,20 @@ __global__ __launch_bounds__(256) void k_route_place(RouteArgs a, const int32_t*
     int4 pre4 = {0, 0, 0, 0}, tot4 = {0, 0, 0, 0};
     const int g = q4 >= 256 ? 0 : tid / q4;
     if (g < G) {
-      for (int cc = g; cc < nchunks; cc += G) {
-        const int4 v = *reinterpret_cast<const int4*>(hist + (int64_t)cc * Ep + 4 * col);
-        tot4.x += v.x; tot4.y += v.y; tot4.z += v.z; tot4.w += v.w;
-        if (cc < c) { pre4.x += v.x; pre4.y += v.y; pre4.z += v.z; pre4.w += v.w; }
+      // eight independent loads in flight per round of the loop
+      for (int cc0 = g; cc0 < nchunks; cc0 += 8 * G) {
+        int4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int cc = cc0 + u * G;
+          v[u] = cc < nchunks ? *reinterpret_cast<const int4*>(hist + (int64_t)cc * Ep + 4 * col) : int4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int cc = cc0 + u * G;
+          tot4.x += v[u].x; tot4.y += v[u].y; tot4.z += v[u].z; tot4.w += v[u].w;
+          if (cc < c) { pre4.x += v[u].x; pre4.y += v[u].y; pre4.z += v[u].z; pre4.w += v[u].w; }
+        }
       }
       *reinterpret_cast<int4*>(red + g * Ep + 4 * col) = pre4;
       *reinterpret_cast<int4*>(red + 1024 + g * Ep + 4 * col) = tot4;
@@ -200,9 +228,8 @@ __global__ __launch_bounds__(256) void k_route_place(RouteArgs a, const int32_t*
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   __syncthreads();  // cnt zeroed, red written
   auto count_round = [&](int r) -> int {
-    const int64_t s = s0 + (int64_t)r * kWave + lane;
     uint32_t unused = 0;
-    const int cls = s < s1 ? classify(a, s, unused) : MOE_SLOT_NONE;
+    const int cls = classify_wave(a, s0 + (int64_t)r * kWave, s1, unused);
     const uint64_t peers = same_expert(cls, nbits);
     if (peers && (peers & below) == 0) cnt[wave * Ep + cls] += __popcll(peers);
     return cls;
@@ -275,9 +302,8 @@ __global__ __launch_bounds__(256) void k_route_place(RouteArgs a, const int32_t*
   for (int i = 0; i < kKeep; ++i)
     if (r0 + i < r1) place_round(r0 + i, keep[i]);
   for (int r = r0 + kKeep; r < r1; ++r) {
-    const int64_t s = s0 + (int64_t)r * kWave + lane;
     uint32_t unused = 0;
-    place_round(r, s < s1 ? classify(a, s, unused) : MOE_SLOT_NONE);
+    place_round(r, classify_wave(a, s0 + (int64_t)r * kWave, s1, unused));
   }
   if constexpr (PERMUTE) {
     __syncthreads();
@@ -294,11 +320,40 @@ __global__ __launch_bounds__(256) void k_route_place(RouteArgs a, const int32_t*
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t v = v0 + q * 256;
-        if (v >= nv) continue;
-        const int64_t lt = v / Hv, col = v % Hv;
-        for (int k = 0; k < a.K; ++k) {
-          const int rr = rows[lt * a.K + k];
-          if (rr >= 0) ex[(int64_t)rr * Hv + col] = val[q];
+        if constexpr (COPY == 2) {
+          // the 16 lanes of an aligned group hold one 128-column block of a token
+          // row (H is a multiple of 128): all of them valid or all past the end
+          float f[8];
+          if (v < nv) unpack8(val[q], f);
+          else
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = 0.f;
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+          for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+          if (v >= nv) continue;
+          const float inv = amax > 0.f ? __fdiv_rn(448.0f, amax) : 0.f;
+          const uint2 code = make_uint2(
+              e4m3x4(__fmul_rn(f[0], inv), __fmul_rn(f[1], inv), __fmul_rn(f[2], inv), __fmul_rn(f[3], inv)),
+              e4m3x4(__fmul_rn(f[4], inv), __fmul_rn(f[5], inv), __fmul_rn(f[6], inv), __fmul_rn(f[7], inv)));
+          const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+          const int64_t lt = v / Hv, col = v % Hv;
+          for (int k = 0; k < a.K; ++k) {
+            const int rr = rows[lt * a.K + k];
+            if (rr < 0) continue;
+            if (ex) ex[(int64_t)rr * Hv + col] = val[q];
+            exq[(int64_t)rr * Hv + col] = code;
+            if ((col & 15) == 0) exs[(col >> 4) * capacity + rr] = scale;
+          }
+        } else {
+          if (v >= nv) continue;
+          const int64_t lt = v / Hv, col = v % Hv;
+          for (int k = 0; k < a.K; ++k) {
+            const int rr = rows[lt * a.K + k];
+            if (rr >= 0) ex[(int64_t)rr * Hv + col] = val[q];
+          }
         }
       }
     }
@@ -436,12 +491,13 @@ moe_status check_dispatch(const moe_shape* s, const int32_t* topk_idx,
   return MOE_OK;
 }
 
-// the routing kernels: counts, then rows, maps (and, given x and expand_x, the
-// copy of every token row to its rows)
+// the routing kernels: counts, then rows and maps, and, given x, the copy of
+// every token row to its rows (bf16 into expand_x, and with expand_xq the e4m3
+// codes and scales too)
 void launch_route(const moe_shape* s, const int32_t* topk_idx, const uint8_t* x_active_mask,
                   int32_t* assist, int32_t* expert_token_nums, int32_t* ep_recv_counts,
                   int32_t* err_flag, void* workspace, hipStream_t strm, const void* x = nullptr,
-                  void* expand_x = nullptr) {
+                  void* expand_x = nullptr, uint8_t* expand_xq = nullptr, float* dynamic_scales = nullptr) {
   const RouteGeom g = route_geom(s);
   RouteArgs a{topk_idx, x_active_mask, s->T, s->K, s->num_experts, s->zero_expert_num,
               s->copy_expert_num, s->const_expert_num, s->mask_ndim};
@@ -454,19 +510,22 @@ void launch_route(const moe_shape* s, const int32_t* topk_idx, const uint8_t* x_
   if (g.nchunks > 0)
     hipLaunchKernelGGL(k_route_count, dim3(g.nchunks), dim3(256), (size_t)4 * g.Ep * sizeof(int32_t), strm, a, hist,
                        cerr, g.tpc, g.rounds, g.Ep, nbits);
-  const bool permute = x != nullptr && g.nchunks > 0;
-  const int P = permute ? g.P : 1;
+  const int copy = (x == nullptr || g.nchunks == 0) ? 0 : (expand_xq ? 2 : 1);
+  const int P = copy ? g.P : 1;
   const int64_t part_tokens = (g.tpc + P - 1) / P;
-  const size_t lds = ((size_t)8 * g.Ep + 2048 + (permute ? part_tokens * s->K : 0)) * sizeof(int32_t);
+  const size_t lds = ((size_t)8 * g.Ep + 2048 + (copy ? part_tokens * s->K : 0)) * sizeof(int32_t);
   const dim3 grid((unsigned)(g.nchunks > 0 ? (int64_t)g.nchunks * P : 1));
-  if (permute)
-    hipLaunchKernelGGL(k_route_place<true>, grid, dim3(256), lds, strm, a, hist, cerr, g.tpc, g.nchunks, g.rounds,
-                       g.Ep, nbits, P, expert_token_nums, ep_recv_counts, err_flag, slot2row, row2slot,
-                       static_cast<const uint4*>(x), s->H / 8, static_cast<uint4*>(expand_x));
-  else
-    hipLaunchKernelGGL(k_route_place<false>, grid, dim3(256), lds, strm, a, hist, cerr, g.tpc, g.nchunks, g.rounds,
-                       g.Ep, nbits, P, expert_token_nums, ep_recv_counts, err_flag, slot2row, row2slot,
-                       static_cast<const uint4*>(nullptr), s->H / 8, static_cast<uint4*>(nullptr));
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint4* ev = static_cast<uint4*>(expand_x);
+  uint2* qv = reinterpret_cast<uint2*>(expand_xq);
+#define PLACE(C)                                                                                                    \
+  hipLaunchKernelGGL(k_route_place<C>, grid, dim3(256), lds, strm, a, hist, cerr, g.tpc, g.nchunks, g.rounds, g.Ep, \
+                     nbits, P, expert_token_nums, ep_recv_counts, err_flag, slot2row, row2slot, xv, s->H / 8, ev, qv, \
+                     dynamic_scales, s->capacity)
+  if (copy == 2) PLACE(2);
+  else if (copy == 1) PLACE(1);
+  else PLACE(0);
+#undef PLACE
 }
 }  // namespace
 
@@ -521,6 +580,27 @@ extern "C" moe_status moe_dispatch(const moe_shape* s, const void* x, const int3
   if (st != MOE_OK) return st;
   return dispatch_impl(s, x, topk_idx, x_active_mask, expand_x, assist, expert_token_nums, ep_recv_counts,
                        err_flag, workspace, as_stream(stream));
+}
+
+extern "C" moe_status moe_dispatch_fp8(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                                       const uint8_t* x_active_mask, void* expand_x, uint8_t* expand_xq,
+                                       float* dynamic_scales, int32_t* assist, int32_t* expert_token_nums,
+                                       int32_t* ep_recv_counts, int32_t* err_flag, void* workspace,
+                                       size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->H % 128 != 0) return MOE_ERR_BAD_SHAPE;
+  // the scales of all rows are addressed with 32-bit offsets like the fp8 GEMMs'
+  if (s->capacity * (s->H / 128) * 4 >= (int64_t)0x7ffffff0) return MOE_ERR_UNSUPPORTED;
+  st = check_dispatch(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag,
+                      workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  MOE_NEED(x, s->T * s->H);
+  MOE_NEED(expand_xq, s->capacity * s->H);
+  MOE_NEED(dynamic_scales, s->capacity * (s->H / 128));
+  launch_route(s, topk_idx, x_active_mask, assist, expert_token_nums, ep_recv_counts, err_flag, workspace,
+               as_stream(stream), x, expand_x, expand_xq, dynamic_scales);
+  return launch_status();
 }
 
 extern "C" moe_status moe_dispatch_int8(const moe_shape* s, const void* x, const int32_t* topk_idx,

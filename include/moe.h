@@ -80,6 +80,16 @@ typedef struct moe_shape {
   int32_t comm_quant_mode;  /* 0: none; 2: int8 expert-output payload in combine (see moe_combine) */
 } moe_shape;
 
+/* One expert weight tensor in block-scaled e4m3, as moe_quantize_weights_fp8
+ * writes it: codes in the (out, in) layout (the forward GEMMs' operand), the
+ * transposed codes (in, out) (the data gradients' operand) and the fp32 scale
+ * of every 128 x 128 block, shared by both layouts. */
+typedef struct moe_fp8_weight {
+  const uint8_t* codes;    /* (E, N, Kdim) */
+  const uint8_t* codes_t;  /* (E, Kdim, N) */
+  const float* scales;     /* (E, N/128, Kdim/128) */
+} moe_fp8_weight;
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_str(moe_status st);
 
@@ -141,6 +151,23 @@ moe_status moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_i
 moe_status moe_grouped_ffn(const moe_shape* s, const void* expand_x, const void* w_gate,
                            const void* w_up, const void* w_down, const int32_t* ep_recv_counts,
                            void* gate_up_save, void* h_act, void* y, void* stream);
+
+/* moe_dispatch_fp8 - moe_dispatch for the fp8 GEMMs: the permute writes every
+ * expanded row as e4m3 codes with one fp32 scale per 128 columns, quantised once
+ * per token (the rule and layout of moe_quant_rows_fp8: amax of the 128 values,
+ * codes e4m3(v * (448/amax)), scale amax/448, an all-zero block codes 0 and scale 1),
+ * and, when expand_x is given, the bf16 rows too (the bf16 weight gradients
+ * read them).  The low_latency_combine page's dispatch returns its quantised
+ * expand_x with dynamic_scales the same way (Example, quant_mode 2).
+ *  out  expand_x        (capacity, H) bf16, or NULL
+ *  out  expand_xq       (capacity, H) uint8 e4m3 codes
+ *  out  dynamic_scales  (H/128, capacity) fp32, block-major
+ *  other arguments, outputs and checks as moe_dispatch; H must be a multiple of
+ *  128 (MOE_ERR_BAD_SHAPE). */
+moe_status moe_dispatch_fp8(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                            const uint8_t* x_active_mask, void* expand_x, uint8_t* expand_xq, float* dynamic_scales,
+                            int32_t* assist_info_for_combine, int32_t* expert_token_nums, int32_t* ep_recv_counts,
+                            int32_t* err_flag, void* workspace, size_t ws_bytes, void* stream);
 
 /* moe_dispatch_noalloc - moe_dispatch for callers that cannot allocate device
  * memory: code under stream capture, tight serving loops, harnesses that forbid
@@ -235,6 +262,21 @@ moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, const void*
                            const void* const_v, void* grad_y, float* grad_topk_weights,
                            void* stream);
 
+/* moe_ffn_gate_up_bwd_weight_gather - moe_ffn_gate_up_bwd_weight with the
+ * dispatch permute folded into its expanded-row operand: expanded row r is read as
+ * x[slot(r) / K] through the row -> slot map of the assist info (as
+ * moe_ffn_gate_up_fwd_gather does for the forward), so a step that routes with
+ * moe_route needs no expand_x at all.  Bit for bit that of
+ * moe_ffn_gate_up_bwd_weight on moe_dispatch's expand_x.
+ *  in   grad_gate_up (capacity, 2F) bf16; x (T, H) bf16; assist_info_for_combine
+ *       as written by the routing; ep_recv_counts (E,)
+ *  out  grad_w_gate, grad_w_up (E, F, H) fp32
+ * MOE_ERR_UNSUPPORTED when (T + 1) * H * 2 bytes exceed 2^31 - 16 (31-bit
+ * operand offsets).  One kernel launch. */
+moe_status moe_ffn_gate_up_bwd_weight_gather(const moe_shape* s, const void* grad_gate_up, const void* x,
+                                             const int32_t* assist_info_for_combine, const int32_t* ep_recv_counts,
+                                             float* grad_w_gate, float* grad_w_up, void* stream);
+
 /*
  * moe_grouped_ffn_bwd - backward of moe_grouped_ffn, four grouped GEMMs.
  *   dH = dY Wd_e;  with s = sigmoid(G): dG = dH*U*s*(1 + G(1-s)), dU = dH*G*s
@@ -274,6 +316,21 @@ moe_status moe_ffn_gate_up_bwd_data(const moe_shape* s, const void* grad_gate_up
 moe_status moe_ffn_gate_up_bwd_weight(const moe_shape* s, const void* grad_gate_up,
                                       const void* expand_x, const int32_t* ep_recv_counts,
                                       float* grad_w_gate, float* grad_w_up, void* stream);
+
+/* moe_combine_bwd_fp8 - moe_combine_bwd for the fp8 data gradients: every dY
+ * row also leaves as e4m3 codes with one fp32 scale per 128 columns, the rule
+ * and layout of moe_quant_rows_fp8 applied to the bf16 dY (so the codes equal
+ * that quantiser run on grad_y).
+ *  out  grad_y         (capacity, H) bf16, or NULL when only the codes are needed
+ *  out  grad_yq        (capacity, H) uint8 e4m3 codes
+ *  out  grad_y_scales  (H/128, capacity) fp32, block-major
+ *  other arguments and outputs as moe_combine_bwd; H must be a multiple of 128. */
+moe_status moe_combine_bwd_fp8(const moe_shape* s, const void* grad_out, const void* y, const int32_t* topk_idx,
+                               const float* topk_weights, const int32_t* assist_info_for_combine,
+                               const int32_t* ep_send_counts, const uint8_t* x_active_mask, const void* ori_x,
+                               const void* const_alpha_1, const void* const_alpha_2, const void* const_v,
+                               void* grad_y, uint8_t* grad_yq, float* grad_y_scales, float* grad_topk_weights,
+                               void* stream);
 
 /*
  * moe_dispatch_bwd - gradient with respect to the layer input x (= ori_x).
@@ -562,6 +619,49 @@ moe_status moe_router(int64_t T, int64_t n_ids, int32_t K, int32_t renorm, const
 moe_status moe_router_bwd(int64_t T, int64_t n_ids, int32_t K, int32_t renorm, const float* logits,
                           const int32_t* topk_idx, const float* topk_weights,
                           const float* grad_topk_weights, float* grad_logits, void* stream);
+
+/* Bytes of device workspace that moe_grouped_ffn_fp8 and moe_grouped_ffn_bwd_fp8
+ * need (the e4m3 codes and scales they pass between their GEMMs). */
+moe_status moe_ffn_fp8_workspace_size(const moe_shape* s, size_t* bytes);
+
+/* moe_grouped_ffn_fp8 - moe_grouped_ffn on block-scaled e4m3 operands (the fp8
+ * reading of the Megatron-LM MoE test page's FP8 precision, Added Test Cases):
+ * the gate/up GEMM on the rows moe_dispatch_fp8 quantised, h's codes (one scale
+ * per 128 columns), the down GEMM.  Three launches.
+ *  in   expand_xq (capacity, H) e4m3, x_scales (H/128, capacity) fp32
+ *  in   w[3]      gate, up (E, F, H) and down (E, H, F) weights, moe_fp8_weight
+ *  out  gate_up_save (capacity, 2F), h_act (capacity, F), y (capacity, H) bf16
+ *  ws   workspace >= moe_ffn_fp8_workspace_size bytes
+ * H and F multiples of 128 (MOE_ERR_BAD_SHAPE). */
+moe_status moe_grouped_ffn_fp8(const moe_shape* s, const uint8_t* expand_xq, const float* x_scales,
+                               const moe_fp8_weight* w, const int32_t* ep_recv_counts, void* gate_up_save,
+                               void* h_act, void* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_grouped_ffn_bwd_fp8 - the backward of moe_grouped_ffn_fp8: the fp8 data
+ * gradients on dY's codes (moe_combine_bwd_fp8) with the SwiGLU backward and the
+ * codes of dG|dU fused into the down data gradient, and the weight gradients in
+ * bf16 on the bf16 dY, h, dG|dU and expanded rows.  Four launches.
+ *  in   grad_y (capacity, H) bf16; grad_yq (capacity, H) e4m3, grad_y_scales (H/128, capacity)
+ *  in   expand_x (capacity, H) bf16 (moe_dispatch_fp8's bf16 rows); gate_up_save, h_act
+ *  in   w[3] as for moe_grouped_ffn_fp8 (the transposed codes are read)
+ *  out  grad_gate_up (capacity, 2F) bf16, grad_expand_x (capacity, H) bf16
+ *  out  grad_w_gate, grad_w_up (E, F, H), grad_w_down (E, H, F) fp32
+ *  ws   workspace >= moe_ffn_fp8_workspace_size bytes */
+moe_status moe_grouped_ffn_bwd_fp8(const moe_shape* s, const void* grad_y, const uint8_t* grad_yq,
+                                   const float* grad_y_scales, const void* expand_x, const void* gate_up_save,
+                                   const void* h_act, const moe_fp8_weight* w, const int32_t* ep_recv_counts,
+                                   void* grad_gate_up, void* grad_expand_x, float* grad_w_gate, float* grad_w_up,
+                                   float* grad_w_down, void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_hbm_stream - a reference streaming kernel (not part of the layer): the
+ * measured HBM ceiling that the gather-reduce kernels are compared with.
+ *  mode 0  copy   bytes from src to dst (each byte read once, written once)
+ *  mode 1  read   bytes of src; writes 4096 * 256 16-byte vectors to sink (16 MiB)
+ *  mode 2  write  bytes to dst (a fixed pattern)
+ * 4096 workgroups, each streaming one contiguous range with 16-byte accesses,
+ * eight loads in flight per lane.  bytes must be
+ * a multiple of 16 (MOE_ERR_BAD_SHAPE); mode outside 0..2 gives MOE_ERR_BAD_RANGE. */
+moe_status moe_hbm_stream(int32_t mode, const void* src, void* dst, int64_t bytes, void* sink, void* stream);
 
 #ifdef __cplusplus
 }
