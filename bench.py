@@ -18,7 +18,9 @@ bandwidth against HBM; `cpu_baseline` is the CPU oracle on a bounded sample.
 (T=4096, hidden 7168, ffn 2048, 32 experts, top-8, Zipf-skewed routing, one
 shared expert run as a one-group GEMM over all tokens), `mixtral` (T=8192,
 hidden 4096, ffn 14336, 8 experts, top-2, fp8 e4m3 block-scaled forward and
-data-gradient GEMMs, bf16 weight gradients, int8 combine payload) and
+data-gradient GEMMs, bf16 weight gradients, int8 combine payload; x's codes
+come out of the dispatch copy and dY's out of the combine backward),
+`mixtral_grouped` (the same through the grouped fp8 FFN entries) and
 `combine_stress` (combine, its backward and dispatch backward alone at T=4096,
 hidden 7168, 256 routed + zero + copy + 2 constant experts, 2-D mask, shared
 term; `value` is the combine's GB/s).
@@ -58,6 +60,9 @@ WORKLOADS = {
     "page1_permute": dict(T=8192, H=1536, F=480, E=64, K=8),
     "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
+    # the same step through the grouped fp8 entries of the C ABI (moe_grouped_ffn_fp8,
+    # moe_grouped_ffn_bwd_fp8: each chains its GEMMs and quantisers)
+    "mixtral_grouped": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True, grouped=True),
     # the same layer with the weight gradients in fp8 too (per-128-token operands)
     "mixtral_fp8w": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True, fp8_wgrad=True),
     # the same layer with microscaled e4m3 (E8M0 scale per 32 values, applied by the
@@ -374,6 +379,12 @@ def build_step(name, T_override=None):
         C.append(("moe_route", lambda: dm.moe_route(shape, idx, None, assist, cnt, recv, err, ws)))
         st.extra_calls.append(("moe_dispatch (route + permute, not in the step)",
                                lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
+    elif fp8 and not mx:
+        # x's e4m3 codes and scales come out of the dispatch copy (the bf16 rows
+        # too: the bf16 gate/up weight gradient reads them)
+        xq, xs = z(cap, H, dt=torch.uint8), z(H // 128, cap, dt=f32)
+        C.append(("moe_dispatch_fp8", lambda: dm.moe_dispatch_fp8(shape, x, idx, None, ex, xq, xs, assist, cnt,
+                                                                  recv, err, ws)))
     else:
         C.append(("moe_dispatch", lambda: dm.moe_dispatch(shape, x, idx, None, ex, assist, cnt, recv, err, ws)))
     if int8:
@@ -405,12 +416,14 @@ def build_step(name, T_override=None):
         nrows = recv[-1:]
         wq = [dm.Fp8Weights.quantize(t) for t in (wg, wu, wd)]
         # row scales are column-block major: (C/128, capacity)
-        xq, xs = z(cap, H, dt=torch.uint8), z(H // 128, cap, dt=f32)
         hq, hs = z(cap, F, dt=torch.uint8), z(F // 128, cap, dt=f32)
         dyq, dys = z(cap, H, dt=torch.uint8), z(H // 128, cap, dt=f32)
         dgq, dgs = z(cap, 2 * F, dt=torch.uint8), z(2 * F // 128, cap, dt=f32)
-        C += [
-            ("moe_quant_rows_fp8 (x)", lambda: dm.moe_quant_rows_fp8(ex, xq, xs, nrows)),
+        if cfg.get("grouped"):
+            fws = z(dm.moe_ffn_fp8_workspace_size(shape), dt=torch.uint8)
+            C.append(("moe_grouped_ffn_fp8 (gate/up, h codes, down)", lambda: dm.moe_grouped_ffn_fp8(
+                shape, xq, xs, wq, recv, gus, h, y, fws)))
+        C += [] if cfg.get("grouped") else [
             ("moe_ffn_gate_up_fwd_fp8", lambda: dm.moe_ffn_gate_up_fwd_fp8(
                 shape, xq, xs, wq[0].codes, wq[0].scales, wq[1].codes, wq[1].scales, recv, gus, h)),
             ("moe_quant_rows_fp8 (h)", lambda: dm.moe_quant_rows_fp8(h, hq, hs, nrows)),
@@ -423,7 +436,7 @@ def build_step(name, T_override=None):
             ns = dm.cols_fp8_slots(cap, E)
             cq = {k: (z(d, 128 * ns, dt=torch.uint8), z(ns, d, dt=f32))
                   for k, d in (("x", H), ("h", F), ("dY", H), ("dGU", 2 * F))}
-            i = [n for n, _ in C].index("moe_quant_rows_fp8 (x)")
+            i = [n for n, _ in C].index("moe_dispatch_fp8")
             C.insert(i + 1, ("moe_quant_cols_fp8 (x)", lambda: dm.moe_quant_cols_fp8(ex, recv, *cq["x"])))
             # h's codes come out of the gate/up GEMM itself
             i = [n for n, _ in C].index("moe_ffn_gate_up_fwd_fp8")
@@ -461,8 +474,14 @@ def build_step(name, T_override=None):
     _add_router(st, cfg, T, K, E, dev, cfg.get("renorm", True))
     if cfg.get("forward_only"):
         return st
-    C.append(("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x, None,
-                                                           None, None, gy, gw)))
+    if fp8 and not mx:
+        # dY's e4m3 codes and scales come out of the combine backward (with the
+        # bf16 dY, which the bf16 down weight gradient reads)
+        C.append(("moe_combine_bwd_fp8", lambda: dm.moe_combine_bwd_fp8(
+            shape, gout, y, idx, w, assist, recv, None, x, None, None, None, gy, dyq, dys, gw)))
+    else:
+        C.append(("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x,
+                                                               None, None, None, gy, gw)))
     # backward order: each gather/scatter right after the kernel that produced
     # its input (grad_expand_x goes to dispatch backward before the last
     # weight gradient evicts it from the caches)
@@ -478,7 +497,6 @@ def build_step(name, T_override=None):
         ]
     elif fp8w:
         C += [
-            ("moe_quant_rows_fp8 (dY)", lambda: dm.moe_quant_rows_fp8(gy, dyq, dys, nrows)),
             ("moe_quant_cols_fp8 (dY)", lambda: dm.moe_quant_cols_fp8(gy, recv, *cq["dY"])),
             # dG/dU leave the data gradient as row codes and per-128-token codes
             # only (nothing else reads them)
@@ -489,9 +507,11 @@ def build_step(name, T_override=None):
             ("moe_ffn_gate_up_bwd_data_fp8", lambda: dm.moe_ffn_gate_up_bwd_data_fp8(
                 shape, dgq, dgs, wq[0].codes_t, wq[0].scales, wq[1].codes_t, wq[1].scales, recv, gxe)),
         ]
+    elif fp8 and cfg.get("grouped"):
+        C += [("moe_grouped_ffn_bwd_fp8 (4 GEMMs, dG|dU codes)", lambda: dm.moe_grouped_ffn_bwd_fp8(
+            shape, gy, dyq, dys, ex, gus, h, wq, recv, ggu, gxe, gwg, gwu, gwd, fws))]
     elif fp8:
         C += [
-            ("moe_quant_rows_fp8 (dY)", lambda: dm.moe_quant_rows_fp8(gy, dyq, dys, nrows)),
             # bf16 dG/dU (for the bf16 weight gradient) and their row codes
             ("moe_ffn_down_bwd_data_fp8", lambda: dm.moe_ffn_down_bwd_data_fp8_quant(
                 shape, dyq, dys, wq[2].codes_t, wq[2].scales, gus, recv, ggu, (dgq, dgs))),
@@ -516,6 +536,8 @@ def build_step(name, T_override=None):
     elif cfg.get("gather"):
         C.append(("moe_ffn_gate_up_bwd_weight_gather", lambda: dm.moe_ffn_gate_up_bwd_weight_gather(
             shape, ggu, x, assist, recv, gwg, gwu)))
+    elif cfg.get("grouped"):
+        pass  # the grouped backward entry ends with the gate/up weight gradient
     else:
         C.append(("moe_ffn_gate_up_bwd_weight", lambda: dm.moe_ffn_gate_up_bwd_weight(shape, ggu, ex, recv, gwg,
                                                                                       gwu)))
@@ -605,9 +627,27 @@ def account(st, A):
         for k, d in (("x", H), ("dY", H)):
             nb[f"moe_quant_rows_mx ({k})"] = A * d * 3 + A * d // 32
     elif fp8:
-        nb["moe_quant_rows_fp8 (x)"] = A * H * 3 + A * H // 128 * 4
-        nb["moe_quant_rows_fp8 (h)"] = A * F * 3 + A * F // 128 * 4
-        nb["moe_quant_rows_fp8 (dY)"] = A * H * 3 + A * H // 128 * 4
+        # x's and dY's codes (one byte per element) and scales (fp32 per 128)
+        # leave the dispatch copy and the combine backward
+        q8 = A * H + A * H // 128 * 4
+        nb["moe_dispatch_fp8"] = nb.pop("moe_dispatch") + q8
+        if "moe_combine_bwd" in nb:
+            nb["moe_combine_bwd_fp8"] = nb.pop("moe_combine_bwd") + q8
+        if st.cfg.get("grouped"):
+            # the grouped entries: their GEMMs at the peak of each GEMM's type
+            # (h's row codes are a launch inside the forward entry)
+            fwd = [k for k in fl if "fwd" in k]
+            f_fwd = sum(fl.pop(k)[0] for k in fwd)
+            fl["moe_grouped_ffn_fp8 (gate/up, h codes, down)"] = (f_fwd, PEAK_FP8_TFLOPS)
+            if not fwd_only:
+                bwd = [k for k in list(fl) if "bwd" in k and not k.startswith("moe_grouped") and
+                       not k.startswith("shared")]
+                parts = [fl.pop(k) for k in bwd]
+                f_bwd = sum(f for f, _ in parts)
+                t_bwd = sum(f / pk for f, pk in parts)
+                fl["moe_grouped_ffn_bwd_fp8 (4 GEMMs, dG|dU codes)"] = (f_bwd, f_bwd / t_bwd)
+        else:
+            nb["moe_quant_rows_fp8 (h)"] = A * F * 3 + A * F // 128 * 4
     if fp8w:
         # bf16 in, codes out, one fp32 scale per (128 tokens, column)
         for k, d in (("x", H), ("dY", H)):
@@ -821,6 +861,8 @@ def main():
         "page1_permute": "Triton-distributed benchmark shape, dispatch permute as a kernel of its own",
         "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
+        "mixtral_grouped": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs through the grouped fp8 "
+                           "entries, int8 combine payload",
         "mixtral_mx": "Mixtral-8x7B-style layer, microscaled fp8 e4m3 GEMMs (E8M0 per 32, block-scaled MFMA), "
                       "int8 combine payload",
         "mixtral_fp8w": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs including the weight "

@@ -1452,8 +1452,9 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // quarter fewer operand bytes per FLOP and win for the gate/up data gradient
   // and both weight gradients, and for the down data gradient once its N (= F)
   // is wide.  A narrow down data gradient has few column tiles; 128 x 128
-  // tiles with K step 32 and two stages (36 KB of LDS, three workgroups per
-  // CU) give it more tiles in flight.  The forward GEMMs run 128 x 128 tiles
+  // tiles with K step 32 and three stages (48 KB of LDS, three workgroups per
+  // CU) give it more tiles and more loads in flight (H = 1536, F = 480: 2-3%
+  // faster than two stages; K step 64, or 128 x 256 tiles, 7-9% slower).  The forward GEMMs run 128 x 128 tiles
   // with K step 64 and two stages (two workgroups per CU; three ran the larger
   // MoE layer a third slower) or 256 x 256 tiles (below).  Eight-wave
   // 256 x 256 tiles lost for the backward GEMMs: the SwiGLU backward epilogue
@@ -1469,7 +1470,7 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
     return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
   } else if constexpr (MODE == DOWN_BWD_DATA) {
     if (g.N >= 1024) return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
-    return launch_cfg<MODE, 128, 128, false, 32, 2>(g, s, strm);
+    return launch_cfg<MODE, 128, 128, false, 32, 3>(g, s, strm);
   } else {
     // forward: 256 x 256 tiles of eight waves (wave tiles 128 x 64, one
     // workgroup of 128 KB LDS per CU) do a fifth more work per memory latency
