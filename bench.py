@@ -924,8 +924,8 @@ def main():
                           "achieved": round(gb[dom] / (per[dom] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": round(gb[dom] / (per[dom] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "traffic": None}),
-            "combine": {"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
-                        "frac": kernels["moe_combine"]["frac_hbm"]},
+            "combine": ({"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
+                         "frac": kernels["moe_combine"]["frac_hbm"]} if "moe_combine" in kernels else None),
             "gemm_ms_per_step": round(gemm_ms, 4),
             "gemm_frac_of_mfma_roofline": round(ideal_ms / gemm_ms, 4),
         })

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libmoe.so")
 MOE_FLAG_ID_RANGE = 1
 MOE_FLAG_ID_DUPLICATE = 2
 MOE_FLAG_MASK_NOT_PREFIX = 4
+MOE_FLAG_SYNC_TIMEOUT = 8
 MOE_SLOT_NONE = -1
 MOE_SLOT_COPY = -2
 
@@ -43,6 +44,7 @@ ENTRY_POINTS = (
     "moe_hbm_stream",
     "moe_ffn_gate_up_bwd_weight_gather", "moe_dispatch_fp8", "moe_combine_bwd_fp8",
     "moe_ffn_fp8_workspace_size", "moe_grouped_ffn_fp8", "moe_grouped_ffn_bwd_fp8",
+    "moe_decode_fused_workspace_size", "moe_decode_fused",
 )
 
 
@@ -104,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_fp8_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_grouped_ffn_fp8.argtypes = [S, P, P, W8, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_grouped_ffn_bwd_fp8.argtypes = [S, P, P, P, P, P, P, W8, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_decode_fused_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_decode_fused.argtypes = [S] + [P] * 15 + [ctypes.c_size_t, P]
         L.moe_grouped_ffn_bwd.argtypes = [S] + [P] * 14
         L.moe_ffn_down_bwd_data.argtypes = [S, P, P, P, P, P, P]
         L.moe_ffn_down_bwd_weight.argtypes = [S, P, P, P, P, P]
@@ -327,6 +331,31 @@ def moe_combine(shape, y, topk_idx, topk_weights, assist_info_for_combine, ep_se
         _ptr(shared_expert_x, BF16, "shared_expert_x"), _ptr(ori_x, BF16, "ori_x"),
         _ptr(const_alpha_1, BF16, "const_alpha_1"), _ptr(const_alpha_2, BF16, "const_alpha_2"),
         _ptr(const_v, BF16, "const_v"), _ptr(out, BF16, "out"), _stream(stream)))
+
+
+def moe_decode_fused_workspace_size(shape: MoeShape) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_decode_fused_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def decode_fused_workspace(shape: MoeShape, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for moe_decode_fused (zero before its first use;
+    each call leaves its control words zero again)."""
+    return torch.zeros(moe_decode_fused_workspace_size(shape), dtype=torch.uint8, device=device)
+
+
+def moe_decode_fused(shape, x, topk_idx, topk_weights, x_active_mask, w_gate, w_up, w_down, shared_expert_x,
+                     ori_x, const_alpha_1, const_alpha_2, const_v, out, err_flag, workspace, stream=None):
+    _check_sizes(shape, locals())
+    _check(lib().moe_decode_fused(
+        ctypes.byref(shape), _ptr(x, BF16, "x"), _ptr(topk_idx, I32, "topk_idx"),
+        _ptr(topk_weights, F32, "topk_weights"), _ptr(x_active_mask, U8, "x_active_mask"),
+        _ptr(w_gate, BF16, "w_gate"), _ptr(w_up, BF16, "w_up"), _ptr(w_down, BF16, "w_down"),
+        _ptr(shared_expert_x, BF16, "shared_expert_x"), _ptr(ori_x, BF16, "ori_x"),
+        _ptr(const_alpha_1, BF16, "const_alpha_1"), _ptr(const_alpha_2, BF16, "const_alpha_2"),
+        _ptr(const_v, BF16, "const_v"), _ptr(out, BF16, "out"), _ptr(err_flag, I32, "err_flag"),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_combine,

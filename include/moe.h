@@ -57,6 +57,8 @@ typedef int32_t moe_status;
 #define MOE_FLAG_ID_RANGE 1          /* topk_idx value outside [0, E+Z+C+Q) */
 #define MOE_FLAG_ID_DUPLICATE 2      /* the same id twice in one row of topk_idx */
 #define MOE_FLAG_MASK_NOT_PREFIX 4   /* 1-D x_active_mask with a true after a false */
+#define MOE_FLAG_SYNC_TIMEOUT 8      /* moe_decode_fused: a wait for another workgroup's
+                                        result timed out; the output is not valid */
 
 #define MOE_DTYPE_BF16 0
 
@@ -652,6 +654,43 @@ moe_status moe_grouped_ffn_bwd_fp8(const moe_shape* s, const void* grad_y, const
                                    const void* h_act, const moe_fp8_weight* w, const int32_t* ep_recv_counts,
                                    void* grad_gate_up, void* grad_expand_x, float* grad_w_gate, float* grad_w_up,
                                    float* grad_w_down, void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_decode_fused - NOT ENABLED in this build: after validating its arguments
+ * it returns MOE_ERR_UNSUPPORTED without launching (its first GPU runs did not
+ * complete and the cause is not found).  What it is written to do:
+ * the layer forward of a decode batch in ONE persistent
+ * launch: routing (moe_dispatch's classification and stable expert order), the
+ * gate/up GEMM with the SwiGLU epilogue on x rows gathered through the routing,
+ * the down GEMM and the combine (moe_combine's formula, special experts, mask,
+ * shared term and int8 payload).  The decode regime of the low_latency_combine
+ * API page (Constraints: BS <= 512; Example: the decode flow of quant_mode 2).
+ * out is bit-identical to moe_dispatch -> moe_ffn_gate_up_fwd ->
+ * moe_ffn_down_fwd -> moe_combine on the same inputs (same arithmetic, same
+ * K order).
+ *  in   x (T, H) bf16, topk_idx (T, K) int32, topk_weights (T, K) fp32,
+ *       x_active_mask as for moe_dispatch (NULL when mask_ndim is 0)
+ *  in   w_gate, w_up (E, F, H), w_down (E, H, F) bf16
+ *  in   shared_expert_x, ori_x, const_alpha_1/_2, const_v as for moe_combine
+ *  out  out (T, H) bf16; err_flag (1,) int32: the routing's MOE_FLAG_* bits,
+ *       plus MOE_FLAG_SYNC_TIMEOUT if a wait timed out
+ *  ws   workspace >= moe_decode_fused_workspace_size bytes, ZERO-FILLED before
+ *       its first use with this function; every call leaves its control words
+ *       zero again.  It also holds the call's routing (expert counts, inclusive
+ *       prefix, slot -> row and row -> slot maps) and the h and y rows.  Calls
+ *       that share a workspace must not overlap (one stream).
+ * One cooperative launch of one 512-thread workgroup per CU: workgroup 0 routes,
+ * then all take gate/up, down and combine work items from an atomic counter;
+ * down items wait for their expert's gate/up items and combine items for all
+ * down items (bounded waits).  Requires T <= 512 (MOE_ERR_UNSUPPORTED), H a
+ * multiple of 128 and F of 64 (MOE_ERR_BAD_SHAPE), T*H*2, F*H*2 and
+ * capacity*F*2 below 2^31 bytes (MOE_ERR_UNSUPPORTED); MOE_ERR_HIP when the
+ * cooperative launch fails. */
+moe_status moe_decode_fused_workspace_size(const moe_shape* s, size_t* bytes);
+moe_status moe_decode_fused(const moe_shape* s, const void* x, const int32_t* topk_idx,
+                            const float* topk_weights, const uint8_t* x_active_mask, const void* w_gate,
+                            const void* w_up, const void* w_down, const void* shared_expert_x, const void* ori_x,
+                            const void* const_alpha_1, const void* const_alpha_2, const void* const_v, void* out,
+                            int32_t* err_flag, void* workspace, size_t workspace_bytes, void* stream);
 
 /* moe_hbm_stream - a reference streaming kernel (not part of the layer): the
  * measured HBM ceiling that the gather-reduce kernels are compared with.

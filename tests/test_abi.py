@@ -302,3 +302,38 @@ def test_noalloc_dispatch_checks_before_any_device_call(L):
                 assert st == OK
                 worst = max(worst, n)
     assert worst <= 256 << 10, worst
+
+
+def test_decode_fused_checks_before_any_device_call(L):
+    """moe_decode_fused (the decode regime: at most 512 tokens) validates the shape,
+    its pointers and the workspace before touching the GPU."""
+    Nn = None
+    n = ctypes.c_size_t()
+    dec = dm.make_shape(512, 7168, 8, 32, F=2048)
+    assert L.moe_decode_fused_workspace_size(ctypes.byref(dec), ctypes.byref(n)) == OK
+    cap = dec.capacity
+    # control words, per-expert counters and counts, both maps, h and y rows
+    assert n.value >= cap * (2048 + 7168) * 2 + (512 * 8 + cap) * 4
+    assert L.moe_decode_fused_workspace_size(ctypes.byref(dec), Nn) == NULL_ARG
+
+    def call(s, ws_bytes=1 << 40, **over):
+        args = dict(x=P(), idx=P(), w=P(), mask=Nn, wg=P(), wu=P(), wd=P(), sh=Nn, ori=Nn, a1=Nn, a2=Nn,
+                    cv=Nn, out=P(), err=P(), ws=P())
+        args.update(over)
+        return L.moe_decode_fused(ctypes.byref(s), *args.values(), ws_bytes, Nn)
+
+    for s, want in ((dm.make_shape(513, 7168, 8, 32, F=2048), UNSUPPORTED),   # more than 512 tokens
+                    (dm.make_shape(64, 7168 + 64, 8, 32, F=2048), BAD_SHAPE),  # H not a multiple of 128
+                    (dm.make_shape(64, 7168, 8, 32, F=2048 + 32), BAD_SHAPE),  # F not a multiple of 64
+                    (dm.make_shape(64, 7168, 0, 32, F=2048), BAD_SHAPE)):
+        assert call(s) == want
+        st = L.moe_decode_fused_workspace_size(ctypes.byref(s), ctypes.byref(n))
+        assert st == want
+    s = dm.make_shape(64, 7168, 8, 32, F=2048)
+    assert call(s, err=Nn) == NULL_ARG
+    assert call(s, wd=Nn) == NULL_ARG
+    assert call(dm.make_shape(64, 7168, 8, 32, F=2048, mask_ndim=2)) == NULL_ARG
+    assert call(dm.make_shape(64, 7168, 8, 32, F=2048, copy_expert_num=1)) == NULL_ARG
+    assert L.moe_decode_fused_workspace_size(ctypes.byref(s), ctypes.byref(n)) == OK
+    assert call(s, ws_bytes=n.value - 1) == WORKSPACE
+    assert call(s, ws=Nn) == WORKSPACE
