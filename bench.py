@@ -25,8 +25,11 @@ come out of the dispatch copy and dY's out of the combine backward),
 hidden 7168, 256 routed + zero + copy + 2 constant experts, 2-D mask, shared
 term; `value` is the combine's GB/s).
 
-Besides the per-kernel rates inside the step, the line carries the step time
-statistics of the event pass (mean, std, mean without the three slowest
+The page-1 workloads' timed steps run the weight-gradient GEMMs on a second
+stream (each after the call whose output it reads; the main stream waits for
+them at the end of the step); the larger layers run on one stream.  Besides the per-kernel rates, taken in a one-stream pass with each
+call bracketed by events, the line carries the step time statistics of that
+event pass (mean, std, mean without the three slowest
 steps), the bandwidth-bound kernels re-timed in isolation after a 512 MB write
 that evicts the Infinity Cache (`kernels_hbm_isolated`), and the layer roofline
 fraction (every GEMM at its MFMA peak plus every other kernel at HBM peak,
@@ -55,9 +58,13 @@ WORKLOADS = {
     # the dispatch permute folded into the two GEMMs that read the expanded rows
     # (moe_route, then x read through the row -> slot map by the gate/up forward
     # and the gate/up weight gradient): no expand_x is written
-    "page1": dict(T=8192, H=1536, F=480, E=64, K=8, gather=True),
+    # two_stream: the weight-gradient GEMMs on a second stream (measured on the
+    # page-1 layer: 1.46-1.50 ms against 1.49-1.53 ms on one stream; on the
+    # DeepSeek-V3-proxy and Mixtral-style layers two concurrent GEMMs of that
+    # size lost 3-4 %, so those run on one stream)
+    "page1": dict(T=8192, H=1536, F=480, E=64, K=8, gather=True, two_stream=True),
     # the same layer with the permute as a kernel of its own (moe_dispatch)
-    "page1_permute": dict(T=8192, H=1536, F=480, E=64, K=8),
+    "page1_permute": dict(T=8192, H=1536, F=480, E=64, K=8, two_stream=True),
     "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
     # the same step through the grouped fp8 entries of the C ABI (moe_grouped_ffn_fp8,
@@ -259,6 +266,53 @@ def cpu_baseline_combine(cfg, seconds=10.0, T_sample=512):
                       f"workload (H={H}, E={E}+{Z}+{C}+{Q}, K={K}), {el:.1f} s"}
 
 
+# The step's weight-gradient GEMMs run on a second stream, each after the call
+# whose output it reads (the rest of the backward stays on the main stream, and
+# the main stream waits for both at the end of the step): they read nothing the
+# main stream writes later in the step, and they fill the time the data-gradient
+# chain leaves the matrix cores idle (page 1: 3% shorter steps).
+SIDE_DEPS = {
+    "moe_ffn_down_bwd_weight": ("moe_combine_bwd", "moe_combine_bwd_fp8"),
+    "moe_ffn_down_bwd_weight_fp8": ("moe_quant_cols_fp8 (dY)",),
+    "moe_ffn_gate_up_bwd_weight": ("moe_ffn_down_bwd_data", "moe_ffn_down_bwd_data_fp8", "moe_ffn_down_bwd_data_mx"),
+    "moe_ffn_gate_up_bwd_weight_gather": ("moe_ffn_down_bwd_data",),
+    "moe_ffn_gate_up_bwd_weight_fp8": ("moe_ffn_down_bwd_data_fp8",),
+}
+
+
+def run_calls(calls, side=None):
+    """Launch `calls` in order on torch's current stream; with `side`, the
+    weight-gradient GEMMs go to that stream after the call they depend on, and
+    the current stream waits for them at the end."""
+    import torch
+    if side is None:
+        for _, fn in calls:
+            fn()
+        return
+    main = torch.cuda.current_stream()
+    # an event only after the calls a side call waits for: a marker after every
+    # call costs the step a few microseconds each
+    needed = {d for name, _ in calls for d in SIDE_DEPS.get(name, ())}
+    done, last = {}, None
+    for name, fn in calls:
+        deps = SIDE_DEPS.get(name)
+        dep = next((d for d in deps if d in done), None) if deps else None
+        if dep is None:
+            fn()
+            if name in needed:
+                ev = torch.cuda.Event()
+                ev.record(main)
+                done[name] = ev
+        else:
+            side.wait_event(done[dep])
+            with torch.cuda.stream(side):
+                fn()
+            last = torch.cuda.Event()
+            last.record(side)
+    if last is not None:
+        main.wait_event(last)
+
+
 class Step:
     """The C-entry calls of one fwd+bwd step of a workload (name, thunk), in order,
     plus calls timed outside the step (fp8 weight quantisation)."""
@@ -267,6 +321,7 @@ class Step:
         self.calls, self.config, self.cfg = [], {}, {}
         self.recv = self.err = self.counts = None
         self.dtype = "bf16"
+        self.two_stream = False
         self.extra_calls = []
 
 
@@ -359,6 +414,7 @@ def build_step(name, T_override=None):
     gwg, gwu, gwd = z(E, F, H, dt=f32), z(E, F, H, dt=f32), z(E, H, F, dt=f32)
     st = Step()
     st.recv, st.err, st.counts = recv, err, cnt
+    st.two_stream = bool(cfg.get("two_stream", False))
     C = st.calls
     sy = sdx = None
     if int8:
@@ -655,18 +711,17 @@ def account(st, A):
     return fl, nb
 
 
-def time_calls(calls, steps):
-    """Mean wall time (ms) of running `calls` in order, from HIP events on torch's
-    current stream, after one untimed pass."""
+def time_calls(calls, steps, side=None):
+    """Mean wall time (ms) of running `calls` (with `side`: the step's two-stream
+    schedule, see run_calls), from HIP events on torch's current stream, after one
+    untimed pass."""
     import torch
-    for _, fn in calls:
-        fn()
+    run_calls(calls, side)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
-        for _, fn in calls:
-            fn()
+        run_calls(calls, side)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
@@ -701,18 +756,20 @@ def hbm_ceiling(nbytes=1 << 30, reps=5):
 
 def token_sweep(workload, tokens, steps):
     """fwd and fwd+bwd ms and TFLOP/s of the workload at other token counts (the
-    columns of the Triton-distributed benchmark page's summary table)."""
+    columns of the Triton-distributed benchmark page's summary table), with the
+    step's schedule."""
     import torch
     rows = []
     for T in tokens:
         st = build_step(workload, T)
+        side = torch.cuda.Stream() if st.two_stream else None
         for _ in range(2):
             for _, fn in st.calls:
                 fn()
         torch.cuda.synchronize()
         A = int(st.recv[-1].item())
         nf = [n for n, _ in st.calls].index("moe_combine") + 1
-        fb = time_calls(st.calls, steps)
+        fb = time_calls(st.calls, steps, side)
         fw = time_calls(st.calls[:nf], steps)
         H, F = st.config["H"], st.config["F"]
         rows.append({"T": T, "routed_rows": A, "fwd_ms": round(fw, 4), "fwd_bwd_ms": round(fb, 4),
@@ -751,9 +808,10 @@ def main():
     st = build_step(args.workload, args.tokens)
     calls = st.calls
 
+    side = torch.cuda.Stream() if st.two_stream else None  # default priority
+
     def step():
-        for _, fn in calls:
-            fn()
+        run_calls(calls, side)
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -908,6 +966,9 @@ def main():
                               f"H={H}, F={F} SwiGLU, "
                               f"E={E} experts on one GPU, top-{K}",
                   "T": T, "H": H, "F": F, "E": E, "K": K, "routed_rows": A, "flop_per_step": total_flops}
+        if st.two_stream:
+            config["schedule"] = ("weight-gradient GEMMs on a second stream (per-kernel times and "
+                                  "step_ms_events: one stream, each call bracketed by events)")
         if st.counts is not None:
             c = st.counts.cpu().numpy()
             config["expert_rows_max_over_mean"] = round(float(c.max() / max(c.mean(), 1e-9)), 3)
