@@ -1029,6 +1029,37 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
                                   reinterpret_cast<u32x4*>(dst + (row0 + row) * ldd + c8));
     }
   };
+  // SwiGLU backward: the saved G and U columns [c0, c0 + W) of the tile's rows
+  // into LDS (G at smem, U at smem + BM * P, row pitch P).  A thread's 16-byte
+  // loads go out in batches of eight before the batch's first LDS write, so
+  // their latencies overlap (a load, wait, write loop pays one memory round
+  // trip per chunk); rows past the expert's end repeat its last row, columns
+  // past N its last eight.
+  auto stage_gu = [&](auto WV, auto PV, int64_t c0) {
+    constexpr int W = decltype(WV)::value, P = decltype(PV)::value;
+    constexpr int kChunks = 2 * BM * (W / 8), kBatch = 8;
+    static_assert(kChunks % (kBatch * kThreads) == 0, "whole batches of eight chunks per thread");
+#pragma unroll 1
+    for (int b0 = 0; b0 < kChunks; b0 += kBatch * kThreads) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int idx = b0 + q * kThreads + tid;
+        const int t = idx / (BM * (W / 8)), w = idx % (BM * (W / 8));
+        const int row = w / (W / 8), c8 = (w % (W / 8)) * 8;
+        const int rr = row < rows_valid ? row : rows_valid - 1;
+        const int64_t col = c0 + c8 < g.N ? c0 + c8 : g.N - 8;
+        v[q] = *reinterpret_cast<const uint4*>(g.aux + (row0 + rr) * 2 * g.F + (t ? g.F : 0) + col);
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int idx = b0 + q * kThreads + tid;
+        const int t = idx / (BM * (W / 8)), w = idx % (BM * (W / 8));
+        const int row = w / (W / 8), c8 = (w % (W / 8)) * 8;
+        *reinterpret_cast<uint4*>(smem + t * BM * P + row * P + c8) = v[q];
+      }
+    }
+  };
   // MX codes of 32 staged bf16 values (one 32-block of an output row): 32 codes
   // at dst, the scale byte in the step-major word layout (block c32 of the row)
   auto mx_block = [&](const bf16_t* src, int64_t row, int64_t c32, uint8_t* dst) {
@@ -1119,14 +1150,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
 #pragma unroll 1
     for (int pc = 0; pc < WN; ++pc) {
       const int64_t c0 = n0 + pc * WC;
-      for (int v = tid; v < 2 * BM * (WC / 8); v += kThreads) {
-        const int t = v / (BM * (WC / 8)), w = v % (BM * (WC / 8));
-        const int row = w / (WC / 8), c8 = (w % (WC / 8)) * 8;
-        const int rr = row < rows_valid ? row : rows_valid - 1;
-        const int64_t col = c0 + c8 < g.N ? c0 + c8 : g.N - 8;
-        *reinterpret_cast<uint4*>(smem + t * BM * CPH + row * CPH + c8) =
-            *reinterpret_cast<const uint4*>(g.aux + (row0 + rr) * 2 * g.F + (t ? g.F : 0) + col);
-      }
+      stage_gu(std::integral_constant<int, WC>(), std::integral_constant<int, CPH>(), c0);
       __syncthreads();
       if (wn == pc) {
 #pragma unroll
@@ -1255,14 +1279,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     // through LDS; dG and dU replace them in place and leave as 16-byte rows.
     bf16_t* tg = smem;
     bf16_t* tu = smem + BM * CP;
-    for (int v = tid; v < 2 * BM * (BN / 8); v += kThreads) {
-      const int t = v / (BM * (BN / 8)), w = v % (BM * (BN / 8));
-      const int row = w / (BN / 8), c8 = (w % (BN / 8)) * 8;
-      const int rr = row < rows_valid ? row : rows_valid - 1;
-      const int64_t col = n0 + c8 < g.N ? n0 + c8 : g.N - 8;
-      *reinterpret_cast<uint4*>(smem + t * BM * CP + row * CP + c8) =
-          *reinterpret_cast<const uint4*>(g.aux + (row0 + rr) * 2 * g.F + (t ? g.F : 0) + col);
-    }
+    stage_gu(std::integral_constant<int, BN>(), std::integral_constant<int, CP>(), n0);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TI; ++i)
