@@ -783,8 +783,11 @@ def token_sweep(workload, tokens, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # defaults: about 30 ms of warm-up steps at the page-1 size, so the timed
+    # steps start at the GPU's working clocks (after the idle input generation,
+    # the first few steps of a run measured 2-4% slower than the following ones)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="page1", choices=list(WORKLOADS))
     ap.add_argument("--tokens", type=int, default=None, help="override T")
     ap.add_argument("--no-cpu-baseline", action="store_true")

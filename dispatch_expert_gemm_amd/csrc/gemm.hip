@@ -157,6 +157,8 @@ template <int W>
 __device__ __forceinline__ int lds_offw(int r, int c) { return r * W + ((c ^ swzw<W>(r)) << 3); }
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
+// weight gradients: fp32 output staged through LDS for full-line stores
+constexpr bool kStagedWgrad = true;
 
 // Compile-time shape of one kernel instance: BM x BN output tile.
 template <int MODE, int BM, int BN, bool FP8, int BK, int S_, int WM_ = 2, int WN_ = 2>
@@ -1392,6 +1394,44 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
           g.sc[tile_m * 2 * g.F + col + 1] = m1 > 0.f ? __fdiv_rn(m1, 448.0f) : 1.0f;
         }
       }
+    }
+  } else if constexpr (kStagedWgrad && WM == 2 && (BM / 2) * (BN + 4) * 4 <= C::kSmem * 2) {
+    // weight gradients, fp32, through LDS one wave row (BM/2 output rows) at a
+    // time: the waves of that row write their accumulators as 16-byte runs,
+    // then every wave stores whole output rows, 64 lanes x 16 bytes per row
+    // piece, so each store covers full cache lines (the direct stores below
+    // write 32-byte pieces of 32 rows per instruction)
+    constexpr int PW = BN + 4;  // floats per staged row (16 bytes of padding)
+    float* st = reinterpret_cast<float*>(smem);
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              *reinterpret_cast<float4*>(st + (i * 32 + ln) * PW + tn(j, t)) =
+                  make_float4(acc[i][j][4 * t], acc[i][j][4 * t + 1], acc[i][j][4 * t + 2], acc[i][j][4 * t + 3]);
+      }
+      __syncthreads();
+      constexpr int kRuns = BN / 4;  // 16-byte runs per row
+      for (int v = tid; v < (BM / 2) * kRuns; v += kThreads) {
+        const int r = v / kRuns, c4 = (v % kRuns) * 4;
+        const int m = half * (BM / 2) + r;
+        const int64_t n = n0 + c4;
+        if (m >= rows_valid || n >= g.N) continue;
+        const float4 val = *reinterpret_cast<const float4*>(st + r * PW + c4);
+        if constexpr (MODE == DOWN_BWD_W) {
+          *reinterpret_cast<float4*>(g.W0 + (int64_t)e * g.M * g.N + (row0 + m) * g.N + n) = val;
+        } else {
+          const int64_t jrow = row0 + m;
+          if (jrow < g.F) *reinterpret_cast<float4*>(g.W0 + (int64_t)e * g.F * g.N + jrow * g.N + n) = val;
+          else *reinterpret_cast<float4*>(g.W1 + (int64_t)e * g.F * g.N + (jrow - g.F) * g.N + n) = val;
+        }
+      }
+      __syncthreads();
     }
   } else {
     // weight gradients, fp32: 16-byte stores of four consecutive columns
