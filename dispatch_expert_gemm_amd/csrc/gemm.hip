@@ -190,8 +190,9 @@ struct Cfg {
   static constexpr int CPH = BN / WN + 8;  // pitch of one wave column's staging
   // gate/up forward beyond the operand LDS: h and G in one pass, then U
   static constexpr bool kEpiGU2 = MODE == GATE_UP_FWD && !kEpiOnePass && 2 * BM * CP * 2 <= 160 * 1024;
+  // (weight gradients: half the fp32 tile, 16 bytes of padding per row)
   static constexpr int kEpi =
-      KGROUP ? 0
+      KGROUP ? (BM / 2) * (BN + 4) * 2
              : (MODE == GATE_UP_FWD ? (kEpiOnePass ? 3 : (kEpiGU2 ? 2 : 1)) * BM * CP
                                     : (MODE == DOWN_BWD_DATA ? (kEpiOnePass ? 2 * BM * CP : 2 * BM * CPH) : BM * CP));
   static constexpr int kSmem = cmax(kMain, kEpi);
@@ -1540,7 +1541,17 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
     return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, true>(g, s, strm);
   } else if constexpr (FP8) {
     return launch_cfg<MODE, 128, 128, true>(g, s, strm);
-  } else if constexpr (MODE == GATE_UP_BWD_DATA || MODE == DOWN_BWD_W || MODE == GATE_UP_BWD_W) {
+  } else if constexpr (MODE == GATE_UP_BWD_W) {
+    // a wide gate/up weight gradient takes eight-wave 256 x 256 tiles (a third
+    // fewer operand bytes per FLOP than two 128 x 256 workgroups; measured
+    // 5% faster at 2F x H = 4096 x 7168 and 28672 x 4096); an expert grid of
+    // few such tiles (page 1: 4 x 6) stays on 128 x 256.  The down weight
+    // gradient measured 2% faster on them at H x F = 7168 x 2048 but 5% slower
+    // at 4096 x 14336, and stays on 128 x 256.
+    const int64_t t256 = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+    if (t256 >= 64) return launch_cfg<MODE, 256, 256, false, 32, 3, 2, 4>(g, s, strm);
+    return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
+  } else if constexpr (MODE == GATE_UP_BWD_DATA || MODE == DOWN_BWD_W) {
     return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);
   } else if constexpr (MODE == DOWN_BWD_DATA) {
     if (g.N >= 1024) return launch_cfg<MODE, 128, 256, false, 32, 3>(g, s, strm);

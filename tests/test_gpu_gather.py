@@ -68,6 +68,8 @@ WGRAD_CASES = {
     "one_token": dict(T=1, H=128, F=64, E=4, K=2),
     "page1_shape": dict(T=8192, H=1536, F=480, E=64, K=8),
     "k16_long_experts": dict(T=1500, H=512, F=256, E=20, K=16),
+    # 2F x H = 2048 x 2048: the eight-wave 256 x 256 weight-gradient tiles
+    "wide_256_tiles": dict(T=301, H=2048, F=1024, E=2, K=2),
 }
 
 

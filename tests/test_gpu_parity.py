@@ -98,10 +98,10 @@ FFN_CASES = {
     # order, 13 row-tile slots = one full group of 8 and a partial one); the
     # down data gradient takes the 128 x 256 tiles (N = F = 1024)
     "wide_ffn": dict(T=700, H=256, F=1024, E=3, K=2),
-    # wide weight gradients: gate/up weight-gradient blocks of 12 row tiles
-    # (a full and a partial group of 8), down weight-gradient blocks of 8 x 3
-    # tiles; grouped order for the gate/up forward, down forward and gate/up
-    # data gradient (24, 32 and 16 column tiles)
+    # wide weight gradients: the gate/up weight gradient on eight-wave
+    # 256 x 256 tiles (a 12 x 16 tile grid per expert), down weight-gradient
+    # blocks of 8 x 3 tiles; grouped order for the gate/up forward, down
+    # forward and gate/up data gradient (24, 32 and 16 column tiles)
     "wide_wgrad": dict(T=600, H=4096, F=1536, E=2, K=1),
     # enough tiles for the 256 x 256 eight-wave forward tiles: the gate/up
     # forward with a K tail (H = 1096) and a partial last column tile (F = 224)
