@@ -135,10 +135,14 @@ def _layer_step(run, shared_x=None, accum=None):
     return out, gy, gw, ggu, gxe, gwg, gwu, gwd, gx
 
 
-def test_page1_benchmark_shape_full_size():
-    """T=8192, H=1536, F=480, E=64, K=8: the benchmark's workload and launch shapes."""
-    print("[full] page1 T=8192", flush=True)
-    inp = wl.layer_inputs(**wl.WORKLOADS["page1"], seed=0)
+@pytest.mark.parametrize("T", [2048, 4096, 8192])
+def test_page1_benchmark_shape_full_size(T):
+    """T tokens at H=1536, F=480, E=64, K=8: the benchmark's workload and launch
+    shapes at the token counts of the Triton-distributed page's summary table
+    (1024 tokens is a layer parity case of its own)."""
+    print(f"[full] page1 T={T}", flush=True)
+    cfg = dict(wl.WORKLOADS["page1"], T=T)
+    inp = wl.layer_inputs(**cfg, seed=0)
     run = Run(inp)
     run.dispatch()
     r = orc.route(inp["topk_idx"], inp["E"])
@@ -146,7 +150,7 @@ def test_page1_benchmark_shape_full_size():
     check_equal("ep_recv_counts", run.d.ep_recv_counts.cpu().numpy(), r.ep_recv_counts)
     check_equal("slot2row", run.d.slot2row(r.T, r.K).cpu().numpy(), r.slot2row)
     check_equal("row2slot", run.d.row2slot(r.T, r.K)[:r.A].cpu().numpy(), r.row2slot)
-    assert r.counts.sum() == 8192 * 8
+    assert r.counts.sum() == T * 8
     rng = np.random.default_rng(11)
     rows = _sample(rng, r.A, 512)
     xf = orc.bf16_to_f32(inp["x"])
