@@ -880,7 +880,9 @@ def main():
     step_ms = sorted(ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(args.steps))
     kept = step_ms[:-3] if len(step_ms) > 3 else step_ms
     step_stats = {"mean": round(float(np.mean(step_ms)), 4), "std": round(float(np.std(step_ms)), 4),
-                  "mean_without_3_slowest": round(float(np.mean(kept)), 4)}
+                  "mean_without_3_slowest": round(float(np.mean(kept)), 4),
+                  # a run whose step times spread more than 5% of their mean is flagged
+                  "stable": bool(np.std(step_ms) <= 0.05 * np.mean(step_ms))}
     # the bandwidth-bound kernels once more in isolation, after writing a buffer
     # larger than the 256 MB Infinity Cache, so their inputs come from HBM
     isolated = {}

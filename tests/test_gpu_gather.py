@@ -70,6 +70,9 @@ WGRAD_CASES = {
     "k16_long_experts": dict(T=1500, H=512, F=256, E=20, K=16),
     # 2F x H = 2048 x 2048: the eight-wave 256 x 256 weight-gradient tiles
     "wide_256_tiles": dict(T=301, H=2048, F=1024, E=2, K=2),
+    # the same tiles with a partial last row tile (2F = 1984) and an 8-column
+    # last column tile (H = 2056)
+    "wide_256_ragged": dict(T=257, H=2056, F=992, E=3, K=2),
 }
 
 
