@@ -228,7 +228,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int WM = C::WM, WN = C::WN, kThreads = C::kThreads;
-  static_assert(!FP8 || kThreads == 256, "the fp8 loop is written for four waves");
+  static_assert(!FP8 || kThreads == 256 || MX, "the fp32-scaled fp8 and int8 loops are written for four waves");
   const int wm = wave / WN, wn = wave % WN;
 
   const int64_t nb = gridDim.x;
@@ -1095,6 +1095,17 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
     g.smx[((c32 / 4) * g.rowsA + row) * 4 + (c32 & 3)] = (uint8_t)(ex + 127);
   };
+  // MX row codes of the staged h (BM rows x BN/2 columns, pitch CP): BN/64
+  // 32-blocks per row, one (row, 32-block) per thread at a time (F is a
+  // multiple of 128, so the tile's columns are all inside h)
+  auto mx_h = [&](const bf16_t* th) {
+    constexpr int NB = BN / 64;
+    for (int p = tid; p < BM * NB; p += kThreads) {
+      const int row = p / NB, b = p % NB;
+      if (row < rows_valid)
+        mx_block(th + row * CP + 32 * b, row0 + row, (n0 + 32 * b) / 32, g.qmx + (row0 + row) * g.F + n0 + 32 * b);
+    }
+  };
   if constexpr (MODE == GATE_UP_FWD && C::kEpiGU2) {
     // h and G side by side, then U
     bf16_t* th = smem;
@@ -1119,6 +1130,10 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     __syncthreads();
     store_tile(th, g.C0 + n0, g.F, g.F - n0);
     store_tile_nt(tg, g.C1 + n0, 2 * g.F, g.F - n0);
+    if constexpr (FP8) {
+      static_assert(!FP8 || MX, "the per-token fp8 codes of h are written by the 128 x 128 tiles only");
+      if (g.qmx) mx_h(th);
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -1224,14 +1239,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     store_tile_nt(tg, g.C1 + n0, 2 * g.F, g.F - n0);
     store_tile_nt(tu, g.C1 + g.F + n0, 2 * g.F, g.F - n0);
     if constexpr (FP8) {
-      if (g.qmx) {
-        // MX row codes of h: the tile's BN/2 = 64 columns are two 32-blocks of
-        // each row, one (row, block) per thread
-        static_assert(BN / 2 * BM / 32 == kThreads, "one (row, 32-block) of h per thread");
-        const int row = tid >> 1, b = tid & 1;
-        if (row < rows_valid)
-          mx_block(th + row * CP + 32 * b, row0 + row, (n0 + 32 * b) / 32, g.qmx + (row0 + row) * g.F + n0 + 32 * b);
-      }
+      if (g.qmx) mx_h(th);
       if (g.qc) {
         // per-128-token e4m3 codes of the staged bf16 h (the tile's rows are
         // one token slot): thread t takes the column pair 2 (t%32), +1 over
@@ -1536,6 +1544,15 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
   // runs four wave-column passes, and the weight gradients get too few tiles
   // per expert block.
   if constexpr (MX) {
+    // eight-wave 256 x 256 tiles for the forward GEMMs and the gate/up data
+    // gradient when they make at least one full round over the CUs (the MX MFMA
+    // applies the block scales itself, so the wave tile needs no partial sums)
+    if constexpr (MODE == GATE_UP_FWD || MODE == DOWN_FWD || MODE == GATE_UP_BWD_DATA) {
+      const int64_t cols256 = MODE == GATE_UP_FWD ? 128 : 256;
+      const int64_t ncols = MODE == GATE_UP_FWD ? g.F : g.N;
+      const int64_t t256 = (s->capacity / 256 + s->num_experts) * ((ncols + cols256 - 1) / cols256);
+      if (t256 >= kCUs) return launch_cfg<MODE, 256, 256, true, 64, 2, 2, 4, false, true>(g, s, strm);
+    }
     return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, false, true>(g, s, strm);
   } else if constexpr (I8) {
     return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, true>(g, s, strm);

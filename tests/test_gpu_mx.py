@@ -75,6 +75,10 @@ MX_CASES = {
     "empty_experts": dict(T=40, H=128, F=128, E=12, K=1),
     "wide": dict(T=700, H=1024, F=640, E=3, K=2),
     "top1_768": dict(T=2496, H=768, F=768, E=4, K=1),
+    # enough tiles for the eight-wave 256 x 256 MX tiles in the gate/up forward,
+    # down forward and gate/up data gradient (a half last column tile at
+    # H = 2176)
+    "w256_ragged": dict(T=4096, H=2176, F=1024, E=4, K=2),
 }
 
 
