@@ -20,10 +20,12 @@ shared expert run as a one-group GEMM over all tokens), `mixtral` (T=8192,
 hidden 4096, ffn 14336, 8 experts, top-2, fp8 e4m3 block-scaled forward and
 data-gradient GEMMs, bf16 weight gradients, int8 combine payload; x's codes
 come out of the dispatch copy and dY's out of the combine backward),
-`mixtral_grouped` (the same through the grouped fp8 FFN entries) and
+`mixtral_grouped` (the same through the grouped fp8 FFN entries),
 `combine_stress` (combine, its backward and dispatch backward alone at T=4096,
 hidden 7168, 256 routed + zero + copy + 2 constant experts, 2-D mask, shared
-term; `value` is the combine's GB/s).
+term; `value` is the combine's GB/s) and `page1_rank_share` (what one of the
+benchmark page's four ranks computes: 16 local experts receiving 65,536 rows,
+modelled as top-8 of 16 over 8192 tokens).
 
 The page-1 workloads' timed steps run the weight-gradient GEMMs on a second
 stream (each after the call whose output it reads; the main stream waits for
@@ -65,6 +67,10 @@ WORKLOADS = {
     "page1": dict(T=8192, H=1536, F=480, E=64, K=8, gather=True, two_stream=True),
     # the same layer with the permute as a kernel of its own (moe_dispatch)
     "page1_permute": dict(T=8192, H=1536, F=480, E=64, K=8, two_stream=True),
+    # one of page 1's four ranks: 16 local experts receiving 65,536 rows (top-8
+    # of 16 over 8192 tokens gives the same rows per expert, 4096), the a2a
+    # replaced by the on-device permute
+    "page1_rank_share": dict(T=8192, H=1536, F=480, E=16, K=8, gather=True, two_stream=True),
     "dsv3_proxy": dict(T=4096, H=7168, F=2048, E=32, K=8, zipf=1.2, shared=True),
     "mixtral": dict(T=8192, H=4096, F=14336, E=8, K=2, fp8=True),
     # the same step through the grouped fp8 entries of the C ABI (moe_grouped_ffn_fp8,
@@ -922,6 +928,8 @@ def main():
     descr = {
         "page1": "Triton-distributed benchmark shape, dispatch permute folded into the gate/up GEMMs' row loads",
         "page1_permute": "Triton-distributed benchmark shape, dispatch permute as a kernel of its own",
+        "page1_rank_share": "one of the Triton-distributed benchmark's four ranks: 16 local experts, 65,536 "
+                            "received rows, dispatch permute folded into the gate/up GEMMs' row loads",
         "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
         "mixtral_grouped": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs through the grouped fp8 "
@@ -1011,8 +1019,9 @@ def main():
         res["kernels_hbm_isolated"] = isolated
     if extra:
         res["outside_step"] = extra
-    if args.workload == "page1":
+    if args.workload in ("page1", "page1_rank_share"):
         res["context"] = {"page1_fwd_bwd_ms_4_nvidia_gpus_T8192": 5.488}
+    if args.workload == "page1":
         if not args.no_sweep and not args.tokens:
             log("[bench] page-1 rows at 1024, 2048, 4096 tokens")
             res["token_rows"] = token_sweep("page1", (1024, 2048, 4096), max(args.steps // 2, 5))

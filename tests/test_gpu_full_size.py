@@ -159,6 +159,21 @@ def test_page1_benchmark_shape_full_size(T):
     _check_sampled_layer(inp, run, r, *res, rng)
 
 
+def test_page1_rank_share_full_size():
+    """One of the benchmark page's four ranks: 16 experts receiving 65,536 rows
+    (top-8 of 16 over 8192 tokens: 4096 rows per expert, bigger GEMM groups than
+    the 64-expert layer), H=1536, F=480."""
+    print("[full] page1 rank share E=16", flush=True)
+    inp = wl.layer_inputs(T=8192, H=1536, F=480, E=16, K=8, seed=0)
+    run = Run(inp)
+    run.dispatch()
+    r = orc.route(inp["topk_idx"], inp["E"])
+    check_equal("ep_recv_counts", run.d.ep_recv_counts.cpu().numpy(), r.ep_recv_counts)
+    check_equal("row2slot", run.d.row2slot(r.T, r.K)[:r.A].cpu().numpy(), r.row2slot)
+    res = _layer_step(run)
+    _check_sampled_layer(inp, run, r, *res, np.random.default_rng(12))
+
+
 def test_combine_stress_full_size():
     """T=4096, H=7168, K=8, 256 routed + 1 zero + 1 copy + 2 constant experts,
     2-D mask with 10% false, shared_expert_x: combine, its backward and dispatch
