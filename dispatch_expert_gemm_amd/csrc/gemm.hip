@@ -228,7 +228,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int WM = C::WM, WN = C::WN, kThreads = C::kThreads;
-  static_assert(!FP8 || kThreads == 256 || MX, "the fp32-scaled fp8 and int8 loops are written for four waves");
+  static_assert(!FP8 || kThreads == 256 || MX || I8, "the fp32-scaled fp8 loop is written for four waves");
   const int wm = wave / WN, wn = wave % WN;
 
   const int64_t nb = gridDim.x;
@@ -1130,10 +1130,9 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     __syncthreads();
     store_tile(th, g.C0 + n0, g.F, g.F - n0);
     store_tile_nt(tg, g.C1 + n0, 2 * g.F, g.F - n0);
-    if constexpr (FP8) {
-      static_assert(!FP8 || MX, "the per-token fp8 codes of h are written by the 128 x 128 tiles only");
+    // (the per-token fp8 codes of h, qc, come from the 128 x 128 fp8 tiles only)
+    if constexpr (MX)
       if (g.qmx) mx_h(th);
-    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -1555,6 +1554,11 @@ moe_status launch(GemmArgs& g, const moe_shape* s, hipStream_t strm) {
     }
     return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, false, true>(g, s, strm);
   } else if constexpr (I8) {
+    // as for bf16: a decode-sized batch streams each expert's gate/up weights
+    // once on 256 x 256 tiles (integer sums, the scales applied after the loop)
+    if constexpr (MODE == GATE_UP_FWD)
+      if (s->T * s->K <= 256 * (int64_t)s->num_experts)
+        return launch_cfg<MODE, 256, 256, true, 64, 2, 2, 4, true>(g, s, strm);
     return launch_cfg<MODE, 128, 128, true, 64, 2, 2, 2, true>(g, s, strm);
   } else if constexpr (FP8) {
     return launch_cfg<MODE, 128, 128, true>(g, s, strm);
