@@ -29,10 +29,11 @@ modelled as top-8 of 16 over 8192 tokens).
 
 The page-1 workloads' timed steps run the weight-gradient GEMMs on a second
 stream (each after the call whose output it reads; the main stream waits for
-them at the end of the step); the larger layers run on one stream.  Besides the per-kernel rates, taken in a one-stream pass with each
-call bracketed by events, the line carries the step time statistics of that
-event pass (mean, std, mean without the three slowest
-steps), the bandwidth-bound kernels re-timed in isolation after a 512 MB write
+them at the end of the step); the larger layers run on one stream.  Besides
+the per-kernel rates, taken in a one-stream pass with each call bracketed by
+events, the line carries the step time statistics of that event pass (mean,
+std, mean without the three slowest steps, and whether the spread stays within
+5% of the mean), the bandwidth-bound kernels re-timed in isolation after a 512 MB write
 that evicts the Infinity Cache (`kernels_hbm_isolated`), and the layer roofline
 fraction (every GEMM at its MFMA peak plus every other kernel at HBM peak,
 over the measured step time).
