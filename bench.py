@@ -111,18 +111,38 @@ def gemm_flops(A, H, F):
     }
 
 
-def gemm_bytes(name, A, H, F, E):
-    """Algorithmic HBM bytes of a forward grouped GEMM: every expert's weights once, its
-    input rows and its outputs (decode-sized batches read the weights far more than rows);
-    int8 GEMMs read 1-byte weights and rows plus one fp32 scale per row and channel."""
+def gemm_bytes(name, A, H, F, E, T=0):
+    """Algorithmic HBM bytes of a bf16 grouped GEMM: every expert's weights once, its
+    input rows (A routed rows, each counted once, also when gathered from x), its
+    saved operands and its outputs; weight gradients are written in fp32.  int8
+    GEMMs read 1-byte weights and rows plus one fp32 scale per row and channel.
+    The shared expert's GEMMs are the same with A = T rows and one expert.  Other
+    8-bit GEMMs: 0 (they are set against the MFMA peak only)."""
+    if name.startswith("shared "):
+        base = name[len("shared "):]
+        if base.startswith("moe_grouped_ffn_bwd"):
+            return sum(gemm_bytes(n, T, H, F, 1) for n in (
+                "moe_ffn_down_bwd_data", "moe_ffn_down_bwd_weight", "moe_ffn_gate_up_bwd_data",
+                "moe_ffn_gate_up_bwd_weight"))
+        return gemm_bytes(base, T, H, F, 1)
     if name == "moe_ffn_gate_up_fwd_int8":
         return E * 2 * F * (H + 4) + A * (H + 4) + A * 3 * F * 2
     if name == "moe_ffn_down_fwd_int8":
         return E * H * (F + 4) + A * (F + 4) + A * H * 2
+    if name.endswith(("_fp8", "_mx", "_int8")) or "fp8" in name:
+        return 0
     if name.startswith("moe_ffn_gate_up_fwd"):
         return E * 2 * F * H * 2 + A * H * 2 + A * 3 * F * 2
     if name.startswith("moe_ffn_down_fwd"):
         return E * H * F * 2 + A * F * 2 + A * H * 2
+    if name == "moe_ffn_down_bwd_data":      # dY, W_down, saved G|U in; dG|dU out
+        return A * H * 2 + E * H * F * 2 + A * 2 * F * 2 * 2
+    if name == "moe_ffn_down_bwd_weight":    # dY, h in; dW_down (fp32) out
+        return A * H * 2 + A * F * 2 + E * H * F * 4
+    if name == "moe_ffn_gate_up_bwd_data":   # dG|dU, W_gate, W_up in; dX out
+        return A * 2 * F * 2 + E * 2 * F * H * 2 + A * H * 2
+    if name.startswith("moe_ffn_gate_up_bwd_weight"):  # dG|dU, x rows in; dW_gate, dW_up (fp32) out
+        return A * 2 * F * 2 + A * H * 2 + E * 2 * F * H * 4
     return 0
 
 
@@ -872,12 +892,22 @@ def main():
     fl, nb = account(st, A)
     combine_only = st.cfg.get("combine_only", False)
     kernels = {}
+    # the GEMMs' algorithmic bytes: each GEMM is set against the roof it meets
+    # first, its FLOPs at the MFMA peak or its bytes at the HBM peak
+    Tq, Hq, Fq, Kq, Eq = st.shape_info
+    gb = {k: gemm_bytes(k, A, Hq, Fq, Eq, Tq) for k in fl}
     for name, ms in per.items():
         rec = {"ms": round(ms, 4)}
         if name in fl:
             f, pk = fl[name]
             rec["TFLOP/s"] = round(f / (ms * 1e-3) / 1e12, 1)
             rec["frac_mfma"] = round(rec["TFLOP/s"] / pk, 4)
+            if gb.get(name):
+                rec["GB/s"] = round(gb[name] / (ms * 1e-3) / 1e9, 1)
+                rec["frac_hbm"] = round(rec["GB/s"] / PEAK_HBM_GBS, 4)
+                t_mfma, t_hbm = f / (pk * 1e12), gb[name] / (PEAK_HBM_GBS * 1e9)
+                rec["bound"] = "hbm" if t_hbm > t_mfma else "mfma"
+                rec["frac_roofline"] = round(max(t_mfma, t_hbm) / (ms * 1e-3), 4)
         if nb.get(name) is not None:
             rec["GB/s"] = round(nb[name] / (ms * 1e-3) / 1e9, 1)
             rec["frac_hbm"] = round(rec["GB/s"] / PEAK_HBM_GBS, 4)
@@ -917,12 +947,9 @@ def main():
             isolated[name] = {"ms": round(ms, 4), "GB/s": round(nbi[name] / (ms * 1e-3) / 1e9, 1),
                               "frac_hbm": round(nbi[name] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         del flush
-    # layer roofline: every GEMM at its MFMA peak (or, at decode batch sizes, at the
-    # HBM rate its expert weights allow, whichever is slower) and every other
-    # kernel at HBM peak
+    # layer roofline: every GEMM at its MFMA peak or at the HBM rate its
+    # algorithmic bytes allow, whichever is slower, and every other kernel at HBM peak
     fwd_only = st.cfg.get("forward_only", False)
-    Tq, Hq, Fq, Kq, Eq = st.shape_info
-    gb = {k: gemm_bytes(k, A, Hq, Fq, Eq) for k in fl} if fwd_only else {}
     t_ideal_ms = (sum(max(f / (pk * 1e12), gb.get(k, 0) / (PEAK_HBM_GBS * 1e9)) for k, (f, pk) in fl.items())
                   + sum(b / (PEAK_HBM_GBS * 1e9) for b in nb.values() if b is not None)) * 1e3
     T, H, F, E, K = (st.config[k] for k in ("T", "H", "F", "E", "K"))
@@ -976,6 +1003,7 @@ def main():
         achieved = dflop / (per[dom] * 1e-3) / 1e12
         gemm_ms = sum(per[k] for k in fl)
         ideal_ms = sum(f / (pk * 1e12) for f, pk in fl.values()) * 1e3
+        roof_ms = sum(max(f / (pk * 1e12), gb.get(k, 0) / (PEAK_HBM_GBS * 1e9)) for k, (f, pk) in fl.items()) * 1e3
         config = {"workload": f"MoE layer {'forward' if fwd_only else 'fwd+bwd'}, {descr}: T={T} tokens, "
                               f"H={H}, F={F} SwiGLU, "
                               f"E={E} experts on one GPU, top-{K}",
@@ -990,20 +1018,22 @@ def main():
             "value": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
             "unit": "TFLOP/s",
             "config": config,
-            "roofline": ({"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                          "peak": dpeak, "unit": "TFLOP/s",
-                          "frac": round(achieved / dpeak, 4),
-                          "traffic": measured_traffic(dom) if args.workload == "page1" and not args.tokens
-                          else None} if not fwd_only else
-                         {"bound": "hbm", "kernel": dom,
+            # the dominant kernel against the roof it meets first (its FLOPs at the
+            # MFMA peak of its type, or its algorithmic bytes at the HBM peak)
+            "roofline": ({"bound": "hbm", "kernel": dom,
                           "achieved": round(gb[dom] / (per[dom] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                          "unit": "GB/s", "frac": round(gb[dom] / (per[dom] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                          "traffic": None}),
+                          "unit": "GB/s", "frac": round(gb[dom] / (per[dom] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                         if kernels[dom].get("bound") == "hbm" else
+                         {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                          "peak": dpeak, "unit": "TFLOP/s", "frac": round(achieved / dpeak, 4)}),
             "combine": ({"GB/s": kernels["moe_combine"]["GB/s"], "peak": PEAK_HBM_GBS,
                          "frac": kernels["moe_combine"]["frac_hbm"]} if "moe_combine" in kernels else None),
             "gemm_ms_per_step": round(gemm_ms, 4),
             "gemm_frac_of_mfma_roofline": round(ideal_ms / gemm_ms, 4),
+            "gemm_frac_of_roofline": round(roof_ms / gemm_ms, 4),
         })
+        res["roofline"]["traffic"] = (measured_traffic(dom) if args.workload == "page1" and not args.tokens
+                                      else None)
     res["layer_roofline_frac"] = round(t_ideal_ms / ms_per_step, 4)
     res["step_ms_events"] = step_stats
     if fwd_ms is not None:

@@ -167,6 +167,43 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in r.stderr
 
 
+def test_bench_gemm_roofs_at_the_page1_shape():
+    """The benchmark's algorithmic bytes of the six bf16 GEMMs at the page-1 shape
+    (A = 65,536 routed rows, H = 1536, F = 480, E = 64), written out by hand per
+    operand, and the roof each meets first (FLOPs at 2.5 PFLOP/s against bytes at
+    8 TB/s)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    A, H, F, E, T = 65536, 1536, 480, 64, 8192
+    mb = 1e6
+    want = {
+        # weights (bf16) + x rows + h, G, U out
+        "moe_ffn_gate_up_fwd_gather": (64 * 960 * 1536 * 2 + A * 1536 * 2 + A * 1440 * 2, "mfma"),
+        # W_down + h rows + y out
+        "moe_ffn_down_fwd": (64 * 1536 * 480 * 2 + A * 480 * 2 + A * 1536 * 2, "hbm"),
+        # dY rows + W_down + saved G|U in, dG|dU out
+        "moe_ffn_down_bwd_data": (A * 1536 * 2 + 64 * 1536 * 480 * 2 + 2 * A * 960 * 2, "hbm"),
+        # dY, h rows in, fp32 dW_down out
+        "moe_ffn_down_bwd_weight": (A * 1536 * 2 + A * 480 * 2 + 64 * 1536 * 480 * 4, "hbm"),
+        # dG|dU rows + both weights in, dX out
+        "moe_ffn_gate_up_bwd_data": (A * 960 * 2 + 64 * 960 * 1536 * 2 + A * 1536 * 2, "mfma"),
+        # dG|dU, x rows in, fp32 dW_gate, dW_up out
+        "moe_ffn_gate_up_bwd_weight_gather": (A * 960 * 2 + A * 1536 * 2 + 64 * 960 * 1536 * 4, "hbm"),
+    }
+    flops = {k: (4 if "gate_up" in k else 2) * A * H * F for k in want}
+    for k, (nbytes, roof) in want.items():
+        got = bench.gemm_bytes(k, A, H, F, E, T)
+        assert got == nbytes, (k, got / mb, nbytes / mb)
+        t_mfma, t_hbm = flops[k] / 2.5e15, got / 8e12
+        assert ("hbm" if t_hbm > t_mfma else "mfma") == roof, k
+    # 8-bit GEMMs other than the int8 forward ones are set against the MFMA peak only
+    assert bench.gemm_bytes("moe_ffn_down_bwd_data_fp8", A, H, F, E, T) == 0
+    # the shared expert: the same counts with T rows and one expert
+    assert bench.gemm_bytes("shared moe_ffn_down_fwd", A, H, F, E, T) == bench.gemm_bytes(
+        "moe_ffn_down_fwd", T, H, F, 1)
+
+
 def test_router_rejects_bad_arguments_before_launch(L):
     Nn = None
     # (T, n_ids, K, renorm): K in (0, min(16, n_ids)], n_ids in [1, 4096], renorm 0/1
