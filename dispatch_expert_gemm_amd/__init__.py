@@ -1078,7 +1078,10 @@ class _MoELayerFn(torch.autograd.Function):
         cap, H, F, T, K = shape.capacity, shape.H, shape.F, shape.T, shape.K
         dev = x.device
         gy = torch.empty((cap, H), dtype=BF16, device=dev)
-        gw = torch.empty((T, K), dtype=F32, device=dev)
+        # routing weights that need no gradient: the combine backward writes grad_y
+        # alone and reads no y row (the fp8 variant always writes both)
+        need_gw = ctx.needs_input_grad[1] or ctx.fused8
+        gw = torch.empty((T, K), dtype=F32, device=dev) if need_gw else None
         if ctx.fused8:
             gyq = torch.empty((cap, H), dtype=U8T, device=dev)
             gys = torch.empty((H // 128, cap), dtype=F32T, device=dev)

@@ -61,8 +61,12 @@ struct CombineBwdArgs {
 // Q8: also the e4m3 codes of the bf16 dY rows, by the rule of the row quantiser
 // on the stored bf16 values (the 16 lanes of an aligned group hold one
 // 128-column block: H is a multiple of 128); dy may then be NULL.
-template <int KMAX, bool ONE_PASS, bool Q8 = false>
+// PART: 0 both outputs; 1 grad_y only (no y row is read); 2 grad_topk_weights
+// only (no grad_y row is written).  Each part computes its outputs exactly as the
+// whole kernel does, so the two halves run on different streams give its bits.
+template <int KMAX, bool ONE_PASS, bool Q8 = false, int PART = 0>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
+  constexpr bool kDY = PART != 2, kDW = PART != 1;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (t >= a.T) return;
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   // int8 payload: one read of the rows when they fit in one chunk (as in combine)
   constexpr bool one_pass = ONE_PASS;
   uint4 pre[ONE_PASS ? U : 1][KMAX];
-  if constexpr (ONE_PASS) {
+  if constexpr (ONE_PASS && kDW) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (lane + u * kWave < Hv) {
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
           if (si.code[k] >= 0) pre[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + lane + u * kWave]);
       }
     int8_params_regs<KMAX, U>(pre, si, lane, Hv, qinv, qsc);
-  } else if (a.qpay) {
+  } else if (kDW && a.qpay) {
     int8_params(y, si, Hv, lane, qinv, qsc);
   }
   float dot[KMAX];
@@ -99,12 +103,13 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
       const int64_t v = v0 + u * kWave;
       if (v < Hv) {
         dr[u] = dout[t * Hv + v];
+        if constexpr (kDW)
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-          if (si.code[k] >= 0) {
-            if constexpr (one_pass) raw[u][k] = pre[u][k];
-            else raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
-          }
+          for (int k = 0; k < KMAX; ++k)
+            if (si.code[k] >= 0) {
+              if constexpr (one_pass) raw[u][k] = pre[u][k];
+              else raw[u][k] = ld_row(&y[(int64_t)si.code[k] * Hv + v]);
+            }
       }
     }
 #pragma unroll
@@ -114,23 +119,25 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
         float d[8];
         unpack8(dr[u], d);
         float ox[8];
-        if (si.any_ori) unpack8(a.ori[t * Hv + v], ox);
+        if (kDW && si.any_ori) unpack8(a.ori[t * Hv + v], ox);
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
           const int c = si.code[k];
           if (c == MOE_SLOT_NONE) continue;
-          float f[8];
-          if (c >= 0) {
-            unpack8(raw[u][k], f);
-            if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
-          } else {
-            special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
-          }
-          float p = dot[k];
+          if constexpr (kDW) {
+            float f[8];
+            if (c >= 0) {
+              unpack8(raw[u][k], f);
+              if (a.qpay) int8_qdq(f, qinv[k], qsc[k]);
+            } else {
+              special_value(c, ox, a.a1, a.a2, a.cv, Hv, v, f);
+            }
+            float p = dot[k];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) p = p + f[i] * d[i];
-          dot[k] = p;
-          if (c >= 0) {
+            for (int i = 0; i < 8; ++i) p = p + f[i] * d[i];
+            dot[k] = p;
+          }
+          if (kDY && c >= 0) {
             float g[8];
             const float wk = si.w[k];
 #pragma unroll
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
   // fixed-shape butterfly over the wave: the same order for every launch
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
-    if (k < a.K) {
+    if (kDW && k < a.K) {
       float p = dot[k];
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) p = p + __shfl_xor(p, o, kWave);
@@ -326,12 +333,14 @@ moe_status combine_bwd_impl(const moe_shape* s, const void* grad_out, const void
   const bool q8 = grad_yq != nullptr;
   if (q8 && s->H % 128 != 0) return MOE_ERR_BAD_SHAPE;
   if (q8 && s->capacity * (s->H / 128) * 4 >= (int64_t)0x7ffffff0) return MOE_ERR_UNSUPPORTED;
+  // bf16: either output may be left out (NULL), not both; the fp8 variant
+  // writes grad_topk_weights always
+  const int part = q8 ? 0 : (!grad_y ? 2 : (!grad_topk_weights ? 1 : 0));
+  if (!q8 && !grad_y && !grad_topk_weights) return MOE_ERR_NULL_ARG;
   if (s->T == 0) return MOE_OK;
-  MOE_NEED(y, s->capacity * s->H);
-  if (!q8) MOE_NEED(grad_y, s->capacity * s->H);
+  if (part != 1) MOE_NEED(y, s->capacity * s->H);
   if (q8) MOE_NEED(grad_y_scales, s->capacity * (s->H / 128));
-  if (!grad_out || !topk_idx || !topk_weights || !assist || !ep_send_counts ||
-      !grad_topk_weights)
+  if (!grad_out || !topk_idx || !topk_weights || !assist || !ep_send_counts || (q8 && !grad_topk_weights))
     return MOE_ERR_NULL_ARG;
   if (s->mask_ndim > 0 && !x_active_mask) return MOE_ERR_NULL_ARG;
   st = check_special(s, ori_x, const_alpha_1, const_alpha_2, const_v);
@@ -360,6 +369,15 @@ moe_status combine_bwd_impl(const moe_shape* s, const void* grad_out, const void
       hipLaunchKernelGGL((k_combine_bwd<KM, true, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
     else if (q8)
       hipLaunchKernelGGL((k_combine_bwd<KM, false, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+    else if (part == 1)  // grad_y alone reads no y row, so it needs no int8 amax either
+      hipLaunchKernelGGL((k_combine_bwd<KM, false, false, 1>), token_grid(s->T), dim3(256), 0, as_stream(stream),
+                         a);
+    else if (part == 2 && one)
+      hipLaunchKernelGGL((k_combine_bwd<KM, true, false, 2>), token_grid(s->T), dim3(256), 0, as_stream(stream),
+                         a);
+    else if (part == 2)
+      hipLaunchKernelGGL((k_combine_bwd<KM, false, false, 2>), token_grid(s->T), dim3(256), 0, as_stream(stream),
+                         a);
     else if (one)
       hipLaunchKernelGGL((k_combine_bwd<KM, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
     else

@@ -255,6 +255,11 @@ moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* topk_id
  * The gradient of shared_expert_x is grad_out itself; the copy/const terms'
  * gradient to ori_x is added by moe_dispatch_bwd.  With comm_quant_mode == 2 the
  * dot product uses the int8 round trip of y, as the forward did.
+ * Either output may be NULL (not both: MOE_ERR_NULL_ARG), and the call then
+ * computes the other alone, bit for bit as the call with both: grad_y alone
+ * reads no y row (y may be NULL; for routing weights that need no gradient, about
+ * half the bytes and time), grad_topk_weights alone writes no grad_y row.
+ * One kernel launch.
  */
 moe_status moe_combine_bwd(const moe_shape* s, const void* grad_out, const void* y,
                            const int32_t* topk_idx, const float* topk_weights,

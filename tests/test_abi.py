@@ -115,6 +115,9 @@ def test_entry_points_reject_bad_arguments_before_launch(L):
     sq = S(const_expert_num=2)
     assert L.moe_combine(ctypes.byref(sq), P(), P(), P(), P(), P(), Nn, Nn, P(), P(), Nn, P(), P(), Nn) == NULL_ARG
     assert L.moe_combine_bwd(ctypes.byref(sq), P(), P(), P(), P(), P(), P(), Nn, P(), P(), P(), Nn, P(), P(), Nn) == NULL_ARG
+    # combine backward: either output may be left out, not both; y only with the weights' gradient
+    assert L.moe_combine_bwd(sp, P(), P(), P(), P(), P(), P(), Nn, Nn, Nn, Nn, Nn, Nn, Nn, Nn) == NULL_ARG
+    assert L.moe_combine_bwd(sp, P(), Nn, P(), P(), P(), P(), Nn, Nn, Nn, Nn, Nn, Nn, P(), Nn) == NULL_ARG
     assert L.moe_dispatch_bwd(ctypes.byref(sq), P(), P(), P(), P(), Nn, P(), Nn, Nn, P(), Nn) == NULL_ARG
     assert L.moe_dispatch_bwd(ctypes.byref(sc), P(), P(), P(), P(), Nn, Nn, Nn, Nn, P(), Nn) == NULL_ARG
     # FFN: F must be a positive multiple of 32

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import dispatch_expert_gemm_amd as dm
 import moe_workloads as wl
 import oracle as orc
 from gpu_util import (DEV, RHO_CHAIN, ULPS_KERNEL, Run, bf, check_close, check_equal, contraction_mag, dev,
@@ -189,6 +190,35 @@ def test_combine_backward(name):
     assert np.all(f32(gw)[r.slot2row.reshape(r.T, r.K) == -1] == 0)
 
 
+@pytest.mark.parametrize("qpay", [False, True])
+@pytest.mark.parametrize("name", list(COMBINE_CASES))
+def test_combine_backward_halves_equal_the_whole(name, qpay):
+    """moe_combine_bwd with one output left out (NULL) computes the other alone,
+    bit for bit as the call with both (grad_y alone without reading y), also with
+    the int8 payload, whose round trip of y only the weights' gradient sees."""
+    inp = _combine_inputs(name)
+    print(f"[combine bwd halves] case={name} qpay={qpay}", flush=True)
+    run = Run(inp)
+    if qpay:
+        run.shape.comm_quant_mode = 2
+    run.dispatch()
+    g, yb = bf(inp["grad_out"]), bf(inp["y"])
+    gy, gw = run.combine_bwd(g, y=yb)
+    args = (run.shape, g, None, run.idx, run.w, run.d.assist_info_for_combine, run.d.ep_recv_counts, run.mask,
+            run.x, run.a1, run.a2, run.cv)
+    gy1 = torch.zeros_like(gy)
+    dm.moe_combine_bwd(*args, gy1, None)                 # grad_y alone, y not passed
+    gw2 = torch.full_like(gw, float("nan"))
+    a2 = list(args)
+    a2[2] = yb
+    dm.moe_combine_bwd(*a2, None, gw2)                   # grad_topk_weights alone
+    torch.cuda.synchronize()
+    assert torch.equal(gy1, gy), "grad_y alone differs from the whole call"
+    assert torch.equal(gw2, gw), "grad_topk_weights alone differs from the whole call"
+    with pytest.raises(dm.MoeError):
+        dm.moe_combine_bwd(*a2, None, None)
+
+
 @pytest.mark.parametrize("name", list(COMBINE_CASES))
 def test_dispatch_backward_bit_exact(name):
     inp = _combine_inputs(name)
@@ -351,6 +381,28 @@ def test_autograd_layer_and_determinism():
         # returned in bf16 (the weights' dtype): one more rounding of the fp32 result
         check_close(k, f32(t), orc.round_bf16(b[k]), mag=m[k], rho=RHO_CHAIN)
     assert torch.equal(res[0][6].view(torch.int16), bf(inp["grad_out"]).cpu().view(torch.int16))
+
+
+def test_autograd_layer_without_routing_weight_gradient():
+    """topk_weights that need no gradient: the layer's backward asks the combine
+    backward for grad_y alone, and every other gradient is bit for bit the same."""
+    import dispatch_expert_gemm_amd as dm
+    inp = wl.layer_inputs(seed=9, **LAYER_CASES["special_mask"])
+    print("[autograd] routing weights without gradient", flush=True)
+    res = []
+    for need_w in (True, False):
+        x = bf(inp["x"]).requires_grad_(True)
+        w = dev(inp["topk_weights"]).requires_grad_(need_w)
+        wg, wu, wd = (bf(inp[k]).requires_grad_(True) for k in ("w_gate", "w_up", "w_down"))
+        out = dm.moe_layer(x, dev(inp["topk_idx"]), w, wg, wu, wd, x_active_mask=dev(inp["mask"]).bool(),
+                           const_alpha_1=bf(inp["const_alpha_1"]), const_alpha_2=bf(inp["const_alpha_2"]),
+                           const_v=bf(inp["const_v"]), zero_expert_num=1, copy_expert_num=1, const_expert_num=2)
+        out.backward(bf(inp["grad_out"]))
+        torch.cuda.synchronize()
+        assert (w.grad is not None) == need_w
+        res.append([t.detach().cpu().view(torch.int16) for t in (out, x.grad, wg.grad, wu.grad, wd.grad)])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
 
 
 def test_autograd_layer_shared_expert():
