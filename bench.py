@@ -135,10 +135,10 @@ def gemm_bytes(name, A, H, F, E, T=0):
         return E * 2 * F * H * 2 + A * H * 2 + A * 3 * F * 2
     if name.startswith("moe_ffn_down_fwd"):
         return E * H * F * 2 + A * F * 2 + A * H * 2
-    if name == "moe_ffn_down_bwd_data":      # dY, W_down, saved G|U in; dG|dU out
-        return A * H * 2 + E * H * F * 2 + A * 2 * F * 2 * 2
-    if name == "moe_ffn_down_bwd_weight":    # dY, h in; dW_down (fp32) out
-        return A * H * 2 + A * F * 2 + E * H * F * 4
+    if name.startswith("moe_ffn_down_bwd_data"):  # dY (or grad_out rows + row weights), W_down, G|U in; dG|dU out
+        return A * H * 2 + E * H * F * 2 + A * 2 * F * 2 * 2 + (A * 4 if name.endswith("_gather") else 0)
+    if name.startswith("moe_ffn_down_bwd_weight"):  # dY (or grad_out rows + row weights), h in; dW_down out
+        return A * H * 2 + A * F * 2 + E * H * F * 4 + (A * 4 if name.endswith("_gather") else 0)
     if name == "moe_ffn_gate_up_bwd_data":   # dG|dU, W_gate, W_up in; dX out
         return A * 2 * F * 2 + E * 2 * F * H * 2 + A * H * 2
     if name.startswith("moe_ffn_gate_up_bwd_weight"):  # dG|dU, x rows in; dW_gate, dW_up (fp32) out
@@ -155,6 +155,8 @@ def bytes_moved(name, T, H, F, K, A, E):
         return A * H * s + T * K * 12 + T * H * s
     if name == "moe_combine_bwd":
         return T * H * s + 2 * A * H * s + T * K * 16
+    if name == "moe_combine_bwd_weights":  # grad_out, y rows, weights, maps in; dw, row weights out
+        return T * H * s + A * H * s + T * K * 16 + A * 4
     if name == "moe_dispatch_bwd":
         return A * H * s + T * H * s + T * K * 8
     return None
@@ -302,7 +304,8 @@ SIDE_DEPS = {
     "moe_ffn_down_bwd_weight": ("moe_combine_bwd", "moe_combine_bwd_fp8"),
     "moe_ffn_down_bwd_weight_fp8": ("moe_quant_cols_fp8 (dY)",),
     "moe_ffn_gate_up_bwd_weight": ("moe_ffn_down_bwd_data", "moe_ffn_down_bwd_data_fp8", "moe_ffn_down_bwd_data_mx"),
-    "moe_ffn_gate_up_bwd_weight_gather": ("moe_ffn_down_bwd_data",),
+    "moe_ffn_down_bwd_weight_gather": ("moe_combine_bwd_weights",),
+    "moe_ffn_gate_up_bwd_weight_gather": ("moe_ffn_down_bwd_data", "moe_ffn_down_bwd_data_gather"),
     "moe_ffn_gate_up_bwd_weight_fp8": ("moe_ffn_down_bwd_data_fp8",),
 }
 
@@ -562,6 +565,12 @@ def build_step(name, T_override=None):
         # bf16 dY, which the bf16 down weight gradient reads)
         C.append(("moe_combine_bwd_fp8", lambda: dm.moe_combine_bwd_fp8(
             shape, gout, y, idx, w, assist, recv, None, x, None, None, None, gy, dyq, dys, gw)))
+    elif cfg.get("gather"):
+        # the combine backward folded into the down GEMMs' operand loads: no
+        # grad_y rows, only the routing weights' gradient and each row's weight
+        roww = z(cap, dt=f32)
+        C.append(("moe_combine_bwd_weights", lambda: dm.moe_combine_bwd_weights(
+            shape, gout, y, idx, w, assist, recv, None, x, None, None, None, gw, roww)))
     else:
         C.append(("moe_combine_bwd", lambda: dm.moe_combine_bwd(shape, gout, y, idx, w, assist, recv, None, x,
                                                                None, None, None, gy, gw)))
@@ -601,6 +610,14 @@ def build_step(name, T_override=None):
             ("moe_ffn_down_bwd_weight", lambda: dm.moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)),
             ("moe_ffn_gate_up_bwd_data_fp8", lambda: dm.moe_ffn_gate_up_bwd_data_fp8(
                 shape, dgq, dgs, wq[0].codes_t, wq[0].scales, wq[1].codes_t, wq[1].scales, recv, gxe)),
+        ]
+    elif cfg.get("gather"):
+        C += [
+            ("moe_ffn_down_bwd_data_gather", lambda: dm.moe_ffn_down_bwd_data_gather(
+                shape, gout, assist, roww, wd, gus, recv, ggu)),
+            ("moe_ffn_down_bwd_weight_gather", lambda: dm.moe_ffn_down_bwd_weight_gather(
+                shape, gout, assist, roww, h, recv, gwd)),
+            ("moe_ffn_gate_up_bwd_data", lambda: dm.moe_ffn_gate_up_bwd_data(shape, ggu, wg, wu, recv, gxe)),
         ]
     else:
         C += [
@@ -698,6 +715,10 @@ def account(st, A):
         fl["moe_ffn_gate_up_fwd_gather"] = fl.pop("moe_ffn_gate_up_fwd")
         if "moe_ffn_gate_up_bwd_weight" in fl:
             fl["moe_ffn_gate_up_bwd_weight_gather"] = fl.pop("moe_ffn_gate_up_bwd_weight")
+            fl["moe_ffn_down_bwd_data_gather"] = fl.pop("moe_ffn_down_bwd_data")
+            fl["moe_ffn_down_bwd_weight_gather"] = fl.pop("moe_ffn_down_bwd_weight")
+            nb["moe_combine_bwd_weights"] = bytes_moved("moe_combine_bwd_weights", T, H, F, K, A, E)
+            del nb["moe_combine_bwd"]
         nb["moe_route"] = nb.pop("moe_dispatch") - T * H * 2 - A * H * 2   # no rows moved
     if int8:
         # int8 rows and one fp32 scale per row written, the smooth scales read once

@@ -45,6 +45,7 @@ ENTRY_POINTS = (
     "moe_ffn_gate_up_bwd_weight_gather", "moe_dispatch_fp8", "moe_combine_bwd_fp8",
     "moe_ffn_fp8_workspace_size", "moe_grouped_ffn_fp8", "moe_grouped_ffn_bwd_fp8",
     "moe_decode_fused_workspace_size", "moe_decode_fused",
+    "moe_combine_bwd_weights", "moe_ffn_down_bwd_data_gather", "moe_ffn_down_bwd_weight_gather",
 )
 
 
@@ -114,6 +115,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_gate_up_bwd_data.argtypes = [S, P, P, P, P, P, P]
         L.moe_ffn_gate_up_bwd_weight.argtypes = [S, P, P, P, P, P, P]
         L.moe_ffn_gate_up_bwd_weight_gather.argtypes = [S] + [P] * 7
+        L.moe_combine_bwd_weights.argtypes = [S] + [P] * 14
+        L.moe_ffn_down_bwd_data_gather.argtypes = [S] + [P] * 8
+        L.moe_ffn_down_bwd_weight_gather.argtypes = [S] + [P] * 7
         L.moe_dispatch_bwd.argtypes = [S] + [P] * 10
         I64 = ctypes.c_int64
         L.moe_quant_rows_fp8.argtypes = [I64, I64, P, P, P, P, P]
@@ -370,6 +374,42 @@ def moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_
         _ptr(const_alpha_1, BF16, "const_alpha_1"), _ptr(const_alpha_2, BF16, "const_alpha_2"),
         _ptr(const_v, BF16, "const_v"), _ptr(grad_y, BF16, "grad_y"),
         _ptr(grad_topk_weights, F32, "grad_topk_weights"), _stream(stream)))
+
+
+def moe_combine_bwd_weights(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_combine,
+                            ep_send_counts, x_active_mask, ori_x, const_alpha_1, const_alpha_2, const_v,
+                            grad_topk_weights, row_weights, stream=None):
+    _check_sizes(shape, locals())
+    _need(row_weights, shape.capacity, "row_weights")
+    _check(lib().moe_combine_bwd_weights(
+        ctypes.byref(shape), _ptr(grad_out, BF16, "grad_out"), _ptr(y, BF16, "y"),
+        _ptr(topk_idx, I32, "topk_idx"), _ptr(topk_weights, F32, "topk_weights"),
+        _ptr(assist_info_for_combine, I32, "assist"), _ptr(ep_send_counts, I32, "ep_send_counts"),
+        _ptr(x_active_mask, U8, "x_active_mask"), _ptr(ori_x, BF16, "ori_x"),
+        _ptr(const_alpha_1, BF16, "const_alpha_1"), _ptr(const_alpha_2, BF16, "const_alpha_2"),
+        _ptr(const_v, BF16, "const_v"), _ptr(grad_topk_weights, F32, "grad_topk_weights"),
+        _ptr(row_weights, F32, "row_weights"), _stream(stream)))
+
+
+def moe_ffn_down_bwd_data_gather(shape, grad_out, assist_info_for_combine, row_weights, w_down, gate_up_save,
+                                 ep_recv_counts, grad_gate_up, stream=None):
+    _check_sizes(shape, locals())
+    _need(row_weights, shape.capacity, "row_weights")
+    _check(lib().moe_ffn_down_bwd_data_gather(
+        ctypes.byref(shape), _ptr(grad_out, BF16, "grad_out"), _ptr(assist_info_for_combine, I32, "assist"),
+        _ptr(row_weights, F32, "row_weights"), _ptr(w_down, BF16, "w_down"),
+        _ptr(gate_up_save, BF16, "gate_up_save"), _ptr(ep_recv_counts, I32, "ep_recv_counts"),
+        _ptr(grad_gate_up, BF16, "grad_gate_up"), _stream(stream)))
+
+
+def moe_ffn_down_bwd_weight_gather(shape, grad_out, assist_info_for_combine, row_weights, h_act, ep_recv_counts,
+                                   grad_w_down, stream=None):
+    _check_sizes(shape, locals())
+    _need(row_weights, shape.capacity, "row_weights")
+    _check(lib().moe_ffn_down_bwd_weight_gather(
+        ctypes.byref(shape), _ptr(grad_out, BF16, "grad_out"), _ptr(assist_info_for_combine, I32, "assist"),
+        _ptr(row_weights, F32, "row_weights"), _ptr(h_act, BF16, "h_act"),
+        _ptr(ep_recv_counts, I32, "ep_recv_counts"), _ptr(grad_w_down, F32, "grad_w_down"), _stream(stream)))
 
 
 def moe_combine_bwd_fp8(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_combine, ep_send_counts,
@@ -1077,7 +1117,9 @@ class _MoELayerFn(torch.autograd.Function):
         grad_out = grad_out.contiguous()
         cap, H, F, T, K = shape.capacity, shape.H, shape.F, shape.T, shape.K
         dev = x.device
-        gy = torch.empty((cap, H), dtype=BF16, device=dev)
+        # grad_y rows exist on the 8-bit paths only (the bf16 down GEMMs read
+        # grad_out through the map)
+        gy = torch.empty((cap, H), dtype=BF16, device=dev) if ctx.fp8 else None
         # routing weights that need no gradient: the combine backward writes grad_y
         # alone and reads no y row (the fp8 variant always writes both)
         need_gw = ctx.needs_input_grad[1] or ctx.fused8
@@ -1087,6 +1129,12 @@ class _MoELayerFn(torch.autograd.Function):
             gys = torch.empty((H // 128, cap), dtype=F32T, device=dev)
             moe_combine_bwd_fp8(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
                                 gy, gyq, gys, gw)
+        elif not ctx.fp8:
+            # bf16: the combine backward folded into the down GEMMs (grad_out rows
+            # read through the map, each row's routing weight applied in the GEMM)
+            roww = torch.empty((cap,), dtype=F32, device=dev)
+            moe_combine_bwd_weights(shape, grad_out, y if need_gw else None, topk_idx, topk_weights, assist, recv,
+                                    mask, x, a1, a2, cv, gw, roww)
         else:
             moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
                             gy, gw)
@@ -1139,8 +1187,8 @@ class _MoELayerFn(torch.autograd.Function):
             moe_ffn_gate_up_bwd_data_fp8(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)
             del dgq, dgs
         else:
-            moe_ffn_down_bwd_data(shape, gy, w_down, gus, recv, ggu)
-            moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
+            moe_ffn_down_bwd_data_gather(shape, grad_out, assist, roww, w_down, gus, recv, ggu)
+            moe_ffn_down_bwd_weight_gather(shape, grad_out, assist, roww, h, recv, gwd)
             moe_ffn_gate_up_bwd_data(shape, ggu, w_gate, w_up, recv, gx_exp)
         accum = None
         s_grads = (None, None, None)

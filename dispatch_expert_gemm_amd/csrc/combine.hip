@@ -56,22 +56,30 @@ struct CombineBwdArgs {
   uint2* dyq;
   float* dys;
   int64_t capacity;
+  // optional: the routing weight of every routed row, roww[row] = w[slot] (the
+  // per-row scales of the gathered down-backward GEMMs)
+  float* roww;
 };
 
 // Q8: also the e4m3 codes of the bf16 dY rows, by the rule of the row quantiser
 // on the stored bf16 values (the 16 lanes of an aligned group hold one
 // 128-column block: H is a multiple of 128); dy may then be NULL.
 // PART: 0 both outputs; 1 grad_y only (no y row is read); 2 grad_topk_weights
-// only (no grad_y row is written).  Each part computes its outputs exactly as the
-// whole kernel does, so the two halves run on different streams give its bits.
+// only (no grad_y row is written); 3 neither (the row weights alone).  Each part
+// computes its outputs exactly as the whole kernel does.
 template <int KMAX, bool ONE_PASS, bool Q8 = false, int PART = 0>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
-  constexpr bool kDY = PART != 2, kDW = PART != 1;
+  constexpr bool kDY = PART == 0 || PART == 1, kDW = PART == 0 || PART == 2;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave;
   if (t >= a.T) return;
   SlotInfo<KMAX> si;
   load_slots(a.slot2row, a.w, t, a.K, lane, si);
+  if (a.roww)
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (lane == k && si.code[k] >= 0) a.roww[si.code[k]] = si.w[k];
+  if constexpr (PART == 3) return;
   const int64_t Hv = a.Hv;
   const uint4* __restrict__ y = a.y;
   const uint4* __restrict__ dout = a.dout;
@@ -327,7 +335,8 @@ moe_status combine_bwd_impl(const moe_shape* s, const void* grad_out, const void
                             const float* topk_weights, const int32_t* assist, const int32_t* ep_send_counts,
                             const uint8_t* x_active_mask, const void* ori_x, const void* const_alpha_1,
                             const void* const_alpha_2, const void* const_v, void* grad_y, uint8_t* grad_yq,
-                            float* grad_y_scales, float* grad_topk_weights, void* stream) {
+                            float* grad_y_scales, float* grad_topk_weights, void* stream,
+                            float* row_weights = nullptr) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   const bool q8 = grad_yq != nullptr;
@@ -335,10 +344,10 @@ moe_status combine_bwd_impl(const moe_shape* s, const void* grad_out, const void
   if (q8 && s->capacity * (s->H / 128) * 4 >= (int64_t)0x7ffffff0) return MOE_ERR_UNSUPPORTED;
   // bf16: either output may be left out (NULL), not both; the fp8 variant
   // writes grad_topk_weights always
-  const int part = q8 ? 0 : (!grad_y ? 2 : (!grad_topk_weights ? 1 : 0));
-  if (!q8 && !grad_y && !grad_topk_weights) return MOE_ERR_NULL_ARG;
+  const int part = q8 ? 0 : (!grad_y ? (grad_topk_weights ? 2 : 3) : (!grad_topk_weights ? 1 : 0));
+  if (!q8 && !grad_y && !grad_topk_weights && !row_weights) return MOE_ERR_NULL_ARG;
   if (s->T == 0) return MOE_OK;
-  if (part != 1) MOE_NEED(y, s->capacity * s->H);
+  if (part == 0 || part == 2) MOE_NEED(y, s->capacity * s->H);
   if (q8) MOE_NEED(grad_y_scales, s->capacity * (s->H / 128));
   if (!grad_out || !topk_idx || !topk_weights || !assist || !ep_send_counts || (q8 && !grad_topk_weights))
     return MOE_ERR_NULL_ARG;
@@ -361,7 +370,8 @@ moe_status combine_bwd_impl(const moe_shape* s, const void* grad_out, const void
                    s->comm_quant_mode == 2,
                    reinterpret_cast<uint2*>(grad_yq),
                    grad_y_scales,
-                   s->capacity};
+                   s->capacity,
+                   row_weights};
   launch_k(s->K, [&](auto km) {
     constexpr int KM = decltype(km)::value;
     const bool one = a.qpay && a.Hv <= (int64_t)kChunk<KM> * kWave;
@@ -369,6 +379,9 @@ moe_status combine_bwd_impl(const moe_shape* s, const void* grad_out, const void
       hipLaunchKernelGGL((k_combine_bwd<KM, true, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
     else if (q8)
       hipLaunchKernelGGL((k_combine_bwd<KM, false, true>), token_grid(s->T), dim3(256), 0, as_stream(stream), a);
+    else if (part == 3)  // the row weights alone
+      hipLaunchKernelGGL((k_combine_bwd<KM, false, false, 3>), token_grid(s->T), dim3(256), 0, as_stream(stream),
+                         a);
     else if (part == 1)  // grad_y alone reads no y row, so it needs no int8 amax either
       hipLaunchKernelGGL((k_combine_bwd<KM, false, false, 1>), token_grid(s->T), dim3(256), 0, as_stream(stream),
                          a);
@@ -410,6 +423,19 @@ extern "C" moe_status moe_combine_bwd_fp8(const moe_shape* s, const void* grad_o
   return combine_bwd_impl(s, grad_out, y, topk_idx, topk_weights, assist, ep_send_counts, x_active_mask, ori_x,
                           const_alpha_1, const_alpha_2, const_v, grad_y, grad_yq, grad_y_scales,
                           grad_topk_weights, stream);
+}
+
+extern "C" moe_status moe_combine_bwd_weights(const moe_shape* s, const void* grad_out, const void* y,
+                                              const int32_t* topk_idx, const float* topk_weights,
+                                              const int32_t* assist, const int32_t* ep_send_counts,
+                                              const uint8_t* x_active_mask, const void* ori_x,
+                                              const void* const_alpha_1, const void* const_alpha_2,
+                                              const void* const_v, float* grad_topk_weights, float* row_weights,
+                                              void* stream) {
+  if (!row_weights) return MOE_ERR_NULL_ARG;
+  return combine_bwd_impl(s, grad_out, y, topk_idx, topk_weights, assist, ep_send_counts, x_active_mask, ori_x,
+                          const_alpha_1, const_alpha_2, const_v, nullptr, nullptr, nullptr, grad_topk_weights,
+                          stream, row_weights);
 }
 
 extern "C" moe_status moe_dispatch_bwd(const moe_shape* s, const void* grad_expand_x,

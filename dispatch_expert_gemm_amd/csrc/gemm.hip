@@ -82,6 +82,11 @@ struct GemmArgs {
   const int32_t* gather;
   int gK;
   int64_t gbytes;  // bytes of x (T * H * 2): the range of the gathered loads
+  // down data and weight gradients with the A operand gathered: row r of the
+  // expert-sorted grad_y is bf16(rowsc[r] * grad_out[slot(r) / K]), rowsc[r] the
+  // routing weight of the row's slot (the operand the combine backward would
+  // have written, rounded the same way)
+  const float* rowsc;
   // gate/up weight gradient with the B operand gathered (rows of x read through
   // the row -> slot map): rows of the map (capacity), and slot / K as
   // (slot * kmagic) >> kshift (exact for slots below 2^31)
@@ -140,6 +145,17 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// bf16(w[i] * v[i]) of the eight bf16 values of a fragment: one fp32 product and
+// one round to nearest even each, the arithmetic of the combine backward's grad_y
+// rows (for finite values the hardware conversion rounds as the written-out one does)
+__device__ __forceinline__ bf16x8 scale_bf16x8_each(bf16x8 v, const float* w) {
+  float f[8];
+  unpack8(__builtin_bit_cast(uint4, v), f);
+  const uint4 o = make_uint4(pk_bf16(w[0] * f[0], w[1] * f[1]), pk_bf16(w[2] * f[2], w[3] * f[3]),
+                             pk_bf16(w[4] * f[4], w[5] * f[5]), pk_bf16(w[6] * f[6], w[7] * f[7]));
+  return __builtin_bit_cast(bf16x8, o);
+}
 
 // LDS operand tile: R rows x W k of bf16, row pitch 2W bytes, in 16-byte
 // chunks of 8 consecutive k.  Chunk c of row r sits at chunk position
@@ -729,7 +745,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
       const int r = RPIK * q + lane / CPRK, c = (lane % CPRK) ^ swz(r);
       const int rr = r < rows_valid ? r : rows_valid - 1;
       int64_t arow = rr;  // row of A relative to abase
-      if constexpr (MODE == GATE_UP_FWD && !FP8)
+      if constexpr ((MODE == GATE_UP_FWD || MODE == DOWN_BWD_DATA) && !FP8)
         if (g.gather) arow = g.gather[row0 + rr] / g.gK;  // the token of this expanded row
       voA[j] = (uint32_t)((arow * g.lda + c * 8) * 2);
       kcA[j] = c * 8;
@@ -764,14 +780,32 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
       kcB[j] = 0;
     }
   }
-  const bool gathered = MODE == GATE_UP_FWD && !FP8 && g.gather;
+  const bool gathered = (MODE == GATE_UP_FWD || MODE == DOWN_BWD_DATA) && !FP8 && g.gather;
   // gate/up weight gradient reading the rows of x through the row -> slot map:
   // lane k-rows and byte columns of its B loads, and a ring of the map's entries
   // per K step (8 steps of 64), filled by wave 0 with direct-to-LDS loads two
   // steps ahead of the step whose tile loads need them
   constexpr bool GATHER_B = MODE == GATE_UP_BWD_W && !FP8;
   const bool gatherB = GATHER_B && g.gather;
-  __shared__ int32_t tokr[GATHER_B ? 8 * 64 : 1];
+  // down weight gradient reading grad_out rows through the same map (A operand),
+  // each k-row scaled by its routing weight: the weights of a K step's k-rows go
+  // into LDS with the step's tiles (wave 0, one dword per lane)
+  constexpr bool GATHER_A = MODE == DOWN_BWD_W && !FP8;
+  const bool gatherA = GATHER_A && g.gather;
+  __shared__ int32_t tokr[(GATHER_A || GATHER_B) ? 8 * 64 : 1];
+  __shared__ __attribute__((aligned(16))) float wst[GATHER_A ? S * 64 : 1];
+  int kA[LA];
+  uint32_t colA[LA];
+  if constexpr (GATHER_A) {
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+      constexpr int CPR = BM / 8, RPI = 64 / CPR;
+      const int q = wave * LA + j;
+      const int k = RPI * q + lane / CPR, c = (lane % CPR) ^ sw4(k);
+      kA[j] = k;
+      colA[j] = (uint32_t)((row0 + c * 8 < g.M ? row0 + c * 8 : g.M - 8) * 2);
+    }
+  }
   int kB[LB];
   uint32_t colB[LB];
 #pragma unroll
@@ -811,6 +845,30 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
       for (int j = 0; j < LA; ++j) {
         const uint32_t vo = (tail && k0 + kcA[j] >= kend) ? kOOB : voA[j];
         dma(r, sa + (wv * LA + j) * 512, vo);
+      }
+    } else if (GATHER_A && gatherA) {
+      // k-row k of the step is expanded row kbeg + k0 + k: grad_out row slot/K;
+      // k-rows past the expert's end read zeros
+      const auto r = rsrc(g.A, g.gbytes);
+      const int32_t* tk = tokr + (kt & 7) * 64;
+#pragma unroll
+      for (int j = 0; j < LA; ++j) {
+        uint32_t vo = kOOB;
+        if (k0 + kA[j] < klen) {
+          const uint32_t sl = (uint32_t)tk[kA[j]];
+          const uint32_t tok = (uint32_t)(((uint64_t)sl * g.kmagic) >> g.kshift);
+          vo = tok * (uint32_t)(g.lda * 2) + colA[j];
+        }
+        dma(r, sa + (wv * LA + j) * 512, vo);
+      }
+      if (wv == 0) {
+        // the routing weights of the step's rows (64 from its first; past the
+        // expert's end: zeros)
+        const auto rw = rsrc(g.rowsc + kbeg + k0, (klen - k0) * 4);
+        const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>(
+            (const __attribute__((address_space(3))) float*)(wst + st * 64));
+        const uint32_t vo = (uint32_t)lane * 4;
+        asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(vo), "s"(rw), "{m0}"(m0));
       }
     } else {
       const auto r = rsrc(abase + k0 * g.lda * 2, (klen - k0) * g.lda * 2);
@@ -909,6 +967,16 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
         if constexpr (!KGROUP) fa[slot][i] = *reinterpret_cast<const bf16x8*>(as + lds_off(arow[i], c));
         else fa[slot][i] = frag_tr(as + trA[i], kk, BM);
       }
+      if constexpr (GATHER_A) {
+        // k-rows 16 kk + 8 (lane / 32) + 0..7 of the step: eight weights
+        if (gatherA) {
+          const float4* wp = reinterpret_cast<const float4*>(wst + st * 64 + 16 * kk + 8 * (lane >> 5));
+          const float4 w0 = wp[0], w1 = wp[1];
+          const float w8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int i = 0; i < TI; ++i) fa[slot][i] = scale_bf16x8_each(fa[slot][i], w8);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         if constexpr (B_KC) fb[slot][j] = *reinterpret_cast<const bf16x8*>(bs + lds_off(brw[j], c));
@@ -954,7 +1022,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     const uint32_t vo = (uint32_t)lane * 4;
     asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(vo), "s"(r), "{m0}"(m0));
   };
-  if (GATHER_B && gatherB) {
+  if ((GATHER_B && gatherB) || (GATHER_A && gatherA)) {
     // the entries of the first S + 1 steps, with plain loads before the pipeline
     static_assert(!GATHER_B || kThreads >= 64, "");
     for (int i = tid; i < (S + 1) * 64; i += kThreads) {
@@ -975,7 +1043,7 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     asm volatile("" ::: "memory");
     // (the map entries go before the tile loads: the wait of a later step then
     // covers them without waiting on a tile load issued after them)
-    if (GATHER_B && gatherB && kt + S + 1 < nk) issue_tok(kt + S + 1);
+    if (((GATHER_B && gatherB) || (GATHER_A && gatherA)) && kt + S + 1 < nk) issue_tok(kt + S + 1);
     if (kt + S - 1 < nk) issue(std::integral_constant<int, (st + S - 1) % S>(), rot(kt + S - 1));
     compute(ST);
   };
@@ -993,6 +1061,20 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
     if constexpr (S > 3) if (kt + 3 < nk) kstep(std::integral_constant<int, 3 % S>(), kt + 3);
   }
   __syncthreads();
+  if constexpr (MODE == DOWN_BWD_DATA && !FP8) {
+    // gathered: grad_y row r is w_r * grad_out[token]; the row's weight multiplies
+    // its fp32 product with W_down (the grad_y path rounds w_r * grad_out to bf16
+    // first: one rounding fewer here)
+    if (gathered)
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const float wr = g.rowsc[row0 + (arow[i] < rows_valid ? arow[i] : rows_valid - 1)];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= wr;
+      }
+  }
 
   }
 
@@ -1731,6 +1813,76 @@ extern "C" moe_status moe_ffn_down_bwd_weight(const moe_shape* s, const void* gr
   GemmArgs g = base_args(s, ep_recv_counts);
   g.A = static_cast<const bf16_t*>(grad_y);
   g.lda = s->H;
+  g.B0 = static_cast<const bf16_t*>(h_act);
+  g.ldb = s->F;
+  g.M = s->H;
+  g.N = s->F;
+  g.W0 = grad_w_down;
+  return launch<DOWN_BWD_W>(g, s, as_stream(stream));
+}
+
+namespace moe {
+namespace {
+// slot / K as (slot * kmagic) >> kshift: l = ceil(log2 K), kmagic = floor(2^(32+l) / K) + 1
+void set_kdiv(GemmArgs& g, int K) {
+  int l = 0;
+  while ((1 << l) < K) ++l;
+  g.kmagic = (((uint64_t)1 << (32 + l)) / (uint64_t)K) + 1;
+  g.kshift = 32 + l;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_ffn_down_bwd_data_gather(const moe_shape* s, const void* grad_out, const int32_t* assist,
+                                                   const float* row_weights, const void* w_down,
+                                                   const void* gate_up_save, const int32_t* ep_recv_counts,
+                                                   void* grad_gate_up, void* stream) {
+  moe_status st = check_ffn_shape(s);
+  if (st != MOE_OK) return st;
+  if (!w_down || !ep_recv_counts) return MOE_ERR_NULL_ARG;
+  // 31-bit per-lane byte offsets into grad_out (the top bit marks a load past
+  // the end of the contraction)
+  if ((s->T + 1) * s->H * 2 > 0x7ffffff0LL) return MOE_ERR_UNSUPPORTED;
+  if (s->capacity == 0) return MOE_OK;
+  if (!grad_out || !assist || !row_weights || !gate_up_save || !grad_gate_up) return MOE_ERR_NULL_ARG;
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.A = static_cast<const bf16_t*>(grad_out);
+  g.gather = assist + s->T * s->K;  // row -> slot
+  g.gK = s->K;
+  g.gbytes = s->T * s->H * 2;
+  g.rowsc = row_weights;
+  g.lda = s->H;
+  g.B0 = static_cast<const bf16_t*>(w_down);
+  g.ldb = s->F;
+  g.bstride = s->H * s->F;
+  g.N = s->F;
+  g.Kd = s->H;
+  g.aux = static_cast<const bf16_t*>(gate_up_save);
+  g.C0 = static_cast<bf16_t*>(grad_gate_up);
+  return launch<DOWN_BWD_DATA>(g, s, as_stream(stream));
+}
+
+extern "C" moe_status moe_ffn_down_bwd_weight_gather(const moe_shape* s, const void* grad_out, const int32_t* assist,
+                                                     const float* row_weights, const void* h_act,
+                                                     const int32_t* ep_recv_counts, float* grad_w_down,
+                                                     void* stream) {
+  moe_status st = check_ffn_shape(s);
+  if (st != MOE_OK) return st;
+  if (!ep_recv_counts || !grad_w_down) return MOE_ERR_NULL_ARG;
+  if ((s->T + 1) * s->H * 2 > 0x7ffffff0LL) return MOE_ERR_UNSUPPORTED;
+  MOE_NEED(grad_out, s->T * s->H);
+  MOE_NEED(assist, s->T * s->K + s->capacity);
+  MOE_NEED(row_weights, s->capacity);
+  MOE_NEED(h_act, s->capacity * s->F);
+  GemmArgs g = base_args(s, ep_recv_counts);
+  g.A = static_cast<const bf16_t*>(grad_out);
+  g.lda = s->H;
+  g.gather = s->capacity > 0 ? assist + s->T * s->K : nullptr;  // row -> slot
+  g.gK = s->K;
+  g.gbytes = s->T * s->H * 2;
+  g.grows = s->capacity;
+  g.rowsc = row_weights;
+  set_kdiv(g, s->K);
   g.B0 = static_cast<const bf16_t*>(h_act);
   g.ldb = s->F;
   g.M = s->H;

@@ -313,6 +313,51 @@ moe_status moe_ffn_down_bwd_weight(const moe_shape* s, const void* grad_y, const
                                    const int32_t* ep_recv_counts, float* grad_w_down,
                                    void* stream);
 
+/*
+ * The combine backward folded into the down GEMMs' operand loads.  The combine
+ * backward's grad_y row of expanded row r is bf16(topk_weights[s] * grad_out[s / K])
+ * with s = slot(r) (low_latency_combine page, "Function": the gradient of the
+ * weighted sum); the two down-backward GEMMs below form it in registers from
+ * grad_out read through the row -> slot map, so the step never writes or reads
+ * grad_y (2 bytes per routed row and column each way).  The weights' gradient and
+ * the down weight gradient are bit for bit those of moe_combine_bwd +
+ * moe_ffn_down_bwd_weight (the weight gradient forms bf16(w * grad_out) rows in
+ * registers); the down data gradient multiplies each row's fp32 product
+ * grad_out[s / K] Wd_e by the row's weight (one bf16 rounding fewer than
+ * moe_ffn_down_bwd_data on grad_y; within the element-wise parity bar of it).
+ *
+ * moe_combine_bwd_weights - grad_topk_weights as moe_combine_bwd computes it, and
+ *   row_weights[r] = topk_weights[slot(r)] for every routed row r (rows past the
+ *   routed ones are not written); no grad_y.  grad_topk_weights may be NULL
+ *   (routing weights that need no gradient): then no y row is read.
+ *  out  grad_topk_weights (T, K) fp32 or NULL, row_weights (capacity,) fp32
+ *  other arguments as moe_combine_bwd.  One kernel launch.
+ */
+moe_status moe_combine_bwd_weights(const moe_shape* s, const void* grad_out, const void* y,
+                                   const int32_t* topk_idx, const float* topk_weights,
+                                   const int32_t* assist_info_for_combine, const int32_t* ep_send_counts,
+                                   const uint8_t* x_active_mask, const void* ori_x, const void* const_alpha_1,
+                                   const void* const_alpha_2, const void* const_v, float* grad_topk_weights,
+                                   float* row_weights, void* stream);
+
+/* moe_ffn_down_bwd_data_gather - moe_ffn_down_bwd_data with dH[r] =
+ * row_weights[r] * (grad_out[slot(r) / K] Wd_e) in fp32, grad_out (T, H) bf16 read
+ * through the assist info's row -> slot map, row_weights from
+ * moe_combine_bwd_weights.  MOE_ERR_UNSUPPORTED when (T + 1) * H * 2 bytes
+ * exceed 2^31 - 16 (31-bit operand offsets).  One kernel launch. */
+moe_status moe_ffn_down_bwd_data_gather(const moe_shape* s, const void* grad_out,
+                                        const int32_t* assist_info_for_combine, const float* row_weights,
+                                        const void* w_down, const void* gate_up_save,
+                                        const int32_t* ep_recv_counts, void* grad_gate_up, void* stream);
+
+/* moe_ffn_down_bwd_weight_gather - moe_ffn_down_bwd_weight on grad_y rows
+ * bf16(row_weights[r] * grad_out[slot(r) / K]) formed in registers (bit for bit).
+ * Same limit.  One kernel launch. */
+moe_status moe_ffn_down_bwd_weight_gather(const moe_shape* s, const void* grad_out,
+                                          const int32_t* assist_info_for_combine, const float* row_weights,
+                                          const void* h_act, const int32_t* ep_recv_counts,
+                                          float* grad_w_down, void* stream);
+
 /* grad_expand_x = grad_gate_up [Wg_e; Wu_e].  One kernel launch. */
 moe_status moe_ffn_gate_up_bwd_data(const moe_shape* s, const void* grad_gate_up,
                                     const void* w_gate, const void* w_up,
