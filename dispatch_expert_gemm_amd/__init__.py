@@ -376,6 +376,15 @@ def moe_combine_bwd(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_
         _ptr(grad_topk_weights, F32, "grad_topk_weights"), _stream(stream)))
 
 
+def fold_combine_bwd(F: int) -> bool:
+    """Whether the bf16 backward folds the combine backward into the down GEMMs
+    (moe_combine_bwd_weights + the *_gather down GEMMs) rather than writing grad_y
+    rows: for a narrow expert FFN.  Measured on MI355X: 3% faster steps at F = 480
+    (H = 1536), 1.3% slower at F = 2048 (H = 7168), where the down weight
+    gradient's scaling of every operand element costs more than grad_y's bytes."""
+    return F < 1024
+
+
 def moe_combine_bwd_weights(shape, grad_out, y, topk_idx, topk_weights, assist_info_for_combine,
                             ep_send_counts, x_active_mask, ori_x, const_alpha_1, const_alpha_2, const_v,
                             grad_topk_weights, row_weights, stream=None):
@@ -1119,7 +1128,7 @@ class _MoELayerFn(torch.autograd.Function):
         dev = x.device
         # grad_y rows exist on the 8-bit paths only (the bf16 down GEMMs read
         # grad_out through the map)
-        gy = torch.empty((cap, H), dtype=BF16, device=dev) if ctx.fp8 else None
+        gy = torch.empty((cap, H), dtype=BF16, device=dev) if ctx.fp8 or not fold_combine_bwd(F) else None
         # routing weights that need no gradient: the combine backward writes grad_y
         # alone and reads no y row (the fp8 variant always writes both)
         need_gw = ctx.needs_input_grad[1] or ctx.fused8
@@ -1129,9 +1138,10 @@ class _MoELayerFn(torch.autograd.Function):
             gys = torch.empty((H // 128, cap), dtype=F32T, device=dev)
             moe_combine_bwd_fp8(shape, grad_out, y, topk_idx, topk_weights, assist, recv, mask, x, a1, a2, cv,
                                 gy, gyq, gys, gw)
-        elif not ctx.fp8:
-            # bf16: the combine backward folded into the down GEMMs (grad_out rows
-            # read through the map, each row's routing weight applied in the GEMM)
+        elif not ctx.fp8 and fold_combine_bwd(F):
+            # bf16, narrow FFN: the combine backward folded into the down GEMMs
+            # (grad_out rows read through the map, each row's routing weight
+            # applied in the GEMM)
             roww = torch.empty((cap,), dtype=F32, device=dev)
             moe_combine_bwd_weights(shape, grad_out, y if need_gw else None, topk_idx, topk_weights, assist, recv,
                                     mask, x, a1, a2, cv, gw, roww)
@@ -1186,9 +1196,13 @@ class _MoELayerFn(torch.autograd.Function):
                 moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
             moe_ffn_gate_up_bwd_data_fp8(shape, dgq, dgs, wgt, wgs, wut, wus, recv, gx_exp)
             del dgq, dgs
-        else:
+        elif fold_combine_bwd(F):
             moe_ffn_down_bwd_data_gather(shape, grad_out, assist, roww, w_down, gus, recv, ggu)
             moe_ffn_down_bwd_weight_gather(shape, grad_out, assist, roww, h, recv, gwd)
+            moe_ffn_gate_up_bwd_data(shape, ggu, w_gate, w_up, recv, gx_exp)
+        else:
+            moe_ffn_down_bwd_data(shape, gy, w_down, gus, recv, ggu)
+            moe_ffn_down_bwd_weight(shape, gy, h, recv, gwd)
             moe_ffn_gate_up_bwd_data(shape, ggu, w_gate, w_up, recv, gx_exp)
         accum = None
         s_grads = (None, None, None)
