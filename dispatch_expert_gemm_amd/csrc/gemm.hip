@@ -82,10 +82,11 @@ struct GemmArgs {
   const int32_t* gather;
   int gK;
   int64_t gbytes;  // bytes of x (T * H * 2): the range of the gathered loads
-  // down data and weight gradients with the A operand gathered: row r of the
-  // expert-sorted grad_y is bf16(rowsc[r] * grad_out[slot(r) / K]), rowsc[r] the
-  // routing weight of the row's slot (the operand the combine backward would
-  // have written, rounded the same way)
+  // down data and weight gradients with the A operand gathered from grad_out:
+  // row r of the expert-sorted grad_y is rowsc[r] * grad_out[slot(r) / K],
+  // rowsc[r] the routing weight of the row's slot; the weight gradient forms it
+  // as the combine backward stores it, bf16(rowsc[r] * grad_out), the data
+  // gradient multiplies each row's fp32 product with W_down by rowsc[r]
   const float* rowsc;
   // gate/up weight gradient with the B operand gathered (rows of x read through
   // the row -> slot map): rows of the map (capacity), and slot / K as
