@@ -968,8 +968,16 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
         if constexpr (!KGROUP) fa[slot][i] = *reinterpret_cast<const bf16x8*>(as + lds_off(arow[i], c));
         else fa[slot][i] = frag_tr(as + trA[i], kk, BM);
       }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (B_KC) fb[slot][j] = *reinterpret_cast<const bf16x8*>(bs + lds_off(brw[j], c));
+        else fb[slot][j] = frag_tr(bs + trB[j], kk, BN);
+      }
+    };
+    // gathered down weight gradient: the A fragments of sub-step kk (k-rows
+    // 16 kk + 8 (lane / 32) + 0..7 of the step) times their eight routing weights
+    auto scale = [&](int kk, int slot) {
       if constexpr (GATHER_A) {
-        // k-rows 16 kk + 8 (lane / 32) + 0..7 of the step: eight weights
         if (gatherA) {
           const float4* wp = reinterpret_cast<const float4*>(wst + st * 64 + 16 * kk + 8 * (lane >> 5));
           const float4 w0 = wp[0], w1 = wp[1];
@@ -978,13 +986,9 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
           for (int i = 0; i < TI; ++i) fa[slot][i] = scale_bf16x8_each(fa[slot][i], w8);
         }
       }
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        if constexpr (B_KC) fb[slot][j] = *reinterpret_cast<const bf16x8*>(bs + lds_off(brw[j], c));
-        else fb[slot][j] = frag_tr(bs + trB[j], kk, BN);
-      }
     };
     fetch(0, 0);
+    scale(0, 0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       if (kk + 1 < BK / 16) fetch(kk + 1, (kk + 1) & 1);
@@ -995,6 +999,10 @@ __global__ __launch_bounds__((Cfg<MODE, BM, BN, FP8, BK, S_, WM_, WN_>::kThreads
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][j], fa[kk & 1][i], acc[i][j], 0, 0, 0);
+      // the scaling of sub-step kk+1 issues behind these MFMAs and runs while
+      // they execute
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < BK / 16) scale(kk + 1, (kk + 1) & 1);
     }
   };
 
