@@ -1129,8 +1129,8 @@ class _MoELayerFn(torch.autograd.Function):
         # grad_y rows exist on the 8-bit paths only (the bf16 down GEMMs read
         # grad_out through the map)
         gy = torch.empty((cap, H), dtype=BF16, device=dev) if ctx.fp8 or not fold_combine_bwd(F) else None
-        # routing weights that need no gradient: the combine backward writes grad_y
-        # alone and reads no y row (the fp8 variant always writes both)
+        # routing weights that need no gradient: the combine backward reads no y row
+        # and writes only grad_y or the row weights (the fp8 variant always writes both)
         need_gw = ctx.needs_input_grad[1] or ctx.fused8
         gw = torch.empty((T, K), dtype=F32, device=dev) if need_gw else None
         if ctx.fused8:
