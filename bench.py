@@ -982,10 +982,13 @@ def main():
                   + sum(b / (PEAK_HBM_GBS * 1e9) for b in nb.values() if b is not None)) * 1e3
     T, H, F, E, K = (st.config[k] for k in ("T", "H", "F", "E", "K"))
     descr = {
-        "page1": "Triton-distributed benchmark shape, dispatch permute folded into the gate/up GEMMs' row loads",
-        "page1_permute": "Triton-distributed benchmark shape, dispatch permute as a kernel of its own",
+        "page1": "Triton-distributed benchmark shape, dispatch permute folded into the gate/up GEMMs' row loads, "
+                 "combine backward into the down GEMMs' row loads",
+        "page1_permute": "Triton-distributed benchmark shape, dispatch permute as a kernel of its own, combine "
+                         "backward folded into the down GEMMs' row loads",
         "page1_rank_share": "one of the Triton-distributed benchmark's four ranks: 16 local experts, 65,536 "
-                            "received rows, dispatch permute folded into the gate/up GEMMs' row loads",
+                            "received rows, dispatch permute folded into the gate/up GEMMs' row loads, "
+                            "combine backward into the down GEMMs' row loads",
         "dsv3_proxy": "DeepSeek-V3-style proxy, Zipf(1.2) routing, one shared expert",
         "mixtral": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs, int8 combine payload",
         "mixtral_grouped": "Mixtral-8x7B-style layer, fp8 e4m3 block-scaled GEMMs through the grouped fp8 "
